@@ -1,0 +1,178 @@
+"""MI355X (gfx950) TQ1_0 x Q8_1 quantized mat-vec.
+
+A thin binding over the C ABI in ``include/bqm.h`` (library ``libbqm.so``,
+built in-tree by ``bit_quantized_mat_amd.build``). Every function here only
+checks and marshals arguments: tensors are torch device tensors used as plain
+device memory, and every step of the computation runs in the HIP kernels.
+There is no CPU fallback: if the library is missing, calls raise.
+"""
+import ctypes
+import os
+
+__all__ = [
+    "BqmError", "library", "library_path", "tq1_pack", "q8_1_quantize", "mmvq_tq1_0",
+    "mmvq_id_tq1_0", "mmvq_id_tq1_0_workspace_bytes", "mmvq_tq1_0_block_isums",
+    "TQ1_BLOCK_BYTES", "Q81_BLOCK_BYTES", "MMVQ_MAX_COLS",
+]
+
+TQ1_BLOCK_BYTES = 54
+Q81_BLOCK_BYTES = 36
+MMVQ_MAX_COLS = 32
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_lib = None
+
+_i32, _i64, _p, _sz = ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p, ctypes.c_size_t
+
+
+class BqmError(RuntimeError):
+    """A library entry point returned a non-zero status."""
+
+    def __init__(self, fn, status):
+        text = library().bqm_status_string(status).decode()
+        super().__init__("%s failed with status %d (%s)" % (fn, status, text))
+        self.status = status
+
+
+def library_path():
+    return os.path.join(_HERE, "libbqm.so")
+
+
+def library():
+    """The loaded C library (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        path = library_path()
+        if not os.path.exists(path):
+            raise RuntimeError("libbqm.so is not built; run bit_quantized_mat_amd.build.build() "
+                               "(or __graft_entry__.build()) first")
+        L = ctypes.CDLL(path)
+        L.tq1_pack.argtypes = [_p, _p, _p, _i64, _i64, _p]
+        L.q8_1_quantize.argtypes = [_p, _p, _i64, _i64, _p]
+        L.mmvq_tq1_0.argtypes = [_p, _p, _p, _i64, _i64, _i32, _p]
+        L.mmvq_tq1_0_block_isums.argtypes = [_p, _p, _p, _i64, _i64, _i32, _p]
+        L.mmvq_id_tq1_0.argtypes = [_p, _p, _p, _p, _i64, _i64, _i64, _i64, _i32, _p, _sz, _p]
+        L.mmvq_id_tq1_0_workspace_bytes.argtypes = [_i64, _i64, _i32]
+        L.mmvq_id_tq1_0_workspace_bytes.restype = _sz
+        L.bqm_status_string.argtypes = [ctypes.c_int]
+        L.bqm_status_string.restype = ctypes.c_char_p
+        L.bqm_version.restype = ctypes.c_int
+        for name in ("tq1_pack", "q8_1_quantize", "mmvq_tq1_0", "mmvq_tq1_0_block_isums",
+                     "mmvq_id_tq1_0"):
+            getattr(L, name).restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _stream(stream, device):
+    torch = _torch()
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _dev_tensor(t, name, dtypes, min_bytes, device=None):
+    torch = _torch()
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError("%s must be a GPU tensor" % name)
+    if t.dtype not in dtypes:
+        raise TypeError("%s has dtype %s, expected one of %s" % (name, t.dtype, dtypes))
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    if t.numel() * t.element_size() < min_bytes:
+        raise ValueError("%s holds %d bytes, needs %d" % (name, t.numel() * t.element_size(), min_bytes))
+    if device is not None and t.device != device:
+        raise ValueError("%s is on %s, expected %s" % (name, t.device, device))
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _call(fn, *args):
+    rc = getattr(library(), fn)(*args)
+    if rc != 0:
+        raise BqmError(fn, rc)
+
+
+def tq1_pack(trits, d16, out=None, stream=None):
+    """trits int8 [N, K] (values -1/0/1), d16 fp16 or int16/uint16 bits [N, K/256]
+    -> TQ1_0 bytes uint8 [N, K/256*54]."""
+    torch = _torch()
+    N, K = trits.shape
+    nb = K // 256
+    if out is None:
+        out = torch.empty((N, nb * TQ1_BLOCK_BYTES), dtype=torch.uint8, device=trits.device)
+    dtypes16 = (torch.float16, torch.int16, torch.uint16)
+    _call("tq1_pack",
+          _dev_tensor(trits, "trits", (torch.int8,), N * K),
+          _dev_tensor(d16, "d16", dtypes16, N * nb * 2, trits.device),
+          _dev_tensor(out, "out", (torch.uint8,), N * nb * TQ1_BLOCK_BYTES, trits.device),
+          N, K, _stream(stream, trits.device))
+    return out
+
+
+def q8_1_quantize(x, out=None, stream=None):
+    """x fp32 [T, K] -> Q8_1 bytes uint8 [T, K/32*36]."""
+    torch = _torch()
+    T, K = x.shape
+    if out is None:
+        out = torch.empty((T, (K // 32) * Q81_BLOCK_BYTES), dtype=torch.uint8, device=x.device)
+    _call("q8_1_quantize",
+          _dev_tensor(x, "x", (torch.float32,), T * K * 4),
+          _dev_tensor(out, "out", (torch.uint8,), T * (K // 32) * Q81_BLOCK_BYTES, x.device),
+          T, K, _stream(stream, x.device))
+    return out
+
+
+def _mmvq_args(w, a, N, K, T):
+    torch = _torch()
+    return (_dev_tensor(w, "w", (torch.uint8,), N * (K // 256) * TQ1_BLOCK_BYTES),
+            _dev_tensor(a, "a", (torch.uint8,), T * (K // 32) * Q81_BLOCK_BYTES, w.device))
+
+
+def mmvq_tq1_0(w, a, N, K, T, out=None, stream=None):
+    """y fp32 [T, N] = TQ1_0 weights [N, K] times T Q8_1 activation columns."""
+    torch = _torch()
+    if out is None:
+        out = torch.empty((T, N), dtype=torch.float32, device=w.device)
+    pw, pa = _mmvq_args(w, a, N, K, T)
+    _call("mmvq_tq1_0", pw, pa, _dev_tensor(out, "out", (torch.float32,), T * N * 4, w.device),
+          N, K, T, _stream(stream, w.device))
+    return out
+
+
+def mmvq_tq1_0_block_isums(w, a, N, K, T, out=None, stream=None):
+    """Exact per-32 integer sums int32 [T, N, K/32] from the production inner loop."""
+    torch = _torch()
+    if out is None:
+        out = torch.empty((T, N, K // 32), dtype=torch.int32, device=w.device)
+    pw, pa = _mmvq_args(w, a, N, K, T)
+    _call("mmvq_tq1_0_block_isums", pw, pa,
+          _dev_tensor(out, "out", (torch.int32,), T * N * (K // 32) * 4, w.device),
+          N, K, T, _stream(stream, w.device))
+    return out
+
+
+def mmvq_id_tq1_0_workspace_bytes(E, T, n_used):
+    return int(library().mmvq_id_tq1_0_workspace_bytes(E, T, n_used))
+
+
+def mmvq_id_tq1_0(w, a, ids, E, N, K, T, n_used, out=None, workspace=None, stream=None):
+    """y fp32 [T, n_used, N]: expert ids[t][s]'s matrix times token t's activation."""
+    torch = _torch()
+    if out is None:
+        out = torch.empty((T, n_used, N), dtype=torch.float32, device=w.device)
+    need = mmvq_id_tq1_0_workspace_bytes(E, T, n_used)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=w.device)
+    pw = _dev_tensor(w, "w", (torch.uint8,), E * N * (K // 256) * TQ1_BLOCK_BYTES)
+    pa = _dev_tensor(a, "a", (torch.uint8,), T * (K // 32) * Q81_BLOCK_BYTES, w.device)
+    pi = _dev_tensor(ids, "ids", (torch.int32,), T * n_used * 4, w.device)
+    py = _dev_tensor(out, "out", (torch.float32,), T * n_used * N * 4, w.device)
+    pws = _dev_tensor(workspace, "workspace", (torch.uint8,), need, w.device)
+    _call("mmvq_id_tq1_0", pw, pa, pi, py, E, N, K, T, n_used, pws,
+          workspace.numel(), _stream(stream, w.device))
+    return out

@@ -1,0 +1,158 @@
+// bqm_api.hip -- the C ABI declared in include/bqm.h: argument validation on
+// the host, one dispatch point per entry, launches on the caller's stream.
+#include <string.h>
+
+#include "launch.hpp"
+
+namespace {
+
+constexpr int kVersion = 100;  // 0.1.0
+constexpr uint64_t kMaxBufferBytes = 0xfffffffcull;  // 32-bit byte offsets inside one matrix
+
+bool aligned4(const void *p) { return ((uintptr_t)p & 3u) == 0; }
+
+// Device check, cached per device ordinal: gfx950 only.
+int check_device()
+{
+    static int cached[64];  // 0 unknown, 1 ok, -1 not gfx950 (benign race: idempotent)
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0)
+        return BQM_ERR_DEVICE;
+    if (dev < 64 && cached[dev])
+        return cached[dev] > 0 ? BQM_OK : BQM_ERR_DEVICE;
+    hipDeviceProp_t prop;
+    int ok = hipGetDeviceProperties(&prop, dev) == hipSuccess &&
+             strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+    if (dev < 64)
+        cached[dev] = ok ? 1 : -1;
+    return ok ? BQM_OK : BQM_ERR_DEVICE;
+}
+
+hipStream_t as_stream(void *s) { return static_cast<hipStream_t>(s); }
+
+int check_matrix(int64_t N, int64_t K)
+{
+    if (N < 1 || K < 256 || K % 256 != 0)
+        return BQM_ERR_SHAPE;
+    if ((uint64_t)N * (uint64_t)(K / 256) * 54ull > kMaxBufferBytes)
+        return BQM_ERR_SHAPE;
+    return BQM_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int tq1_pack(const int8_t *trits, const uint16_t *d, void *w, int64_t N, int64_t K,
+             void *stream)
+{
+    if (!trits || !d || !w)
+        return BQM_ERR_NULL;
+    if (int rc = check_matrix(N, K))
+        return rc;
+    if (int rc = check_device())
+        return rc;
+    return bqm::launch_tq1_pack(trits, d, w, N, K, as_stream(stream));
+}
+
+int q8_1_quantize(const float *x, void *a, int64_t T, int64_t K, void *stream)
+{
+    if (!x || !a)
+        return BQM_ERR_NULL;
+    if (T < 1 || K < 32 || K % 32 != 0 || (uint64_t)T * (uint64_t)K > (1ull << 40))
+        return BQM_ERR_SHAPE;
+    if (!aligned4(x) || !aligned4(a))
+        return BQM_ERR_ALIGN;
+    if (int rc = check_device())
+        return rc;
+    return bqm::launch_q8_1_quantize(x, a, T, K, as_stream(stream));
+}
+
+static int mmvq_common(const void *w, const void *a, const void *out, int64_t N, int64_t K,
+                       int32_t T)
+{
+    if (!w || !a || !out)
+        return BQM_ERR_NULL;
+    if (int rc = check_matrix(N, K))
+        return rc;
+    if (T < 1 || T > BQM_MMVQ_MAX_COLS)
+        return BQM_ERR_SHAPE;
+    if ((uint64_t)T * (uint64_t)(K / 32) * 36ull > kMaxBufferBytes)
+        return BQM_ERR_SHAPE;
+    if (!aligned4(w) || !aligned4(a) || !aligned4(out))
+        return BQM_ERR_ALIGN;
+    return check_device();
+}
+
+int mmvq_tq1_0(const void *w, const void *a, float *y, int64_t N, int64_t K, int32_t T,
+               void *stream)
+{
+    if (int rc = mmvq_common(w, a, y, N, K, T))
+        return rc;
+    return bqm::launch_mmvq(w, a, y, nullptr, N, K, T, as_stream(stream));
+}
+
+int mmvq_tq1_0_block_isums(const void *w, const void *a, int32_t *isums, int64_t N, int64_t K,
+                           int32_t T, void *stream)
+{
+    if (int rc = mmvq_common(w, a, isums, N, K, T))
+        return rc;
+    return bqm::launch_mmvq(w, a, nullptr, isums, N, K, T, as_stream(stream));
+}
+
+size_t mmvq_id_tq1_0_workspace_bytes(int64_t E, int64_t T, int32_t n_used)
+{
+    if (E < 1 || T < 1 || n_used < 1 || n_used > E || T * (int64_t)n_used > 65535)
+        return 0;
+    return bqm::mmvq_id_workspace_bytes(E, T, n_used);
+}
+
+int mmvq_id_tq1_0(const void *w, const void *a, const int32_t *ids, float *y, int64_t E,
+                  int64_t N, int64_t K, int64_t T, int32_t n_used, void *workspace,
+                  size_t workspace_bytes, void *stream)
+{
+    if (!w || !a || !ids || !y)
+        return BQM_ERR_NULL;
+    if (E < 1 || T < 1 || n_used < 1 || n_used > E || T * (int64_t)n_used > 65535)
+        return BQM_ERR_SHAPE;
+    if (int rc = check_matrix(N, K))
+        return rc;
+    if ((uint64_t)T * (uint64_t)(K / 32) * 36ull > kMaxBufferBytes)
+        return BQM_ERR_SHAPE;
+    if (!aligned4(w) || !aligned4(a) || !aligned4(ids) || !aligned4(y))
+        return BQM_ERR_ALIGN;
+    const size_t need = bqm::mmvq_id_workspace_bytes(E, T, n_used);
+    if (!workspace || workspace_bytes < need)
+        return BQM_ERR_WORKSPACE;
+    if (((uintptr_t)workspace & 255u) != 0)
+        return BQM_ERR_ALIGN;
+    if (int rc = check_device())
+        return rc;
+    return bqm::launch_mmvq_id(w, a, ids, y, E, N, K, T, n_used, workspace, as_stream(stream));
+}
+
+const char *bqm_status_string(int status)
+{
+    switch (status) {
+    case BQM_OK:
+        return "ok";
+    case BQM_ERR_NULL:
+        return "a required pointer is NULL";
+    case BQM_ERR_SHAPE:
+        return "a size is out of range";
+    case BQM_ERR_ALIGN:
+        return "a buffer is misaligned";
+    case BQM_ERR_WORKSPACE:
+        return "workspace missing or too small";
+    case BQM_ERR_LAUNCH:
+        return "the HIP runtime reported a launch error";
+    case BQM_ERR_DEVICE:
+        return "the current device is not a gfx950 GPU";
+    default:
+        return "unknown status";
+    }
+}
+
+int bqm_version(void) { return kVersion; }
+
+}  // extern "C"

@@ -1,0 +1,78 @@
+// common.hpp -- device helpers shared by the gfx950 kernels of this library.
+//
+// All global reads of packed weights and activations go through raw buffer
+// resources: the descriptor carries the buffer's byte size, so a load whose
+// dword starts past the end returns zero instead of touching memory outside
+// the buffer. The descriptor size is rounded up to a whole dword; the at most
+// three slack bytes that this admits lie in the same aligned dword (hence the
+// same page) as the buffer's last byte.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace bqm {
+
+constexpr int kTq1BlockElems = 256;
+constexpr int kTq1BlockBytes = 54;
+constexpr int kQ81BlockElems = 32;
+constexpr int kQ81BlockBytes = 36;
+
+// Fourth descriptor dword for raw (untyped, stride 0) buffers on gfx9-family GPUs.
+constexpr int kRawBufferFlags = 0x00020000;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint64_t bytes)
+{
+    uint32_t n = bytes >= 0xfffffffcull ? 0xfffffffcu : (uint32_t)((bytes + 3) & ~3ull);
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)n,
+                                             kRawBufferFlags);
+}
+
+__device__ __forceinline__ uint32_t ld_b32(__amdgpu_buffer_rsrc_t r, uint32_t off)
+{
+    return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
+}
+
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ u32x2 ld_b64(__amdgpu_buffer_rsrc_t r, uint32_t off)
+{
+    return __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
+}
+
+__device__ __forceinline__ u32x4 ld_b128(__amdgpu_buffer_rsrc_t r, uint32_t off)
+{
+    return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+}
+
+// fp16 bits -> fp32 (exact).
+__device__ __forceinline__ float f16_bits_to_f32(uint32_t h)
+{
+    _Float16 v;
+    uint16_t b = (uint16_t)h;
+    __builtin_memcpy(&v, &b, 2);
+    return (float)v;
+}
+
+// fp32 -> fp16 bits, round to nearest even (the hardware conversion).
+__device__ __forceinline__ uint32_t f32_to_f16_bits(float f)
+{
+    _Float16 v = (_Float16)f;
+    uint16_t b;
+    __builtin_memcpy(&b, &v, 2);
+    return b;
+}
+
+// Bytes [s, s+4) of the 8-byte little-endian value hi:lo, s in {0, 2}.
+__device__ __forceinline__ uint32_t align_bytes(uint32_t hi, uint32_t lo, uint32_t s)
+{
+    return __builtin_amdgcn_alignbyte(hi, lo, s);
+}
+
+__device__ __forceinline__ int sdot4(uint32_t a, uint32_t b, int c)
+{
+    return __builtin_amdgcn_sdot4((int)a, (int)b, c, false);
+}
+
+}  // namespace bqm

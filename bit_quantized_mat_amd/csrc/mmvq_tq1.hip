@@ -1,0 +1,314 @@
+// mmvq_tq1.hip -- TQ1_0 x Q8_1 mat-vec and small-batch product on gfx950.
+//
+// Byte-major decode ("CUDA: TQ1_0 mat-vec is load-bound by the per-32-element
+// chunk contract", "Upstream state" and "Proposed approach"): each thread owns
+// whole 256-element blocks, loads every packed byte of a block once, expands
+// all of its base-3 digits in registers, and spends each digit against the
+// matching Q8_1 activation bytes. Digit u = trit + 1 is in {0,1,2}, so the
+// integer dot uses the unsigned digits and subtracts the activation block's
+// sum of q once: sum(t*q) = sum(u*q) - sum(q).
+//
+// Thread mapping: Lr lanes (a power of two, at most 64) share one output row;
+// lane i of a row takes blocks i, i+Lr, ... of that row. A wave thus covers a
+// contiguous run of 64 packed blocks per step, so its loads are coalesced.
+// The T activation columns reuse the decoded digits held in registers.
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace bqm {
+
+// Digits of the four bytes of w, one byte per digit slot:
+// out[c] holds digit c of byte k in its byte k.
+template <int NDIG>
+__device__ __forceinline__ void digits4(uint32_t w, uint32_t (&out)[NDIG])
+{
+    uint32_t b0 = w & 0xffu, b1 = (w >> 8) & 0xffu, b2 = (w >> 16) & 0xffu, b3 = w >> 24;
+#pragma unroll
+    for (int c = 0; c < NDIG; c++) {
+        const uint32_t q0 = b0 / 3u, q1 = b1 / 3u, q2 = b2 / 3u, q3 = b3 / 3u;
+        out[c] = (b0 - 3u * q0) | ((b1 - 3u * q1) << 8) | ((b2 - 3u * q2) << 16) |
+                 ((b3 - 3u * q3) << 24);
+        b0 = q0;
+        b1 = q1;
+        b2 = q2;
+        b3 = q3;
+    }
+}
+
+// A decoded TQ1_0 block: U[c][j] = digit c of qs dword j (j < 12);
+// H[c] = digit c of the qh dword; dw = fp32 scale.
+struct DecodedBlock {
+    uint32_t U[5][12];
+    uint32_t H[4];
+    float dw;
+};
+
+// Load the 54-byte block starting at byte offset off (even) and decode it.
+// Odd blocks of a row start 2 bytes past a dword boundary: the 14 aligned
+// dwords covering the block are realigned with alignbyte.
+__device__ __forceinline__ void load_decode_block(__amdgpu_buffer_rsrc_t rw, uint32_t off,
+                                                  DecodedBlock &blk)
+{
+    const uint32_t base = off & ~3u;
+    const uint32_t sh = off & 3u;
+    uint32_t r[14];
+#pragma unroll
+    for (int i = 0; i < 12; i += 4) {
+        u32x4 v = ld_b128(rw, base + 4 * i);
+        r[i] = v.x;
+        r[i + 1] = v.y;
+        r[i + 2] = v.z;
+        r[i + 3] = v.w;
+    }
+    u32x2 t = ld_b64(rw, base + 48);
+    r[12] = t.x;
+    r[13] = t.y;
+    uint32_t qs[12], qh, dh;
+#pragma unroll
+    for (int i = 0; i < 12; i++)
+        qs[i] = align_bytes(r[i + 1], r[i], sh);
+    qh = align_bytes(r[13], r[12], sh);
+    dh = sh ? (r[13] >> 16) : (r[13] & 0xffffu);
+#pragma unroll
+    for (int j = 0; j < 12; j++) {
+        uint32_t u[5];
+        digits4<5>(qs[j], u);
+#pragma unroll
+        for (int c = 0; c < 5; c++)
+            blk.U[c][j] = u[c];
+    }
+    digits4<4>(qh, blk.H);
+    blk.dw = f16_bits_to_f32(dh);
+}
+
+// Exact per-32 sums of one decoded block against activation column t:
+// isum[b] for the 8 Q8_1 sub-blocks, and the fp32 scales d_a[b].
+// Activation block (column t, sub-block j) starts at byte (t*nblk + j)*36.
+__device__ __forceinline__ void block_isums(const DecodedBlock &blk, __amdgpu_buffer_rsrc_t ra,
+                                            uint32_t aoff, int (&isum)[8], float (&da)[8])
+{
+#pragma unroll
+    for (int b = 0; b < 8; b++) {
+        uint32_t q[9];
+        const uint32_t o = aoff + b * kQ81BlockBytes;
+        u32x4 v0 = ld_b128(ra, o);
+        u32x4 v1 = ld_b128(ra, o + 16);
+        q[0] = v0.x; q[1] = v0.y; q[2] = v0.z; q[3] = v0.w;
+        q[4] = v1.x; q[5] = v1.y; q[6] = v1.z; q[7] = v1.w;
+        q[8] = ld_b32(ra, o + 32);
+        int s = 0, sq = 0;
+#pragma unroll
+        for (int j = 0; j < 8; j++)
+            sq = sdot4(0x01010101u, q[j], sq);
+        if (b < 5) {
+            // sub-blocks 0..4: digit b of qs[0..31]
+#pragma unroll
+            for (int j = 0; j < 8; j++)
+                s = sdot4(blk.U[b][j], q[j], s);
+        } else if (b < 7) {
+            // sub-block 5: digits 0, 1 of qs[32..47]; sub-block 6: digits 2, 3
+            const int c0 = 2 * (b - 5);
+#pragma unroll
+            for (int j = 0; j < 4; j++) {
+                s = sdot4(blk.U[c0][8 + j], q[j], s);
+                s = sdot4(blk.U[c0 + 1][8 + j], q[4 + j], s);
+            }
+        } else {
+            // sub-block 7: digit 4 of qs[32..47], then digits 0..3 of qh
+#pragma unroll
+            for (int j = 0; j < 4; j++) {
+                s = sdot4(blk.U[4][8 + j], q[j], s);
+                s = sdot4(blk.H[j], q[4 + j], s);
+            }
+        }
+        isum[b] = s - sq;
+        da[b] = f16_bits_to_f32(q[8] & 0xffffu);
+    }
+}
+
+// Fixed-order fp32 combination of a block's eight scaled sums.
+__device__ __forceinline__ float block_scaled_sum(const int (&isum)[8], const float (&da)[8])
+{
+    float p[8];
+#pragma unroll
+    for (int b = 0; b < 8; b++)
+        p[b] = da[b] * (float)isum[b];
+    return ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
+}
+
+// Work description for one output row group: where the weight rows start,
+// which activation columns, and where the outputs go.
+template <int TC, bool ISUMS>
+__device__ __forceinline__ void rows_product(const uint8_t *__restrict__ w, uint64_t w_bytes,
+                                             const uint8_t *__restrict__ a, uint64_t a_bytes,
+                                             int64_t row, bool row_ok, int nb, int sub, int Lr,
+                                             int T, int tcol0, float *__restrict__ y,
+                                             int64_t y_col_stride, int32_t *__restrict__ isums,
+                                             int64_t N)
+{
+    const __amdgpu_buffer_rsrc_t rw = make_rsrc(w, w_bytes);
+    const __amdgpu_buffer_rsrc_t ra = make_rsrc(a, a_bytes);
+    const int nblk = nb * 8;
+    float acc[TC];
+#pragma unroll
+    for (int t = 0; t < TC; t++)
+        acc[t] = 0.0f;
+    if (row_ok) {
+        for (int B = sub; B < nb; B += Lr) {
+            DecodedBlock blk;
+            load_decode_block(rw, (uint32_t)((row * nb + B) * kTq1BlockBytes), blk);
+#pragma unroll
+            for (int t = 0; t < TC; t++) {
+                if (t < T) {
+                    int isum[8];
+                    float da[8];
+                    const uint32_t aoff =
+                        (uint32_t)(((int64_t)(tcol0 + t) * nblk + 8 * B) * kQ81BlockBytes);
+                    block_isums(blk, ra, aoff, isum, da);
+                    if (ISUMS) {
+                        int32_t *dst = isums + ((int64_t)t * N + row) * nblk + 8 * B;
+#pragma unroll
+                        for (int b = 0; b < 8; b++)
+                            dst[b] = isum[b];
+                    } else {
+                        acc[t] = fmaf(blk.dw, block_scaled_sum(isum, da), acc[t]);
+                    }
+                }
+            }
+        }
+    }
+    if (!ISUMS) {
+        // butterfly over the Lr lanes of the row (all lanes of the wave take part)
+#pragma unroll
+        for (int t = 0; t < TC; t++) {
+            float v = acc[t];
+            for (int m = Lr >> 1; m >= 1; m >>= 1)
+                v += __shfl_xor(v, m, 64);
+            acc[t] = v;
+        }
+        if (row_ok && sub == 0) {
+#pragma unroll
+            for (int t = 0; t < TC; t++)
+                if (t < T)
+                    y[t * y_col_stride + row] = acc[t];
+        }
+    }
+}
+
+template <int TC, bool ISUMS>
+__global__ __launch_bounds__(256) void mmvq_tq1_kernel(const uint8_t *__restrict__ w,
+                                                       const uint8_t *__restrict__ a,
+                                                       float *__restrict__ y,
+                                                       int32_t *__restrict__ isums, int64_t N,
+                                                       int nb, int T, int lr_log2)
+{
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int Lr = 1 << lr_log2;
+    const int rows_per_wave = 64 >> lr_log2;
+    const int64_t row =
+        ((int64_t)blockIdx.x * 4 + wave) * rows_per_wave + (lane >> lr_log2);
+    const int sub = lane & (Lr - 1);
+    const uint64_t w_bytes = (uint64_t)N * nb * kTq1BlockBytes;
+    const uint64_t a_bytes = (uint64_t)T * nb * 8 * kQ81BlockBytes;
+    rows_product<TC, ISUMS>(w, w_bytes, a, a_bytes, row, row < N, nb, sub, Lr, T, 0, y, N,
+                            isums, N);
+}
+
+static int lanes_per_row_log2(int64_t nb)
+{
+    int l = 0;
+    while (l < 6 && (2ll << l) <= nb)
+        l++;
+    return l;
+}
+
+template <bool ISUMS>
+static int launch_mmvq_t(const void *w, const void *a, float *y, int32_t *isums, int64_t N,
+                         int64_t K, int32_t T, hipStream_t stream)
+{
+    const int nb = (int)(K / kTq1BlockElems);
+    const int lr = lanes_per_row_log2(nb);
+    const int64_t rows_per_wg = 4 * (64 >> lr);
+    const dim3 grid((unsigned)((N + rows_per_wg - 1) / rows_per_wg));
+    const uint8_t *wp = static_cast<const uint8_t *>(w);
+    const uint8_t *ap = static_cast<const uint8_t *>(a);
+#define BQM_LAUNCH(TC)                                                                       \
+    hipLaunchKernelGGL((mmvq_tq1_kernel<TC, ISUMS>), grid, dim3(256), 0, stream, wp, ap, y, \
+                       isums, N, nb, (int)T, lr)
+    if (T <= 1)
+        BQM_LAUNCH(1);
+    else if (T <= 2)
+        BQM_LAUNCH(2);
+    else if (T <= 4)
+        BQM_LAUNCH(4);
+    else if (T <= 8)
+        BQM_LAUNCH(8);
+    else if (T <= 16)
+        BQM_LAUNCH(16);
+    else
+        BQM_LAUNCH(32);
+#undef BQM_LAUNCH
+    return check_launch();
+}
+
+int launch_mmvq(const void *w, const void *a, float *y, int32_t *isums, int64_t N, int64_t K,
+                int32_t T, hipStream_t stream)
+{
+    if (isums)
+        return launch_mmvq_t<true>(w, a, nullptr, isums, N, K, T, stream);
+    return launch_mmvq_t<false>(w, a, y, nullptr, N, K, T, stream);
+}
+
+// ---------------------------------------------------------------------------
+// Expert-routed product: blockIdx.y enumerates the (token, slot) pairs; the
+// pair's expert matrix is multiplied by its token's activation column.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void mmvq_id_tq1_kernel(const uint8_t *__restrict__ w,
+                                                          const uint8_t *__restrict__ a,
+                                                          const int32_t *__restrict__ ids,
+                                                          float *__restrict__ y, int64_t E,
+                                                          int64_t N, int nb, int n_used,
+                                                          int lr_log2)
+{
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int Lr = 1 << lr_log2;
+    const int rows_per_wave = 64 >> lr_log2;
+    const int64_t row =
+        ((int64_t)blockIdx.x * 4 + wave) * rows_per_wave + (lane >> lr_log2);
+    const int sub = lane & (Lr - 1);
+    const int64_t pair = blockIdx.y;  // t * n_used + s
+    const int64_t t = pair / n_used;
+    int e = ids[pair];
+    e = e < 0 ? 0 : (e >= E ? (int)E - 1 : e);  // keep accesses inside w for bad ids
+    const uint64_t expert_bytes = (uint64_t)N * nb * kTq1BlockBytes;
+    const uint64_t col_bytes = (uint64_t)nb * 8 * kQ81BlockBytes;
+    rows_product<1, false>(w + e * expert_bytes, expert_bytes, a + t * col_bytes, col_bytes, row,
+                           row < N, nb, sub, Lr, 1, 0, y + pair * N, N, nullptr, N);
+}
+
+size_t mmvq_id_workspace_bytes(int64_t E, int64_t T, int32_t n_used)
+{
+    (void)E;
+    (void)T;
+    (void)n_used;
+    return 256;
+}
+
+int launch_mmvq_id(const void *w, const void *a, const int32_t *ids, float *y, int64_t E,
+                   int64_t N, int64_t K, int64_t T, int32_t n_used, void *workspace,
+                   hipStream_t stream)
+{
+    (void)workspace;
+    const int nb = (int)(K / kTq1BlockElems);
+    const int lr = lanes_per_row_log2(nb);
+    const int64_t rows_per_wg = 4 * (64 >> lr);
+    const dim3 grid((unsigned)((N + rows_per_wg - 1) / rows_per_wg), (unsigned)(T * n_used));
+    hipLaunchKernelGGL(mmvq_id_tq1_kernel, grid, dim3(256), 0, stream,
+                       static_cast<const uint8_t *>(w), static_cast<const uint8_t *>(a), ids, y,
+                       E, N, nb, (int)n_used, lr);
+    return check_launch();
+}
+
+}  // namespace bqm

@@ -1,0 +1,138 @@
+/*
+ * bqm.h -- C ABI of the MI355X (gfx950) TQ1_0 x Q8_1 quantized mat-vec library.
+ *
+ * The operation: ternary weights stored in the TQ1_0 block format (five
+ * base-3 trits per byte, 256-element blocks) multiplied against activations
+ * quantized to Q8_1 (32-element int8 blocks), one or a few activation columns
+ * at a time ("MMVQ"), plus the expert-routed variant used by mixture-of-experts
+ * layers. Sources, cited by page title and section:
+ *   - "CUDA: TQ1_0 mat-vec is load-bound by the per-32-element chunk
+ *     contract": "Current behavior" (block format, digit-strided chunks, the
+ *     Q8_1 activation blocks of the mat-vec path), "Proposed approach" (a
+ *     dedicated byte-major kernel that consumes whole 256-element blocks),
+ *     "Acceptance criteria" (plain and expert-routed mat-vec; experts at one
+ *     activation per token, more than one block per row, fewer experts used
+ *     than available).
+ *   - "cuda: opt-in MMVQ activation reuse across output rows": exact
+ *     multi-column mat-vec whose columns equal single-column calls.
+ *
+ * Formats (byte exact; every entry point reads or writes exactly these):
+ *   TQ1_0 block, 54 bytes: qs[48] at 0, qh[4] at 48, fp16 scale d at 52
+ *     (little endian). Byte value v = sum_c u_c * 3^c, digit u_c in {0,1,2},
+ *     trit = u_c - 1. Element e of the block lives in
+ *       e <  160: digit e/32         of qs[e % 32]
+ *       e <  240: digit (e-160)/16   of qs[32 + (e-160) % 16]
+ *       e >= 240: digit (e-240)/4    of qh[(e-240) % 4]
+ *     and has value fp32(d) * trit. A weight matrix [N][K] is N rows of K/256
+ *     blocks, rows contiguous: block (n, B) starts at byte (n*(K/256) + B)*54.
+ *   Q8_1 block, 36 bytes: int8 q[32] at 0, fp16 d at 32, fp16 s at 34. An
+ *     activation matrix [T][K] is T columns of K/32 blocks, columns contiguous.
+ *     Quantization of 32 floats x: amax = max|x|, d = amax/127 (fp32),
+ *     q = round-half-away(x * (1/d)) clamped to [-127, 127] (q = 0 if d = 0),
+ *     stored d16 = fp16(d), s16 = fp16(d * sum(q)); fp16 rounding is to
+ *     nearest even.
+ *
+ * Common contract:
+ *   - All buffer pointers are DEVICE pointers owned by the caller; the library
+ *     never allocates, frees or synchronizes, holds no mutable global state,
+ *     and enqueues work only on `stream` (a hipStream_t; NULL = the null
+ *     stream). Calls are asynchronous; outputs are fully overwritten.
+ *   - Inputs must not alias outputs.
+ *   - Arguments are validated on the host before anything is enqueued; on an
+ *     error nothing is enqueued and nothing is written.
+ *   - Return value: BQM_OK (0) or a negative BQM_ERR_* code.
+ *   - Contents the format rules out (trits outside {-1,0,1} given to tq1_pack,
+ *     packed bytes qs > 242 or qh > 80, expert ids outside [0, E)) are not
+ *     checked on the device; results for them are unspecified but every
+ *     memory access stays inside the buffers described by the sizes given.
+ */
+#ifndef BQM_H
+#define BQM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#if defined(__GNUC__) || defined(__clang__)
+#define BQM_API __attribute__((visibility("default")))
+#else
+#define BQM_API
+#endif
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+    BQM_OK = 0,
+    BQM_ERR_NULL = -1,       /* a required pointer is NULL                     */
+    BQM_ERR_SHAPE = -2,      /* a size is out of range (see each entry point)  */
+    BQM_ERR_ALIGN = -3,      /* a buffer base is not 4-byte aligned            */
+    BQM_ERR_WORKSPACE = -4,  /* workspace missing or too small                 */
+    BQM_ERR_LAUNCH = -5,     /* the HIP runtime reported a launch error        */
+    BQM_ERR_DEVICE = -6      /* the current device is not a gfx950 GPU         */
+};
+
+/* Largest number of activation columns mmvq_tq1_0 accepts. */
+#define BQM_MMVQ_MAX_COLS 32
+
+/* Pack ternary weights into TQ1_0 blocks.
+ *   trits [N][K] int8, values -1, 0, +1, row-major.
+ *   d     [N][K/256] fp16 bit patterns (uint16), the block scales.
+ *   w     [N][K/256] x 54 bytes, output.
+ * Shapes: N >= 1, K >= 256, K % 256 == 0. Alignment: none required. */
+BQM_API int tq1_pack(const int8_t *trits, const uint16_t *d, void *w,
+             int64_t N, int64_t K, void *stream);
+
+/* Quantize activations to Q8_1.
+ *   x [T][K] fp32, row-major (column t of the product is row t of x).
+ *   a [T][K/32] x 36 bytes, output.
+ * Shapes: T >= 1, K >= 32, K % 32 == 0. Alignment: x 4 bytes, a 4 bytes. */
+BQM_API int q8_1_quantize(const float *x, void *a, int64_t T, int64_t K, void *stream);
+
+/* Quantized mat-vec / small-batch product:
+ *   y[t][n] = sum_{j < K/32} fp32(d_w[n][j/8]) * fp32(d_a[t][j]) * isum[t][n][j]
+ *   isum[t][n][j] = sum_{i < 32} trit[n][32j+i] * q[t][32j+i]   (exact int32)
+ *   w [N][K/256] TQ1_0 blocks; a [T][K/32] Q8_1 blocks; y [T][N] fp32 output.
+ * Shapes: N >= 1, K >= 256, K % 256 == 0, 1 <= T <= BQM_MMVQ_MAX_COLS, and
+ * the weight matrix is below 4 GiB. Alignment: w, a, y 4 bytes. fp32 results
+ * differ from the exact sum by at most 1e-5 of sum |terms|; integer sums are
+ * exact. */
+BQM_API int mmvq_tq1_0(const void *w, const void *a, float *y,
+               int64_t N, int64_t K, int32_t T, void *stream);
+
+/* Expert-routed product (mixture of experts):
+ *   y[t][s][n] = mmvq(W[ids[t][s]], a[t])[n]   for t < T, s < n_used
+ *   w   [E][N][K/256] TQ1_0 blocks (expert-major, each expert an N x K matrix).
+ *   a   [T][K/32] Q8_1 blocks, one activation per token shared by its slots.
+ *   ids [T][n_used] int32 expert ids in [0, E) (a repeated id is computed twice).
+ *   y   [T][n_used][N] fp32 output.
+ *   workspace: device scratch of at least mmvq_id_tq1_0_workspace_bytes(E, T,
+ *   n_used) bytes, 256-byte aligned, owned by the caller; it may be reused
+ *   between calls that are ordered on one stream.
+ * Shapes: E >= 1, N >= 1, K >= 256, K % 256 == 0, T >= 1, 1 <= n_used <= E,
+ * T * n_used <= 65535; one expert's matrix is below 4 GiB.
+ * Alignment: w, a, y, ids 4 bytes; workspace 256 bytes. */
+BQM_API int mmvq_id_tq1_0(const void *w, const void *a, const int32_t *ids, float *y,
+                  int64_t E, int64_t N, int64_t K, int64_t T, int32_t n_used,
+                  void *workspace, size_t workspace_bytes, void *stream);
+
+/* Workspace size mmvq_id_tq1_0 needs for these sizes (0 on bad sizes). */
+BQM_API size_t mmvq_id_tq1_0_workspace_bytes(int64_t E, int64_t T, int32_t n_used);
+
+/* Test twin of mmvq_tq1_0: runs the same decode and integer inner loop and
+ * writes the exact per-32-element sums isum[t][n][j] (int32 [T][N][K/32])
+ * instead of the scaled outputs. Same shapes and alignment as mmvq_tq1_0. */
+BQM_API int mmvq_tq1_0_block_isums(const void *w, const void *a, int32_t *isums,
+                           int64_t N, int64_t K, int32_t T, void *stream);
+
+/* Human-readable text for a status code (static storage). */
+BQM_API const char *bqm_status_string(int status);
+
+/* Library version, as major * 10000 + minor * 100 + patch. */
+BQM_API int bqm_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BQM_H */

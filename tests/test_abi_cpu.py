@@ -1,0 +1,124 @@
+"""CPU checks of the C ABI: the library loads, exports every entry point that
+include/bqm.h declares, and rejects bad arguments on the host before any
+device work (no compute call is made without a GPU)."""
+import ctypes
+
+import os
+import re
+
+import pytest
+
+import bit_quantized_mat_amd as bqm
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared_functions():
+    text = open(os.path.join(ROOT, "include", "bqm.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    text = re.sub(r"#define BQM_API.*", "", text)
+    return sorted(set(re.findall(r"BQM_API\s+[\w\s\*]*?\b(\w+)\s*\(", text)))
+
+
+def test_header_declares_the_four_calls():
+    names = _declared_functions()
+    for n in ("tq1_pack", "q8_1_quantize", "mmvq_tq1_0", "mmvq_id_tq1_0",
+              "mmvq_id_tq1_0_workspace_bytes", "mmvq_tq1_0_block_isums",
+              "bqm_status_string", "bqm_version"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = bqm.library()
+    for name in _declared_functions():
+        assert hasattr(lib, name), name
+    assert lib.bqm_version() >= 100
+
+
+def test_status_strings():
+    lib = bqm.library()
+    for code in range(0, -7, -1):
+        assert lib.bqm_status_string(code) not in (b"", b"unknown status")
+    assert lib.bqm_status_string(-99) == b"unknown status"
+
+
+P = ctypes.c_void_p
+GOOD = P(0x10000)       # aligned, never dereferenced: validation fails first
+ODD = P(0x10002)
+
+
+@pytest.mark.parametrize("args,expect", [
+    # null pointers
+    ((None, GOOD, GOOD, 4, 256, None), -1),
+    ((GOOD, None, GOOD, 4, 256, None), -1),
+    ((GOOD, GOOD, None, 4, 256, None), -1),
+    # shapes
+    ((GOOD, GOOD, GOOD, 0, 256, None), -2),
+    ((GOOD, GOOD, GOOD, 4, 255, None), -2),
+    ((GOOD, GOOD, GOOD, 4, 384, None), -2),
+    ((GOOD, GOOD, GOOD, 4, 0, None), -2),
+    ((GOOD, GOOD, GOOD, 1 << 40, 1 << 20, None), -2),
+])
+def test_tq1_pack_rejects(args, expect):
+    assert bqm.library().tq1_pack(*args) == expect
+
+
+@pytest.mark.parametrize("args,expect", [
+    ((None, GOOD, 1, 32, None), -1),
+    ((GOOD, None, 1, 32, None), -1),
+    ((GOOD, GOOD, 0, 32, None), -2),
+    ((GOOD, GOOD, 1, 48, None), -2),
+    ((GOOD, GOOD, 1, 0, None), -2),
+    ((ODD, GOOD, 1, 32, None), -3),
+    ((GOOD, ODD, 1, 32, None), -3),
+])
+def test_q8_1_quantize_rejects(args, expect):
+    assert bqm.library().q8_1_quantize(*args) == expect
+
+
+@pytest.mark.parametrize("fn", ["mmvq_tq1_0", "mmvq_tq1_0_block_isums"])
+@pytest.mark.parametrize("args,expect", [
+    ((None, GOOD, GOOD, 8, 256, 1, None), -1),
+    ((GOOD, None, GOOD, 8, 256, 1, None), -1),
+    ((GOOD, GOOD, None, 8, 256, 1, None), -1),
+    ((GOOD, GOOD, GOOD, 0, 256, 1, None), -2),
+    ((GOOD, GOOD, GOOD, 8, 288, 1, None), -2),
+    ((GOOD, GOOD, GOOD, 8, 256, 0, None), -2),
+    ((GOOD, GOOD, GOOD, 8, 256, 33, None), -2),
+    ((GOOD, GOOD, GOOD, 8, 256, -1, None), -2),
+    ((ODD, GOOD, GOOD, 8, 256, 1, None), -3),
+    ((GOOD, ODD, GOOD, 8, 256, 1, None), -3),
+    ((GOOD, GOOD, ODD, 8, 256, 1, None), -3),
+])
+def test_mmvq_rejects(fn, args, expect):
+    assert getattr(bqm.library(), fn)(*args) == expect
+
+
+def test_mmvq_id_rejects():
+    lib = bqm.library()
+    ws = P(0x100000)
+    need = lib.mmvq_id_tq1_0_workspace_bytes(8, 4, 2)
+    assert need > 0
+    base = [GOOD, GOOD, GOOD, GOOD, 8, 16, 256, 4, 2, ws, need, None]
+
+    def call(**kw):
+        args = list(base)
+        names = ["w", "a", "ids", "y", "E", "N", "K", "T", "n_used", "ws", "wsb", "s"]
+        for k, v in kw.items():
+            args[names.index(k)] = v
+        return lib.mmvq_id_tq1_0(*args)
+
+    assert call(w=None) == -1 and call(ids=None) == -1 and call(y=None) == -1
+    assert call(E=0) == -2 and call(n_used=0) == -2 and call(n_used=9) == -2
+    assert call(T=0) == -2 and call(K=100) == -2 and call(N=0) == -2
+    assert call(ids=ODD) == -3 and call(a=ODD) == -3
+    assert call(ws=None) == -4 and call(wsb=need - 1) == -4
+    assert call(ws=P(0x100010)) == -3
+    assert lib.mmvq_id_tq1_0_workspace_bytes(0, 4, 2) == 0
+    assert lib.mmvq_id_tq1_0_workspace_bytes(8, 4, 9) == 0
+
+
+def test_binding_raises_without_gpu_tensors():
+    import torch
+    with pytest.raises(TypeError):
+        bqm.mmvq_tq1_0(torch.zeros(54, dtype=torch.uint8), torch.zeros(36, dtype=torch.uint8), 1, 256, 1)

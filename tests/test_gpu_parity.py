@@ -1,0 +1,283 @@
+"""GPU parity: the HIP path (through the C ABI binding) against the CPU oracle
+on the same seeded inputs.
+
+Bars: packed TQ1_0 bytes and Q8_1 bytes identical; per-32 integer sums
+identical (through the production inner loop's test twin); fp32 outputs
+within 1e-5 of sum |terms| of the exact fp64 result. Shapes span several
+tiles and ragged tails; full workload shapes are covered too.
+"""
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+from bit_quantized_mat_amd import synth
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+REL_TOL = 1e-5
+
+
+def _say(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+@pytest.fixture(scope="module")
+def bqm():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import bit_quantized_mat_amd as m
+    m.library()
+    return m
+
+
+def _dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def _host(t):
+    torch.cuda.synchronize()
+    return t.cpu().numpy()
+
+
+def _assert_close(y, y64, ab, what):
+    err = np.abs(y.astype(np.float64) - y64)
+    bound = REL_TOL * ab
+    bad = err > bound
+    zero = ab == 0
+    assert np.all(y[zero] == 0), what
+    if bad.any():
+        i = np.argwhere(bad)[0]
+        raise AssertionError("%s: %d outputs outside 1e-5*sum|terms|, first at %s: gpu %r exact %r "
+                             "bound %r" % (what, bad.sum(), tuple(i), y[tuple(i)], y64[tuple(i)],
+                                           bound[tuple(i)]))
+
+
+def _case(N, K, T, seed, p_zero=1 / 3, outliers=0.01, d_lo=0.01, d_hi=0.1):
+    rng = np.random.default_rng(seed)
+    trits = synth.ternary(rng, (N, K), p_zero)
+    d16 = synth.block_scales_f16(rng, (N, K // 256), d_lo, d_hi)
+    x = synth.activations(rng, T, K, outlier_frac=outliers)
+    return trits, d16, x
+
+
+# shapes: (N, K, T) spanning several row tiles, ragged row counts, odd block
+# counts (2-byte aligned blocks), one-block rows and wide rows
+SHAPES = [(256, 1024, 1), (1, 256, 1), (33, 256, 2), (67, 768, 3), (130, 2304, 5),
+          (515, 4096, 8), (96, 6144, 4), (40, 16384, 1), (17, 1280, 32), (300, 512, 16)]
+
+
+# ---------------------------------------------------------------------------
+# q8_1_quantize: every byte identical
+# ---------------------------------------------------------------------------
+
+def _q8_edge_activations():
+    rng = np.random.default_rng(77)
+    x = synth.activations(rng, 3, 1024, outlier_frac=0.02)
+    x[0, :32] = 0.0                                        # amax = 0
+    x[0, 32:64] = np.linspace(-127, 127, 32).astype(np.float32)
+    x[0, 64:72] = [127.0, 2.5, -2.5, 0.5, -0.5, 1.5, -126.5, 3.5]  # exact ties
+    x[0, 72:96] = 0.0
+    x[1, :32] = (rng.standard_normal(32) * 1e-6).astype(np.float32)  # subnormal fp16 d
+    x[1, 32:64] = (rng.standard_normal(32) * 1e-9).astype(np.float32)  # d rounds to 0 in fp16
+    x[1, 64:96] = 3000.0                                    # d * sum(q) overflows fp16 -> inf
+    x[2, :32] = -1.0
+    return x
+
+
+@pytest.mark.parametrize("name", ["edge", "tiny", "decode", "ffn", "moe64"])
+def test_q8_1_quantize_bit_exact(bqm, name):
+    if name == "edge":
+        x = _q8_edge_activations()
+    else:
+        wl = {"tiny": "tiny", "decode": "decode", "ffn": "ffn", "moe64": "moe"}[name]
+        wlo = synth.WORKLOADS[wl]
+        rng = np.random.default_rng(wlo.seeds[1])
+        x = synth.activations(rng, max(wlo.Ts), wlo.K, wlo.outlier_frac, wlo.outlier_scale)
+    _say("q8_1_quantize", name, x.shape)
+    got = _host(bqm.q8_1_quantize(_dev(x)))
+    ref = oracle.q8_1_quantize(x)
+    assert np.array_equal(got, ref)
+
+
+# ---------------------------------------------------------------------------
+# tq1_pack: every byte identical
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("N,K", [(1, 256), (3, 768), (256, 1024), (129, 4096), (64, 6144)])
+def test_tq1_pack_byte_exact(bqm, N, K):
+    trits, d16, _ = _case(N, K, 1, 1000 + N)
+    _say("tq1_pack", N, K)
+    got = _host(bqm.tq1_pack(_dev(trits), _dev(d16.view(np.int16))))
+    assert np.array_equal(got, oracle.tq1_pack(trits, d16))
+
+
+def test_tq1_pack_all_byte_values(bqm):
+    # every qs and qh byte value appears; packs match byte for byte
+    rng = np.random.default_rng(5)
+    wb = np.zeros((243, 54), dtype=np.uint8)
+    wb[:, :48] = (np.arange(243)[:, None] + np.arange(48)[None, :]) % 243
+    wb[:, 48:52] = (np.arange(243)[:, None] + np.arange(4)[None, :]) % 81
+    wb[:, 52:54] = rng.integers(0, 256, (243, 2))
+    trits, d16 = oracle.tq1_unpack(wb, 243, 256)
+    got = _host(bqm.tq1_pack(_dev(trits), _dev(d16.view(np.int16))))
+    assert np.array_equal(got, wb)
+
+
+# ---------------------------------------------------------------------------
+# mmvq: exact integer sums, fp32 within tolerance
+# ---------------------------------------------------------------------------
+
+def _prep(bqm, trits, d16, x):
+    w_ref = oracle.tq1_pack(trits, d16)
+    a_ref = oracle.q8_1_quantize(x)
+    w = bqm.tq1_pack(_dev(trits), _dev(d16.view(np.int16)))
+    a = bqm.q8_1_quantize(_dev(x))
+    assert np.array_equal(_host(w), w_ref)
+    assert np.array_equal(_host(a), a_ref)
+    return w, a, w_ref, a_ref
+
+
+@pytest.mark.parametrize("N,K,T", SHAPES)
+def test_block_isums_bit_exact(bqm, N, K, T):
+    trits, d16, x = _case(N, K, T, 2000 + N + T)
+    w, a, w_ref, a_ref = _prep(bqm, trits, d16, x)
+    _say("block_isums", N, K, T)
+    got = _host(bqm.mmvq_tq1_0_block_isums(w, a, N, K, T))
+    assert np.array_equal(got, oracle.block_isums(w_ref, a_ref, N, K, T))
+
+
+@pytest.mark.parametrize("N,K,T", SHAPES)
+def test_mmvq_within_tolerance(bqm, N, K, T):
+    trits, d16, x = _case(N, K, T, 3000 + N + T)
+    w, a, w_ref, a_ref = _prep(bqm, trits, d16, x)
+    _say("mmvq", N, K, T)
+    y = _host(bqm.mmvq_tq1_0(w, a, N, K, T))
+    _, y64, ab = oracle.mmvq(w_ref, a_ref, N, K, T)
+    _assert_close(y, y64, ab, "mmvq %dx%d T=%d" % (N, K, T))
+
+
+def test_mmvq_unit_scales_exact_integer_matvec(bqm):
+    """d_w = d_a = 1: the product is the integer mat-vec, exact in fp32."""
+    N, K, T = 200, 2304, 6
+    rng = np.random.default_rng(99)
+    trits = synth.ternary(rng, (N, K))
+    q = rng.integers(-127, 128, (T, K)).astype(np.int8)
+    ones_w = np.full((N, K // 256), 0x3C00, np.uint16)
+    a_np = synth.q8_1_blocks_from_fields(q, np.full((T, K // 32), 0x3C00, np.uint16),
+                                         np.zeros((T, K // 32), np.uint16))
+    w = bqm.tq1_pack(_dev(trits), _dev(ones_w.view(np.int16)))
+    y = _host(bqm.mmvq_tq1_0(w, _dev(a_np), N, K, T))
+    ref = (q.astype(np.int64) @ trits.astype(np.int64).T).astype(np.float32)
+    assert np.array_equal(y, ref)
+
+
+def test_mmvq_one_hot_element_map(bqm):
+    """A one-hot activation at element e reads back d_w * trit[n, e] for
+    every element position of the block: pins the kernel's decode against
+    the oracle's packing of the element map."""
+    N, K = 64, 256
+    rng = np.random.default_rng(123)
+    trits = synth.ternary(rng, (N, K))
+    d16 = synth.block_scales_f16(rng, (N, 1), 0.01, 0.1)
+    w = bqm.tq1_pack(_dev(trits), _dev(d16.view(np.int16)))
+    q = np.zeros((K, K), dtype=np.int8)
+    np.fill_diagonal(q, 1)
+    ones = np.full((K, K // 32), 0x3C00, np.uint16)
+    a = _dev(synth.q8_1_blocks_from_fields(q, ones, np.zeros_like(ones)))
+    dw = d16.view(np.float16).astype(np.float32)[:, 0]
+    for e0 in range(0, K, 32):
+        y = _host(bqm.mmvq_tq1_0(w, a[e0:e0 + 32].contiguous(), N, K, 32))
+        ref = (trits[:, e0:e0 + 32].astype(np.float32) * dw[:, None]).T
+        assert np.array_equal(y, ref), "elements %d..%d" % (e0, e0 + 31)
+
+
+def test_mmvq_columns_equal_single_column_calls(bqm):
+    N, K, T = 320, 6144, 8
+    trits, d16, x = _case(N, K, T, 4242)
+    w, a, _, _ = _prep(bqm, trits, d16, x)
+    yT = _host(bqm.mmvq_tq1_0(w, a, N, K, T))
+    iT = _host(bqm.mmvq_tq1_0_block_isums(w, a, N, K, T))
+    row = a.shape[1]
+    for t in range(T):
+        at = a[t:t + 1].contiguous()
+        assert np.array_equal(_host(bqm.mmvq_tq1_0_block_isums(w, at, N, K, 1))[0], iT[t])
+        assert np.array_equal(_host(bqm.mmvq_tq1_0(w, at, N, K, 1))[0], yT[t]), t
+    assert row == (K // 32) * 36
+
+
+def test_mmvq_deterministic(bqm):
+    N, K, T = 1024, 4096, 4
+    trits, d16, x = _case(N, K, T, 55)
+    w, a, _, _ = _prep(bqm, trits, d16, x)
+    first = _host(bqm.mmvq_tq1_0(w, a, N, K, T))
+    for _ in range(10):
+        assert np.array_equal(_host(bqm.mmvq_tq1_0(w, a, N, K, T)), first)
+
+
+# ---------------------------------------------------------------------------
+# Full workload shapes
+# ---------------------------------------------------------------------------
+
+def _workload_inputs(name):
+    wl = synth.WORKLOADS[name]
+    return wl, synth.make_inputs(wl)
+
+
+@pytest.mark.parametrize("name", ["tiny", "decode", "multicol", "ffn"])
+def test_workload_mmvq_parity(bqm, name):
+    wl, inp = _workload_inputs(name)
+    N, K = wl.N, wl.K
+    w, a_all, w_ref, a_ref_all = _prep(bqm, inp.trits, inp.d16, inp.x)
+    for T in wl.Ts:
+        _say("workload", name, N, K, T)
+        a = a_all[:T].contiguous()
+        y = _host(bqm.mmvq_tq1_0(w, a, N, K, T))
+        _, y64, ab = oracle.mmvq(w_ref, a_ref_all[:T], N, K, T)
+        _assert_close(y, y64, ab, "%s T=%d" % (name, T))
+        if T == max(wl.Ts):
+            s = _host(bqm.mmvq_tq1_0_block_isums(w, a, N, K, T))
+            assert np.array_equal(s, oracle.block_isums(w_ref, a_ref_all[:T], N, K, T))
+
+
+# ---------------------------------------------------------------------------
+# Expert-routed product
+# ---------------------------------------------------------------------------
+
+def test_mmvq_id_small_cases(bqm):
+    for (E, N, K, T, n_used, seed) in [(6, 40, 512, 5, 3, 1), (4, 1, 256, 1, 4, 2),
+                                       (9, 130, 2304, 17, 2, 3), (3, 64, 1024, 2, 1, 4)]:
+        rng = np.random.default_rng(seed)
+        trits = synth.ternary(rng, (E * N, K))
+        d16 = synth.block_scales_f16(rng, (E * N, K // 256), 0.01, 0.1)
+        x = synth.activations(rng, T, K)
+        ids = synth.zipf_routing(rng, T, E, n_used)
+        w, a, w_ref, a_ref = _prep(bqm, trits, d16, x)
+        _say("mmvq_id", E, N, K, T, n_used)
+        y = _host(bqm.mmvq_id_tq1_0(w, a, _dev(ids), E, N, K, T, n_used))
+        _, y64, ab = oracle.mmvq_id(w_ref, a_ref, ids, E, N, K, T, n_used)
+        _assert_close(y, y64, ab, "mmvq_id E=%d N=%d K=%d T=%d" % (E, N, K, T))
+        # invariant: each slot equals a plain mat-vec on the gathered expert
+        wr = w.view(E, N, -1)
+        for t in range(T):
+            for s in range(n_used):
+                y1 = _host(bqm.mmvq_tq1_0(wr[ids[t, s]].contiguous(), a[t:t + 1].contiguous(),
+                                          N, K, 1))
+                assert np.array_equal(y1[0], y[t, s])
+
+
+def test_workload_moe_parity(bqm):
+    wl, inp = _workload_inputs("moe")
+    E, N, K, n_used = wl.experts, wl.N, wl.K, wl.n_used
+    w, a_all, w_ref, a_ref_all = _prep(bqm, inp.trits, inp.d16, inp.x)
+    for T in wl.Ts:
+        _say("workload moe", T)
+        ids = inp.ids[:T]
+        y = _host(bqm.mmvq_id_tq1_0(w, a_all[:T].contiguous(), _dev(ids), E, N, K, T, n_used))
+        # oracle on a sample of tokens (rows of y are independent per token)
+        ts = sorted(set([0, T - 1, T // 2]))
+        for t in ts:
+            _, y64, ab = oracle.mmvq_id(w_ref, a_ref_all[t:t + 1], ids[t:t + 1], E, N, K, 1, n_used)
+            _assert_close(y[t:t + 1], y64, ab, "moe T=%d token %d" % (T, t))
