@@ -15,6 +15,10 @@ FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared", "-fvisibility=hidden",
     # no packed-fp32 instructions anywhere in device code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # every fp32 operation rounds once, as written; fused multiply-adds only
+    # where the source calls fmaf (HIP's default would also fuse a product
+    # with its fp16 conversion, rounding once instead of twice)
+    "-ffp-contract=off",
     "-Wall", "-Wno-unused-function",
 ]
 

@@ -55,9 +55,14 @@ __device__ __forceinline__ float f16_bits_to_f32(uint32_t h)
     return (float)v;
 }
 
-// fp32 -> fp16 bits, round to nearest even (the hardware conversion).
+// fp32 -> fp16 bits, round to nearest even (the hardware conversion). The
+// argument is first pinned in a register as an fp32 value: without that the
+// backend folds a product feeding this conversion into one mixed-precision
+// fma that rounds only once, straight to fp16, instead of to fp32 and then
+// to fp16.
 __device__ __forceinline__ uint32_t f32_to_f16_bits(float f)
 {
+    asm volatile("" : "+v"(f));
     _Float16 v = (_Float16)f;
     uint16_t b;
     __builtin_memcpy(&b, &v, 2);

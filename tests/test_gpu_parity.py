@@ -84,7 +84,28 @@ def _q8_edge_activations():
     x[1, 32:64] = (rng.standard_normal(32) * 1e-9).astype(np.float32)  # d rounds to 0 in fp16
     x[1, 64:96] = 3000.0                                    # d * sum(q) overflows fp16 -> inf
     x[2, :32] = -1.0
-    return x
+    return np.concatenate([x, _double_rounding_blocks(32)], axis=0)  # 32 blocks = 1024
+
+
+def _double_rounding_blocks(count):
+    """Activation blocks for which rounding d*sum(q) to fp32 and then to fp16
+    differs from rounding it once: the stored s must follow the two-step
+    rule, so a fused product-and-convert on the device shows up here."""
+    rng = np.random.default_rng(2024)
+    found = []
+    while len(found) < count:
+        xb = synth.activations(rng, 4096, 32)
+        amax = np.abs(xb).max(axis=1).astype(np.float32)
+        d = (amax / np.float32(127.0)).astype(np.float32)
+        inv = (np.float32(1.0) / d).astype(np.float32)
+        v = (xb * inv[:, None]).astype(np.float32).astype(np.float64)
+        q = np.where(v >= 0, np.floor(v + 0.5), -np.floor(-v + 0.5))
+        sq = q.sum(axis=1)
+        two_step = (d * sq.astype(np.float32)).astype(np.float32).astype(np.float16)
+        one_step = (d.astype(np.float64) * sq).astype(np.float16)
+        hit = np.nonzero(two_step.view(np.uint16) != one_step.view(np.uint16))[0]
+        found.extend(xb[i] for i in hit[:count - len(found)])
+    return np.stack(found).reshape(1, count * 32)
 
 
 @pytest.mark.parametrize("name", ["edge", "tiny", "decode", "ffn", "moe64"])
@@ -263,7 +284,8 @@ def test_mmvq_id_small_cases(bqm):
         wr = w.view(E, N, -1)
         for t in range(T):
             for s in range(n_used):
-                y1 = _host(bqm.mmvq_tq1_0(wr[ids[t, s]].contiguous(), a[t:t + 1].contiguous(),
+                # clone: a 54-byte expert slice can start 2 bytes off a dword
+                y1 = _host(bqm.mmvq_tq1_0(wr[ids[t, s]].clone(), a[t:t + 1].clone(),
                                           N, K, 1))
                 assert np.array_equal(y1[0], y[t, s])
 
