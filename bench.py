@@ -71,6 +71,15 @@ def traffic_from_counters(N, K, T):
     return c.get("hbm_bytes_per_launch")
 
 
+def lanes_per_row_log2(nb):
+    """Lanes per output row in the one-column kernel (largest power of two
+    dividing the row's block count, at most 64)."""
+    lr = 0
+    while lr < 6 and nb % (2 << lr) == 0:
+        lr += 1
+    return lr
+
+
 def cpu_baseline(inp, N, K, T, step_bytes, seconds):
     import oracle
     threads = max(1, min(16, os.cpu_count() or 1))
@@ -165,14 +174,21 @@ def main():
     # dominant kernel: per-launch HIP events on the launch stream
     stream = torch.cuda.current_stream(dev)
     M = args.kernel_launches
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(M)]
-    for i, (s, e) in enumerate(evs):
-        s.record(stream)
+
+    def per_launch_us(launch, count):
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(count)]
+        for i, (s, e) in enumerate(evs):
+            s.record(stream)
+            launch(i)
+            e.record(stream)
+        torch.cuda.synchronize()
+        return np.array([s.elapsed_time(e) * 1e3 for s, e in evs])
+
+    def mmvq_launch(i):
         bqm.mmvq_tq1_0(wrot[(7 * i) % R], a, N, K, T, out=y, stream=stream)
-        e.record(stream)
-    torch.cuda.synchronize()
-    durs_us = np.array([s.elapsed_time(e) * 1e3 for s, e in evs])
+
+    durs_us = per_launch_us(mmvq_launch, M)
     us_call = float(np.mean(durs_us))
     # back-to-back launches bracketed by one event pair (includes dispatch gaps)
     s0, e0 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -183,16 +199,28 @@ def main():
     torch.cuda.synchronize()
     us_b2b = s0.elapsed_time(e0) * 1e3 / M
 
-    # a plain device copy of the same number of weight bytes, for calibration
-    src, dst = wrot[0], torch.empty_like(wrot[0])
-    cs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(50)]
-    for i, (s, e) in enumerate(cs):
-        s.record(stream)
-        dst.copy_(wrot[(13 * i + 1) % R])
-        e.record(stream)
-    torch.cuda.synchronize()
-    us_copy = float(np.mean([s.elapsed_time(e) * 1e3 for s, e in cs]))
+    # calibration: an empty dispatch, and a streaming read of the same weight
+    # bytes with the mat-vec's grid and with a wider grid
+    import ctypes
+    probes = ctypes.CDLL(os.path.join(ROOT, "bit_quantized_mat_amd", "libbqm_probes.so"))
+    probes.bqm_probe_empty.argtypes = [ctypes.c_int, ctypes.c_void_p]
+    probes.bqm_probe_read.argtypes = [ctypes.c_void_p, ctypes.c_uint64, ctypes.c_void_p,
+                                      ctypes.c_int, ctypes.c_void_p]
+    sptr = ctypes.c_void_p(stream.cuda_stream)
+    pout = torch.empty(4096, dtype=torch.int32, device=dev)
+    mm_grid = int(np.ceil(N / (4 * (64 >> lanes_per_row_log2(K // 256)))))
+    rd_bytes = wbytes - wbytes % 16
+    cal = {"empty_kernel_us": float(np.mean(per_launch_us(
+        lambda i: probes.bqm_probe_empty(mm_grid, sptr), 200)))}
+    for g in (mm_grid, 1024):
+        d = per_launch_us(lambda i: probes.bqm_probe_read(
+            ctypes.c_void_p(wrot[(13 * i + 1) % R].data_ptr()), rd_bytes,
+            ctypes.c_void_p(pout.data_ptr()), g, sptr), 200)
+        cal["read_%d_wg_us" % g] = float(np.mean(d))
+        cal["read_%d_wg_gbs" % g] = round(rd_bytes / float(np.mean(d)) / 1e3, 1)
+    cal["read_bytes"] = int(rd_bytes)
+    cal["mmvq_grid_wg"] = mm_grid
+    log("calibration:", cal)
 
     mm_bytes = algorithmic_bytes(N, K, T)
     step_bytes = mm_bytes + quantize_bytes(T, K)
@@ -203,8 +231,7 @@ def main():
         "%.3f us back-to-back; %.1f GB/s = %.1f%% of %.0f GB/s"
         % (us_call, np.median(durs_us), np.percentile(durs_us, 10), np.percentile(durs_us, 90),
            us_b2b, achieved, 100 * achieved / HBM_PEAK_GBS, HBM_PEAK_GBS))
-    log("step: %.3f us graph-replayed, %.3f us eager; copy of %d B: %.3f us (%.1f GB/s r+w)"
-        % (ms_per_step * 1e3, eager_ms * 1e3, wbytes, us_copy, 2 * wbytes / us_copy / 1e3))
+    log("step: %.3f us graph-replayed, %.3f us eager" % (ms_per_step * 1e3, eager_ms * 1e3))
 
     base = None
     if not args.no_cpu_baseline:
@@ -235,7 +262,7 @@ def main():
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic, "kernel": "mmvq_tq1_0",
                      "algorithmic_bytes_per_launch": mm_bytes},
-        "calibration": {"torch_copy_us": round(us_copy, 4), "copy_bytes_each_way": wbytes},
+        "calibration": {k: (round(v, 4) if isinstance(v, float) else v) for k, v in cal.items()},
         "cpu_baseline": base,
     }
     print(json.dumps(line), flush=True)

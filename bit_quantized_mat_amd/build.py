@@ -9,6 +9,9 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libbqm.so")
+# calibration kernels used only by bench.py (empty dispatch, streaming read)
+PROBE_SRC = os.path.join(HERE, "probes", "probes.hip")
+PROBE_LIB = os.path.join(HERE, "libbqm_probes.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [
@@ -27,14 +30,20 @@ def sources():
     return sorted(glob.glob(os.path.join(CSRC, "*.hip")))
 
 
-def build(verbose: bool = False) -> str:
-    """Compile the library (always recompiles); returns the .so path."""
-    tmp = LIB + ".tmp%d" % os.getpid()
-    cmd = [HIPCC, *FLAGS, "-I", os.path.join(HERE, "..", "include"), *sources(), "-o", tmp]
+def _compile(srcs, out, verbose):
+    tmp = out + ".tmp%d" % os.getpid()
+    cmd = [HIPCC, *FLAGS, "-I", os.path.join(HERE, "..", "include"), *srcs, "-o", tmp]
     if verbose:
         print(" ".join(cmd), file=sys.stderr)
     subprocess.run(cmd, check=True)
-    os.replace(tmp, LIB)
+    os.replace(tmp, out)
+
+
+def build(verbose: bool = False) -> str:
+    """Compile the library and the benchmark's probe library (always
+    recompiles); returns the library path."""
+    _compile(sources(), LIB, verbose)
+    _compile([PROBE_SRC], PROBE_LIB, verbose)
     return LIB
 
 

@@ -18,6 +18,11 @@ inline int check_launch()
 int launch_q8_1_quantize(const float *x, void *a, int64_t T, int64_t K, hipStream_t stream);
 int launch_tq1_pack(const int8_t *trits, const uint16_t *d, void *w, int64_t N, int64_t K,
                     hipStream_t stream);
+// Largest power of two (at most 64) dividing a row's block count: the number
+// of lanes that share one output row in the mat-vec kernels.
+int lanes_per_row_log2(int64_t nb);
+int launch_mmvq_t1(const void *w, const void *a, float *y, int32_t *isums, int64_t N,
+                   int64_t K, hipStream_t stream);
 int launch_mmvq(const void *w, const void *a, float *y, int32_t *isums, int64_t N, int64_t K,
                 int32_t T, hipStream_t stream);
 int launch_mmvq_id(const void *w, const void *a, const int32_t *ids, float *y, int64_t E,

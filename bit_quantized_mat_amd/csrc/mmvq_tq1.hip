@@ -12,8 +12,8 @@
 // lane i of a row takes blocks i, i+Lr, ... of that row. A wave thus covers a
 // contiguous run of 64 packed blocks per step, so its loads are coalesced.
 // The T activation columns reuse the decoded digits held in registers.
-#include "common.hpp"
 #include "launch.hpp"
+#include "tq1_decode.hpp"
 
 namespace bqm {
 
@@ -126,16 +126,6 @@ __device__ __forceinline__ void block_isums(const DecodedBlock &blk, __amdgpu_bu
     }
 }
 
-// Fixed-order fp32 combination of a block's eight scaled sums.
-__device__ __forceinline__ float block_scaled_sum(const int (&isum)[8], const float (&da)[8])
-{
-    float p[8];
-#pragma unroll
-    for (int b = 0; b < 8; b++)
-        p[b] = da[b] * (float)isum[b];
-    return ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
-}
-
 // Work description for one output row group: where the weight rows start,
 // which activation columns, and where the outputs go.
 template <int TC, bool ISUMS>
@@ -171,7 +161,7 @@ __device__ __forceinline__ void rows_product(const uint8_t *__restrict__ w, uint
                         for (int b = 0; b < 8; b++)
                             dst[b] = isum[b];
                     } else {
-                        acc[t] = fmaf(blk.dw, block_scaled_sum(isum, da), acc[t]);
+                        acc[t] = fmaf(blk.dw, block_dot_f32(isum, da), acc[t]);
                     }
                 }
             }
@@ -215,14 +205,6 @@ __global__ __launch_bounds__(256) void mmvq_tq1_kernel(const uint8_t *__restrict
                             isums, N);
 }
 
-static int lanes_per_row_log2(int64_t nb)
-{
-    int l = 0;
-    while (l < 6 && (2ll << l) <= nb)
-        l++;
-    return l;
-}
-
 template <bool ISUMS>
 static int launch_mmvq_t(const void *w, const void *a, float *y, int32_t *isums, int64_t N,
                          int64_t K, int32_t T, hipStream_t stream)
@@ -255,6 +237,8 @@ static int launch_mmvq_t(const void *w, const void *a, float *y, int32_t *isums,
 int launch_mmvq(const void *w, const void *a, float *y, int32_t *isums, int64_t N, int64_t K,
                 int32_t T, hipStream_t stream)
 {
+    if (T == 1)
+        return launch_mmvq_t1(w, a, y, isums, N, K, stream);
     if (isums)
         return launch_mmvq_t<true>(w, a, nullptr, isums, N, K, T, stream);
     return launch_mmvq_t<false>(w, a, y, nullptr, N, K, T, stream);

@@ -1,0 +1,90 @@
+"""CPU check of the integer arithmetic the gfx950 kernels use to expand
+base-3 digits (bit_quantized_mat_amd/csrc/tq1_decode.hpp): the multiply-shift
+constants are read from the header and the two-bytes-per-register lane
+arithmetic is emulated for every qs byte (0..242) and qh byte (0..80), against
+Python's own integer division."""
+import os
+import re
+
+import numpy as np
+
+HDR = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
+                   "bit_quantized_mat_amd", "csrc", "tq1_decode.hpp")
+
+
+def _constants():
+    text = open(HDR).read()
+    def get(name):
+        m = re.search(r"\b%s\s*=\s*(\d+)u(?:\s*\*\s*0x00010001u)?" % name, text)
+        assert m, name
+        return int(m.group(1))
+    return {k: get(k) for k in ("kQsMul", "kQsAdd", "kQsShift", "kQhMul", "kQhAdd", "kQhShift")}
+
+
+C = _constants()
+M16 = 0xFFFF
+
+
+def _lane_chain(v, mul, add, shift, mults):
+    """Emulate one 16-bit lane: X1 = (mul*v + add) >> shift, then X1 * m."""
+    x1 = (mul * v + add) & M16
+    assert mul * v + add <= M16, "lane overflow in the first product"
+    x1 >>= shift
+    xs = [x1]
+    for m in mults:
+        assert x1 * m <= M16, "lane overflow"
+        xs.append((x1 * m) & M16)
+    return xs
+
+
+def test_qs_digit_chain_exhaustive():
+    for v in range(243):
+        x1, x2, x3, x4 = _lane_chain(v, C["kQsMul"], C["kQsAdd"], C["kQsShift"], (3, 9, 27))
+        x5 = 3 * (x4 & 0xFF)
+        floors = [(x >> 8) & 0xFF for x in (x1, x2, x3, x4)]
+        assert floors == [v // 81, v // 27, v // 9, v // 3], v
+        assert (x5 >> 8) & 0xFF == v % 3, v
+        # the unsigned digits recovered as F_m - 3 F_(m+1) match base 3
+        f = [v // 3 ** m for m in range(6)]
+        digits = [f[m] - 3 * f[m + 1] for m in range(5)]
+        assert int("".join(str(d) for d in reversed(digits)), 3) == v
+
+
+def test_qh_digit_chain_exhaustive():
+    for v in range(81):
+        x1, x2, x3 = _lane_chain(v, C["kQhMul"], C["kQhAdd"], C["kQhShift"], (3, 9))
+        x4 = 3 * (x3 & 0xFF)
+        floors = [(x >> 8) & 0xFF for x in (x1, x2, x3)]
+        assert floors == [v // 27, v // 9, v // 3], v
+        assert (x4 >> 8) & 0xFF == v % 3, v
+
+
+def test_two_lanes_share_a_register_without_crosstalk():
+    # the first step is one 24-bit multiply-add on bytes 0 and 2 of a dword
+    rng = np.random.default_rng(0)
+    for _ in range(2000):
+        b0, b2 = (int(t) for t in rng.integers(0, 243, 2))
+        e = b0 | (b2 << 16)
+        r = (e * C["kQsMul"] + C["kQsAdd"] * 0x00010001) & 0xFFFFFFFF
+        assert e < (1 << 24)
+        assert r & M16 == C["kQsMul"] * b0 + C["kQsAdd"]
+        assert r >> 16 == C["kQsMul"] * b2 + C["kQsAdd"]
+
+
+def _perm(s0, s1, sel):
+    """v_perm_b32: selector bytes 0-3 pick bytes of s1, 4-7 bytes of s0, 12 -> 0."""
+    src = [(s1 >> (8 * i)) & 0xFF for i in range(4)] + [(s0 >> (8 * i)) & 0xFF for i in range(4)]
+    out = 0
+    for i in range(4):
+        s = (sel >> (8 * i)) & 0xFF
+        b = src[s] if s < 8 else (0 if s == 12 else 0xFF)
+        out |= b << (8 * i)
+    return out
+
+
+def test_byte_split_and_merge_selectors():
+    w = 0x44332211
+    assert w & 0x00FF00FF == 0x00330011
+    assert _perm(0, w, 0x0C030C01) == 0x00440022          # bytes 1, 3 into lanes
+    e, o = 0xAA01BB02, 0xCC03DD04                          # byte 1/3 of each lane
+    assert _perm(o, e, 0x07030501) == 0xCCAADDBB          # [e.b1, o.b1, e.b3, o.b3]
