@@ -166,13 +166,17 @@ def mmvq_id_tq1_0(w, a, ids, E, N, K, T, n_used, out=None, workspace=None, strea
     if out is None:
         out = torch.empty((T, n_used, N), dtype=torch.float32, device=w.device)
     need = mmvq_id_tq1_0_workspace_bytes(E, T, n_used)
-    if workspace is None:
-        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=w.device)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=w.device)
     pw = _dev_tensor(w, "w", (torch.uint8,), E * N * (K // 256) * TQ1_BLOCK_BYTES)
     pa = _dev_tensor(a, "a", (torch.uint8,), T * (K // 32) * Q81_BLOCK_BYTES, w.device)
     pi = _dev_tensor(ids, "ids", (torch.int32,), T * n_used * 4, w.device)
     py = _dev_tensor(out, "out", (torch.float32,), T * n_used * N * 4, w.device)
-    pws = _dev_tensor(workspace, "workspace", (torch.uint8,), need, w.device)
-    _call("mmvq_id_tq1_0", pw, pa, pi, py, E, N, K, T, n_used, pws,
-          workspace.numel(), _stream(stream, w.device))
+    if workspace is None:
+        pws, nws = ctypes.c_void_p(None), 0
+    else:
+        pws = _dev_tensor(workspace, "workspace", (torch.uint8,), need, w.device)
+        nws = workspace.numel()
+    _call("mmvq_id_tq1_0", pw, pa, pi, py, E, N, K, T, n_used, pws, nws,
+          _stream(stream, w.device))
     return out

@@ -122,9 +122,9 @@ int mmvq_id_tq1_0(const void *w, const void *a, const int32_t *ids, float *y, in
     if (!aligned4(w) || !aligned4(a) || !aligned4(ids) || !aligned4(y))
         return BQM_ERR_ALIGN;
     const size_t need = bqm::mmvq_id_workspace_bytes(E, T, n_used);
-    if (!workspace || workspace_bytes < need)
+    if (need > 0 && (!workspace || workspace_bytes < need))
         return BQM_ERR_WORKSPACE;
-    if (((uintptr_t)workspace & 255u) != 0)
+    if (workspace && ((uintptr_t)workspace & 255u) != 0)
         return BQM_ERR_ALIGN;
     if (int rc = check_device())
         return rc;

@@ -21,13 +21,18 @@ int launch_tq1_pack(const int8_t *trits, const uint16_t *d, void *w, int64_t N, 
 // Largest power of two (at most 64) dividing a row's block count: the number
 // of lanes that share one output row in the mat-vec kernels.
 int lanes_per_row_log2(int64_t nb);
-int launch_mmvq_t1(const void *w, const void *a, float *y, int32_t *isums, int64_t N,
-                   int64_t K, hipStream_t stream);
+// Staged kernel (one to eight columns, activations staged in LDS): whether it
+// takes this shape, and its launcher.
+bool staged_supported(int64_t K, int32_t T);
+int launch_mmvq_staged(const void *w, const void *a, float *y, int32_t *isums, int64_t N,
+                       int64_t K, int32_t T, hipStream_t stream);
 int launch_mmvq(const void *w, const void *a, float *y, int32_t *isums, int64_t N, int64_t K,
                 int32_t T, hipStream_t stream);
 int launch_mmvq_id(const void *w, const void *a, const int32_t *ids, float *y, int64_t E,
                    int64_t N, int64_t K, int64_t T, int32_t n_used, void *workspace,
                    hipStream_t stream);
 size_t mmvq_id_workspace_bytes(int64_t E, int64_t T, int32_t n_used);
+int launch_mmvq_id_pairs(const void *w, const void *a, const int32_t *ids, float *y, int64_t E,
+                         int64_t N, int64_t K, int64_t T, int32_t n_used, hipStream_t stream);
 
 }  // namespace bqm

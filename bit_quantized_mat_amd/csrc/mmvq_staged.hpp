@@ -1,0 +1,237 @@
+// mmvq_staged.hpp -- device building blocks of the staged TQ1_0 x Q8_1 kernels
+// (activations staged in LDS, byte-major weight decode), shared by the plain
+// and the expert-routed products.
+#pragma once
+
+#include "launch.hpp"
+#include "tq1_decode.hpp"
+
+namespace bqm {
+
+
+// Staged layout of one 256-element block of activations, in dwords:
+//   [8j + c]   dword j of sub-block c's q bytes     (j, c < 8)
+//   [64 + c]   fp32 scale of sub-block c
+//   [72 + c]   -sum(q) of sub-block c
+//   [80..83]   padding (keeps the per-block stride at 16-byte alignment and
+//              spreads the blocks of a wave over distinct LDS banks)
+constexpr int kActStride = 84;
+constexpr int kMaxChunkBlocks = 128;
+constexpr int kStagedMaxCols = 8;
+
+__device__ __forceinline__ void stage_activations(uint32_t *__restrict__ act,
+                                                  __amdgpu_buffer_rsrc_t ra, uint32_t col_off,
+                                                  int B0, int cb, int tid, int nthreads)
+{
+    for (int i = tid; i < cb * 8; i += nthreads) {
+        const int bi = i >> 3, c = i & 7;
+        const uint32_t off = col_off + (uint32_t)((B0 + bi) * 8 + c) * kQ81BlockBytes;
+        const u32x4 v0 = ld_b128(ra, off);
+        const u32x4 v1 = ld_b128(ra, off + 16);
+        const uint32_t ds = ld_b32(ra, off + 32);
+        uint32_t *dst = act + bi * kActStride;
+        const uint32_t q[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+        int sq = 0;
+#pragma unroll
+        for (int j = 0; j < 8; j++) {
+            dst[8 * j + c] = q[j];
+            sq = sdot4(0x01010101u, q[j], sq);
+        }
+        dst[64 + c] = __float_as_uint(f16_bits_to_f32(ds & 0xffffu));
+        dst[72 + c] = (uint32_t)(-sq);
+    }
+}
+
+// Integer sums of one block (raw weights) against one staged activation column,
+// with the floor-pair products (cheapest when a decoded block meets one column).
+__device__ __forceinline__ void block_sums_staged(const RawBlock &raw,
+                                                  const uint32_t *__restrict__ ab, int (&isum)[8])
+{
+    BlockSums s;
+#pragma unroll
+    for (int c = 0; c < 8; c++) {
+        s.P[c] = (int)ab[72 + c];
+        s.N[c] = 0;
+    }
+    uint32_t q[8][8];
+#pragma unroll
+    for (int j = 0; j < 8; j++) {
+        const uint4 lo = *reinterpret_cast<const uint4 *>(ab + 8 * j);
+        const uint4 hi = *reinterpret_cast<const uint4 *>(ab + 8 * j + 4);
+        q[j][0] = lo.x; q[j][1] = lo.y; q[j][2] = lo.z; q[j][3] = lo.w;
+        q[j][4] = hi.x; q[j][5] = hi.y; q[j][6] = hi.z; q[j][7] = hi.w;
+    }
+#pragma unroll
+    for (int j = 0; j < 8; j++)
+        dot_qs_lo(raw_dword(raw, j), q[j][0], q[j][1], q[j][2], q[j][3], q[j][4], s);
+#pragma unroll
+    for (int i = 0; i < 4; i++)
+        dot_qs_hi(raw_dword(raw, 8 + i), q[i][5], q[4 + i][5], q[i][6], q[4 + i][6], q[i][7], s);
+    dot_qh(raw_dword(raw, 12), q[4][7], q[5][7], q[6][7], q[7][7], s);
+    finish_isums(s, isum);
+}
+
+// A block expanded to clean digits, for reuse across several columns.
+struct DigitBlock {
+    uint32_t lo[8][5];   // qs dword j < 8, digit c
+    uint32_t hi[4][5];   // qs dword 8 + i, digit c
+    uint32_t qh[4];      // qh dword, digit c
+};
+
+__device__ __forceinline__ void expand_block(const RawBlock &raw, DigitBlock &d)
+{
+#pragma unroll
+    for (int j = 0; j < 8; j++) {
+        const QsDigits u = qs_digits(raw_dword(raw, j));
+#pragma unroll
+        for (int c = 0; c < 5; c++)
+            d.lo[j][c] = u.U[c];
+    }
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+        const QsDigits u = qs_digits(raw_dword(raw, 8 + i));
+#pragma unroll
+        for (int c = 0; c < 5; c++)
+            d.hi[i][c] = u.U[c];
+    }
+    const QhDigits h = qh_digits(raw_dword(raw, 12));
+#pragma unroll
+    for (int c = 0; c < 4; c++)
+        d.qh[c] = h.U[c];
+}
+
+// Integer sums of an expanded block against one staged activation column.
+// Element map (see include/bqm.h): digit c of qs dword j < 8 is dword j of
+// sub-block c; digits 0..4 of qs dword 8+i are dwords i, 4+i of sub-block 5,
+// i, 4+i of sub-block 6 and i of sub-block 7; digit c of qh is dword 4+c of
+// sub-block 7.
+__device__ __forceinline__ void digit_sums_staged(const DigitBlock &d,
+                                                  const uint32_t *__restrict__ ab, int (&isum)[8])
+{
+#pragma unroll
+    for (int c = 0; c < 8; c++)
+        isum[c] = (int)ab[72 + c];
+#pragma unroll
+    for (int j = 0; j < 8; j++) {
+        const uint4 lo = *reinterpret_cast<const uint4 *>(ab + 8 * j);
+        const uint32_t q4 = ab[8 * j + 4];
+        isum[0] = sdot4(d.lo[j][0], lo.x, isum[0]);
+        isum[1] = sdot4(d.lo[j][1], lo.y, isum[1]);
+        isum[2] = sdot4(d.lo[j][2], lo.z, isum[2]);
+        isum[3] = sdot4(d.lo[j][3], lo.w, isum[3]);
+        isum[4] = sdot4(d.lo[j][4], q4, isum[4]);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+        const uint4 a = *reinterpret_cast<const uint4 *>(ab + 8 * i + 4);        // sb 4..7, dword i
+        const uint4 b = *reinterpret_cast<const uint4 *>(ab + 8 * (4 + i) + 4);  // sb 4..7, dword 4+i
+        isum[5] = sdot4(d.hi[i][0], a.y, isum[5]);
+        isum[5] = sdot4(d.hi[i][1], b.y, isum[5]);
+        isum[6] = sdot4(d.hi[i][2], a.z, isum[6]);
+        isum[6] = sdot4(d.hi[i][3], b.z, isum[6]);
+        isum[7] = sdot4(d.hi[i][4], a.w, isum[7]);
+        isum[7] = sdot4(d.qh[i], b.w, isum[7]);
+    }
+}
+
+// The rows of one workgroup against T <= TC activation columns. Column t's
+// Q8_1 row starts at byte col_off[t] of the activation buffer ra and its
+// outputs go to out[t][row]. All 256 threads of the workgroup must call this
+// (it synchronizes); lanes whose row is out of range only help with staging.
+template <int TC, bool ISUMS>
+__device__ __forceinline__ void staged_rows(__amdgpu_buffer_rsrc_t rw, __amdgpu_buffer_rsrc_t ra,
+                                            const uint32_t (&col_off)[TC],
+                                            float *const (&out)[TC], int32_t *__restrict__ isums,
+                                            uint32_t *__restrict__ act, int64_t row, bool row_ok,
+                                            int64_t N, int nb, int T, int lr_log2, int chunk)
+{
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int Lr = 1 << lr_log2;
+    const int sub = lane & (Lr - 1);
+    const int nblk = nb * 8;
+    const uint32_t row_off = (uint32_t)((row_ok ? row : 0) * nb * kTq1BlockBytes);
+    float acc[TC];
+#pragma unroll
+    for (int t = 0; t < TC; t++)
+        acc[t] = 0.0f;
+
+    for (int B0 = 0; B0 < nb; B0 += chunk) {
+        const int end = min(B0 + chunk, nb);
+        const int cb = end - B0;
+        const int first = B0 + sub;
+        // issue this lane's first weight block before staging, so the HBM
+        // latency overlaps the activation copy; later blocks of the chunk are
+        // loaded into the same registers at the top of their iteration
+        RawBlock cur;
+        if (row_ok && first < end)
+            cur = load_raw_block(rw, row_off + (uint32_t)first * kTq1BlockBytes);
+        __syncthreads();  // readers of the previous chunk are done
+#pragma unroll
+        for (int t = 0; t < TC; t++)
+            if (t < T)
+                stage_activations(act + t * cb * kActStride, ra, col_off[t], B0, cb, tid, 256);
+        __syncthreads();
+        if (row_ok) {
+            for (int B = first; B < end; B += Lr) {
+                if (B != first)
+                    cur = load_raw_block(rw, row_off + (uint32_t)B * kTq1BlockBytes);
+                const float dw = f16_bits_to_f32(raw_scale_bits(cur));
+                DigitBlock d;
+                if (TC > 1)
+                    expand_block(cur, d);
+#pragma unroll
+                for (int t = 0; t < TC; t++) {
+                    if (t < T) {
+                        const uint32_t *ab = act + (t * cb + (B - B0)) * kActStride;
+                        int isum[8];
+                        if (TC == 1)
+                            block_sums_staged(cur, ab, isum);
+                        else
+                            digit_sums_staged(d, ab, isum);
+                        if (ISUMS) {
+                            int32_t *dst = isums + ((int64_t)t * N + row) * nblk + 8 * B;
+#pragma unroll
+                            for (int b = 0; b < 8; b++)
+                                dst[b] = isum[b];
+                        } else {
+                            float da[8];
+#pragma unroll
+                            for (int b = 0; b < 8; b++)
+                                da[b] = __uint_as_float(ab[64 + b]);
+                            acc[t] = fmaf(dw, block_dot_f32(isum, da), acc[t]);
+                        }
+                    }
+                }
+            }
+        }
+    }
+    if (!ISUMS) {
+        // butterfly over the Lr lanes of the row (every lane of the wave takes part)
+#pragma unroll
+        for (int t = 0; t < TC; t++)
+            for (int m = Lr >> 1; m >= 1; m >>= 1)
+                acc[t] += __shfl_xor(acc[t], m, 64);
+        if (row_ok && sub == 0) {
+#pragma unroll
+            for (int t = 0; t < TC; t++)
+                if (t < T)
+                    out[t][row] = acc[t];
+        }
+    }
+}
+
+// Largest chunk (a multiple of the lanes per row, at most 128 blocks) whose
+// staged activations for T columns fit lds_budget bytes; 0 if none does. The
+// budget stays within the 64 KiB of dynamic LDS a launch gets by default.
+constexpr size_t kLdsBudget = 64 * 1024;
+
+inline int staged_chunk(int nb, int lr, int T, size_t lds_budget = kLdsBudget)
+{
+    const int Lr = 1 << lr;
+    int chunk = nb < kMaxChunkBlocks ? nb : kMaxChunkBlocks;
+    while (chunk >= Lr && (size_t)T * chunk * kActStride * 4 > lds_budget)
+        chunk -= Lr;
+    return chunk >= Lr ? chunk : 0;
+}
+
+}  // namespace bqm

@@ -237,16 +237,17 @@ static int launch_mmvq_t(const void *w, const void *a, float *y, int32_t *isums,
 int launch_mmvq(const void *w, const void *a, float *y, int32_t *isums, int64_t N, int64_t K,
                 int32_t T, hipStream_t stream)
 {
-    if (T == 1)
-        return launch_mmvq_t1(w, a, y, isums, N, K, stream);
+    if (staged_supported(K, T))
+        return launch_mmvq_staged(w, a, y, isums, N, K, T, stream);
     if (isums)
         return launch_mmvq_t<true>(w, a, nullptr, isums, N, K, T, stream);
     return launch_mmvq_t<false>(w, a, y, nullptr, N, K, T, stream);
 }
 
 // ---------------------------------------------------------------------------
-// Expert-routed product: blockIdx.y enumerates the (token, slot) pairs; the
-// pair's expert matrix is multiplied by its token's activation column.
+// Expert-routed product, one (token, slot) pair per blockIdx.y: the pair's
+// expert matrix times its token's activation column. Used for shapes whose
+// staged activations do not fit the grouped kernel's LDS budget.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void mmvq_id_tq1_kernel(const uint8_t *__restrict__ w,
                                                           const uint8_t *__restrict__ a,
@@ -272,19 +273,9 @@ __global__ __launch_bounds__(256) void mmvq_id_tq1_kernel(const uint8_t *__restr
                            row < N, nb, sub, Lr, 1, 0, y + pair * N, N, nullptr, N);
 }
 
-size_t mmvq_id_workspace_bytes(int64_t E, int64_t T, int32_t n_used)
+int launch_mmvq_id_pairs(const void *w, const void *a, const int32_t *ids, float *y, int64_t E,
+                         int64_t N, int64_t K, int64_t T, int32_t n_used, hipStream_t stream)
 {
-    (void)E;
-    (void)T;
-    (void)n_used;
-    return 256;
-}
-
-int launch_mmvq_id(const void *w, const void *a, const int32_t *ids, float *y, int64_t E,
-                   int64_t N, int64_t K, int64_t T, int32_t n_used, void *workspace,
-                   hipStream_t stream)
-{
-    (void)workspace;
     const int nb = (int)(K / kTq1BlockElems);
     const int lr = lanes_per_row_log2(nb);
     const int64_t rows_per_wg = 4 * (64 >> lr);

@@ -159,6 +159,42 @@ __device__ __forceinline__ void dot_qh(uint32_t w, uint32_t q74, uint32_t q75, u
     s.P[7] = sdot4(f.U0, q74, s.P[7]);
 }
 
+// Clean packed digits of a qs dword: U[c] holds digit c of each of its four
+// bytes. u_c = F_c - 3 F_(c+1) per byte; the subtraction never borrows across
+// bytes because every per-byte result is a digit (>= 0), and 3 F stays
+// below 256. Worth its six extra operations once a decoded dword is spent on
+// two or more activation columns (five products per column instead of eight).
+struct QsDigits {
+    uint32_t U[5];
+};
+
+__device__ __forceinline__ QsDigits qs_digits(uint32_t w)
+{
+    const QsFloors f = qs_floors(w);
+    QsDigits d;
+    d.U[0] = f.U0;
+    d.U[1] = f.F1 - 3u * f.F2;
+    d.U[2] = f.F2 - 3u * f.F3;
+    d.U[3] = f.F3 - 3u * f.F4;
+    d.U[4] = f.F4;
+    return d;
+}
+
+struct QhDigits {
+    uint32_t U[4];
+};
+
+__device__ __forceinline__ QhDigits qh_digits(uint32_t w)
+{
+    const QhFloors f = qh_floors(w);
+    QhDigits d;
+    d.U[0] = f.U0;
+    d.U[1] = f.F1 - 3u * f.F2;
+    d.U[2] = f.F2 - 3u * f.F3;
+    d.U[3] = f.F3;
+    return d;
+}
+
 // Exact per-sub-block trit sums from the two running sums.
 __device__ __forceinline__ void finish_isums(const BlockSums &s, int (&isum)[8])
 {

@@ -108,7 +108,10 @@ BQM_API int mmvq_tq1_0(const void *w, const void *a, float *y,
  *   y   [T][n_used][N] fp32 output.
  *   workspace: device scratch of at least mmvq_id_tq1_0_workspace_bytes(E, T,
  *   n_used) bytes, 256-byte aligned, owned by the caller; it may be reused
- *   between calls that are ordered on one stream.
+ *   between calls that are ordered on one stream. When that size is 0 (the
+ *   current implementation routes inside the kernel and needs none), NULL is
+ *   accepted. Tokens that share an expert are multiplied together, so the
+ *   expert's weights are read once per group of up to eight tokens.
  * Shapes: E >= 1, N >= 1, K >= 256, K % 256 == 0, T >= 1, 1 <= n_used <= E,
  * T * n_used <= 65535; one expert's matrix is below 4 GiB.
  * Alignment: w, a, y, ids 4 bytes; workspace 256 bytes. */
@@ -116,7 +119,7 @@ BQM_API int mmvq_id_tq1_0(const void *w, const void *a, const int32_t *ids, floa
                   int64_t E, int64_t N, int64_t K, int64_t T, int32_t n_used,
                   void *workspace, size_t workspace_bytes, void *stream);
 
-/* Workspace size mmvq_id_tq1_0 needs for these sizes (0 on bad sizes). */
+/* Workspace size mmvq_id_tq1_0 needs for these sizes (may be 0). */
 BQM_API size_t mmvq_id_tq1_0_workspace_bytes(int64_t E, int64_t T, int32_t n_used);
 
 /* Test twin of mmvq_tq1_0: runs the same decode and integer inner loop and

@@ -95,11 +95,12 @@ def test_mmvq_rejects(fn, args, expect):
 
 
 def test_mmvq_id_rejects():
+    # every call below carries at least one invalid argument, so it returns
+    # before touching the device (the pointers are never dereferenced)
     lib = bqm.library()
     ws = P(0x100000)
     need = lib.mmvq_id_tq1_0_workspace_bytes(8, 4, 2)
-    assert need > 0
-    base = [GOOD, GOOD, GOOD, GOOD, 8, 16, 256, 4, 2, ws, need, None]
+    base = [GOOD, GOOD, GOOD, GOOD, 8, 16, 256, 4, 2, ws, max(need, 256), None]
 
     def call(**kw):
         args = list(base)
@@ -111,9 +112,12 @@ def test_mmvq_id_rejects():
     assert call(w=None) == -1 and call(ids=None) == -1 and call(y=None) == -1
     assert call(E=0) == -2 and call(n_used=0) == -2 and call(n_used=9) == -2
     assert call(T=0) == -2 and call(K=100) == -2 and call(N=0) == -2
+    assert call(T=40000, n_used=2) == -2          # more than 65535 (token, slot) pairs
     assert call(ids=ODD) == -3 and call(a=ODD) == -3
-    assert call(ws=None) == -4 and call(wsb=need - 1) == -4
-    assert call(ws=P(0x100010)) == -3
+    assert call(ws=P(0x100010)) == -3             # workspace given but not 256-byte aligned
+    if need > 0:
+        assert call(ws=None) == -4 and call(wsb=need - 1) == -4
+    assert need == 0                              # routing runs in LDS: no workspace needed
     assert lib.mmvq_id_tq1_0_workspace_bytes(0, 4, 2) == 0
     assert lib.mmvq_id_tq1_0_workspace_bytes(8, 4, 9) == 0
 

@@ -290,6 +290,36 @@ def test_mmvq_id_small_cases(bqm):
                 assert np.array_equal(y1[0], y[t, s])
 
 
+@pytest.mark.parametrize("case", ["one_expert", "repeats", "all_experts"])
+def test_mmvq_id_routing_edge_cases(bqm, case):
+    """Routing edge cases: every pair on one expert (several groups of eight),
+    the same expert twice in a token (computed twice), and n_used == E."""
+    rng = np.random.default_rng({"one_expert": 7, "repeats": 8, "all_experts": 9}[case])
+    if case == "one_expert":
+        E, N, K, T, n_used = 4, 72, 512, 21, 1
+        ids = np.full((T, n_used), 2, np.int32)
+    elif case == "repeats":
+        E, N, K, T, n_used = 5, 40, 768, 6, 3
+        ids = rng.integers(0, E, (T, n_used)).astype(np.int32)
+        ids[:, 1] = ids[:, 0]
+    else:
+        E, N, K, T, n_used = 3, 33, 256, 9, 3
+        ids = np.stack([rng.permutation(E) for _ in range(T)]).astype(np.int32)
+    trits = synth.ternary(rng, (E * N, K))
+    d16 = synth.block_scales_f16(rng, (E * N, K // 256), 0.01, 0.1)
+    x = synth.activations(rng, T, K)
+    w, a, w_ref, a_ref = _prep(bqm, trits, d16, x)
+    _say("mmvq_id edge", case)
+    y = _host(bqm.mmvq_id_tq1_0(w, a, _dev(ids), E, N, K, T, n_used))
+    _, y64, ab = oracle.mmvq_id(w_ref, a_ref, ids, E, N, K, T, n_used)
+    _assert_close(y, y64, ab, "mmvq_id " + case)
+    wr = w.view(E, N, -1)
+    for t in range(T):
+        for s in range(n_used):
+            y1 = _host(bqm.mmvq_tq1_0(wr[ids[t, s]].clone(), a[t:t + 1].clone(), N, K, 1))
+            assert np.array_equal(y1[0], y[t, s])
+
+
 def test_workload_moe_parity(bqm):
     wl, inp = _workload_inputs("moe")
     E, N, K, n_used = wl.experts, wl.N, wl.K, wl.n_used
