@@ -3,21 +3,25 @@
 
 A step is one pass of the hot path for one decode token on the 4096 x 4096
 workload: Q8_1-quantize the fp32 activation column, then the TQ1_0 mat-vec.
-Inputs are synthetic (seeded), resident in HBM before timing starts. Each
+Inputs are synthetic (seeded) and resident in HBM before timing starts. Each
 step reads a different copy of the packed weights from a rotation of at
 least 1 GiB, so every mat-vec streams its weights from HBM rather than from
 the 256 MB last-level cache.
 
-Timed region: K steps captured once in a HIP graph and replayed, bracketed by
-device synchronizations (the eager, launch-by-launch rate is reported beside
-it). The dominant kernel's duration is measured separately with HIP events
-around each launch on its stream; the roofline fraction divides its
-algorithmic bytes by that duration. The CPU oracle is timed on a bounded
-sample as a reported baseline.
+Timing: K steps are captured once in a HIP graph; one warm replay, then one
+replay bracketed by HIP events on the launch stream (host launch cost is
+not in the timed region; the eager rate is reported beside it). The dominant
+kernel (the mat-vec) is timed the same way, as a graph of mat-vec launches
+only; its algorithmic bytes divided by that time give the roofline figure.
+The CPU oracle is timed on a bounded sample as a reported baseline.
+
+--sweep PATH additionally measures every workload shape and column count
+(the plain mat-vec and the expert-routed one) and writes a JSON table.
 
 Prints ONE JSON line on stdout; details go to stderr.
 """
 import argparse
+import ctypes
 import hashlib
 import json
 import os
@@ -31,6 +35,7 @@ if ROOT not in sys.path:
 METRIC = "µs/call and achieved HBM GB/s (% peak), TQ1_0 mat-vec N=4096 K=4096 T=1"
 HBM_PEAK_GBS = 8000.0
 COUNTERS_FILE = os.path.join(ROOT, "profiles", "counters_mmvq_tq1_0_decode_4096x4096.json")
+ROTATION_BYTES = 1 << 30
 
 
 def log(*a):
@@ -54,6 +59,15 @@ def algorithmic_bytes(N, K, T):
     return N * (K // 256) * 54 + T * (K // 32) * 36 + T * N * 4
 
 
+def moe_algorithmic_bytes(ids, N, K):
+    """Expert-routed call: the matrices of the distinct experts routed to,
+    once each; the tokens' Q8_1 activations; fp32 outputs; the ids."""
+    T, n_used = ids.shape
+    distinct = len(set(ids.ravel().tolist()))
+    return (distinct * N * (K // 256) * 54 + T * (K // 32) * 36 + T * n_used * N * 4
+            + T * n_used * 4), distinct
+
+
 def quantize_bytes(T, K):
     return T * K * 4 + T * (K // 32) * 36
 
@@ -72,12 +86,40 @@ def traffic_from_counters(N, K, T):
 
 
 def lanes_per_row_log2(nb):
-    """Lanes per output row in the one-column kernel (largest power of two
-    dividing the row's block count, at most 64)."""
+    """Lanes per output row in the staged kernels (log2): the smallest power
+    of two, at most 64, not below the row's block count."""
     lr = 0
-    while lr < 6 and nb % (2 << lr) == 0:
+    while lr < 6 and (1 << lr) < nb:
         lr += 1
     return lr
+
+
+def graph_us(torch, launch, count):
+    """Average microseconds per launch: `count` launches captured in one HIP
+    graph, one warm replay, then one replay timed with events on the stream."""
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for i in range(count):
+            launch(i)
+    graph.replay()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s.record(stream)
+    graph.replay()
+    e.record(stream)
+    torch.cuda.synchronize()
+    del graph
+    return s.elapsed_time(e) * 1e3 / count
+
+
+def rotation(torch, w0, dev, extra=1):
+    """Copies of the packed weights totalling at least ROTATION_BYTES."""
+    nbytes = w0.numel()
+    R = max(2, -(-ROTATION_BYTES // nbytes)) + extra
+    wrot = torch.empty((R, nbytes), dtype=torch.uint8, device=dev)
+    wrot.copy_(w0.reshape(1, -1).expand(R, nbytes))
+    return wrot, R
 
 
 def cpu_baseline(inp, N, K, T, step_bytes, seconds):
@@ -101,17 +143,90 @@ def cpu_baseline(inp, N, K, T, step_bytes, seconds):
                       "%.1f ms per step" % (n, N, K, T, el, 1e3 * el / n)}
 
 
+def calibrate(torch, np, wrot, R, nbytes, grid_wg):
+    """Empty dispatch and plain streaming reads of the same weight bytes."""
+    probes = ctypes.CDLL(os.path.join(ROOT, "bit_quantized_mat_amd", "libbqm_probes.so"))
+    probes.bqm_probe_empty.argtypes = [ctypes.c_int, ctypes.c_void_p]
+    probes.bqm_probe_read.argtypes = [ctypes.c_void_p, ctypes.c_uint64, ctypes.c_void_p,
+                                      ctypes.c_int, ctypes.c_void_p]
+    pout = torch.empty(4096, dtype=torch.int32, device=wrot.device)
+    rd = nbytes - nbytes % 16
+    cur = lambda: ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    cal = {"empty_kernel_us": graph_us(torch, lambda i: probes.bqm_probe_empty(grid_wg, cur()), 200)}
+    for g in (grid_wg, 1024):
+        us = graph_us(torch, lambda i: probes.bqm_probe_read(
+            ctypes.c_void_p(wrot[(13 * i + 1) % R].data_ptr()), rd,
+            ctypes.c_void_p(pout.data_ptr()), g, cur()), 200)
+        cal["read_%d_wg_us" % g] = us
+        cal["read_%d_wg_gbs" % g] = round(rd / us / 1e3, 1)
+    cal["read_bytes"] = int(rd)
+    cal["mmvq_grid_wg"] = int(grid_wg)
+    return {k: (round(v, 4) if isinstance(v, float) else v) for k, v in cal.items()}
+
+
+def sweep(path, torch, np, bqm, synth, dev, launches):
+    """Every workload shape and column count, cold weights, graph-timed."""
+    table = []
+    for name in ("tiny", "decode", "multicol", "ffn"):
+        wl = synth.WORKLOADS[name]
+        inp = synth.make_inputs(wl)
+        N, K = wl.N, wl.K
+        w0 = bqm.tq1_pack(torch.from_numpy(inp.trits).to(dev),
+                          torch.from_numpy(inp.d16.view(np.int16)).to(dev))
+        wrot, R = rotation(torch, w0, dev)
+        a_all = bqm.q8_1_quantize(torch.from_numpy(inp.x).to(dev))
+        for T in wl.Ts:
+            a = a_all[:T].contiguous()
+            y = torch.empty((T, N), dtype=torch.float32, device=dev)
+            us = graph_us(torch, lambda i: bqm.mmvq_tq1_0(wrot[i % R], a, N, K, T, out=y),
+                          launches)
+            b = algorithmic_bytes(N, K, T)
+            row = {"workload": name, "op": "mmvq_tq1_0", "N": N, "K": K, "T": T, "us": round(us, 3),
+                   "algorithmic_bytes": b, "gbs": round(b / us / 1e3, 1),
+                   "frac_of_8tbs": round(b / us / 1e3 / HBM_PEAK_GBS, 4)}
+            table.append(row)
+            log("sweep", row)
+        del wrot, a_all, w0
+        torch.cuda.empty_cache()
+    wl = synth.WORKLOADS["moe"]
+    inp = synth.make_inputs(wl)
+    E, N, K, n_used = wl.experts, wl.N, wl.K, wl.n_used
+    w0 = bqm.tq1_pack(torch.from_numpy(inp.trits).to(dev),
+                      torch.from_numpy(inp.d16.view(np.int16)).to(dev))
+    wrot, R = rotation(torch, w0, dev)
+    a_all = bqm.q8_1_quantize(torch.from_numpy(inp.x).to(dev))
+    for T in wl.Ts:
+        ids_np = np.ascontiguousarray(inp.ids[:T])
+        ids = torch.from_numpy(ids_np).to(dev)
+        a = a_all[:T].contiguous()
+        y = torch.empty((T, n_used, N), dtype=torch.float32, device=dev)
+        us = graph_us(torch, lambda i: bqm.mmvq_id_tq1_0(wrot[i % R], a, ids, E, N, K, T, n_used,
+                                                         out=y), launches)
+        b, distinct = moe_algorithmic_bytes(ids_np, N, K)
+        row = {"workload": "moe", "op": "mmvq_id_tq1_0", "E": E, "N": N, "K": K, "T": T,
+               "n_used": n_used, "distinct_experts": distinct, "us": round(us, 3),
+               "algorithmic_bytes": b, "gbs": round(b / us / 1e3, 1),
+               "frac_of_8tbs": round(b / us / 1e3 / HBM_PEAK_GBS, 4)}
+        table.append(row)
+        log("sweep", row)
+    del wrot, a_all, w0
+    torch.cuda.empty_cache()
+    with open(path, "w") as f:
+        json.dump(table, f, indent=1)
+    return table
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=500)
     ap.add_argument("--warmup", type=int, default=50)
-    ap.add_argument("--rotation-gib", type=float, default=1.0,
-                    help="total size of the rotated weight copies")
     ap.add_argument("--kernel-launches", type=int, default=400,
-                    help="individually event-timed launches of the dominant kernel")
+                    help="graph-captured launches of the dominant kernel")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--sweep", metavar="PATH", help="also measure every workload; JSON table")
+    ap.add_argument("--sweep-launches", type=int, default=100)
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -135,9 +250,7 @@ def main():
     w0 = bqm.tq1_pack(torch.from_numpy(inp.trits).to(dev),
                       torch.from_numpy(inp.d16.view(np.int16)).to(dev))
     wbytes = w0.numel()
-    R = max(2, int(np.ceil(args.rotation_gib * (1 << 30) / wbytes)))
-    wrot = torch.empty((R, wbytes), dtype=torch.uint8, device=dev)
-    wrot.copy_(w0.view(1, -1).expand(R, wbytes))
+    wrot, R = rotation(torch, w0, dev)
     x = torch.from_numpy(inp.x[:T]).to(dev)
     a = torch.empty((T, (K // 32) * 36), dtype=torch.uint8, device=dev)
     y = torch.empty((T, N), dtype=torch.float32, device=dev)
@@ -151,87 +264,36 @@ def main():
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
-
-    # eager rate (host launch cost included)
     t0 = time.perf_counter()
     for i in range(args.steps):
         step(i)
     torch.cuda.synchronize()
-    eager_ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    eager_us = (time.perf_counter() - t0) * 1e6 / args.steps
 
-    # timed region: the K steps captured in one graph
-    graph = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(graph):
-        for i in range(args.steps):
-            step(args.warmup + i)
-    graph.replay()
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    graph.replay()
-    torch.cuda.synchronize()
-    ms_per_step = (time.perf_counter() - t0) * 1e3 / args.steps
-
-    # dominant kernel: per-launch HIP events on the launch stream
-    stream = torch.cuda.current_stream(dev)
-    M = args.kernel_launches
-
-    def per_launch_us(launch, count):
-        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-               for _ in range(count)]
-        for i, (s, e) in enumerate(evs):
-            s.record(stream)
-            launch(i)
-            e.record(stream)
-        torch.cuda.synchronize()
-        return np.array([s.elapsed_time(e) * 1e3 for s, e in evs])
-
-    def mmvq_launch(i):
-        bqm.mmvq_tq1_0(wrot[(7 * i) % R], a, N, K, T, out=y, stream=stream)
-
-    durs_us = per_launch_us(mmvq_launch, M)
-    us_call = float(np.mean(durs_us))
-    # back-to-back launches bracketed by one event pair (includes dispatch gaps)
-    s0, e0 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    s0.record(stream)
-    for i in range(M):
-        bqm.mmvq_tq1_0(wrot[(11 * i) % R], a, N, K, T, out=y, stream=stream)
-    e0.record(stream)
-    torch.cuda.synchronize()
-    us_b2b = s0.elapsed_time(e0) * 1e3 / M
-
-    # calibration: an empty dispatch, and a streaming read of the same weight
-    # bytes with the mat-vec's grid and with a wider grid
-    import ctypes
-    probes = ctypes.CDLL(os.path.join(ROOT, "bit_quantized_mat_amd", "libbqm_probes.so"))
-    probes.bqm_probe_empty.argtypes = [ctypes.c_int, ctypes.c_void_p]
-    probes.bqm_probe_read.argtypes = [ctypes.c_void_p, ctypes.c_uint64, ctypes.c_void_p,
-                                      ctypes.c_int, ctypes.c_void_p]
-    sptr = ctypes.c_void_p(stream.cuda_stream)
-    pout = torch.empty(4096, dtype=torch.int32, device=dev)
-    mm_grid = int(np.ceil(N / (4 * (64 >> lanes_per_row_log2(K // 256)))))
-    rd_bytes = wbytes - wbytes % 16
-    cal = {"empty_kernel_us": float(np.mean(per_launch_us(
-        lambda i: probes.bqm_probe_empty(mm_grid, sptr), 200)))}
-    for g in (mm_grid, 1024):
-        d = per_launch_us(lambda i: probes.bqm_probe_read(
-            ctypes.c_void_p(wrot[(13 * i + 1) % R].data_ptr()), rd_bytes,
-            ctypes.c_void_p(pout.data_ptr()), g, sptr), 200)
-        cal["read_%d_wg_us" % g] = float(np.mean(d))
-        cal["read_%d_wg_gbs" % g] = round(rd_bytes / float(np.mean(d)) / 1e3, 1)
-    cal["read_bytes"] = int(rd_bytes)
-    cal["mmvq_grid_wg"] = mm_grid
+    # timed region: the K steps as one graph
+    step_us = graph_us(torch, lambda i: step(args.warmup + i), args.steps)
+    # dominant kernel: the mat-vec alone, graph of launches on rotating weights
+    us_call = graph_us(torch, lambda i: bqm.mmvq_tq1_0(wrot[(7 * i) % R], a, N, K, T, out=y),
+                       args.kernel_launches)
+    quant_us = graph_us(torch, lambda i: bqm.q8_1_quantize(x, out=a), 200)
+    grid_wg = -(-N // (4 * (64 >> lanes_per_row_log2(K // 256))))
+    cal = calibrate(torch, np, wrot, R, wbytes, grid_wg)
     log("calibration:", cal)
 
     mm_bytes = algorithmic_bytes(N, K, T)
     step_bytes = mm_bytes + quantize_bytes(T, K)
-    achieved = mm_bytes / (us_call * 1e-6) / 1e9
-    value = step_bytes / (ms_per_step * 1e-3) / 1e9
-    traffic = traffic_from_counters(N, K, T)
-    log("mmvq: %.3f us/launch (events per launch, median %.3f, p10 %.3f, p90 %.3f), "
-        "%.3f us back-to-back; %.1f GB/s = %.1f%% of %.0f GB/s"
-        % (us_call, np.median(durs_us), np.percentile(durs_us, 10), np.percentile(durs_us, 90),
-           us_b2b, achieved, 100 * achieved / HBM_PEAK_GBS, HBM_PEAK_GBS))
-    log("step: %.3f us graph-replayed, %.3f us eager" % (ms_per_step * 1e3, eager_ms * 1e3))
+    achieved = mm_bytes / us_call / 1e3
+    value = step_bytes / step_us / 1e3
+    log("mmvq: %.3f us per call (graph of %d), %.1f GB/s = %.2f%% of %.0f GB/s; quantize %.3f us"
+        % (us_call, args.kernel_launches, achieved, 100 * achieved / HBM_PEAK_GBS, HBM_PEAK_GBS,
+           quant_us))
+    log("step: %.3f us graph-replayed, %.3f us eager" % (step_us, eager_us))
+
+    table = None
+    if args.sweep:
+        del wrot
+        torch.cuda.empty_cache()
+        table = sweep(args.sweep, torch, np, bqm, synth, dev, args.sweep_launches)
 
     base = None
     if not args.no_cpu_baseline:
@@ -245,26 +307,29 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms_per_step, 6),
+        "ms_per_step": round(step_us / 1e3, 6),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "i8",
         "data": "synthetic",
-        "config": {"workload": "decode mat-vec TQ1_0 N=4096 K=4096 T=1 (quantize + mmvq per step)",
+        "config": {"workload": "decode mat-vec TQ1_0 N=4096 K=4096 T=1 (Q8_1 quantize + mat-vec "
+                               "per step)",
                    "N": N, "K": K, "T": T, "weight_rotation_bytes": int(R * wbytes),
-                   "timed": "HIP graph of all steps, replayed once"},
+                   "timed": "HIP graph of all steps, replayed once after a warm replay"},
         "us_per_call": round(us_call, 4),
-        "us_per_call_back_to_back": round(us_b2b, 4),
-        "us_per_step_eager": round(eager_ms * 1e3, 4),
         "mmvq_gbs": round(achieved, 2),
+        "quantize_us": round(quant_us, 4),
+        "us_per_step_eager": round(eager_us, 4),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": traffic, "kernel": "mmvq_tq1_0",
+                     "traffic": traffic_from_counters(N, K, T), "kernel": "mmvq_tq1_0",
                      "algorithmic_bytes_per_launch": mm_bytes},
-        "calibration": {k: (round(v, 4) if isinstance(v, float) else v) for k, v in cal.items()},
+        "calibration": cal,
         "cpu_baseline": base,
     }
+    if table is not None:
+        line["sweep_file"] = args.sweep
     print(json.dumps(line), flush=True)
 
 

@@ -18,9 +18,11 @@ inline int check_launch()
 int launch_q8_1_quantize(const float *x, void *a, int64_t T, int64_t K, hipStream_t stream);
 int launch_tq1_pack(const int8_t *trits, const uint16_t *d, void *w, int64_t N, int64_t K,
                     hipStream_t stream);
-// Largest power of two (at most 64) dividing a row's block count: the number
-// of lanes that share one output row in the mat-vec kernels.
+// Lanes that share one output row in the mat-vec kernels (log2): the smallest
+// power of two, at most 64, not below the row's block count.
 int lanes_per_row_log2(int64_t nb);
+// Dynamic LDS bytes a workgroup may use on the current device.
+size_t lds_budget();
 // Staged kernel (one to eight columns, activations staged in LDS): whether it
 // takes this shape, and its launcher.
 bool staged_supported(int64_t K, int32_t T);

@@ -132,7 +132,7 @@ static int id_chunk(int64_t E, int nb, int lr)
 {
     if (E > kIdMaxExperts)
         return 0;
-    return staged_chunk(nb, lr, kIdCols, kLdsBudget - (size_t)route_dwords(E) * 4);
+    return staged_chunk(nb, lr, kIdCols, lds_budget() - (size_t)route_dwords(E) * 4);
 }
 
 size_t mmvq_id_workspace_bytes(int64_t E, int64_t T, int32_t n_used)
@@ -160,6 +160,7 @@ int launch_mmvq_id(const void *w, const void *a, const int32_t *ids, float *y, i
     const dim3 grid((unsigned)((N + rows_per_wg - 1) / rows_per_wg), (unsigned)max_items);
     const int rd = route_dwords(E);
     const size_t lds = (size_t)rd * 4 + (size_t)kIdCols * chunk * kActStride * 4;
+    allow_dynamic_lds(reinterpret_cast<const void *>(&mmvq_id_kernel), lds);
     hipLaunchKernelGGL(mmvq_id_kernel, grid, dim3(256), lds, stream,
                        static_cast<const uint8_t *>(w), static_cast<const uint8_t *>(a), ids, y,
                        (int)E, N, nb, (int)T, (int)n_used, lr, chunk, rd);

@@ -47,11 +47,29 @@ __global__ __launch_bounds__(256) void mmvq_staged_kernel(const uint8_t *__restr
 
 int lanes_per_row_log2(int64_t nb)
 {
-    // largest power of two (<= 64) that divides the row's block count
+    // smallest power of two (<= 64) not below the row's block count; lanes
+    // beyond the count stay idle and add zeros in the butterfly
     int l = 0;
-    while (l < 6 && nb % (2ll << l) == 0)
+    while (l < 6 && (1ll << l) < nb)
         l++;
     return l;
+}
+
+size_t lds_budget()
+{
+    // dynamic LDS per workgroup this device allows, cached per device
+    static size_t cached[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64)
+        return kLdsDefault;
+    if (!cached[dev]) {
+        int v = 0;
+        if (hipDeviceGetAttribute(&v, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess ||
+            v <= 0)
+            v = (int)kLdsDefault;
+        cached[dev] = (size_t)v < kLdsMax ? (size_t)v : kLdsMax;
+    }
+    return cached[dev];
 }
 
 bool staged_supported(int64_t K, int32_t T)
@@ -59,7 +77,7 @@ bool staged_supported(int64_t K, int32_t T)
     if (T < 1 || T > kStagedMaxCols)
         return false;
     const int nb = (int)(K / kTq1BlockElems);
-    return staged_chunk(nb, lanes_per_row_log2(nb), T) > 0;
+    return staged_chunk(nb, lanes_per_row_log2(nb), T, lds_budget()) > 0;
 }
 
 template <int TC>
@@ -67,6 +85,8 @@ static void launch_staged_tc(const uint8_t *w, const uint8_t *a, float *y, int32
                              int64_t N, int nb, int T, int lr, int chunk, dim3 grid, size_t lds,
                              hipStream_t stream)
 {
+    allow_dynamic_lds(reinterpret_cast<const void *>(&mmvq_staged_kernel<TC, true>), lds);
+    allow_dynamic_lds(reinterpret_cast<const void *>(&mmvq_staged_kernel<TC, false>), lds);
     if (isums)
         hipLaunchKernelGGL((mmvq_staged_kernel<TC, true>), grid, dim3(256), lds, stream, w, a,
                            nullptr, isums, N, nb, T, lr, chunk);
@@ -80,7 +100,7 @@ int launch_mmvq_staged(const void *w, const void *a, float *y, int32_t *isums, i
 {
     const int nb = (int)(K / kTq1BlockElems);
     const int lr = lanes_per_row_log2(nb);
-    const int chunk = staged_chunk(nb, lr, T);
+    const int chunk = staged_chunk(nb, lr, T, lds_budget());
     const int64_t rows_per_wg = 4 * (64 >> lr);
     const dim3 grid((unsigned)((N + rows_per_wg - 1) / rows_per_wg));
     const size_t lds = (size_t)T * chunk * kActStride * 4;

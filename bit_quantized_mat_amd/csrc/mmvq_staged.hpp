@@ -220,16 +220,31 @@ __device__ __forceinline__ void staged_rows(__amdgpu_buffer_rsrc_t rw, __amdgpu_
     }
 }
 
-// Largest chunk (a multiple of the lanes per row, at most 128 blocks) whose
-// staged activations for T columns fit lds_budget bytes; 0 if none does. The
-// budget stays within the 64 KiB of dynamic LDS a launch gets by default.
-constexpr size_t kLdsBudget = 64 * 1024;
+// Dynamic LDS: 64 KiB is always available; beyond that the launcher raises
+// the kernel's limit up to what the device reports (160 KiB on gfx950).
+constexpr size_t kLdsDefault = 64 * 1024;
+constexpr size_t kLdsMax = 160 * 1024;
 
-inline int staged_chunk(int nb, int lr, int T, size_t lds_budget = kLdsBudget)
+// Raise a kernel's dynamic-LDS limit when a launch needs more than the
+// default (idempotent; the runtime keeps the attribute per function).
+inline void allow_dynamic_lds(const void *kernel, size_t bytes)
+{
+    if (bytes > kLdsDefault)
+        (void)hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+}
+
+// Blocks staged per pass: all of a row's blocks if they fit (rows with fewer
+// blocks than lanes leave the surplus lanes idle), else the largest multiple
+// of the lanes per row, at most 128, whose T staged columns fit lds_budget
+// bytes; 0 if not even one multiple fits.
+inline int staged_chunk(int nb, int lr, int T, size_t lds_budget)
 {
     const int Lr = 1 << lr;
-    int chunk = nb < kMaxChunkBlocks ? nb : kMaxChunkBlocks;
-    while (chunk >= Lr && (size_t)T * chunk * kActStride * 4 > lds_budget)
+    auto fits = [&](int c) { return (size_t)T * c * kActStride * 4 <= lds_budget; };
+    if (nb <= Lr)
+        return fits(nb) ? nb : 0;
+    int chunk = (nb < kMaxChunkBlocks ? nb : kMaxChunkBlocks) / Lr * Lr;
+    while (chunk >= Lr && !fits(chunk))
         chunk -= Lr;
     return chunk >= Lr ? chunk : 0;
 }
