@@ -164,10 +164,13 @@ def calibrate(torch, np, wrot, R, nbytes, grid_wg):
     return {k: (round(v, 4) if isinstance(v, float) else v) for k, v in cal.items()}
 
 
-def sweep(path, torch, np, bqm, synth, dev, launches):
-    """Every workload shape and column count, cold weights, graph-timed."""
+def sweep(path, torch, np, bqm, synth, dev, launches, only=None):
+    """Every workload shape and column count, cold weights, graph-timed.
+    only: optional set of workload names to restrict the sweep to."""
     table = []
     for name in ("tiny", "decode", "multicol", "ffn"):
+        if only and name not in only:
+            continue
         wl = synth.WORKLOADS[name]
         inp = synth.make_inputs(wl)
         N, K = wl.N, wl.K
@@ -188,6 +191,10 @@ def sweep(path, torch, np, bqm, synth, dev, launches):
             log("sweep", row)
         del wrot, a_all, w0
         torch.cuda.empty_cache()
+    if only and "moe" not in only:
+        with open(path, "w") as f:
+            json.dump(table, f, indent=1)
+        return table
     wl = synth.WORKLOADS["moe"]
     inp = synth.make_inputs(wl)
     E, N, K, n_used = wl.experts, wl.N, wl.K, wl.n_used
@@ -216,6 +223,47 @@ def sweep(path, torch, np, bqm, synth, dev, launches):
     return table
 
 
+def profile_run(spec, torch, np, bqm, synth, dev):
+    """A few launches of one workload shape for counter collection: `launches`
+    mat-vec calls on cold weight copies, then as many streaming reads of the
+    same weight bytes by the probe kernel (a reference of known size)."""
+    parts = spec.split(":")
+    name, T = parts[0], int(parts[1])
+    launches = int(parts[2]) if len(parts) > 2 else 20
+    wl = synth.WORKLOADS[name]
+    inp = synth.make_inputs(wl, T=T)
+    N, K = wl.N, wl.K
+    w0 = bqm.tq1_pack(torch.from_numpy(inp.trits).to(dev),
+                      torch.from_numpy(inp.d16.view(np.int16)).to(dev))
+    wrot, R = rotation(torch, w0, dev)
+    a = bqm.q8_1_quantize(torch.from_numpy(inp.x[:T]).to(dev))
+    if wl.experts:
+        ids = torch.from_numpy(np.ascontiguousarray(inp.ids[:T])).to(dev)
+        y = torch.empty((T, wl.n_used, N), dtype=torch.float32, device=dev)
+        run = lambda i: bqm.mmvq_id_tq1_0(wrot[i % R], a, ids, wl.experts, N, K, T, wl.n_used,
+                                          out=y)
+    else:
+        y = torch.empty((T, N), dtype=torch.float32, device=dev)
+        run = lambda i: bqm.mmvq_tq1_0(wrot[i % R], a, N, K, T, out=y)
+    torch.cuda.synchronize()
+    for i in range(launches):
+        run(i)
+    torch.cuda.synchronize()
+    probes = ctypes.CDLL(os.path.join(ROOT, "bit_quantized_mat_amd", "libbqm_probes.so"))
+    probes.bqm_probe_read.argtypes = [ctypes.c_void_p, ctypes.c_uint64, ctypes.c_void_p,
+                                      ctypes.c_int, ctypes.c_void_p]
+    pout = torch.empty(4096, dtype=torch.int32, device=dev)
+    nbytes = w0.numel() - w0.numel() % 16
+    for i in range(launches):
+        probes.bqm_probe_read(ctypes.c_void_p(wrot[(i + 1) % R].data_ptr()), nbytes,
+                              ctypes.c_void_p(pout.data_ptr()), 1024,
+                              ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+    torch.cuda.synchronize()
+    print(json.dumps({"profile": name, "N": N, "K": K, "T": T, "launches": launches,
+                      "weight_bytes": int(w0.numel()), "probe_read_bytes": int(nbytes),
+                      "kernel_source_hash": kernel_source_hash()}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -227,6 +275,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--sweep", metavar="PATH", help="also measure every workload; JSON table")
     ap.add_argument("--sweep-launches", type=int, default=100)
+    ap.add_argument("--sweep-only", default="", help="comma-separated workload names")
+    ap.add_argument("--profile", metavar="WORKLOAD:T[:LAUNCHES]",
+                    help="only run a few launches of one shape (for counter collection)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -240,10 +291,13 @@ def main():
     import bit_quantized_mat_amd as bqm
     from bit_quantized_mat_amd import synth
 
-    wl = synth.WORKLOADS["decode"]
-    N, K, T = wl.N, wl.K, 1
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.profile:
+        profile_run(args.profile, torch, np, bqm, synth, dev)
+        return
+    wl = synth.WORKLOADS["decode"]
+    N, K, T = wl.N, wl.K, 1
     inp = synth.make_inputs(wl)
     log("workload decode N=%d K=%d T=%d" % (N, K, T))
 
@@ -293,7 +347,8 @@ def main():
     if args.sweep:
         del wrot
         torch.cuda.empty_cache()
-        table = sweep(args.sweep, torch, np, bqm, synth, dev, args.sweep_launches)
+        only = set(filter(None, args.sweep_only.split(",")))
+        table = sweep(args.sweep, torch, np, bqm, synth, dev, args.sweep_launches, only)
 
     base = None
     if not args.no_cpu_baseline:

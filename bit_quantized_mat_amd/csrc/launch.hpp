@@ -28,6 +28,9 @@ size_t lds_budget();
 bool staged_supported(int64_t K, int32_t T);
 int launch_mmvq_staged(const void *w, const void *a, float *y, int32_t *isums, int64_t N,
                        int64_t K, int32_t T, hipStream_t stream);
+// Matrix-core kernel for 9 to 32 columns.
+int launch_mmvq_mfma(const void *w, const void *a, float *y, int32_t *isums, int64_t N,
+                     int64_t K, int32_t T, hipStream_t stream);
 int launch_mmvq(const void *w, const void *a, float *y, int32_t *isums, int64_t N, int64_t K,
                 int32_t T, hipStream_t stream);
 int launch_mmvq_id(const void *w, const void *a, const int32_t *ids, float *y, int64_t E,

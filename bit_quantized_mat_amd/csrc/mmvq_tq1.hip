@@ -239,6 +239,8 @@ int launch_mmvq(const void *w, const void *a, float *y, int32_t *isums, int64_t 
 {
     if (staged_supported(K, T))
         return launch_mmvq_staged(w, a, y, isums, N, K, T, stream);
+    if (T > 8)
+        return launch_mmvq_mfma(w, a, y, isums, N, K, T, stream);
     if (isums)
         return launch_mmvq_t<true>(w, a, nullptr, isums, N, K, T, stream);
     return launch_mmvq_t<false>(w, a, y, nullptr, N, K, T, stream);

@@ -52,6 +52,12 @@ __device__ __forceinline__ uint32_t pk_mul(uint32_t x, unsigned short k)
     return __builtin_bit_cast(uint32_t, v);
 }
 
+// 3 * f for a dword of four floor bytes, each at most 80 (so 3 f per byte
+// stays below 256 and no byte carries into the next). As two 16-bit lanes the
+// product is exact too; the packed multiply keeps the compiler from choosing a
+// quarter-rate 32-bit multiply where it would not use a shift-add.
+__device__ __forceinline__ uint32_t mul3_bytes(uint32_t f) { return pk_mul(f, 3); }
+
 // Bytes 1 and 3 of e (bytes 0, 2 of the source dword) and of o (bytes 1, 3)
 // interleaved back into source byte order.
 __device__ __forceinline__ uint32_t hi_bytes(uint32_t o, uint32_t e)
@@ -193,6 +199,53 @@ __device__ __forceinline__ QhDigits qh_digits(uint32_t w)
     d.U[2] = f.F2 - 3u * f.F3;
     d.U[3] = f.F3;
     return d;
+}
+
+// Packed signed trits t = u - 1 (bytes 0xff, 0x00, 0x01) from a floor pair:
+// t = F_c - 3 F_(c+1) - 1 per byte. Offsetting every byte by 0x80 first keeps
+// the subtraction free of borrows; the final xor removes the offset.
+__device__ __forceinline__ uint32_t trits_from_floors(uint32_t f, uint32_t f_next)
+{
+    const uint32_t biased = ((f ^ 0x80808080u) + 0xfefefeffu) - mul3_bytes(f_next);  // 0x7f + u
+    return biased ^ 0x80808080u;
+}
+
+// Same for a lowest digit already in hand (u in {0,1,2} per byte).
+__device__ __forceinline__ uint32_t trits_from_digits(uint32_t u)
+{
+    return ((u ^ 0x80808080u) + 0xfefefeffu) ^ 0x80808080u;
+}
+
+// Trits of all five digits of a qs dword: T[c] holds trit c of each byte.
+struct QsTrits {
+    uint32_t T[5];
+};
+
+__device__ __forceinline__ QsTrits qs_trits(uint32_t w)
+{
+    const QsFloors f = qs_floors(w);
+    QsTrits t;
+    t.T[0] = trits_from_digits(f.U0);
+    t.T[1] = trits_from_floors(f.F1, f.F2);
+    t.T[2] = trits_from_floors(f.F2, f.F3);
+    t.T[3] = trits_from_floors(f.F3, f.F4);
+    t.T[4] = trits_from_digits(f.F4);
+    return t;
+}
+
+struct QhTrits {
+    uint32_t T[4];
+};
+
+__device__ __forceinline__ QhTrits qh_trits(uint32_t w)
+{
+    const QhFloors f = qh_floors(w);
+    QhTrits t;
+    t.T[0] = trits_from_digits(f.U0);
+    t.T[1] = trits_from_floors(f.F1, f.F2);
+    t.T[2] = trits_from_floors(f.F2, f.F3);
+    t.T[3] = trits_from_digits(f.F3);
+    return t;
 }
 
 // Exact per-sub-block trit sums from the two running sums.

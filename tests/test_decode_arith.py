@@ -88,3 +88,37 @@ def test_byte_split_and_merge_selectors():
     assert _perm(0, w, 0x0C030C01) == 0x00440022          # bytes 1, 3 into lanes
     e, o = 0xAA01BB02, 0xCC03DD04                          # byte 1/3 of each lane
     assert _perm(o, e, 0x07030501) == 0xCCAADDBB          # [e.b1, o.b1, e.b3, o.b3]
+
+
+def _trits_from_floors(f, fn):
+    return ((((f ^ 0x80808080) + 0xFEFEFEFF) - 3 * fn) & 0xFFFFFFFF) ^ 0x80808080
+
+
+def _trits_from_digits(u):
+    return (((u ^ 0x80808080) + 0xFEFEFEFF) & 0xFFFFFFFF) ^ 0x80808080
+
+
+def _pack(b):
+    return b[0] | (b[1] << 8) | (b[2] << 16) | (b[3] << 24)
+
+
+def _signed_bytes(x):
+    return [((x >> (8 * i)) & 0xFF) - (256 if (x >> (8 * i)) & 0x80 else 0) for i in range(4)]
+
+
+def test_packed_trit_conversion_exhaustive():
+    """Signed trits from floor pairs (digits 1..3 of a qs byte, 1..2 of qh)
+    and from a digit in hand (digit 0, the top digit): every byte value in
+    every byte position of a dword, against Python's digits minus one."""
+    for v in range(243):
+        for pos in range(4):
+            vs = [(v + 37 * k) % 243 for k in range(4)]
+            vs[pos] = v
+            for c in (1, 2, 3):
+                t = _trits_from_floors(_pack([x // 3 ** c for x in vs]),
+                                       _pack([x // 3 ** (c + 1) for x in vs]))
+                assert _signed_bytes(t) == [(x // 3 ** c) % 3 - 1 for x in vs]
+            assert _signed_bytes(_trits_from_digits(_pack([x % 3 for x in vs]))) == \
+                [x % 3 - 1 for x in vs]
+            assert _signed_bytes(_trits_from_digits(_pack([x // 81 for x in vs]))) == \
+                [x // 81 - 1 for x in vs]

@@ -215,9 +215,13 @@ def test_mmvq_one_hot_element_map(bqm):
         assert np.array_equal(y, ref), "elements %d..%d" % (e0, e0 + 31)
 
 
-def test_mmvq_columns_equal_single_column_calls(bqm):
-    N, K, T = 320, 6144, 8
-    trits, d16, x = _case(N, K, T, 4242)
+@pytest.mark.parametrize("N,K,T", [(320, 6144, 8), (100, 6144, 20), (70, 16384, 32),
+                                   (48, 4096, 12), (33, 768, 9)])
+def test_mmvq_columns_equal_single_column_calls(bqm, N, K, T):
+    """Column t of a T-column call equals the one-column call bit for bit:
+    integer sums and fp32 outputs (staged kernel up to 8 columns, matrix-core
+    kernel beyond, both against the one-column kernel)."""
+    trits, d16, x = _case(N, K, T, 4242 + T)
     w, a, _, _ = _prep(bqm, trits, d16, x)
     yT = _host(bqm.mmvq_tq1_0(w, a, N, K, T))
     iT = _host(bqm.mmvq_tq1_0_block_isums(w, a, N, K, T))
