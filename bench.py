@@ -42,14 +42,20 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+# Sources the decode mat-vec (the staged kernel) is compiled from: counter
+# readings taken on other sources do not describe it.
+DOMINANT_KERNEL_SOURCES = ("common.hpp", "tq1_decode.hpp", "mmvq_staged.hpp", "mmvq_staged.hip",
+                           "launch.hpp", "bqm_api.hip")
+
+
 def kernel_source_hash():
-    """Hash of the HIP sources; counter readings are only valid for this hash."""
+    """Hash of the dominant kernel's HIP sources; counter readings are only
+    valid for this hash."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "bit_quantized_mat_amd", "csrc")
-    for name in sorted(os.listdir(csrc)):
-        if name.endswith((".hip", ".hpp")):
-            with open(os.path.join(csrc, name), "rb") as f:
-                h.update(name.encode() + b"\0" + f.read())
+    for name in DOMINANT_KERNEL_SOURCES:
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode() + b"\0" + f.read())
     return h.hexdigest()[:16]
 
 
@@ -252,16 +258,71 @@ def profile_run(spec, torch, np, bqm, synth, dev):
     probes = ctypes.CDLL(os.path.join(ROOT, "bit_quantized_mat_amd", "libbqm_probes.so"))
     probes.bqm_probe_read.argtypes = [ctypes.c_void_p, ctypes.c_uint64, ctypes.c_void_p,
                                       ctypes.c_int, ctypes.c_void_p]
+    probes.bqm_probe_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_uint64,
+                                      ctypes.c_int, ctypes.c_void_p]
     pout = torch.empty(4096, dtype=torch.int32, device=dev)
     nbytes = w0.numel() - w0.numel() % 16
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
     for i in range(launches):
         probes.bqm_probe_read(ctypes.c_void_p(wrot[(i + 1) % R].data_ptr()), nbytes,
-                              ctypes.c_void_p(pout.data_ptr()), 1024,
-                              ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+                              ctypes.c_void_p(pout.data_ptr()), 1024, stream)
+    torch.cuda.synchronize()
+    # the copies are all equal, so copying one onto another changes nothing
+    for i in range(launches):
+        probes.bqm_probe_copy(ctypes.c_void_p(wrot[(i + 2) % R].data_ptr()),
+                              ctypes.c_void_p(wrot[(i + R // 2) % R].data_ptr()), nbytes, 1024,
+                              stream)
     torch.cuda.synchronize()
     print(json.dumps({"profile": name, "N": N, "K": K, "T": T, "launches": launches,
-                      "weight_bytes": int(w0.numel()), "probe_read_bytes": int(nbytes),
+                      "weight_bytes": int(w0.numel()), "probe_bytes": int(nbytes),
                       "kernel_source_hash": kernel_source_hash()}), flush=True)
+
+
+def _counter_medians(csv_dir, counter):
+    """Median per-dispatch value of one counter, by kernel family, from a
+    rocprofv3 --pmc csv output directory."""
+    import csv
+    import glob
+    import statistics
+    vals = {}
+    for path in glob.glob(os.path.join(csv_dir, "*counter_collection.csv")):
+        with open(path) as f:
+            for r in csv.DictReader(f):
+                if r["Counter_Name"] != counter:
+                    continue
+                name = r["Kernel_Name"]
+                fam = ("copy_probe" if "copy_kernel" in name else
+                       "read_probe" if "read_kernel" in name else
+                       "mmvq" if "mmvq" in name else None)
+                if fam:
+                    vals.setdefault(fam, []).append(float(r["Counter_Value"]))
+    return {k: statistics.median(v) for k, v in vals.items()}
+
+
+def write_counters(fetch_dir, write_dir, probe_bytes):
+    """HBM bytes per mat-vec launch from two counter runs of `--profile
+    decode:1`: FETCH_SIZE and WRITE_SIZE (KiB per dispatch) of the mat-vec,
+    each scaled by bytes moved / counter reading of the copy probe, which
+    reads and writes probe_bytes bytes."""
+    f = _counter_medians(fetch_dir, "FETCH_SIZE")
+    w = _counter_medians(write_dir, "WRITE_SIZE")
+    fetch_scale = probe_bytes / f["copy_probe"]
+    write_scale = probe_bytes / w["copy_probe"]
+    wl_N, wl_K = 4096, 4096
+    out = {"kernel_source_hash": kernel_source_hash(), "shape": [wl_N, wl_K, 1],
+           "fetch_size_kib": f["mmvq"], "write_size_kib": w["mmvq"],
+           "copy_probe_bytes": probe_bytes, "copy_probe_fetch_kib": f["copy_probe"],
+           "copy_probe_write_kib": w["copy_probe"],
+           "read_probe_fetch_kib": f.get("read_probe"),
+           "fetch_bytes_per_kib": round(fetch_scale, 3), "write_bytes_per_kib": round(write_scale, 3),
+           "hbm_fetch_bytes_per_launch": round(f["mmvq"] * fetch_scale),
+           "hbm_write_bytes_per_launch": round(w["mmvq"] * write_scale)}
+    out["hbm_bytes_per_launch"] = out["hbm_fetch_bytes_per_launch"] + out["hbm_write_bytes_per_launch"]
+    out["algorithmic_bytes_per_launch"] = algorithmic_bytes(wl_N, wl_K, 1)
+    with open(COUNTERS_FILE, "w") as fh:
+        json.dump(out, fh, indent=1)
+        fh.write("\n")
+    print(json.dumps(out))
 
 
 def main():
@@ -278,7 +339,15 @@ def main():
     ap.add_argument("--sweep-only", default="", help="comma-separated workload names")
     ap.add_argument("--profile", metavar="WORKLOAD:T[:LAUNCHES]",
                     help="only run a few launches of one shape (for counter collection)")
+    ap.add_argument("--write-counters", nargs=3, metavar=("FETCH_DIR", "WRITE_DIR", "PROBE_BYTES"),
+                    help="no GPU: turn two rocprofv3 --pmc runs of --profile decode:1 "
+                         "(FETCH_SIZE, then WRITE_SIZE) into the committed traffic figures")
     args = ap.parse_args()
+
+    if args.write_counters:
+        write_counters(args.write_counters[0], args.write_counters[1],
+                       int(args.write_counters[2]))
+        return
 
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "

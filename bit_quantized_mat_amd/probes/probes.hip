@@ -3,7 +3,9 @@
 // bqm_probe_empty: a kernel that does nothing, for the fixed cost of one
 // dispatch. bqm_probe_read: streams a buffer once with 16-byte loads and
 // writes one dword per workgroup, for the HBM read rate that any kernel of the
-// same grid can reach on the same number of bytes.
+// same grid can reach on the same number of bytes. bqm_probe_copy: copies a
+// buffer with 16-byte loads and stores, a transfer of known size against which
+// the memory counters (bytes fetched from and written to HBM) are scaled.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -30,6 +32,14 @@ __global__ __launch_bounds__(256) void read_kernel(const uint4 *__restrict__ src
         out[blockIdx.x] = part[0] ^ part[1] ^ part[2] ^ part[3];
 }
 
+__global__ __launch_bounds__(256) void copy_kernel(const uint4 *__restrict__ src,
+                                                   uint4 *__restrict__ dst, uint64_t n16)
+{
+    const uint64_t stride = (uint64_t)gridDim.x * blockDim.x;
+    for (uint64_t i = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n16; i += stride)
+        dst[i] = src[i];
+}
+
 }  // namespace
 
 extern "C" {
@@ -49,6 +59,18 @@ __attribute__((visibility("default"))) int bqm_probe_read(const void *buf, uint6
         return -2;
     hipLaunchKernelGGL(read_kernel, dim3(grid), dim3(256), 0, (hipStream_t)stream,
                        (const uint4 *)buf, bytes / 16, out);
+    return hipGetLastError() == hipSuccess ? 0 : -5;
+}
+
+// src, dst: device buffers of `bytes` bytes each (a multiple of 16, 16-byte
+// aligned, not overlapping).
+__attribute__((visibility("default"))) int bqm_probe_copy(const void *src, void *dst,
+                                                          uint64_t bytes, int grid, void *stream)
+{
+    if (!src || !dst || grid < 1 || bytes % 16 != 0 || (((uintptr_t)src | (uintptr_t)dst) & 15u))
+        return -2;
+    hipLaunchKernelGGL(copy_kernel, dim3(grid), dim3(256), 0, (hipStream_t)stream,
+                       (const uint4 *)src, (uint4 *)dst, bytes / 16);
     return hipGetLastError() == hipSuccess ? 0 : -5;
 }
 
