@@ -42,10 +42,11 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-# Sources the decode mat-vec (the staged kernel) is compiled from: counter
-# readings taken on other sources do not describe it.
-DOMINANT_KERNEL_SOURCES = ("common.hpp", "tq1_decode.hpp", "mmvq_staged.hpp", "mmvq_staged.hip",
-                           "launch.hpp", "bqm_api.hip")
+# Sources the decode step's kernel (the staged kernel, fused with the Q8_1
+# quantization) is compiled from: counter readings taken on other sources do
+# not describe it.
+DOMINANT_KERNEL_SOURCES = ("common.hpp", "q8_1.hpp", "tq1_decode.hpp", "mmvq_staged.hpp",
+                           "mmvq_staged.hip", "launch.hpp", "bqm_api.hip")
 
 
 def kernel_source_hash():
@@ -76,6 +77,13 @@ def moe_algorithmic_bytes(ids, N, K):
 
 def quantize_bytes(T, K):
     return T * K * 4 + T * (K // 32) * 36
+
+
+def fused_bytes(N, K, T):
+    """Bytes the fused quantize-and-multiply call must move at minimum: the
+    packed weights, the fp32 activations and the fp32 outputs, once each
+    (the Q8_1 blocks never leave the chip)."""
+    return N * (K // 256) * 54 + T * K * 4 + T * N * 4
 
 
 def traffic_from_counters(N, K, T):
@@ -170,6 +178,27 @@ def calibrate(torch, np, wrot, R, nbytes, grid_wg):
     return {k: (round(v, 4) if isinstance(v, float) else v) for k, v in cal.items()}
 
 
+def read_probe_row(torch, wrot, R, nbytes, name, launches):
+    """A plain streaming read of one weight copy (what any kernel reading
+    the same bytes from HBM can reach), best of a few grid sizes."""
+    probes = ctypes.CDLL(os.path.join(ROOT, "bit_quantized_mat_amd", "libbqm_probes.so"))
+    probes.bqm_probe_read.argtypes = [ctypes.c_void_p, ctypes.c_uint64, ctypes.c_void_p,
+                                      ctypes.c_int, ctypes.c_void_p]
+    pout = torch.empty(8192, dtype=torch.int32, device=wrot.device)
+    rd = nbytes - nbytes % 16
+    cur = lambda: ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    best = None
+    for g in (1024, 2048, 4096, 8192):
+        us = graph_us(torch, lambda i: probes.bqm_probe_read(
+            ctypes.c_void_p(wrot[i % R].data_ptr()), rd, ctypes.c_void_p(pout.data_ptr()), g,
+            cur()), launches)
+        if best is None or us < best[0]:
+            best = (us, g)
+    return {"workload": name, "op": "read_probe", "bytes": int(rd), "grid_wg": best[1],
+            "us": round(best[0], 3), "gbs": round(rd / best[0] / 1e3, 1),
+            "frac_of_8tbs": round(rd / best[0] / 1e3 / HBM_PEAK_GBS, 4)}
+
+
 def sweep(path, torch, np, bqm, synth, dev, launches, only=None):
     """Every workload shape and column count, cold weights, graph-timed.
     only: optional set of workload names to restrict the sweep to."""
@@ -184,6 +213,8 @@ def sweep(path, torch, np, bqm, synth, dev, launches, only=None):
                           torch.from_numpy(inp.d16.view(np.int16)).to(dev))
         wrot, R = rotation(torch, w0, dev)
         a_all = bqm.q8_1_quantize(torch.from_numpy(inp.x).to(dev))
+        table.append(read_probe_row(torch, wrot, R, w0.numel(), name, launches))
+        log("sweep", table[-1])
         for T in wl.Ts:
             a = a_all[:T].contiguous()
             y = torch.empty((T, N), dtype=torch.float32, device=dev)
@@ -208,6 +239,8 @@ def sweep(path, torch, np, bqm, synth, dev, launches, only=None):
                       torch.from_numpy(inp.d16.view(np.int16)).to(dev))
     wrot, R = rotation(torch, w0, dev)
     a_all = bqm.q8_1_quantize(torch.from_numpy(inp.x).to(dev))
+    table.append(read_probe_row(torch, wrot, R, w0.numel(), "moe (all experts)", launches))
+    log("sweep", table[-1])
     for T in wl.Ts:
         ids_np = np.ascontiguousarray(inp.ids[:T])
         ids = torch.from_numpy(ids_np).to(dev)
@@ -255,6 +288,12 @@ def profile_run(spec, torch, np, bqm, synth, dev):
     for i in range(launches):
         run(i)
     torch.cuda.synchronize()
+    if not wl.experts and T <= bqm.MMVQ_F32_MAX_COLS:
+        # the fused quantize-and-multiply kernel on the same shapes
+        x = torch.from_numpy(inp.x[:T]).to(dev)
+        for i in range(launches):
+            bqm.mmvq_tq1_0_f32(wrot[(i + 5) % R], x, N, K, T, out=y)
+        torch.cuda.synchronize()
     probes = ctypes.CDLL(os.path.join(ROOT, "bit_quantized_mat_amd", "libbqm_probes.so"))
     probes.bqm_probe_read.argtypes = [ctypes.c_void_p, ctypes.c_uint64, ctypes.c_void_p,
                                       ctypes.c_int, ctypes.c_void_p]
@@ -270,7 +309,7 @@ def profile_run(spec, torch, np, bqm, synth, dev):
     # the copies are all equal, so copying one onto another changes nothing
     for i in range(launches):
         probes.bqm_probe_copy(ctypes.c_void_p(wrot[(i + 2) % R].data_ptr()),
-                              ctypes.c_void_p(wrot[(i + R // 2) % R].data_ptr()), nbytes, 1024,
+                              ctypes.c_void_p(wrot[(i + 3) % R].data_ptr()), nbytes, 1024,
                               stream)
     torch.cuda.synchronize()
     print(json.dumps({"profile": name, "N": N, "K": K, "T": T, "launches": launches,
@@ -293,6 +332,7 @@ def _counter_medians(csv_dir, counter):
                 name = r["Kernel_Name"]
                 fam = ("copy_probe" if "copy_kernel" in name else
                        "read_probe" if "read_kernel" in name else
+                       "fused" if "mmvq_staged_kernel<1, false, true>" in name else
                        "mmvq" if "mmvq" in name else None)
                 if fam:
                     vals.setdefault(fam, []).append(float(r["Counter_Value"]))
@@ -300,25 +340,27 @@ def _counter_medians(csv_dir, counter):
 
 
 def write_counters(fetch_dir, write_dir, probe_bytes):
-    """HBM bytes per mat-vec launch from two counter runs of `--profile
-    decode:1`: FETCH_SIZE and WRITE_SIZE (KiB per dispatch) of the mat-vec,
-    each scaled by bytes moved / counter reading of the copy probe, which
-    reads and writes probe_bytes bytes."""
+    """HBM bytes per launch of the decode step's kernel (the fused quantize
+    and mat-vec) from two counter runs of `--profile decode:1`: FETCH_SIZE and
+    WRITE_SIZE (KiB per dispatch), each scaled by bytes moved / counter
+    reading of the copy probe, which reads and writes probe_bytes bytes."""
     f = _counter_medians(fetch_dir, "FETCH_SIZE")
     w = _counter_medians(write_dir, "WRITE_SIZE")
     fetch_scale = probe_bytes / f["copy_probe"]
     write_scale = probe_bytes / w["copy_probe"]
     wl_N, wl_K = 4096, 4096
     out = {"kernel_source_hash": kernel_source_hash(), "shape": [wl_N, wl_K, 1],
-           "fetch_size_kib": f["mmvq"], "write_size_kib": w["mmvq"],
+           "kernel": "mmvq_staged_kernel<1, false, true> (mmvq_tq1_0_f32)",
+           "fetch_size_kib": f["fused"], "write_size_kib": w["fused"],
            "copy_probe_bytes": probe_bytes, "copy_probe_fetch_kib": f["copy_probe"],
            "copy_probe_write_kib": w["copy_probe"],
            "read_probe_fetch_kib": f.get("read_probe"),
+           "plain_mmvq_fetch_kib": f.get("mmvq"), "plain_mmvq_write_kib": w.get("mmvq"),
            "fetch_bytes_per_kib": round(fetch_scale, 3), "write_bytes_per_kib": round(write_scale, 3),
-           "hbm_fetch_bytes_per_launch": round(f["mmvq"] * fetch_scale),
-           "hbm_write_bytes_per_launch": round(w["mmvq"] * write_scale)}
+           "hbm_fetch_bytes_per_launch": round(f["fused"] * fetch_scale),
+           "hbm_write_bytes_per_launch": round(w["fused"] * write_scale)}
     out["hbm_bytes_per_launch"] = out["hbm_fetch_bytes_per_launch"] + out["hbm_write_bytes_per_launch"]
-    out["algorithmic_bytes_per_launch"] = algorithmic_bytes(wl_N, wl_K, 1)
+    out["algorithmic_bytes_per_launch"] = fused_bytes(wl_N, wl_K, 1)
     with open(COUNTERS_FILE, "w") as fh:
         json.dump(out, fh, indent=1)
         fh.write("\n")
@@ -380,9 +422,10 @@ def main():
     torch.cuda.synchronize()
     log("rotation: %d copies of %d bytes (%.2f GiB)" % (R, wbytes, R * wbytes / 2**30))
 
+    # one step of the hot path: quantize the fp32 column and multiply, fused
+    # into one launch (bitwise the same result as the two calls)
     def step(i):
-        bqm.q8_1_quantize(x, out=a)
-        bqm.mmvq_tq1_0(wrot[i % R], a, N, K, T, out=y)
+        bqm.mmvq_tq1_0_f32(wrot[i % R], x, N, K, T, out=y)
 
     for i in range(args.warmup):
         step(i)
@@ -395,21 +438,27 @@ def main():
 
     # timed region: the K steps as one graph
     step_us = graph_us(torch, lambda i: step(args.warmup + i), args.steps)
-    # dominant kernel: the mat-vec alone, graph of launches on rotating weights
-    us_call = graph_us(torch, lambda i: bqm.mmvq_tq1_0(wrot[(7 * i) % R], a, N, K, T, out=y),
+    # dominant kernel (the fused one): a graph of launches on rotating weights
+    us_call = graph_us(torch, lambda i: bqm.mmvq_tq1_0_f32(wrot[(7 * i) % R], x, N, K, T, out=y),
+                       args.kernel_launches)
+    # for comparison: the same step as two calls, and each call alone
+    two_call_us = graph_us(torch, lambda i: (bqm.q8_1_quantize(x, out=a),
+                                             bqm.mmvq_tq1_0(wrot[(7 * i) % R], a, N, K, T, out=y)),
+                           args.kernel_launches)
+    mmvq_us = graph_us(torch, lambda i: bqm.mmvq_tq1_0(wrot[(7 * i) % R], a, N, K, T, out=y),
                        args.kernel_launches)
     quant_us = graph_us(torch, lambda i: bqm.q8_1_quantize(x, out=a), 200)
     grid_wg = -(-N // (4 * (64 >> lanes_per_row_log2(K // 256))))
     cal = calibrate(torch, np, wrot, R, wbytes, grid_wg)
     log("calibration:", cal)
 
-    mm_bytes = algorithmic_bytes(N, K, T)
-    step_bytes = mm_bytes + quantize_bytes(T, K)
-    achieved = mm_bytes / us_call / 1e3
+    step_bytes = fused_bytes(N, K, T)
+    achieved = step_bytes / us_call / 1e3
     value = step_bytes / step_us / 1e3
-    log("mmvq: %.3f us per call (graph of %d), %.1f GB/s = %.2f%% of %.0f GB/s; quantize %.3f us"
-        % (us_call, args.kernel_launches, achieved, 100 * achieved / HBM_PEAK_GBS, HBM_PEAK_GBS,
-           quant_us))
+    log("fused quantize + mat-vec: %.3f us per call (graph of %d), %.1f GB/s = %.2f%% of %.0f GB/s"
+        % (us_call, args.kernel_launches, achieved, 100 * achieved / HBM_PEAK_GBS, HBM_PEAK_GBS))
+    log("two calls: %.3f us (quantize %.3f us, mat-vec %.3f us = %.1f GB/s)"
+        % (two_call_us, quant_us, mmvq_us, algorithmic_bytes(N, K, T) / mmvq_us / 1e3))
     log("step: %.3f us graph-replayed, %.3f us eager" % (step_us, eager_us))
 
     table = None
@@ -437,18 +486,21 @@ def main():
         "vs_baseline": None,
         "dtype": "i8",
         "data": "synthetic",
-        "config": {"workload": "decode mat-vec TQ1_0 N=4096 K=4096 T=1 (Q8_1 quantize + mat-vec "
-                               "per step)",
+        "config": {"workload": "decode mat-vec TQ1_0 N=4096 K=4096 T=1 (fp32 column quantized to "
+                               "Q8_1 and multiplied, one fused launch per step)",
                    "N": N, "K": K, "T": T, "weight_rotation_bytes": int(R * wbytes),
                    "timed": "HIP graph of all steps, replayed once after a warm replay"},
         "us_per_call": round(us_call, 4),
-        "mmvq_gbs": round(achieved, 2),
+        "two_call_step_us": round(two_call_us, 4),
+        "mmvq_us": round(mmvq_us, 4),
+        "mmvq_gbs": round(algorithmic_bytes(N, K, T) / mmvq_us / 1e3, 2),
         "quantize_us": round(quant_us, 4),
         "us_per_step_eager": round(eager_us, 4),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": traffic_from_counters(N, K, T), "kernel": "mmvq_tq1_0",
-                     "algorithmic_bytes_per_launch": mm_bytes},
+                     "traffic": traffic_from_counters(N, K, T),
+                     "kernel": "mmvq_tq1_0_f32 (mmvq_staged_kernel<1, false, true>)",
+                     "algorithmic_bytes_per_launch": step_bytes},
         "calibration": cal,
         "cpu_baseline": base,
     }

@@ -11,6 +11,7 @@ import os
 
 __all__ = [
     "BqmError", "library", "library_path", "tq1_pack", "q8_1_quantize", "mmvq_tq1_0",
+    "mmvq_tq1_0_f32", "MMVQ_F32_MAX_COLS",
     "mmvq_id_tq1_0", "mmvq_id_tq1_0_workspace_bytes", "mmvq_tq1_0_block_isums",
     "TQ1_BLOCK_BYTES", "Q81_BLOCK_BYTES", "MMVQ_MAX_COLS",
 ]
@@ -18,6 +19,7 @@ __all__ = [
 TQ1_BLOCK_BYTES = 54
 Q81_BLOCK_BYTES = 36
 MMVQ_MAX_COLS = 32
+MMVQ_F32_MAX_COLS = 8
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _lib = None
@@ -50,6 +52,7 @@ def library():
         L.tq1_pack.argtypes = [_p, _p, _p, _i64, _i64, _p]
         L.q8_1_quantize.argtypes = [_p, _p, _i64, _i64, _p]
         L.mmvq_tq1_0.argtypes = [_p, _p, _p, _i64, _i64, _i32, _p]
+        L.mmvq_tq1_0_f32.argtypes = [_p, _p, _p, _i64, _i64, _i32, _p]
         L.mmvq_tq1_0_block_isums.argtypes = [_p, _p, _p, _i64, _i64, _i32, _p]
         L.mmvq_id_tq1_0.argtypes = [_p, _p, _p, _p, _i64, _i64, _i64, _i64, _i32, _p, _sz, _p]
         L.mmvq_id_tq1_0_workspace_bytes.argtypes = [_i64, _i64, _i32]
@@ -57,8 +60,8 @@ def library():
         L.bqm_status_string.argtypes = [ctypes.c_int]
         L.bqm_status_string.restype = ctypes.c_char_p
         L.bqm_version.restype = ctypes.c_int
-        for name in ("tq1_pack", "q8_1_quantize", "mmvq_tq1_0", "mmvq_tq1_0_block_isums",
-                     "mmvq_id_tq1_0"):
+        for name in ("tq1_pack", "q8_1_quantize", "mmvq_tq1_0", "mmvq_tq1_0_f32",
+                     "mmvq_tq1_0_block_isums", "mmvq_id_tq1_0"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -140,6 +143,21 @@ def mmvq_tq1_0(w, a, N, K, T, out=None, stream=None):
         out = torch.empty((T, N), dtype=torch.float32, device=w.device)
     pw, pa = _mmvq_args(w, a, N, K, T)
     _call("mmvq_tq1_0", pw, pa, _dev_tensor(out, "out", (torch.float32,), T * N * 4, w.device),
+          N, K, T, _stream(stream, w.device))
+    return out
+
+
+def mmvq_tq1_0_f32(w, x, N, K, T, out=None, stream=None):
+    """y fp32 [T, N] = TQ1_0 weights [N, K] times T fp32 activation columns
+    x [T, K], quantized to Q8_1 inside the call (bitwise q8_1_quantize then
+    mmvq_tq1_0); T <= 8."""
+    torch = _torch()
+    if out is None:
+        out = torch.empty((T, N), dtype=torch.float32, device=w.device)
+    _call("mmvq_tq1_0_f32",
+          _dev_tensor(w, "w", (torch.uint8,), N * (K // 256) * TQ1_BLOCK_BYTES),
+          _dev_tensor(x, "x", (torch.float32,), T * K * 4, w.device),
+          _dev_tensor(out, "out", (torch.float32,), T * N * 4, w.device),
           N, K, T, _stream(stream, w.device))
     return out
 

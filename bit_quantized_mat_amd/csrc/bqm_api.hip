@@ -92,6 +92,24 @@ int mmvq_tq1_0(const void *w, const void *a, float *y, int64_t N, int64_t K, int
     return bqm::launch_mmvq(w, a, y, nullptr, N, K, T, as_stream(stream));
 }
 
+int mmvq_tq1_0_f32(const void *w, const float *x, float *y, int64_t N, int64_t K, int32_t T,
+                   void *stream)
+{
+    if (!w || !x || !y)
+        return BQM_ERR_NULL;
+    if (int rc = check_matrix(N, K))
+        return rc;
+    if (T < 1 || T > BQM_MMVQ_F32_MAX_COLS || (uint64_t)T * (uint64_t)K * 4ull > kMaxBufferBytes)
+        return BQM_ERR_SHAPE;
+    if (!aligned4(w) || !aligned4(x) || !aligned4(y))
+        return BQM_ERR_ALIGN;
+    if (int rc = check_device())
+        return rc;
+    if (!bqm::staged_supported(K, T))
+        return BQM_ERR_SHAPE;
+    return bqm::launch_mmvq_staged_f32(w, x, y, N, K, T, as_stream(stream));
+}
+
 int mmvq_tq1_0_block_isums(const void *w, const void *a, int32_t *isums, int64_t N, int64_t K,
                            int32_t T, void *stream)
 {

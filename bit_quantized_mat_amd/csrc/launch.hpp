@@ -15,6 +15,19 @@ inline int check_launch()
     return e == hipSuccess ? BQM_OK : BQM_ERR_LAUNCH;
 }
 
+// Dynamic LDS: 64 KiB is always available; beyond that the launcher raises
+// the kernel's limit up to what the device reports (160 KiB on gfx950).
+constexpr size_t kLdsDefault = 64 * 1024;
+constexpr size_t kLdsMax = 160 * 1024;
+
+// Raise a kernel's dynamic-LDS limit when a launch needs more than the
+// default (idempotent; the runtime keeps the attribute per function).
+inline void allow_dynamic_lds(const void *kernel, size_t bytes)
+{
+    if (bytes > kLdsDefault)
+        (void)hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+}
+
 int launch_q8_1_quantize(const float *x, void *a, int64_t T, int64_t K, hipStream_t stream);
 int launch_tq1_pack(const int8_t *trits, const uint16_t *d, void *w, int64_t N, int64_t K,
                     hipStream_t stream);
@@ -23,14 +36,32 @@ int launch_tq1_pack(const int8_t *trits, const uint16_t *d, void *w, int64_t N, 
 int lanes_per_row_log2(int64_t nb);
 // Dynamic LDS bytes a workgroup may use on the current device.
 size_t lds_budget();
+// Compute units of the current device.
+int compute_units();
+// Workgroups of `kernel` (with this block size and dynamic LDS) that the
+// current device runs at once.
+int resident_workgroups(const void *kernel, int threads, size_t lds);
 // Staged kernel (one to eight columns, activations staged in LDS): whether it
 // takes this shape, and its launcher.
 bool staged_supported(int64_t K, int32_t T);
 int launch_mmvq_staged(const void *w, const void *a, float *y, int32_t *isums, int64_t N,
                        int64_t K, int32_t T, hipStream_t stream);
-// Matrix-core kernel for 9 to 32 columns.
+// The staged kernel on fp32 activations, quantized to Q8_1 while staging.
+int launch_mmvq_staged_f32(const void *w, const float *x, float *y, int64_t N, int64_t K,
+                           int32_t T, hipStream_t stream);
+// Matrix-core kernel: any shape, 1 to 32 columns; the dispatcher gives it
+// every call of at least kMfmaMinCols columns and the calls whose activations
+// do not fit the staged kernel's LDS.
+constexpr int kMfmaMinCols = 5;
+
 int launch_mmvq_mfma(const void *w, const void *a, float *y, int32_t *isums, int64_t N,
                      int64_t K, int32_t T, hipStream_t stream);
+// Matrix-core kernel with all activation columns resident in LDS: whether it
+// takes this shape (the columns fit and a row has at least as many lane
+// groups as the workgroup has waves), and its launcher.
+bool mfma_resident_supported(int64_t K, int32_t T);
+int launch_mmvq_mfma_resident(const void *w, const void *a, float *y, int32_t *isums, int64_t N,
+                              int64_t K, int32_t T, hipStream_t stream);
 int launch_mmvq(const void *w, const void *a, float *y, int32_t *isums, int64_t N, int64_t K,
                 int32_t T, hipStream_t stream);
 int launch_mmvq_id(const void *w, const void *a, const int32_t *ids, float *y, int64_t E,

@@ -1,290 +1,361 @@
-// mmvq_mfma.hip -- TQ1_0 x Q8_1 product for 9 to 32 activation columns on
-// gfx950, with the integer sums on the matrix cores.
+// mmvq_mfma.hip -- TQ1_0 x Q8_1 product for many activation columns on
+// gfx950, with the integer sums on the matrix cores; activations streamed
+// through LDS one block at a time (any K).
 //
 // With many columns the product is a real contraction: per 32-element Q8_1
-// sub-block, a 16-row tile of weight trits times up to 16 activation columns
+// sub-block, a 16-row tile of weight digits times up to 16 activation columns
 // is exactly one v_mfma_i32_16x16x32_i8, whose int32 results are the exact
-// per-sub-block sums. The decoded trits of a 256-element block feed all
-// column tiles; the fp32 scaling uses the same order as the one-column
-// kernel, so a column's result does not depend on how many columns the call
-// carries (the exactness the multi-column kernel of "cuda: opt-in MMVQ
-// activation reuse across output rows" keeps against single-column calls).
+// per-sub-block sums. The decoded digits of a 256-element block feed all
+// column tiles; the fp32 scaling uses the same order as the staged kernels,
+// so a column's result does not depend on how many columns the call carries
+// (the exactness the multi-column kernel of "cuda: opt-in MMVQ activation
+// reuse across output rows" keeps against single-column calls).
 //
-// Operand layout of v_mfma_i32_16x16x32_i8 (K = 32 = one sub-block):
-//   A (weights): lane (r, kg) = (lane % 16, lane / 16) holds 8 trits of row r;
-//   B (activations): lane (c, kg) holds the 8 matching q bytes of column c;
-//   D: lane (c, rg) holds rows 4rg..4rg+3 of column c.
-// The eight K positions of lane group kg are, per sub-block b:
-//   b < 5: elements 8kg..8kg+7  (digit b of qs bytes 8kg..8kg+7),
-//   b = 5: elements 4kg..4kg+3 and 16+4kg..16+4kg+3 (digits 0, 1 of qs dword
-//          8+kg), b = 6 likewise with digits 2, 3, and b = 7: digit 4 of qs
-//          dword 8+kg, then digit kg of the qh dword (elements 16+4kg..),
-// so every lane decodes two qs dwords of the first 32 bytes, one of the next
-// 16 and the qh dword, and the activation operands are plain Q8_1 dwords.
+// (operand layouts and the digit decode: mfma_common.hpp)
+//
+// Activations: for each block it works on, a wave copies the block's Q8_1 data
+// of every column (8 x 36 bytes per column) into its own slice of LDS with
+// plain coalesced 8-byte loads, then reads each lane's 8-byte B operand and
+// the sub-block scale from there. Loading the operands straight from memory
+// instead would cost one scattered load per sub-block and column tile, each
+// touching 16 cache lines.
 //
 // Reduction order: a row's blocks are split into the same Lr lane groups as
 // in the staged kernel (block B belongs to group B mod Lr). Each wave of the
 // workgroup owns Lr / nw groups, accumulates each group's blocks in order,
 // and the groups are then combined by the same xor butterfly, first inside
 // the wave and then across waves through LDS.
-#include "launch.hpp"
-#include "tq1_decode.hpp"
+#include "mfma_common.hpp"
 
 namespace bqm {
 
-typedef int i32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x3 __attribute__((ext_vector_type(3)));
+constexpr int kMfmaMaxWaves = 8;     // waves per workgroup
+constexpr int kStageCol = 74;        // dwords per staged column: 8 x 9 of Q8_1 data, 2 of padding
 
-constexpr int kMfmaMaxWaves = 8;  // waves per workgroup
+// Block B of activation columns 0 .. 16 NT - 1, in flight to this wave's
+// stage: column c's eight Q8_1 blocks (288 bytes, 36 pieces of 8 bytes) go to
+// dwords c * kStageCol .. c * kStageCol + 71. A 16-column tile is 576 pieces,
+// nine per lane: piece i = lane + 64 k. The loads are issued one block ahead
+// and written to LDS once the stage is free.
+//
+// Columns at or past T are not masked: their loads fall past the end of the
+// activation buffer and read zeros, or (when the 32-bit offset wraps) some
+// in-range bytes, and either way they only feed output columns that are never
+// stored.
+struct StageMap {
+    uint32_t gofs[9];  // byte offset of piece k in block 0 of column tile 0
+    uint32_t lofs[9];  // its dword offset in the stage
 
-// This lane's share of one 54-byte block (see the layout above): qs dwords
-// 2kg and 2kg+1, qs dword 8+kg, the qh dword and the fp16 scale, read as the
-// aligned dwords that cover them and realigned (odd blocks of a row start two
-// bytes past a dword boundary).
-struct LaneBlock {
-    uint32_t lo0, lo1, hi, qh, dbits;
-};
-
-__device__ __forceinline__ LaneBlock load_lane_block(__amdgpu_buffer_rsrc_t rw, uint32_t off, int kg)
-{
-    const uint32_t sh = off & 3u, base = off - sh;
-    const u32x3 l = __builtin_amdgcn_raw_buffer_load_b96(rw, base + 8 * kg, 0, 0);
-    const u32x2 h = ld_b64(rw, base + 32 + 4 * kg);
-    const u32x2 t = ld_b64(rw, base + 48);
-    LaneBlock b;
-    b.lo0 = align_bytes(l.y, l.x, sh);
-    b.lo1 = align_bytes(l.z, l.y, sh);
-    b.hi = align_bytes(h.y, h.x, sh);
-    b.qh = align_bytes(t.y, t.x, sh);
-    b.dbits = sh ? (t.y >> 16) : (t.y & 0xffffu);
-    return b;
-}
-
-// Decoded weight operands of one lane for one 16-row tile and block: A[b] is
-// the 8-byte trit operand of sub-block b, dw the fp32 scale of the lane's row.
-struct TileOperands {
-    long A[8];
-    float dw;
-};
-
-__device__ __forceinline__ TileOperands decode_lane_block(const LaneBlock &lb, int kg)
-{
-    const QsTrits lo0 = qs_trits(lb.lo0);
-    const QsTrits lo1 = qs_trits(lb.lo1);
-    const QsTrits hi = qs_trits(lb.hi);
-    const QhTrits qh = qh_trits(lb.qh);
-    const uint32_t qhk = kg == 0 ? qh.T[0] : kg == 1 ? qh.T[1] : kg == 2 ? qh.T[2] : qh.T[3];
-    TileOperands t;
+    __device__ __forceinline__ StageMap(uint32_t col_bytes, int lane)
+    {
 #pragma unroll
-    for (int c = 0; c < 5; c++)
-        t.A[c] = (long)(((uint64_t)lo1.T[c] << 32) | lo0.T[c]);
-    t.A[5] = (long)(((uint64_t)hi.T[1] << 32) | hi.T[0]);
-    t.A[6] = (long)(((uint64_t)hi.T[3] << 32) | hi.T[2]);
-    t.A[7] = (long)(((uint64_t)qhk << 32) | hi.T[4]);
-    t.dw = f16_bits_to_f32(lb.dbits);
-    return t;
-}
+        for (int k = 0; k < 9; k++) {
+            const int i = lane + 64 * k;
+            const int c = i / 36, p = i - 36 * c;
+            gofs[k] = (uint32_t)c * col_bytes + 8 * p;
+            lofs[k] = c * kStageCol + 2 * p;
+        }
+    }
+};
+
+template <int NT>
+struct StagePieces {
+    u32x2 v[NT][9];
+
+    __device__ __forceinline__ void issue(__amdgpu_buffer_rsrc_t ra, const StageMap &m,
+                                          uint32_t col_bytes, int B)
+    {
+#pragma unroll
+        for (int ct = 0; ct < NT; ct++) {
+            // wave-uniform part of the offset
+            const uint32_t so = __builtin_amdgcn_readfirstlane(
+                (uint32_t)B * (8 * kQ81BlockBytes) + (uint32_t)ct * 16 * col_bytes);
+#pragma unroll
+            for (int k = 0; k < 9; k++)
+                v[ct][k] = __builtin_amdgcn_raw_buffer_load_b64(ra, m.gofs[k], so, 0);
+        }
+    }
+
+    __device__ __forceinline__ void land(uint32_t *__restrict__ stage, const StageMap &m) const
+    {
+#pragma unroll
+        for (int ct = 0; ct < NT; ct++)
+#pragma unroll
+            for (int k = 0; k < 9; k++)
+                *reinterpret_cast<u32x2 *>(stage + ct * 16 * kStageCol + m.lofs[k]) = v[ct][k];
+    }
+};
 
 // GPW: butterfly groups per wave (Lr / waves); NT: 16-column tiles (1 or 2);
-// R: 16-row tiles per workgroup, which share each block's activation
-// operands; ISUMS: write the exact per-sub-block sums instead of outputs.
+// R: 16-row tiles that share each staged activation block; ISUMS: write the
+// exact per-sub-block sums instead of outputs.
+//
+// The grid is sized to what the GPU holds at once and each workgroup walks
+// row tiles (16 R rows each) tile = blockIdx.x, + gridDim.x, ...; the one-block
+// lookahead runs across tile boundaries, so the next tile's first block is in
+// flight while the current tile finishes and reduces.
 template <int GPW, int NT, int R, bool ISUMS>
 __global__ __launch_bounds__(512) void mmvq_mfma_kernel(const uint8_t *__restrict__ w,
                                                         const uint8_t *__restrict__ a,
                                                         float *__restrict__ y,
                                                         int32_t *__restrict__ isums, int64_t N,
-                                                        int nb, int T, int lr_log2)
+                                                        int nb, int T, int lr_log2, int ntiles)
 {
-    extern __shared__ float red[];  // [waves][64][R * NT * 4]: cross-wave butterfly
+    // per wave: its staged activation block; after those, the cross-wave
+    // butterfly exchange
+    extern __shared__ uint32_t smem[];
     const int nw = blockDim.x >> 6;
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    // the wave index is uniform across the wave; saying so keeps the block
+    // loop, the activation offsets and the branches on scalar registers
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
     const int Lr = 1 << lr_log2;
     const int kg = lane >> 4;                   // decode lane: row lane % 16, K group kg
     const int col = lane & 15, rg = lane >> 4;  // output lane: column col, rows 4rg..4rg+3
-    const int64_t r0 = (int64_t)blockIdx.x * 16 * R;
     const int nblk = nb * 8;
-    const uint64_t col_bytes = (uint64_t)nblk * kQ81BlockBytes;
+    const uint32_t col_bytes = (uint32_t)nblk * kQ81BlockBytes;
     const __amdgpu_buffer_rsrc_t rw = make_rsrc(w, (uint64_t)N * nb * kTq1BlockBytes);
-    // columns past T read as zero (beyond the buffer's range)
     const __amdgpu_buffer_rsrc_t ra = make_rsrc(a, (uint64_t)T * col_bytes);
-    uint32_t row_off[R];
-#pragma unroll
-    for (int rt = 0; rt < R; rt++) {
-        const int64_t rowA = r0 + 16 * rt + (lane & 15);
-        row_off[rt] = (uint32_t)((rowA < N ? rowA : 0) * nb * kTq1BlockBytes);
-    }
+    uint32_t *stage = smem + wave * (NT * 16 * kStageCol);
+    float *red = reinterpret_cast<float *>(smem + nw * (NT * 16 * kStageCol));
+    const StageMap smap(col_bytes, lane);
 
-    float acc[GPW][R][NT][4];
+    // byte offsets of this decode lane's rows in tile t (rows past N read row 0)
+    auto tile_rows = [&](int t, uint32_t (&ro)[R]) {
 #pragma unroll
-    for (int gi = 0; gi < GPW; gi++)
+        for (int rt = 0; rt < R; rt++) {
+            const int64_t rowA = (int64_t)t * 16 * R + 16 * rt + (lane & 15);
+            ro[rt] = (uint32_t)((rowA < N ? rowA : 0) * nb * kTq1BlockBytes);
+        }
+    };
+
+    int tile = blockIdx.x;
+    uint32_t row_off[R];
+    tile_rows(tile, row_off);
+    // one block of lookahead: while block B is decoded and multiplied, the
+    // weights and activations of the wave's next block are in flight
+    LaneBlock lb[R];
+    StagePieces<NT> pieces;
+    if (tile < ntiles && wave < nb) {
 #pragma unroll
         for (int rt = 0; rt < R; rt++)
-#pragma unroll
-            for (int ct = 0; ct < NT; ct++)
-#pragma unroll
-                for (int i = 0; i < 4; i++)
-                    acc[gi][rt][ct][i] = 0.0f;
+            lb[rt] = load_lane_block(rw, row_off[rt] + (uint32_t)wave * kTq1BlockBytes, kg);
+        pieces.issue(ra, smap, col_bytes, wave);
+        pieces.land(stage, smap);
+        wave_lds_order();
+    }
 
+    for (; tile < ntiles; tile += gridDim.x) {
+        const int64_t r0 = (int64_t)tile * 16 * R;
+        const int next_tile = tile + gridDim.x;
+        uint32_t next_off[R];
+        tile_rows(next_tile, next_off);
+
+        float acc[GPW][R][NT][4];
 #pragma unroll
-    for (int gi = 0; gi < GPW; gi++) {
-        const int g = wave + nw * gi;
-        for (int B = g; B < nb; B += Lr) {
-            // weights of all row tiles first (HBM), then the activations (L2)
-            LaneBlock lb[R];
+        for (int gi = 0; gi < GPW; gi++)
 #pragma unroll
             for (int rt = 0; rt < R; rt++)
-                lb[rt] = load_lane_block(rw, row_off[rt] + (uint32_t)B * kTq1BlockBytes, kg);
-            long Bq[NT][8];
-            float da[NT][8];
 #pragma unroll
-            for (int ct = 0; ct < NT; ct++) {
-                const uint32_t cbase = (uint32_t)((uint64_t)(ct * 16 + col) * col_bytes) +
-                                       (uint32_t)(8 * B) * kQ81BlockBytes;
+                for (int ct = 0; ct < NT; ct++)
 #pragma unroll
-                for (int b = 0; b < 8; b++) {
-                    const uint32_t o = cbase + b * kQ81BlockBytes;
-                    uint32_t q0, q1;
-                    if (b < 5) {
-                        const u32x2 v = ld_b64(ra, o + 8 * kg);
-                        q0 = v.x;
-                        q1 = v.y;
-                    } else {
-                        q0 = ld_b32(ra, o + 4 * kg);
-                        q1 = ld_b32(ra, o + 16 + 4 * kg);
-                    }
-                    Bq[ct][b] = (long)(((uint64_t)q1 << 32) | q0);
-                    da[ct][b] = f16_bits_to_f32(ld_b32(ra, o + 32) & 0xffffu);
+                    for (int i = 0; i < 4; i++)
+                        acc[gi][rt][ct][i] = 0.0f;
+
+#pragma unroll
+        for (int gi = 0; gi < GPW; gi++) {
+            const int g = wave + nw * gi;
+            for (int B = g; B < nb; B += Lr) {
+                // the wave's next block: the group's next one, else the next
+                // group's first, else the first block of the next tile
+                const bool same_tile = B + Lr < nb || (gi + 1 < GPW && g + nw < nb);
+                const int Bn = B + Lr < nb ? B + Lr : (same_tile ? g + nw : wave);
+                const bool have_next = same_tile || next_tile < ntiles;
+                LaneBlock ln[R];
+                if (have_next) {
+#pragma unroll
+                    for (int rt = 0; rt < R; rt++)
+                        ln[rt] = load_lane_block(
+                            rw, (same_tile ? row_off[rt] : next_off[rt]) + (uint32_t)Bn * kTq1BlockBytes,
+                            kg);
+                    pieces.issue(ra, smap, col_bytes, Bn);
                 }
-            }
+
+                // one row tile at a time: its digit operands meet every
+                // sub-block and column tile of the staged activations (re-read
+                // from LDS per row tile, which keeps one tile's operands in
+                // registers)
 #pragma unroll
-            for (int rt = 0; rt < R; rt++) {
-                const TileOperands op = decode_lane_block(lb[rt], kg);
-                // block scales of the four rows this output lane holds
-                float dw[4];
+                for (int rt = 0; rt < R; rt++) {
+                    const TileOperands op = decode_lane_block(lb[rt], kg);
+                    float dw[4];  // block scales of the four rows this output lane holds
 #pragma unroll
-                for (int i = 0; i < 4; i++)
-                    dw[i] = __shfl(op.dw, 4 * rg + i, 64);
+                    for (int i = 0; i < 4; i++)
+                        dw[i] = __shfl(op.dw, 4 * rg + i, 64);
+                    float s[NT][4];
 #pragma unroll
-                for (int ct = 0; ct < NT; ct++) {
-                    i32x4 C[8];
+                    for (int b = 0; b < 8; b++) {
 #pragma unroll
-                    for (int b = 0; b < 8; b++)
-                        C[b] = __builtin_amdgcn_mfma_i32_16x16x32_i8(op.A[b], Bq[ct][b],
-                                                                      (i32x4){0, 0, 0, 0}, 0, 0, 0);
-                    const int c = ct * 16 + col;
-                    if (ISUMS) {
+                        for (int ct = 0; ct < NT; ct++) {
+                            const uint32_t *cs = stage + (ct * 16 + col) * kStageCol + 9 * b;
+                            const uint32_t q0 = b < 5 ? cs[2 * kg] : cs[kg];
+                            const uint32_t q1 = b < 5 ? cs[2 * kg + 1] : cs[4 + kg];
+                            const long Bq = (long)(((uint64_t)q1 << 32) | q0);
+                            // -sum(q) of this lane's column on every row, then + sum(u q)
+                            const i32x4 neg_sum = __builtin_amdgcn_mfma_i32_16x16x32_i8(
+                                kAllMinusOne, Bq, (i32x4){0, 0, 0, 0}, 0, 0, 0);
+                            const i32x4 C = __builtin_amdgcn_mfma_i32_16x16x32_i8(op.A[b], Bq,
+                                                                                  neg_sum, 0, 0, 0);
+                            if (ISUMS) {
+                                const int c = ct * 16 + col;
 #pragma unroll
-                        for (int i = 0; i < 4; i++) {
-                            const int64_t row = r0 + 16 * rt + 4 * rg + i;
-                            if (c < T && row < N) {
-                                int32_t *dst = isums + ((int64_t)c * N + row) * nblk + 8 * B;
+                                for (int i = 0; i < 4; i++) {
+                                    const int64_t row = r0 + 16 * rt + 4 * rg + i;
+                                    if (c < T && row < N)
+                                        isums[((int64_t)c * N + row) * nblk + 8 * B + b] = C[i];
+                                }
+                            } else {
+                                // the staged kernels' fp32 order: s = sum_b da[b] * isum[b]
+                                // from b = 0 up, then acc + dw * s
+                                const float da = f16_bits_to_f32(cs[8] & 0xffffu);
 #pragma unroll
-                                for (int b = 0; b < 8; b++)
-                                    dst[b] = C[b][i];
+                                for (int i = 0; i < 4; i++)
+                                    s[ct][i] = b == 0 ? da * (float)C[i]
+                                                      : fmaf(da, (float)C[i], s[ct][i]);
                             }
                         }
-                    } else {
-                        // the one-column kernel's fp32 order: s = sum_b da[b] * isum[b]
-                        // from b = 0 up, then acc + dw * s
-#pragma unroll
-                        for (int i = 0; i < 4; i++) {
-                            float sum = da[ct][0] * (float)C[0][i];
-#pragma unroll
-                            for (int b = 1; b < 8; b++)
-                                sum = fmaf(da[ct][b], (float)C[b][i], sum);
-                            acc[gi][rt][ct][i] = fmaf(dw[i], sum, acc[gi][rt][ct][i]);
-                        }
                     }
+                    if (!ISUMS) {
+#pragma unroll
+                        for (int ct = 0; ct < NT; ct++)
+#pragma unroll
+                            for (int i = 0; i < 4; i++)
+                                acc[gi][rt][ct][i] = fmaf(dw[i], s[ct][i], acc[gi][rt][ct][i]);
+                    }
+                }
+                if (have_next) {
+                    wave_lds_order();  // this block's operand reads come first
+                    pieces.land(stage, smap);
+                    wave_lds_order();
+#pragma unroll
+                    for (int rt = 0; rt < R; rt++)
+                        lb[rt] = ln[rt];
                 }
             }
         }
-    }
-    if (ISUMS)
-        return;
 
-    // butterfly over the Lr groups: first the levels that pair groups held by
-    // this wave (group g = wave + nw * gi; the partner differs in gi), then
-    // the levels across waves through LDS. Each side forms mine + partner, so
-    // every group ends with the same value.
+        if (!ISUMS) {
+            // butterfly over the Lr groups: first the levels that pair groups
+            // held by this wave (group g = wave + nw * gi; the partner differs
+            // in gi), then the levels across waves through LDS. Each side
+            // forms mine + partner, so every group ends with the same value.
 #pragma unroll
-    for (int m = GPW >> 1; m >= 1; m >>= 1) {
-        float nxt[GPW][R][NT][4];
+            for (int m = GPW >> 1; m >= 1; m >>= 1) {
+                float nxt[GPW][R][NT][4];
 #pragma unroll
-        for (int gi = 0; gi < GPW; gi++)
+                for (int gi = 0; gi < GPW; gi++)
 #pragma unroll
-            for (int rt = 0; rt < R; rt++)
+                    for (int rt = 0; rt < R; rt++)
 #pragma unroll
-                for (int ct = 0; ct < NT; ct++)
+                        for (int ct = 0; ct < NT; ct++)
 #pragma unroll
-                    for (int i = 0; i < 4; i++)
-                        nxt[gi][rt][ct][i] = acc[gi][rt][ct][i] + acc[gi ^ m][rt][ct][i];
+                            for (int i = 0; i < 4; i++)
+                                nxt[gi][rt][ct][i] = acc[gi][rt][ct][i] + acc[gi ^ m][rt][ct][i];
 #pragma unroll
-        for (int gi = 0; gi < GPW; gi++)
+                for (int gi = 0; gi < GPW; gi++)
 #pragma unroll
-            for (int rt = 0; rt < R; rt++)
+                    for (int rt = 0; rt < R; rt++)
 #pragma unroll
-                for (int ct = 0; ct < NT; ct++)
+                        for (int ct = 0; ct < NT; ct++)
 #pragma unroll
-                    for (int i = 0; i < 4; i++)
-                        acc[gi][rt][ct][i] = nxt[gi][rt][ct][i];
-    }
-    constexpr int kPer = R * NT * 4;
-    float *mine = red + ((size_t)wave * 64 + lane) * kPer;
-    for (int m = nw >> 1; m >= 1; m >>= 1) {
-#pragma unroll
-        for (int rt = 0; rt < R; rt++)
-#pragma unroll
-            for (int ct = 0; ct < NT; ct++)
-#pragma unroll
-                for (int i = 0; i < 4; i++)
-                    mine[(rt * NT + ct) * 4 + i] = acc[0][rt][ct][i];
-        __syncthreads();
-        const float *other = red + ((size_t)(wave ^ m) * 64 + lane) * kPer;
-#pragma unroll
-        for (int rt = 0; rt < R; rt++)
-#pragma unroll
-            for (int ct = 0; ct < NT; ct++)
-#pragma unroll
-                for (int i = 0; i < 4; i++)
-                    acc[0][rt][ct][i] = acc[0][rt][ct][i] + other[(rt * NT + ct) * 4 + i];
-        __syncthreads();
-    }
-    if (wave == 0) {
-#pragma unroll
-        for (int rt = 0; rt < R; rt++)
-#pragma unroll
-            for (int ct = 0; ct < NT; ct++) {
-                const int c = ct * 16 + col;
-                if (c < T) {
-#pragma unroll
-                    for (int i = 0; i < 4; i++) {
-                        const int64_t row = r0 + 16 * rt + 4 * rg + i;
-                        if (row < N)
-                            y[(int64_t)c * N + row] = acc[0][rt][ct][i];
-                    }
-                }
+                            for (int i = 0; i < 4; i++)
+                                acc[gi][rt][ct][i] = nxt[gi][rt][ct][i];
             }
+            constexpr int kPer = R * NT * 4;
+            float *mine = red + ((size_t)wave * 64 + lane) * kPer;
+            for (int m = nw >> 1; m >= 1; m >>= 1) {
+                __syncthreads();  // the previous level's (or tile's) reads are done
+#pragma unroll
+                for (int rt = 0; rt < R; rt++)
+#pragma unroll
+                    for (int ct = 0; ct < NT; ct++)
+#pragma unroll
+                        for (int i = 0; i < 4; i++)
+                            mine[(rt * NT + ct) * 4 + i] = acc[0][rt][ct][i];
+                __syncthreads();
+                const float *other = red + ((size_t)(wave ^ m) * 64 + lane) * kPer;
+#pragma unroll
+                for (int rt = 0; rt < R; rt++)
+#pragma unroll
+                    for (int ct = 0; ct < NT; ct++)
+#pragma unroll
+                        for (int i = 0; i < 4; i++)
+                            acc[0][rt][ct][i] = acc[0][rt][ct][i] + other[(rt * NT + ct) * 4 + i];
+            }
+            if (wave == 0) {
+#pragma unroll
+                for (int rt = 0; rt < R; rt++)
+#pragma unroll
+                    for (int ct = 0; ct < NT; ct++) {
+                        const int c = ct * 16 + col;
+                        if (c < T) {
+#pragma unroll
+                            for (int i = 0; i < 4; i++) {
+                                const int64_t row = r0 + 16 * rt + 4 * rg + i;
+                                if (row < N)
+                                    y[(int64_t)c * N + row] = acc[0][rt][ct][i];
+                            }
+                        }
+                    }
+            }
+        }
+#pragma unroll
+        for (int rt = 0; rt < R; rt++)
+            row_off[rt] = next_off[rt];
     }
+}
+
+template <int GPW, int NT, int R>
+static void launch_mfma_r(const uint8_t *w, const uint8_t *a, float *y, int32_t *isums,
+                          int64_t N, int nb, int T, int lr, int nw, hipStream_t stream)
+{
+    const int64_t ntiles = (N + 16 * R - 1) / (16 * R);
+    const size_t stage = (size_t)nw * NT * 16 * kStageCol * sizeof(uint32_t);
+    const size_t exchange = (size_t)nw * 64 * R * NT * 4 * sizeof(float);
+    const size_t lds = stage + exchange;
+    const void *kt = reinterpret_cast<const void *>(&mmvq_mfma_kernel<GPW, NT, R, true>);
+    const void *kf = reinterpret_cast<const void *>(&mmvq_mfma_kernel<GPW, NT, R, false>);
+    allow_dynamic_lds(kt, lds);
+    allow_dynamic_lds(kf, lds);
+    // as many workgroups as are resident at once, each taking the same number
+    // of tiles (give or take one)
+    const int cap = resident_workgroups(isums ? kt : kf, 64 * nw, lds);
+    const int64_t per = (ntiles + cap - 1) / cap;
+    const dim3 grid((unsigned)((ntiles + per - 1) / per));
+    if (isums)
+        hipLaunchKernelGGL((mmvq_mfma_kernel<GPW, NT, R, true>), grid, dim3(64 * nw), lds,
+                           stream, w, a, nullptr, isums, N, nb, T, lr, (int)ntiles);
+    else
+        hipLaunchKernelGGL((mmvq_mfma_kernel<GPW, NT, R, false>), grid, dim3(64 * nw), lds,
+                           stream, w, a, y, nullptr, N, nb, T, lr, (int)ntiles);
 }
 
 template <int GPW, int NT>
 static void launch_mfma_gn(const uint8_t *w, const uint8_t *a, float *y, int32_t *isums,
                            int64_t N, int nb, int T, int lr, int nw, hipStream_t stream)
 {
-    // row tiles sharing each block's activation operands: as many as keep the
-    // wave's accumulators (GPW * R * NT sets of four) within eight sets and
-    // the activation operands plus accumulators within the register file
-    constexpr int Rcap = NT == 1 ? 4 : 2;
+    // R, the row tiles sharing each staged activation block: at most what
+    // keeps the wave's accumulators (GPW * R * NT sets of four) within eight
+    // sets and the digit operands within the register file; within that, the
+    // most that still gives every compute unit two tiles.
+    constexpr int Rcap = NT == 1 ? 2 : 1;
     constexpr int Racc = GPW * NT >= 8 ? 1 : 8 / (GPW * NT);
-    constexpr int R = Racc < Rcap ? Racc : Rcap;
-    const dim3 grid((unsigned)((N + 16 * R - 1) / (16 * R)));
-    const size_t lds = (size_t)nw * 64 * R * NT * 4 * sizeof(float);
-    if (isums)
-        hipLaunchKernelGGL((mmvq_mfma_kernel<GPW, NT, R, true>), grid, dim3(64 * nw), lds,
-                           stream, w, a, nullptr, isums, N, nb, T, lr);
+    constexpr int Rmax = Racc < Rcap ? Racc : Rcap;
+    const int64_t want = 2 * (int64_t)compute_units();
+    if (Rmax >= 2 && (N + 31) / 32 >= want)
+        launch_mfma_r<GPW, NT, (Rmax >= 2 ? 2 : 1)>(w, a, y, isums, N, nb, T, lr, nw, stream);
     else
-        hipLaunchKernelGGL((mmvq_mfma_kernel<GPW, NT, R, false>), grid, dim3(64 * nw), lds,
-                           stream, w, a, y, nullptr, N, nb, T, lr);
+        launch_mfma_r<GPW, NT, 1>(w, a, y, isums, N, nb, T, lr, nw, stream);
 }
 
 template <int NT>

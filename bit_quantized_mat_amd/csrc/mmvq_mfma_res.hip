@@ -1,0 +1,350 @@
+// mmvq_mfma_res.hip -- TQ1_0 x Q8_1 product for many activation columns on
+// gfx950, matrix cores, with every activation column resident in LDS.
+//
+// Same arithmetic as the streamed matrix-core kernel (mmvq_mfma.hip): digit
+// operands decoded in registers, one v_mfma_i32_16x16x32_i8 per sub-block,
+// -sum q from an all -1 operand, the staged kernels' fp32 order. What differs
+// is where the activations live. The grid holds one workgroup per compute
+// unit at most; each workgroup first copies all T Q8_1 columns into LDS, laid
+// out as the matrix-core B operands (lane-contiguous 8-byte pieces, so every
+// operand read is one conflict-free ds_read_b64) plus each column's fp16
+// sub-block scales, and then walks its row tiles, streaming only weights.
+// The activations are read from L2 once per workgroup instead of once per
+// block and wave ("cuda: opt-in MMVQ activation reuse across output rows"
+// reuses the Q8_1 fragments across rows for the same reason).
+//
+// Reduction order: a row's blocks are split into Lr lane groups (block B in
+// group B mod Lr); each wave owns Lr / NW groups, accumulates each group's
+// blocks in order and combines its own groups by the xor butterfly; wave 0
+// then combines the waves' partial sums by the remaining butterfly levels,
+// read from LDS. The result is bitwise the staged kernel's.
+#include "mfma_common.hpp"
+
+namespace bqm {
+
+// LDS layout, in dwords (nb blocks per row, NT column tiles of 16):
+//   bq   [ct][B][b][lane] x 2   B operand of `lane` for sub-block b of block B
+//   dah  [B][c] x 4             fp16 scales of column c's sub-blocks 8B..8B+7
+//   red  [DB ? 2 : 1][NW][lane][R NT 4]  partial sums of the waves
+// The partial sums are double-buffered (one barrier per tile) when LDS has
+// room for both halves, else single (a second barrier per tile).
+__host__ __device__ inline size_t res_bq_dwords(int NT, int nb) { return (size_t)NT * nb * 8 * 128; }
+__host__ __device__ inline size_t res_dah_dwords(int NT, int nb) { return (size_t)nb * 16 * NT * 4; }
+inline size_t res_lds_bytes(int NW, int NT, int R, int nb, bool db)
+{
+    return (res_bq_dwords(NT, nb) + res_dah_dwords(NT, nb) +
+            (size_t)(db ? 2 : 1) * NW * 64 * R * NT * 4) * 4;
+}
+
+// Copy all T activation columns into bq / dah: one Q8_1 block per item,
+// consecutive threads on consecutive columns. Columns T .. 16 NT - 1 are left
+// as they are: they only feed output columns that are never stored.
+template <int NT>
+__device__ __forceinline__ void stage_all_columns(uint32_t *__restrict__ bq,
+                                                  uint32_t *__restrict__ dah,
+                                                  __amdgpu_buffer_rsrc_t ra, int T, int nb)
+{
+    const int nblk = nb * 8;
+    const int items = T * nblk;
+    for (int it = threadIdx.x; it < items; it += blockDim.x) {
+        const int j = it / T, c = it - j * T;
+        const int B = j >> 3, b = j & 7;
+        const uint32_t off = (uint32_t)(c * nblk + j) * kQ81BlockBytes;
+        const u32x4 v0 = ld_b128(ra, off);
+        const u32x4 v1 = ld_b128(ra, off + 16);
+        const uint32_t ds = ld_b32(ra, off + 32);
+        const uint32_t q[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+        const int ct = c >> 4, cc = c & 15;
+        uint32_t *dst = bq + ((size_t)(ct * nb + B) * 8 + b) * 128;
+#pragma unroll
+        for (int kg = 0; kg < 4; kg++) {
+            const uint32_t lo = b < 5 ? q[2 * kg] : q[kg];
+            const uint32_t hi = b < 5 ? q[2 * kg + 1] : q[4 + kg];
+            *reinterpret_cast<u32x2 *>(dst + 2 * (16 * kg + cc)) = (u32x2){lo, hi};
+        }
+        reinterpret_cast<uint16_t *>(dah + ((size_t)B * 16 * NT + c) * 4)[b] = (uint16_t)ds;
+    }
+}
+
+// NW: waves per workgroup; GPW: butterfly groups per wave (Lr / NW); NT:
+// 16-column tiles (1 or 2); R: 16-row tiles per workgroup tile; DB: partial
+// sums double-buffered; ISUMS: write the exact per-sub-block sums instead of
+// outputs.
+template <int NW, int GPW, int NT, int R, bool DB, bool ISUMS>
+__global__ __launch_bounds__(64 * NW) void mmvq_mfma_res_kernel(const uint8_t *__restrict__ w,
+                                                                const uint8_t *__restrict__ a,
+                                                                float *__restrict__ y,
+                                                                int32_t *__restrict__ isums,
+                                                                int64_t N, int nb, int T,
+                                                                int ntiles)
+{
+    extern __shared__ uint32_t smem[];
+    uint32_t *bq = smem;
+    uint32_t *dah = smem + res_bq_dwords(NT, nb);
+    float *red = reinterpret_cast<float *>(dah + res_dah_dwords(NT, nb));
+    // the wave index is uniform across the wave; saying so keeps the block
+    // loop and its branches on scalar registers
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    constexpr int Lr = NW * GPW;
+    const int kg = lane >> 4;                   // decode lane: row lane % 16, K group kg
+    const int col = lane & 15, rg = lane >> 4;  // output lane: column col, rows 4rg..4rg+3
+    const int nblk = nb * 8;
+    const __amdgpu_buffer_rsrc_t rw = make_rsrc(w, (uint64_t)N * nb * kTq1BlockBytes);
+    const __amdgpu_buffer_rsrc_t ra = make_rsrc(a, (uint64_t)T * nblk * kQ81BlockBytes);
+
+    // byte offsets of this decode lane's rows in tile t (rows past N read row 0)
+    auto tile_rows = [&](int t, uint32_t (&ro)[R]) {
+#pragma unroll
+        for (int rt = 0; rt < R; rt++) {
+            const int64_t rowA = (int64_t)t * 16 * R + 16 * rt + (lane & 15);
+            ro[rt] = (uint32_t)((rowA < N ? rowA : 0) * nb * kTq1BlockBytes);
+        }
+    };
+
+    int tile = blockIdx.x;
+    uint32_t row_off[R];
+    tile_rows(tile, row_off);
+    // the first block's weights are in flight while the activations are staged
+    LaneBlock lb[R];
+    if (wave < nb) {
+#pragma unroll
+        for (int rt = 0; rt < R; rt++)
+            lb[rt] = load_lane_block(rw, row_off[rt] + (uint32_t)wave * kTq1BlockBytes, kg);
+    }
+    stage_all_columns<NT>(bq, dah, ra, T, nb);
+    __syncthreads();
+
+    int parity = 0;
+    for (; tile < ntiles; tile += gridDim.x, parity ^= 1) {
+        const int64_t r0 = (int64_t)tile * 16 * R;
+        const int next_tile = tile + gridDim.x;
+        uint32_t next_off[R];
+        tile_rows(next_tile, next_off);
+
+        float acc[GPW][R][NT][4];
+#pragma unroll
+        for (int gi = 0; gi < GPW; gi++)
+#pragma unroll
+            for (int rt = 0; rt < R; rt++)
+#pragma unroll
+                for (int ct = 0; ct < NT; ct++)
+#pragma unroll
+                    for (int i = 0; i < 4; i++)
+                        acc[gi][rt][ct][i] = 0.0f;
+
+#pragma unroll
+        for (int gi = 0; gi < GPW; gi++) {
+            const int g = wave + NW * gi;
+            for (int B = g; B < nb; B += Lr) {
+                // one block of lookahead: the group's next block, else the next
+                // group's first, else the first block of the next tile
+                const bool same_tile = B + Lr < nb || (gi + 1 < GPW && g + NW < nb);
+                const int Bn = B + Lr < nb ? B + Lr : (same_tile ? g + NW : wave);
+                const bool have_next = same_tile || next_tile < ntiles;
+                LaneBlock ln[R];
+                if (have_next) {
+#pragma unroll
+                    for (int rt = 0; rt < R; rt++)
+                        ln[rt] = load_lane_block(
+                            rw, (same_tile ? row_off[rt] : next_off[rt]) + (uint32_t)Bn * kTq1BlockBytes,
+                            kg);
+                }
+#pragma unroll
+                for (int rt = 0; rt < R; rt++) {
+                    const TileOperands op = decode_lane_block(lb[rt], kg);
+                    float dw[4];  // block scales of the four rows this output lane holds
+#pragma unroll
+                    for (int i = 0; i < 4; i++)
+                        dw[i] = __shfl(op.dw, 4 * rg + i, 64);
+#pragma unroll
+                    for (int ct = 0; ct < NT; ct++) {
+                        // this output lane's column scales, sub-blocks 8B .. 8B+7
+                        const u32x4 dv = *reinterpret_cast<const u32x4 *>(
+                            dah + ((size_t)B * 16 * NT + ct * 16 + col) * 4);
+                        const uint32_t *bqb = bq + (size_t)(ct * nb + B) * 8 * 128 + 2 * lane;
+                        float s[4];
+#pragma unroll
+                        for (int b = 0; b < 8; b++) {
+                            const u32x2 bv = *reinterpret_cast<const u32x2 *>(bqb + b * 128);
+                            const long Bq = (long)(((uint64_t)bv.y << 32) | bv.x);
+                            // -sum(q) of this lane's column on every row, then + sum(u q)
+                            const i32x4 neg_sum = __builtin_amdgcn_mfma_i32_16x16x32_i8(
+                                kAllMinusOne, Bq, (i32x4){0, 0, 0, 0}, 0, 0, 0);
+                            const i32x4 C = __builtin_amdgcn_mfma_i32_16x16x32_i8(op.A[b], Bq,
+                                                                                  neg_sum, 0, 0, 0);
+                            if (ISUMS) {
+                                const int c = ct * 16 + col;
+#pragma unroll
+                                for (int i = 0; i < 4; i++) {
+                                    const int64_t row = r0 + 16 * rt + 4 * rg + i;
+                                    if (c < T && row < N)
+                                        isums[((int64_t)c * N + row) * nblk + 8 * B + b] = C[i];
+                                }
+                            } else {
+                                // the staged kernels' fp32 order: s = sum_b da[b] * isum[b]
+                                // from b = 0 up, then acc + dw * s
+                                const float da = f16_bits_to_f32(dv[b >> 1] >> (16 * (b & 1)));
+#pragma unroll
+                                for (int i = 0; i < 4; i++)
+                                    s[i] = b == 0 ? da * (float)C[i] : fmaf(da, (float)C[i], s[i]);
+                            }
+                        }
+                        if (!ISUMS) {
+#pragma unroll
+                            for (int i = 0; i < 4; i++)
+                                acc[gi][rt][ct][i] = fmaf(dw[i], s[i], acc[gi][rt][ct][i]);
+                        }
+                    }
+                }
+                if (have_next) {
+#pragma unroll
+                    for (int rt = 0; rt < R; rt++)
+                        lb[rt] = ln[rt];
+                }
+            }
+        }
+
+        if (!ISUMS) {
+            // butterfly levels inside the wave (the partner group differs in gi)
+#pragma unroll
+            for (int m = GPW >> 1; m >= 1; m >>= 1) {
+                float nxt[GPW][R][NT][4];
+#pragma unroll
+                for (int gi = 0; gi < GPW; gi++)
+#pragma unroll
+                    for (int rt = 0; rt < R; rt++)
+#pragma unroll
+                        for (int ct = 0; ct < NT; ct++)
+#pragma unroll
+                            for (int i = 0; i < 4; i++)
+                                nxt[gi][rt][ct][i] = acc[gi][rt][ct][i] + acc[gi ^ m][rt][ct][i];
+#pragma unroll
+                for (int gi = 0; gi < GPW; gi++)
+#pragma unroll
+                    for (int rt = 0; rt < R; rt++)
+#pragma unroll
+                        for (int ct = 0; ct < NT; ct++)
+#pragma unroll
+                            for (int i = 0; i < 4; i++)
+                                acc[gi][rt][ct][i] = nxt[gi][rt][ct][i];
+            }
+            // the levels across waves: every wave leaves its partial sums in
+            // this tile's half of red; wave 0 folds them, at level m adding
+            // wave w + m's running value to wave w's for w < m (the value the
+            // xor butterfly gives wave 0). The other half belongs to the next
+            // tile, so one barrier per tile suffices.
+            constexpr int kPer = R * NT * 4;
+            float *half = red + (size_t)(DB ? parity : 0) * NW * 64 * kPer;
+#pragma unroll
+            for (int rt = 0; rt < R; rt++)
+#pragma unroll
+                for (int ct = 0; ct < NT; ct++)
+#pragma unroll
+                    for (int i = 0; i < 4; i++)
+                        half[((size_t)wave * 64 + lane) * kPer + (rt * NT + ct) * 4 + i] =
+                            acc[0][rt][ct][i];
+            __syncthreads();
+            if (wave == 0) {
+#pragma unroll
+                for (int rt = 0; rt < R; rt++)
+#pragma unroll
+                    for (int ct = 0; ct < NT; ct++)
+#pragma unroll
+                        for (int i = 0; i < 4; i++) {
+                            const int k = (rt * NT + ct) * 4 + i;
+                            float v[NW];
+#pragma unroll
+                            for (int u = 0; u < NW; u++)
+                                v[u] = half[((size_t)u * 64 + lane) * kPer + k];
+#pragma unroll
+                            for (int m = NW >> 1; m >= 1; m >>= 1)
+#pragma unroll
+                                for (int u = 0; u < m; u++)
+                                    v[u] = v[u] + v[u + m];
+                            acc[0][rt][ct][i] = v[0];
+                        }
+#pragma unroll
+                for (int rt = 0; rt < R; rt++)
+#pragma unroll
+                    for (int ct = 0; ct < NT; ct++) {
+                        const int c = ct * 16 + col;
+                        if (c < T) {
+#pragma unroll
+                            for (int i = 0; i < 4; i++) {
+                                const int64_t row = r0 + 16 * rt + 4 * rg + i;
+                                if (row < N)
+                                    y[(int64_t)c * N + row] = acc[0][rt][ct][i];
+                            }
+                        }
+                    }
+            }
+            if (!DB)
+                __syncthreads();  // wave 0 has read the partial sums
+        }
+#pragma unroll
+        for (int rt = 0; rt < R; rt++)
+            row_off[rt] = next_off[rt];
+    }
+}
+
+template <int NW, int GPW, int NT, bool DB>
+static int launch_res(const uint8_t *w, const uint8_t *a, float *y, int32_t *isums, int64_t N,
+                      int nb, int T, hipStream_t stream)
+{
+    constexpr int R = 1;
+    const int64_t ntiles = (N + 16 * R - 1) / (16 * R);
+    const size_t lds = res_lds_bytes(NW, NT, R, nb, DB);
+    const void *kt =
+        reinterpret_cast<const void *>(&mmvq_mfma_res_kernel<NW, GPW, NT, R, DB, true>);
+    const void *kf =
+        reinterpret_cast<const void *>(&mmvq_mfma_res_kernel<NW, GPW, NT, R, DB, false>);
+    allow_dynamic_lds(kt, lds);
+    allow_dynamic_lds(kf, lds);
+    const int cap = resident_workgroups(isums ? kt : kf, 64 * NW, lds);
+    const dim3 grid((unsigned)(ntiles < cap ? ntiles : cap));
+    if (isums)
+        hipLaunchKernelGGL((mmvq_mfma_res_kernel<NW, GPW, NT, R, DB, true>), grid, dim3(64 * NW),
+                           lds, stream, w, a, nullptr, isums, N, nb, T, (int)ntiles);
+    else
+        hipLaunchKernelGGL((mmvq_mfma_res_kernel<NW, GPW, NT, R, DB, false>), grid,
+                           dim3(64 * NW), lds, stream, w, a, y, nullptr, N, nb, T, (int)ntiles);
+    return check_launch();
+}
+
+// 16 waves for one column tile, 8 for two (their register budgets); the
+// column tiles' partial sums double-buffered for one tile, single for two
+static int res_waves(int NT) { return NT == 1 ? 16 : 8; }
+
+bool mfma_resident_supported(int64_t K, int32_t T)
+{
+    const int nb = (int)(K / kTq1BlockElems);
+    const int Lr = 1 << lanes_per_row_log2(nb);
+    const int NT = T <= 16 ? 1 : 2;
+    const int NW = res_waves(NT);
+    return Lr >= NW && res_lds_bytes(NW, NT, 1, nb, NT == 1) <= lds_budget();
+}
+
+int launch_mmvq_mfma_resident(const void *w, const void *a, float *y, int32_t *isums, int64_t N,
+                              int64_t K, int32_t T, hipStream_t stream)
+{
+    const int nb = (int)(K / kTq1BlockElems);
+    const int Lr = 1 << lanes_per_row_log2(nb);
+    const uint8_t *wp = static_cast<const uint8_t *>(w);
+    const uint8_t *ap = static_cast<const uint8_t *>(a);
+    if (T <= 16) {
+        switch (Lr) {
+        case 16: return launch_res<16, 1, 1, true>(wp, ap, y, isums, N, nb, T, stream);
+        case 32: return launch_res<16, 2, 1, true>(wp, ap, y, isums, N, nb, T, stream);
+        default: return launch_res<16, 4, 1, true>(wp, ap, y, isums, N, nb, T, stream);
+        }
+    }
+    switch (Lr) {
+    case 8: return launch_res<8, 1, 2, false>(wp, ap, y, isums, N, nb, T, stream);
+    case 16: return launch_res<8, 2, 2, false>(wp, ap, y, isums, N, nb, T, stream);
+    case 32: return launch_res<8, 4, 2, false>(wp, ap, y, isums, N, nb, T, stream);
+    default: return launch_res<8, 8, 2, false>(wp, ap, y, isums, N, nb, T, stream);
+    }
+}
+
+}  // namespace bqm

@@ -7,10 +7,10 @@
 // byte is loaded from HBM once and all of its digits are expanded in registers
 // (tq1_decode.hpp).
 //
-// Thread mapping: Lr lanes share an output row (Lr = the largest power of two
-// dividing the row's block count, at most 64); lane i of the row takes blocks
-// i, i+Lr, ... Consecutive lanes therefore read consecutive 54-byte blocks,
-// and a wave's weight loads cover one contiguous stretch of rows.
+// Thread mapping: Lr lanes share an output row (Lr = the smallest power of
+// two, at most 64, not below the row's block count); lane i of the row takes
+// blocks i, i+Lr, ... Consecutive lanes therefore read consecutive 54-byte
+// blocks, and a wave's weight loads cover one contiguous stretch of rows.
 //
 // Activations: the workgroup copies the Q8_1 column into LDS once per chunk of
 // up to 128 blocks, transposed so that dword j of all eight sub-blocks of a
@@ -20,8 +20,9 @@
 
 namespace bqm {
 
-// Plain product: T columns of a [T][K/32] activation matrix, y [T][N].
-template <int TC, bool ISUMS>
+// Plain product: T columns of a [T][K/32] Q8_1 activation matrix (F32: of
+// a [T][K] fp32 matrix, quantized while staging), y [T][N].
+template <int TC, bool ISUMS, bool F32>
 __global__ __launch_bounds__(256) void mmvq_staged_kernel(const uint8_t *__restrict__ w,
                                                           const uint8_t *__restrict__ a,
                                                           float *__restrict__ y,
@@ -32,17 +33,18 @@ __global__ __launch_bounds__(256) void mmvq_staged_kernel(const uint8_t *__restr
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int64_t row = ((int64_t)blockIdx.x * 4 + wave) * (64 >> lr_log2) + (lane >> lr_log2);
     const int nblk = nb * 8;
+    const uint32_t col_bytes = F32 ? (uint32_t)nb * kTq1BlockElems * 4 : (uint32_t)nblk * kQ81BlockBytes;
     const __amdgpu_buffer_rsrc_t rw = make_rsrc(w, (uint64_t)N * nb * kTq1BlockBytes);
-    const __amdgpu_buffer_rsrc_t ra = make_rsrc(a, (uint64_t)T * nblk * kQ81BlockBytes);
+    const __amdgpu_buffer_rsrc_t ra = make_rsrc(a, (uint64_t)T * col_bytes);
     uint32_t col_off[TC];
     float *out[TC];
 #pragma unroll
     for (int t = 0; t < TC; t++) {
-        col_off[t] = (uint32_t)t * nblk * kQ81BlockBytes;
+        col_off[t] = (uint32_t)t * col_bytes;
         out[t] = ISUMS ? nullptr : y + (int64_t)t * N;
     }
-    staged_rows<TC, ISUMS>(rw, ra, col_off, out, isums, reinterpret_cast<uint32_t *>(act_lds),
-                           row, row < N, N, nb, T, lr_log2, chunk);
+    staged_rows<TC, ISUMS, F32>(rw, ra, col_off, out, isums, reinterpret_cast<uint32_t *>(act_lds),
+                                row, row < N, N, nb, T, lr_log2, chunk);
 }
 
 int lanes_per_row_log2(int64_t nb)
@@ -72,6 +74,50 @@ size_t lds_budget()
     return cached[dev];
 }
 
+int compute_units()
+{
+    // compute units of the current device, cached per device
+    static int cached[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64)
+        return 256;
+    if (!cached[dev]) {
+        int v = 0;
+        if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+            v <= 0)
+            v = 256;
+        cached[dev] = v;
+    }
+    return cached[dev];
+}
+
+int resident_workgroups(const void *kernel, int threads, size_t lds)
+{
+    // workgroups of this kernel the whole device holds at once; remembered for
+    // the last few (kernel, shape, device) triples asked about
+    struct Entry {
+        const void *kernel;
+        int threads, dev;
+        size_t lds;
+        int count;
+    };
+    static Entry cache[32];
+    static int next;
+    int dev = 0;
+    (void)hipGetDevice(&dev);
+    for (const Entry &e : cache)
+        if (e.kernel == kernel && e.threads == threads && e.lds == lds && e.dev == dev && e.count > 0)
+            return e.count;
+    int per_cu = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, threads, lds) != hipSuccess ||
+        per_cu < 1)
+        per_cu = 1;
+    const int count = per_cu * compute_units();
+    cache[next] = Entry{kernel, threads, dev, lds, count};
+    next = (next + 1) % 32;
+    return count;
+}
+
 bool staged_supported(int64_t K, int32_t T)
 {
     if (T < 1 || T > kStagedMaxCols)
@@ -80,23 +126,25 @@ bool staged_supported(int64_t K, int32_t T)
     return staged_chunk(nb, lanes_per_row_log2(nb), T, lds_budget()) > 0;
 }
 
-template <int TC>
+template <int TC, bool F32>
 static void launch_staged_tc(const uint8_t *w, const uint8_t *a, float *y, int32_t *isums,
                              int64_t N, int nb, int T, int lr, int chunk, dim3 grid, size_t lds,
                              hipStream_t stream)
 {
-    allow_dynamic_lds(reinterpret_cast<const void *>(&mmvq_staged_kernel<TC, true>), lds);
-    allow_dynamic_lds(reinterpret_cast<const void *>(&mmvq_staged_kernel<TC, false>), lds);
-    if (isums)
-        hipLaunchKernelGGL((mmvq_staged_kernel<TC, true>), grid, dim3(256), lds, stream, w, a,
-                           nullptr, isums, N, nb, T, lr, chunk);
-    else
-        hipLaunchKernelGGL((mmvq_staged_kernel<TC, false>), grid, dim3(256), lds, stream, w, a,
-                           y, nullptr, N, nb, T, lr, chunk);
+    if (isums && !F32) {
+        allow_dynamic_lds(reinterpret_cast<const void *>(&mmvq_staged_kernel<TC, true, false>), lds);
+        hipLaunchKernelGGL((mmvq_staged_kernel<TC, true, false>), grid, dim3(256), lds, stream, w,
+                           a, nullptr, isums, N, nb, T, lr, chunk);
+    } else {
+        allow_dynamic_lds(reinterpret_cast<const void *>(&mmvq_staged_kernel<TC, false, F32>), lds);
+        hipLaunchKernelGGL((mmvq_staged_kernel<TC, false, F32>), grid, dim3(256), lds, stream, w,
+                           a, y, nullptr, N, nb, T, lr, chunk);
+    }
 }
 
-int launch_mmvq_staged(const void *w, const void *a, float *y, int32_t *isums, int64_t N,
-                       int64_t K, int32_t T, hipStream_t stream)
+template <bool F32>
+static int launch_staged(const void *w, const void *a, float *y, int32_t *isums, int64_t N,
+                         int64_t K, int32_t T, hipStream_t stream)
 {
     const int nb = (int)(K / kTq1BlockElems);
     const int lr = lanes_per_row_log2(nb);
@@ -108,14 +156,26 @@ int launch_mmvq_staged(const void *w, const void *a, float *y, int32_t *isums, i
     const uint8_t *ap = static_cast<const uint8_t *>(a);
     // column-capacity ladder: a call pays for the next rung up, never for 8
     if (T == 1)
-        launch_staged_tc<1>(wp, ap, y, isums, N, nb, T, lr, chunk, grid, lds, stream);
+        launch_staged_tc<1, F32>(wp, ap, y, isums, N, nb, T, lr, chunk, grid, lds, stream);
     else if (T == 2)
-        launch_staged_tc<2>(wp, ap, y, isums, N, nb, T, lr, chunk, grid, lds, stream);
+        launch_staged_tc<2, F32>(wp, ap, y, isums, N, nb, T, lr, chunk, grid, lds, stream);
     else if (T <= 4)
-        launch_staged_tc<4>(wp, ap, y, isums, N, nb, T, lr, chunk, grid, lds, stream);
+        launch_staged_tc<4, F32>(wp, ap, y, isums, N, nb, T, lr, chunk, grid, lds, stream);
     else
-        launch_staged_tc<8>(wp, ap, y, isums, N, nb, T, lr, chunk, grid, lds, stream);
+        launch_staged_tc<8, F32>(wp, ap, y, isums, N, nb, T, lr, chunk, grid, lds, stream);
     return check_launch();
+}
+
+int launch_mmvq_staged(const void *w, const void *a, float *y, int32_t *isums, int64_t N,
+                       int64_t K, int32_t T, hipStream_t stream)
+{
+    return launch_staged<false>(w, a, y, isums, N, K, T, stream);
+}
+
+int launch_mmvq_staged_f32(const void *w, const float *x, float *y, int64_t N, int64_t K,
+                           int32_t T, hipStream_t stream)
+{
+    return launch_staged<true>(w, x, y, nullptr, N, K, T, stream);
 }
 
 }  // namespace bqm

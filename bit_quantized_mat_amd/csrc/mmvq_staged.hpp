@@ -4,6 +4,7 @@
 #pragma once
 
 #include "launch.hpp"
+#include "q8_1.hpp"
 #include "tq1_decode.hpp"
 
 namespace bqm {
@@ -39,6 +40,48 @@ __device__ __forceinline__ void stage_activations(uint32_t *__restrict__ act,
         }
         dst[64 + c] = __float_as_uint(f16_bits_to_f32(ds & 0xffffu));
         dst[72 + c] = (uint32_t)(-sq);
+    }
+}
+
+// The same staged layout filled from fp32 activations, quantized on the fly
+// (q8_1_block_by_8: the bytes the stand-alone quantize kernel would write).
+// Column data start at byte col_off of rx; eight lanes per Q8_1 block.
+__device__ __forceinline__ void stage_activations_f32(uint32_t *__restrict__ act,
+                                                      __amdgpu_buffer_rsrc_t rx, uint32_t col_off,
+                                                      int B0, int cb, int tid, int nthreads)
+{
+    constexpr int kAhead = 4;   // loads in flight per lane before any is quantized
+    const int tasks = cb * 64;  // cb blocks x 8 sub-blocks x 8 lanes
+    for (int base = 0; base < tasks; base += kAhead * nthreads) {
+        // every lane takes part in the group shuffles: groups past the end
+        // (whole groups, tasks being a multiple of 8) redo the last one and
+        // store nothing
+        u32x4 v[kAhead];
+#pragma unroll
+        for (int k = 0; k < kAhead; k++) {
+            const int i = base + k * nthreads + tid;
+            const int ii = i < tasks ? i : tasks - 1;
+            const int g = ii >> 3, j = ii & 7;
+            const int bi = g >> 3, c = g & 7;
+            v[k] = ld_b128(rx, col_off + (uint32_t)(((B0 + bi) * kTq1BlockElems +
+                                                     c * kQ81BlockElems + 4 * j) * 4));
+        }
+#pragma unroll
+        for (int k = 0; k < kAhead; k++) {
+            const int i = base + k * nthreads + tid;
+            const Q81Part p = q8_1_block_by_8(__uint_as_float(v[k].x), __uint_as_float(v[k].y),
+                                              __uint_as_float(v[k].z), __uint_as_float(v[k].w));
+            if (i < tasks) {
+                const int g = i >> 3, j = i & 7;
+                const int bi = g >> 3, c = g & 7;
+                uint32_t *dst = act + bi * kActStride;
+                dst[8 * j + c] = p.q4;
+                if (j == 0) {
+                    dst[64 + c] = __float_as_uint(f16_bits_to_f32(f32_to_f16_bits(p.d)));
+                    dst[72 + c] = (uint32_t)(-p.sum);
+                }
+            }
+        }
     }
 }
 
@@ -135,10 +178,11 @@ __device__ __forceinline__ void digit_sums_staged(const DigitBlock &d,
 }
 
 // The rows of one workgroup against T <= TC activation columns. Column t's
-// Q8_1 row starts at byte col_off[t] of the activation buffer ra and its
-// outputs go to out[t][row]. All 256 threads of the workgroup must call this
-// (it synchronizes); lanes whose row is out of range only help with staging.
-template <int TC, bool ISUMS>
+// Q8_1 row (fp32 row when F32: quantized while staging) starts at byte
+// col_off[t] of the activation buffer ra and its outputs go to out[t][row].
+// All 256 threads of the workgroup must call this (it synchronizes); lanes
+// whose row is out of range only help with staging.
+template <int TC, bool ISUMS, bool F32 = false>
 __device__ __forceinline__ void staged_rows(__amdgpu_buffer_rsrc_t rw, __amdgpu_buffer_rsrc_t ra,
                                             const uint32_t (&col_off)[TC],
                                             float *const (&out)[TC], int32_t *__restrict__ isums,
@@ -168,8 +212,13 @@ __device__ __forceinline__ void staged_rows(__amdgpu_buffer_rsrc_t rw, __amdgpu_
         __syncthreads();  // readers of the previous chunk are done
 #pragma unroll
         for (int t = 0; t < TC; t++)
-            if (t < T)
-                stage_activations(act + t * cb * kActStride, ra, col_off[t], B0, cb, tid, 256);
+            if (t < T) {
+                if (F32)
+                    stage_activations_f32(act + t * cb * kActStride, ra, col_off[t], B0, cb, tid,
+                                          256);
+                else
+                    stage_activations(act + t * cb * kActStride, ra, col_off[t], B0, cb, tid, 256);
+            }
         __syncthreads();
         if (row_ok) {
             for (int B = first; B < end; B += Lr) {
@@ -218,19 +267,6 @@ __device__ __forceinline__ void staged_rows(__amdgpu_buffer_rsrc_t rw, __amdgpu_
                     out[t][row] = acc[t];
         }
     }
-}
-
-// Dynamic LDS: 64 KiB is always available; beyond that the launcher raises
-// the kernel's limit up to what the device reports (160 KiB on gfx950).
-constexpr size_t kLdsDefault = 64 * 1024;
-constexpr size_t kLdsMax = 160 * 1024;
-
-// Raise a kernel's dynamic-LDS limit when a launch needs more than the
-// default (idempotent; the runtime keeps the attribute per function).
-inline void allow_dynamic_lds(const void *kernel, size_t bytes)
-{
-    if (bytes > kLdsDefault)
-        (void)hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
 }
 
 // Blocks staged per pass: all of a row's blocks if they fit (rows with fewer

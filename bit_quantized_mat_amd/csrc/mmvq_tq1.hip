@@ -1,17 +1,18 @@
-// mmvq_tq1.hip -- TQ1_0 x Q8_1 mat-vec and small-batch product on gfx950.
+// mmvq_tq1.hip -- dispatch of the plain product, and the ungrouped
+// expert-routed kernel (one (token, slot) pair per workgroup row), used when
+// the grouped kernel's staged activations do not fit its LDS budget.
 //
-// Byte-major decode ("CUDA: TQ1_0 mat-vec is load-bound by the per-32-element
-// chunk contract", "Upstream state" and "Proposed approach"): each thread owns
-// whole 256-element blocks, loads every packed byte of a block once, expands
-// all of its base-3 digits in registers, and spends each digit against the
-// matching Q8_1 activation bytes. Digit u = trit + 1 is in {0,1,2}, so the
-// integer dot uses the unsigned digits and subtracts the activation block's
-// sum of q once: sum(t*q) = sum(u*q) - sum(q).
+// The ungrouped kernel is byte-major ("CUDA: TQ1_0 mat-vec is load-bound by
+// the per-32-element chunk contract", "Upstream state" and "Proposed
+// approach"): each thread owns whole 256-element blocks, loads every packed
+// byte of a block once, expands all of its base-3 digits in registers, and
+// spends each digit against the matching Q8_1 activation bytes. Digit
+// u = trit + 1 is in {0,1,2}, so the integer dot uses the unsigned digits and
+// subtracts the activation block's sum of q once: sum(t*q) = sum(u*q) - sum(q).
 //
 // Thread mapping: Lr lanes (a power of two, at most 64) share one output row;
 // lane i of a row takes blocks i, i+Lr, ... of that row. A wave thus covers a
 // contiguous run of 64 packed blocks per step, so its loads are coalesced.
-// The T activation columns reuse the decoded digits held in registers.
 #include "launch.hpp"
 #include "tq1_decode.hpp"
 
@@ -185,65 +186,16 @@ __device__ __forceinline__ void rows_product(const uint8_t *__restrict__ w, uint
     }
 }
 
-template <int TC, bool ISUMS>
-__global__ __launch_bounds__(256) void mmvq_tq1_kernel(const uint8_t *__restrict__ w,
-                                                       const uint8_t *__restrict__ a,
-                                                       float *__restrict__ y,
-                                                       int32_t *__restrict__ isums, int64_t N,
-                                                       int nb, int T, int lr_log2)
-{
-    const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
-    const int Lr = 1 << lr_log2;
-    const int rows_per_wave = 64 >> lr_log2;
-    const int64_t row =
-        ((int64_t)blockIdx.x * 4 + wave) * rows_per_wave + (lane >> lr_log2);
-    const int sub = lane & (Lr - 1);
-    const uint64_t w_bytes = (uint64_t)N * nb * kTq1BlockBytes;
-    const uint64_t a_bytes = (uint64_t)T * nb * 8 * kQ81BlockBytes;
-    rows_product<TC, ISUMS>(w, w_bytes, a, a_bytes, row, row < N, nb, sub, Lr, T, 0, y, N,
-                            isums, N);
-}
-
-template <bool ISUMS>
-static int launch_mmvq_t(const void *w, const void *a, float *y, int32_t *isums, int64_t N,
-                         int64_t K, int32_t T, hipStream_t stream)
-{
-    const int nb = (int)(K / kTq1BlockElems);
-    const int lr = lanes_per_row_log2(nb);
-    const int64_t rows_per_wg = 4 * (64 >> lr);
-    const dim3 grid((unsigned)((N + rows_per_wg - 1) / rows_per_wg));
-    const uint8_t *wp = static_cast<const uint8_t *>(w);
-    const uint8_t *ap = static_cast<const uint8_t *>(a);
-#define BQM_LAUNCH(TC)                                                                       \
-    hipLaunchKernelGGL((mmvq_tq1_kernel<TC, ISUMS>), grid, dim3(256), 0, stream, wp, ap, y, \
-                       isums, N, nb, (int)T, lr)
-    if (T <= 1)
-        BQM_LAUNCH(1);
-    else if (T <= 2)
-        BQM_LAUNCH(2);
-    else if (T <= 4)
-        BQM_LAUNCH(4);
-    else if (T <= 8)
-        BQM_LAUNCH(8);
-    else if (T <= 16)
-        BQM_LAUNCH(16);
-    else
-        BQM_LAUNCH(32);
-#undef BQM_LAUNCH
-    return check_launch();
-}
-
+// Plain product: the staged kernel for narrow calls whose activations fit its
+// LDS, the matrix-core kernel for everything else.
 int launch_mmvq(const void *w, const void *a, float *y, int32_t *isums, int64_t N, int64_t K,
                 int32_t T, hipStream_t stream)
 {
-    if (staged_supported(K, T))
+    if (T < kMfmaMinCols && staged_supported(K, T))
         return launch_mmvq_staged(w, a, y, isums, N, K, T, stream);
-    if (T > 8)
-        return launch_mmvq_mfma(w, a, y, isums, N, K, T, stream);
-    if (isums)
-        return launch_mmvq_t<true>(w, a, nullptr, isums, N, K, T, stream);
-    return launch_mmvq_t<false>(w, a, y, nullptr, N, K, T, stream);
+    if (mfma_resident_supported(K, T))
+        return launch_mmvq_mfma_resident(w, a, y, isums, N, K, T, stream);
+    return launch_mmvq_mfma(w, a, y, isums, N, K, T, stream);
 }
 
 // ---------------------------------------------------------------------------

@@ -7,47 +7,42 @@
 // Byte layouts and rounding rules are the ones declared in include/bqm.h.
 #include "common.hpp"
 #include "launch.hpp"
+#include "q8_1.hpp"
 
 namespace bqm {
 
-// One 32-lane half-wave per Q8_1 block: lane i owns element i.
-// amax, the scale, and sum(q) are exact wave reductions; the scale and the
-// reciprocal use IEEE division (the build keeps HIP's correctly rounded fp32
-// divide), and q rounds half away from zero.
+// Eight lanes per Q8_1 block, four elements per lane (one 16-byte load and
+// one dword of q bytes each); the arithmetic is q8_1_block_by_8.
 __global__ __launch_bounds__(256) void q8_1_quantize_kernel(const float *__restrict__ x,
                                                             uint8_t *__restrict__ a,
                                                             int64_t nblocks)
 {
-    const int lane = threadIdx.x & 31;
-    const int64_t blk = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) >> 5;
-    if (blk >= nblocks)
-        return;  // whole half-waves exit together (nblocks counts 32-lane groups)
-    const float v = x[blk * kQ81BlockElems + lane];
-    float amax = fabsf(v);
-#pragma unroll
-    for (int m = 16; m >= 1; m >>= 1)
-        amax = fmaxf(amax, __shfl_xor(amax, m, 32));
-    const float d = amax / 127.0f;
-    const float id = d != 0.0f ? 1.0f / d : 0.0f;
-    int q = (int)roundf(v * id);
-    q = q > 127 ? 127 : (q < -127 ? -127 : q);
-    int sum = q;
-#pragma unroll
-    for (int m = 16; m >= 1; m >>= 1)
-        sum += __shfl_xor(sum, m, 32);
-    uint8_t *out = a + blk * kQ81BlockBytes;
-    out[lane] = (uint8_t)(int8_t)q;
-    if (lane == 0) {
-        const uint32_t dh = f32_to_f16_bits(d);
-        const uint32_t sh = f32_to_f16_bits(d * (float)sum);
-        *reinterpret_cast<uint32_t *>(out + 32) = dh | (sh << 16);
+    const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int64_t blk = t >> 3;
+    const int j = (int)(t & 7);
+    // groups past the end compute on a copy of the last block and store nothing,
+    // so that every lane takes part in the group shuffles
+    const int64_t src = blk < nblocks ? blk : nblocks - 1;
+    // a buffer load needs only the dword alignment the entry point checks; the
+    // descriptor covers this workgroup's 32 blocks
+    const int64_t first = (int64_t)blockIdx.x * (blockDim.x >> 3);
+    const __amdgpu_buffer_rsrc_t rx = make_rsrc(
+        x + first * kQ81BlockElems, (uint64_t)(nblocks - first) * kQ81BlockElems * sizeof(float));
+    const u32x4 v = ld_b128(rx, (uint32_t)((src - first) * kQ81BlockElems + 4 * j) * 4);
+    const Q81Part p = q8_1_block_by_8(__uint_as_float(v.x), __uint_as_float(v.y),
+                                      __uint_as_float(v.z), __uint_as_float(v.w));
+    if (blk < nblocks) {
+        uint32_t *out = reinterpret_cast<uint32_t *>(a + blk * kQ81BlockBytes);
+        out[j] = p.q4;
+        if (j == 0)
+            out[8] = q8_1_scale_field(p);
     }
 }
 
 int launch_q8_1_quantize(const float *x, void *a, int64_t T, int64_t K, hipStream_t stream)
 {
     const int64_t nblocks = T * (K / kQ81BlockElems);
-    const int64_t threads = nblocks * 32;
+    const int64_t threads = nblocks * 8;
     const int64_t grid = (threads + 255) / 256;
     hipLaunchKernelGGL(q8_1_quantize_kernel, dim3((unsigned)grid), dim3(256), 0, stream, x,
                        static_cast<uint8_t *>(a), nblocks);

@@ -170,18 +170,28 @@ __device__ __forceinline__ void dot_qh(uint32_t w, uint32_t q74, uint32_t q75, u
 // bytes because every per-byte result is a digit (>= 0), and 3 F stays
 // below 256. Worth its six extra operations once a decoded dword is spent on
 // two or more activation columns (five products per column instead of eight).
+// PK selects how 3 F is formed: a packed 16-bit multiply (full rate, but it
+// ties up more registers in the compiler's schedule), or a plain 32-bit
+// multiply-subtract.
+template <bool PK>
+__device__ __forceinline__ uint32_t minus3(uint32_t f, uint32_t f_next)
+{
+    return PK ? f - mul3_bytes(f_next) : f - 3u * f_next;
+}
+
 struct QsDigits {
     uint32_t U[5];
 };
 
+template <bool PK = false>
 __device__ __forceinline__ QsDigits qs_digits(uint32_t w)
 {
     const QsFloors f = qs_floors(w);
     QsDigits d;
     d.U[0] = f.U0;
-    d.U[1] = f.F1 - 3u * f.F2;
-    d.U[2] = f.F2 - 3u * f.F3;
-    d.U[3] = f.F3 - 3u * f.F4;
+    d.U[1] = minus3<PK>(f.F1, f.F2);
+    d.U[2] = minus3<PK>(f.F2, f.F3);
+    d.U[3] = minus3<PK>(f.F3, f.F4);
     d.U[4] = f.F4;
     return d;
 }
@@ -190,13 +200,14 @@ struct QhDigits {
     uint32_t U[4];
 };
 
+template <bool PK = false>
 __device__ __forceinline__ QhDigits qh_digits(uint32_t w)
 {
     const QhFloors f = qh_floors(w);
     QhDigits d;
     d.U[0] = f.U0;
-    d.U[1] = f.F1 - 3u * f.F2;
-    d.U[2] = f.F2 - 3u * f.F3;
+    d.U[1] = minus3<PK>(f.F1, f.F2);
+    d.U[2] = minus3<PK>(f.F2, f.F3);
     d.U[3] = f.F3;
     return d;
 }

@@ -100,6 +100,23 @@ BQM_API int q8_1_quantize(const float *x, void *a, int64_t T, int64_t K, void *s
 BQM_API int mmvq_tq1_0(const void *w, const void *a, float *y,
                int64_t N, int64_t K, int32_t T, void *stream);
 
+/* Largest number of activation columns mmvq_tq1_0_f32 accepts. */
+#define BQM_MMVQ_F32_MAX_COLS 8
+
+/* The same product on fp32 activations, quantized to Q8_1 inside the call:
+ * the result is bitwise that of q8_1_quantize(x) followed by mmvq_tq1_0, with
+ * one launch instead of two and no Q8_1 buffer (the quantized blocks live in
+ * on-chip memory only). The decode step of a layer, where the two launches
+ * would cost more than the product itself.
+ *   w [N][K/256] TQ1_0 blocks; x [T][K] fp32, row-major; y [T][N] fp32 output.
+ * Shapes: N >= 1, K >= 256, K % 256 == 0, 1 <= T <= BQM_MMVQ_F32_MAX_COLS,
+ * the weight matrix and x each below 4 GiB, and the T quantized columns of
+ * one staging pass fit the device's LDS (on a 160 KiB-LDS device, every shape
+ * but T = 8 with K > 8192); otherwise BQM_ERR_SHAPE.
+ * Alignment: w, x, y 4 bytes. */
+BQM_API int mmvq_tq1_0_f32(const void *w, const float *x, float *y,
+                   int64_t N, int64_t K, int32_t T, void *stream);
+
 /* Expert-routed product (mixture of experts):
  *   y[t][s][n] = mmvq(W[ids[t][s]], a[t])[n]   for t < T, s < n_used
  *   w   [E][N][K/256] TQ1_0 blocks (expert-major, each expert an N x K matrix).

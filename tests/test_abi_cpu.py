@@ -22,7 +22,7 @@ def _declared_functions():
 
 def test_header_declares_the_four_calls():
     names = _declared_functions()
-    for n in ("tq1_pack", "q8_1_quantize", "mmvq_tq1_0", "mmvq_id_tq1_0",
+    for n in ("tq1_pack", "q8_1_quantize", "mmvq_tq1_0", "mmvq_tq1_0_f32", "mmvq_id_tq1_0",
               "mmvq_id_tq1_0_workspace_bytes", "mmvq_tq1_0_block_isums",
               "bqm_status_string", "bqm_version"):
         assert n in names
@@ -92,6 +92,23 @@ def test_q8_1_quantize_rejects(args, expect):
 ])
 def test_mmvq_rejects(fn, args, expect):
     assert getattr(bqm.library(), fn)(*args) == expect
+
+
+@pytest.mark.parametrize("args,expect", [
+    ((None, GOOD, GOOD, 8, 256, 1, None), -1),
+    ((GOOD, None, GOOD, 8, 256, 1, None), -1),
+    ((GOOD, GOOD, None, 8, 256, 1, None), -1),
+    ((GOOD, GOOD, GOOD, 0, 256, 1, None), -2),
+    ((GOOD, GOOD, GOOD, 8, 288, 1, None), -2),
+    ((GOOD, GOOD, GOOD, 8, 256, 0, None), -2),
+    ((GOOD, GOOD, GOOD, 8, 256, 9, None), -2),            # beyond BQM_MMVQ_F32_MAX_COLS
+    ((GOOD, GOOD, GOOD, 1, 1 << 28, 8, None), -2),        # x above 4 GiB
+    ((ODD, GOOD, GOOD, 8, 256, 1, None), -3),
+    ((GOOD, ODD, GOOD, 8, 256, 1, None), -3),
+    ((GOOD, GOOD, ODD, 8, 256, 1, None), -3),
+])
+def test_mmvq_f32_rejects(args, expect):
+    assert bqm.library().mmvq_tq1_0_f32(*args) == expect
 
 
 def test_mmvq_id_rejects():

@@ -65,8 +65,12 @@ def _case(N, K, T, seed, p_zero=1 / 3, outliers=0.01, d_lo=0.01, d_hi=0.1):
 
 # shapes: (N, K, T) spanning several row tiles, ragged row counts, odd block
 # counts (2-byte aligned blocks), one-block rows and wide rows
+# (which kernel takes each: staged for T < 5; from T = 5 the matrix-core kernel,
+# with the activations resident in LDS when they fit and a row has at least
+# as many lane groups as the workgroup has waves, else streamed per block)
 SHAPES = [(256, 1024, 1), (1, 256, 1), (33, 256, 2), (67, 768, 3), (130, 2304, 5),
-          (515, 4096, 8), (96, 6144, 4), (40, 16384, 1), (17, 1280, 32), (300, 512, 16)]
+          (515, 4096, 8), (96, 6144, 4), (40, 16384, 1), (17, 1280, 32), (300, 512, 16),
+          (40, 16384, 6), (50, 9216, 5), (21, 4096, 17), (1, 2304, 9)]
 
 
 # ---------------------------------------------------------------------------
@@ -337,3 +341,47 @@ def test_workload_moe_parity(bqm):
         for t in ts:
             _, y64, ab = oracle.mmvq_id(w_ref, a_ref_all[t:t + 1], ids[t:t + 1], E, N, K, 1, n_used)
             _assert_close(y[t:t + 1], y64, ab, "moe T=%d token %d" % (T, t))
+
+
+# ---------------------------------------------------------------------------
+# Fused quantize-and-multiply: bitwise the two-call path, within tolerance of
+# the oracle
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("N,K,T", [(256, 1024, 1), (1, 256, 1), (33, 256, 2), (67, 768, 3),
+                                   (130, 2304, 5), (515, 4096, 8), (96, 6144, 4),
+                                   (40, 16384, 1), (17, 8192, 7), (9, 8448, 6)])
+def test_mmvq_f32_equals_quantize_then_mmvq(bqm, N, K, T):
+    trits, d16, x = _case(N, K, T, seed=N * 7 + K + T)
+    w, a, w_ref, a_ref = _prep(bqm, trits, d16, x)
+    _say("mmvq_f32", N, K, T)
+    y2 = _host(bqm.mmvq_tq1_0(w, a, N, K, T))
+    y1 = _host(bqm.mmvq_tq1_0_f32(w, _dev(x), N, K, T))
+    assert np.array_equal(y1.view(np.uint32), y2.view(np.uint32))
+    _, y64, ab = oracle.mmvq(w_ref, a_ref, N, K, T)
+    _assert_close(y1, y64, ab, "mmvq_f32 %d %d %d" % (N, K, T))
+
+
+def test_mmvq_f32_quantization_edge_blocks(bqm):
+    """The fused staging quantizes exactly like q8_1_quantize, also on the
+    blocks where single and double rounding of s differ, zero blocks, ties,
+    fp16-subnormal and fp16-zero scales."""
+    x = _q8_edge_activations()
+    T, K = x.shape
+    rng = np.random.default_rng(11)
+    N = 70
+    trits = synth.ternary(rng, (N, K))
+    d16 = synth.block_scales_f16(rng, (N, K // 256), 0.01, 0.1)
+    w, a, w_ref, a_ref = _prep(bqm, trits, d16, x)
+    y2 = _host(bqm.mmvq_tq1_0(w, a, N, K, T))
+    y1 = _host(bqm.mmvq_tq1_0_f32(w, _dev(x), N, K, T))
+    assert np.array_equal(y1.view(np.uint32), y2.view(np.uint32))
+
+
+def test_mmvq_f32_decode_workload(bqm):
+    wl, inp = _workload_inputs("decode")
+    N, K = wl.N, wl.K
+    w, a, w_ref, a_ref = _prep(bqm, inp.trits, inp.d16, inp.x)
+    y = _host(bqm.mmvq_tq1_0_f32(w, _dev(inp.x[:1]), N, K, 1))
+    _, y64, ab = oracle.mmvq(w_ref, a_ref[:1], N, K, 1)
+    _assert_close(y, y64, ab, "decode fused")
