@@ -199,6 +199,53 @@ def read_probe_row(torch, wrot, R, nbytes, name, launches):
             "frac_of_8tbs": round(rd / best[0] / 1e3 / HBM_PEAK_GBS, 4)}
 
 
+def dequant_rows(torch, bqm, wrot, R, wbytes, name, N, K, launches):
+    """Dequantize the whole matrix (fp16, bf16, fp32) and gather 1024 rows
+    (fp16); beside them a copy probe moving as many bytes, for scale."""
+    rows_out = []
+    for dt, size in ((torch.float16, 2), (torch.bfloat16, 2), (torch.float32, 4)):
+        out = torch.empty((N, K), dtype=dt, device=wrot.device)
+        us = graph_us(torch, lambda i: bqm.tq1_dequantize(wrot[i % R], N, K, dtype=dt, out=out),
+                      launches)
+        b = wbytes + N * K * size
+        rows_out.append({"workload": name, "op": "tq1_dequantize", "dtype": str(dt).split(".")[1],
+                         "N": N, "K": K, "us": round(us, 3), "algorithmic_bytes": b,
+                         "gbs": round(b / us / 1e3, 1), "frac_of_8tbs": round(b / us / 1e3 / HBM_PEAK_GBS, 4)})
+        log("sweep", rows_out[-1])
+        del out
+    g = min(1024, N)
+    ids = torch.randint(0, N, (g,), dtype=torch.int32, device=wrot.device, generator=torch.Generator(
+        device=wrot.device).manual_seed(7))
+    out = torch.empty((g, K), dtype=torch.float16, device=wrot.device)
+    us = graph_us(torch, lambda i: bqm.tq1_dequantize(wrot[i % R], N, K, rows=ids, out=out), launches)
+    b = g * (K // 256) * 54 + g * 4 + g * K * 2
+    rows_out.append({"workload": name, "op": "tq1_get_rows", "dtype": "float16", "N": N, "K": K,
+                     "rows": g, "us": round(us, 3), "algorithmic_bytes": b,
+                     "gbs": round(b / us / 1e3, 1), "frac_of_8tbs": round(b / us / 1e3 / HBM_PEAK_GBS, 4)})
+    log("sweep", rows_out[-1])
+    # the copy probe on a buffer as large as the fp16 output: read + write
+    probes = ctypes.CDLL(os.path.join(ROOT, "bit_quantized_mat_amd", "libbqm_probes.so"))
+    probes.bqm_probe_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_uint64,
+                                      ctypes.c_int, ctypes.c_void_p]
+    nbytes = N * K * 2
+    src = torch.empty(nbytes, dtype=torch.uint8, device=wrot.device)
+    dst = torch.empty(nbytes, dtype=torch.uint8, device=wrot.device)
+    cur = lambda: ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    best = None
+    for grid in (1024, 4096, 16384):
+        us = graph_us(torch, lambda i: probes.bqm_probe_copy(ctypes.c_void_p(src.data_ptr()),
+                                                            ctypes.c_void_p(dst.data_ptr()),
+                                                            nbytes, grid, cur()), launches)
+        best = us if best is None else min(best, us)
+    rows_out.append({"workload": name, "op": "copy_probe", "bytes_moved": 2 * nbytes,
+                     "us": round(best, 3), "gbs": round(2 * nbytes / best / 1e3, 1),
+                     "frac_of_8tbs": round(2 * nbytes / best / 1e3 / HBM_PEAK_GBS, 4)})
+    log("sweep", rows_out[-1])
+    del src, dst, out
+    torch.cuda.empty_cache()
+    return rows_out
+
+
 def sweep(path, torch, np, bqm, synth, dev, launches, only=None):
     """Every workload shape and column count, cold weights, graph-timed.
     only: optional set of workload names to restrict the sweep to."""
@@ -215,6 +262,8 @@ def sweep(path, torch, np, bqm, synth, dev, launches, only=None):
         a_all = bqm.q8_1_quantize(torch.from_numpy(inp.x).to(dev))
         table.append(read_probe_row(torch, wrot, R, w0.numel(), name, launches))
         log("sweep", table[-1])
+        if name in ("decode", "ffn"):
+            table.extend(dequant_rows(torch, bqm, wrot, R, w0.numel(), name, N, K, launches))
         for T in wl.Ts:
             a = a_all[:T].contiguous()
             y = torch.empty((T, N), dtype=torch.float32, device=dev)

@@ -11,7 +11,7 @@ import os
 
 __all__ = [
     "BqmError", "library", "library_path", "tq1_pack", "q8_1_quantize", "mmvq_tq1_0",
-    "mmvq_tq1_0_f32", "MMVQ_F32_MAX_COLS",
+    "mmvq_tq1_0_f32", "MMVQ_F32_MAX_COLS", "tq1_dequantize",
     "mmvq_id_tq1_0", "mmvq_id_tq1_0_workspace_bytes", "mmvq_tq1_0_block_isums",
     "TQ1_BLOCK_BYTES", "Q81_BLOCK_BYTES", "MMVQ_MAX_COLS",
 ]
@@ -53,6 +53,7 @@ def library():
         L.q8_1_quantize.argtypes = [_p, _p, _i64, _i64, _p]
         L.mmvq_tq1_0.argtypes = [_p, _p, _p, _i64, _i64, _i32, _p]
         L.mmvq_tq1_0_f32.argtypes = [_p, _p, _p, _i64, _i64, _i32, _p]
+        L.tq1_dequantize.argtypes = [_p, _p, _p, _i64, _i64, _i64, _i32, _p]
         L.mmvq_tq1_0_block_isums.argtypes = [_p, _p, _p, _i64, _i64, _i32, _p]
         L.mmvq_id_tq1_0.argtypes = [_p, _p, _p, _p, _i64, _i64, _i64, _i64, _i32, _p, _sz, _p]
         L.mmvq_id_tq1_0_workspace_bytes.argtypes = [_i64, _i64, _i32]
@@ -61,7 +62,7 @@ def library():
         L.bqm_status_string.restype = ctypes.c_char_p
         L.bqm_version.restype = ctypes.c_int
         for name in ("tq1_pack", "q8_1_quantize", "mmvq_tq1_0", "mmvq_tq1_0_f32",
-                     "mmvq_tq1_0_block_isums", "mmvq_id_tq1_0"):
+                     "mmvq_tq1_0_block_isums", "mmvq_id_tq1_0", "tq1_dequantize"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -159,6 +160,27 @@ def mmvq_tq1_0_f32(w, x, N, K, T, out=None, stream=None):
           _dev_tensor(x, "x", (torch.float32,), T * K * 4, w.device),
           _dev_tensor(out, "out", (torch.float32,), T * N * 4, w.device),
           N, K, T, _stream(stream, w.device))
+    return out
+
+
+def tq1_dequantize(w, N, K, rows=None, dtype=None, out=None, stream=None):
+    """Dequantized rows [n_rows, K] of the packed [N, K] matrix w: row
+    rows[i] (int32 GPU tensor) or, with rows=None, all N rows; dtype
+    torch.float32, torch.float16 (default) or torch.bfloat16."""
+    torch = _torch()
+    dtype = torch.float16 if dtype is None else dtype
+    codes = {torch.float32: 0, torch.float16: 1, torch.bfloat16: 2}
+    if dtype not in codes:
+        raise TypeError("dtype must be float32, float16 or bfloat16")
+    n_rows = N if rows is None else rows.numel()
+    if out is None:
+        out = torch.empty((n_rows, K), dtype=dtype, device=w.device)
+    pr = ctypes.c_void_p(None) if rows is None else _dev_tensor(rows, "rows", (torch.int32,),
+                                                                 n_rows * 4, w.device)
+    _call("tq1_dequantize",
+          _dev_tensor(w, "w", (torch.uint8,), N * (K // 256) * TQ1_BLOCK_BYTES),
+          pr, _dev_tensor(out, "out", (dtype,), n_rows * K * out.element_size(), w.device),
+          N, K, n_rows, codes[dtype], _stream(stream, w.device))
     return out
 
 

@@ -118,6 +118,24 @@ int mmvq_tq1_0_block_isums(const void *w, const void *a, int32_t *isums, int64_t
     return bqm::launch_mmvq(w, a, nullptr, isums, N, K, T, as_stream(stream));
 }
 
+int tq1_dequantize(const void *w, const int32_t *rows, void *out, int64_t N, int64_t K,
+                   int64_t n_rows, int32_t out_dtype, void *stream)
+{
+    if (!w || !out)
+        return BQM_ERR_NULL;
+    if (int rc = check_matrix(N, K))
+        return rc;
+    if (n_rows < 1 || (!rows && n_rows > N) || n_rows * (K / 256) >= (1ll << 27) ||
+        out_dtype < BQM_DTYPE_F32 || out_dtype > BQM_DTYPE_BF16)
+        return BQM_ERR_SHAPE;
+    const uintptr_t out_align = out_dtype == BQM_DTYPE_F32 ? 15u : 7u;
+    if (!aligned4(w) || (rows && !aligned4(rows)) || ((uintptr_t)out & out_align))
+        return BQM_ERR_ALIGN;
+    if (int rc = check_device())
+        return rc;
+    return bqm::launch_tq1_dequantize(w, rows, out, N, K, n_rows, out_dtype, as_stream(stream));
+}
+
 size_t mmvq_id_tq1_0_workspace_bytes(int64_t E, int64_t T, int32_t n_used)
 {
     if (E < 1 || T < 1 || n_used < 1 || n_used > E || T * (int64_t)n_used > 65535)

@@ -1,0 +1,170 @@
+// dequant.hip -- TQ1_0 dequantization and row gather on gfx950.
+//
+// The two operations beside the mat-vec in "CUDA: TQ1_0 mat-vec is
+// load-bound by the per-32-element chunk contract" ("Current behavior": a
+// TQ1_0 dequantize kernel; "Proposed approach": the Vulkan work covering
+// dequant and get_rows): out[i][k] = fp32(d) * trit for source row rows[i]
+// (or i), written as fp32, fp16 or bf16.
+//
+// One wave per 256-element block, in element order: lane L writes elements
+// 4L..4L+3, so a wave's store is one contiguous run of the block's outputs
+// (512 bytes of fp16, 1 KiB of fp32). Those four elements are one digit
+// level c of one packed dword (the element map in include/bqm.h puts four
+// consecutive elements on four consecutive bytes), so the lane loads that
+// dword and extracts only level c: with X = v / 3^k in 8.8 fixed point per
+// 16-bit lane (tq1_decode.hpp), floor(v / 3^c) is byte 1 of X * 3^(k - c),
+// and the digit is floor(v / 3^c) - 3 floor(v / 3^(c+1)).
+#include "launch.hpp"
+#include "tq1_decode.hpp"
+
+namespace bqm {
+
+// fp32 -> bf16 bits, round to nearest even (finite values).
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f)
+{
+    const uint32_t x = __float_as_uint(f);
+    return (x + 0x7fffu + ((x >> 16) & 1u)) >> 16;
+}
+
+// The three values an element can take, d * (u - 1) for digit u = 0, 1, 2,
+// as 16-bit patterns (fp16 or bf16 of the fp32 products; -d is the negated
+// pattern, and d * 0 is a zero with d's sign): a byte-permute table,
+// t_lo = [-d | d * 0] (bytes 0..3), t_hi = [d | -] (bytes 4..7).
+struct HalfTable {
+    uint32_t lo, hi;
+};
+
+template <int DT>
+__device__ __forceinline__ HalfTable half_table(float d, uint32_t d16)
+{
+    // fp16 output: d itself is an fp16 value, so its pattern is the scale's
+    const uint32_t pd = DT == BQM_DTYPE_F16 ? d16 : f32_to_bf16_bits(d);
+    const uint32_t nd = pd ^ 0x8000u, zd = pd & 0x8000u;
+    return HalfTable{nd | (zd << 16), pd};
+}
+
+// Store the four values d * (u - 1) of the digit bytes of `u` at out + e.
+template <int DT>
+__device__ __forceinline__ void store_run(void *__restrict__ out, int64_t e, uint32_t u, float d,
+                                          const HalfTable &tab)
+{
+    if (DT == BQM_DTYPE_F32) {
+        float v[4];
+#pragma unroll
+        for (int k = 0; k < 4; k++)
+            v[k] = d * (float)((int)((u >> (8 * k)) & 0xffu) - 1);
+        *reinterpret_cast<float4 *>(static_cast<float *>(out) + e) = make_float4(v[0], v[1], v[2], v[3]);
+    } else {
+        // selector bytes (2u, 2u + 1) pick the element's pattern from the table
+        const uint32_t u2 = u + u;
+        const uint32_t s01 = __builtin_amdgcn_perm(0u, u2, 0x0c010c00u) * 0x0101u + 0x01000100u;
+        const uint32_t s23 = __builtin_amdgcn_perm(0u, u2, 0x0c030c02u) * 0x0101u + 0x01000100u;
+        const uint32_t lo = __builtin_amdgcn_perm(tab.hi, tab.lo, s01);
+        const uint32_t hi = __builtin_amdgcn_perm(tab.hi, tab.lo, s23);
+        *reinterpret_cast<u32x2 *>(static_cast<uint16_t *>(out) + e) = (u32x2){lo, hi};
+    }
+}
+
+// Digit level c (0..4) of the four bytes of a qs dword, or (qh) of a qh dword.
+__device__ __forceinline__ uint32_t digit_level(uint32_t w, int c, bool qh)
+{
+    const uint32_t e = w & kLaneMask;
+    const uint32_t o = __builtin_amdgcn_perm(0u, w, 0x0c030c01u);  // bytes 1, 3 -> lanes
+    const uint32_t mul = qh ? kQhMul : kQsMul, add = qh ? kQhAdd : kQsAdd;
+    const uint32_t shift = qh ? kQhShift : kQsShift;
+    const uint32_t e1 = pk_shr(__umul24(e, mul) + add, shift);
+    const uint32_t o1 = pk_shr(__umul24(o, mul) + add, shift);
+    // X1 holds v / 3^k with k = 4 (qs) or 3 (qh): floor(v / 3^c) is byte 1 of
+    // X1 * 3^(k-c); floor(v / 3^(c+1)) of X1 * 3^(k-c-1) (0 past the top digit)
+    const int k = qh ? 3 : 4;
+    const unsigned short pw[6] = {1, 3, 9, 27, 81, 0};
+    const unsigned short m_c = pw[k - c];
+    const unsigned short m_n = c + 1 <= k ? pw[k - c - 1] : (unsigned short)0;
+    const uint32_t f_c = hi_bytes(pk_mul(o1, m_c), pk_mul(e1, m_c));
+    const uint32_t f_n = hi_bytes(pk_mul(o1, m_n), pk_mul(e1, m_n));
+    return f_c - mul3_bytes(f_n);
+}
+
+constexpr int kDqBlocksPerWave = 8;  // loads of all of them are issued before any decode
+
+template <int DT>
+__global__ __launch_bounds__(256) void tq1_dequantize_kernel(const uint8_t *__restrict__ w,
+                                                             const int32_t *__restrict__ rows,
+                                                             void *__restrict__ out, int64_t N,
+                                                             int nb, int64_t n_rows)
+{
+    const int lane = threadIdx.x & 63;
+    // wave-uniform block coordinates (scalar registers)
+    const int64_t wave = (int64_t)blockIdx.x * (blockDim.x >> 6) +
+                         __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int64_t nblocks = n_rows * nb;
+    const int64_t first = wave * kDqBlocksPerWave;
+    if (first >= nblocks)
+        return;  // whole waves
+    // this lane's elements 4L..4L+3 of every block: their dword and digit level
+    const int e0 = 4 * lane;
+    int j, c;
+    if (e0 < 160) {
+        j = lane & 7;
+        c = e0 >> 5;
+    } else if (e0 < 240) {
+        j = 8 + (((e0 - 160) & 15) >> 2);
+        c = (e0 - 160) >> 4;
+    } else {
+        j = 12;
+        c = lane - 60;
+    }
+    const __amdgpu_buffer_rsrc_t rw = make_rsrc(w, (uint64_t)N * nb * kTq1BlockBytes);
+    int64_t i = first / nb;
+    int B = (int)(first - i * nb);
+    u32x2 v[kDqBlocksPerWave];
+    uint32_t dd[kDqBlocksPerWave], sh[kDqBlocksPerWave];
+#pragma unroll
+    for (int k = 0; k < kDqBlocksPerWave; k++) {
+        // blocks past the end reload the last one (their stores are skipped)
+        const int64_t ic = first + k < nblocks ? i : n_rows - 1;
+        const int Bc = first + k < nblocks ? B : nb - 1;
+        int64_t r = rows ? rows[ic] : ic;
+        r = r < 0 ? 0 : (r >= N ? N - 1 : r);  // ids outside [0, N) stay inside w
+        const uint32_t off = (uint32_t)((r * nb + Bc) * kTq1BlockBytes);
+        sh[k] = off & 3u;
+        const uint32_t base = off - sh[k];
+        v[k] = ld_b64(rw, base + 4 * j);
+        dd[k] = ld_b32(rw, base + 52);
+        if (++B == nb) {
+            B = 0;
+            i++;
+        }
+    }
+#pragma unroll
+    for (int k = 0; k < kDqBlocksPerWave; k++) {
+        if (first + k < nblocks) {
+            const uint32_t d16 = sh[k] ? (dd[k] >> 16) : (dd[k] & 0xffffu);
+            const float d = f16_bits_to_f32(d16);
+            const uint32_t u = digit_level(align_bytes(v[k].y, v[k].x, sh[k]), c, j == 12);
+            store_run<DT>(out, (first + k) * kTq1BlockElems + e0, u, d, half_table<DT>(d, d16));
+        }
+    }
+}
+
+int launch_tq1_dequantize(const void *w, const int32_t *rows, void *out, int64_t N, int64_t K,
+                          int64_t n_rows, int dtype, hipStream_t stream)
+{
+    const int nb = (int)(K / kTq1BlockElems);
+    const int64_t waves = (n_rows * nb + kDqBlocksPerWave - 1) / kDqBlocksPerWave;
+    const int64_t threads = waves * 64;
+    const dim3 grid((unsigned)((threads + 255) / 256));
+    const uint8_t *wp = static_cast<const uint8_t *>(w);
+    if (dtype == BQM_DTYPE_F32)
+        hipLaunchKernelGGL((tq1_dequantize_kernel<BQM_DTYPE_F32>), grid, dim3(256), 0, stream, wp,
+                           rows, out, N, nb, n_rows);
+    else if (dtype == BQM_DTYPE_F16)
+        hipLaunchKernelGGL((tq1_dequantize_kernel<BQM_DTYPE_F16>), grid, dim3(256), 0, stream, wp,
+                           rows, out, N, nb, n_rows);
+    else
+        hipLaunchKernelGGL((tq1_dequantize_kernel<BQM_DTYPE_BF16>), grid, dim3(256), 0, stream, wp,
+                           rows, out, N, nb, n_rows);
+    return check_launch();
+}
+
+}  // namespace bqm

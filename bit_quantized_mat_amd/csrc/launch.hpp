@@ -29,6 +29,8 @@ inline void allow_dynamic_lds(const void *kernel, size_t bytes)
 }
 
 int launch_q8_1_quantize(const float *x, void *a, int64_t T, int64_t K, hipStream_t stream);
+int launch_tq1_dequantize(const void *w, const int32_t *rows, void *out, int64_t N, int64_t K,
+                          int64_t n_rows, int dtype, hipStream_t stream);
 int launch_tq1_pack(const int8_t *trits, const uint16_t *d, void *w, int64_t N, int64_t K,
                     hipStream_t stream);
 // Lanes that share one output row in the mat-vec kernels (log2): the smallest

@@ -27,7 +27,6 @@
 namespace bqm {
 
 typedef int i32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x3 __attribute__((ext_vector_type(3)));
 
 // This lane's share of one 54-byte block (see the layout above): qs dwords
 // 2kg and 2kg+1, qs dword 8+kg, the qh dword and the fp16 scale, read as the

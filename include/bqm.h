@@ -72,6 +72,13 @@ enum {
     BQM_ERR_DEVICE = -6      /* the current device is not a gfx950 GPU         */
 };
 
+/* Element types of dequantized output. */
+enum {
+    BQM_DTYPE_F32 = 0,   /* IEEE binary32                                     */
+    BQM_DTYPE_F16 = 1,   /* IEEE binary16 (exact here: +-d or 0)              */
+    BQM_DTYPE_BF16 = 2   /* bfloat16, rounded to nearest even                 */
+};
+
 /* Largest number of activation columns mmvq_tq1_0 accepts. */
 #define BQM_MMVQ_MAX_COLS 32
 
@@ -116,6 +123,21 @@ BQM_API int mmvq_tq1_0(const void *w, const void *a, float *y,
  * Alignment: w, x, y 4 bytes. */
 BQM_API int mmvq_tq1_0_f32(const void *w, const float *x, float *y,
                    int64_t N, int64_t K, int32_t T, void *stream);
+
+/* Dequantize TQ1_0 rows (the dequantize and get_rows operations that sit
+ * beside the mat-vec, "CUDA: TQ1_0 mat-vec is load-bound by the per-32-element
+ * chunk contract", "Current behavior" and "Proposed approach"):
+ *   out[i][k] = fp32(d[r][k/256]) * trit[r][k], r = rows[i] (rows == NULL: r = i),
+ *   computed as an fp32 product (a zero trit under a negative scale gives -0)
+ *   and stored as out_dtype (BQM_DTYPE_*).
+ *   w [N][K/256] TQ1_0 blocks; rows [n_rows] int32 (may be NULL, then
+ *   n_rows <= N); out [n_rows][K] elements of out_dtype.
+ * Shapes: N >= 1, K >= 256, K % 256 == 0, n_rows >= 1, n_rows * K / 256 < 2^27,
+ * the weight matrix below 4 GiB. Row ids outside [0, N) are not checked;
+ * they read a clamped row, never outside w.
+ * Alignment: w and rows 4 bytes; out 16 bytes (fp32) or 8 bytes (fp16, bf16). */
+BQM_API int tq1_dequantize(const void *w, const int32_t *rows, void *out,
+                   int64_t N, int64_t K, int64_t n_rows, int32_t out_dtype, void *stream);
 
 /* Expert-routed product (mixture of experts):
  *   y[t][s][n] = mmvq(W[ids[t][s]], a[t])[n]   for t < T, s < n_used

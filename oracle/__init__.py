@@ -55,6 +55,10 @@ def lib():
         L.oracle_mmvq.restype = ctypes.c_int
         L.oracle_mmvq_id.argtypes = [_p, _p, _p, _p, _p, _p, _i64, _i64, _i64, _i64, _i64]
         L.oracle_mmvq_id.restype = ctypes.c_int
+        L.oracle_f32_to_bf16.restype = ctypes.c_uint16
+        L.oracle_f32_to_bf16.argtypes = [ctypes.c_float]
+        L.oracle_tq1_dequantize_rows.argtypes = [_p, _p, _p, _i64, _i64, _i64, ctypes.c_int]
+        L.oracle_tq1_dequantize_rows.restype = ctypes.c_int
         L.oracle_set_threads.argtypes = [ctypes.c_int]
         L.oracle_max_threads.restype = ctypes.c_int
         _lib = L
@@ -185,6 +189,30 @@ def mmvq_id(w, a, ids, E, N, K, T, n_used):
     _check(lib().oracle_mmvq_id(_ptr(w), _ptr(a), _ptr(ids), _ptr(y), _ptr(y64), _ptr(ab),
                                 E, N, K, T, n_used), "mmvq_id")
     return y, y64, ab
+
+
+DTYPES = {"f32": (0, np.float32), "f16": (1, np.uint16), "bf16": (2, np.uint16)}
+
+
+def f32_to_bf16_bits(x):
+    """bfloat16 bit patterns (uint16) of fp32 values, round to nearest even."""
+    x = np.asarray(x, dtype=np.float32)
+    f = lib().oracle_f32_to_bf16
+    return np.array([f(float(v)) for v in x.ravel()], dtype=np.uint16).reshape(x.shape)
+
+
+def tq1_dequantize(w, N, K, dtype="f32", rows=None):
+    """Dequantized rows [n_rows, K] of a packed [N, K] matrix: fp32 values,
+    or fp16 / bf16 bit patterns (uint16); rows=None takes rows 0..N-1."""
+    code, npdt = DTYPES[dtype]
+    w = _c(w, np.uint8)
+    rws = None if rows is None else _c(rows, np.int32)
+    n_rows = N if rows is None else int(rws.size)
+    out = np.empty((n_rows, K), dtype=npdt)
+    rc = lib().oracle_tq1_dequantize_rows(_ptr(w), None if rws is None else _ptr(rws), _ptr(out),
+                                          N, K, n_rows, code)
+    _check(rc, "tq1_dequantize")
+    return out
 
 
 def set_threads(n):

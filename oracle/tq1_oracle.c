@@ -484,6 +484,65 @@ int oracle_mmvq_id(const uint8_t *w, const uint8_t *a, const int32_t *ids,
     return bad ? -1 : 0;
 }
 
+/* ------------------------------------------------------------------------ */
+/* Dequantization and row gather (the dequantize and get_rows operations    */
+/* [P1] "Current behavior" and "Proposed approach" list beside the mat-vec). */
+/* ------------------------------------------------------------------------ */
+
+/* float -> bfloat16 bits, round to nearest, ties to even (finite inputs):
+ * bfloat16 is the upper half of the binary32 pattern; the lower half decides
+ * the rounding. */
+uint16_t oracle_f32_to_bf16(float f)
+{
+    uint32_t x;
+    memcpy(&x, &f, 4);
+    uint32_t upper = x >> 16, lower = x & 0xffffu;
+    if (lower > 0x8000u || (lower == 0x8000u && (upper & 1u)))
+        upper += 1u;
+    return (uint16_t)upper;
+}
+
+/* out row i = dequantized source row (rows ? rows[i] : i): element k is
+ * v = fp32(d) * trit (an fp32 product, so a zero trit under a negative scale
+ * gives -0), stored as out_dtype 0 = fp32, 1 = fp16 bits, 2 = bf16 bits.
+ * Returns -1 on a bad shape, a row id outside [0, N) or a bad packed byte. */
+int oracle_tq1_dequantize_rows(const uint8_t *w, const int32_t *rows, void *out,
+                               int64_t N, int64_t K, int64_t n_rows, int out_dtype)
+{
+    if (N <= 0 || n_rows < 0 || K <= 0 || K % TQ1_BLOCK_ELEMS || out_dtype < 0 ||
+        out_dtype > 2)
+        return -1;
+    int64_t nb = K / TQ1_BLOCK_ELEMS;
+    for (int64_t i = 0; i < n_rows; i++)
+        if (rows && (rows[i] < 0 || rows[i] >= N))
+            return -1;
+    int bad = 0;
+#pragma omp parallel for schedule(static) reduction(| : bad)
+    for (int64_t i = 0; i < n_rows; i++) {
+        int64_t r = rows ? rows[i] : i;
+        int8_t *tr = (int8_t *)malloc((size_t)K);
+        uint16_t *dd = (uint16_t *)malloc((size_t)nb * sizeof(uint16_t));
+        if (!tr || !dd || unpack_row(w + r * nb * TQ1_BLOCK_BYTES, K, tr, dd)) {
+            bad = 1;
+            free(tr);
+            free(dd);
+            continue;
+        }
+        for (int64_t k = 0; k < K; k++) {
+            float v = oracle_f16_to_f32(dd[k / TQ1_BLOCK_ELEMS]) * (float)tr[k];
+            if (out_dtype == 0)
+                ((float *)out)[i * K + k] = v;
+            else if (out_dtype == 1)
+                ((uint16_t *)out)[i * K + k] = oracle_f32_to_f16(v);
+            else
+                ((uint16_t *)out)[i * K + k] = oracle_f32_to_bf16(v);
+        }
+        free(tr);
+        free(dd);
+    }
+    return bad ? -1 : 0;
+}
+
 /* Thread control for the timed CPU baseline (OpenMP over output rows). */
 void oracle_set_threads(int n)
 {

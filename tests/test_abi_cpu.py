@@ -23,6 +23,7 @@ def _declared_functions():
 def test_header_declares_the_four_calls():
     names = _declared_functions()
     for n in ("tq1_pack", "q8_1_quantize", "mmvq_tq1_0", "mmvq_tq1_0_f32", "mmvq_id_tq1_0",
+              "tq1_dequantize",
               "mmvq_id_tq1_0_workspace_bytes", "mmvq_tq1_0_block_isums",
               "bqm_status_string", "bqm_version"):
         assert n in names
@@ -109,6 +110,24 @@ def test_mmvq_rejects(fn, args, expect):
 ])
 def test_mmvq_f32_rejects(args, expect):
     assert bqm.library().mmvq_tq1_0_f32(*args) == expect
+
+
+@pytest.mark.parametrize("args,expect", [
+    ((None, None, GOOD, 8, 256, 8, 1, None), -1),
+    ((GOOD, None, None, 8, 256, 8, 1, None), -1),
+    ((GOOD, None, GOOD, 0, 256, 8, 1, None), -2),
+    ((GOOD, None, GOOD, 8, 300, 8, 1, None), -2),
+    ((GOOD, None, GOOD, 8, 256, 0, 1, None), -2),
+    ((GOOD, None, GOOD, 8, 256, 9, 1, None), -2),         # more rows than N without ids
+    ((GOOD, GOOD, GOOD, 8, 256, 9, 3, None), -2),         # unknown dtype
+    ((GOOD, GOOD, GOOD, 8, 256, 1 << 27, 0, None), -2),   # too many blocks
+    ((ODD, None, GOOD, 8, 256, 8, 1, None), -3),
+    ((GOOD, ODD, GOOD, 8, 256, 8, 1, None), -3),
+    ((GOOD, None, P(0x100008), 8, 256, 8, 0, None), -3),  # fp32 output needs 16 bytes
+    ((GOOD, None, P(0x100004), 8, 256, 8, 1, None), -3),  # fp16 output needs 8 bytes
+])
+def test_tq1_dequantize_rejects(args, expect):
+    assert bqm.library().tq1_dequantize(*args) == expect
 
 
 def test_mmvq_id_rejects():

@@ -122,3 +122,24 @@ def test_packed_trit_conversion_exhaustive():
                 [x % 3 - 1 for x in vs]
             assert _signed_bytes(_trits_from_digits(_pack([x // 81 for x in vs]))) == \
                 [x // 81 - 1 for x in vs]
+
+
+def test_single_level_digit_extraction_exhaustive():
+    """Dequantization extracts one digit level per lane: floor(v / 3^c) is
+    byte 1 of X1 * 3^(k - c) in each 16-bit lane (k = 4 for qs bytes, 3 for
+    qh), and the digit is that floor minus 3 times the next one. Every byte
+    value, every level, against Python's base-3 digits."""
+    for qh, nbytes_max, k in ((False, 243, 4), (True, 81, 3)):
+        mul = C["kQhMul"] if qh else C["kQsMul"]
+        add = C["kQhAdd"] if qh else C["kQsAdd"]
+        shift = C["kQhShift"] if qh else C["kQsShift"]
+        for v in range(nbytes_max):
+            x1 = ((mul * v + add) & M16) >> shift
+            for c in range(k + 1):
+                m_c = 3 ** (k - c)
+                m_n = 3 ** (k - c - 1) if c + 1 <= k else 0
+                assert x1 * m_c <= M16
+                f_c = ((x1 * m_c) & M16) >> 8
+                f_n = ((x1 * m_n) & M16) >> 8
+                assert f_c == v // 3 ** c, (qh, v, c)
+                assert f_c - 3 * f_n == (v // 3 ** c) % 3, (qh, v, c)

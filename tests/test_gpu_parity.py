@@ -385,3 +385,36 @@ def test_mmvq_f32_decode_workload(bqm):
     y = _host(bqm.mmvq_tq1_0_f32(w, _dev(inp.x[:1]), N, K, 1))
     _, y64, ab = oracle.mmvq(w_ref, a_ref[:1], N, K, 1)
     _assert_close(y, y64, ab, "decode fused")
+
+
+# ---------------------------------------------------------------------------
+# Dequantization and row gather: every bit equal to the oracle's
+# ---------------------------------------------------------------------------
+
+def _dq_bits(t):
+    import torch
+    if t.dtype == torch.float32:
+        return t.view(torch.int32).cpu().numpy().view(np.uint32)
+    return t.view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+@pytest.mark.parametrize("N,K", [(1, 256), (3, 768), (70, 4096), (129, 2304), (16, 16384)])
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
+def test_tq1_dequantize_bit_exact(bqm, N, K, dtype):
+    import torch
+    tdt = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}[dtype]
+    trits, d16, _ = _case(N, K, 1, seed=N + K)
+    d16[0, 0] = 0xB800                          # one negative scale: zero trits give -0
+    w = bqm.tq1_pack(_dev(trits), _dev(d16.view(np.int16)))
+    w_ref = oracle.tq1_pack(trits, d16)
+    _say("tq1_dequantize", N, K, dtype)
+    got = _dq_bits(bqm.tq1_dequantize(w, N, K, dtype=tdt))
+    ref = oracle.tq1_dequantize(w_ref, N, K, dtype)
+    assert np.array_equal(got, ref.view(got.dtype))
+    # row gather: repeats, first and last rows, and more rows than N
+    rng = np.random.default_rng(N * 3 + K)
+    rows = rng.integers(0, N, 2 * N + 3).astype(np.int32)
+    rows[0], rows[-1] = 0, N - 1
+    got = _dq_bits(bqm.tq1_dequantize(w, N, K, rows=_dev(rows), dtype=tdt))
+    ref = oracle.tq1_dequantize(w_ref, N, K, dtype, rows=rows)
+    assert np.array_equal(got, ref.view(got.dtype))

@@ -24,6 +24,10 @@ MUTATIONS = {
     "byte_walk_drops_sum_q": ("= su[b] - sq;", "= su[b];"),
     "f16_ties_up": ("if (rem > half || (rem == half && (n & 1)))", "if (rem >= half)"),
     "clamp_126": ("if (q > 127)\n                    q = 127;", "if (q > 126)\n                    q = 126;"),
+    "dequant_scale_of_next_block": ("oracle_f16_to_f32(dd[k / TQ1_BLOCK_ELEMS])",
+                                    "oracle_f16_to_f32(dd[(k / TQ1_BLOCK_ELEMS + 1) % nb])"),
+    "bf16_truncates": ("if (lower > 0x8000u || (lower == 0x8000u && (upper & 1u)))",
+                       "if (0)"),
 }
 
 

@@ -366,3 +366,69 @@ def test_zipf_routing_has_no_repeats_per_token():
     for row in ids:
         assert len(set(row.tolist())) == 8
     assert ids.min() >= 0 and ids.max() < 128
+
+
+# ---------------------------------------------------------------------------
+# Dequantization and row gather
+# ---------------------------------------------------------------------------
+
+def test_bf16_rounding_matches_torch():
+    """The oracle's fp32 -> bfloat16 rounding against torch's CPU conversion
+    (round to nearest even), on random values, exact ties and neighbours."""
+    import torch
+    rng = np.random.default_rng(41)
+    bits = rng.integers(0, 2**32, 20000, dtype=np.uint64).astype(np.uint32)
+    ties = (rng.integers(0, 2**16, 2000, dtype=np.uint64).astype(np.uint32) << 16) | 0x8000
+    x = np.concatenate([bits, ties, ties + 1, ties - 1]).view(np.float32)
+    x = x[np.isfinite(x) & (np.abs(x) < 3e38)]
+    got = oracle.f32_to_bf16_bits(x)
+    ref = torch.from_numpy(x.copy()).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(got, ref)
+
+
+@pytest.mark.parametrize("name,trits,expect", _parse_golden_blocks(), ids=lambda v: v if isinstance(v, str) else "")
+def test_dequantize_hand_worked_blocks(name, trits, expect):
+    """Pack the hand-worked blocks with a scale of -1.5 and dequantize: every
+    element is -1.5 * trit (fp16 -1.5 = 0xBE00)."""
+    w = oracle.tq1_pack(trits.reshape(1, 256), np.array([[0xBE00]], np.uint16))
+    v = oracle.tq1_dequantize(w, 1, 256, "f32")
+    assert np.array_equal(v[0], np.float32(-1.5) * trits.astype(np.float32)), name
+    # a zero trit under a negative scale is the fp32 product, -0
+    zeros = trits == 0
+    assert np.all(np.signbit(v[0][zeros]))
+
+
+def test_dequantize_then_dot_is_the_unit_scale_mat_vec():
+    """Dequantized weights times integer activations equal the oracle mat-vec
+    with unit activation scales (itself pinned to the integer mat-vec)."""
+    N, K, T = 20, 1280, 3
+    rng = np.random.default_rng(43)
+    trits = synth.ternary(rng, (N, K))
+    d16 = synth.block_scales_f16(rng, (N, K // 256), 0.01, 0.1)
+    w = oracle.tq1_pack(trits, d16)
+    q = rng.integers(-127, 128, (T, K)).astype(np.int8)
+    a = synth.q8_1_blocks_from_fields(q, np.full((T, K // 32), 0x3C00, np.uint16),
+                                      np.zeros((T, K // 32), np.uint16))
+    _, y64, ab = oracle.mmvq(w, a, N, K, T)
+    W = oracle.tq1_dequantize(w, N, K, "f32").astype(np.float64)
+    ref = q.astype(np.float64) @ W.T
+    assert np.all(np.abs(ref - y64) <= 1e-12 * ab + 1e-300)
+
+
+def test_dequantize_dtypes_and_row_gather():
+    N, K = 7, 768
+    rng = np.random.default_rng(44)
+    trits = synth.ternary(rng, (N, K))
+    d16 = synth.block_scales_f16(rng, (N, K // 256), 0.01, 0.1)
+    d16[3, 1] = 0xB800                      # a negative scale (-0.5)
+    w = oracle.tq1_pack(trits, d16)
+    f32 = oracle.tq1_dequantize(w, N, K, "f32")
+    assert np.array_equal(oracle.tq1_dequantize(w, N, K, "f16"),
+                          f32.astype(np.float16).view(np.uint16))
+    assert np.array_equal(oracle.tq1_dequantize(w, N, K, "bf16"), oracle.f32_to_bf16_bits(f32))
+    rows = np.array([6, 0, 3, 3, 1], np.int32)
+    for dt in ("f32", "f16", "bf16"):
+        full = oracle.tq1_dequantize(w, N, K, dt)
+        assert np.array_equal(oracle.tq1_dequantize(w, N, K, dt, rows=rows), full[rows])
+    with pytest.raises(oracle.OracleError):
+        oracle.tq1_dequantize(w, N, K, "f32", rows=np.array([0, 7], np.int32))
