@@ -295,8 +295,10 @@ def sweep(path, torch, np, bqm, synth, dev, launches, only=None):
         ids = torch.from_numpy(ids_np).to(dev)
         a = a_all[:T].contiguous()
         y = torch.empty((T, n_used, N), dtype=torch.float32, device=dev)
+        ws = torch.empty(max(bqm.mmvq_id_tq1_0_workspace_bytes(E, T, n_used), 256),
+                         dtype=torch.uint8, device=dev)
         us = graph_us(torch, lambda i: bqm.mmvq_id_tq1_0(wrot[i % R], a, ids, E, N, K, T, n_used,
-                                                         out=y), launches)
+                                                         out=y, workspace=ws), launches)
         b, distinct = moe_algorithmic_bytes(ids_np, N, K)
         row = {"workload": "moe", "op": "mmvq_id_tq1_0", "E": E, "N": N, "K": K, "T": T,
                "n_used": n_used, "distinct_experts": distinct, "us": round(us, 3),
@@ -328,8 +330,10 @@ def profile_run(spec, torch, np, bqm, synth, dev):
     if wl.experts:
         ids = torch.from_numpy(np.ascontiguousarray(inp.ids[:T])).to(dev)
         y = torch.empty((T, wl.n_used, N), dtype=torch.float32, device=dev)
+        ws = torch.empty(max(bqm.mmvq_id_tq1_0_workspace_bytes(wl.experts, T, wl.n_used), 256),
+                         dtype=torch.uint8, device=dev)
         run = lambda i: bqm.mmvq_id_tq1_0(wrot[i % R], a, ids, wl.experts, N, K, T, wl.n_used,
-                                          out=y)
+                                          out=y, workspace=ws)
     else:
         y = torch.empty((T, N), dtype=torch.float32, device=dev)
         run = lambda i: bqm.mmvq_tq1_0(wrot[i % R], a, N, K, T, out=y)

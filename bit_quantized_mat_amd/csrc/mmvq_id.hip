@@ -9,161 +9,411 @@
 // per-expert grid that "tools: add mmq-tune, an MMQ tile-width autotuning
 // harness" (Summary) describes for the production MoE path.
 //
-// Routing runs inside every workgroup, from ids alone, with no second launch
-// and no host round trip:
-//   1. count the (token, slot) pairs of each expert (LDS atomics; exact);
-//   2. exclusive scan of ceil(count / 8) over experts gives each expert's
-//      first work item; work item blockIdx.y belongs to the expert whose range
-//      holds it, and is that expert's k-th group of eight pairs;
-//   3. the workgroup's pairs are the k-th eight of its expert in pair-index
-//      order (one wave, ballots and prefix popcounts), so every workgroup of
-//      an item agrees on its columns.
-// The multiply itself is the staged multi-column body of mmvq_staged.hip with
-// the columns gathered by token and the outputs scattered by pair. Each
-// column's arithmetic does not depend on which other columns share the item,
-// so results are bitwise those of a plain one-column call on the expert.
+// Work item: one expert and up to kIdCols of its (token, slot) pairs. Two ways
+// to find them, both exact and both free of host round trips:
+//   - up to 64 pairs: inside every wave, from ids alone. Each lane holds one
+//     pair; ballots over the bits of the expert id give each lane the set of
+//     lanes routed to the same expert, hence its rank among them. A pair whose
+//     rank is a multiple of kIdCols opens an item; items are numbered in
+//     pair-index order of their first pair.
+//   - more pairs: a one-workgroup pre-pass (mmvq_id_route_kernel) counts,
+//     scans and scatters the pairs by expert into the caller's workspace, and
+//     the product kernel reads its item from there.
+// The multiply is the staged multi-column body (byte-major decode, activations
+// in LDS) with the columns gathered by token and the outputs scattered by pair.
+// A workgroup stages its item's columns once and then walks several groups of
+// rows, so the staging is amortised over more weight bytes as the number of
+// items grows. Each column's arithmetic does not depend on which other columns
+// share the item, nor on the rows a workgroup walks, so results are bitwise
+// those of a plain one-column call on the expert.
 #include "launch.hpp"
 #include "mmvq_staged.hpp"
 
 namespace bqm {
 
-constexpr int kIdCols = 8;       // pairs per work item
-constexpr int kIdMaxExperts = 4096;
+constexpr int kIdCols = 8;             // pairs per work item
+constexpr int kIdWaveRouteMax = 64;    // pairs routed inside the wave
+constexpr int kIdMaxExperts = 4096;    // experts the routing pre-pass handles
+constexpr int kRouteThreads = 1024;
 
-__global__ __launch_bounds__(256) void mmvq_id_kernel(const uint8_t *__restrict__ w,
-                                                      const uint8_t *__restrict__ a,
-                                                      const int32_t *__restrict__ ids,
-                                                      float *__restrict__ y, int E, int64_t N,
-                                                      int nb, int T, int n_used, int lr_log2,
-                                                      int chunk, int route_dwords)
+// Upper bound of the number of work items: sum over experts of
+// ceil(count / kIdCols) with at most min(E, P) experts in use.
+static int64_t id_max_items(int64_t E, int64_t P)
 {
-    extern __shared__ uint4 lds4[];
-    int *cnt = reinterpret_cast<int *>(lds4);        // [E]
-    int *start = cnt + E;                             // [E + 1]
-    int *sel = start + E + 1;                         // [kIdCols + 1]
-    uint32_t *act = reinterpret_cast<uint32_t *>(lds4) + route_dwords;
-    const int tid = threadIdx.x;
-    const int P = T * n_used;
+    const int64_t active = E < P ? E : P;
+    return (P + (kIdCols - 1) * active + kIdCols - 1) / kIdCols;
+}
 
-    // 1. pairs per expert
-    for (int e = tid; e < E; e += 256)
+// ---------------------------------------------------------------------------
+// Routing pre-pass. Workspace layout (int32):
+//   ws[0]                            number of items
+//   ws[1 + 3k], [2 + 3k], [3 + 3k]   item k: expert, first run slot, pairs
+//   ws[1 + 3 max_items + slot]       pair index held by run slot `slot`
+// An expert's pairs occupy consecutive run slots; the order inside the run
+// follows atomic timing, which is harmless because the columns of an item are
+// computed independently. Pairs whose id is outside [0, E) are dropped.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(kRouteThreads) void mmvq_id_route_kernel(
+    const int32_t *__restrict__ ids, int32_t *__restrict__ ws, int E, int P, int max_items)
+{
+    __shared__ int cnt[kIdMaxExperts];   // pair counts, then first run slots
+    __shared__ int fill[kIdMaxExperts];  // run slots taken so far
+    __shared__ int part[kRouteThreads];  // per-thread pair sums, then their exclusive scan
+    __shared__ int ipart[kRouteThreads]; // the same for items
+    const int tid = threadIdx.x;
+    for (int e = tid; e < E; e += kRouteThreads) {
         cnt[e] = 0;
+        fill[e] = 0;
+    }
     __syncthreads();
-    for (int p = tid; p < P; p += 256) {
+    for (int p = tid; p < P; p += kRouteThreads) {
         const int e = ids[p];
         if ((unsigned)e < (unsigned)E)
             atomicAdd(&cnt[e], 1);
     }
     __syncthreads();
-    // 2. first work item of each expert
+    // thread t owns experts [t*per, (t+1)*per): its sums, then one wave scans
+    // the 1024 sums (16 per lane) and each thread walks its experts again
+    const int per = (E + kRouteThreads - 1) / kRouteThreads;
+    int s = 0, si = 0;
+    for (int k = 0; k < per; k++) {
+        const int e = tid * per + k;
+        if (e < E) {
+            s += cnt[e];
+            si += (cnt[e] + kIdCols - 1) / kIdCols;
+        }
+    }
+    part[tid] = s;
+    ipart[tid] = si;
+    __syncthreads();
     if (tid < 64) {
-        int run = 0;
-        for (int base = 0; base < E; base += 64) {
-            const int e = base + tid;
-            const int v = e < E ? (cnt[e] + kIdCols - 1) / kIdCols : 0;
-            int x = v;
-            for (int m = 1; m < 64; m <<= 1) {
-                const int u = __shfl_up(x, m, 64);
-                if (tid >= m)
-                    x += u;
+        int a[16], b[16], ra = 0, rb = 0;
+#pragma unroll
+        for (int k = 0; k < 16; k++) {
+            a[k] = part[tid * 16 + k];
+            b[k] = ipart[tid * 16 + k];
+            ra += a[k];
+            rb += b[k];
+        }
+        int xa = ra, xb = rb;
+#pragma unroll
+        for (int m = 1; m < 64; m <<= 1) {
+            const int ua = __shfl_up(xa, m, 64), ub = __shfl_up(xb, m, 64);
+            if (tid >= m) {
+                xa += ua;
+                xb += ub;
             }
-            if (e < E)
-                start[e] = run + x - v;
-            run += __shfl(x, 63, 64);
         }
-        if (tid == 0)
-            start[E] = run;
+        int oa = xa - ra, ob = xb - rb;
+#pragma unroll
+        for (int k = 0; k < 16; k++) {
+            part[tid * 16 + k] = oa;
+            ipart[tid * 16 + k] = ob;
+            oa += a[k];
+            ob += b[k];
+        }
+        if (tid == 63)
+            ws[0] = xb;
     }
     __syncthreads();
-    const int item = blockIdx.y;
-    if (item >= start[E])
-        return;  // uniform: every thread read the same LDS value
-    int lo = 0, hi = E;  // largest expert whose first item is <= item
-    while (hi - lo > 1) {
-        const int mid = (lo + hi) >> 1;
-        if (start[mid] <= item)
-            lo = mid;
-        else
-            hi = mid;
-    }
-    const int e = lo;
-    const int want0 = (item - start[e]) * kIdCols;
-    // 3. this item's pairs, in pair-index order
-    if (tid < 64) {
-        int run = 0;
-        for (int base = 0; base < P && run < want0 + kIdCols; base += 64) {
-            const int p = base + tid;
-            const bool m = p < P && ids[p] == e;
-            const unsigned long long mask = __ballot(m);
-            const int rank = run + __popcll(mask & ((1ull << tid) - 1ull));
-            if (m && rank >= want0 && rank < want0 + kIdCols)
-                sel[rank - want0] = p;
-            run += __popcll(mask);
+    int32_t *items = ws + 1;
+    int32_t *runs = ws + 1 + 3 * max_items;
+    int off = part[tid], ioff = ipart[tid];
+    for (int k = 0; k < per; k++) {
+        const int e = tid * per + k;
+        if (e < E) {
+            const int c = cnt[e];
+            for (int i = 0; i * kIdCols < c; i++) {
+                int32_t *it = items + 3 * (ioff + i);
+                it[0] = e;
+                it[1] = off + i * kIdCols;
+                it[2] = min(kIdCols, c - i * kIdCols);
+            }
+            cnt[e] = off;
+            off += c;
+            ioff += (c + kIdCols - 1) / kIdCols;
         }
-        if (tid == 0)
-            sel[kIdCols] = min(run - want0, kIdCols);
     }
     __syncthreads();
-    const int Tc = sel[kIdCols];
+    for (int p = tid; p < P; p += kRouteThreads) {
+        const int e = ids[p];
+        if ((unsigned)e < (unsigned)E)
+            runs[cnt[e] + atomicAdd(&fill[e], 1)] = p;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// The work item of this workgroup (values uniform across the workgroup).
+// ---------------------------------------------------------------------------
+struct IdItem {
+    int e;               // expert
+    int Tc;              // pairs, 1..kIdCols
+    int sel[kIdCols];    // pair indices (t >= Tc: a copy of sel[0])
+};
+
+// Wave-local routing of P <= 64 pairs; false if item is past the last one.
+__device__ __forceinline__ bool route_in_wave(const int32_t *__restrict__ ids, int E, int P,
+                                              int item, IdItem &it)
+{
+    const int lane = threadIdx.x & 63;
+    const int e = lane < P ? ids[lane] : -1;
+    const bool valid = (unsigned)e < (unsigned)E;
+    const uint64_t below = (1ull << lane) - 1ull;
+    // lanes routed to my expert: valid lanes that agree on every id bit
+    uint64_t same = __ballot(valid);
+    const int nbits = E > 1 ? 32 - __clz(E - 1) : 0;
+    for (int k = 0; k < nbits; k++) {
+        const bool bit = (e >> k) & 1;
+        const uint64_t b = __ballot(bit);
+        same &= bit ? b : ~b;
+    }
+    const int rank = __popcll(same & below);
+    const bool opens = valid && rank % kIdCols == 0;
+    const uint64_t openers = __ballot(opens);
+    if (item >= __popcll(openers))
+        return false;
+    const uint64_t mine = __ballot(opens && __popcll(openers & below) == item);
+    const int lead = __builtin_amdgcn_readfirstlane(__builtin_ctzll(mine));
+    const int e_it = __builtin_amdgcn_readlane(e, lead);
+    const int r0 = __builtin_amdgcn_readlane(rank, lead);
+    uint64_t m = __ballot(valid && e == e_it && rank >= r0 && rank < r0 + kIdCols);
+    it.e = e_it;
+    it.Tc = __popcll(m);
+    const int first = __builtin_ctzll(m);
+#pragma unroll
+    for (int t = 0; t < kIdCols; t++) {
+        it.sel[t] = m ? (int)__builtin_ctzll(m) : first;
+        m &= m - 1;
+    }
+    return true;
+}
+
+// The item written by the routing pre-pass; false if item is past the last one.
+__device__ __forceinline__ bool route_from_workspace(const int32_t *__restrict__ routed,
+                                                     int max_items, int item, IdItem &it)
+{
+    if (item >= routed[0])
+        return false;
+    const int32_t *p = routed + 1 + 3 * item;
+    const int32_t *runs = routed + 1 + 3 * max_items + p[1];
+    it.e = p[0];
+    it.Tc = p[2];
+#pragma unroll
+    for (int t = 0; t < kIdCols; t++)
+        it.sel[t] = runs[t < it.Tc ? t : 0];
+    return true;
+}
+
+// Stage Tc whole activation columns (nb blocks each) in the staged layout,
+// column t at act + t * nb * kActStride, with several loads in flight per lane.
+__device__ __forceinline__ void stage_item_columns(uint32_t *__restrict__ act,
+                                                   __amdgpu_buffer_rsrc_t ra,
+                                                   const uint32_t (&col_off)[kIdCols], int Tc,
+                                                   int nb)
+{
+    constexpr int kAhead = 4;
+    const int tid = threadIdx.x;
+    const int per_col = nb * 8;
+    const int tasks = Tc * per_col;
+    for (int base = 0; base < tasks; base += kAhead * 256) {
+        u32x4 v0[kAhead], v1[kAhead];
+        uint32_t ds[kAhead];
+#pragma unroll
+        for (int k = 0; k < kAhead; k++) {
+            const int i = base + k * 256 + tid;
+            if (i < tasks) {
+                const int t = i / per_col, j = i - t * per_col;
+                uint32_t coff = col_off[0];
+#pragma unroll
+                for (int u = 1; u < kIdCols; u++)
+                    coff = t == u ? col_off[u] : coff;
+                const uint32_t off = coff + (uint32_t)j * kQ81BlockBytes;
+                v0[k] = ld_b128(ra, off);
+                v1[k] = ld_b128(ra, off + 16);
+                ds[k] = ld_b32(ra, off + 32);
+            }
+        }
+#pragma unroll
+        for (int k = 0; k < kAhead; k++) {
+            const int i = base + k * 256 + tid;
+            if (i < tasks) {
+                const int t = i / per_col, j = i - t * per_col;
+                const int bi = j >> 3, c = j & 7;
+                uint32_t *dst = act + (t * nb + bi) * kActStride;
+                const uint32_t q[8] = {v0[k].x, v0[k].y, v0[k].z, v0[k].w,
+                                       v1[k].x, v1[k].y, v1[k].z, v1[k].w};
+                int sq = 0;
+#pragma unroll
+                for (int jj = 0; jj < 8; jj++) {
+                    dst[8 * jj + c] = q[jj];
+                    sq = sdot4(0x01010101u, q[jj], sq);
+                }
+                dst[64 + c] = __float_as_uint(f16_bits_to_f32(ds[k] & 0xffffu));
+                dst[72 + c] = (uint32_t)(-sq);
+            }
+        }
+    }
+}
+
+// Rows of groups g0, g0 + gstride, ... (< ngroups; a group is the 4 waves x
+// 64/Lr rows of one workgroup step) against the item's staged columns. The
+// kernel takes rows of at most 64 blocks, so Lr >= nb and lane `sub` of a row
+// owns block sub alone (none if sub >= nb): a column's result is that one
+// block's fmaf(dw, s, 0), summed over the row's lanes by the xor butterfly --
+// the library's fp32 order for a row of nb <= Lr blocks. Columns are finished
+// one after the other, each through the one-column floor-pair sums, so no
+// per-column state stays live across columns. The lane's block in the next
+// group is loaded before the current one is used.
+struct RowWalk {
+    __amdgpu_buffer_rsrc_t rw;
+    int64_t N;
+    int nb, lr_log2, wave, sub, g0, gstride, ngroups;
+
+    __device__ int64_t row(int g) const
+    {
+        const int lane = threadIdx.x & 63;
+        return ((int64_t)g * 4 + wave) * (64 >> lr_log2) + (lane >> lr_log2);
+    }
+    // this lane's block of its row in group g, if there is one
+    __device__ void load(int g, RawBlock &b) const
+    {
+        const int64_t r = row(g);
+        if (g < ngroups && r < N && sub < nb)
+            b = load_raw_block(rw, (uint32_t)((r * nb + sub) * kTq1BlockBytes));
+    }
+};
+
+__device__ __forceinline__ void item_rows(const RowWalk &wk, RawBlock cur, const uint32_t *act,
+                                          float *__restrict__ y, const int *pair, int Tc)
+{
+    const int Lr = 1 << wk.lr_log2;
+    // blocks past the row's end read block nb - 1's staged columns, and
+    // contribute +0 like the lanes of the other kernels that own no block
+    const uint32_t *ab0 = act + (wk.sub < wk.nb ? wk.sub : wk.nb - 1) * kActStride;
+    for (int g = wk.g0; g < wk.ngroups; g += wk.gstride) {
+        const int64_t row = wk.row(g);
+        const bool own = row < wk.N && wk.sub < wk.nb;
+        RawBlock nxt;
+        wk.load(g + wk.gstride, nxt);
+        const float dw = f16_bits_to_f32(raw_scale_bits(cur));
+        for (int t = 0; t < Tc; t++) {
+            const uint32_t *ab = ab0 + t * wk.nb * kActStride;
+            int isum[8];
+            block_sums_staged(cur, ab, isum);
+            float da[8];
+#pragma unroll
+            for (int b = 0; b < 8; b++)
+                da[b] = __uint_as_float(ab[64 + b]);
+            float v = own ? fmaf(dw, block_dot_f32(isum, da), 0.0f) : 0.0f;
+            for (int m = Lr >> 1; m >= 1; m >>= 1)
+                v += __shfl_xor(v, m, 64);
+            if (row < wk.N && wk.sub == 0)
+                y[(int64_t)pair[t] * wk.N + row] = v;
+        }
+        cur = nxt;
+    }
+}
+
+// Product kernel. grid.x: slices of the row groups; grid.y: work items (an
+// upper bound; workgroups past the last item return at once). The item's whole
+// activation columns are staged once, before the slice's rows.
+__global__ __launch_bounds__(256) void mmvq_id_kernel(const uint8_t *__restrict__ w,
+                                                      const uint8_t *__restrict__ a,
+                                                      const int32_t *__restrict__ ids,
+                                                      const int32_t *__restrict__ routed,
+                                                      float *__restrict__ y, int E, int64_t N,
+                                                      int nb, int T, int n_used, int lr_log2,
+                                                      int max_items, int ngroups)
+{
+    extern __shared__ uint4 lds4[];
+    uint32_t *act = reinterpret_cast<uint32_t *>(lds4);
+    __shared__ int pair[kIdCols];
+    IdItem it;
+    const bool have = routed ? route_from_workspace(routed, max_items, blockIdx.y, it)
+                             : route_in_wave(ids, E, T * n_used, blockIdx.y, it);
+    if (!have)
+        return;  // uniform
     const int nblk = nb * 8;
     const uint64_t expert_bytes = (uint64_t)N * nb * kTq1BlockBytes;
     const uint64_t col_bytes = (uint64_t)nblk * kQ81BlockBytes;
     uint32_t col_off[kIdCols];
-    float *out[kIdCols];
 #pragma unroll
-    for (int t = 0; t < kIdCols; t++) {
-        const int p = t < Tc ? sel[t] : sel[0];
-        col_off[t] = (uint32_t)((p / n_used) * col_bytes);
-        out[t] = y + (int64_t)p * N;
-    }
-    const __amdgpu_buffer_rsrc_t rw = make_rsrc(w + (uint64_t)e * expert_bytes, expert_bytes);
+    for (int t = 0; t < kIdCols; t++)
+        col_off[t] = (uint32_t)((it.sel[t] / n_used) * col_bytes);
+    if (threadIdx.x < kIdCols)
+        pair[threadIdx.x] = it.sel[0];
+#pragma unroll
+    for (int t = 1; t < kIdCols; t++)
+        if (threadIdx.x == t)
+            pair[t] = it.sel[t];
     const __amdgpu_buffer_rsrc_t ra = make_rsrc(a, (uint64_t)T * col_bytes);
-    const int wave = tid >> 6, lane = tid & 63;
-    const int64_t row = ((int64_t)blockIdx.x * 4 + wave) * (64 >> lr_log2) + (lane >> lr_log2);
-    staged_rows<kIdCols, false>(rw, ra, col_off, out, nullptr, act, row, row < N, N, nb, Tc,
-                                lr_log2, chunk);
+    RowWalk wk;
+    wk.rw = make_rsrc(w + (uint64_t)it.e * expert_bytes, expert_bytes);
+    wk.N = N;
+    wk.nb = nb;
+    wk.lr_log2 = lr_log2;
+    wk.wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    wk.sub = (threadIdx.x & 63) & ((1 << lr_log2) - 1);
+    wk.g0 = blockIdx.x;
+    wk.gstride = gridDim.x;
+    wk.ngroups = ngroups;
+    // the first weight block is in flight while the columns are staged
+    RawBlock first;
+    wk.load(wk.g0, first);
+    stage_item_columns(act, ra, col_off, it.Tc, nb);
+    __syncthreads();
+    item_rows(wk, first, act, y, pair, it.Tc);
 }
 
-// LDS words of the routing tables (counts, first items, the item's pairs),
-// rounded to 16 bytes so the staged activations that follow stay aligned.
-static int route_dwords(int64_t E) { return (int)((2 * E + 1 + kIdCols + 1 + 3) & ~3ll); }
-
-static int id_chunk(int64_t E, int nb, int lr)
+static bool id_uses_prepass(int64_t E, int64_t P)
 {
-    if (E > kIdMaxExperts)
-        return 0;
-    return staged_chunk(nb, lr, kIdCols, lds_budget() - (size_t)route_dwords(E) * 4);
+    return P > kIdWaveRouteMax && E <= kIdMaxExperts;
 }
 
 size_t mmvq_id_workspace_bytes(int64_t E, int64_t T, int32_t n_used)
 {
-    (void)E;
-    (void)T;
-    (void)n_used;
-    return 0;  // routing happens in LDS inside the kernel
+    const int64_t P = T * n_used;
+    if (!id_uses_prepass(E, P))
+        return 0;
+    const size_t words = 1 + 3 * (size_t)id_max_items(E, P) + (size_t)P;
+    return (words * 4 + 255) & ~(size_t)255;
 }
 
 int launch_mmvq_id(const void *w, const void *a, const int32_t *ids, float *y, int64_t E,
                    int64_t N, int64_t K, int64_t T, int32_t n_used, void *workspace,
                    hipStream_t stream)
 {
-    (void)workspace;
     const int nb = (int)(K / kTq1BlockElems);
     const int lr = lanes_per_row_log2(nb);
-    const int chunk = id_chunk(E, nb, lr);
-    if (chunk == 0)
-        return launch_mmvq_id_pairs(w, a, ids, y, E, N, K, T, n_used, stream);
     const int64_t P = T * n_used;
-    const int64_t active = E < P ? E : P;
-    const int64_t max_items = (P + (kIdCols - 1) * active + kIdCols - 1) / kIdCols;
+    const bool prepass = id_uses_prepass(E, P);
+    // the item's columns must fit LDS whole (on 160 KiB: K <= 15360), and a
+    // row must have at most 64 blocks (one per lane)
+    const size_t lds = (size_t)kIdCols * nb * kActStride * 4;
+    if (nb > 64 || lds > lds_budget() || (P > kIdWaveRouteMax && !prepass))
+        return launch_mmvq_id_pairs(w, a, ids, y, E, N, K, T, n_used, stream);
+    const int64_t max_items = id_max_items(E, P);
+    int32_t *routed = nullptr;
+    if (prepass) {
+        routed = static_cast<int32_t *>(workspace);
+        hipLaunchKernelGGL(mmvq_id_route_kernel, dim3(1), dim3(kRouteThreads), 0, stream, ids,
+                           routed, (int)E, (int)P, (int)max_items);
+        if (int rc = check_launch())
+            return rc;
+    }
     const int64_t rows_per_wg = 4 * (64 >> lr);
-    const dim3 grid((unsigned)((N + rows_per_wg - 1) / rows_per_wg), (unsigned)max_items);
-    const int rd = route_dwords(E);
-    const size_t lds = (size_t)rd * 4 + (size_t)kIdCols * chunk * kActStride * 4;
+    const int64_t ngroups = (N + rows_per_wg - 1) / rows_per_wg;
+    // enough slices of the row groups to give the device about
+    // kIdTargetWorkgroups workgroups when every item is in use
+    constexpr int64_t kIdTargetWorkgroups = 2048;
+    int64_t slices = (kIdTargetWorkgroups + max_items - 1) / max_items;
+    slices = slices > ngroups ? ngroups : slices;
+    const dim3 grid((unsigned)slices, (unsigned)max_items);
     allow_dynamic_lds(reinterpret_cast<const void *>(&mmvq_id_kernel), lds);
     hipLaunchKernelGGL(mmvq_id_kernel, grid, dim3(256), lds, stream,
-                       static_cast<const uint8_t *>(w), static_cast<const uint8_t *>(a), ids, y,
-                       (int)E, N, nb, (int)T, (int)n_used, lr, chunk, rd);
+                       static_cast<const uint8_t *>(w), static_cast<const uint8_t *>(a), ids,
+                       routed, y, (int)E, N, nb, (int)T, (int)n_used, lr, (int)max_items,
+                       (int)ngroups);
     return check_launch();
 }
 

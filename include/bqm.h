@@ -147,10 +147,15 @@ BQM_API int tq1_dequantize(const void *w, const int32_t *rows, void *out,
  *   y   [T][n_used][N] fp32 output.
  *   workspace: device scratch of at least mmvq_id_tq1_0_workspace_bytes(E, T,
  *   n_used) bytes, 256-byte aligned, owned by the caller; it may be reused
- *   between calls that are ordered on one stream. When that size is 0 (the
- *   current implementation routes inside the kernel and needs none), NULL is
- *   accepted. Tokens that share an expert are multiplied together, so the
- *   expert's weights are read once per group of up to eight tokens.
+ *   between calls that are ordered on one stream (calls that overlap on two
+ *   streams need one each). Up to 64 (token, slot) pairs are routed inside
+ *   the product kernel and the size is 0: NULL is then accepted. More pairs
+ *   (with E <= 4096) are routed by a pre-pass kernel that writes the work
+ *   items to the workspace. Tokens that share an expert are multiplied
+ *   together, so the expert's weights are read once per group of up to eight
+ *   tokens. Ids outside [0, E) are not checked: depending on the kernel
+ *   the call takes, such a pair's outputs are left unwritten or computed from
+ *   a clamped expert; no access leaves w.
  * Shapes: E >= 1, N >= 1, K >= 256, K % 256 == 0, T >= 1, 1 <= n_used <= E,
  * T * n_used <= 65535; one expert's matrix is below 4 GiB.
  * Alignment: w, a, y, ids 4 bytes; workspace 256 bytes. */

@@ -153,9 +153,24 @@ def test_mmvq_id_rejects():
     assert call(ws=P(0x100010)) == -3             # workspace given but not 256-byte aligned
     if need > 0:
         assert call(ws=None) == -4 and call(wsb=need - 1) == -4
-    assert need == 0                              # routing runs in LDS: no workspace needed
+    assert need == 0                              # up to 64 pairs: routed inside the wave
     assert lib.mmvq_id_tq1_0_workspace_bytes(0, 4, 2) == 0
     assert lib.mmvq_id_tq1_0_workspace_bytes(8, 4, 9) == 0
+    # more pairs: the routing pre-pass needs 1 + 3 * items + pairs int32 words
+    # (items at most (P + 7 * min(E, P) + 7) / 8), rounded up to 256 bytes
+    for E, T, n_used in [(128, 64, 8), (128, 9, 8), (4, 65, 1), (4096, 1000, 4)]:
+        pairs = T * n_used
+        items = (pairs + 7 * min(E, pairs) + 7) // 8
+        words = 1 + 3 * items + pairs
+        assert lib.mmvq_id_tq1_0_workspace_bytes(E, T, n_used) == (4 * words + 255) // 256 * 256
+    assert lib.mmvq_id_tq1_0_workspace_bytes(128, 8, 8) == 0      # exactly 64 pairs
+    assert lib.mmvq_id_tq1_0_workspace_bytes(4097, 100, 1) == 0   # past the pre-pass's experts
+    need = lib.mmvq_id_tq1_0_workspace_bytes(8, 40, 2)
+    assert need > 0
+    args = [GOOD, GOOD, GOOD, GOOD, 8, 16, 256, 40, 2, None, 0, None]
+    assert lib.mmvq_id_tq1_0(*args) == -4                         # workspace missing
+    args[9], args[10] = ws, need - 1
+    assert lib.mmvq_id_tq1_0(*args) == -4                         # workspace too small
 
 
 def test_binding_raises_without_gpu_tensors():

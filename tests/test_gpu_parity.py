@@ -276,8 +276,13 @@ def test_workload_mmvq_parity(bqm, name):
 # ---------------------------------------------------------------------------
 
 def test_mmvq_id_small_cases(bqm):
+    # up to 64 (token, slot) pairs are routed inside each wave; more go through
+    # the routing pre-pass and the workspace (12 experts x 40 tokens x 3 slots),
+    # or, past 4096 experts, through the one-pair-per-workgroup kernel
     for (E, N, K, T, n_used, seed) in [(6, 40, 512, 5, 3, 1), (4, 1, 256, 1, 4, 2),
-                                       (9, 130, 2304, 17, 2, 3), (3, 64, 1024, 2, 1, 4)]:
+                                       (9, 130, 2304, 17, 2, 3), (3, 64, 1024, 2, 1, 4),
+                                       (12, 70, 512, 40, 3, 5), (5000, 2, 256, 3, 4, 6),
+                                       (5000, 3, 512, 70, 1, 7), (7, 20, 16640, 12, 2, 8)]:
         rng = np.random.default_rng(seed)
         trits = synth.ternary(rng, (E * N, K))
         d16 = synth.block_scales_f16(rng, (E * N, K // 256), 0.01, 0.1)
@@ -298,16 +303,20 @@ def test_mmvq_id_small_cases(bqm):
                 assert np.array_equal(y1[0], y[t, s])
 
 
-@pytest.mark.parametrize("case", ["one_expert", "repeats", "all_experts"])
+@pytest.mark.parametrize("case", ["one_expert", "one_expert_many", "repeats", "repeats_many",
+                                  "all_experts"])
 def test_mmvq_id_routing_edge_cases(bqm, case):
     """Routing edge cases: every pair on one expert (several groups of eight),
-    the same expert twice in a token (computed twice), and n_used == E."""
-    rng = np.random.default_rng({"one_expert": 7, "repeats": 8, "all_experts": 9}[case])
-    if case == "one_expert":
-        E, N, K, T, n_used = 4, 72, 512, 21, 1
+    the same expert twice in a token (computed twice), and n_used == E; the
+    "_many" cases carry more than 64 pairs and take the routing pre-pass."""
+    seeds = {"one_expert": 7, "one_expert_many": 10, "repeats": 8, "repeats_many": 11,
+             "all_experts": 9}
+    rng = np.random.default_rng(seeds[case])
+    if case.startswith("one_expert"):
+        E, N, K, T, n_used = 4, 72, 512, (21 if case == "one_expert" else 101), 1
         ids = np.full((T, n_used), 2, np.int32)
-    elif case == "repeats":
-        E, N, K, T, n_used = 5, 40, 768, 6, 3
+    elif case.startswith("repeats"):
+        E, N, K, T, n_used = 5, 40, 768, (6 if case == "repeats" else 30), 3
         ids = rng.integers(0, E, (T, n_used)).astype(np.int32)
         ids[:, 1] = ids[:, 0]
     else:
