@@ -64,6 +64,12 @@ int launch_mmvq_mfma(const void *w, const void *a, float *y, int32_t *isums, int
 bool mfma_resident_supported(int64_t K, int32_t T);
 int launch_mmvq_mfma_resident(const void *w, const void *a, float *y, int32_t *isums, int64_t N,
                               int64_t K, int32_t T, hipStream_t stream);
+// Its expert-routed mode (wide work items of up to 16 pairs, written by the
+// routing pre-pass): whether it takes rows of K elements, and its launcher.
+bool mfma_resident_id_supported(int64_t K);
+int launch_mmvq_mfma_resident_id(const void *w, const void *a, float *y, int64_t N, int64_t K,
+                                 int64_t a_cols, const int32_t *routed, int max_items,
+                                 int max_wide, int n_used, hipStream_t stream);
 int launch_mmvq(const void *w, const void *a, float *y, int32_t *isums, int64_t N, int64_t K,
                 int32_t T, hipStream_t stream);
 int launch_mmvq_id(const void *w, const void *a, const int32_t *ids, float *y, int64_t E,

@@ -45,21 +45,65 @@ static int64_t id_max_items(int64_t E, int64_t P)
 }
 
 // ---------------------------------------------------------------------------
-// Routing pre-pass. Workspace layout (int32):
-//   ws[0]                            number of items
-//   ws[1 + 3k], [2 + 3k], [3 + 3k]   item k: expert, first run slot, pairs
-//   ws[1 + 3 max_items + slot]       pair index held by run slot `slot`
+// Routing pre-pass. An expert with at least wide_min pairs gets wide items of
+// up to kWideCols pairs (the matrix-core kernel's 16 columns), any other
+// expert narrow items of up to narrow_cap pairs (the staged kernel). Workspace
+// layout (int32, M = max_items):
+//   ws[0], ws[1]                        number of narrow, wide items
+//   ws[2 + 3k .. 4 + 3k]                narrow item k: expert, first run slot, pairs
+//   ws[2 + 3(M + k) .. 4 + 3(M + k)]    wide item k, the same fields
+//   ws[2 + 6M + slot]                   pair index held by run slot `slot`
 // An expert's pairs occupy consecutive run slots; the order inside the run
 // follows atomic timing, which is harmless because the columns of an item are
 // computed independently. Pairs whose id is outside [0, E) are dropped.
 // ---------------------------------------------------------------------------
+constexpr int kWideCols = 16;
+
+// Exclusive scan of three per-thread values over a kRouteThreads workgroup
+// (in place in v0..v2, which hold one value per thread); the totals go to
+// tot[0..2]. One wave scans, 16 values per lane.
+__device__ __forceinline__ void route_scan3(int *v0, int *v1, int *v2, int *tot)
+{
+    const int tid = threadIdx.x;
+    if (tid < 64) {
+        int *v[3] = {v0, v1, v2};
+#pragma unroll
+        for (int k = 0; k < 3; k++) {
+            int x[16], r = 0;
+#pragma unroll
+            for (int i = 0; i < 16; i++) {
+                x[i] = v[k][tid * 16 + i];
+                r += x[i];
+            }
+            int inc = r;
+#pragma unroll
+            for (int m = 1; m < 64; m <<= 1) {
+                const int u = __shfl_up(inc, m, 64);
+                if (tid >= m)
+                    inc += u;
+            }
+            int o = inc - r;
+#pragma unroll
+            for (int i = 0; i < 16; i++) {
+                v[k][tid * 16 + i] = o;
+                o += x[i];
+            }
+            if (tid == 63)
+                tot[k] = inc;
+        }
+    }
+}
+
 __global__ __launch_bounds__(kRouteThreads) void mmvq_id_route_kernel(
-    const int32_t *__restrict__ ids, int32_t *__restrict__ ws, int E, int P, int max_items)
+    const int32_t *__restrict__ ids, int32_t *__restrict__ ws, int E, int P, int max_items,
+    int narrow_cap, int wide_min)
 {
     __shared__ int cnt[kIdMaxExperts];   // pair counts, then first run slots
     __shared__ int fill[kIdMaxExperts];  // run slots taken so far
-    __shared__ int part[kRouteThreads];  // per-thread pair sums, then their exclusive scan
-    __shared__ int ipart[kRouteThreads]; // the same for items
+    __shared__ int pp[kRouteThreads];    // per-thread pairs, narrow and wide items,
+    __shared__ int np[kRouteThreads];    // then their exclusive scans
+    __shared__ int wp[kRouteThreads];
+    __shared__ int tot[3];
     const int tid = threadIdx.x;
     for (int e = tid; e < E; e += kRouteThreads) {
         cnt[e] = 0;
@@ -72,66 +116,50 @@ __global__ __launch_bounds__(kRouteThreads) void mmvq_id_route_kernel(
             atomicAdd(&cnt[e], 1);
     }
     __syncthreads();
-    // thread t owns experts [t*per, (t+1)*per): its sums, then one wave scans
-    // the 1024 sums (16 per lane) and each thread walks its experts again
+    // thread t owns experts [t*per, (t+1)*per)
     const int per = (E + kRouteThreads - 1) / kRouteThreads;
-    int s = 0, si = 0;
+    auto narrow_items = [&](int c) { return c >= wide_min ? 0 : (c + narrow_cap - 1) / narrow_cap; };
+    auto wide_items = [&](int c) { return c >= wide_min ? (c + kWideCols - 1) / kWideCols : 0; };
+    int sp = 0, sn = 0, sw = 0;
     for (int k = 0; k < per; k++) {
         const int e = tid * per + k;
         if (e < E) {
-            s += cnt[e];
-            si += (cnt[e] + kIdCols - 1) / kIdCols;
+            sp += cnt[e];
+            sn += narrow_items(cnt[e]);
+            sw += wide_items(cnt[e]);
         }
     }
-    part[tid] = s;
-    ipart[tid] = si;
+    pp[tid] = sp;
+    np[tid] = sn;
+    wp[tid] = sw;
     __syncthreads();
-    if (tid < 64) {
-        int a[16], b[16], ra = 0, rb = 0;
-#pragma unroll
-        for (int k = 0; k < 16; k++) {
-            a[k] = part[tid * 16 + k];
-            b[k] = ipart[tid * 16 + k];
-            ra += a[k];
-            rb += b[k];
-        }
-        int xa = ra, xb = rb;
-#pragma unroll
-        for (int m = 1; m < 64; m <<= 1) {
-            const int ua = __shfl_up(xa, m, 64), ub = __shfl_up(xb, m, 64);
-            if (tid >= m) {
-                xa += ua;
-                xb += ub;
-            }
-        }
-        int oa = xa - ra, ob = xb - rb;
-#pragma unroll
-        for (int k = 0; k < 16; k++) {
-            part[tid * 16 + k] = oa;
-            ipart[tid * 16 + k] = ob;
-            oa += a[k];
-            ob += b[k];
-        }
-        if (tid == 63)
-            ws[0] = xb;
+    route_scan3(pp, np, wp, tot);
+    __syncthreads();
+    if (tid == 0) {
+        ws[0] = tot[1];
+        ws[1] = tot[2];
     }
-    __syncthreads();
-    int32_t *items = ws + 1;
-    int32_t *runs = ws + 1 + 3 * max_items;
-    int off = part[tid], ioff = ipart[tid];
+    int32_t *runs = ws + 2 + 6 * max_items;
+    int off = pp[tid], noff = np[tid], woff = wp[tid];
     for (int k = 0; k < per; k++) {
         const int e = tid * per + k;
         if (e < E) {
             const int c = cnt[e];
-            for (int i = 0; i * kIdCols < c; i++) {
-                int32_t *it = items + 3 * (ioff + i);
-                it[0] = e;
-                it[1] = off + i * kIdCols;
-                it[2] = min(kIdCols, c - i * kIdCols);
+            const bool wide = c >= wide_min;
+            const int cap = wide ? kWideCols : narrow_cap;
+            int32_t *list = ws + 2 + 3 * (wide ? max_items + woff : noff);
+            const int n = (c + cap - 1) / cap;
+            for (int i = 0; i < n; i++) {
+                list[3 * i] = e;
+                list[3 * i + 1] = off + i * cap;
+                list[3 * i + 2] = min(cap, c - i * cap);
             }
+            if (wide)
+                woff += n;
+            else
+                noff += n;
             cnt[e] = off;
             off += c;
-            ioff += (c + kIdCols - 1) / kIdCols;
         }
     }
     __syncthreads();
@@ -151,32 +179,45 @@ struct IdItem {
     int sel[kIdCols];    // pair indices (t >= Tc: a copy of sel[0])
 };
 
-// Wave-local routing of P <= 64 pairs; false if item is past the last one.
-__device__ __forceinline__ bool route_in_wave(const int32_t *__restrict__ ids, int E, int P,
-                                              int item, IdItem &it)
+// Wave-local routing of P <= 64 pairs: each lane's pair, its rank among the
+// pairs of the same expert, and the lanes that open an item.
+struct WaveRoute {
+    int e;              // this lane's expert (-1 past P)
+    bool valid;         // e in [0, E)
+    int rank;           // pairs of the same expert in lanes below
+    uint64_t openers;   // lanes whose rank is a multiple of kIdCols
+};
+
+__device__ __forceinline__ WaveRoute wave_route(const int32_t *__restrict__ ids, int E, int P)
 {
     const int lane = threadIdx.x & 63;
-    const int e = lane < P ? ids[lane] : -1;
-    const bool valid = (unsigned)e < (unsigned)E;
-    const uint64_t below = (1ull << lane) - 1ull;
+    WaveRoute r;
+    r.e = lane < P ? ids[lane] : -1;
+    r.valid = (unsigned)r.e < (unsigned)E;
     // lanes routed to my expert: valid lanes that agree on every id bit
-    uint64_t same = __ballot(valid);
+    uint64_t same = __ballot(r.valid);
     const int nbits = E > 1 ? 32 - __clz(E - 1) : 0;
     for (int k = 0; k < nbits; k++) {
-        const bool bit = (e >> k) & 1;
+        const bool bit = (r.e >> k) & 1;
         const uint64_t b = __ballot(bit);
         same &= bit ? b : ~b;
     }
-    const int rank = __popcll(same & below);
-    const bool opens = valid && rank % kIdCols == 0;
-    const uint64_t openers = __ballot(opens);
-    if (item >= __popcll(openers))
-        return false;
-    const uint64_t mine = __ballot(opens && __popcll(openers & below) == item);
+    r.rank = __popcll(same & ((1ull << lane) - 1ull));
+    r.openers = __ballot(r.valid && r.rank % kIdCols == 0);
+    return r;
+}
+
+// Item `item` (< popcount(openers)) of a wave-local routing.
+__device__ __forceinline__ void wave_route_item(const WaveRoute &r, int item, IdItem &it)
+{
+    const int lane = threadIdx.x & 63;
+    const bool opens = (r.openers >> lane) & 1;
+    const uint64_t mine =
+        __ballot(opens && __popcll(r.openers & ((1ull << lane) - 1ull)) == item);
     const int lead = __builtin_amdgcn_readfirstlane(__builtin_ctzll(mine));
-    const int e_it = __builtin_amdgcn_readlane(e, lead);
-    const int r0 = __builtin_amdgcn_readlane(rank, lead);
-    uint64_t m = __ballot(valid && e == e_it && rank >= r0 && rank < r0 + kIdCols);
+    const int e_it = __builtin_amdgcn_readlane(r.e, lead);
+    const int r0 = __builtin_amdgcn_readlane(r.rank, lead);
+    uint64_t m = __ballot(r.valid && r.e == e_it && r.rank >= r0 && r.rank < r0 + kIdCols);
     it.e = e_it;
     it.Tc = __popcll(m);
     const int first = __builtin_ctzll(m);
@@ -185,23 +226,19 @@ __device__ __forceinline__ bool route_in_wave(const int32_t *__restrict__ ids, i
         it.sel[t] = m ? (int)__builtin_ctzll(m) : first;
         m &= m - 1;
     }
-    return true;
 }
 
-// The item written by the routing pre-pass; false if item is past the last one.
-__device__ __forceinline__ bool route_from_workspace(const int32_t *__restrict__ routed,
-                                                     int max_items, int item, IdItem &it)
+// Narrow item `item` (< routed[0]) written by the routing pre-pass.
+__device__ __forceinline__ void workspace_item(const int32_t *__restrict__ routed, int max_items,
+                                               int item, IdItem &it)
 {
-    if (item >= routed[0])
-        return false;
-    const int32_t *p = routed + 1 + 3 * item;
-    const int32_t *runs = routed + 1 + 3 * max_items + p[1];
+    const int32_t *p = routed + 2 + 3 * item;
+    const int32_t *runs = routed + 2 + 6 * max_items + p[1];
     it.e = p[0];
     it.Tc = p[2];
 #pragma unroll
     for (int t = 0; t < kIdCols; t++)
         it.sel[t] = runs[t < it.Tc ? t : 0];
-    return true;
 }
 
 // Stage Tc whole activation columns (nb blocks each) in the staged layout,
@@ -255,19 +292,18 @@ __device__ __forceinline__ void stage_item_columns(uint32_t *__restrict__ act,
     }
 }
 
-// Rows of groups g0, g0 + gstride, ... (< ngroups; a group is the 4 waves x
-// 64/Lr rows of one workgroup step) against the item's staged columns. The
-// kernel takes rows of at most 64 blocks, so Lr >= nb and lane `sub` of a row
-// owns block sub alone (none if sub >= nb): a column's result is that one
-// block's fmaf(dw, s, 0), summed over the row's lanes by the xor butterfly --
-// the library's fp32 order for a row of nb <= Lr blocks. Columns are finished
-// one after the other, each through the one-column floor-pair sums, so no
-// per-column state stays live across columns. The lane's block in the next
-// group is loaded before the current one is used.
+// One group of rows (the 4 waves x 64/Lr rows of one workgroup step) against
+// the item's staged columns. The kernel takes rows of at most 64 blocks, so
+// Lr >= nb and lane `sub` of a row owns block sub alone (none if sub >= nb): a
+// column's result is that one block's fmaf(dw, s, 0), summed over the row's
+// lanes by the xor butterfly -- the library's fp32 order for a row of
+// nb <= Lr blocks. Columns are finished one after the other, each through the
+// one-column floor-pair sums, so no per-column state stays live across
+// columns.
 struct RowWalk {
     __amdgpu_buffer_rsrc_t rw;
     int64_t N;
-    int nb, lr_log2, wave, sub, g0, gstride, ngroups;
+    int nb, lr_log2, wave, sub;
 
     __device__ int64_t row(int g) const
     {
@@ -278,45 +314,44 @@ struct RowWalk {
     __device__ void load(int g, RawBlock &b) const
     {
         const int64_t r = row(g);
-        if (g < ngroups && r < N && sub < nb)
+        if (r < N && sub < nb)
             b = load_raw_block(rw, (uint32_t)((r * nb + sub) * kTq1BlockBytes));
     }
 };
 
-__device__ __forceinline__ void item_rows(const RowWalk &wk, RawBlock cur, const uint32_t *act,
-                                          float *__restrict__ y, const int *pair, int Tc)
+__device__ __forceinline__ void group_rows(const RowWalk &wk, int g, const RawBlock &cur,
+                                           const uint32_t *act, float *__restrict__ y,
+                                           const int *pair, int Tc)
 {
     const int Lr = 1 << wk.lr_log2;
     // blocks past the row's end read block nb - 1's staged columns, and
     // contribute +0 like the lanes of the other kernels that own no block
     const uint32_t *ab0 = act + (wk.sub < wk.nb ? wk.sub : wk.nb - 1) * kActStride;
-    for (int g = wk.g0; g < wk.ngroups; g += wk.gstride) {
-        const int64_t row = wk.row(g);
-        const bool own = row < wk.N && wk.sub < wk.nb;
-        RawBlock nxt;
-        wk.load(g + wk.gstride, nxt);
-        const float dw = f16_bits_to_f32(raw_scale_bits(cur));
-        for (int t = 0; t < Tc; t++) {
-            const uint32_t *ab = ab0 + t * wk.nb * kActStride;
-            int isum[8];
-            block_sums_staged(cur, ab, isum);
-            float da[8];
+    const int64_t row = wk.row(g);
+    const bool own = row < wk.N && wk.sub < wk.nb;
+    const float dw = f16_bits_to_f32(raw_scale_bits(cur));
+    for (int t = 0; t < Tc; t++) {
+        const uint32_t *ab = ab0 + t * wk.nb * kActStride;
+        int isum[8];
+        block_sums_staged(cur, ab, isum);
+        float da[8];
 #pragma unroll
-            for (int b = 0; b < 8; b++)
-                da[b] = __uint_as_float(ab[64 + b]);
-            float v = own ? fmaf(dw, block_dot_f32(isum, da), 0.0f) : 0.0f;
-            for (int m = Lr >> 1; m >= 1; m >>= 1)
-                v += __shfl_xor(v, m, 64);
-            if (row < wk.N && wk.sub == 0)
-                y[(int64_t)pair[t] * wk.N + row] = v;
-        }
-        cur = nxt;
+        for (int b = 0; b < 8; b++)
+            da[b] = __uint_as_float(ab[64 + b]);
+        float v = own ? fmaf(dw, block_dot_f32(isum, da), 0.0f) : 0.0f;
+        for (int m = Lr >> 1; m >= 1; m >>= 1)
+            v += __shfl_xor(v, m, 64);
+        if (row < wk.N && wk.sub == 0)
+            y[(int64_t)pair[t] * wk.N + row] = v;
     }
 }
 
-// Product kernel. grid.x: slices of the row groups; grid.y: work items (an
-// upper bound; workgroups past the last item return at once). The item's whole
-// activation columns are staged once, before the slice's rows.
+// Product kernel. grid.y: work items (an upper bound; workgroups past the
+// last item return at once); grid.x: slices of the item's row groups, the
+// workgroup taking groups blockIdx.x, blockIdx.x + gridDim.x, ... The many
+// small workgroups of unequal cost (an item's pairs set its cost) are balanced
+// by the hardware's dispatch. The item's columns are staged once; the lane's
+// block in the next group is loaded before the current one is used.
 __global__ __launch_bounds__(256) void mmvq_id_kernel(const uint8_t *__restrict__ w,
                                                       const uint8_t *__restrict__ a,
                                                       const int32_t *__restrict__ ids,
@@ -328,25 +363,20 @@ __global__ __launch_bounds__(256) void mmvq_id_kernel(const uint8_t *__restrict_
     extern __shared__ uint4 lds4[];
     uint32_t *act = reinterpret_cast<uint32_t *>(lds4);
     __shared__ int pair[kIdCols];
+    const int item = blockIdx.y;
     IdItem it;
-    const bool have = routed ? route_from_workspace(routed, max_items, blockIdx.y, it)
-                             : route_in_wave(ids, E, T * n_used, blockIdx.y, it);
-    if (!have)
-        return;  // uniform
-    const int nblk = nb * 8;
+    if (routed) {
+        if (item >= routed[0])
+            return;  // uniform
+        workspace_item(routed, max_items, item, it);
+    } else {
+        const WaveRoute wr = wave_route(ids, E, T * n_used);
+        if (item >= __popcll(wr.openers))
+            return;  // uniform
+        wave_route_item(wr, item, it);
+    }
     const uint64_t expert_bytes = (uint64_t)N * nb * kTq1BlockBytes;
-    const uint64_t col_bytes = (uint64_t)nblk * kQ81BlockBytes;
-    uint32_t col_off[kIdCols];
-#pragma unroll
-    for (int t = 0; t < kIdCols; t++)
-        col_off[t] = (uint32_t)((it.sel[t] / n_used) * col_bytes);
-    if (threadIdx.x < kIdCols)
-        pair[threadIdx.x] = it.sel[0];
-#pragma unroll
-    for (int t = 1; t < kIdCols; t++)
-        if (threadIdx.x == t)
-            pair[t] = it.sel[t];
-    const __amdgpu_buffer_rsrc_t ra = make_rsrc(a, (uint64_t)T * col_bytes);
+    const uint64_t col_bytes = (uint64_t)nb * 8 * kQ81BlockBytes;
     RowWalk wk;
     wk.rw = make_rsrc(w + (uint64_t)it.e * expert_bytes, expert_bytes);
     wk.N = N;
@@ -354,15 +384,26 @@ __global__ __launch_bounds__(256) void mmvq_id_kernel(const uint8_t *__restrict_
     wk.lr_log2 = lr_log2;
     wk.wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     wk.sub = (threadIdx.x & 63) & ((1 << lr_log2) - 1);
-    wk.g0 = blockIdx.x;
-    wk.gstride = gridDim.x;
-    wk.ngroups = ngroups;
     // the first weight block is in flight while the columns are staged
-    RawBlock first;
-    wk.load(wk.g0, first);
-    stage_item_columns(act, ra, col_off, it.Tc, nb);
+    RawBlock cur;
+    wk.load(blockIdx.x, cur);
+    uint32_t col_off[kIdCols];
+#pragma unroll
+    for (int t = 0; t < kIdCols; t++)
+        col_off[t] = (uint32_t)((it.sel[t] / n_used) * col_bytes);
+#pragma unroll
+    for (int t = 0; t < kIdCols; t++)
+        if ((int)threadIdx.x == t)
+            pair[t] = it.sel[t];
+    stage_item_columns(act, make_rsrc(a, (uint64_t)T * col_bytes), col_off, it.Tc, nb);
     __syncthreads();
-    item_rows(wk, first, act, y, pair, it.Tc);
+    for (int g = blockIdx.x; g < ngroups; g += gridDim.x) {
+        RawBlock nxt;
+        if (g + (int)gridDim.x < ngroups)
+            wk.load(g + gridDim.x, nxt);
+        group_rows(wk, g, cur, act, y, pair, it.Tc);
+        cur = nxt;
+    }
 }
 
 static bool id_uses_prepass(int64_t E, int64_t P)
@@ -375,7 +416,7 @@ size_t mmvq_id_workspace_bytes(int64_t E, int64_t T, int32_t n_used)
     const int64_t P = T * n_used;
     if (!id_uses_prepass(E, P))
         return 0;
-    const size_t words = 1 + 3 * (size_t)id_max_items(E, P) + (size_t)P;
+    const size_t words = 2 + 6 * (size_t)id_max_items(E, P) + (size_t)P;
     return (words * 4 + 255) & ~(size_t)255;
 }
 
@@ -387,9 +428,14 @@ int launch_mmvq_id(const void *w, const void *a, const int32_t *ids, float *y, i
     const int lr = lanes_per_row_log2(nb);
     const int64_t P = T * n_used;
     const bool prepass = id_uses_prepass(E, P);
+    // experts with at least kMfmaMinCols pairs go to the matrix cores when the
+    // pre-pass sorts the pairs; then every other expert holds at most
+    // kMfmaMinCols - 1 pairs, one narrow item
+    const bool wide = prepass && mfma_resident_id_supported(K);
+    const int narrow_cap = wide ? kMfmaMinCols - 1 : kIdCols;
     // the item's columns must fit LDS whole (on 160 KiB: K <= 15360), and a
     // row must have at most 64 blocks (one per lane)
-    const size_t lds = (size_t)kIdCols * nb * kActStride * 4;
+    const size_t lds = (size_t)narrow_cap * nb * kActStride * 4;
     if (nb > 64 || lds > lds_budget() || (P > kIdWaveRouteMax && !prepass))
         return launch_mmvq_id_pairs(w, a, ids, y, E, N, K, T, n_used, stream);
     const int64_t max_items = id_max_items(E, P);
@@ -397,24 +443,38 @@ int launch_mmvq_id(const void *w, const void *a, const int32_t *ids, float *y, i
     if (prepass) {
         routed = static_cast<int32_t *>(workspace);
         hipLaunchKernelGGL(mmvq_id_route_kernel, dim3(1), dim3(kRouteThreads), 0, stream, ids,
-                           routed, (int)E, (int)P, (int)max_items);
+                           routed, (int)E, (int)P, (int)max_items, narrow_cap,
+                           wide ? kMfmaMinCols : INT32_MAX);
         if (int rc = check_launch())
             return rc;
     }
+    const int64_t active = E < P ? E : P;
+    const int64_t max_narrow = wide ? active : max_items;
     const int64_t rows_per_wg = 4 * (64 >> lr);
     const int64_t ngroups = (N + rows_per_wg - 1) / rows_per_wg;
-    // enough slices of the row groups to give the device about
-    // kIdTargetWorkgroups workgroups when every item is in use
-    constexpr int64_t kIdTargetWorkgroups = 2048;
-    int64_t slices = (kIdTargetWorkgroups + max_items - 1) / max_items;
-    slices = slices > ngroups ? ngroups : slices;
-    const dim3 grid((unsigned)slices, (unsigned)max_items);
     allow_dynamic_lds(reinterpret_cast<const void *>(&mmvq_id_kernel), lds);
-    hipLaunchKernelGGL(mmvq_id_kernel, grid, dim3(256), lds, stream,
-                       static_cast<const uint8_t *>(w), static_cast<const uint8_t *>(a), ids,
-                       routed, y, (int)E, N, nb, (int)T, (int)n_used, lr, (int)max_items,
-                       (int)ngroups);
-    return check_launch();
+    // about kIdTargetWorkgroups workgroups when every item is in use, but at
+    // most kIdGroupsPerSlice row groups per workgroup: restaging the columns
+    // costs less than the lost balance of longer workgroups
+    constexpr int64_t kIdTargetWorkgroups = 2048, kIdGroupsPerSlice = 3;
+    int64_t slices = (kIdTargetWorkgroups + max_narrow - 1) / max_narrow;
+    const int64_t fewest = (ngroups + kIdGroupsPerSlice - 1) / kIdGroupsPerSlice;
+    slices = slices > fewest ? slices : fewest;
+    slices = slices < ngroups ? slices : ngroups;
+    hipLaunchKernelGGL(mmvq_id_kernel, dim3((unsigned)slices, (unsigned)max_narrow), dim3(256),
+                       lds, stream, static_cast<const uint8_t *>(w),
+                       static_cast<const uint8_t *>(a), ids, routed, y, (int)E, N, nb, (int)T,
+                       (int)n_used, lr, (int)max_items, (int)ngroups);
+    if (int rc = check_launch())
+        return rc;
+    if (!wide)
+        return BQM_OK;
+    // wide items: at most one per expert with kMfmaMinCols or more pairs, plus
+    // one per further kWideCols pairs
+    const int64_t wide_experts = P / kMfmaMinCols < E ? P / kMfmaMinCols : E;
+    const int64_t max_wide = wide_experts + P / kWideCols;
+    return launch_mmvq_mfma_resident_id(w, a, y, N, K, T, routed, (int)max_items, (int)max_wide,
+                                        n_used, stream);
 }
 
 }  // namespace bqm

@@ -30,26 +30,35 @@ namespace bqm {
 // room for both halves, else single (a second barrier per tile).
 __host__ __device__ inline size_t res_bq_dwords(int NT, int nb) { return (size_t)NT * nb * 8 * 128; }
 __host__ __device__ inline size_t res_dah_dwords(int NT, int nb) { return (size_t)nb * 16 * NT * 4; }
-inline size_t res_lds_bytes(int NW, int NT, int R, int nb, bool db)
+__host__ __device__ inline size_t res_red_dwords(int NW, int NT, int R, bool db)
 {
-    return (res_bq_dwords(NT, nb) + res_dah_dwords(NT, nb) +
-            (size_t)(db ? 2 : 1) * NW * 64 * R * NT * 4) * 4;
+    return (size_t)(db ? 2 : 1) * NW * 64 * R * NT * 4;
+}
+// id: room for the expert-routed mode's two 16 NT-entry column tables
+inline size_t res_lds_bytes(int NW, int NT, int R, int nb, bool db, bool id = false)
+{
+    return (res_bq_dwords(NT, nb) + res_dah_dwords(NT, nb) + res_red_dwords(NW, NT, R, db) +
+            (id ? 32 * NT : 0)) * 4;
 }
 
 // Copy all T activation columns into bq / dah: one Q8_1 block per item,
-// consecutive threads on consecutive columns. Columns T .. 16 NT - 1 are left
-// as they are: they only feed output columns that are never stored.
-template <int NT>
+// consecutive threads on consecutive columns. Column c's Q8_1 row starts at
+// byte c * nb * 8 * 36 of ra, or, for expert items (ID), at byte colbase[c]
+// (an LDS table). Columns T .. 16 NT - 1 are left as they are: they only feed
+// output columns that are never stored.
+template <int NT, bool ID>
 __device__ __forceinline__ void stage_all_columns(uint32_t *__restrict__ bq,
                                                   uint32_t *__restrict__ dah,
-                                                  __amdgpu_buffer_rsrc_t ra, int T, int nb)
+                                                  __amdgpu_buffer_rsrc_t ra, int T, int nb,
+                                                  const uint32_t *colbase)
 {
     const int nblk = nb * 8;
     const int items = T * nblk;
     for (int it = threadIdx.x; it < items; it += blockDim.x) {
         const int j = it / T, c = it - j * T;
         const int B = j >> 3, b = j & 7;
-        const uint32_t off = (uint32_t)(c * nblk + j) * kQ81BlockBytes;
+        const uint32_t off = (ID ? colbase[c] : (uint32_t)c * nblk * kQ81BlockBytes) +
+                             (uint32_t)j * kQ81BlockBytes;
         const u32x4 v0 = ld_b128(ra, off);
         const u32x4 v1 = ld_b128(ra, off + 16);
         const uint32_t ds = ld_b32(ra, off + 32);
@@ -66,22 +75,40 @@ __device__ __forceinline__ void stage_all_columns(uint32_t *__restrict__ bq,
     }
 }
 
+// Work item of the expert-routed mode: its entry in the routing table the
+// routing pre-pass writes (mmvq_id.hip): item k of the wide list is
+// routed[2 + 3 (max_items + k) ..] = (expert, first run slot, pairs), and run
+// slot s holds pair index routed[2 + 6 max_items + s]; routed[1] counts the
+// wide items.
+struct WideItems {
+    const int32_t *routed;
+    int max_items;
+    int n_used;
+};
+
 // NW: waves per workgroup; GPW: butterfly groups per wave (Lr / NW); NT:
 // 16-column tiles (1 or 2); R: 16-row tiles per workgroup tile; DB: partial
 // sums double-buffered; ISUMS: write the exact per-sub-block sums instead of
-// outputs.
-template <int NW, int GPW, int NT, int R, bool DB, bool ISUMS>
+// outputs; ID: expert-routed mode, one wide work item per blockIdx.y (its
+// expert's matrix, its pairs' token columns, outputs y[pair][row]); `a_cols`
+// is the number of columns a holds (T in the plain mode).
+template <int NW, int GPW, int NT, int R, bool DB, bool ISUMS, bool ID>
 __global__ __launch_bounds__(64 * NW) void mmvq_mfma_res_kernel(const uint8_t *__restrict__ w,
                                                                 const uint8_t *__restrict__ a,
                                                                 float *__restrict__ y,
                                                                 int32_t *__restrict__ isums,
                                                                 int64_t N, int nb, int T,
-                                                                int ntiles)
+                                                                int ntiles, int a_cols,
+                                                                WideItems items)
 {
     extern __shared__ uint32_t smem[];
     uint32_t *bq = smem;
     uint32_t *dah = smem + res_bq_dwords(NT, nb);
     float *red = reinterpret_cast<float *>(dah + res_dah_dwords(NT, nb));
+    // ID: per-column tables after the partial sums (byte offset of the token's
+    // Q8_1 row, pair index)
+    uint32_t *colbase = reinterpret_cast<uint32_t *>(red) + res_red_dwords(NW, NT, R, DB);
+    int *colpair = reinterpret_cast<int *>(colbase + 16 * NT);
     // the wave index is uniform across the wave; saying so keeps the block
     // loop and its branches on scalar registers
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -90,8 +117,42 @@ __global__ __launch_bounds__(64 * NW) void mmvq_mfma_res_kernel(const uint8_t *_
     const int kg = lane >> 4;                   // decode lane: row lane % 16, K group kg
     const int col = lane & 15, rg = lane >> 4;  // output lane: column col, rows 4rg..4rg+3
     const int nblk = nb * 8;
-    const __amdgpu_buffer_rsrc_t rw = make_rsrc(w, (uint64_t)N * nb * kTq1BlockBytes);
-    const __amdgpu_buffer_rsrc_t ra = make_rsrc(a, (uint64_t)T * nblk * kQ81BlockBytes);
+    const uint64_t w_bytes = (uint64_t)N * nb * kTq1BlockBytes;
+    const __amdgpu_buffer_rsrc_t ra = make_rsrc(a, (uint64_t)a_cols * nblk * kQ81BlockBytes);
+
+    // Work units: in the plain mode the row tiles, strided over the grid; in
+    // the expert mode (wide item, row tile) pairs, item-major, workgroup i
+    // taking the contiguous range [i U / G, (i + 1) U / G) of the U units, so
+    // that it restages columns only when its range enters the next item.
+    int64_t u, u_end;
+    int ustride;
+    if (ID) {
+        const int64_t units = (int64_t)items.routed[1] * ntiles;
+        u = (int64_t)blockIdx.x * units / gridDim.x;
+        u_end = (int64_t)(blockIdx.x + 1) * units / gridDim.x;
+        ustride = 1;
+    } else {
+        u = blockIdx.x;
+        u_end = ntiles;
+        ustride = gridDim.x;
+    }
+    if (u >= u_end)
+        return;  // uniform
+    int item = ID ? (int)(u / ntiles) : 0;
+    int tile = (int)(u - (int64_t)item * ntiles);
+    // the item's matrix, column count and column tables (ID)
+    auto take_item = [&](int k) {
+        const int32_t *it = items.routed + 2 + 3 * (items.max_items + k);
+        const int first = it[1];
+        T = it[2];
+        if ((int)threadIdx.x < T) {
+            const int pr = items.routed[2 + 6 * items.max_items + first + threadIdx.x];
+            colpair[threadIdx.x] = pr;
+            colbase[threadIdx.x] = (uint32_t)(pr / items.n_used) * (uint32_t)nblk * kQ81BlockBytes;
+        }
+        return make_rsrc(w + (uint64_t)it[0] * w_bytes, w_bytes);
+    };
+    __amdgpu_buffer_rsrc_t rw = ID ? take_item(item) : make_rsrc(w, w_bytes);
 
     // byte offsets of this decode lane's rows in tile t (rows past N read row 0)
     auto tile_rows = [&](int t, uint32_t (&ro)[R]) {
@@ -102,23 +163,31 @@ __global__ __launch_bounds__(64 * NW) void mmvq_mfma_res_kernel(const uint8_t *_
         }
     };
 
-    int tile = blockIdx.x;
     uint32_t row_off[R];
-    tile_rows(tile, row_off);
-    // the first block's weights are in flight while the activations are staged
     LaneBlock lb[R];
-    if (wave < nb) {
+    // the first block's weights are in flight while the activations are staged
+    auto start_item = [&]() {
+        tile_rows(tile, row_off);
+        if (wave < nb) {
 #pragma unroll
-        for (int rt = 0; rt < R; rt++)
-            lb[rt] = load_lane_block(rw, row_off[rt] + (uint32_t)wave * kTq1BlockBytes, kg);
-    }
-    stage_all_columns<NT>(bq, dah, ra, T, nb);
-    __syncthreads();
+            for (int rt = 0; rt < R; rt++)
+                lb[rt] = load_lane_block(rw, row_off[rt] + (uint32_t)wave * kTq1BlockBytes, kg);
+        }
+        if (ID)
+            __syncthreads();  // the column tables
+        stage_all_columns<NT, ID>(bq, dah, ra, T, nb, colbase);
+        __syncthreads();
+    };
+    start_item();
 
     int parity = 0;
-    for (; tile < ntiles; tile += gridDim.x, parity ^= 1) {
+    for (;;) {
         const int64_t r0 = (int64_t)tile * 16 * R;
-        const int next_tile = tile + gridDim.x;
+        const int64_t un = u + ustride;
+        const int item_n = ID ? (int)(un / ntiles) : 0;
+        const int next_tile = (int)(un - (int64_t)item_n * ntiles);
+        // the next unit works on the columns staged now
+        const bool next_here = un < u_end && item_n == item;
         uint32_t next_off[R];
         tile_rows(next_tile, next_off);
 
@@ -141,7 +210,7 @@ __global__ __launch_bounds__(64 * NW) void mmvq_mfma_res_kernel(const uint8_t *_
                 // group's first, else the first block of the next tile
                 const bool same_tile = B + Lr < nb || (gi + 1 < GPW && g + NW < nb);
                 const int Bn = B + Lr < nb ? B + Lr : (same_tile ? g + NW : wave);
-                const bool have_next = same_tile || next_tile < ntiles;
+                const bool have_next = same_tile || next_here;
                 LaneBlock ln[R];
                 if (have_next) {
 #pragma unroll
@@ -270,11 +339,12 @@ __global__ __launch_bounds__(64 * NW) void mmvq_mfma_res_kernel(const uint8_t *_
                     for (int ct = 0; ct < NT; ct++) {
                         const int c = ct * 16 + col;
                         if (c < T) {
+                            const int64_t yc = ID ? colpair[c] : c;
 #pragma unroll
                             for (int i = 0; i < 4; i++) {
                                 const int64_t row = r0 + 16 * rt + 4 * rg + i;
                                 if (row < N)
-                                    y[(int64_t)c * N + row] = acc[0][rt][ct][i];
+                                    y[yc * N + row] = acc[0][rt][ct][i];
                             }
                         }
                     }
@@ -285,6 +355,17 @@ __global__ __launch_bounds__(64 * NW) void mmvq_mfma_res_kernel(const uint8_t *_
 #pragma unroll
         for (int rt = 0; rt < R; rt++)
             row_off[rt] = next_off[rt];
+        u = un;
+        tile = next_tile;
+        parity ^= 1;
+        if (u >= u_end)
+            break;
+        if (ID && item_n != item) {
+            __syncthreads();  // every wave is done with this item's LDS
+            item = item_n;
+            rw = take_item(item);
+            start_item();
+        }
     }
 }
 
@@ -296,25 +377,80 @@ static int launch_res(const uint8_t *w, const uint8_t *a, float *y, int32_t *isu
     const int64_t ntiles = (N + 16 * R - 1) / (16 * R);
     const size_t lds = res_lds_bytes(NW, NT, R, nb, DB);
     const void *kt =
-        reinterpret_cast<const void *>(&mmvq_mfma_res_kernel<NW, GPW, NT, R, DB, true>);
+        reinterpret_cast<const void *>(&mmvq_mfma_res_kernel<NW, GPW, NT, R, DB, true, false>);
     const void *kf =
-        reinterpret_cast<const void *>(&mmvq_mfma_res_kernel<NW, GPW, NT, R, DB, false>);
+        reinterpret_cast<const void *>(&mmvq_mfma_res_kernel<NW, GPW, NT, R, DB, false, false>);
     allow_dynamic_lds(kt, lds);
     allow_dynamic_lds(kf, lds);
     const int cap = resident_workgroups(isums ? kt : kf, 64 * NW, lds);
     const dim3 grid((unsigned)(ntiles < cap ? ntiles : cap));
+    const WideItems none = {nullptr, 0, 1};
     if (isums)
-        hipLaunchKernelGGL((mmvq_mfma_res_kernel<NW, GPW, NT, R, DB, true>), grid, dim3(64 * NW),
-                           lds, stream, w, a, nullptr, isums, N, nb, T, (int)ntiles);
+        hipLaunchKernelGGL((mmvq_mfma_res_kernel<NW, GPW, NT, R, DB, true, false>), grid,
+                           dim3(64 * NW), lds, stream, w, a, nullptr, isums, N, nb, T,
+                           (int)ntiles, T, none);
     else
-        hipLaunchKernelGGL((mmvq_mfma_res_kernel<NW, GPW, NT, R, DB, false>), grid,
-                           dim3(64 * NW), lds, stream, w, a, y, nullptr, N, nb, T, (int)ntiles);
+        hipLaunchKernelGGL((mmvq_mfma_res_kernel<NW, GPW, NT, R, DB, false, false>), grid,
+                           dim3(64 * NW), lds, stream, w, a, y, nullptr, N, nb, T, (int)ntiles,
+                           T, none);
+    return check_launch();
+}
+
+// Expert-routed mode: one 16-column tile (items of at most 16 pairs), 16
+// waves, a persistent grid of the workgroups the device runs at once.
+template <int GPW>
+static int launch_res_id(const uint8_t *w, const uint8_t *a, float *y, int64_t N, int nb,
+                         int a_cols, const int32_t *routed, int max_items, int max_wide,
+                         int n_used, hipStream_t stream)
+{
+    constexpr int NW = 16, NT = 1, R = 1;
+    constexpr bool DB = true;
+    const int64_t ntiles = (N + 16 * R - 1) / (16 * R);
+    const size_t lds = res_lds_bytes(NW, NT, R, nb, DB, true);
+    const void *k =
+        reinterpret_cast<const void *>(&mmvq_mfma_res_kernel<NW, GPW, NT, R, DB, false, true>);
+    allow_dynamic_lds(k, lds);
+    const int64_t cap = resident_workgroups(k, 64 * NW, lds);
+    const int64_t most = (int64_t)max_wide * ntiles;  // units when every item is in use
+    const dim3 grid((unsigned)(most < cap ? most : cap));
+    const WideItems items = {routed, max_items, n_used};
+    hipLaunchKernelGGL((mmvq_mfma_res_kernel<NW, GPW, NT, R, DB, false, true>), grid,
+                       dim3(64 * NW), lds, stream, w, a, y, nullptr, N, nb, 16, (int)ntiles,
+                       a_cols, items);
     return check_launch();
 }
 
 // 16 waves for one column tile, 8 for two (their register budgets); the
 // column tiles' partial sums double-buffered for one tile, single for two
 static int res_waves(int NT) { return NT == 1 ? 16 : 8; }
+
+bool mfma_resident_id_supported(int64_t K)
+{
+    const int nb = (int)(K / kTq1BlockElems);
+    const int Lr = 1 << lanes_per_row_log2(nb);
+    return Lr >= 16 && res_lds_bytes(16, 1, 1, nb, true, true) <= lds_budget();
+}
+
+int launch_mmvq_mfma_resident_id(const void *w, const void *a, float *y, int64_t N, int64_t K,
+                                 int64_t a_cols, const int32_t *routed, int max_items,
+                                 int max_wide, int n_used, hipStream_t stream)
+{
+    const int nb = (int)(K / kTq1BlockElems);
+    const int Lr = 1 << lanes_per_row_log2(nb);
+    const uint8_t *wp = static_cast<const uint8_t *>(w);
+    const uint8_t *ap = static_cast<const uint8_t *>(a);
+    switch (Lr) {
+    case 16:
+        return launch_res_id<1>(wp, ap, y, N, nb, (int)a_cols, routed, max_items, max_wide,
+                                n_used, stream);
+    case 32:
+        return launch_res_id<2>(wp, ap, y, N, nb, (int)a_cols, routed, max_items, max_wide,
+                                n_used, stream);
+    default:
+        return launch_res_id<4>(wp, ap, y, N, nb, (int)a_cols, routed, max_items, max_wide,
+                                n_used, stream);
+    }
+}
 
 bool mfma_resident_supported(int64_t K, int32_t T)
 {

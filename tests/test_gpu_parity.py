@@ -278,11 +278,16 @@ def test_workload_mmvq_parity(bqm, name):
 def test_mmvq_id_small_cases(bqm):
     # up to 64 (token, slot) pairs are routed inside each wave; more go through
     # the routing pre-pass and the workspace (12 experts x 40 tokens x 3 slots),
-    # or, past 4096 experts, through the one-pair-per-workgroup kernel
+    # or, past 4096 experts, through the one-pair-per-workgroup kernel. With
+    # the pre-pass, experts of five or more pairs go to the matrix cores when a
+    # row has at least 16 lane groups and the columns fit LDS (K = 2304, 4096,
+    # 6144 here: wide items next to narrow ones)
     for (E, N, K, T, n_used, seed) in [(6, 40, 512, 5, 3, 1), (4, 1, 256, 1, 4, 2),
                                        (9, 130, 2304, 17, 2, 3), (3, 64, 1024, 2, 1, 4),
                                        (12, 70, 512, 40, 3, 5), (5000, 2, 256, 3, 4, 6),
-                                       (5000, 3, 512, 70, 1, 7), (7, 20, 16640, 12, 2, 8)]:
+                                       (5000, 3, 512, 70, 1, 7), (7, 20, 16640, 12, 2, 8),
+                                       (20, 100, 4096, 40, 4, 9), (6, 50, 6144, 30, 3, 10),
+                                       (9, 33, 2304, 25, 3, 11), (40, 17, 4096, 70, 2, 12)]:
         rng = np.random.default_rng(seed)
         trits = synth.ternary(rng, (E * N, K))
         d16 = synth.block_scales_f16(rng, (E * N, K // 256), 0.01, 0.1)
@@ -312,11 +317,16 @@ def test_mmvq_id_routing_edge_cases(bqm, case):
     seeds = {"one_expert": 7, "one_expert_many": 10, "repeats": 8, "repeats_many": 11,
              "all_experts": 9}
     rng = np.random.default_rng(seeds[case])
-    if case.startswith("one_expert"):
-        E, N, K, T, n_used = 4, 72, 512, (21 if case == "one_expert" else 101), 1
+    if case == "one_expert":
+        E, N, K, T, n_used = 4, 72, 512, 21, 1
+        ids = np.full((T, n_used), 2, np.int32)
+    elif case == "one_expert_many":
+        # 101 pairs on one expert: seven matrix-core items, the last of 5 pairs
+        E, N, K, T, n_used = 4, 72, 2304, 101, 1
         ids = np.full((T, n_used), 2, np.int32)
     elif case.startswith("repeats"):
-        E, N, K, T, n_used = 5, 40, 768, (6 if case == "repeats" else 30), 3
+        E, N, K, T, n_used = 5, 40, (768 if case == "repeats" else 4096), \
+            (6 if case == "repeats" else 30), 3
         ids = rng.integers(0, E, (T, n_used)).astype(np.int32)
         ids[:, 1] = ids[:, 0]
     else:
