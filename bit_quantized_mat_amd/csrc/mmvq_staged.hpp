@@ -20,57 +20,80 @@ constexpr int kActStride = 84;
 constexpr int kMaxChunkBlocks = 128;
 constexpr int kStagedMaxCols = 8;
 
-__device__ __forceinline__ void stage_activations(uint32_t *__restrict__ act,
-                                                  __amdgpu_buffer_rsrc_t ra, uint32_t col_off,
-                                                  int B0, int cb, int tid, int nthreads)
+// Staging works in batches: a lane loads the tasks base + k * nthreads + tid
+// (k < kStageAhead) of a column into registers, then writes them to LDS. A
+// kernel issues the first batch before its weight loads: loads retire in issue
+// order, so a batch issued after the weights would wait for them.
+//   Q8_1 source: a task is one Q8_1 block (q dwords, d and s).
+//   fp32 source: a task is 4 of the 32 elements of a Q8_1 block; eight lanes
+//   quantize a block together (q8_1_block_by_8: the bytes the stand-alone
+//   quantize kernel would write). Every lane takes part in the group
+//   shuffles: groups past the end (whole groups, the task count being a
+//   multiple of 8) redo the last one and store nothing.
+template <bool F32>
+struct StageBatch;
+
+template <>
+struct StageBatch<false> {
+    static constexpr int kAhead = 1;
+    u32x4 v0[kAhead], v1[kAhead];
+    uint32_t ds[kAhead];
+};
+
+template <>
+struct StageBatch<true> {
+    static constexpr int kAhead = 4;
+    u32x4 v[kAhead];
+};
+
+// Tasks of one column of cb blocks starting at block B0: 8 per block (Q8_1)
+// or 64 (fp32).
+template <bool F32>
+__device__ __forceinline__ int stage_tasks(int cb)
 {
-    for (int i = tid; i < cb * 8; i += nthreads) {
-        const int bi = i >> 3, c = i & 7;
-        const uint32_t off = col_off + (uint32_t)((B0 + bi) * 8 + c) * kQ81BlockBytes;
-        const u32x4 v0 = ld_b128(ra, off);
-        const u32x4 v1 = ld_b128(ra, off + 16);
-        const uint32_t ds = ld_b32(ra, off + 32);
-        uint32_t *dst = act + bi * kActStride;
-        const uint32_t q[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
-        int sq = 0;
-#pragma unroll
-        for (int j = 0; j < 8; j++) {
-            dst[8 * j + c] = q[j];
-            sq = sdot4(0x01010101u, q[j], sq);
-        }
-        dst[64 + c] = __float_as_uint(f16_bits_to_f32(ds & 0xffffu));
-        dst[72 + c] = (uint32_t)(-sq);
-    }
+    return cb * (F32 ? 64 : 8);
 }
 
-// The same staged layout filled from fp32 activations, quantized on the fly
-// (q8_1_block_by_8: the bytes the stand-alone quantize kernel would write).
-// Column data start at byte col_off of rx; eight lanes per Q8_1 block.
-__device__ __forceinline__ void stage_activations_f32(uint32_t *__restrict__ act,
-                                                      __amdgpu_buffer_rsrc_t rx, uint32_t col_off,
-                                                      int B0, int cb, int tid, int nthreads)
+template <bool F32>
+__device__ __forceinline__ void stage_load(StageBatch<F32> &sb, __amdgpu_buffer_rsrc_t ra,
+                                           uint32_t col_off, int B0, int cb, int base, int tid,
+                                           int nthreads)
 {
-    constexpr int kAhead = 4;   // loads in flight per lane before any is quantized
-    const int tasks = cb * 64;  // cb blocks x 8 sub-blocks x 8 lanes
-    for (int base = 0; base < tasks; base += kAhead * nthreads) {
-        // every lane takes part in the group shuffles: groups past the end
-        // (whole groups, tasks being a multiple of 8) redo the last one and
-        // store nothing
-        u32x4 v[kAhead];
+    constexpr int kAhead = StageBatch<F32>::kAhead;
+    const int tasks = stage_tasks<F32>(cb);
 #pragma unroll
-        for (int k = 0; k < kAhead; k++) {
-            const int i = base + k * nthreads + tid;
+    for (int k = 0; k < kAhead; k++) {
+        const int i = base + k * nthreads + tid;
+        if constexpr (F32) {
             const int ii = i < tasks ? i : tasks - 1;
             const int g = ii >> 3, j = ii & 7;
             const int bi = g >> 3, c = g & 7;
-            v[k] = ld_b128(rx, col_off + (uint32_t)(((B0 + bi) * kTq1BlockElems +
-                                                     c * kQ81BlockElems + 4 * j) * 4));
+            sb.v[k] = ld_b128(ra, col_off + (uint32_t)(((B0 + bi) * kTq1BlockElems +
+                                                        c * kQ81BlockElems + 4 * j) * 4));
+        } else {
+            // lanes past the end load the last task again (no branch around
+            // the loads, so the compiler can count them) and store nothing
+            const int ii = i < tasks ? i : tasks - 1;
+            const uint32_t off = col_off + (uint32_t)(B0 * 8 + ii) * kQ81BlockBytes;
+            sb.v0[k] = ld_b128(ra, off);
+            sb.v1[k] = ld_b128(ra, off + 16);
+            sb.ds[k] = ld_b32(ra, off + 32);
         }
+    }
+}
+
+template <bool F32>
+__device__ __forceinline__ void stage_store(const StageBatch<F32> &sb, uint32_t *__restrict__ act,
+                                            int cb, int base, int tid, int nthreads)
+{
+    constexpr int kAhead = StageBatch<F32>::kAhead;
+    const int tasks = stage_tasks<F32>(cb);
 #pragma unroll
-        for (int k = 0; k < kAhead; k++) {
-            const int i = base + k * nthreads + tid;
-            const Q81Part p = q8_1_block_by_8(__uint_as_float(v[k].x), __uint_as_float(v[k].y),
-                                              __uint_as_float(v[k].z), __uint_as_float(v[k].w));
+    for (int k = 0; k < kAhead; k++) {
+        const int i = base + k * nthreads + tid;
+        if constexpr (F32) {
+            const Q81Part p = q8_1_block_by_8(__uint_as_float(sb.v[k].x), __uint_as_float(sb.v[k].y),
+                                              __uint_as_float(sb.v[k].z), __uint_as_float(sb.v[k].w));
             if (i < tasks) {
                 const int g = i >> 3, j = i & 7;
                 const int bi = g >> 3, c = g & 7;
@@ -81,7 +104,43 @@ __device__ __forceinline__ void stage_activations_f32(uint32_t *__restrict__ act
                     dst[72 + c] = (uint32_t)(-p.sum);
                 }
             }
+        } else {
+            if (i < tasks) {
+                const int bi = i >> 3, c = i & 7;
+                uint32_t *dst = act + bi * kActStride;
+                const uint32_t q[8] = {sb.v0[k].x, sb.v0[k].y, sb.v0[k].z, sb.v0[k].w,
+                                       sb.v1[k].x, sb.v1[k].y, sb.v1[k].z, sb.v1[k].w};
+                int sq = 0;
+#pragma unroll
+                for (int j = 0; j < 8; j++) {
+                    dst[8 * j + c] = q[j];
+                    sq = sdot4(0x01010101u, q[j], sq);
+                }
+                dst[64 + c] = __float_as_uint(f16_bits_to_f32(sb.ds[k] & 0xffffu));
+                dst[72 + c] = (uint32_t)(-sq);
+            }
         }
+    }
+}
+
+// Stage one column (cb blocks from block B0) into act. If `first` is given,
+// it holds the column's first batch, already loaded.
+template <bool F32>
+__device__ __forceinline__ void stage_column(uint32_t *__restrict__ act, __amdgpu_buffer_rsrc_t ra,
+                                             uint32_t col_off, int B0, int cb, int tid,
+                                             int nthreads, const StageBatch<F32> *first)
+{
+    const int step = StageBatch<F32>::kAhead * nthreads;
+    const int tasks = stage_tasks<F32>(cb);
+    int base = 0;
+    if (first) {
+        stage_store<F32>(*first, act, cb, 0, tid, nthreads);
+        base = step;
+    }
+    for (; base < tasks; base += step) {
+        StageBatch<F32> sb;
+        stage_load<F32>(sb, ra, col_off, B0, cb, base, tid, nthreads);
+        stage_store<F32>(sb, act, cb, base, tid, nthreads);
     }
 }
 
@@ -199,26 +258,35 @@ __device__ __forceinline__ void staged_rows(__amdgpu_buffer_rsrc_t rw, __amdgpu_
     for (int t = 0; t < TC; t++)
         acc[t] = 0.0f;
 
-    for (int B0 = 0; B0 < nb; B0 += chunk) {
+    // one pass over the blocks [B0, B0 + chunk) of the row
+    auto pass = [&](int B0) {
         const int end = min(B0 + chunk, nb);
         const int cb = end - B0;
         const int first = B0 + sub;
-        // issue this lane's first weight block before staging, so the HBM
-        // latency overlaps the activation copy; later blocks of the chunk are
-        // loaded into the same registers at the top of their iteration
-        RawBlock cur;
-        if (row_ok && first < end)
-            cur = load_raw_block(rw, row_off + (uint32_t)first * kTq1BlockBytes);
-        __syncthreads();  // readers of the previous chunk are done
+        if (B0 > 0)
+            __syncthreads();  // readers of the previous chunk are done
+        // the first column's first staging batch, then this lane's first
+        // weight block: the HBM latency of the weights overlaps the activation
+        // copy, and the copy does not wait for the weights. The weight load is
+        // issued by every lane (lanes without a block read one they ignore),
+        // so the compiler knows how many loads follow the batch and waits for
+        // the batch alone. Later blocks of the chunk are loaded into the same
+        // registers at the top of their iteration.
+        // Wavefront-scope fences (no instructions) keep the compiler from
+        // moving the loads across each other: it would otherwise sink the
+        // batch's loads towards their first use, below the weights'.
+        StageBatch<F32> head;
+        stage_load<F32>(head, ra, col_off[0], B0, cb, 0, tid, 256);
+        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+        RawBlock cur = load_raw_block(
+            rw, row_off + (uint32_t)(first < end ? first : B0) * kTq1BlockBytes);
+        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+        stage_column<F32>(act, ra, col_off[0], B0, cb, tid, 256, &head);  // T >= 1
 #pragma unroll
-        for (int t = 0; t < TC; t++)
-            if (t < T) {
-                if (F32)
-                    stage_activations_f32(act + t * cb * kActStride, ra, col_off[t], B0, cb, tid,
-                                          256);
-                else
-                    stage_activations(act + t * cb * kActStride, ra, col_off[t], B0, cb, tid, 256);
-            }
+        for (int t = 1; t < TC; t++)
+            if (t < T)
+                stage_column<F32>(act + t * cb * kActStride, ra, col_off[t], B0, cb, tid, 256,
+                                  nullptr);
         __syncthreads();
         if (row_ok) {
             for (int B = first; B < end; B += Lr) {
@@ -253,6 +321,14 @@ __device__ __forceinline__ void staged_rows(__amdgpu_buffer_rsrc_t rw, __amdgpu_
                 }
             }
         }
+    };
+    // rows that fit one pass take straight-line code: with no loop around
+    // it, the compiler knows exactly which loads are in flight at each wait
+    if (chunk >= nb) {
+        pass(0);
+    } else {
+        for (int B0 = 0; B0 < nb; B0 += chunk)
+            pass(B0);
     }
     if (!ISUMS) {
         // butterfly over the Lr lanes of the row (every lane of the wave takes part)
