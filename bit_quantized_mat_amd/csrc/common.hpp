@@ -28,6 +28,13 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, ui
                                              kRawBufferFlags);
 }
 
+// Byte offset for a load a lane issues only to keep the count of loads in
+// flight the same on every lane: past the range of every resource below
+// 0xffffffc0 bytes, so the hardware's range check returns zeros without a
+// memory access (a larger resource reads in-range bytes there; either way
+// the lane ignores the result and nothing faults).
+constexpr uint32_t kIdleLoadOffset = 0xffffffc0u;
+
 __device__ __forceinline__ uint32_t ld_b32(__amdgpu_buffer_rsrc_t r, uint32_t off)
 {
     return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);

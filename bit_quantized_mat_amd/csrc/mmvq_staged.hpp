@@ -24,7 +24,8 @@ constexpr int kStagedMaxCols = 8;
 // (k < kStageAhead) of a column into registers, then writes them to LDS. A
 // kernel issues the first batch before its weight loads: loads retire in issue
 // order, so a batch issued after the weights would wait for them.
-//   Q8_1 source: a task is one Q8_1 block (q dwords, d and s).
+//   Q8_1 source: a task is one Q8_1 block (q dwords, d and s); lanes past
+//   the last task issue their loads at kIdleLoadOffset.
 //   fp32 source: a task is 4 of the 32 elements of a Q8_1 block; eight lanes
 //   quantize a block together (q8_1_block_by_8: the bytes the stand-alone
 //   quantize kernel would write). Every lane takes part in the group
@@ -71,10 +72,10 @@ __device__ __forceinline__ void stage_load(StageBatch<F32> &sb, __amdgpu_buffer_
             sb.v[k] = ld_b128(ra, col_off + (uint32_t)(((B0 + bi) * kTq1BlockElems +
                                                         c * kQ81BlockElems + 4 * j) * 4));
         } else {
-            // lanes past the end load the last task again (no branch around
-            // the loads, so the compiler can count them) and store nothing
-            const int ii = i < tasks ? i : tasks - 1;
-            const uint32_t off = col_off + (uint32_t)(B0 * 8 + ii) * kQ81BlockBytes;
+            // lanes past the end load nothing real (no branch around the
+            // loads, so the compiler can count them) and store nothing
+            const uint32_t off = i < tasks ? col_off + (uint32_t)(B0 * 8 + i) * kQ81BlockBytes
+                                           : kIdleLoadOffset;
             sb.v0[k] = ld_b128(ra, off);
             sb.v1[k] = ld_b128(ra, off + 16);
             sb.ds[k] = ld_b32(ra, off + 32);
@@ -268,9 +269,9 @@ __device__ __forceinline__ void staged_rows(__amdgpu_buffer_rsrc_t rw, __amdgpu_
         // the first column's first staging batch, then this lane's first
         // weight block: the HBM latency of the weights overlaps the activation
         // copy, and the copy does not wait for the weights. The weight load is
-        // issued by every lane (lanes without a block read one they ignore),
-        // so the compiler knows how many loads follow the batch and waits for
-        // the batch alone. Later blocks of the chunk are loaded into the same
+        // issued by every lane (lanes without a block load at
+        // kIdleLoadOffset), so the compiler knows how many loads follow the
+        // batch and waits for the batch alone. Later blocks of the chunk are loaded into the same
         // registers at the top of their iteration.
         // Wavefront-scope fences (no instructions) keep the compiler from
         // moving the loads across each other: it would otherwise sink the
@@ -278,8 +279,9 @@ __device__ __forceinline__ void staged_rows(__amdgpu_buffer_rsrc_t rw, __amdgpu_
         StageBatch<F32> head;
         stage_load<F32>(head, ra, col_off[0], B0, cb, 0, tid, 256);
         __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-        RawBlock cur = load_raw_block(
-            rw, row_off + (uint32_t)(first < end ? first : B0) * kTq1BlockBytes);
+        RawBlock cur = load_raw_block(rw, row_ok && first < end
+                                              ? row_off + (uint32_t)first * kTq1BlockBytes
+                                              : kIdleLoadOffset);
         __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
         stage_column<F32>(act, ra, col_off[0], B0, cb, tid, 256, &head);  // T >= 1
 #pragma unroll
