@@ -52,8 +52,9 @@ int launch_mmvq_staged(const void *w, const void *a, float *y, int32_t *isums, i
 int launch_mmvq_staged_f32(const void *w, const float *x, float *y, int64_t N, int64_t K,
                            int32_t T, hipStream_t stream);
 // Matrix-core kernel: any shape, 1 to 32 columns; the dispatcher gives it
-// every call of at least kMfmaMinCols columns and the calls whose activations
-// do not fit the staged kernel's LDS.
+// every call of at least kMfmaMinCols columns, the calls whose activations
+// do not fit the staged kernel's LDS, and calls of three or more columns too
+// small to give the staged kernel a second wave per SIMD.
 constexpr int kMfmaMinCols = 5;
 
 int launch_mmvq_mfma(const void *w, const void *a, float *y, int32_t *isums, int64_t N,

@@ -186,12 +186,28 @@ __device__ __forceinline__ void rows_product(const uint8_t *__restrict__ w, uint
     }
 }
 
+// Whether a call of T < kMfmaMinCols columns takes the staged kernel. From
+// three columns on it does so only when its grid gives the device more than
+// one wave per SIMD: with one block per lane and no second wave to overlap
+// it, the multi-column work after the weights arrive outlasts the
+// matrix-core kernel's (4096 x 4096 at three columns: 6.2 against 5.5 us;
+// 5120 x 6144 and 14336 x 4096, with more waves, favour the staged kernel).
+static bool use_staged(int64_t N, int64_t K, int32_t T)
+{
+    if (T >= kMfmaMinCols || !staged_supported(K, T))
+        return false;
+    if (T < 3 || !mfma_resident_supported(K, T))
+        return true;
+    const int64_t waves = N * (1ll << lanes_per_row_log2(K / kTq1BlockElems)) / 64;
+    return waves > 4ll * compute_units();
+}
+
 // Plain product: the staged kernel for narrow calls whose activations fit its
 // LDS, the matrix-core kernel for everything else.
 int launch_mmvq(const void *w, const void *a, float *y, int32_t *isums, int64_t N, int64_t K,
                 int32_t T, hipStream_t stream)
 {
-    if (T < kMfmaMinCols && staged_supported(K, T))
+    if (use_staged(N, K, T))
         return launch_mmvq_staged(w, a, y, isums, N, K, T, stream);
     if (mfma_resident_supported(K, T))
         return launch_mmvq_mfma_resident(w, a, y, isums, N, K, T, stream);

@@ -65,12 +65,16 @@ def _case(N, K, T, seed, p_zero=1 / 3, outliers=0.01, d_lo=0.01, d_hi=0.1):
 
 # shapes: (N, K, T) spanning several row tiles, ragged row counts, odd block
 # counts (2-byte aligned blocks), one-block rows and wide rows
-# (which kernel takes each: staged for T < 5; from T = 5 the matrix-core kernel,
-# with the activations resident in LDS when they fit and a row has at least
-# as many lane groups as the workgroup has waves, else streamed per block)
+# (which kernel takes each: staged for T < 3, and for T = 3, 4 when the
+# call gives the staged grid more than one wave per SIMD (4500 x 4096,
+# 4200 x 2560) or the matrix-core kernel cannot keep the columns resident
+# (67 x 768); otherwise the matrix-core kernel, with the activations resident
+# in LDS when they fit and a row has at least as many lane groups as the
+# workgroup has waves, else streamed per block)
 SHAPES = [(256, 1024, 1), (1, 256, 1), (33, 256, 2), (67, 768, 3), (130, 2304, 5),
           (515, 4096, 8), (96, 6144, 4), (40, 16384, 1), (17, 1280, 32), (300, 512, 16),
-          (40, 16384, 6), (50, 9216, 5), (21, 4096, 17), (1, 2304, 9)]
+          (40, 16384, 6), (50, 9216, 5), (21, 4096, 17), (1, 2304, 9), (4500, 4096, 3),
+          (4200, 2560, 4)]
 
 
 # ---------------------------------------------------------------------------
