@@ -55,6 +55,8 @@ def lib():
         L.oracle_mmvq.restype = ctypes.c_int
         L.oracle_mmvq_id.argtypes = [_p, _p, _p, _p, _p, _p, _i64, _i64, _i64, _i64, _i64]
         L.oracle_mmvq_id.restype = ctypes.c_int
+        L.oracle_mmvq_id_slots.argtypes = [_p, _p, _p, _p, _p, _p, _i64, _i64, _i64, _i64, _i64]
+        L.oracle_mmvq_id_slots.restype = ctypes.c_int
         L.oracle_f32_to_bf16.restype = ctypes.c_uint16
         L.oracle_f32_to_bf16.argtypes = [ctypes.c_float]
         L.oracle_tq1_dequantize_rows.argtypes = [_p, _p, _p, _i64, _i64, _i64, ctypes.c_int]
@@ -177,8 +179,10 @@ def mmvq(w, a, N, K, T):
     return y, y64, ab
 
 
-def mmvq_id(w, a, ids, E, N, K, T, n_used):
-    """Returns (y, y64, abs64), each [T, n_used, N]."""
+def mmvq_id(w, a, ids, E, N, K, T, n_used, per_slot=False):
+    """Returns (y, y64, abs64), each [T, n_used, N]. a holds one Q8_1 column
+    per token ([T, K/32] blocks), or per (token, slot) pair with per_slot
+    ([T, n_used, K/32] blocks)."""
     w = _c(w, np.uint8)
     a = _c(a, np.uint8)
     ids = _c(ids, np.int32)
@@ -186,8 +190,9 @@ def mmvq_id(w, a, ids, E, N, K, T, n_used):
     y = np.empty(shape, dtype=np.float32)
     y64 = np.empty(shape, dtype=np.float64)
     ab = np.empty(shape, dtype=np.float64)
-    _check(lib().oracle_mmvq_id(_ptr(w), _ptr(a), _ptr(ids), _ptr(y), _ptr(y64), _ptr(ab),
-                                E, N, K, T, n_used), "mmvq_id")
+    f = lib().oracle_mmvq_id_slots if per_slot else lib().oracle_mmvq_id
+    _check(f(_ptr(w), _ptr(a), _ptr(ids), _ptr(y), _ptr(y64), _ptr(ab), E, N, K, T, n_used),
+           "mmvq_id")
     return y, y64, ab
 
 

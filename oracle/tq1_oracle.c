@@ -441,12 +441,13 @@ int oracle_mmvq(const uint8_t *w, const uint8_t *a, float *y, double *y64,
     return bad ? -1 : 0;
 }
 
-/* Expert-routed mat-vec: y[t][s][n] = mmvq(W[ids[t][s]], a[t])[n], with one
- * activation per token shared by its n_used slots ([P1-acc], ne11 = 1).
+/* The expert-routed products: pair ts = t * n_used + s multiplies expert
+ * ids[ts]'s matrix by activation column col(ts), where col(ts) = t when a
+ * token's slots share its column and col(ts) = ts when every pair has its own.
  * Returns -1 on a bad shape, an id outside [0, E) or a bad packed byte. */
-int oracle_mmvq_id(const uint8_t *w, const uint8_t *a, const int32_t *ids,
-                   float *y, double *y64, double *abs64, int64_t E, int64_t N,
-                   int64_t K, int64_t T, int64_t n_used)
+static int mmvq_id_pairs(const uint8_t *w, const uint8_t *a, const int32_t *ids,
+                         float *y, double *y64, double *abs64, int64_t E, int64_t N,
+                         int64_t K, int64_t T, int64_t n_used, int column_per_pair)
 {
     if (E <= 0 || N < 0 || T < 0 || n_used <= 0 || n_used > E || K <= 0 ||
         K % TQ1_BLOCK_ELEMS)
@@ -462,7 +463,7 @@ int oracle_mmvq_id(const uint8_t *w, const uint8_t *a, const int32_t *ids,
     for (int64_t idx = 0; idx < total; idx++) {
         int64_t n = idx % N;
         int64_t ts = idx / N;     /* t * n_used + s */
-        int64_t t = ts / n_used;
+        int64_t col = column_per_pair ? ts : ts / n_used;
         const uint8_t *row = w + (int64_t)ids[ts] * expert_bytes +
                              n * nb * TQ1_BLOCK_BYTES;
         int8_t *tr = (int8_t *)malloc((size_t)K);
@@ -472,7 +473,7 @@ int oracle_mmvq_id(const uint8_t *w, const uint8_t *a, const int32_t *ids,
             continue;
         }
         double v, va;
-        row_dot(row, tr, a, nblk, t, K, &v, &va);
+        row_dot(row, tr, a, nblk, col, K, &v, &va);
         if (y)
             y[idx] = (float)v;
         if (y64)
@@ -482,6 +483,25 @@ int oracle_mmvq_id(const uint8_t *w, const uint8_t *a, const int32_t *ids,
         free(tr);
     }
     return bad ? -1 : 0;
+}
+
+/* Expert-routed mat-vec: y[t][s][n] = mmvq(W[ids[t][s]], a[t])[n], with one
+ * activation per token shared by its n_used slots ([P1-acc], ne11 = 1). */
+int oracle_mmvq_id(const uint8_t *w, const uint8_t *a, const int32_t *ids,
+                   float *y, double *y64, double *abs64, int64_t E, int64_t N,
+                   int64_t K, int64_t T, int64_t n_used)
+{
+    return mmvq_id_pairs(w, a, ids, y, y64, abs64, E, N, K, T, n_used, 0);
+}
+
+/* The same with one activation per (token, slot) pair, a [T][n_used][K/32]
+ * (the down-projection shape, ne11 = n_used):
+ * y[t][s][n] = mmvq(W[ids[t][s]], a[t][s])[n]. */
+int oracle_mmvq_id_slots(const uint8_t *w, const uint8_t *a, const int32_t *ids,
+                         float *y, double *y64, double *abs64, int64_t E, int64_t N,
+                         int64_t K, int64_t T, int64_t n_used)
+{
+    return mmvq_id_pairs(w, a, ids, y, y64, abs64, E, N, K, T, n_used, 1);
 }
 
 /* ------------------------------------------------------------------------ */

@@ -360,6 +360,47 @@ def test_mmvq_id_equals_gathered_mmvq():
             assert np.array_equal(ab[t, s], abr[0])
 
 
+def test_mmvq_id_slots_equals_dequantize_then_dot():
+    """Per-slot activations (one Q8_1 column per (token, slot) pair) against
+    numpy's plain product of the dequantized expert matrix and that pair's
+    dequantized column, in fp64."""
+    E, N, K, T, n_used = 5, 9, 768, 3, 2
+    rng = np.random.default_rng(43)
+    trits = synth.ternary(rng, (E * N, K))
+    d16 = synth.block_scales_f16(rng, (E * N, K // 256), 0.01, 0.1)
+    x = synth.activations(rng, T * n_used, K)
+    ids = synth.zipf_routing(rng, T, E, n_used)
+    w = oracle.tq1_pack(trits, d16)
+    a = oracle.q8_1_quantize(x)
+    q, da16, _ = oracle.q8_1_fields(a, T * n_used, K)
+    W = trits.astype(np.float64) * np.repeat(d16.view(np.float16).astype(np.float64), 256, axis=1)
+    A = q.astype(np.float64) * np.repeat(da16.view(np.float16).astype(np.float64), 32, axis=1)
+    y, y64, ab = oracle.mmvq_id(w, a, ids, E, N, K, T, n_used, per_slot=True)
+    for t in range(T):
+        for s in range(n_used):
+            e, p = ids[t, s], t * n_used + s
+            ref = W[e * N:(e + 1) * N] @ A[p]
+            assert np.all(np.abs(y64[t, s] - ref) <= 1e-12 * ab[t, s] + 1e-300)
+    assert np.array_equal(y, y64.astype(np.float32))
+
+
+def test_mmvq_id_slots_with_shared_columns_is_mmvq_id():
+    """Repeating each token's column over its slots turns the per-slot
+    product into the shared-column one, bit for bit."""
+    E, N, K, T, n_used = 4, 7, 512, 3, 3
+    rng = np.random.default_rng(44)
+    trits = synth.ternary(rng, (E * N, K))
+    d16 = synth.block_scales_f16(rng, (E * N, K // 256), 0.01, 0.1)
+    x = synth.activations(rng, T, K)
+    ids = synth.zipf_routing(rng, T, E, n_used)
+    w = oracle.tq1_pack(trits, d16)
+    a = oracle.q8_1_quantize(x)
+    a_slots = np.repeat(a.reshape(T, 1, -1), n_used, axis=1).reshape(T * n_used, -1)
+    y1, y64a, ab1 = oracle.mmvq_id(w, a, ids, E, N, K, T, n_used)
+    y2, y64b, ab2 = oracle.mmvq_id(w, a_slots, ids, E, N, K, T, n_used, per_slot=True)
+    assert np.array_equal(y64a, y64b) and np.array_equal(ab1, ab2) and np.array_equal(y1, y2)
+
+
 def test_zipf_routing_has_no_repeats_per_token():
     ids = synth.zipf_routing(np.random.default_rng(0), 64, 128, 8)
     assert ids.shape == (64, 8)
