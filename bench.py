@@ -66,12 +66,14 @@ def algorithmic_bytes(N, K, T):
     return N * (K // 256) * 54 + T * (K // 32) * 36 + T * N * 4
 
 
-def moe_algorithmic_bytes(ids, N, K):
+def moe_algorithmic_bytes(ids, N, K, per_slot=False):
     """Expert-routed call: the matrices of the distinct experts routed to,
-    once each; the tokens' Q8_1 activations; fp32 outputs; the ids."""
+    once each; the Q8_1 activations (one column per token, or per pair with
+    per_slot); fp32 outputs; the ids."""
     T, n_used = ids.shape
     distinct = len(set(ids.ravel().tolist()))
-    return (distinct * N * (K // 256) * 54 + T * (K // 32) * 36 + T * n_used * N * 4
+    cols = T * n_used if per_slot else T
+    return (distinct * N * (K // 256) * 54 + cols * (K // 32) * 36 + T * n_used * N * 4
             + T * n_used * 4), distinct
 
 
@@ -306,7 +308,26 @@ def sweep(path, torch, np, bqm, synth, dev, launches, only=None):
                "frac_of_8tbs": round(b / us / 1e3 / HBM_PEAK_GBS, 4)}
         table.append(row)
         log("sweep", row)
-    del wrot, a_all, w0
+    # one activation per (token, slot) pair: the down-projection shape
+    a_slots = bqm.q8_1_quantize(torch.from_numpy(synth.slot_activations(wl)).to(dev))
+    for T in wl.Ts:
+        ids_np = np.ascontiguousarray(inp.ids[:T])
+        ids = torch.from_numpy(ids_np).to(dev)
+        a = a_slots[:T * n_used].contiguous()
+        y = torch.empty((T, n_used, N), dtype=torch.float32, device=dev)
+        ws = torch.empty(max(bqm.mmvq_id_tq1_0_workspace_bytes(E, T, n_used), 256),
+                         dtype=torch.uint8, device=dev)
+        us = graph_us(torch, lambda i: bqm.mmvq_id_tq1_0_slots(wrot[i % R], a, ids, E, N, K, T,
+                                                               n_used, out=y, workspace=ws),
+                      launches)
+        b, distinct = moe_algorithmic_bytes(ids_np, N, K, per_slot=True)
+        row = {"workload": "moe", "op": "mmvq_id_tq1_0_slots", "E": E, "N": N, "K": K, "T": T,
+               "n_used": n_used, "distinct_experts": distinct, "us": round(us, 3),
+               "algorithmic_bytes": b, "gbs": round(b / us / 1e3, 1),
+               "frac_of_8tbs": round(b / us / 1e3 / HBM_PEAK_GBS, 4)}
+        table.append(row)
+        log("sweep", row)
+    del wrot, a_all, a_slots, w0
     torch.cuda.empty_cache()
     with open(path, "w") as f:
         json.dump(table, f, indent=1)

@@ -12,7 +12,8 @@ import os
 __all__ = [
     "BqmError", "library", "library_path", "tq1_pack", "q8_1_quantize", "mmvq_tq1_0",
     "mmvq_tq1_0_f32", "MMVQ_F32_MAX_COLS", "tq1_dequantize",
-    "mmvq_id_tq1_0", "mmvq_id_tq1_0_workspace_bytes", "mmvq_tq1_0_block_isums",
+    "mmvq_id_tq1_0", "mmvq_id_tq1_0_slots", "mmvq_id_tq1_0_workspace_bytes",
+    "mmvq_tq1_0_block_isums",
     "TQ1_BLOCK_BYTES", "Q81_BLOCK_BYTES", "MMVQ_MAX_COLS",
 ]
 
@@ -56,13 +57,15 @@ def library():
         L.tq1_dequantize.argtypes = [_p, _p, _p, _i64, _i64, _i64, _i32, _p]
         L.mmvq_tq1_0_block_isums.argtypes = [_p, _p, _p, _i64, _i64, _i32, _p]
         L.mmvq_id_tq1_0.argtypes = [_p, _p, _p, _p, _i64, _i64, _i64, _i64, _i32, _p, _sz, _p]
+        L.mmvq_id_tq1_0_slots.argtypes = L.mmvq_id_tq1_0.argtypes
         L.mmvq_id_tq1_0_workspace_bytes.argtypes = [_i64, _i64, _i32]
         L.mmvq_id_tq1_0_workspace_bytes.restype = _sz
         L.bqm_status_string.argtypes = [ctypes.c_int]
         L.bqm_status_string.restype = ctypes.c_char_p
         L.bqm_version.restype = ctypes.c_int
         for name in ("tq1_pack", "q8_1_quantize", "mmvq_tq1_0", "mmvq_tq1_0_f32",
-                     "mmvq_tq1_0_block_isums", "mmvq_id_tq1_0", "tq1_dequantize"):
+                     "mmvq_tq1_0_block_isums", "mmvq_id_tq1_0", "mmvq_id_tq1_0_slots",
+                     "tq1_dequantize"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -200,8 +203,7 @@ def mmvq_id_tq1_0_workspace_bytes(E, T, n_used):
     return int(library().mmvq_id_tq1_0_workspace_bytes(E, T, n_used))
 
 
-def mmvq_id_tq1_0(w, a, ids, E, N, K, T, n_used, out=None, workspace=None, stream=None):
-    """y fp32 [T, n_used, N]: expert ids[t][s]'s matrix times token t's activation."""
+def _mmvq_id(name, a_cols, w, a, ids, E, N, K, T, n_used, out, workspace, stream):
     torch = _torch()
     if out is None:
         out = torch.empty((T, n_used, N), dtype=torch.float32, device=w.device)
@@ -209,7 +211,7 @@ def mmvq_id_tq1_0(w, a, ids, E, N, K, T, n_used, out=None, workspace=None, strea
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=w.device)
     pw = _dev_tensor(w, "w", (torch.uint8,), E * N * (K // 256) * TQ1_BLOCK_BYTES)
-    pa = _dev_tensor(a, "a", (torch.uint8,), T * (K // 32) * Q81_BLOCK_BYTES, w.device)
+    pa = _dev_tensor(a, "a", (torch.uint8,), a_cols * (K // 32) * Q81_BLOCK_BYTES, w.device)
     pi = _dev_tensor(ids, "ids", (torch.int32,), T * n_used * 4, w.device)
     py = _dev_tensor(out, "out", (torch.float32,), T * n_used * N * 4, w.device)
     if workspace is None:
@@ -217,6 +219,17 @@ def mmvq_id_tq1_0(w, a, ids, E, N, K, T, n_used, out=None, workspace=None, strea
     else:
         pws = _dev_tensor(workspace, "workspace", (torch.uint8,), need, w.device)
         nws = workspace.numel()
-    _call("mmvq_id_tq1_0", pw, pa, pi, py, E, N, K, T, n_used, pws, nws,
-          _stream(stream, w.device))
+    _call(name, pw, pa, pi, py, E, N, K, T, n_used, pws, nws, _stream(stream, w.device))
     return out
+
+
+def mmvq_id_tq1_0(w, a, ids, E, N, K, T, n_used, out=None, workspace=None, stream=None):
+    """y fp32 [T, n_used, N]: expert ids[t][s]'s matrix times token t's activation."""
+    return _mmvq_id("mmvq_id_tq1_0", T, w, a, ids, E, N, K, T, n_used, out, workspace, stream)
+
+
+def mmvq_id_tq1_0_slots(w, a, ids, E, N, K, T, n_used, out=None, workspace=None, stream=None):
+    """y fp32 [T, n_used, N]: expert ids[t][s]'s matrix times pair (t, s)'s own
+    activation (a: [T * n_used, K/32] Q8_1 blocks)."""
+    return _mmvq_id("mmvq_id_tq1_0_slots", T * n_used, w, a, ids, E, N, K, T, n_used, out,
+                    workspace, stream)

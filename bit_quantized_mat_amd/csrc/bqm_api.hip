@@ -143,9 +143,11 @@ size_t mmvq_id_tq1_0_workspace_bytes(int64_t E, int64_t T, int32_t n_used)
     return bqm::mmvq_id_workspace_bytes(E, T, n_used);
 }
 
-int mmvq_id_tq1_0(const void *w, const void *a, const int32_t *ids, float *y, int64_t E,
-                  int64_t N, int64_t K, int64_t T, int32_t n_used, void *workspace,
-                  size_t workspace_bytes, void *stream)
+// Both expert-routed products; per_slot: one activation column per
+// (token, slot) pair instead of one per token.
+static int mmvq_id_call(const void *w, const void *a, const int32_t *ids, float *y, int64_t E,
+                        int64_t N, int64_t K, int64_t T, int32_t n_used, bool per_slot,
+                        void *workspace, size_t workspace_bytes, void *stream)
 {
     if (!w || !a || !ids || !y)
         return BQM_ERR_NULL;
@@ -153,7 +155,8 @@ int mmvq_id_tq1_0(const void *w, const void *a, const int32_t *ids, float *y, in
         return BQM_ERR_SHAPE;
     if (int rc = check_matrix(N, K))
         return rc;
-    if ((uint64_t)T * (uint64_t)(K / 32) * 36ull > kMaxBufferBytes)
+    const uint64_t a_cols = (uint64_t)T * (per_slot ? (uint64_t)n_used : 1ull);
+    if (a_cols * (uint64_t)(K / 32) * 36ull > kMaxBufferBytes)
         return BQM_ERR_SHAPE;
     if (!aligned4(w) || !aligned4(a) || !aligned4(ids) || !aligned4(y))
         return BQM_ERR_ALIGN;
@@ -164,7 +167,24 @@ int mmvq_id_tq1_0(const void *w, const void *a, const int32_t *ids, float *y, in
         return BQM_ERR_ALIGN;
     if (int rc = check_device())
         return rc;
-    return bqm::launch_mmvq_id(w, a, ids, y, E, N, K, T, n_used, workspace, as_stream(stream));
+    return bqm::launch_mmvq_id(w, a, ids, y, E, N, K, T, n_used, per_slot, workspace,
+                               as_stream(stream));
+}
+
+int mmvq_id_tq1_0(const void *w, const void *a, const int32_t *ids, float *y, int64_t E,
+                  int64_t N, int64_t K, int64_t T, int32_t n_used, void *workspace,
+                  size_t workspace_bytes, void *stream)
+{
+    return mmvq_id_call(w, a, ids, y, E, N, K, T, n_used, false, workspace, workspace_bytes,
+                        stream);
+}
+
+int mmvq_id_tq1_0_slots(const void *w, const void *a, const int32_t *ids, float *y, int64_t E,
+                        int64_t N, int64_t K, int64_t T, int32_t n_used, void *workspace,
+                        size_t workspace_bytes, void *stream)
+{
+    return mmvq_id_call(w, a, ids, y, E, N, K, T, n_used, true, workspace, workspace_bytes,
+                        stream);
 }
 
 const char *bqm_status_string(int status)

@@ -70,14 +70,17 @@ int launch_mmvq_mfma_resident(const void *w, const void *a, float *y, int32_t *i
 bool mfma_resident_id_supported(int64_t K);
 int launch_mmvq_mfma_resident_id(const void *w, const void *a, float *y, int64_t N, int64_t K,
                                  int64_t a_cols, const int32_t *routed, int max_items,
-                                 int max_wide, int n_used, hipStream_t stream);
+                                 int max_wide, int pairs_per_col, hipStream_t stream);
 int launch_mmvq(const void *w, const void *a, float *y, int32_t *isums, int64_t N, int64_t K,
                 int32_t T, hipStream_t stream);
+// per_slot: a holds one Q8_1 column per (token, slot) pair instead of one
+// per token.
 int launch_mmvq_id(const void *w, const void *a, const int32_t *ids, float *y, int64_t E,
-                   int64_t N, int64_t K, int64_t T, int32_t n_used, void *workspace,
-                   hipStream_t stream);
+                   int64_t N, int64_t K, int64_t T, int32_t n_used, bool per_slot,
+                   void *workspace, hipStream_t stream);
 size_t mmvq_id_workspace_bytes(int64_t E, int64_t T, int32_t n_used);
 int launch_mmvq_id_pairs(const void *w, const void *a, const int32_t *ids, float *y, int64_t E,
-                         int64_t N, int64_t K, int64_t T, int32_t n_used, hipStream_t stream);
+                         int64_t N, int64_t K, int64_t T, int32_t n_used, int pairs_per_col,
+                         hipStream_t stream);
 
 }  // namespace bqm

@@ -358,7 +358,7 @@ __global__ __launch_bounds__(256) void mmvq_id_kernel(const uint8_t *__restrict_
                                                       const int32_t *__restrict__ routed,
                                                       float *__restrict__ y, int E, int64_t N,
                                                       int nb, int T, int n_used, int lr_log2,
-                                                      int max_items, int ngroups)
+                                                      int max_items, int ngroups, int pairs_per_col)
 {
     extern __shared__ uint4 lds4[];
     uint32_t *act = reinterpret_cast<uint32_t *>(lds4);
@@ -390,12 +390,13 @@ __global__ __launch_bounds__(256) void mmvq_id_kernel(const uint8_t *__restrict_
     uint32_t col_off[kIdCols];
 #pragma unroll
     for (int t = 0; t < kIdCols; t++)
-        col_off[t] = (uint32_t)((it.sel[t] / n_used) * col_bytes);
+        col_off[t] = (uint32_t)((it.sel[t] / pairs_per_col) * col_bytes);
 #pragma unroll
     for (int t = 0; t < kIdCols; t++)
         if ((int)threadIdx.x == t)
             pair[t] = it.sel[t];
-    stage_item_columns(act, make_rsrc(a, (uint64_t)T * col_bytes), col_off, it.Tc, nb);
+    stage_item_columns(act, make_rsrc(a, (uint64_t)(T * n_used / pairs_per_col) * col_bytes),
+                       col_off, it.Tc, nb);
     __syncthreads();
     for (int g = blockIdx.x; g < ngroups; g += gridDim.x) {
         RawBlock nxt;
@@ -421,9 +422,12 @@ size_t mmvq_id_workspace_bytes(int64_t E, int64_t T, int32_t n_used)
 }
 
 int launch_mmvq_id(const void *w, const void *a, const int32_t *ids, float *y, int64_t E,
-                   int64_t N, int64_t K, int64_t T, int32_t n_used, void *workspace,
-                   hipStream_t stream)
+                   int64_t N, int64_t K, int64_t T, int32_t n_used, bool per_slot,
+                   void *workspace, hipStream_t stream)
 {
+    // consecutive pairs that read one activation column: a token's slots, or
+    // each pair alone
+    const int pairs_per_col = per_slot ? 1 : n_used;
     const int nb = (int)(K / kTq1BlockElems);
     const int lr = lanes_per_row_log2(nb);
     const int64_t P = T * n_used;
@@ -437,7 +441,7 @@ int launch_mmvq_id(const void *w, const void *a, const int32_t *ids, float *y, i
     // row must have at most 64 blocks (one per lane)
     const size_t lds = (size_t)narrow_cap * nb * kActStride * 4;
     if (nb > 64 || lds > lds_budget() || (P > kIdWaveRouteMax && !prepass))
-        return launch_mmvq_id_pairs(w, a, ids, y, E, N, K, T, n_used, stream);
+        return launch_mmvq_id_pairs(w, a, ids, y, E, N, K, T, n_used, pairs_per_col, stream);
     const int64_t max_items = id_max_items(E, P);
     int32_t *routed = nullptr;
     if (prepass) {
@@ -464,7 +468,7 @@ int launch_mmvq_id(const void *w, const void *a, const int32_t *ids, float *y, i
     hipLaunchKernelGGL(mmvq_id_kernel, dim3((unsigned)slices, (unsigned)max_narrow), dim3(256),
                        lds, stream, static_cast<const uint8_t *>(w),
                        static_cast<const uint8_t *>(a), ids, routed, y, (int)E, N, nb, (int)T,
-                       (int)n_used, lr, (int)max_items, (int)ngroups);
+                       (int)n_used, lr, (int)max_items, (int)ngroups, pairs_per_col);
     if (int rc = check_launch())
         return rc;
     if (!wide)
@@ -473,8 +477,8 @@ int launch_mmvq_id(const void *w, const void *a, const int32_t *ids, float *y, i
     // one per further kWideCols pairs
     const int64_t wide_experts = P / kMfmaMinCols < E ? P / kMfmaMinCols : E;
     const int64_t max_wide = wide_experts + P / kWideCols;
-    return launch_mmvq_mfma_resident_id(w, a, y, N, K, T, routed, (int)max_items, (int)max_wide,
-                                        n_used, stream);
+    return launch_mmvq_mfma_resident_id(w, a, y, N, K, P / pairs_per_col, routed, (int)max_items,
+                                        (int)max_wide, pairs_per_col, stream);
 }
 
 }  // namespace bqm

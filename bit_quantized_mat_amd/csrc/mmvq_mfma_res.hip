@@ -83,7 +83,7 @@ __device__ __forceinline__ void stage_all_columns(uint32_t *__restrict__ bq,
 struct WideItems {
     const int32_t *routed;
     int max_items;
-    int n_used;
+    int pairs_per_col;  // consecutive pairs that read one activation column
 };
 
 // NW: waves per workgroup; GPW: butterfly groups per wave (Lr / NW); NT:
@@ -148,7 +148,8 @@ __global__ __launch_bounds__(64 * NW) void mmvq_mfma_res_kernel(const uint8_t *_
         if ((int)threadIdx.x < T) {
             const int pr = items.routed[2 + 6 * items.max_items + first + threadIdx.x];
             colpair[threadIdx.x] = pr;
-            colbase[threadIdx.x] = (uint32_t)(pr / items.n_used) * (uint32_t)nblk * kQ81BlockBytes;
+            colbase[threadIdx.x] =
+                (uint32_t)(pr / items.pairs_per_col) * (uint32_t)nblk * kQ81BlockBytes;
         }
         return make_rsrc(w + (uint64_t)it[0] * w_bytes, w_bytes);
     };
@@ -401,7 +402,7 @@ static int launch_res(const uint8_t *w, const uint8_t *a, float *y, int32_t *isu
 template <int GPW>
 static int launch_res_id(const uint8_t *w, const uint8_t *a, float *y, int64_t N, int nb,
                          int a_cols, const int32_t *routed, int max_items, int max_wide,
-                         int n_used, hipStream_t stream)
+                         int pairs_per_col, hipStream_t stream)
 {
     constexpr int NW = 16, NT = 1, R = 1;
     constexpr bool DB = true;
@@ -413,7 +414,7 @@ static int launch_res_id(const uint8_t *w, const uint8_t *a, float *y, int64_t N
     const int64_t cap = resident_workgroups(k, 64 * NW, lds);
     const int64_t most = (int64_t)max_wide * ntiles;  // units when every item is in use
     const dim3 grid((unsigned)(most < cap ? most : cap));
-    const WideItems items = {routed, max_items, n_used};
+    const WideItems items = {routed, max_items, pairs_per_col};
     hipLaunchKernelGGL((mmvq_mfma_res_kernel<NW, GPW, NT, R, DB, false, true>), grid,
                        dim3(64 * NW), lds, stream, w, a, y, nullptr, N, nb, 16, (int)ntiles,
                        a_cols, items);
@@ -433,7 +434,7 @@ bool mfma_resident_id_supported(int64_t K)
 
 int launch_mmvq_mfma_resident_id(const void *w, const void *a, float *y, int64_t N, int64_t K,
                                  int64_t a_cols, const int32_t *routed, int max_items,
-                                 int max_wide, int n_used, hipStream_t stream)
+                                 int max_wide, int pairs_per_col, hipStream_t stream)
 {
     const int nb = (int)(K / kTq1BlockElems);
     const int Lr = 1 << lanes_per_row_log2(nb);
@@ -442,13 +443,13 @@ int launch_mmvq_mfma_resident_id(const void *w, const void *a, float *y, int64_t
     switch (Lr) {
     case 16:
         return launch_res_id<1>(wp, ap, y, N, nb, (int)a_cols, routed, max_items, max_wide,
-                                n_used, stream);
+                                pairs_per_col, stream);
     case 32:
         return launch_res_id<2>(wp, ap, y, N, nb, (int)a_cols, routed, max_items, max_wide,
-                                n_used, stream);
+                                pairs_per_col, stream);
     default:
         return launch_res_id<4>(wp, ap, y, N, nb, (int)a_cols, routed, max_items, max_wide,
-                                n_used, stream);
+                                pairs_per_col, stream);
     }
 }
 

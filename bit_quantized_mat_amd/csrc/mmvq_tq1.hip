@@ -223,7 +223,7 @@ __global__ __launch_bounds__(256) void mmvq_id_tq1_kernel(const uint8_t *__restr
                                                           const uint8_t *__restrict__ a,
                                                           const int32_t *__restrict__ ids,
                                                           float *__restrict__ y, int64_t E,
-                                                          int64_t N, int nb, int n_used,
+                                                          int64_t N, int nb, int pairs_per_col,
                                                           int lr_log2)
 {
     const int lane = threadIdx.x & 63;
@@ -234,7 +234,7 @@ __global__ __launch_bounds__(256) void mmvq_id_tq1_kernel(const uint8_t *__restr
         ((int64_t)blockIdx.x * 4 + wave) * rows_per_wave + (lane >> lr_log2);
     const int sub = lane & (Lr - 1);
     const int64_t pair = blockIdx.y;  // t * n_used + s
-    const int64_t t = pair / n_used;
+    const int64_t t = pair / pairs_per_col;  // its activation column
     int e = ids[pair];
     e = e < 0 ? 0 : (e >= E ? (int)E - 1 : e);  // keep accesses inside w for bad ids
     const uint64_t expert_bytes = (uint64_t)N * nb * kTq1BlockBytes;
@@ -244,7 +244,8 @@ __global__ __launch_bounds__(256) void mmvq_id_tq1_kernel(const uint8_t *__restr
 }
 
 int launch_mmvq_id_pairs(const void *w, const void *a, const int32_t *ids, float *y, int64_t E,
-                         int64_t N, int64_t K, int64_t T, int32_t n_used, hipStream_t stream)
+                         int64_t N, int64_t K, int64_t T, int32_t n_used, int pairs_per_col,
+                         hipStream_t stream)
 {
     const int nb = (int)(K / kTq1BlockElems);
     const int lr = lanes_per_row_log2(nb);
@@ -252,7 +253,7 @@ int launch_mmvq_id_pairs(const void *w, const void *a, const int32_t *ids, float
     const dim3 grid((unsigned)((N + rows_per_wg - 1) / rows_per_wg), (unsigned)(T * n_used));
     hipLaunchKernelGGL(mmvq_id_tq1_kernel, grid, dim3(256), 0, stream,
                        static_cast<const uint8_t *>(w), static_cast<const uint8_t *>(a), ids, y,
-                       E, N, nb, (int)n_used, lr);
+                       E, N, nb, pairs_per_col, lr);
     return check_launch();
 }
 

@@ -37,7 +37,7 @@ class Workload:
     d_hi: float = 0.1
     outlier_frac: float = 0.0          # fraction of activation entries scaled by outlier_scale
     outlier_scale: float = 20.0
-    seeds: Tuple[int, ...] = (0, 0)    # (weights, activations[, ids])
+    seeds: Tuple[int, ...] = (0, 0)    # (weights, activations[, ids, per-slot activations])
     experts: int = 0                   # > 0: MoE with this many experts
     n_used: int = 0                    # experts per token
     zipf_s: float = 1.1
@@ -54,7 +54,7 @@ WORKLOADS = {
     "ffn": Workload("ffn", N=14336, K=4096, Ts=(1, 2, 4, 8, 16, 32), p_zero=0.4,
                     d_lo=0.005, d_hi=0.05, outlier_frac=0.01, seeds=(401, 402),
                     note="FFN-shaped small batch with 1% x20 activation outliers"),
-    "moe": Workload("moe", N=1536, K=4096, Ts=(1, 8, 64), seeds=(501, 502, 503),
+    "moe": Workload("moe", N=1536, K=4096, Ts=(1, 8, 64), seeds=(501, 502, 503, 504),
                     experts=128, n_used=8, note="MoE expert-routed mat-vec, top-8 Zipf(1.1)"),
 }
 
@@ -125,6 +125,16 @@ def make_inputs(wl: Workload, T: int = None, N: int = None, K: int = None, E: in
         rng_i = np.random.default_rng(wl.seeds[2])
         ids = zipf_routing(rng_i, T, E, wl.n_used, wl.zipf_s)
     return Inputs(wl, trits, d16, x, ids)
+
+
+def slot_activations(wl: Workload, T: int = None, K: int = None):
+    """One fp32 activation column per (token, slot) pair of an MoE workload,
+    float32 [T * n_used, K], for the per-slot product (the down-projection
+    shape); same law as the workload's token activations, own seed."""
+    K = wl.K if K is None else K
+    T = max(wl.Ts) if T is None else T
+    rng = np.random.default_rng(wl.seeds[3])
+    return activations(rng, T * wl.n_used, K, wl.outlier_frac, wl.outlier_scale)
 
 
 def q8_1_blocks_from_fields(q, d16, s16):

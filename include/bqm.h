@@ -163,7 +163,22 @@ BQM_API int mmvq_id_tq1_0(const void *w, const void *a, const int32_t *ids, floa
                   int64_t E, int64_t N, int64_t K, int64_t T, int32_t n_used,
                   void *workspace, size_t workspace_bytes, void *stream);
 
-/* Workspace size mmvq_id_tq1_0 needs for these sizes (may be 0). */
+/* Expert-routed product with one activation per (token, slot) pair: the
+ * down-projection shape of a mixture of experts, where each slot's input is
+ * its own expert's earlier output (MUL_MAT_ID with ne11 = n_used, the other
+ * MoE shape beside the ne11 = 1 one of "CUDA: TQ1_0 mat-vec is load-bound by
+ * the per-32-element chunk contract", "Acceptance criteria"):
+ *   y[t][s][n] = mmvq(W[ids[t][s]], a[t][s])[n]
+ *   a [T][n_used][K/32] Q8_1 blocks, one column per pair; every other
+ *   argument, the workspace (same size query), the shapes, the alignment and
+ *   the error codes as mmvq_id_tq1_0, with the T * n_used columns of a below
+ *   4 GiB. Pairs that share an expert are multiplied together. */
+BQM_API int mmvq_id_tq1_0_slots(const void *w, const void *a, const int32_t *ids, float *y,
+                        int64_t E, int64_t N, int64_t K, int64_t T, int32_t n_used,
+                        void *workspace, size_t workspace_bytes, void *stream);
+
+/* Workspace size mmvq_id_tq1_0 and mmvq_id_tq1_0_slots need for these sizes
+ * (may be 0). */
 BQM_API size_t mmvq_id_tq1_0_workspace_bytes(int64_t E, int64_t T, int32_t n_used);
 
 /* Test twin of mmvq_tq1_0: runs the same decode and integer inner loop and

@@ -23,7 +23,7 @@ def _declared_functions():
 def test_header_declares_the_four_calls():
     names = _declared_functions()
     for n in ("tq1_pack", "q8_1_quantize", "mmvq_tq1_0", "mmvq_tq1_0_f32", "mmvq_id_tq1_0",
-              "tq1_dequantize",
+              "mmvq_id_tq1_0_slots", "tq1_dequantize",
               "mmvq_id_tq1_0_workspace_bytes", "mmvq_tq1_0_block_isums",
               "bqm_status_string", "bqm_version"):
         assert n in names
@@ -128,6 +128,29 @@ def test_mmvq_f32_rejects(args, expect):
 ])
 def test_tq1_dequantize_rejects(args, expect):
     assert bqm.library().tq1_dequantize(*args) == expect
+
+
+def test_mmvq_id_slots_rejects():
+    # the per-slot product validates like the shared one, and its activation
+    # buffer holds T * n_used columns: 1000 tokens x 8 slots of K = 2^20 is
+    # 9.4 GB, past the 4 GiB buffer limit (the shared shape would be 1.2 GB)
+    lib = bqm.library()
+    ws = P(0x100000)
+    base = [GOOD, GOOD, GOOD, GOOD, 8, 16, 256, 4, 2, ws, 1 << 20, None]
+
+    def call(**kw):
+        args = list(base)
+        names = ["w", "a", "ids", "y", "E", "N", "K", "T", "n_used", "ws", "wsb", "s"]
+        for k, v in kw.items():
+            args[names.index(k)] = v
+        return lib.mmvq_id_tq1_0_slots(*args)
+
+    assert call(a=None) == -1 and call(ids=None) == -1
+    assert call(E=0) == -2 and call(n_used=9) == -2 and call(K=100) == -2
+    assert call(T=40000, n_used=2) == -2
+    assert call(K=1 << 20, T=1000, n_used=8, E=8) == -2
+    assert call(a=ODD) == -3 and call(ws=P(0x100010)) == -3
+    assert call(T=40, n_used=2, ws=None, wsb=0) == -4        # more than 64 pairs need a workspace
 
 
 def test_mmvq_id_rejects():

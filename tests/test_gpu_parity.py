@@ -351,6 +351,34 @@ def test_mmvq_id_routing_edge_cases(bqm, case):
             assert np.array_equal(y1[0], y[t, s])
 
 
+@pytest.mark.parametrize("E,N,K,T,n_used,seed", [
+    (6, 40, 512, 5, 3, 1),        # routed inside the wave
+    (20, 100, 4096, 40, 4, 2),    # pre-pass, narrow and wide (matrix-core) items
+    (4, 72, 2304, 30, 3, 3),      # pre-pass, every expert wide
+    (5000, 3, 512, 70, 1, 4),     # past 4096 experts: one pair per workgroup row
+    (7, 20, 16640, 12, 2, 5),     # columns too long for LDS: one pair per workgroup row
+])
+def test_mmvq_id_slots_parity(bqm, E, N, K, T, n_used, seed):
+    """One activation per (token, slot) pair: against the oracle, and each
+    slot bitwise equal to the plain mat-vec of its expert on its own column."""
+    rng = np.random.default_rng(100 + seed)
+    trits = synth.ternary(rng, (E * N, K))
+    d16 = synth.block_scales_f16(rng, (E * N, K // 256), 0.01, 0.1)
+    x = synth.activations(rng, T * n_used, K)
+    ids = synth.zipf_routing(rng, T, E, n_used)
+    w, a, w_ref, a_ref = _prep(bqm, trits, d16, x)
+    _say("mmvq_id_slots", E, N, K, T, n_used)
+    y = _host(bqm.mmvq_id_tq1_0_slots(w, a, _dev(ids), E, N, K, T, n_used))
+    _, y64, ab = oracle.mmvq_id(w_ref, a_ref, ids, E, N, K, T, n_used, per_slot=True)
+    _assert_close(y, y64, ab, "mmvq_id_slots E=%d N=%d K=%d T=%d" % (E, N, K, T))
+    wr = w.view(E, N, -1)
+    for t in range(T):
+        for s in range(n_used):
+            p = t * n_used + s
+            y1 = _host(bqm.mmvq_tq1_0(wr[ids[t, s]].clone(), a[p:p + 1].clone(), N, K, 1))
+            assert np.array_equal(y1[0], y[t, s])
+
+
 def test_workload_moe_parity(bqm):
     wl, inp = _workload_inputs("moe")
     E, N, K, n_used = wl.experts, wl.N, wl.K, wl.n_used
@@ -364,6 +392,24 @@ def test_workload_moe_parity(bqm):
         for t in ts:
             _, y64, ab = oracle.mmvq_id(w_ref, a_ref_all[t:t + 1], ids[t:t + 1], E, N, K, 1, n_used)
             _assert_close(y[t:t + 1], y64, ab, "moe T=%d token %d" % (T, t))
+
+
+def test_workload_moe_slots_parity(bqm):
+    """The MoE workload with one activation per (token, slot) pair."""
+    wl, inp = _workload_inputs("moe")
+    E, N, K, n_used = wl.experts, wl.N, wl.K, wl.n_used
+    xs = synth.slot_activations(wl)
+    w, a_all, w_ref, a_ref_all = _prep(bqm, inp.trits, inp.d16, xs)
+    for T in wl.Ts:
+        _say("workload moe slots", T)
+        ids = inp.ids[:T]
+        y = _host(bqm.mmvq_id_tq1_0_slots(w, a_all[:T * n_used].contiguous(), _dev(ids),
+                                          E, N, K, T, n_used))
+        for t in sorted(set([0, T - 1, T // 2])):
+            cols = a_ref_all[t * n_used:(t + 1) * n_used]
+            _, y64, ab = oracle.mmvq_id(w_ref, cols, ids[t:t + 1], E, N, K, 1, n_used,
+                                        per_slot=True)
+            _assert_close(y[t:t + 1], y64, ab, "moe slots T=%d token %d" % (T, t))
 
 
 # ---------------------------------------------------------------------------
