@@ -26,11 +26,11 @@ constexpr int kStagedMaxCols = 8;
 // order, so a batch issued after the weights would wait for them.
 //   Q8_1 source: a task is one Q8_1 block (q dwords, d and s); lanes past
 //   the last task issue their loads at kIdleLoadOffset.
-//   fp32 source: a task is 4 of the 32 elements of a Q8_1 block; eight lanes
-//   quantize a block together (q8_1_block_by_8: the bytes the stand-alone
-//   quantize kernel would write). Every lane takes part in the group
-//   shuffles: groups past the end (whole groups, the task count being a
-//   multiple of 8) redo the last one and store nothing.
+//   fp32 source: a task is 16 of the 32 elements of a Q8_1 block; two lanes
+//   quantize a block together (q8_1_block_by_2: the bytes the stand-alone
+//   quantize kernel would write). Every lane takes part in the pair
+//   exchanges: pairs past the end (whole pairs, the task count being even)
+//   redo the last one and store nothing.
 template <bool F32>
 struct StageBatch;
 
@@ -43,16 +43,16 @@ struct StageBatch<false> {
 
 template <>
 struct StageBatch<true> {
-    static constexpr int kAhead = 4;
-    u32x4 v[kAhead];
+    static constexpr int kAhead = 1;
+    u32x4 v[kAhead][4];
 };
 
 // Tasks of one column of cb blocks starting at block B0: 8 per block (Q8_1)
-// or 64 (fp32).
+// or 16 (fp32).
 template <bool F32>
 __device__ __forceinline__ int stage_tasks(int cb)
 {
-    return cb * (F32 ? 64 : 8);
+    return cb * (F32 ? 16 : 8);
 }
 
 template <bool F32>
@@ -67,10 +67,13 @@ __device__ __forceinline__ void stage_load(StageBatch<F32> &sb, __amdgpu_buffer_
         const int i = base + k * nthreads + tid;
         if constexpr (F32) {
             const int ii = i < tasks ? i : tasks - 1;
-            const int g = ii >> 3, j = ii & 7;
+            const int g = ii >> 1, h = ii & 1;  // Q8_1 block of the chunk, its half
             const int bi = g >> 3, c = g & 7;
-            sb.v[k] = ld_b128(ra, col_off + (uint32_t)(((B0 + bi) * kTq1BlockElems +
-                                                        c * kQ81BlockElems + 4 * j) * 4));
+            const uint32_t off = col_off + (uint32_t)(((B0 + bi) * kTq1BlockElems +
+                                                       c * kQ81BlockElems + 16 * h) * 4);
+#pragma unroll
+            for (int u = 0; u < 4; u++)
+                sb.v[k][u] = ld_b128(ra, off + 16 * u);
         } else {
             // lanes past the end load nothing real (no branch around the
             // loads, so the compiler can count them) and store nothing
@@ -93,14 +96,23 @@ __device__ __forceinline__ void stage_store(const StageBatch<F32> &sb, uint32_t 
     for (int k = 0; k < kAhead; k++) {
         const int i = base + k * nthreads + tid;
         if constexpr (F32) {
-            const Q81Part p = q8_1_block_by_8(__uint_as_float(sb.v[k].x), __uint_as_float(sb.v[k].y),
-                                              __uint_as_float(sb.v[k].z), __uint_as_float(sb.v[k].w));
+            float xs[16];
+#pragma unroll
+            for (int u = 0; u < 4; u++) {
+                xs[4 * u] = __uint_as_float(sb.v[k][u].x);
+                xs[4 * u + 1] = __uint_as_float(sb.v[k][u].y);
+                xs[4 * u + 2] = __uint_as_float(sb.v[k][u].z);
+                xs[4 * u + 3] = __uint_as_float(sb.v[k][u].w);
+            }
+            const Q81Part p = q8_1_block_by_2(xs);
             if (i < tasks) {
-                const int g = i >> 3, j = i & 7;
+                const int g = i >> 1, h = i & 1;
                 const int bi = g >> 3, c = g & 7;
                 uint32_t *dst = act + bi * kActStride;
-                dst[8 * j + c] = p.q4;
-                if (j == 0) {
+#pragma unroll
+                for (int u = 0; u < 4; u++)
+                    dst[8 * (4 * h + u) + c] = p.q4[u];
+                if (h == 0) {
                     dst[64 + c] = __float_as_uint(f16_bits_to_f32(f32_to_f16_bits(p.d)));
                     dst[72 + c] = (uint32_t)(-p.sum);
                 }
@@ -283,6 +295,9 @@ __device__ __forceinline__ void staged_rows(__amdgpu_buffer_rsrc_t rw, __amdgpu_
                                               ? row_off + (uint32_t)first * kTq1BlockBytes
                                               : kIdleLoadOffset);
         __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+        // and no arithmetic on the batch (with its wait) moves up between
+        // the weight loads
+        __builtin_amdgcn_sched_barrier(0);
         stage_column<F32>(act, ra, col_off[0], B0, cb, tid, 256, &head);  // T >= 1
 #pragma unroll
         for (int t = 1; t < TC; t++)

@@ -1,4 +1,4 @@
-// q8_1.hpp -- Q8_1 quantization of one 32-element block by eight lanes.
+// q8_1.hpp -- Q8_1 quantization of one 32-element block by two lanes.
 //
 // Q8_1 ("CUDA: TQ1_0 mat-vec is load-bound by the per-32-element chunk
 // contract", "Current behavior": the mat-vec consumes Q8_1 activations in
@@ -14,63 +14,49 @@
 
 namespace bqm {
 
-// Reductions over an aligned group of eight lanes with DPP lane moves (no
-// LDS round trip): swap neighbours, swap pairs (quad permutes), then mirror
-// the two quads of the half row. Every lane ends with the group's value.
-constexpr int kDppQuadXor1 = 0xb1;       // quad_perm [1, 0, 3, 2]
-constexpr int kDppQuadXor2 = 0x4e;       // quad_perm [2, 3, 0, 1]
-constexpr int kDppHalfRowMirror = 0x141; // lane i <- lane 7 - i within 8
+// A block is quantized by two neighbouring lanes (an aligned pair in the
+// wave), lane h of the pair holding elements 16h..16h+15: per lane, one
+// block-wide step (the two divisions) and one lane exchange per reduction,
+// against sixteen elements of per-element work.
+constexpr int kDppQuadXor1 = 0xb1;  // quad_perm [1, 0, 3, 2]: swap neighbouring lanes
 
-template <int CTRL>
-__device__ __forceinline__ int dpp_i32(int v)
+__device__ __forceinline__ int dpp_swap_pair(int v)
 {
-    return __builtin_amdgcn_mov_dpp(v, CTRL, 0xf, 0xf, true);
+    return __builtin_amdgcn_mov_dpp(v, kDppQuadXor1, 0xf, 0xf, true);
 }
 
-__device__ __forceinline__ float group8_max(float v)
-{
-    v = fmaxf(v, __int_as_float(dpp_i32<kDppQuadXor1>(__float_as_int(v))));
-    v = fmaxf(v, __int_as_float(dpp_i32<kDppQuadXor2>(__float_as_int(v))));
-    v = fmaxf(v, __int_as_float(dpp_i32<kDppHalfRowMirror>(__float_as_int(v))));
-    return v;
-}
-
-__device__ __forceinline__ int group8_sum(int v)
-{
-    v += dpp_i32<kDppQuadXor1>(v);
-    v += dpp_i32<kDppQuadXor2>(v);
-    v += dpp_i32<kDppHalfRowMirror>(v);
-    return v;
-}
-
-// The block held by eight consecutive lanes (an aligned group of 8 in the
-// wave), lane j of the group holding elements 4j..4j+3. Every lane of the
-// wave must call this (the reductions move values between lanes of a group).
 struct Q81Part {
-    uint32_t q4;  // this lane's four q bytes, element 4j in the low byte
-    float d;      // the block's scale (fp32, before rounding to fp16)
-    int sum;      // sum of the block's 32 q values
+    uint32_t q4[4];  // this lane's sixteen q bytes, element 16h + 4k + i in byte i of q4[k]
+    float d;         // the block's scale (fp32, before rounding to fp16)
+    int sum;         // sum of the block's 32 q values
 };
 
-__device__ __forceinline__ Q81Part q8_1_block_by_8(float x0, float x1, float x2, float x3)
+// Every lane of the wave must call this (the reductions move values between
+// the lanes of a pair).
+__device__ __forceinline__ Q81Part q8_1_block_by_2(const float (&x)[16])
 {
-    const float amax =
-        group8_max(fmaxf(fmaxf(fabsf(x0), fabsf(x1)), fmaxf(fabsf(x2), fabsf(x3))));
+    float m = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 16; i++)
+        m = fmaxf(m, fabsf(x[i]));
+    const float amax = fmaxf(m, __int_as_float(dpp_swap_pair(__float_as_int(m))));
     Q81Part r;
     r.d = amax / 127.0f;
     const float id = r.d != 0.0f ? 1.0f / r.d : 0.0f;
-    const float xs[4] = {x0, x1, x2, x3};
-    uint32_t q4 = 0;
     int sum = 0;
 #pragma unroll
-    for (int i = 0; i < 4; i++) {
-        int q = (int)roundf(xs[i] * id);
-        q = q > 127 ? 127 : (q < -127 ? -127 : q);
-        sum += q;
-        q4 |= (uint32_t)(q & 0xff) << (8 * i);
+    for (int k = 0; k < 4; k++) {
+        uint32_t q4 = 0;
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            int q = (int)roundf(x[4 * k + i] * id);
+            q = q > 127 ? 127 : (q < -127 ? -127 : q);
+            sum += q;
+            q4 |= (uint32_t)(q & 0xff) << (8 * i);
+        }
+        r.q4[k] = q4;
     }
-    r.q4 = q4;
-    r.sum = group8_sum(sum);
+    r.sum = sum + dpp_swap_pair(sum);
     return r;
 }
 

@@ -11,30 +11,42 @@
 
 namespace bqm {
 
-// Eight lanes per Q8_1 block, four elements per lane (one 16-byte load and
-// one dword of q bytes each); the arithmetic is q8_1_block_by_8.
+// Two lanes per Q8_1 block, sixteen elements per lane (four 16-byte loads
+// and four dwords of q bytes each); the arithmetic is q8_1_block_by_2.
 __global__ __launch_bounds__(256) void q8_1_quantize_kernel(const float *__restrict__ x,
                                                             uint8_t *__restrict__ a,
                                                             int64_t nblocks)
 {
     const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    const int64_t blk = t >> 3;
-    const int j = (int)(t & 7);
-    // groups past the end compute on a copy of the last block and store nothing,
-    // so that every lane takes part in the group shuffles
+    const int64_t blk = t >> 1;
+    const int h = (int)(t & 1);
+    // pairs past the end compute on a copy of the last block and store nothing,
+    // so that both lanes of every pair take part in the exchanges
     const int64_t src = blk < nblocks ? blk : nblocks - 1;
     // a buffer load needs only the dword alignment the entry point checks; the
-    // descriptor covers this workgroup's 32 blocks
-    const int64_t first = (int64_t)blockIdx.x * (blockDim.x >> 3);
+    // descriptor covers this workgroup's 128 blocks
+    const int64_t first = (int64_t)blockIdx.x * (blockDim.x >> 1);
     const __amdgpu_buffer_rsrc_t rx = make_rsrc(
         x + first * kQ81BlockElems, (uint64_t)(nblocks - first) * kQ81BlockElems * sizeof(float));
-    const u32x4 v = ld_b128(rx, (uint32_t)((src - first) * kQ81BlockElems + 4 * j) * 4);
-    const Q81Part p = q8_1_block_by_8(__uint_as_float(v.x), __uint_as_float(v.y),
-                                      __uint_as_float(v.z), __uint_as_float(v.w));
+    const uint32_t off = (uint32_t)((src - first) * kQ81BlockElems + 16 * h) * 4;
+    float xs[16];
+#pragma unroll
+    for (int k = 0; k < 4; k++) {
+        const u32x4 v = ld_b128(rx, off + 16 * k);
+        xs[4 * k] = __uint_as_float(v.x);
+        xs[4 * k + 1] = __uint_as_float(v.y);
+        xs[4 * k + 2] = __uint_as_float(v.z);
+        xs[4 * k + 3] = __uint_as_float(v.w);
+    }
+    const Q81Part p = q8_1_block_by_2(xs);
     if (blk < nblocks) {
         uint32_t *out = reinterpret_cast<uint32_t *>(a + blk * kQ81BlockBytes);
-        out[j] = p.q4;
-        if (j == 0)
+        // blocks are 36 bytes apart: dword stores (the output is only
+        // dword-aligned)
+#pragma unroll
+        for (int k = 0; k < 4; k++)
+            out[4 * h + k] = p.q4[k];
+        if (h == 0)
             out[8] = q8_1_scale_field(p);
     }
 }
@@ -42,7 +54,7 @@ __global__ __launch_bounds__(256) void q8_1_quantize_kernel(const float *__restr
 int launch_q8_1_quantize(const float *x, void *a, int64_t T, int64_t K, hipStream_t stream)
 {
     const int64_t nblocks = T * (K / kQ81BlockElems);
-    const int64_t threads = nblocks * 8;
+    const int64_t threads = nblocks * 2;
     const int64_t grid = (threads + 255) / 256;
     hipLaunchKernelGGL(q8_1_quantize_kernel, dim3((unsigned)grid), dim3(256), 0, stream, x,
                        static_cast<uint8_t *>(a), nblocks);
