@@ -34,6 +34,8 @@ if ROOT not in sys.path:
 
 METRIC = "µs/call and achieved HBM GB/s (% peak), TQ1_0 mat-vec N=4096 K=4096 T=1"
 HBM_PEAK_GBS = 8000.0
+# column counts of the prefill rows of the sweep (many-column product)
+PREFILL_COLS = (64, 128, 512)
 COUNTERS_FILE = os.path.join(ROOT, "profiles", "counters_mmvq_tq1_0_decode_4096x4096.json")
 ROTATION_BYTES = 1 << 30
 
@@ -275,6 +277,32 @@ def sweep(path, torch, np, bqm, synth, dev, launches, only=None):
             row = {"workload": name, "op": "mmvq_tq1_0", "N": N, "K": K, "T": T, "us": round(us, 3),
                    "algorithmic_bytes": b, "gbs": round(b / us / 1e3, 1),
                    "frac_of_8tbs": round(b / us / 1e3 / HBM_PEAK_GBS, 4)}
+            table.append(row)
+            log("sweep", row)
+        del wrot, a_all, w0
+        torch.cuda.empty_cache()
+    # many-column product: prefill batches on the decode and ffn matrices
+    for name in ("decode", "ffn"):
+        if only and "prefill" not in only:
+            break
+        wl = synth.WORKLOADS[name]
+        Tmax = max(PREFILL_COLS)
+        inp = synth.make_inputs(wl, T=Tmax)
+        N, K = wl.N, wl.K
+        w0 = bqm.tq1_pack(torch.from_numpy(inp.trits).to(dev),
+                          torch.from_numpy(inp.d16.view(np.int16)).to(dev))
+        wrot, R = rotation(torch, w0, dev)
+        a_all = bqm.q8_1_quantize(torch.from_numpy(inp.x).to(dev))
+        for T in PREFILL_COLS:
+            a = a_all[:T].contiguous()
+            y = torch.empty((T, N), dtype=torch.float32, device=dev)
+            us = graph_us(torch, lambda i: bqm.mm_tq1_0(wrot[i % R], a, N, K, T, out=y),
+                          max(10, launches // 4))
+            b = algorithmic_bytes(N, K, T)
+            row = {"workload": name + " prefill", "op": "mm_tq1_0", "N": N, "K": K, "T": T,
+                   "us": round(us, 3), "algorithmic_bytes": b, "gbs": round(b / us / 1e3, 1),
+                   "frac_of_8tbs": round(b / us / 1e3 / HBM_PEAK_GBS, 4),
+                   "int8_tops": round(2.0 * N * K * T / us / 1e6, 1)}
             table.append(row)
             log("sweep", row)
         del wrot, a_all, w0

@@ -10,7 +10,8 @@ import ctypes
 import os
 
 __all__ = [
-    "BqmError", "library", "library_path", "tq1_pack", "q8_1_quantize", "mmvq_tq1_0",
+    "BqmError", "library", "library_path", "tq1_pack", "q8_1_quantize", "mmvq_tq1_0", "mm_tq1_0",
+    "MM_MAX_COLS",
     "mmvq_tq1_0_f32", "MMVQ_F32_MAX_COLS", "tq1_dequantize",
     "mmvq_id_tq1_0", "mmvq_id_tq1_0_slots", "mmvq_id_tq1_0_workspace_bytes",
     "mmvq_tq1_0_block_isums",
@@ -21,6 +22,7 @@ TQ1_BLOCK_BYTES = 54
 Q81_BLOCK_BYTES = 36
 MMVQ_MAX_COLS = 32
 MMVQ_F32_MAX_COLS = 8
+MM_MAX_COLS = 65536
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _lib = None
@@ -54,6 +56,7 @@ def library():
         L.q8_1_quantize.argtypes = [_p, _p, _i64, _i64, _p]
         L.mmvq_tq1_0.argtypes = [_p, _p, _p, _i64, _i64, _i32, _p]
         L.mmvq_tq1_0_f32.argtypes = [_p, _p, _p, _i64, _i64, _i32, _p]
+        L.mm_tq1_0.argtypes = [_p, _p, _p, _i64, _i64, _i64, _p]
         L.tq1_dequantize.argtypes = [_p, _p, _p, _i64, _i64, _i64, _i32, _p]
         L.mmvq_tq1_0_block_isums.argtypes = [_p, _p, _p, _i64, _i64, _i32, _p]
         L.mmvq_id_tq1_0.argtypes = [_p, _p, _p, _p, _i64, _i64, _i64, _i64, _i32, _p, _sz, _p]
@@ -63,7 +66,7 @@ def library():
         L.bqm_status_string.argtypes = [ctypes.c_int]
         L.bqm_status_string.restype = ctypes.c_char_p
         L.bqm_version.restype = ctypes.c_int
-        for name in ("tq1_pack", "q8_1_quantize", "mmvq_tq1_0", "mmvq_tq1_0_f32",
+        for name in ("tq1_pack", "q8_1_quantize", "mmvq_tq1_0", "mm_tq1_0", "mmvq_tq1_0_f32",
                      "mmvq_tq1_0_block_isums", "mmvq_id_tq1_0", "mmvq_id_tq1_0_slots",
                      "tq1_dequantize"):
             getattr(L, name).restype = ctypes.c_int
@@ -147,6 +150,18 @@ def mmvq_tq1_0(w, a, N, K, T, out=None, stream=None):
         out = torch.empty((T, N), dtype=torch.float32, device=w.device)
     pw, pa = _mmvq_args(w, a, N, K, T)
     _call("mmvq_tq1_0", pw, pa, _dev_tensor(out, "out", (torch.float32,), T * N * 4, w.device),
+          N, K, T, _stream(stream, w.device))
+    return out
+
+
+def mm_tq1_0(w, a, N, K, T, out=None, stream=None):
+    """y fp32 [T, N] = TQ1_0 weights [N, K] times T Q8_1 activation columns,
+    any T up to MM_MAX_COLS (each column bitwise mmvq_tq1_0's)."""
+    torch = _torch()
+    if out is None:
+        out = torch.empty((T, N), dtype=torch.float32, device=w.device)
+    pw, pa = _mmvq_args(w, a, N, K, T)
+    _call("mm_tq1_0", pw, pa, _dev_tensor(out, "out", (torch.float32,), T * N * 4, w.device),
           N, K, T, _stream(stream, w.device))
     return out
 

@@ -92,6 +92,22 @@ int mmvq_tq1_0(const void *w, const void *a, float *y, int64_t N, int64_t K, int
     return bqm::launch_mmvq(w, a, y, nullptr, N, K, T, as_stream(stream));
 }
 
+int mm_tq1_0(const void *w, const void *a, float *y, int64_t N, int64_t K, int64_t T,
+             void *stream)
+{
+    if (!w || !a || !y)
+        return BQM_ERR_NULL;
+    if (int rc = check_matrix(N, K))
+        return rc;
+    if (T < 1 || T > BQM_MM_MAX_COLS || (uint64_t)T * (uint64_t)(K / 32) * 36ull > kMaxBufferBytes)
+        return BQM_ERR_SHAPE;
+    if (!aligned4(w) || !aligned4(a) || !aligned4(y))
+        return BQM_ERR_ALIGN;
+    if (int rc = check_device())
+        return rc;
+    return bqm::launch_mm(w, a, y, N, K, T, as_stream(stream));
+}
+
 int mmvq_tq1_0_f32(const void *w, const float *x, float *y, int64_t N, int64_t K, int32_t T,
                    void *stream)
 {

@@ -71,8 +71,16 @@ bool mfma_resident_id_supported(int64_t K);
 int launch_mmvq_mfma_resident_id(const void *w, const void *a, float *y, int64_t N, int64_t K,
                                  int64_t a_cols, const int32_t *routed, int max_items,
                                  int max_wide, int pairs_per_col, hipStream_t stream);
+// Many-column product (any T): the resident kernel's item mode over chunks
+// of 32 (or 16) columns; whether it takes rows of K elements, and its
+// launcher.
+bool mm_chunked_supported(int64_t K);
+int launch_mm_chunked(const void *w, const void *a, float *y, int64_t N, int64_t K, int64_t T,
+                      hipStream_t stream);
 int launch_mmvq(const void *w, const void *a, float *y, int32_t *isums, int64_t N, int64_t K,
                 int32_t T, hipStream_t stream);
+int launch_mm(const void *w, const void *a, float *y, int64_t N, int64_t K, int64_t T,
+              hipStream_t stream);
 // per_slot: a holds one Q8_1 column per (token, slot) pair instead of one
 // per token.
 int launch_mmvq_id(const void *w, const void *a, const int32_t *ids, float *y, int64_t E,

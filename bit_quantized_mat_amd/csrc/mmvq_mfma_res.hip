@@ -75,11 +75,12 @@ __device__ __forceinline__ void stage_all_columns(uint32_t *__restrict__ bq,
     }
 }
 
-// Work item of the expert-routed mode: its entry in the routing table the
+// Work items of the item mode. Expert-routed products: the routing table the
 // routing pre-pass writes (mmvq_id.hip): item k of the wide list is
 // routed[2 + 3 (max_items + k) ..] = (expert, first run slot, pairs), and run
 // slot s holds pair index routed[2 + 6 max_items + s]; routed[1] counts the
-// wide items.
+// wide items. Many-column products (routed == nullptr): item k is columns
+// 16 NT k .. 16 NT k + 16 NT - 1 of the one matrix's a_cols columns.
 struct WideItems {
     const int32_t *routed;
     int max_items;
@@ -89,9 +90,10 @@ struct WideItems {
 // NW: waves per workgroup; GPW: butterfly groups per wave (Lr / NW); NT:
 // 16-column tiles (1 or 2); R: 16-row tiles per workgroup tile; DB: partial
 // sums double-buffered; ISUMS: write the exact per-sub-block sums instead of
-// outputs; ID: expert-routed mode, one wide work item per blockIdx.y (its
-// expert's matrix, its pairs' token columns, outputs y[pair][row]); `a_cols`
-// is the number of columns a holds (T in the plain mode).
+// outputs; ID: item mode, work items of up to 16 NT columns (an expert's
+// matrix against its pairs' columns, outputs y[pair][row]; or a chunk of the
+// columns of a many-column product); `a_cols` is the number of columns a
+// holds (T in the plain mode).
 template <int NW, int GPW, int NT, int R, bool DB, bool ISUMS, bool ID>
 __global__ __launch_bounds__(64 * NW) void mmvq_mfma_res_kernel(const uint8_t *__restrict__ w,
                                                                 const uint8_t *__restrict__ a,
@@ -126,8 +128,10 @@ __global__ __launch_bounds__(64 * NW) void mmvq_mfma_res_kernel(const uint8_t *_
     // that it restages columns only when its range enters the next item.
     int64_t u, u_end;
     int ustride;
+    constexpr int C = 16 * NT;  // columns of a chunk (item mode, no routing table)
     if (ID) {
-        const int64_t units = (int64_t)items.routed[1] * ntiles;
+        const int n_items = items.routed ? items.routed[1] : (a_cols + C - 1) / C;
+        const int64_t units = (int64_t)n_items * ntiles;
         u = (int64_t)blockIdx.x * units / gridDim.x;
         u_end = (int64_t)(blockIdx.x + 1) * units / gridDim.x;
         ustride = 1;
@@ -142,6 +146,15 @@ __global__ __launch_bounds__(64 * NW) void mmvq_mfma_res_kernel(const uint8_t *_
     int tile = (int)(u - (int64_t)item * ntiles);
     // the item's matrix, column count and column tables (ID)
     auto take_item = [&](int k) {
+        if (!items.routed) {
+            const int c0 = k * C;
+            T = a_cols - c0 < C ? a_cols - c0 : C;
+            if ((int)threadIdx.x < T) {
+                colpair[threadIdx.x] = c0 + threadIdx.x;
+                colbase[threadIdx.x] = (uint32_t)(c0 + threadIdx.x) * nblk * kQ81BlockBytes;
+            }
+            return make_rsrc(w, w_bytes);
+        }
         const int32_t *it = items.routed + 2 + 3 * (items.max_items + k);
         const int first = it[1];
         T = it[2];
@@ -424,6 +437,62 @@ static int launch_res_id(const uint8_t *w, const uint8_t *a, float *y, int64_t N
 // 16 waves for one column tile, 8 for two (their register budgets); the
 // column tiles' partial sums double-buffered for one tile, single for two
 static int res_waves(int NT) { return NT == 1 ? 16 : 8; }
+
+// Many-column product: chunks of 32 columns on 8 waves where they fit LDS,
+// else of 16 columns on 16 waves; 0 if neither fits.
+static int mm_chunk_cols(int nb)
+{
+    const int Lr = 1 << lanes_per_row_log2(nb);
+    if (Lr >= 8 && res_lds_bytes(8, 2, 1, nb, false, true) <= lds_budget())
+        return 32;
+    if (Lr >= 16 && res_lds_bytes(16, 1, 1, nb, true, true) <= lds_budget())
+        return 16;
+    return 0;
+}
+
+bool mm_chunked_supported(int64_t K) { return mm_chunk_cols((int)(K / kTq1BlockElems)) > 0; }
+
+template <int NW, int GPW, int NT, bool DB>
+static int launch_mm(const uint8_t *w, const uint8_t *a, float *y, int64_t N, int nb, int T,
+                     hipStream_t stream)
+{
+    constexpr int R = 1;
+    const int64_t ntiles = (N + 16 * R - 1) / (16 * R);
+    const size_t lds = res_lds_bytes(NW, NT, R, nb, DB, true);
+    const void *k =
+        reinterpret_cast<const void *>(&mmvq_mfma_res_kernel<NW, GPW, NT, R, DB, false, true>);
+    allow_dynamic_lds(k, lds);
+    const int64_t cap = resident_workgroups(k, 64 * NW, lds);
+    const int64_t units = (int64_t)((T + 16 * NT - 1) / (16 * NT)) * ntiles;
+    const dim3 grid((unsigned)(units < cap ? units : cap));
+    const WideItems chunks = {nullptr, 0, 1};
+    hipLaunchKernelGGL((mmvq_mfma_res_kernel<NW, GPW, NT, R, DB, false, true>), grid,
+                       dim3(64 * NW), lds, stream, w, a, y, nullptr, N, nb, 16 * NT, (int)ntiles,
+                       T, chunks);
+    return check_launch();
+}
+
+int launch_mm_chunked(const void *w, const void *a, float *y, int64_t N, int64_t K, int64_t T,
+                      hipStream_t stream)
+{
+    const int nb = (int)(K / kTq1BlockElems);
+    const int Lr = 1 << lanes_per_row_log2(nb);
+    const uint8_t *wp = static_cast<const uint8_t *>(w);
+    const uint8_t *ap = static_cast<const uint8_t *>(a);
+    if (mm_chunk_cols(nb) == 32) {
+        switch (Lr) {
+        case 8: return launch_mm<8, 1, 2, false>(wp, ap, y, N, nb, (int)T, stream);
+        case 16: return launch_mm<8, 2, 2, false>(wp, ap, y, N, nb, (int)T, stream);
+        case 32: return launch_mm<8, 4, 2, false>(wp, ap, y, N, nb, (int)T, stream);
+        default: return launch_mm<8, 8, 2, false>(wp, ap, y, N, nb, (int)T, stream);
+        }
+    }
+    switch (Lr) {
+    case 16: return launch_mm<16, 1, 1, true>(wp, ap, y, N, nb, (int)T, stream);
+    case 32: return launch_mm<16, 2, 1, true>(wp, ap, y, N, nb, (int)T, stream);
+    default: return launch_mm<16, 4, 1, true>(wp, ap, y, N, nb, (int)T, stream);
+    }
+}
 
 bool mfma_resident_id_supported(int64_t K)
 {

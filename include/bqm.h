@@ -107,6 +107,20 @@ BQM_API int q8_1_quantize(const float *x, void *a, int64_t T, int64_t K, void *s
 BQM_API int mmvq_tq1_0(const void *w, const void *a, float *y,
                int64_t N, int64_t K, int32_t T, void *stream);
 
+/* Largest number of activation columns mm_tq1_0 accepts. */
+#define BQM_MM_MAX_COLS 65536
+
+/* Many-column product (prefill-sized batches; row f2 beside the decode
+ * product: the pages' pp512 workload, "CUDA: TQ1_0 mat-vec is load-bound by
+ * the per-32-element chunk contract", "Measured impact"): the same
+ *   y[t][n] = sum_j fp32(d_w[n][j/8]) * fp32(d_a[t][j]) * isum[t][n][j]
+ * as mmvq_tq1_0, for 1 <= T <= BQM_MM_MAX_COLS columns, the T columns of a
+ * below 4 GiB. Every output is bitwise the one mmvq_tq1_0 gives for its
+ * column (up to 32 columns the call is mmvq_tq1_0). Other shapes, alignment,
+ * ownership and errors as mmvq_tq1_0. */
+BQM_API int mm_tq1_0(const void *w, const void *a, float *y,
+             int64_t N, int64_t K, int64_t T, void *stream);
+
 /* Largest number of activation columns mmvq_tq1_0_f32 accepts. */
 #define BQM_MMVQ_F32_MAX_COLS 8
 

@@ -22,7 +22,8 @@ def _declared_functions():
 
 def test_header_declares_the_four_calls():
     names = _declared_functions()
-    for n in ("tq1_pack", "q8_1_quantize", "mmvq_tq1_0", "mmvq_tq1_0_f32", "mmvq_id_tq1_0",
+    for n in ("tq1_pack", "q8_1_quantize", "mmvq_tq1_0", "mm_tq1_0", "mmvq_tq1_0_f32",
+              "mmvq_id_tq1_0",
               "mmvq_id_tq1_0_slots", "tq1_dequantize",
               "mmvq_id_tq1_0_workspace_bytes", "mmvq_tq1_0_block_isums",
               "bqm_status_string", "bqm_version"):
@@ -128,6 +129,19 @@ def test_mmvq_f32_rejects(args, expect):
 ])
 def test_tq1_dequantize_rejects(args, expect):
     assert bqm.library().tq1_dequantize(*args) == expect
+
+
+def test_mm_rejects():
+    # invalid arguments return before touching the device
+    lib = bqm.library()
+    mm = lib.mm_tq1_0
+    assert mm(None, GOOD, GOOD, 16, 256, 100, None) == -1
+    assert mm(GOOD, GOOD, GOOD, 16, 256, 0, None) == -2
+    assert mm(GOOD, GOOD, GOOD, 16, 256, 65537, None) == -2        # past BQM_MM_MAX_COLS
+    assert mm(GOOD, GOOD, GOOD, 16, 100, 100, None) == -2          # K % 256
+    assert mm(GOOD, GOOD, GOOD, 0, 256, 100, None) == -2
+    assert mm(GOOD, GOOD, GOOD, 16, 1 << 24, 65536, None) == -2    # activations past 4 GiB
+    assert mm(GOOD, ODD, GOOD, 16, 256, 100, None) == -3
 
 
 def test_mmvq_id_slots_rejects():

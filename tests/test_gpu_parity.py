@@ -413,6 +413,46 @@ def test_workload_moe_slots_parity(bqm):
 
 
 # ---------------------------------------------------------------------------
+# Many-column product (prefill batches)
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("N,K,T", [
+    (300, 4096, 100),   # chunks of 32 columns, a ragged last chunk
+    (67, 2304, 40),     # chunks of 32, rows of 9 blocks
+    (130, 6144, 70),    # 32-column chunks do not fit LDS: chunks of 16
+    (40, 16384, 50),    # no chunk fits: successive 32-column products
+    (33, 256, 33),      # one-block rows: successive 32-column products
+    (515, 4096, 32),    # up to 32 columns: the plain product
+])
+def test_mm_parity(bqm, N, K, T):
+    trits, d16, x = _case(N, K, T, seed=7000 + N + T)
+    w, a, w_ref, a_ref = _prep(bqm, trits, d16, x)
+    _say("mm", N, K, T)
+    y = _host(bqm.mm_tq1_0(w, a, N, K, T))
+    _, y64, ab = oracle.mmvq(w_ref, a_ref, N, K, T)
+    _assert_close(y, y64, ab, "mm N=%d K=%d T=%d" % (N, K, T))
+    # columns are bitwise those of the single-column product
+    for t in sorted(set([0, 1, 31, 32, T // 2, T - 1])):
+        if t < T:
+            y1 = _host(bqm.mmvq_tq1_0(w, a[t:t + 1].clone(), N, K, 1))
+            assert np.array_equal(y1[0].view(np.uint32), y[t].view(np.uint32)), t
+
+
+def test_mm_prefill_workload(bqm):
+    """The ffn matrix against 512 columns (a prefill batch), sampled columns
+    against the oracle."""
+    wl = synth.WORKLOADS["ffn"]
+    inp = synth.make_inputs(wl, T=512)
+    N, K, T = wl.N, wl.K, 512
+    w, a, w_ref, a_ref = _prep(bqm, inp.trits, inp.d16, inp.x)
+    _say("mm prefill", N, K, T)
+    y = _host(bqm.mm_tq1_0(w, a, N, K, T))
+    for t in (0, 255, 511):
+        _, y64, ab = oracle.mmvq(w_ref, a_ref[t:t + 1], N, K, 1)
+        _assert_close(y[t:t + 1], y64, ab, "prefill column %d" % t)
+
+
+# ---------------------------------------------------------------------------
 # Fused quantize-and-multiply: bitwise the two-call path, within tolerance of
 # the oracle
 # ---------------------------------------------------------------------------
