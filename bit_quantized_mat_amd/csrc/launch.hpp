@@ -81,6 +81,11 @@ int launch_mmvq(const void *w, const void *a, float *y, int32_t *isums, int64_t 
                 int32_t T, hipStream_t stream);
 int launch_mm(const void *w, const void *a, float *y, int64_t N, int64_t K, int64_t T,
               hipStream_t stream);
+// K-streaming matrix-core kernel for many columns (any K and T): its grid
+// size for a call, and its launcher.
+int64_t mm_stream_workgroups(int64_t N, int64_t T);
+int launch_mm_stream(const void *w, const void *a, float *y, int64_t N, int64_t K, int64_t T,
+                     hipStream_t stream);
 // per_slot: a holds one Q8_1 column per (token, slot) pair instead of one
 // per token.
 int launch_mmvq_id(const void *w, const void *a, const int32_t *ids, float *y, int64_t E,

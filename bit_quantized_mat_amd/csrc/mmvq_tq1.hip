@@ -214,25 +214,21 @@ int launch_mmvq(const void *w, const void *a, float *y, int32_t *isums, int64_t 
     return launch_mmvq_mfma(w, a, y, isums, N, K, T, stream);
 }
 
-// Many-column product: up to BQM_MMVQ_MAX_COLS columns the plain product;
-// beyond, the resident matrix-core kernel over column chunks in one launch
-// where a chunk's columns fit LDS, else successive calls of the plain product
-// on BQM_MMVQ_MAX_COLS columns each (all on the caller's stream, in order).
+// Many-column product: up to BQM_MMVQ_MAX_COLS columns the plain product.
+// Beyond, the K-streaming kernel (mm_stream.hip) once its grid gives the
+// device at least 1.5 workgroups per compute unit: each of its workgroups
+// walks all of K, so with fewer of them that walk is exposed, and the
+// resident kernel over column chunks (whose columns must fit LDS) is faster
+// (4096 x 4096 at 64 columns: 18.6 against 45 us; 14336 x 4096 at 128
+// columns: 75 against 64 us, at 512: 277 against 170 us).
 int launch_mm(const void *w, const void *a, float *y, int64_t N, int64_t K, int64_t T,
               hipStream_t stream)
 {
     if (T <= BQM_MMVQ_MAX_COLS)
         return launch_mmvq(w, a, y, nullptr, N, K, (int32_t)T, stream);
-    if (mm_chunked_supported(K))
+    if (2 * mm_stream_workgroups(N, T) < 3ll * compute_units() && mm_chunked_supported(K))
         return launch_mm_chunked(w, a, y, N, K, T, stream);
-    const uint64_t col_bytes = (uint64_t)(K / kQ81BlockElems) * kQ81BlockBytes;
-    for (int64_t c0 = 0; c0 < T; c0 += BQM_MMVQ_MAX_COLS) {
-        const int32_t n = (int32_t)(T - c0 < BQM_MMVQ_MAX_COLS ? T - c0 : BQM_MMVQ_MAX_COLS);
-        if (int rc = launch_mmvq(w, static_cast<const uint8_t *>(a) + c0 * col_bytes, y + c0 * N,
-                                 nullptr, N, K, n, stream))
-            return rc;
-    }
-    return BQM_OK;
+    return launch_mm_stream(w, a, y, N, K, T, stream);
 }
 
 // ---------------------------------------------------------------------------

@@ -115,9 +115,13 @@ BQM_API int mmvq_tq1_0(const void *w, const void *a, float *y,
  * the per-32-element chunk contract", "Measured impact"): the same
  *   y[t][n] = sum_j fp32(d_w[n][j/8]) * fp32(d_a[t][j]) * isum[t][n][j]
  * as mmvq_tq1_0, for 1 <= T <= BQM_MM_MAX_COLS columns, the T columns of a
- * below 4 GiB. Every output is bitwise the one mmvq_tq1_0 gives for its
- * column (up to 32 columns the call is mmvq_tq1_0). Other shapes, alignment,
- * ownership and errors as mmvq_tq1_0. */
+ * below 4 GiB. Up to 32 columns the call is mmvq_tq1_0. Beyond, the fp32 sums
+ * of large calls run over K in order (folded every 64 blocks), so outputs
+ * differ from the exact sum by at most about (73 + K/16384) * 2^-24 of
+ * sum |terms| (below 1e-5 for K up to 2^20); smaller calls keep the plain
+ * product's order. Either way the result is within that bound, and not
+ * necessarily bitwise mmvq_tq1_0's. Other shapes, alignment, ownership and
+ * errors as mmvq_tq1_0. */
 BQM_API int mm_tq1_0(const void *w, const void *a, float *y,
              int64_t N, int64_t K, int64_t T, void *stream);
 

@@ -417,11 +417,12 @@ def test_workload_moe_slots_parity(bqm):
 # ---------------------------------------------------------------------------
 
 @pytest.mark.parametrize("N,K,T", [
-    (300, 4096, 100),   # chunks of 32 columns, a ragged last chunk
-    (67, 2304, 40),     # chunks of 32, rows of 9 blocks
-    (130, 6144, 70),    # 32-column chunks do not fit LDS: chunks of 16
-    (40, 16384, 50),    # no chunk fits: successive 32-column products
-    (33, 256, 33),      # one-block rows: successive 32-column products
+    (300, 4096, 100),   # column chunks of 32 on the resident kernel, a ragged last one
+    (67, 2304, 40),     # rows of 9 blocks
+    (130, 6144, 170),   # chunks of 16 (32 do not fit LDS)
+    (40, 16384, 50),    # no chunk fits: the K-streaming kernel, one fold (64 blocks)
+    (21, 33024, 33),    # K-streaming, 129 blocks: two folds and a tail
+    (33, 256, 33),      # one-block rows: K-streaming
     (515, 4096, 32),    # up to 32 columns: the plain product
 ])
 def test_mm_parity(bqm, N, K, T):
@@ -431,11 +432,27 @@ def test_mm_parity(bqm, N, K, T):
     y = _host(bqm.mm_tq1_0(w, a, N, K, T))
     _, y64, ab = oracle.mmvq(w_ref, a_ref, N, K, T)
     _assert_close(y, y64, ab, "mm N=%d K=%d T=%d" % (N, K, T))
-    # columns are bitwise those of the single-column product
-    for t in sorted(set([0, 1, 31, 32, T // 2, T - 1])):
-        if t < T:
+    if T <= 32:
+        # the plain product: columns bitwise the single-column calls'
+        for t in sorted(set([0, T // 2, T - 1])):
             y1 = _host(bqm.mmvq_tq1_0(w, a[t:t + 1].clone(), N, K, 1))
             assert np.array_equal(y1[0].view(np.uint32), y[t].view(np.uint32)), t
+
+
+def test_mm_stream_kernel(bqm):
+    """A call large enough for the K-streaming kernel (96 row groups x 4
+    column groups): sampled columns against the oracle, and each column's bits
+    independent of the other columns (a wider call on the same kernel)."""
+    N, K, T = 6144, 1024, 256
+    trits, d16, x = _case(N, K, T + 64, seed=7700)
+    w, a, w_ref, a_ref = _prep(bqm, trits, d16, x)
+    _say("mm stream", N, K, T)
+    y = _host(bqm.mm_tq1_0(w, a[:T].contiguous(), N, K, T))
+    for t in (0, 63, 64, 200, 255):
+        _, y64, ab = oracle.mmvq(w_ref, a_ref[t:t + 1], N, K, 1)
+        _assert_close(y[t:t + 1], y64, ab, "stream column %d" % t)
+    y2 = _host(bqm.mm_tq1_0(w, a, N, K, T + 64))
+    assert np.array_equal(y2[:T].view(np.uint32), y.view(np.uint32))
 
 
 def test_mm_prefill_workload(bqm):
