@@ -68,27 +68,33 @@ __global__ __launch_bounds__(256) void mm_stream_kernel(const uint8_t *__restric
             outer[ct][i] = 0.0f;
         }
 
-    LaneBlock lb = load_lane_block(rw, row_off, kg);
-    for (int B = 0; B < nb; B++) {
-        // this block's activations: task i = column (i >> 3), sub-block (i & 7);
-        // columns past T load at the idle offset (zeros) and stage zeros
-        u32x4 v0[kMmAhead], v1[kMmAhead];
-        uint32_t ds[kMmAhead];
+    // block B's activations for this workgroup's columns: task i = column
+    // (i >> 3), sub-block (i & 7); columns past T load at the idle offset
+    // (zeros) and stage zeros
+    u32x4 v0[kMmAhead], v1[kMmAhead];
+    uint32_t ds[kMmAhead];
+    // (B = nb: every lane loads at the idle offset, so that the loads are
+    // issued unconditionally and the compiler can count them)
+    auto issue_stage = [&](int B) {
 #pragma unroll
         for (int k = 0; k < kMmAhead; k++) {
             const int i = k * 256 + tid;
             const int c = c0 + (i >> 3), b = i & 7;
-            const uint32_t off = c < T ? (uint32_t)c * col_bytes +
-                                             (uint32_t)(8 * B + b) * kQ81BlockBytes
-                                       : kIdleLoadOffset;
+            const uint32_t off = c < T && B < nb ? (uint32_t)c * col_bytes +
+                                                       (uint32_t)(8 * B + b) * kQ81BlockBytes
+                                                 : kIdleLoadOffset;
             v0[k] = ld_b128(ra, off);
             v1[k] = ld_b128(ra, off + 16);
             ds[k] = ld_b32(ra, off + 32);
         }
-        // the next block's weights, in flight during this block
-        LaneBlock ln;
-        if (B + 1 < nb)
-            ln = load_lane_block(rw, row_off + (uint32_t)(B + 1) * kTq1BlockBytes, kg);
+    };
+    // the loads of block B + 1 (activations, then weights) are in flight
+    // while block B is multiplied
+    issue_stage(0);
+    LaneBlock lb = load_lane_block(rw, row_off, kg);
+    for (int B = 0; B < nb; B++) {
+        const LaneBlock ln = load_lane_block(
+            rw, B + 1 < nb ? row_off + (uint32_t)(B + 1) * kTq1BlockBytes : kIdleLoadOffset, kg);
         if (B > 0)
             __syncthreads();  // every wave is done with the previous block
 #pragma unroll
@@ -107,6 +113,7 @@ __global__ __launch_bounds__(256) void mm_stream_kernel(const uint8_t *__restric
             }
             reinterpret_cast<uint16_t *>(dah + c * 4)[b] = (uint16_t)ds[k];
         }
+        issue_stage(B + 1);
         __syncthreads();
 
         const TileOperands op = decode_lane_block(lb, kg);
