@@ -33,13 +33,11 @@ constexpr int kFoldBlocks = 64;
 constexpr int kMmBqDwords = kMmCols * 8 * 128;
 constexpr int kMmDahDwords = kMmCols * 16 * 4;
 
-__global__ __launch_bounds__(256) void mm_stream_kernel(const uint8_t *__restrict__ w,
-                                                        const uint8_t *__restrict__ a,
-                                                        float *__restrict__ y, int64_t N, int nb,
-                                                        int T, int ncolgroups)
+// One 64-row group of a workgroup against its columns c0 .. c0 + 16 kMmCols - 1.
+__device__ __forceinline__ void row_group(__amdgpu_buffer_rsrc_t rw, __amdgpu_buffer_rsrc_t ra,
+                                          float *__restrict__ y, int64_t N, int nb, int T, int c0,
+                                          int64_t rgroup, uint32_t *bq, uint32_t *dah)
 {
-    __shared__ uint32_t bq[kMmBqDwords];
-    __shared__ uint32_t dah[kMmDahDwords];
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lane = tid & 63;
@@ -47,14 +45,6 @@ __global__ __launch_bounds__(256) void mm_stream_kernel(const uint8_t *__restric
     const int col = lane & 15, rg = lane >> 4;  // output lane: column col, rows 4rg..4rg+3
     const int nblk = nb * 8;
     const uint32_t col_bytes = (uint32_t)nblk * kQ81BlockBytes;
-    // workgroups of one row group are adjacent, so the L2 serves the weights
-    // of the row group's column groups from one HBM read
-    const int rgroup = (int)(blockIdx.x / ncolgroups);
-    const int cgroup = (int)(blockIdx.x - (unsigned)rgroup * ncolgroups);
-    const int c0 = cgroup * 16 * kMmCols;
-    const __amdgpu_buffer_rsrc_t rw = make_rsrc(w, (uint64_t)N * nb * kTq1BlockBytes);
-    const __amdgpu_buffer_rsrc_t ra = make_rsrc(a, (uint64_t)T * col_bytes);
-
     // this decode lane's row (rows past N read row 0 and store nothing)
     const int64_t rowA = ((int64_t)rgroup * 4 + wave) * 16 + (lane & 15);
     const uint32_t row_off = (uint32_t)((rowA < N ? rowA : 0) * nb * kTq1BlockBytes);
@@ -166,6 +156,28 @@ __global__ __launch_bounds__(256) void mm_stream_kernel(const uint8_t *__restric
     }
 }
 
+// grid.x: column groups of 16 kMmCols columns; grid.y and grid.z: 64-row
+// groups, row group blockIdx.z gridDim.y + blockIdx.y (grid.y stays within
+// 65535; the few workgroups past the last row group exit at once).
+// Workgroups of one row group are adjacent in dispatch order, so the L2
+// serves the row group's weights to its column groups from one HBM read.
+__global__ __launch_bounds__(256) void mm_stream_kernel(const uint8_t *__restrict__ w,
+                                                        const uint8_t *__restrict__ a,
+                                                        float *__restrict__ y, int64_t N, int nb,
+                                                        int T, int64_t nrowgroups)
+{
+    __shared__ uint32_t bq[kMmBqDwords];
+    __shared__ uint32_t dah[kMmDahDwords];
+    const int64_t rgroup = (int64_t)blockIdx.z * gridDim.y + blockIdx.y;
+    if (rgroup >= nrowgroups)
+        return;
+    const uint32_t col_bytes = (uint32_t)nb * 8 * kQ81BlockBytes;
+    const int c0 = (int)blockIdx.x * 16 * kMmCols;
+    const __amdgpu_buffer_rsrc_t rw = make_rsrc(w, (uint64_t)N * nb * kTq1BlockBytes);
+    const __amdgpu_buffer_rsrc_t ra = make_rsrc(a, (uint64_t)T * col_bytes);
+    row_group(rw, ra, y, N, nb, T, c0, rgroup, bq, dah);
+}
+
 int64_t mm_stream_workgroups(int64_t N, int64_t T)
 {
     return (N + 63) / 64 * ((T + 16 * kMmCols - 1) / (16 * kMmCols));
@@ -177,9 +189,11 @@ int launch_mm_stream(const void *w, const void *a, float *y, int64_t N, int64_t 
     const int nb = (int)(K / kTq1BlockElems);
     const int64_t nrowgroups = (N + 63) / 64;
     const int64_t ncolgroups = (T + 16 * kMmCols - 1) / (16 * kMmCols);
-    hipLaunchKernelGGL(mm_stream_kernel, dim3((unsigned)(nrowgroups * ncolgroups)), dim3(256), 0,
-                       stream, static_cast<const uint8_t *>(w), static_cast<const uint8_t *>(a),
-                       y, N, nb, (int)T, (int)ncolgroups);
+    const int64_t gy = nrowgroups < 65535 ? nrowgroups : 65535;
+    const dim3 grid((unsigned)ncolgroups, (unsigned)gy, (unsigned)((nrowgroups + gy - 1) / gy));
+    hipLaunchKernelGGL(mm_stream_kernel, grid, dim3(256), 0, stream,
+                       static_cast<const uint8_t *>(w), static_cast<const uint8_t *>(a), y, N,
+                       nb, (int)T, nrowgroups);
     return check_launch();
 }
 
