@@ -29,25 +29,25 @@ namespace bqm {
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 
 // This lane's share of one 54-byte block (see the layout above): qs dwords
-// 2kg and 2kg+1, qs dword 8+kg, the qh dword and the fp16 scale, read as the
-// aligned dwords that cover them and realigned (odd blocks of a row start two
-// bytes past a dword boundary).
+// 2kg and 2kg+1, qs dword 8+kg, the qh dword and the fp16 scale, held as the
+// aligned dwords that cover them plus the block's byte shift (odd blocks of a
+// row start two bytes past a dword boundary). The realignment waits for
+// decode_lane_block, so a block loaded ahead stays in flight until it is used.
 struct LaneBlock {
-    uint32_t lo0, lo1, hi, qh, dbits;
+    u32x3 l;      // qs dwords 2kg, 2kg+1
+    u32x2 h;      // qs dword 8+kg
+    u32x2 t;      // the qh dword and d
+    uint32_t sh;  // byte shift, 0 or 2
 };
 
 __device__ __forceinline__ LaneBlock load_lane_block(__amdgpu_buffer_rsrc_t rw, uint32_t off, int kg)
 {
-    const uint32_t sh = off & 3u, base = off - sh;
-    const u32x3 l = __builtin_amdgcn_raw_buffer_load_b96(rw, base + 8 * kg, 0, 0);
-    const u32x2 h = ld_b64(rw, base + 32 + 4 * kg);
-    const u32x2 t = ld_b64(rw, base + 48);
     LaneBlock b;
-    b.lo0 = align_bytes(l.y, l.x, sh);
-    b.lo1 = align_bytes(l.z, l.y, sh);
-    b.hi = align_bytes(h.y, h.x, sh);
-    b.qh = align_bytes(t.y, t.x, sh);
-    b.dbits = sh ? (t.y >> 16) : (t.y & 0xffffu);
+    b.sh = off & 3u;
+    const uint32_t base = off - b.sh;
+    b.l = __builtin_amdgcn_raw_buffer_load_b96(rw, base + 8 * kg, 0, 0);
+    b.h = ld_b64(rw, base + 32 + 4 * kg);
+    b.t = ld_b64(rw, base + 48);
     return b;
 }
 
@@ -58,13 +58,13 @@ struct TileOperands {
     float dw;
 };
 
-__device__ __forceinline__ TileOperands decode_lane_block(const LaneBlock &lb, int kg)
+// qm: the lane's multipliers for qh digit kg (qh_lane_muls(kg)).
+__device__ __forceinline__ TileOperands decode_lane_block(const LaneBlock &lb, QhLaneMuls qm)
 {
-    const QsDigits lo0 = qs_digits<true>(lb.lo0);
-    const QsDigits lo1 = qs_digits<true>(lb.lo1);
-    const QsDigits hi = qs_digits<true>(lb.hi);
-    const QhDigits qh = qh_digits<true>(lb.qh);
-    const uint32_t qhk = kg == 0 ? qh.U[0] : kg == 1 ? qh.U[1] : kg == 2 ? qh.U[2] : qh.U[3];
+    const QsDigits lo0 = qs_digits<true>(align_bytes(lb.l.y, lb.l.x, lb.sh));
+    const QsDigits lo1 = qs_digits<true>(align_bytes(lb.l.z, lb.l.y, lb.sh));
+    const QsDigits hi = qs_digits<true>(align_bytes(lb.h.y, lb.h.x, lb.sh));
+    const uint32_t qhk = qh_digit_lane(align_bytes(lb.t.y, lb.t.x, lb.sh), qm);
     TileOperands t;
 #pragma unroll
     for (int c = 0; c < 5; c++)
@@ -72,7 +72,7 @@ __device__ __forceinline__ TileOperands decode_lane_block(const LaneBlock &lb, i
     t.A[5] = (long)(((uint64_t)hi.U[1] << 32) | hi.U[0]);
     t.A[6] = (long)(((uint64_t)hi.U[3] << 32) | hi.U[2]);
     t.A[7] = (long)(((uint64_t)qhk << 32) | hi.U[4]);
-    t.dw = f16_bits_to_f32(lb.dbits);
+    t.dw = f16_bits_to_f32(lb.sh ? (lb.t.y >> 16) : (lb.t.y & 0xffffu));
     return t;
 }
 

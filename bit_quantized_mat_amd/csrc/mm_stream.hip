@@ -42,6 +42,7 @@ __device__ __forceinline__ void row_group(__amdgpu_buffer_rsrc_t rw, __amdgpu_bu
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lane = tid & 63;
     const int kg = lane >> 4;                   // decode lane: row lane % 16, K group kg
+    const QhLaneMuls qm = qh_lane_muls(kg);
     const int col = lane & 15, rg = lane >> 4;  // output lane: column col, rows 4rg..4rg+3
     const int nblk = nb * 8;
     const uint32_t col_bytes = (uint32_t)nblk * kQ81BlockBytes;
@@ -106,7 +107,7 @@ __device__ __forceinline__ void row_group(__amdgpu_buffer_rsrc_t rw, __amdgpu_bu
         issue_stage(B + 1);
         __syncthreads();
 
-        const TileOperands op = decode_lane_block(lb, kg);
+        const TileOperands op = decode_lane_block(lb, qm);
         float dw[4];  // block scales of the four rows this output lane holds
 #pragma unroll
         for (int i = 0; i < 4; i++)
@@ -161,10 +162,13 @@ __device__ __forceinline__ void row_group(__amdgpu_buffer_rsrc_t rw, __amdgpu_bu
 // 65535; the few workgroups past the last row group exit at once).
 // Workgroups of one row group are adjacent in dispatch order, so the L2
 // serves the row group's weights to its column groups from one HBM read.
-__global__ __launch_bounds__(256) void mm_stream_kernel(const uint8_t *__restrict__ w,
-                                                        const uint8_t *__restrict__ a,
-                                                        float *__restrict__ y, int64_t N, int nb,
-                                                        int T, int64_t nrowgroups)
+// Three waves per SIMD rather than four: at the 128 registers of four, the
+// compiler funnels every matrix-core product through one or two accumulator
+// quads and serializes them; with room for about 133 each sub-block's
+// products get registers of their own.
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void mm_stream_kernel(
+    const uint8_t *__restrict__ w, const uint8_t *__restrict__ a, float *__restrict__ y, int64_t N,
+    int nb, int T, int64_t nrowgroups)
 {
     __shared__ uint32_t bq[kMmBqDwords];
     __shared__ uint32_t dah[kMmDahDwords];

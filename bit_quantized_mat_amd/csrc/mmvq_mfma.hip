@@ -111,6 +111,7 @@ __global__ __launch_bounds__(512) void mmvq_mfma_kernel(const uint8_t *__restric
     const int lane = threadIdx.x & 63;
     const int Lr = 1 << lr_log2;
     const int kg = lane >> 4;                   // decode lane: row lane % 16, K group kg
+    const QhLaneMuls qm = qh_lane_muls(kg);
     const int col = lane & 15, rg = lane >> 4;  // output lane: column col, rows 4rg..4rg+3
     const int nblk = nb * 8;
     const uint32_t col_bytes = (uint32_t)nblk * kQ81BlockBytes;
@@ -171,15 +172,20 @@ __global__ __launch_bounds__(512) void mmvq_mfma_kernel(const uint8_t *__restric
                 const bool same_tile = B + Lr < nb || (gi + 1 < GPW && g + nw < nb);
                 const int Bn = B + Lr < nb ? B + Lr : (same_tile ? g + nw : wave);
                 const bool have_next = same_tile || next_tile < ntiles;
+                // the weights are loaded by every lane (at kIdleLoadOffset
+                // when there is no next block), so that their data is first
+                // waited for where it is decoded
                 LaneBlock ln[R];
-                if (have_next) {
 #pragma unroll
-                    for (int rt = 0; rt < R; rt++)
-                        ln[rt] = load_lane_block(
-                            rw, (same_tile ? row_off[rt] : next_off[rt]) + (uint32_t)Bn * kTq1BlockBytes,
-                            kg);
+                for (int rt = 0; rt < R; rt++)
+                    ln[rt] = load_lane_block(
+                        rw,
+                        have_next ? (same_tile ? row_off[rt] : next_off[rt]) +
+                                        (uint32_t)Bn * kTq1BlockBytes
+                                  : kIdleLoadOffset,
+                        kg);
+                if (have_next)
                     pieces.issue(ra, smap, col_bytes, Bn);
-                }
 
                 // one row tile at a time: its digit operands meet every
                 // sub-block and column tile of the staged activations (re-read
@@ -187,7 +193,7 @@ __global__ __launch_bounds__(512) void mmvq_mfma_kernel(const uint8_t *__restric
                 // registers)
 #pragma unroll
                 for (int rt = 0; rt < R; rt++) {
-                    const TileOperands op = decode_lane_block(lb[rt], kg);
+                    const TileOperands op = decode_lane_block(lb[rt], qm);
                     float dw[4];  // block scales of the four rows this output lane holds
 #pragma unroll
                     for (int i = 0; i < 4; i++)
@@ -237,10 +243,10 @@ __global__ __launch_bounds__(512) void mmvq_mfma_kernel(const uint8_t *__restric
                     wave_lds_order();  // this block's operand reads come first
                     pieces.land(stage, smap);
                     wave_lds_order();
-#pragma unroll
-                    for (int rt = 0; rt < R; rt++)
-                        lb[rt] = ln[rt];
                 }
+#pragma unroll
+                for (int rt = 0; rt < R; rt++)
+                    lb[rt] = ln[rt];
             }
         }
 

@@ -117,6 +117,7 @@ __global__ __launch_bounds__(64 * NW) void mmvq_mfma_res_kernel(const uint8_t *_
     const int lane = threadIdx.x & 63;
     constexpr int Lr = NW * GPW;
     const int kg = lane >> 4;                   // decode lane: row lane % 16, K group kg
+    const QhLaneMuls qm = qh_lane_muls(kg);
     const int col = lane & 15, rg = lane >> 4;  // output lane: column col, rows 4rg..4rg+3
     const int nblk = nb * 8;
     const uint64_t w_bytes = (uint64_t)N * nb * kTq1BlockBytes;
@@ -225,17 +226,21 @@ __global__ __launch_bounds__(64 * NW) void mmvq_mfma_res_kernel(const uint8_t *_
                 const bool same_tile = B + Lr < nb || (gi + 1 < GPW && g + NW < nb);
                 const int Bn = B + Lr < nb ? B + Lr : (same_tile ? g + NW : wave);
                 const bool have_next = same_tile || next_here;
+                // issued by every lane (at kIdleLoadOffset when there is no
+                // next block), so that the compiler can count the loads in
+                // flight and the data is first waited for where it is decoded
                 LaneBlock ln[R];
-                if (have_next) {
 #pragma unroll
-                    for (int rt = 0; rt < R; rt++)
-                        ln[rt] = load_lane_block(
-                            rw, (same_tile ? row_off[rt] : next_off[rt]) + (uint32_t)Bn * kTq1BlockBytes,
-                            kg);
-                }
+                for (int rt = 0; rt < R; rt++)
+                    ln[rt] = load_lane_block(
+                        rw,
+                        have_next ? (same_tile ? row_off[rt] : next_off[rt]) +
+                                        (uint32_t)Bn * kTq1BlockBytes
+                                  : kIdleLoadOffset,
+                        kg);
 #pragma unroll
                 for (int rt = 0; rt < R; rt++) {
-                    const TileOperands op = decode_lane_block(lb[rt], kg);
+                    const TileOperands op = decode_lane_block(lb[rt], qm);
                     float dw[4];  // block scales of the four rows this output lane holds
 #pragma unroll
                     for (int i = 0; i < 4; i++)
@@ -280,11 +285,9 @@ __global__ __launch_bounds__(64 * NW) void mmvq_mfma_res_kernel(const uint8_t *_
                         }
                     }
                 }
-                if (have_next) {
 #pragma unroll
-                    for (int rt = 0; rt < R; rt++)
-                        lb[rt] = ln[rt];
-                }
+                for (int rt = 0; rt < R; rt++)
+                    lb[rt] = ln[rt];
             }
         }
 

@@ -212,6 +212,41 @@ __device__ __forceinline__ QhDigits qh_digits(uint32_t w)
     return d;
 }
 
+// Digit c of each byte of a qh dword, for a digit index that differs from
+// lane to lane. F_m = floor(v / 3^m) is byte 1 of X1 3^(3-m) in each 16-bit
+// lane (X1 as in qh_floors: X1 / 256 lies in [v/27, (v+1)/27), so X1 3^(3-m)
+// / 256 lies in [v/3^m, (v+1)/3^m), which holds no integer above
+// floor(v/3^m); and X1 27 < 2^16). With the lane's multipliers 3^(3-c) and
+// 3^(2-c) (0 for c = 3) on both 16-bit lanes, the digit is F_c - 3 F_(c+1).
+struct QhLaneMuls {
+    uint32_t cur, next;
+};
+
+__device__ __forceinline__ QhLaneMuls qh_lane_muls(int c)
+{
+    const uint32_t m = c == 0 ? 27u : c == 1 ? 9u : c == 2 ? 3u : 1u;
+    const uint32_t n = m / 3u;  // 0 for c = 3
+    return {m * 0x00010001u, n * 0x00010001u};
+}
+
+// x * y on each 16-bit lane (v_pk_mul_lo_u16; no lane exceeds 16 bits here).
+__device__ __forceinline__ uint32_t pk_mul_lanes(uint32_t x, uint32_t y)
+{
+    const u16x2 a = __builtin_bit_cast(u16x2, x), b = __builtin_bit_cast(u16x2, y);
+    return __builtin_bit_cast(uint32_t, (u16x2)(a * b));
+}
+
+__device__ __forceinline__ uint32_t qh_digit_lane(uint32_t w, QhLaneMuls m)
+{
+    const uint32_t e = w & kLaneMask;
+    const uint32_t o = __builtin_amdgcn_perm(0u, w, 0x0c030c01u);
+    const uint32_t e1 = pk_shr(__umul24(e, kQhMul) + kQhAdd, kQhShift);
+    const uint32_t o1 = pk_shr(__umul24(o, kQhMul) + kQhAdd, kQhShift);
+    const uint32_t fc = hi_bytes(pk_mul_lanes(o1, m.cur), pk_mul_lanes(e1, m.cur));
+    const uint32_t fn = hi_bytes(pk_mul_lanes(o1, m.next), pk_mul_lanes(e1, m.next));
+    return minus3<true>(fc, fn);
+}
+
 // Packed signed trits t = u - 1 (bytes 0xff, 0x00, 0x01) from a floor pair:
 // t = F_c - 3 F_(c+1) - 1 per byte. Offsetting every byte by 0x80 first keeps
 // the subtraction free of borrows; the final xor removes the offset.

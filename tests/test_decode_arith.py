@@ -59,6 +59,31 @@ def test_qh_digit_chain_exhaustive():
         assert (x4 >> 8) & 0xFF == v % 3, v
 
 
+def _qh_lane_multipliers():
+    """The per-lane multipliers 3^(3-c) of qh_lane_muls, read from the header."""
+    text = open(HDR).read()
+    m = re.search(r"c == 0 \? (\d+)u : c == 1 \? (\d+)u : c == 2 \? (\d+)u : (\d+)u", text)
+    assert m, "qh_lane_muls"
+    return [int(g) for g in m.groups()]
+
+
+def test_qh_lane_digit_exhaustive():
+    # qh_digit_lane: digit c of a qh byte from F_c - 3 F_(c+1), where F_m is
+    # byte 1 of X1 * 3^(3-m) and the next multiplier is the current one / 3
+    # (0 for c = 3)
+    muls = _qh_lane_multipliers()
+    assert muls == [27, 9, 3, 1]
+    for v in range(81):
+        (x1,) = _lane_chain(v, C["kQhMul"], C["kQhAdd"], C["kQhShift"], ())
+        for c in range(4):
+            cur, nxt = muls[c], muls[c] // 3
+            assert x1 * cur <= M16 and x1 * nxt <= M16
+            fc = ((x1 * cur) >> 8) & 0xFF
+            fn = ((x1 * nxt) >> 8) & 0xFF
+            assert fc == v // 3 ** c and fn == (v // 3 ** (c + 1) if c < 3 else 0), (v, c)
+            assert 3 * fn <= fc and fc - 3 * fn == (v // 3 ** c) % 3, (v, c)
+
+
 def test_two_lanes_share_a_register_without_crosstalk():
     # the first step is one 24-bit multiply-add on bytes 0 and 2 of a dword
     rng = np.random.default_rng(0)
