@@ -41,18 +41,62 @@ inline size_t res_lds_bytes(int NW, int NT, int R, int nb, bool db, bool id = fa
             (id ? 32 * NT : 0)) * 4;
 }
 
-// Copy all T activation columns into bq / dah: one Q8_1 block per item,
-// consecutive threads on consecutive columns. Column c's Q8_1 row starts at
-// byte c * nb * 8 * 36 of ra, or, for expert items (ID), at byte colbase[c]
-// (an LDS table). Columns T .. 16 NT - 1 are left as they are: they only feed
-// output columns that are never stored.
-template <int NT, bool ID>
+// Store one staged Q8_1 block (block j of column c, its 36 bytes in v0, v1,
+// ds) as B operands in bq and its fp16 scale in dah.
+template <int NT>
+__device__ __forceinline__ void stage_block(uint32_t *__restrict__ bq, uint32_t *__restrict__ dah,
+                                            int nb, int c, int j, const u32x4 &v0, const u32x4 &v1,
+                                            uint32_t ds)
+{
+    const int ct = c >> 4, cc = c & 15;
+    const int B = j >> 3, b = j & 7;
+    const uint32_t q[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+    uint32_t *dst = bq + ((size_t)(ct * nb + B) * 8 + b) * 128;
+#pragma unroll
+    for (int kg = 0; kg < 4; kg++) {
+        const uint32_t lo = b < 5 ? q[2 * kg] : q[kg];
+        const uint32_t hi = b < 5 ? q[2 * kg + 1] : q[4 + kg];
+        *reinterpret_cast<u32x2 *>(dst + 2 * (16 * kg + cc)) = (u32x2){lo, hi};
+    }
+    reinterpret_cast<uint16_t *>(dah + ((size_t)B * 16 * NT + c) * 4)[b] = (uint16_t)ds;
+}
+
+// Copy all T activation columns into bq / dah, one Q8_1 block per thread and
+// step. Column c's Q8_1 row starts at byte c * nb * 8 * 36 of ra, or, for
+// expert items (ID), at byte colbase[c] (an LDS table). With RUNS (plain
+// products and column chunks) above 8 columns, lane l of a wave takes
+// column 8 g + (l & 7) and blocks (l >> 3) + (blockDim / 8) i: each load of a
+// wave reads 8 runs of 8 consecutive blocks (288 bytes each) instead of 64
+// blocks of 64 different columns, and the 8 lanes of one block store 8
+// consecutive operand slots. Otherwise (few columns, or an expert item's
+// 5 to 16 gathered columns) consecutive threads take consecutive columns of
+// one block, which keeps every lane busy when T is not a multiple of 8.
+// Columns T .. 16 NT - 1 are left as they are: they only feed output columns
+// that are never stored.
+template <int NT, bool ID, bool RUNS>
 __device__ __forceinline__ void stage_all_columns(uint32_t *__restrict__ bq,
                                                   uint32_t *__restrict__ dah,
                                                   __amdgpu_buffer_rsrc_t ra, int T, int nb,
                                                   const uint32_t *colbase)
 {
     const int nblk = nb * 8;
+    if (RUNS && T > 8) {
+        const int cl = threadIdx.x & 7, jl = (int)threadIdx.x >> 3;
+        const int jstep = (int)blockDim.x >> 3;
+        for (int c0 = 0; c0 < T; c0 += 8) {
+            const int c = c0 + cl;
+            if (c >= T)
+                continue;
+            const uint32_t cbase = ID ? colbase[c] : (uint32_t)c * nblk * kQ81BlockBytes;
+            for (int j = jl; j < nblk; j += jstep) {
+                const uint32_t off = cbase + (uint32_t)j * kQ81BlockBytes;
+                const u32x4 v0 = ld_b128(ra, off);
+                const u32x4 v1 = ld_b128(ra, off + 16);
+                stage_block<NT>(bq, dah, nb, c, j, v0, v1, ld_b32(ra, off + 32));
+            }
+        }
+        return;
+    }
     const int items = T * nblk;
     for (int it = threadIdx.x; it < items; it += blockDim.x) {
         const int j = it / T, c = it - j * T;
@@ -92,9 +136,10 @@ struct WideItems {
 // sums double-buffered; ISUMS: write the exact per-sub-block sums instead of
 // outputs; ID: item mode, work items of up to 16 NT columns (an expert's
 // matrix against its pairs' columns, outputs y[pair][row]; or a chunk of the
-// columns of a many-column product); `a_cols` is the number of columns a
-// holds (T in the plain mode).
-template <int NW, int GPW, int NT, int R, bool DB, bool ISUMS, bool ID>
+// columns of a many-column product); RUNS: columns copied in runs of blocks
+// (stage_all_columns; plain products and column chunks, not expert items);
+// `a_cols` is the number of columns a holds (T in the plain mode).
+template <int NW, int GPW, int NT, int R, bool DB, bool ISUMS, bool ID, bool RUNS>
 __global__ __launch_bounds__(64 * NW) void mmvq_mfma_res_kernel(const uint8_t *__restrict__ w,
                                                                 const uint8_t *__restrict__ a,
                                                                 float *__restrict__ y,
@@ -190,7 +235,7 @@ __global__ __launch_bounds__(64 * NW) void mmvq_mfma_res_kernel(const uint8_t *_
         }
         if (ID)
             __syncthreads();  // the column tables
-        stage_all_columns<NT, ID>(bq, dah, ra, T, nb, colbase);
+        stage_all_columns<NT, ID, RUNS>(bq, dah, ra, T, nb, colbase);
         __syncthreads();
     };
     start_item();
@@ -394,20 +439,20 @@ static int launch_res(const uint8_t *w, const uint8_t *a, float *y, int32_t *isu
     const int64_t ntiles = (N + 16 * R - 1) / (16 * R);
     const size_t lds = res_lds_bytes(NW, NT, R, nb, DB);
     const void *kt =
-        reinterpret_cast<const void *>(&mmvq_mfma_res_kernel<NW, GPW, NT, R, DB, true, false>);
+        reinterpret_cast<const void *>(&mmvq_mfma_res_kernel<NW, GPW, NT, R, DB, true, false, true>);
     const void *kf =
-        reinterpret_cast<const void *>(&mmvq_mfma_res_kernel<NW, GPW, NT, R, DB, false, false>);
+        reinterpret_cast<const void *>(&mmvq_mfma_res_kernel<NW, GPW, NT, R, DB, false, false, true>);
     allow_dynamic_lds(kt, lds);
     allow_dynamic_lds(kf, lds);
     const int cap = resident_workgroups(isums ? kt : kf, 64 * NW, lds);
     const dim3 grid((unsigned)(ntiles < cap ? ntiles : cap));
     const WideItems none = {nullptr, 0, 1};
     if (isums)
-        hipLaunchKernelGGL((mmvq_mfma_res_kernel<NW, GPW, NT, R, DB, true, false>), grid,
+        hipLaunchKernelGGL((mmvq_mfma_res_kernel<NW, GPW, NT, R, DB, true, false, true>), grid,
                            dim3(64 * NW), lds, stream, w, a, nullptr, isums, N, nb, T,
                            (int)ntiles, T, none);
     else
-        hipLaunchKernelGGL((mmvq_mfma_res_kernel<NW, GPW, NT, R, DB, false, false>), grid,
+        hipLaunchKernelGGL((mmvq_mfma_res_kernel<NW, GPW, NT, R, DB, false, false, true>), grid,
                            dim3(64 * NW), lds, stream, w, a, y, nullptr, N, nb, T, (int)ntiles,
                            T, none);
     return check_launch();
@@ -425,13 +470,13 @@ static int launch_res_id(const uint8_t *w, const uint8_t *a, float *y, int64_t N
     const int64_t ntiles = (N + 16 * R - 1) / (16 * R);
     const size_t lds = res_lds_bytes(NW, NT, R, nb, DB, true);
     const void *k =
-        reinterpret_cast<const void *>(&mmvq_mfma_res_kernel<NW, GPW, NT, R, DB, false, true>);
+        reinterpret_cast<const void *>(&mmvq_mfma_res_kernel<NW, GPW, NT, R, DB, false, true, false>);
     allow_dynamic_lds(k, lds);
     const int64_t cap = resident_workgroups(k, 64 * NW, lds);
     const int64_t most = (int64_t)max_wide * ntiles;  // units when every item is in use
     const dim3 grid((unsigned)(most < cap ? most : cap));
     const WideItems items = {routed, max_items, pairs_per_col};
-    hipLaunchKernelGGL((mmvq_mfma_res_kernel<NW, GPW, NT, R, DB, false, true>), grid,
+    hipLaunchKernelGGL((mmvq_mfma_res_kernel<NW, GPW, NT, R, DB, false, true, false>), grid,
                        dim3(64 * NW), lds, stream, w, a, y, nullptr, N, nb, 16, (int)ntiles,
                        a_cols, items);
     return check_launch();
@@ -463,13 +508,13 @@ static int launch_mm(const uint8_t *w, const uint8_t *a, float *y, int64_t N, in
     const int64_t ntiles = (N + 16 * R - 1) / (16 * R);
     const size_t lds = res_lds_bytes(NW, NT, R, nb, DB, true);
     const void *k =
-        reinterpret_cast<const void *>(&mmvq_mfma_res_kernel<NW, GPW, NT, R, DB, false, true>);
+        reinterpret_cast<const void *>(&mmvq_mfma_res_kernel<NW, GPW, NT, R, DB, false, true, true>);
     allow_dynamic_lds(k, lds);
     const int64_t cap = resident_workgroups(k, 64 * NW, lds);
     const int64_t units = (int64_t)((T + 16 * NT - 1) / (16 * NT)) * ntiles;
     const dim3 grid((unsigned)(units < cap ? units : cap));
     const WideItems chunks = {nullptr, 0, 1};
-    hipLaunchKernelGGL((mmvq_mfma_res_kernel<NW, GPW, NT, R, DB, false, true>), grid,
+    hipLaunchKernelGGL((mmvq_mfma_res_kernel<NW, GPW, NT, R, DB, false, true, true>), grid,
                        dim3(64 * NW), lds, stream, w, a, y, nullptr, N, nb, 16 * NT, (int)ntiles,
                        T, chunks);
     return check_launch();
