@@ -83,6 +83,45 @@ __device__ __forceinline__ uint32_t align_bytes(uint32_t hi, uint32_t lo, uint32
     return __builtin_amdgcn_alignbyte(hi, lo, s);
 }
 
+// A DPP move of v (all lanes active): quad_perm, row rotation, ...
+template <int CTRL>
+__device__ __forceinline__ float dpp_move(float v)
+{
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xf, 0xf, true));
+}
+
+// Sum of v over the 1 << lr_log2 aligned lanes of a row (lr_log2 <= 6,
+// uniform), bitwise the value the xor butterfly leaves in every lane of the
+// row (levels m = Lr/2 down to 1, v = v + v of lane ^ m), with all lanes of
+// the wave taking part. Levels of 16 lanes and more exchange through the LDS
+// crossbar. Inside a 16-lane DPP row the levels 8, 4, 2, 1 are row rotations,
+// a few cycles each: a rotation by m reads lane (k -+ m) mod 16, which is
+// lane k ^ m itself for m = 8 and for smaller m differs from it by a sum of
+// the larger levels' strides, so after those levels (a + b == b + a) it holds
+// the same value. Rows of 8 lanes or fewer take the 4-lane level exactly and
+// quad permutations below.
+__device__ __forceinline__ float row_sum(float v, int lr_log2)
+{
+    if (lr_log2 >= 6)
+        v += __shfl_xor(v, 32, 64);
+    if (lr_log2 >= 5)
+        v += __shfl_xor(v, 16, 64);
+    if (lr_log2 >= 4) {
+        v += dpp_move<0x128>(v);  // row_ror:8
+        v += dpp_move<0x124>(v);  // row_ror:4
+        v += dpp_move<0x122>(v);  // row_ror:2
+        v += dpp_move<0x121>(v);  // row_ror:1
+    } else {
+        if (lr_log2 >= 3)
+            v += __shfl_xor(v, 4, 64);
+        if (lr_log2 >= 2)
+            v += dpp_move<0x4e>(v);  // quad_perm [2, 3, 0, 1]
+        if (lr_log2 >= 1)
+            v += dpp_move<0xb1>(v);  // quad_perm [1, 0, 3, 2]
+    }
+    return v;
+}
+
 __device__ __forceinline__ int sdot4(uint32_t a, uint32_t b, int c)
 {
     return __builtin_amdgcn_sdot4((int)a, (int)b, c, false);

@@ -323,7 +323,6 @@ __device__ __forceinline__ void group_rows(const RowWalk &wk, int g, const RawBl
                                            const uint32_t *act, float *__restrict__ y,
                                            const int *pair, int Tc)
 {
-    const int Lr = 1 << wk.lr_log2;
     // blocks past the row's end read block nb - 1's staged columns, and
     // contribute +0 like the lanes of the other kernels that own no block
     const uint32_t *ab0 = act + (wk.sub < wk.nb ? wk.sub : wk.nb - 1) * kActStride;
@@ -339,8 +338,7 @@ __device__ __forceinline__ void group_rows(const RowWalk &wk, int g, const RawBl
         for (int b = 0; b < 8; b++)
             da[b] = __uint_as_float(ab[64 + b]);
         float v = own ? fmaf(dw, block_dot_f32(isum, da), 0.0f) : 0.0f;
-        for (int m = Lr >> 1; m >= 1; m >>= 1)
-            v += __shfl_xor(v, m, 64);
+        v = row_sum(v, wk.lr_log2);
         if (row < wk.N && wk.sub == 0)
             y[(int64_t)pair[t] * wk.N + row] = v;
     }

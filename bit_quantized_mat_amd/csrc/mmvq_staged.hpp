@@ -351,8 +351,7 @@ __device__ __forceinline__ void staged_rows(__amdgpu_buffer_rsrc_t rw, __amdgpu_
         // butterfly over the Lr lanes of the row (every lane of the wave takes part)
 #pragma unroll
         for (int t = 0; t < TC; t++)
-            for (int m = Lr >> 1; m >= 1; m >>= 1)
-                acc[t] += __shfl_xor(acc[t], m, 64);
+            acc[t] = row_sum(acc[t], lr_log2);
         if (row_ok && sub == 0) {
 #pragma unroll
             for (int t = 0; t < TC; t++)

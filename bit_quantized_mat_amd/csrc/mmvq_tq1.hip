@@ -172,10 +172,7 @@ __device__ __forceinline__ void rows_product(const uint8_t *__restrict__ w, uint
         // butterfly over the Lr lanes of the row (all lanes of the wave take part)
 #pragma unroll
         for (int t = 0; t < TC; t++) {
-            float v = acc[t];
-            for (int m = Lr >> 1; m >= 1; m >>= 1)
-                v += __shfl_xor(v, m, 64);
-            acc[t] = v;
+            acc[t] = row_sum(acc[t], __builtin_ctz(Lr));  // Lr: a power of two
         }
         if (row_ok && sub == 0) {
 #pragma unroll
