@@ -14,9 +14,9 @@
 //
 // so byte 1 of each 16-bit lane of X(k) holds F = floor(v / 3^m) for the
 // successive powers m (the integer part of the fixed-point value; byte 0 is
-// its fraction), and the lowest digit is byte 1 of 3 * (X & 0xff). The
-// constants were found by exhaustive search over every byte value and are
-// re-checked on the CPU by tests/test_decode_arith.py.
+// its fraction), and the lowest digit is v - 3 floor(v / 3). The constants
+// were found by exhaustive search over every byte value and are re-checked
+// on the CPU by tests/test_decode_arith.py.
 //
 // A digit is u_m = F_m - 3 F_(m+1). Rather than forming it, the dot products
 // keep two integer sums per Q8_1 sub-block: P = sum F_m q and N = sum F_(m+1) q,
@@ -67,7 +67,8 @@ __device__ __forceinline__ uint32_t hi_bytes(uint32_t o, uint32_t e)
 
 // Floor quotients of the four bytes of a qs dword: F[m] holds
 // floor(v / 3^(4-m)) per byte for m = 0..3 (i.e. F4, F3, F2, F1), and U0 the
-// lowest digit.
+// lowest digit, v - 3 floor(v / 3) per byte: every byte of that difference
+// is a digit (>= 0), so the dword subtraction never borrows across bytes.
 struct QsFloors {
     uint32_t F4, F3, F2, F1, U0;
 };
@@ -81,13 +82,12 @@ __device__ __forceinline__ QsFloors qs_floors(uint32_t w)
     const uint32_t e2 = pk_mul(e1, 3), o2 = pk_mul(o1, 3);
     const uint32_t e3 = pk_mul(e1, 9), o3 = pk_mul(o1, 9);
     const uint32_t e4 = pk_mul(e1, 27), o4 = pk_mul(o1, 27);
-    const uint32_t e5 = pk_mul(e4 & kLaneMask, 3), o5 = pk_mul(o4 & kLaneMask, 3);
     QsFloors f;
     f.F4 = hi_bytes(o1, e1);
     f.F3 = hi_bytes(o2, e2);
     f.F2 = hi_bytes(o3, e3);
     f.F1 = hi_bytes(o4, e4);
-    f.U0 = hi_bytes(o5, e5);
+    f.U0 = w - mul3_bytes(f.F1);
     return f;
 }
 
@@ -104,12 +104,11 @@ __device__ __forceinline__ QhFloors qh_floors(uint32_t w)
     const uint32_t o1 = pk_shr(__umul24(o, kQhMul) + kQhAdd, kQhShift);
     const uint32_t e2 = pk_mul(e1, 3), o2 = pk_mul(o1, 3);
     const uint32_t e3 = pk_mul(e1, 9), o3 = pk_mul(o1, 9);
-    const uint32_t e4 = pk_mul(e3 & kLaneMask, 3), o4 = pk_mul(o3 & kLaneMask, 3);
     QhFloors f;
     f.F3 = hi_bytes(o1, e1);
     f.F2 = hi_bytes(o2, e2);
     f.F1 = hi_bytes(o3, e3);
-    f.U0 = hi_bytes(o4, e4);
+    f.U0 = w - mul3_bytes(f.F1);
     return f;
 }
 
@@ -245,53 +244,6 @@ __device__ __forceinline__ uint32_t qh_digit_lane(uint32_t w, QhLaneMuls m)
     const uint32_t fc = hi_bytes(pk_mul_lanes(o1, m.cur), pk_mul_lanes(e1, m.cur));
     const uint32_t fn = hi_bytes(pk_mul_lanes(o1, m.next), pk_mul_lanes(e1, m.next));
     return minus3<true>(fc, fn);
-}
-
-// Packed signed trits t = u - 1 (bytes 0xff, 0x00, 0x01) from a floor pair:
-// t = F_c - 3 F_(c+1) - 1 per byte. Offsetting every byte by 0x80 first keeps
-// the subtraction free of borrows; the final xor removes the offset.
-__device__ __forceinline__ uint32_t trits_from_floors(uint32_t f, uint32_t f_next)
-{
-    const uint32_t biased = ((f ^ 0x80808080u) + 0xfefefeffu) - mul3_bytes(f_next);  // 0x7f + u
-    return biased ^ 0x80808080u;
-}
-
-// Same for a lowest digit already in hand (u in {0,1,2} per byte).
-__device__ __forceinline__ uint32_t trits_from_digits(uint32_t u)
-{
-    return ((u ^ 0x80808080u) + 0xfefefeffu) ^ 0x80808080u;
-}
-
-// Trits of all five digits of a qs dword: T[c] holds trit c of each byte.
-struct QsTrits {
-    uint32_t T[5];
-};
-
-__device__ __forceinline__ QsTrits qs_trits(uint32_t w)
-{
-    const QsFloors f = qs_floors(w);
-    QsTrits t;
-    t.T[0] = trits_from_digits(f.U0);
-    t.T[1] = trits_from_floors(f.F1, f.F2);
-    t.T[2] = trits_from_floors(f.F2, f.F3);
-    t.T[3] = trits_from_floors(f.F3, f.F4);
-    t.T[4] = trits_from_digits(f.F4);
-    return t;
-}
-
-struct QhTrits {
-    uint32_t T[4];
-};
-
-__device__ __forceinline__ QhTrits qh_trits(uint32_t w)
-{
-    const QhFloors f = qh_floors(w);
-    QhTrits t;
-    t.T[0] = trits_from_digits(f.U0);
-    t.T[1] = trits_from_floors(f.F1, f.F2);
-    t.T[2] = trits_from_floors(f.F2, f.F3);
-    t.T[3] = trits_from_digits(f.F3);
-    return t;
 }
 
 // Exact per-sub-block trit sums from the two running sums.

@@ -40,10 +40,11 @@ def _lane_chain(v, mul, add, shift, mults):
 def test_qs_digit_chain_exhaustive():
     for v in range(243):
         x1, x2, x3, x4 = _lane_chain(v, C["kQsMul"], C["kQsAdd"], C["kQsShift"], (3, 9, 27))
-        x5 = 3 * (x4 & 0xFF)
         floors = [(x >> 8) & 0xFF for x in (x1, x2, x3, x4)]
         assert floors == [v // 81, v // 27, v // 9, v // 3], v
-        assert (x5 >> 8) & 0xFF == v % 3, v
+        # the lowest digit as the byte's value minus 3 floor(v / 3), which
+        # never goes below zero (no borrow into the next byte of the dword)
+        assert 0 <= v - 3 * floors[3] == v % 3, v
         # the unsigned digits recovered as F_m - 3 F_(m+1) match base 3
         f = [v // 3 ** m for m in range(6)]
         digits = [f[m] - 3 * f[m + 1] for m in range(5)]
@@ -53,10 +54,9 @@ def test_qs_digit_chain_exhaustive():
 def test_qh_digit_chain_exhaustive():
     for v in range(81):
         x1, x2, x3 = _lane_chain(v, C["kQhMul"], C["kQhAdd"], C["kQhShift"], (3, 9))
-        x4 = 3 * (x3 & 0xFF)
         floors = [(x >> 8) & 0xFF for x in (x1, x2, x3)]
         assert floors == [v // 27, v // 9, v // 3], v
-        assert (x4 >> 8) & 0xFF == v % 3, v
+        assert 0 <= v - 3 * floors[2] == v % 3, v
 
 
 def _qh_lane_multipliers():
@@ -113,40 +113,6 @@ def test_byte_split_and_merge_selectors():
     assert _perm(0, w, 0x0C030C01) == 0x00440022          # bytes 1, 3 into lanes
     e, o = 0xAA01BB02, 0xCC03DD04                          # byte 1/3 of each lane
     assert _perm(o, e, 0x07030501) == 0xCCAADDBB          # [e.b1, o.b1, e.b3, o.b3]
-
-
-def _trits_from_floors(f, fn):
-    return ((((f ^ 0x80808080) + 0xFEFEFEFF) - 3 * fn) & 0xFFFFFFFF) ^ 0x80808080
-
-
-def _trits_from_digits(u):
-    return (((u ^ 0x80808080) + 0xFEFEFEFF) & 0xFFFFFFFF) ^ 0x80808080
-
-
-def _pack(b):
-    return b[0] | (b[1] << 8) | (b[2] << 16) | (b[3] << 24)
-
-
-def _signed_bytes(x):
-    return [((x >> (8 * i)) & 0xFF) - (256 if (x >> (8 * i)) & 0x80 else 0) for i in range(4)]
-
-
-def test_packed_trit_conversion_exhaustive():
-    """Signed trits from floor pairs (digits 1..3 of a qs byte, 1..2 of qh)
-    and from a digit in hand (digit 0, the top digit): every byte value in
-    every byte position of a dword, against Python's digits minus one."""
-    for v in range(243):
-        for pos in range(4):
-            vs = [(v + 37 * k) % 243 for k in range(4)]
-            vs[pos] = v
-            for c in (1, 2, 3):
-                t = _trits_from_floors(_pack([x // 3 ** c for x in vs]),
-                                       _pack([x // 3 ** (c + 1) for x in vs]))
-                assert _signed_bytes(t) == [(x // 3 ** c) % 3 - 1 for x in vs]
-            assert _signed_bytes(_trits_from_digits(_pack([x % 3 for x in vs]))) == \
-                [x % 3 - 1 for x in vs]
-            assert _signed_bytes(_trits_from_digits(_pack([x // 81 for x in vs]))) == \
-                [x // 81 - 1 for x in vs]
 
 
 def test_single_level_digit_extraction_exhaustive():
