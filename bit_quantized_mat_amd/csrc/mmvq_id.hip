@@ -58,6 +58,12 @@ static int64_t id_max_items(int64_t E, int64_t P)
 // computed independently. Pairs whose id is outside [0, E) are dropped.
 // ---------------------------------------------------------------------------
 constexpr int kWideCols = 16;
+// Pairs from which an expert takes the matrix cores (wide items) once the
+// pre-pass has sorted the pairs. From three pairs, one decode per 16-row tile
+// shared by all of an item's columns beats the staged kernel's one floor-pair
+// pass per column (moe 128 x 1536 x 4096, 512 pairs: 92.5 us at five pairs,
+// 87.3 us at three, 96.7 us at two).
+constexpr int kIdWideMin = 3;
 
 // Exclusive scan of three per-thread values over a kRouteThreads workgroup
 // (in place in v0..v2, which hold one value per thread); the totals go to
@@ -430,11 +436,11 @@ int launch_mmvq_id(const void *w, const void *a, const int32_t *ids, float *y, i
     const int lr = lanes_per_row_log2(nb);
     const int64_t P = T * n_used;
     const bool prepass = id_uses_prepass(E, P);
-    // experts with at least kMfmaMinCols pairs go to the matrix cores when the
+    // experts with at least kIdWideMin pairs go to the matrix cores when the
     // pre-pass sorts the pairs; then every other expert holds at most
-    // kMfmaMinCols - 1 pairs, one narrow item
+    // kIdWideMin - 1 pairs, one narrow item
     const bool wide = prepass && mfma_resident_id_supported(K);
-    const int narrow_cap = wide ? kMfmaMinCols - 1 : kIdCols;
+    const int narrow_cap = wide ? kIdWideMin - 1 : kIdCols;
     // the item's columns must fit LDS whole (on 160 KiB: K <= 15360), and a
     // row must have at most 64 blocks (one per lane)
     const size_t lds = (size_t)narrow_cap * nb * kActStride * 4;
@@ -446,7 +452,7 @@ int launch_mmvq_id(const void *w, const void *a, const int32_t *ids, float *y, i
         routed = static_cast<int32_t *>(workspace);
         hipLaunchKernelGGL(mmvq_id_route_kernel, dim3(1), dim3(kRouteThreads), 0, stream, ids,
                            routed, (int)E, (int)P, (int)max_items, narrow_cap,
-                           wide ? kMfmaMinCols : INT32_MAX);
+                           wide ? kIdWideMin : INT32_MAX);
         if (int rc = check_launch())
             return rc;
     }
@@ -471,9 +477,9 @@ int launch_mmvq_id(const void *w, const void *a, const int32_t *ids, float *y, i
         return rc;
     if (!wide)
         return BQM_OK;
-    // wide items: at most one per expert with kMfmaMinCols or more pairs, plus
+    // wide items: at most one per expert with kIdWideMin or more pairs, plus
     // one per further kWideCols pairs
-    const int64_t wide_experts = P / kMfmaMinCols < E ? P / kMfmaMinCols : E;
+    const int64_t wide_experts = P / kIdWideMin < E ? P / kIdWideMin : E;
     const int64_t max_wide = wide_experts + P / kWideCols;
     return launch_mmvq_mfma_resident_id(w, a, y, N, K, P / pairs_per_col, routed, (int)max_items,
                                         (int)max_wide, pairs_per_col, stream);

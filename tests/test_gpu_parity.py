@@ -285,7 +285,7 @@ def test_mmvq_id_small_cases(bqm):
     # up to 64 (token, slot) pairs are routed inside each wave; more go through
     # the routing pre-pass and the workspace (12 experts x 40 tokens x 3 slots),
     # or, past 4096 experts, through the one-pair-per-workgroup kernel. With
-    # the pre-pass, experts of five or more pairs go to the matrix cores when a
+    # the pre-pass, experts of three or more pairs go to the matrix cores when a
     # row has at least 16 lane groups and the columns fit LDS (K = 2304, 4096,
     # 6144 here: wide items next to narrow ones)
     for (E, N, K, T, n_used, seed) in [(6, 40, 512, 5, 3, 1), (4, 1, 256, 1, 4, 2),
