@@ -261,6 +261,27 @@ def _workload_inputs(name):
     return wl, synth.make_inputs(wl)
 
 
+# One column over many row groups (several workgroups per compute unit): rows
+# of 16 lanes with one block each, of 16 lanes with 7 idle, and of 32 lanes.
+# Against the oracle, the exact sums, the fused quantize-and-multiply call,
+# and bit for bit against column 0 of a two-column call (the two-column
+# kernel, which expands clean digits once for both columns).
+@pytest.mark.parametrize("N,K", [(12345, 4096), (12300, 2304), (6200, 6144)])
+def test_mmvq_one_column_many_row_groups(bqm, N, K):
+    trits, d16, x = _case(N, K, 2, 9000 + N)
+    w, a, w_ref, a_ref = _prep(bqm, trits, d16, x)
+    _say("one column, many row groups", N, K)
+    y = _host(bqm.mmvq_tq1_0(w, a[:1].contiguous(), N, K, 1))
+    _, y64, ab = oracle.mmvq(w_ref, a_ref[:1], N, K, 1)
+    _assert_close(y, y64, ab, "N=%d K=%d" % (N, K))
+    s = _host(bqm.mmvq_tq1_0_block_isums(w, a[:1].contiguous(), N, K, 1))
+    assert np.array_equal(s, oracle.block_isums(w_ref, a_ref[:1], N, K, 1))
+    y2 = _host(bqm.mmvq_tq1_0(w, a, N, K, 2))
+    assert np.array_equal(y[0], y2[0])
+    yf = _host(bqm.mmvq_tq1_0_f32(w, _dev(x[:1]), N, K, 1))
+    assert np.array_equal(yf, y)
+
+
 @pytest.mark.parametrize("name", ["tiny", "decode", "multicol", "ffn"])
 def test_workload_mmvq_parity(bqm, name):
     wl, inp = _workload_inputs(name)
