@@ -144,8 +144,8 @@ int tq1_dequantize(const void *w, const int32_t *rows, void *out, int64_t N, int
     if (n_rows < 1 || (!rows && n_rows > N) || n_rows * (K / 256) >= (1ll << 27) ||
         out_dtype < BQM_DTYPE_F32 || out_dtype > BQM_DTYPE_BF16)
         return BQM_ERR_SHAPE;
-    const uintptr_t out_align = out_dtype == BQM_DTYPE_F32 ? 15u : 7u;
-    if (!aligned4(w) || (rows && !aligned4(rows)) || ((uintptr_t)out & out_align))
+    // every dtype's kernel stores 16 bytes per lane
+    if (!aligned4(w) || (rows && !aligned4(rows)) || ((uintptr_t)out & 15u))
         return BQM_ERR_ALIGN;
     if (int rc = check_device())
         return rc;

@@ -153,7 +153,7 @@ BQM_API int mmvq_tq1_0_f32(const void *w, const float *x, float *y,
  * Shapes: N >= 1, K >= 256, K % 256 == 0, n_rows >= 1, n_rows * K / 256 < 2^27,
  * the weight matrix below 4 GiB. Row ids outside [0, N) are not checked;
  * they read a clamped row, never outside w.
- * Alignment: w and rows 4 bytes; out 16 bytes (fp32) or 8 bytes (fp16, bf16). */
+ * Alignment: w and rows 4 bytes; out 16 bytes. */
 BQM_API int tq1_dequantize(const void *w, const int32_t *rows, void *out,
                    int64_t N, int64_t K, int64_t n_rows, int32_t out_dtype, void *stream);
 
@@ -171,9 +171,10 @@ BQM_API int tq1_dequantize(const void *w, const int32_t *rows, void *out,
  *   (with E <= 4096) are routed by a pre-pass kernel that writes the work
  *   items to the workspace. Tokens that share an expert are multiplied
  *   together, so the expert's weights are read once per group of up to eight
- *   tokens. Ids outside [0, E) are not checked: depending on the kernel
- *   the call takes, such a pair's outputs are left unwritten or computed from
- *   a clamped expert; no access leaves w.
+ *   of its tokens (64 pairs or fewer) or up to sixteen (more pairs, when the
+ *   columns fit the device's LDS). Ids outside [0, E) are not checked:
+ *   depending on the kernel the call takes, such a pair's outputs are left
+ *   unwritten or computed from a clamped expert; no access leaves w.
  * Shapes: E >= 1, N >= 1, K >= 256, K % 256 == 0, T >= 1, 1 <= n_used <= E,
  * T * n_used <= 65535; one expert's matrix is below 4 GiB.
  * Alignment: w, a, y, ids 4 bytes; workspace 256 bytes. */

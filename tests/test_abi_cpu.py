@@ -125,7 +125,8 @@ def test_mmvq_f32_rejects(args, expect):
     ((ODD, None, GOOD, 8, 256, 8, 1, None), -3),
     ((GOOD, ODD, GOOD, 8, 256, 8, 1, None), -3),
     ((GOOD, None, P(0x100008), 8, 256, 8, 0, None), -3),  # fp32 output needs 16 bytes
-    ((GOOD, None, P(0x100004), 8, 256, 8, 1, None), -3),  # fp16 output needs 8 bytes
+    ((GOOD, None, P(0x100004), 8, 256, 8, 1, None), -3),  # every output needs 16 bytes
+    ((GOOD, None, P(0x100008), 8, 256, 8, 2, None), -3),
 ])
 def test_tq1_dequantize_rejects(args, expect):
     assert bqm.library().tq1_dequantize(*args) == expect
