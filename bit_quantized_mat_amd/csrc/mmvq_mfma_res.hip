@@ -201,16 +201,21 @@ __global__ __launch_bounds__(64 * NW) void mmvq_mfma_res_kernel(const uint8_t *_
             }
             return make_rsrc(w, w_bytes);
         }
+        // the item's fields are the same for the whole workgroup: read into
+        // scalar registers, so that the weights' buffer descriptor is too
+        // (a descriptor in vector registers wraps every load in a loop over
+        // the lanes' distinct values)
         const int32_t *it = items.routed + 2 + 3 * (items.max_items + k);
-        const int first = it[1];
-        T = it[2];
+        const int expert = __builtin_amdgcn_readfirstlane(it[0]);
+        const int first = __builtin_amdgcn_readfirstlane(it[1]);
+        T = __builtin_amdgcn_readfirstlane(it[2]);
         if ((int)threadIdx.x < T) {
             const int pr = items.routed[2 + 6 * items.max_items + first + threadIdx.x];
             colpair[threadIdx.x] = pr;
             colbase[threadIdx.x] =
                 (uint32_t)(pr / items.pairs_per_col) * (uint32_t)nblk * kQ81BlockBytes;
         }
-        return make_rsrc(w + (uint64_t)it[0] * w_bytes, w_bytes);
+        return make_rsrc(w + (uint64_t)expert * w_bytes, w_bytes);
     };
     __amdgpu_buffer_rsrc_t rw = ID ? take_item(item) : make_rsrc(w, w_bytes);
 
