@@ -15,9 +15,10 @@
 //
 // Reduction order: a row's blocks are split into Lr lane groups (block B in
 // group B mod Lr); each wave owns Lr / NW groups, accumulates each group's
-// blocks in order and combines its own groups by the xor butterfly; wave 0
-// then combines the waves' partial sums by the remaining butterfly levels,
-// read from LDS. The result is bitwise the staged kernel's.
+// blocks in order and combines its own groups by the xor butterfly; the
+// waves' partial sums then go through LDS, and every wave combines 16 of the
+// tile's outputs per pass by the remaining butterfly levels (four lanes per
+// output). The result is bitwise the staged kernel's.
 #include "mfma_common.hpp"
 
 namespace bqm {
@@ -366,11 +367,23 @@ __global__ __launch_bounds__(64 * NW) void mmvq_mfma_res_kernel(const uint8_t *_
                                 acc[gi][rt][ct][i] = nxt[gi][rt][ct][i];
             }
             // the levels across waves: every wave leaves its partial sums in
-            // this tile's half of red; wave 0 folds them, at level m adding
-            // wave w + m's running value to wave w's for w < m (the value the
-            // xor butterfly gives wave 0). The other half belongs to the next
-            // tile, so one barrier per tile suffices.
+            // this tile's half of red, and then (kAllWavesFold) every wave
+            // folds 16 of the tile's outputs per pass, four lanes per output,
+            // or wave 0 folds them all. Lane j of a
+            // quad takes waves j, j + 4, ...: it applies the levels of 4 and
+            // up among its own values, the quad the levels 2 and 1 by DPP, so
+            // that the quad's lane 0 ends with what the xor butterfly gives
+            // wave 0 (level m adds wave w + m's running value to wave w's). The
+            // other half belongs to the next tile, so one barrier per tile
+            // suffices.
             constexpr int kPer = R * NT * 4;
+            // expert items fold in wave 0 alone (the spread fold measured
+            // slower there: moe 128 x 1536 x 4096, T = 64, 82.9 against
+            // 84.7 us; it gains 2 to 7% on plain products and column chunks)
+            constexpr bool kAllWavesFold = !ID || RUNS;
+            constexpr int kWavesPerLane = NW / 4;
+            constexpr int kPasses = 4 * kPer / NW;
+            static_assert(NW % 4 == 0 && (4 * kPer) % NW == 0, "fold layout");
             float *half = red + (size_t)(DB ? parity : 0) * NW * 64 * kPer;
 #pragma unroll
             for (int rt = 0; rt < R; rt++)
@@ -381,43 +394,73 @@ __global__ __launch_bounds__(64 * NW) void mmvq_mfma_res_kernel(const uint8_t *_
                         half[((size_t)wave * 64 + lane) * kPer + (rt * NT + ct) * 4 + i] =
                             acc[0][rt][ct][i];
             __syncthreads();
-            if (wave == 0) {
+            if constexpr (kAllWavesFold) {
+                const int j = lane & 3;
 #pragma unroll
-                for (int rt = 0; rt < R; rt++)
+                for (int pass = 0; pass < kPasses; pass++) {
+                    // output o of the tile: lane slot o / kPer, value o % kPer
+                    const int o = (pass * NW + wave) * 16 + (lane >> 2);
+                    float x[kWavesPerLane];
 #pragma unroll
-                    for (int ct = 0; ct < NT; ct++)
+                    for (int q = 0; q < kWavesPerLane; q++)
+                        x[q] = half[(size_t)(j + 4 * q) * 64 * kPer + o];
 #pragma unroll
-                        for (int i = 0; i < 4; i++) {
-                            const int k = (rt * NT + ct) * 4 + i;
-                            float v[NW];
+                    for (int m = kWavesPerLane >> 1; m >= 1; m >>= 1)
 #pragma unroll
-                            for (int u = 0; u < NW; u++)
-                                v[u] = half[((size_t)u * 64 + lane) * kPer + k];
+                        for (int q = 0; q < m; q++)
+                            x[q] = x[q] + x[q + m];
+                    float v = x[0];
+                    v = v + dpp_move<0x4e>(v);  // quad_perm [2, 3, 0, 1]: level 2
+                    v = v + dpp_move<0xb1>(v);  // quad_perm [1, 0, 3, 2]: level 1
+                    const int ls = o / kPer, k = o - (o / kPer) * kPer;
+                    const int oc = ls & 15, org = ls >> 4;
+                    const int rt = k / (NT * 4), ct = (k >> 2) % NT, i = k & 3;
+                    const int c = ct * 16 + oc;
+                    const int64_t row = r0 + 16 * rt + 4 * org + i;
+                    if (j == 0 && c < T && row < N) {
+                        const int64_t yc = ID ? colpair[c] : c;
+                        y[yc * N + row] = v;
+                    }
+                }
+            } else {
+                if (wave == 0) {
 #pragma unroll
-                            for (int m = NW >> 1; m >= 1; m >>= 1)
+                    for (int rt = 0; rt < R; rt++)
 #pragma unroll
-                                for (int u = 0; u < m; u++)
-                                    v[u] = v[u] + v[u + m];
-                            acc[0][rt][ct][i] = v[0];
-                        }
-#pragma unroll
-                for (int rt = 0; rt < R; rt++)
-#pragma unroll
-                    for (int ct = 0; ct < NT; ct++) {
-                        const int c = ct * 16 + col;
-                        if (c < T) {
-                            const int64_t yc = ID ? colpair[c] : c;
+                        for (int ct = 0; ct < NT; ct++)
 #pragma unroll
                             for (int i = 0; i < 4; i++) {
-                                const int64_t row = r0 + 16 * rt + 4 * rg + i;
-                                if (row < N)
-                                    y[yc * N + row] = acc[0][rt][ct][i];
+                                const int k = (rt * NT + ct) * 4 + i;
+                                float v[NW];
+#pragma unroll
+                                for (int u = 0; u < NW; u++)
+                                    v[u] = half[((size_t)u * 64 + lane) * kPer + k];
+#pragma unroll
+                                for (int m = NW >> 1; m >= 1; m >>= 1)
+#pragma unroll
+                                    for (int u = 0; u < m; u++)
+                                        v[u] = v[u] + v[u + m];
+                                acc[0][rt][ct][i] = v[0];
+                            }
+#pragma unroll
+                    for (int rt = 0; rt < R; rt++)
+#pragma unroll
+                        for (int ct = 0; ct < NT; ct++) {
+                            const int c = ct * 16 + col;
+                            if (c < T) {
+                                const int64_t yc = ID ? colpair[c] : c;
+#pragma unroll
+                                for (int i = 0; i < 4; i++) {
+                                    const int64_t row = r0 + 16 * rt + 4 * rg + i;
+                                    if (row < N)
+                                        y[yc * N + row] = acc[0][rt][ct][i];
+                                }
                             }
                         }
-                    }
+                }
             }
             if (!DB)
-                __syncthreads();  // wave 0 has read the partial sums
+                __syncthreads();  // the partial sums have been read
         }
 #pragma unroll
         for (int rt = 0; rt < R; rt++)
