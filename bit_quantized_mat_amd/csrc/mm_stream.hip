@@ -29,7 +29,7 @@ constexpr int kMmAhead = 2;        // staging tasks per thread per block
 constexpr int kFoldBlocks = 64;
 
 // LDS per block, in dwords: bq [ct][b][lane] x 2, then the fp16 sub-block
-// scales of each column, [c] x 4 dwords.
+// scales of each column, [c] x 4 dwords; two of each, for consecutive blocks.
 constexpr int kMmBqDwords = kMmCols * 8 * 128;
 constexpr int kMmDahDwords = kMmCols * 16 * 4;
 
@@ -86,8 +86,11 @@ __device__ __forceinline__ void row_group(__amdgpu_buffer_rsrc_t rw, __amdgpu_bu
     for (int B = 0; B < nb; B++) {
         const LaneBlock ln = load_lane_block(
             rw, B + 1 < nb ? row_off + (uint32_t)(B + 1) * kTq1BlockBytes : kIdleLoadOffset, kg);
-        if (B > 0)
-            __syncthreads();  // every wave is done with the previous block
+        // block B's copy goes to buffer B & 1: the other buffer may still be
+        // read for block B - 1, and every wave finished block B - 2's reads of
+        // this one before the previous barrier
+        uint32_t *const bqB = bq + (B & 1) * kMmBqDwords;
+        uint32_t *const dahB = dah + (B & 1) * kMmDahDwords;
 #pragma unroll
         for (int k = 0; k < kMmAhead; k++) {
             const int i = k * 256 + tid;
@@ -95,17 +98,17 @@ __device__ __forceinline__ void row_group(__amdgpu_buffer_rsrc_t rw, __amdgpu_bu
             const uint32_t q[8] = {v0[k].x, v0[k].y, v0[k].z, v0[k].w,
                                    v1[k].x, v1[k].y, v1[k].z, v1[k].w};
             const int ct = c >> 4, cc = c & 15;
-            uint32_t *dst = bq + (ct * 8 + b) * 128;
+            uint32_t *dst = bqB + (ct * 8 + b) * 128;
 #pragma unroll
             for (int g = 0; g < 4; g++) {
                 const uint32_t lo = b < 5 ? q[2 * g] : q[g];
                 const uint32_t hi = b < 5 ? q[2 * g + 1] : q[4 + g];
                 *reinterpret_cast<u32x2 *>(dst + 2 * (16 * g + cc)) = (u32x2){lo, hi};
             }
-            reinterpret_cast<uint16_t *>(dah + c * 4)[b] = (uint16_t)ds[k];
+            reinterpret_cast<uint16_t *>(dahB + c * 4)[b] = (uint16_t)ds[k];
         }
         issue_stage(B + 1);
-        __syncthreads();
+        __syncthreads();  // block B's copy is complete
 
         const TileOperands op = decode_lane_block(lb, qm);
         float dw[4];  // block scales of the four rows this output lane holds
@@ -114,8 +117,8 @@ __device__ __forceinline__ void row_group(__amdgpu_buffer_rsrc_t rw, __amdgpu_bu
             dw[i] = __shfl(op.dw, 4 * rg + i, 64);
 #pragma unroll
         for (int ct = 0; ct < kMmCols; ct++) {
-            const u32x4 dv = *reinterpret_cast<const u32x4 *>(dah + (ct * 16 + col) * 4);
-            const uint32_t *bqc = bq + ct * 8 * 128 + 2 * lane;
+            const u32x4 dv = *reinterpret_cast<const u32x4 *>(dahB + (ct * 16 + col) * 4);
+            const uint32_t *bqc = bqB + ct * 8 * 128 + 2 * lane;
             float s[4];
 #pragma unroll
             for (int b = 0; b < 8; b++) {
@@ -170,8 +173,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void m
     const uint8_t *__restrict__ w, const uint8_t *__restrict__ a, float *__restrict__ y, int64_t N,
     int nb, int T, int64_t nrowgroups)
 {
-    __shared__ uint32_t bq[kMmBqDwords];
-    __shared__ uint32_t dah[kMmDahDwords];
+    __shared__ uint32_t bq[2 * kMmBqDwords];  // two buffers: blocks B and B + 1
+    __shared__ uint32_t dah[2 * kMmDahDwords];
     const int64_t rgroup = (int64_t)blockIdx.z * gridDim.y + blockIdx.y;
     if (rgroup >= nrowgroups)
         return;
