@@ -249,6 +249,54 @@ __device__ __forceinline__ void digit_sums_staged(const DigitBlock &d,
     }
 }
 
+// Exact sub-block sums of one block against NC staged columns (column t at
+// ab0 + t * col_stride), one packed dword at a time: its clean digits meet
+// every column before the next dword is expanded, so no expanded block stays
+// live (about 60 registers where a whole DigitBlock takes 64 on its own).
+template <int NC>
+__device__ __forceinline__ void dword_sums_staged(const RawBlock &raw,
+                                                  const uint32_t *__restrict__ ab0, int col_stride,
+                                                  int (&isum)[NC][8])
+{
+#pragma unroll
+    for (int t = 0; t < NC; t++)
+#pragma unroll
+        for (int c = 0; c < 8; c++)
+            isum[t][c] = (int)ab0[t * col_stride + 72 + c];
+#pragma unroll
+    for (int j = 0; j < 8; j++) {
+        const QsDigits u = qs_digits(raw_dword(raw, j));
+#pragma unroll
+        for (int t = 0; t < NC; t++) {
+            const uint32_t *ab = ab0 + t * col_stride;
+            const uint4 lo = *reinterpret_cast<const uint4 *>(ab + 8 * j);
+            const uint32_t q4 = ab[8 * j + 4];
+            isum[t][0] = sdot4(u.U[0], lo.x, isum[t][0]);
+            isum[t][1] = sdot4(u.U[1], lo.y, isum[t][1]);
+            isum[t][2] = sdot4(u.U[2], lo.z, isum[t][2]);
+            isum[t][3] = sdot4(u.U[3], lo.w, isum[t][3]);
+            isum[t][4] = sdot4(u.U[4], q4, isum[t][4]);
+        }
+    }
+    const QhDigits qh = qh_digits(raw_dword(raw, 12));
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+        const QsDigits u = qs_digits(raw_dword(raw, 8 + i));
+#pragma unroll
+        for (int t = 0; t < NC; t++) {
+            const uint32_t *ab = ab0 + t * col_stride;
+            const uint4 a = *reinterpret_cast<const uint4 *>(ab + 8 * i + 4);
+            const uint4 b = *reinterpret_cast<const uint4 *>(ab + 8 * (4 + i) + 4);
+            isum[t][5] = sdot4(u.U[0], a.y, isum[t][5]);
+            isum[t][5] = sdot4(u.U[1], b.y, isum[t][5]);
+            isum[t][6] = sdot4(u.U[2], a.z, isum[t][6]);
+            isum[t][6] = sdot4(u.U[3], b.z, isum[t][6]);
+            isum[t][7] = sdot4(u.U[4], a.w, isum[t][7]);
+            isum[t][7] = sdot4(qh.U[i], b.w, isum[t][7]);
+        }
+    }
+}
+
 // The rows of one workgroup against T <= TC activation columns. Column t's
 // Q8_1 row (fp32 row when F32: quantized while staging) starts at byte
 // col_off[t] of the activation buffer ra and its outputs go to out[t][row].
@@ -311,8 +359,22 @@ __device__ __forceinline__ void staged_rows(__amdgpu_buffer_rsrc_t rw, __amdgpu_
                     cur = load_raw_block(rw, row_off + (uint32_t)B * kTq1BlockBytes);
                 const float dw = f16_bits_to_f32(raw_scale_bits(cur));
                 DigitBlock d;
-                if (TC > 1)
+                if (TC > 2)
                     expand_block(cur, d);
+                // two columns (T == 2 exactly): one dword's digits at a time
+                int isum2[2][8];
+                if (TC == 2) {
+                    dword_sums_staged<2>(cur, act + (B - B0) * kActStride, cb * kActStride, isum2);
+                    // the exact sums pass through an empty asm statement
+                    // before their fp32 terms: without it the compiler
+                    // reshapes the products around the conversions and needs
+                    // over 250 registers
+#pragma unroll
+                    for (int t = 0; t < 2; t++)
+#pragma unroll
+                        for (int b = 0; b < 8; b++)
+                            asm volatile("" : "+v"(isum2[t][b]));
+                }
 #pragma unroll
                 for (int t = 0; t < TC; t++) {
                     if (t < T) {
@@ -320,6 +382,10 @@ __device__ __forceinline__ void staged_rows(__amdgpu_buffer_rsrc_t rw, __amdgpu_
                         int isum[8];
                         if (TC == 1)
                             block_sums_staged(cur, ab, isum);
+                        else if (TC == 2)
+#pragma unroll
+                            for (int b = 0; b < 8; b++)
+                                isum[b] = isum2[t][b];
                         else
                             digit_sums_staged(d, ab, isum);
                         if (ISUMS) {
