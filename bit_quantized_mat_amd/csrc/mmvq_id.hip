@@ -5,7 +5,7 @@
 // load-bound by the per-32-element chunk contract", "Acceptance criteria":
 // expert mat-vec at one activation per token, fewer experts used than
 // available). Tokens routed to the same expert are grouped so that the
-// expert's weights stream once per group of up to eight tokens, the compacted
+// expert's weights stream once per group of up to kIdCols tokens, the compacted
 // per-expert grid that "tools: add mmq-tune, an MMQ tile-width autotuning
 // harness" (Summary) describes for the production MoE path.
 //
@@ -31,7 +31,12 @@
 
 namespace bqm {
 
-constexpr int kIdCols = 8;             // pairs per work item
+// Pairs per work item of the staged expert kernel. It finishes an item's
+// columns one after another, so under skewed routing the few items of the
+// most used experts set the kernel's length; four splits them at the cost of
+// a second read of those experts' weights (moe 128 x 1536 x 4096, T = 8:
+// 24.9 us at eight, 23.3 at four, 25.1 at two).
+constexpr int kIdCols = 4;
 constexpr int kIdWaveRouteMax = 64;    // pairs routed inside the wave
 constexpr int kIdMaxExperts = 4096;    // experts the routing pre-pass handles
 constexpr int kRouteThreads = 1024;

@@ -170,7 +170,7 @@ BQM_API int tq1_dequantize(const void *w, const int32_t *rows, void *out,
  *   the product kernel and the size is 0: NULL is then accepted. More pairs
  *   (with E <= 4096) are routed by a pre-pass kernel that writes the work
  *   items to the workspace. Tokens that share an expert are multiplied
- *   together, so the expert's weights are read once per group of up to eight
+ *   together, so the expert's weights are read once per group of up to four
  *   of its tokens (64 pairs or fewer) or up to sixteen (more pairs, when the
  *   columns fit the device's LDS). Ids outside [0, E) are not checked:
  *   depending on the kernel the call takes, such a pair's outputs are left

@@ -195,11 +195,12 @@ def test_mmvq_id_rejects():
     assert lib.mmvq_id_tq1_0_workspace_bytes(0, 4, 2) == 0
     assert lib.mmvq_id_tq1_0_workspace_bytes(8, 4, 9) == 0
     # more pairs: the routing pre-pass needs 2 + 6 * items + pairs int32 words
-    # (two item lists of at most (P + 7 * min(E, P) + 7) / 8 entries of three
-    # words, one run slot per pair), rounded up to 256 bytes
+    # (two item lists of at most (P + 3 * min(E, P) + 3) / 4 entries of three
+    # words -- items of up to four pairs -- one run slot per pair), rounded up
+    # to 256 bytes
     for E, T, n_used in [(128, 64, 8), (128, 9, 8), (4, 65, 1), (4096, 1000, 4)]:
         pairs = T * n_used
-        items = (pairs + 7 * min(E, pairs) + 7) // 8
+        items = (pairs + 3 * min(E, pairs) + 3) // 4
         words = 2 + 6 * items + pairs
         assert lib.mmvq_id_tq1_0_workspace_bytes(E, T, n_used) == (4 * words + 255) // 256 * 256
     assert lib.mmvq_id_tq1_0_workspace_bytes(128, 8, 8) == 0      # exactly 64 pairs

@@ -224,9 +224,12 @@ def test_mmvq_one_hot_element_map(bqm):
 
 
 # rows of 32, 64, 16, 4, 8 and 2 lanes (the one-column kernel's row sum
-# against the matrix-core kernels' butterfly through LDS)
+# against the matrix-core kernels' butterfly through LDS); two and three
+# columns on the staged kernels (one dword's digits at a time for two columns,
+# the expanded block for three)
 @pytest.mark.parametrize("N,K,T", [(320, 6144, 8), (100, 6144, 20), (70, 16384, 32),
-                                   (48, 4096, 12), (33, 768, 9), (40, 2048, 10), (24, 512, 6)])
+                                   (48, 4096, 12), (33, 768, 9), (40, 2048, 10), (24, 512, 6),
+                                   (4500, 4096, 2), (4300, 6144, 3)])
 def test_mmvq_columns_equal_single_column_calls(bqm, N, K, T):
     """Column t of a T-column call equals the one-column call bit for bit:
     integer sums and fp32 outputs (staged kernel up to 8 columns, matrix-core
