@@ -70,6 +70,21 @@ constexpr int kWideCols = 16;
 // 87.3 us at three, 96.7 us at two).
 constexpr int kIdWideMin = 3;
 
+// Inclusive sum over lanes 0..L of the wave, for every lane L: within each
+// 16-lane row by shifts of 1, 2, 4, 8 (lanes without a source add 0), then
+// row 1 and 3 add lane 15 of the row before, rows 2 and 3 lane 31 (DPP row
+// broadcasts).
+__device__ __forceinline__ int wave_inclusive_sum(int v)
+{
+    v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xf, 0xf, false);  // row_shr:1
+    v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xf, 0xf, false);  // row_shr:2
+    v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xf, 0xf, false);  // row_shr:4
+    v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xf, 0xf, false);  // row_shr:8
+    v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xa, 0xf, false);  // row_bcast:15
+    v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xc, 0xf, false);  // row_bcast:31
+    return v;
+}
+
 // Exclusive scan of three per-thread values over a kRouteThreads workgroup
 // (in place in v0..v2, which hold one value per thread); the totals go to
 // tot[0..2]. One wave scans, 16 values per lane.
@@ -78,26 +93,24 @@ __device__ __forceinline__ void route_scan3(int *v0, int *v1, int *v2, int *tot)
     const int tid = threadIdx.x;
     if (tid < 64) {
         int *v[3] = {v0, v1, v2};
+        int x[3][16], r[3];
 #pragma unroll
         for (int k = 0; k < 3; k++) {
-            int x[16], r = 0;
+            r[k] = 0;
 #pragma unroll
             for (int i = 0; i < 16; i++) {
-                x[i] = v[k][tid * 16 + i];
-                r += x[i];
+                x[k][i] = v[k][tid * 16 + i];
+                r[k] += x[k][i];
             }
-            int inc = r;
+        }
 #pragma unroll
-            for (int m = 1; m < 64; m <<= 1) {
-                const int u = __shfl_up(inc, m, 64);
-                if (tid >= m)
-                    inc += u;
-            }
-            int o = inc - r;
+        for (int k = 0; k < 3; k++) {
+            const int inc = wave_inclusive_sum(r[k]);
+            int o = inc - r[k];
 #pragma unroll
             for (int i = 0; i < 16; i++) {
                 v[k][tid * 16 + i] = o;
-                o += x[i];
+                o += x[k][i];
             }
             if (tid == 63)
                 tot[k] = inc;
@@ -121,7 +134,18 @@ __global__ __launch_bounds__(kRouteThreads) void mmvq_id_route_kernel(
         fill[e] = 0;
     }
     __syncthreads();
-    for (int p = tid; p < P; p += kRouteThreads) {
+    // the first kRouteHeld ids of each thread stay in registers for the
+    // scatter below (P <= kRouteHeld * kRouteThreads reads ids once)
+    constexpr int kRouteHeld = 4;
+    int held[kRouteHeld];
+#pragma unroll
+    for (int h = 0; h < kRouteHeld; h++) {
+        const int p = tid + h * kRouteThreads;
+        held[h] = p < P ? ids[p] : -1;
+        if ((unsigned)held[h] < (unsigned)E)
+            atomicAdd(&cnt[held[h]], 1);
+    }
+    for (int p = tid + kRouteHeld * kRouteThreads; p < P; p += kRouteThreads) {
         const int e = ids[p];
         if ((unsigned)e < (unsigned)E)
             atomicAdd(&cnt[e], 1);
@@ -174,7 +198,13 @@ __global__ __launch_bounds__(kRouteThreads) void mmvq_id_route_kernel(
         }
     }
     __syncthreads();
-    for (int p = tid; p < P; p += kRouteThreads) {
+#pragma unroll
+    for (int h = 0; h < kRouteHeld; h++) {
+        const int p = tid + h * kRouteThreads;
+        if ((unsigned)held[h] < (unsigned)E)
+            runs[cnt[held[h]] + atomicAdd(&fill[held[h]], 1)] = p;
+    }
+    for (int p = tid + kRouteHeld * kRouteThreads; p < P; p += kRouteThreads) {
         const int e = ids[p];
         if ((unsigned)e < (unsigned)E)
             runs[cnt[e] + atomicAdd(&fill[e], 1)] = p;
