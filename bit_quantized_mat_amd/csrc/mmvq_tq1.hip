@@ -187,8 +187,9 @@ __device__ __forceinline__ void rows_product(const uint8_t *__restrict__ w, uint
 // three columns on it does so only when its grid gives the device more than
 // one wave per SIMD: with one block per lane and no second wave to overlap
 // it, the multi-column work after the weights arrive outlasts the
-// matrix-core kernel's (4096 x 4096 at three columns: 6.2 against 5.5 us;
-// 5120 x 6144 and 14336 x 4096, with more waves, favour the staged kernel).
+// matrix-core kernel's (4096 x 4096: 5.6 against 5.3 us at three columns,
+// 6.2 against 5.5 at four; at 5120 x 6144 and 14336 x 4096, with more waves,
+// the staged kernel is as fast or faster).
 static bool use_staged(int64_t N, int64_t K, int32_t T)
 {
     if (T >= kMfmaMinCols || !staged_supported(K, T))
@@ -216,8 +217,9 @@ int launch_mmvq(const void *w, const void *a, float *y, int32_t *isums, int64_t 
 // device at least 1.5 workgroups per compute unit: each of its workgroups
 // walks all of K, so with fewer of them that walk is exposed, and the
 // resident kernel over column chunks (whose columns must fit LDS) is faster
-// (4096 x 4096 at 64 columns: 18.6 against 45 us; 14336 x 4096 at 128
-// columns: 75 against 64 us, at 512: 277 against 170 us).
+// (4096 x 4096 at 64 columns: 16.2 against 45.0 us, at 512: 69.5 against
+// 56.9; 14336 x 4096 at 128 columns: 62.1 against 57.2, at 512: 223 against
+// 145 us).
 int launch_mm(const void *w, const void *a, float *y, int64_t N, int64_t K, int64_t T,
               hipStream_t stream)
 {
