@@ -121,6 +121,11 @@ int mmvq_tq1_0_f32(const void *w, const float *x, float *y, int64_t N, int64_t K
         return BQM_ERR_ALIGN;
     if (int rc = check_device())
         return rc;
+    // three to eight columns: the quad kernel where it takes the shape (it
+    // stages, and so quantizes, each column once per 16 rows like the staged
+    // kernel, with a quarter of the staged kernel's LDS reads)
+    if (bqm::quad_supported(K, T))
+        return bqm::launch_mmvq_quad_f32(w, x, y, N, K, T, as_stream(stream));
     if (!bqm::staged_supported(K, T))
         return BQM_ERR_SHAPE;
     return bqm::launch_mmvq_staged_f32(w, x, y, N, K, T, as_stream(stream));

@@ -51,10 +51,19 @@ int launch_mmvq_staged(const void *w, const void *a, float *y, int32_t *isums, i
 // The staged kernel on fp32 activations, quantized to Q8_1 while staging.
 int launch_mmvq_staged_f32(const void *w, const float *x, float *y, int64_t N, int64_t K,
                            int32_t T, hipStream_t stream);
+// Quad kernel (three to eight columns, whole-block decode per lane, sub-block
+// sums on the matrix cores; rows of more than 8 blocks): whether it takes this
+// shape, and its launchers (Q8_1 activations, and fp32 activations quantized
+// while staging).
+bool quad_supported(int64_t K, int32_t T);
+int launch_mmvq_quad(const void *w, const void *a, float *y, int32_t *isums, int64_t N,
+                     int64_t K, int32_t T, hipStream_t stream);
+int launch_mmvq_quad_f32(const void *w, const float *x, float *y, int64_t N, int64_t K,
+                         int32_t T, hipStream_t stream);
 // Matrix-core kernel: any shape, 1 to 32 columns; the dispatcher gives it
-// every call of at least kMfmaMinCols columns, the calls whose activations
-// do not fit the staged kernel's LDS, and calls of three or more columns too
-// small to give the staged kernel a second wave per SIMD.
+// every call of at least kMfmaMinCols columns, and the calls of fewer that
+// neither the quad kernel nor the staged kernel takes or that are too small
+// to give the staged kernel a second wave per SIMD.
 constexpr int kMfmaMinCols = 5;
 
 int launch_mmvq_mfma(const void *w, const void *a, float *y, int32_t *isums, int64_t N,

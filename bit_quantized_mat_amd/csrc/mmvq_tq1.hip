@@ -200,11 +200,19 @@ static bool use_staged(int64_t N, int64_t K, int32_t T)
     return waves > 4ll * compute_units();
 }
 
-// Plain product: the staged kernel for narrow calls whose activations fit its
-// LDS, the matrix-core kernel for everything else.
+// Plain product: the quad kernel for three and four columns where it takes
+// the shape, the staged kernel for other narrow calls whose activations fit
+// its LDS, the matrix-core kernel for everything else. The quad kernel's two
+// column groups (five to eight columns) need about 210 registers, two waves
+// per SIMD, and lose to the resident matrix-core kernel on Q8_1 input
+// (14336 x 4096 at eight columns: 14.2 against 11.4 us); at three and four
+// columns they win (8.9 against 11.6 us at four, 4096 x 4096: 5.1 against
+// 5.6 us).
 int launch_mmvq(const void *w, const void *a, float *y, int32_t *isums, int64_t N, int64_t K,
                 int32_t T, hipStream_t stream)
 {
+    if (T >= 3 && T <= 4 && quad_supported(K, T))
+        return launch_mmvq_quad(w, a, y, isums, N, K, T, stream);
     if (use_staged(N, K, T))
         return launch_mmvq_staged(w, a, y, isums, N, K, T, stream);
     if (mfma_resident_supported(K, T))

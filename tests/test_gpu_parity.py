@@ -246,6 +246,31 @@ def test_mmvq_columns_equal_single_column_calls(bqm, N, K, T):
     assert row == (K // 32) * 36
 
 
+
+# the quad kernel (three and four columns here; three to eight on fp32
+# input): two staging passes (65536 at three columns, 32768 at four), rows of
+# 9 and 17 blocks (slots without a block; two groups per lane), 56 and 256
+# blocks (four groups per lane), a last wave past N
+@pytest.mark.parametrize("N,K,T", [(64, 65536, 3), (77, 32768, 4), (333, 2304, 4),
+                                   (1000, 4352, 3), (515, 14336, 4), (4100, 4096, 4)])
+def test_mmvq_quad_shapes(bqm, N, K, T):
+    """Exact integer sums, fp32 within tolerance of the oracle, every column
+    bitwise its one-column call, and the fp32-input call bitwise equal."""
+    trits, d16, x = _case(N, K, T, 5000 + N + T)
+    w, a, w_ref, a_ref = _prep(bqm, trits, d16, x)
+    _say("quad", N, K, T)
+    got = _host(bqm.mmvq_tq1_0_block_isums(w, a, N, K, T))
+    assert np.array_equal(got, oracle.block_isums(w_ref, a_ref, N, K, T))
+    y = _host(bqm.mmvq_tq1_0(w, a, N, K, T))
+    _, y64, ab = oracle.mmvq(w_ref, a_ref, N, K, T)
+    _assert_close(y, y64, ab, "quad %dx%d T=%d" % (N, K, T))
+    for t in range(T):
+        y1 = _host(bqm.mmvq_tq1_0(w, a[t:t + 1].contiguous(), N, K, 1))[0]
+        assert np.array_equal(y1.view(np.uint32), y[t].view(np.uint32)), t
+    yf = _host(bqm.mmvq_tq1_0_f32(w, _dev(x), N, K, T))
+    assert np.array_equal(yf.view(np.uint32), y.view(np.uint32))
+
+
 def test_mmvq_deterministic(bqm):
     N, K, T = 1024, 4096, 4
     trits, d16, x = _case(N, K, T, 55)
@@ -502,7 +527,8 @@ def test_mm_prefill_workload(bqm):
 
 @pytest.mark.parametrize("N,K,T", [(256, 1024, 1), (1, 256, 1), (33, 256, 2), (67, 768, 3),
                                    (130, 2304, 5), (515, 4096, 8), (96, 6144, 4),
-                                   (40, 16384, 1), (17, 8192, 7), (9, 8448, 6)])
+                                   (40, 16384, 1), (17, 8192, 7), (9, 8448, 6),
+                                   (77, 32768, 7), (64, 65536, 5), (4100, 4096, 8)])
 def test_mmvq_f32_equals_quantize_then_mmvq(bqm, N, K, T):
     trits, d16, x = _case(N, K, T, seed=N * 7 + K + T)
     w, a, w_ref, a_ref = _prep(bqm, trits, d16, x)
