@@ -52,9 +52,10 @@ static int quad_chunk(int nb, int lr, int T, size_t budget)
     return chunk >= Lr ? chunk : 0;
 }
 
-// CG column groups of four (T <= 4 CG), GPW = Lr / 16 groups per lane.
-template <int CG, int GPW, bool ISUMS, bool F32>
-__global__ __launch_bounds__(256) void mmvq_quad_kernel(const uint8_t *__restrict__ w,
+// CG column groups of four (T <= 4 CG), GPW = Lr / 16 groups per lane, WPG
+// waves (4 WPG rows) per workgroup.
+template <int CG, int GPW, bool ISUMS, bool F32, int WPG>
+__global__ __launch_bounds__(64 * WPG) void mmvq_quad_kernel(const uint8_t *__restrict__ w,
                                                         const uint8_t *__restrict__ a,
                                                         float *__restrict__ y,
                                                         int32_t *__restrict__ isums, int64_t N,
@@ -64,7 +65,7 @@ __global__ __launch_bounds__(256) void mmvq_quad_kernel(const uint8_t *__restric
     uint32_t *act = reinterpret_cast<uint32_t *>(act_lds);
     const int tid = threadIdx.x, lane = tid & 63;
     const int g = lane >> 2, qi = lane & 3;
-    const int64_t row0 = ((int64_t)blockIdx.x * 4 + (tid >> 6)) * 4;  // the wave's first row
+    const int64_t row0 = ((int64_t)blockIdx.x * WPG + (tid >> 6)) * 4;  // the wave's first row
     const int64_t row = row0 + qi;                                      // this lane's A row
     const bool row_ok = row < N;
     const int nblk = nb * 8;
@@ -97,18 +98,18 @@ __global__ __launch_bounds__(256) void mmvq_quad_kernel(const uint8_t *__restric
         // first staging batch, then this lane's first weight block (as in the
         // staged kernel: the weights' latency overlaps the activation copy)
         StageBatch<F32> head;
-        stage_load<F32>(head, ra, 0, B0, cb, 0, tid, 256);
+        stage_load<F32>(head, ra, 0, B0, cb, 0, tid, 64 * WPG);
         __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
         RawBlock cur = load_raw_block(rw, row_ok && first < end
                                               ? row_off + (uint32_t)first * kTq1BlockBytes
                                               : kIdleLoadOffset);
         __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
         __builtin_amdgcn_sched_barrier(0);
-        stage_column<F32>(act, ra, 0, B0, cb, tid, 256, &head);
+        stage_column<F32>(act, ra, 0, B0, cb, tid, 64 * WPG, &head);
 #pragma unroll
         for (int t = 1; t < 4 * CG; t++)
             if (t < T)
-                stage_column<F32>(act + t * S, ra, (uint32_t)t * col_bytes, B0, cb, tid, 256,
+                stage_column<F32>(act + t * S, ra, (uint32_t)t * col_bytes, B0, cb, tid, 64 * WPG,
                                   nullptr);
         __syncthreads();
         // the slot's blocks B = first + 16 m; the trip count is the same for
@@ -277,20 +278,49 @@ bool quad_supported(int64_t K, int32_t T)
     return lr >= 4 && quad_chunk(nb, lr, T, lds_budget()) > 0;
 }
 
-template <int CG, int GPW, bool F32>
-static void launch_quad_cg(const uint8_t *w, const uint8_t *a, float *y, int32_t *isums,
-                           int64_t N, int nb, int T, int chunk, dim3 grid, size_t lds,
-                           hipStream_t stream)
+// Waves per workgroup: eight (32 rows) unless that puts more waves on the
+// busiest SIMD than four do (counted as rounds of workgroups per compute unit
+// times waves per workgroup). Eight halves the staging per row, which is the
+// activation copy and, on fp32 input, the quantization (14336 x 4096 fp32 at
+// eight columns: 22.3 against 24.0 us; 5120 x 6144: 16.0 against 23.2 us);
+// four keep every compute unit busy on 4096 rows (4.85 against 5.63 us).
+static int quad_waves(int64_t N)
 {
+    const int64_t cu = compute_units();
+    const int64_t r4 = ((N + 15) / 16 + cu - 1) / cu;
+    const int64_t r8 = ((N + 31) / 32 + cu - 1) / cu;
+    return 2 * r8 <= r4 ? 8 : 4;
+}
+
+template <int CG, int GPW, bool F32, int WPG>
+static void launch_quad_cg(const uint8_t *w, const uint8_t *a, float *y, int32_t *isums,
+                           int64_t N, int nb, int T, int chunk, size_t lds, hipStream_t stream)
+{
+    const dim3 grid((unsigned)((N + 4 * WPG - 1) / (4 * WPG))), block(64 * WPG);
     if (isums && !F32) {
-        allow_dynamic_lds(reinterpret_cast<const void *>(&mmvq_quad_kernel<CG, GPW, true, false>), lds);
-        hipLaunchKernelGGL((mmvq_quad_kernel<CG, GPW, true, false>), grid, dim3(256), lds, stream,
+        const void *k = reinterpret_cast<const void *>(&mmvq_quad_kernel<CG, GPW, true, false, WPG>);
+        allow_dynamic_lds(k, lds);
+        hipLaunchKernelGGL((mmvq_quad_kernel<CG, GPW, true, false, WPG>), grid, block, lds, stream,
                            w, a, nullptr, isums, N, nb, T, chunk);
     } else {
-        allow_dynamic_lds(reinterpret_cast<const void *>(&mmvq_quad_kernel<CG, GPW, false, F32>), lds);
-        hipLaunchKernelGGL((mmvq_quad_kernel<CG, GPW, false, F32>), grid, dim3(256), lds, stream,
+        const void *k = reinterpret_cast<const void *>(&mmvq_quad_kernel<CG, GPW, false, F32, WPG>);
+        allow_dynamic_lds(k, lds);
+        hipLaunchKernelGGL((mmvq_quad_kernel<CG, GPW, false, F32, WPG>), grid, block, lds, stream,
                            w, a, y, nullptr, N, nb, T, chunk);
     }
+}
+
+template <int GPW, bool F32>
+static void launch_quad_gpw(const uint8_t *w, const uint8_t *a, float *y, int32_t *isums,
+                            int64_t N, int nb, int T, int chunk, size_t lds, hipStream_t stream)
+{
+    const bool two = T > 4, wide = quad_waves(N) == 8;
+    if (two)
+        wide ? launch_quad_cg<2, GPW, F32, 8>(w, a, y, isums, N, nb, T, chunk, lds, stream)
+             : launch_quad_cg<2, GPW, F32, 4>(w, a, y, isums, N, nb, T, chunk, lds, stream);
+    else
+        wide ? launch_quad_cg<1, GPW, F32, 8>(w, a, y, isums, N, nb, T, chunk, lds, stream)
+             : launch_quad_cg<1, GPW, F32, 4>(w, a, y, isums, N, nb, T, chunk, lds, stream);
 }
 
 template <bool F32>
@@ -302,24 +332,13 @@ static int launch_quad(const void *w, const void *a, float *y, int32_t *isums, i
     const int chunk = quad_chunk(nb, lr, T, lds_budget());
     if (T < 3 || T > 8 || lr < 4 || chunk <= 0)
         return BQM_ERR_SHAPE;
-    const dim3 grid((unsigned)((N + 15) / 16));
     const size_t lds = (size_t)T * quad_col_stride(chunk) * 4;
     const uint8_t *wp = static_cast<const uint8_t *>(w);
     const uint8_t *ap = static_cast<const uint8_t *>(a);
-    const bool two = T > 4;
     switch (lr) {
-    case 4:
-        two ? launch_quad_cg<2, 1, F32>(wp, ap, y, isums, N, nb, T, chunk, grid, lds, stream)
-            : launch_quad_cg<1, 1, F32>(wp, ap, y, isums, N, nb, T, chunk, grid, lds, stream);
-        break;
-    case 5:
-        two ? launch_quad_cg<2, 2, F32>(wp, ap, y, isums, N, nb, T, chunk, grid, lds, stream)
-            : launch_quad_cg<1, 2, F32>(wp, ap, y, isums, N, nb, T, chunk, grid, lds, stream);
-        break;
-    default:
-        two ? launch_quad_cg<2, 4, F32>(wp, ap, y, isums, N, nb, T, chunk, grid, lds, stream)
-            : launch_quad_cg<1, 4, F32>(wp, ap, y, isums, N, nb, T, chunk, grid, lds, stream);
-        break;
+    case 4: launch_quad_gpw<1, F32>(wp, ap, y, isums, N, nb, T, chunk, lds, stream); break;
+    case 5: launch_quad_gpw<2, F32>(wp, ap, y, isums, N, nb, T, chunk, lds, stream); break;
+    default: launch_quad_gpw<4, F32>(wp, ap, y, isums, N, nb, T, chunk, lds, stream); break;
     }
     return check_launch();
 }
