@@ -22,8 +22,8 @@ namespace bqm {
 
 // Plain product: T columns of a [T][K/32] Q8_1 activation matrix (F32: of
 // a [T][K] fp32 matrix, quantized while staging), y [T][N].
-template <int TC, bool ISUMS, bool F32>
-__global__ __launch_bounds__(256) void mmvq_staged_kernel(const uint8_t *__restrict__ w,
+template <int TC, bool ISUMS, bool F32, int WPG>
+__global__ __launch_bounds__(64 * WPG) void mmvq_staged_kernel(const uint8_t *__restrict__ w,
                                                           const uint8_t *__restrict__ a,
                                                           float *__restrict__ y,
                                                           int32_t *__restrict__ isums, int64_t N,
@@ -31,7 +31,7 @@ __global__ __launch_bounds__(256) void mmvq_staged_kernel(const uint8_t *__restr
 {
     extern __shared__ uint4 act_lds[];
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int64_t row = ((int64_t)blockIdx.x * 4 + wave) * (64 >> lr_log2) + (lane >> lr_log2);
+    const int64_t row = ((int64_t)blockIdx.x * WPG + wave) * (64 >> lr_log2) + (lane >> lr_log2);
     const int nblk = nb * 8;
     const uint32_t col_bytes = F32 ? (uint32_t)nb * kTq1BlockElems * 4 : (uint32_t)nblk * kQ81BlockBytes;
     const __amdgpu_buffer_rsrc_t rw = make_rsrc(w, (uint64_t)N * nb * kTq1BlockBytes);
@@ -44,7 +44,7 @@ __global__ __launch_bounds__(256) void mmvq_staged_kernel(const uint8_t *__restr
         out[t] = ISUMS ? nullptr : y + (int64_t)t * N;
     }
     staged_rows<TC, ISUMS, F32>(rw, ra, col_off, out, isums, reinterpret_cast<uint32_t *>(act_lds),
-                                row, row < N, N, nb, T, lr_log2, chunk);
+                                row, row < N, N, nb, T, lr_log2, chunk, 64 * WPG);
 }
 
 int lanes_per_row_log2(int64_t nb)
@@ -126,20 +126,44 @@ bool staged_supported(int64_t K, int32_t T)
     return staged_chunk(nb, lanes_per_row_log2(nb), T, lds_budget()) > 0;
 }
 
-template <int TC, bool F32>
+template <int TC, bool F32, int WPG>
 static void launch_staged_tc(const uint8_t *w, const uint8_t *a, float *y, int32_t *isums,
-                             int64_t N, int nb, int T, int lr, int chunk, dim3 grid, size_t lds,
+                             int64_t N, int nb, int T, int lr, int chunk, size_t lds,
                              hipStream_t stream)
 {
+    const int64_t rows_per_wg = WPG * (64 >> lr);
+    const dim3 grid((unsigned)((N + rows_per_wg - 1) / rows_per_wg)), block(64 * WPG);
     if (isums && !F32) {
-        allow_dynamic_lds(reinterpret_cast<const void *>(&mmvq_staged_kernel<TC, true, false>), lds);
-        hipLaunchKernelGGL((mmvq_staged_kernel<TC, true, false>), grid, dim3(256), lds, stream, w,
+        allow_dynamic_lds(reinterpret_cast<const void *>(&mmvq_staged_kernel<TC, true, false, WPG>), lds);
+        hipLaunchKernelGGL((mmvq_staged_kernel<TC, true, false, WPG>), grid, block, lds, stream, w,
                            a, nullptr, isums, N, nb, T, lr, chunk);
     } else {
-        allow_dynamic_lds(reinterpret_cast<const void *>(&mmvq_staged_kernel<TC, false, F32>), lds);
-        hipLaunchKernelGGL((mmvq_staged_kernel<TC, false, F32>), grid, dim3(256), lds, stream, w,
+        allow_dynamic_lds(reinterpret_cast<const void *>(&mmvq_staged_kernel<TC, false, F32, WPG>), lds);
+        hipLaunchKernelGGL((mmvq_staged_kernel<TC, false, F32, WPG>), grid, block, lds, stream, w,
                            a, y, nullptr, N, nb, T, lr, chunk);
     }
+}
+
+// Waves per workgroup: eight unless that puts more waves on the busiest SIMD
+// than four do (rounds of workgroups per compute unit times waves per
+// workgroup); eight halve the staging per row.
+static int staged_waves(int64_t N, int lr)
+{
+    const int64_t cu = compute_units(), rows4 = 4 * (64 >> lr);
+    const int64_t r4 = ((N + rows4 - 1) / rows4 + cu - 1) / cu;
+    const int64_t r8 = ((N + 2 * rows4 - 1) / (2 * rows4) + cu - 1) / cu;
+    return 2 * r8 <= r4 ? 8 : 4;
+}
+
+template <int TC, bool F32>
+static void launch_staged_w(const uint8_t *w, const uint8_t *a, float *y, int32_t *isums,
+                            int64_t N, int nb, int T, int lr, int chunk, size_t lds,
+                            hipStream_t stream)
+{
+    if (staged_waves(N, lr) == 8)
+        launch_staged_tc<TC, F32, 8>(w, a, y, isums, N, nb, T, lr, chunk, lds, stream);
+    else
+        launch_staged_tc<TC, F32, 4>(w, a, y, isums, N, nb, T, lr, chunk, lds, stream);
 }
 
 template <bool F32>
@@ -149,20 +173,18 @@ static int launch_staged(const void *w, const void *a, float *y, int32_t *isums,
     const int nb = (int)(K / kTq1BlockElems);
     const int lr = lanes_per_row_log2(nb);
     const int chunk = staged_chunk(nb, lr, T, lds_budget());
-    const int64_t rows_per_wg = 4 * (64 >> lr);
-    const dim3 grid((unsigned)((N + rows_per_wg - 1) / rows_per_wg));
     const size_t lds = (size_t)T * chunk * kActStride * 4;
     const uint8_t *wp = static_cast<const uint8_t *>(w);
     const uint8_t *ap = static_cast<const uint8_t *>(a);
     // column-capacity ladder: a call pays for the next rung up, never for 8
     if (T == 1)
-        launch_staged_tc<1, F32>(wp, ap, y, isums, N, nb, T, lr, chunk, grid, lds, stream);
+        launch_staged_w<1, F32>(wp, ap, y, isums, N, nb, T, lr, chunk, lds, stream);
     else if (T == 2)
-        launch_staged_tc<2, F32>(wp, ap, y, isums, N, nb, T, lr, chunk, grid, lds, stream);
+        launch_staged_w<2, F32>(wp, ap, y, isums, N, nb, T, lr, chunk, lds, stream);
     else if (T <= 4)
-        launch_staged_tc<4, F32>(wp, ap, y, isums, N, nb, T, lr, chunk, grid, lds, stream);
+        launch_staged_w<4, F32>(wp, ap, y, isums, N, nb, T, lr, chunk, lds, stream);
     else
-        launch_staged_tc<8, F32>(wp, ap, y, isums, N, nb, T, lr, chunk, grid, lds, stream);
+        launch_staged_w<8, F32>(wp, ap, y, isums, N, nb, T, lr, chunk, lds, stream);
     return check_launch();
 }
 

@@ -300,14 +300,15 @@ __device__ __forceinline__ void dword_sums_staged(const RawBlock &raw,
 // The rows of one workgroup against T <= TC activation columns. Column t's
 // Q8_1 row (fp32 row when F32: quantized while staging) starts at byte
 // col_off[t] of the activation buffer ra and its outputs go to out[t][row].
-// All 256 threads of the workgroup must call this (it synchronizes); lanes
-// whose row is out of range only help with staging.
+// All nthreads threads of the workgroup (its whole size) must call this (it
+// synchronizes); lanes whose row is out of range only help with staging.
 template <int TC, bool ISUMS, bool F32 = false>
 __device__ __forceinline__ void staged_rows(__amdgpu_buffer_rsrc_t rw, __amdgpu_buffer_rsrc_t ra,
                                             const uint32_t (&col_off)[TC],
                                             float *const (&out)[TC], int32_t *__restrict__ isums,
                                             uint32_t *__restrict__ act, int64_t row, bool row_ok,
-                                            int64_t N, int nb, int T, int lr_log2, int chunk)
+                                            int64_t N, int nb, int T, int lr_log2, int chunk,
+                                            int nthreads = 256)
 {
     const int tid = threadIdx.x, lane = tid & 63;
     const int Lr = 1 << lr_log2;
@@ -337,7 +338,7 @@ __device__ __forceinline__ void staged_rows(__amdgpu_buffer_rsrc_t rw, __amdgpu_
         // moving the loads across each other: it would otherwise sink the
         // batch's loads towards their first use, below the weights'.
         StageBatch<F32> head;
-        stage_load<F32>(head, ra, col_off[0], B0, cb, 0, tid, 256);
+        stage_load<F32>(head, ra, col_off[0], B0, cb, 0, tid, nthreads);
         __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
         RawBlock cur = load_raw_block(rw, row_ok && first < end
                                               ? row_off + (uint32_t)first * kTq1BlockBytes
@@ -346,11 +347,11 @@ __device__ __forceinline__ void staged_rows(__amdgpu_buffer_rsrc_t rw, __amdgpu_
         // and no arithmetic on the batch (with its wait) moves up between
         // the weight loads
         __builtin_amdgcn_sched_barrier(0);
-        stage_column<F32>(act, ra, col_off[0], B0, cb, tid, 256, &head);  // T >= 1
+        stage_column<F32>(act, ra, col_off[0], B0, cb, tid, nthreads, &head);  // T >= 1
 #pragma unroll
         for (int t = 1; t < TC; t++)
             if (t < T)
-                stage_column<F32>(act + t * cb * kActStride, ra, col_off[t], B0, cb, tid, 256,
+                stage_column<F32>(act + t * cb * kActStride, ra, col_off[t], B0, cb, tid, nthreads,
                                   nullptr);
         __syncthreads();
         if (row_ok) {
