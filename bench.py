@@ -434,7 +434,7 @@ def _counter_medians(csv_dir, counter):
                 name = r["Kernel_Name"]
                 fam = ("copy_probe" if "copy_kernel" in name else
                        "read_probe" if "read_kernel" in name else
-                       "fused" if "mmvq_staged_kernel<1, false, true>" in name else
+                       "fused" if "mmvq_staged_kernel<1, false, true, 4>" in name else
                        "mmvq" if "mmvq" in name else None)
                 if fam:
                     vals.setdefault(fam, []).append(float(r["Counter_Value"]))
@@ -452,7 +452,7 @@ def write_counters(fetch_dir, write_dir, probe_bytes):
     write_scale = probe_bytes / w["copy_probe"]
     wl_N, wl_K = 4096, 4096
     out = {"kernel_source_hash": kernel_source_hash(), "shape": [wl_N, wl_K, 1],
-           "kernel": "mmvq_staged_kernel<1, false, true> (mmvq_tq1_0_f32)",
+           "kernel": "mmvq_staged_kernel<1, false, true, 4> (mmvq_tq1_0_f32)",
            "fetch_size_kib": f["fused"], "write_size_kib": w["fused"],
            "copy_probe_bytes": probe_bytes, "copy_probe_fetch_kib": f["copy_probe"],
            "copy_probe_write_kib": w["copy_probe"],
@@ -601,7 +601,7 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic_from_counters(N, K, T),
-                     "kernel": "mmvq_tq1_0_f32 (mmvq_staged_kernel<1, false, true>)",
+                     "kernel": "mmvq_tq1_0_f32 (mmvq_staged_kernel<1, false, true, 4>)",
                      "algorithmic_bytes_per_launch": step_bytes},
         "calibration": cal,
         "cpu_baseline": base,
