@@ -17,7 +17,7 @@
  *  [P1-acc] same page, section "Acceptance criteria": MUL_MAT_ID at ne11 = 1
  *       (one activation per token, broadcast over its expert slots).
  *
- * Readings where the pages are silent (each is also listed in the design doc):
+ * Readings where the pages are silent:
  *  - block = 54 bytes: qs[48] at 0, qh[4] at 48, fp16 d (little endian) at 52;
  *    byte value v = sum_c u_c * 3^c with digit u_c in {0,1,2} and trit
  *    t = u_c - 1 (digit 0 is the least significant);
