@@ -251,10 +251,12 @@ def test_mmvq_columns_equal_single_column_calls(bqm, N, K, T):
 # input): two staging passes (65536 at three columns, 32768 at four), rows of
 # 9 and 17 blocks (slots without a block; two groups per lane), 56 and 256
 # blocks (four groups per lane), a last wave past N; workgroups of eight
-# waves (14330 rows: the last one partly past N) and of four
+# waves (14330 rows: the last one partly past N) and of four; one and five
+# rows (a workgroup almost wholly past N)
 @pytest.mark.parametrize("N,K,T", [(64, 65536, 3), (77, 32768, 4), (333, 2304, 4),
                                    (1000, 4352, 3), (515, 14336, 4), (4100, 4096, 4),
-                                   (14330, 2304, 3), (14330, 6144, 4)])
+                                   (14330, 2304, 3), (14330, 6144, 4), (1, 4096, 3),
+                                   (5, 2304, 4)])
 def test_mmvq_quad_shapes(bqm, N, K, T):
     """Exact integer sums, fp32 within tolerance of the oracle, every column
     bitwise its one-column call, and the fp32-input call bitwise equal."""
@@ -532,7 +534,7 @@ def test_mm_prefill_workload(bqm):
                                    (40, 16384, 1), (17, 8192, 7), (9, 8448, 6),
                                    (77, 32768, 7), (64, 65536, 5), (4100, 4096, 8),
                                    (14330, 4096, 8), (14330, 2304, 5), (14330, 4096, 1),
-                                   (12345, 6144, 2)])
+                                   (12345, 6144, 2), (1, 4096, 6), (3, 2560, 8)])
 def test_mmvq_f32_equals_quantize_then_mmvq(bqm, N, K, T):
     trits, d16, x = _case(N, K, T, seed=N * 7 + K + T)
     w, a, w_ref, a_ref = _prep(bqm, trits, d16, x)
