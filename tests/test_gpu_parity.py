@@ -534,7 +534,8 @@ def test_mm_prefill_workload(bqm):
                                    (40, 16384, 1), (17, 8192, 7), (9, 8448, 6),
                                    (77, 32768, 7), (64, 65536, 5), (4100, 4096, 8),
                                    (14330, 4096, 8), (14330, 2304, 5), (14330, 4096, 1),
-                                   (12345, 6144, 2), (1, 4096, 6), (3, 2560, 8)])
+                                   (12345, 6144, 2), (1, 4096, 6), (3, 2560, 8),
+                                   (70, 2048, 6), (33, 1024, 8)])
 def test_mmvq_f32_equals_quantize_then_mmvq(bqm, N, K, T):
     trits, d16, x = _case(N, K, T, seed=N * 7 + K + T)
     w, a, w_ref, a_ref = _prep(bqm, trits, d16, x)
