@@ -183,13 +183,15 @@ __device__ __forceinline__ void rows_product(const uint8_t *__restrict__ w, uint
     }
 }
 
-// Whether a call of T < kMfmaMinCols columns takes the staged kernel. From
-// three columns on it does so only when its grid gives the device more than
-// one wave per SIMD: with one block per lane and no second wave to overlap
-// it, the multi-column work after the weights arrive outlasts the
-// matrix-core kernel's (4096 x 4096: 5.6 against 5.3 us at three columns,
-// 6.2 against 5.5 at four; at 5120 x 6144 and 14336 x 4096, with more waves,
-// the staged kernel is as fast or faster).
+// Whether a call of T < kMfmaMinCols columns that the quad kernel does not
+// take (rows of at most 8 blocks, from three columns) goes to the staged
+// kernel. From three columns on it does so only when its grid gives the
+// device more than one wave per SIMD: with one block per lane and no second
+// wave to overlap it, the multi-column work after the weights arrive
+// outlasts the matrix-core kernel's (measured on 4096 x 4096 with the two
+// kernels alone: 5.6 against 5.3 us at three columns, 6.2 against 5.5 at
+// four; at 5120 x 6144 and 14336 x 4096, with more waves, the staged kernel
+// is as fast or faster).
 static bool use_staged(int64_t N, int64_t K, int32_t T)
 {
     if (T >= kMfmaMinCols || !staged_supported(K, T))
