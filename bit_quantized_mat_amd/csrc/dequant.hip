@@ -96,9 +96,15 @@ __device__ __forceinline__ uint32_t digit_level(uint32_t w, int c, bool qh)
 
 // Blocks per wave, the loads of all of them issued before any decode: fp32
 // 8; fp16 and bf16 16 on large calls (more bytes per wave to cover its HBM
-// round trip), 8 below kDqLargeBlocks blocks (more waves).
+// round trip), and fewer, for more waves, on smaller ones: 8 below
+// kDqLargeBlocks blocks, 4 below kDqMidBlocks, 2 below kDqSmallBlocks
+// (row gathers from a 14336 x 4096 matrix: 64 rows 3.54 -> 2.23 us, 256 rows
+// 3.96 -> 2.63 us, 1024 rows 5.80 -> 4.91 us, 2048 rows 7.85 -> 7.08 us; at
+// 3072 rows eight blocks per wave stay faster, 8.9 against 9.8 us).
 constexpr int kDqBlocksPerWave = 8;
 constexpr int64_t kDqLargeBlocks = 65536;
+constexpr int64_t kDqMidBlocks = 40960;
+constexpr int64_t kDqSmallBlocks = 8192;
 
 // fp16 and bf16 output: lane L of a wave takes elements 8 (L mod 32) .. +7 of
 // block 2 k + L / 32 of its step k, a 16-byte store; a wave's store covers two
@@ -258,22 +264,30 @@ int launch_tq1_dequantize(const void *w, const int32_t *rows, void *out, int64_t
 {
     const int nb = (int)(K / kTq1BlockElems);
     const uint8_t *wp = static_cast<const uint8_t *>(w);
-    const bool large = n_rows * nb >= kDqLargeBlocks;
+    const int64_t blocks = n_rows * nb;
     if (dtype == BQM_DTYPE_F32) {
         const int64_t waves = (n_rows * nb + kDqBlocksPerWave - 1) / kDqBlocksPerWave;
         const dim3 grid((unsigned)((waves * 64 + 255) / 256));
         hipLaunchKernelGGL(tq1_dequantize_f32_kernel, grid, dim3(256), 0, stream, wp, rows, out, N,
                            nb, n_rows);
     } else if (dtype == BQM_DTYPE_F16) {
-        if (large)
+        if (blocks >= kDqLargeBlocks)
             launch_half<BQM_DTYPE_F16, 16>(wp, rows, out, N, nb, n_rows, stream);
-        else
+        else if (blocks >= kDqMidBlocks)
             launch_half<BQM_DTYPE_F16, 8>(wp, rows, out, N, nb, n_rows, stream);
-    } else {
-        if (large)
-            launch_half<BQM_DTYPE_BF16, 16>(wp, rows, out, N, nb, n_rows, stream);
+        else if (blocks >= kDqSmallBlocks)
+            launch_half<BQM_DTYPE_F16, 4>(wp, rows, out, N, nb, n_rows, stream);
         else
+            launch_half<BQM_DTYPE_F16, 2>(wp, rows, out, N, nb, n_rows, stream);
+    } else {
+        if (blocks >= kDqLargeBlocks)
+            launch_half<BQM_DTYPE_BF16, 16>(wp, rows, out, N, nb, n_rows, stream);
+        else if (blocks >= kDqMidBlocks)
             launch_half<BQM_DTYPE_BF16, 8>(wp, rows, out, N, nb, n_rows, stream);
+        else if (blocks >= kDqSmallBlocks)
+            launch_half<BQM_DTYPE_BF16, 4>(wp, rows, out, N, nb, n_rows, stream);
+        else
+            launch_half<BQM_DTYPE_BF16, 2>(wp, rows, out, N, nb, n_rows, stream);
     }
     return check_launch();
 }

@@ -583,10 +583,11 @@ def _dq_bits(t):
     return t.view(torch.int16).cpu().numpy().view(np.uint16)
 
 
-# (4100, 4096): 65,600 blocks, the large-call path of the 16-bit outputs (16
-# blocks per wave) with a partial last wave; its gather takes 8,203 rows
+# 16-bit outputs take 2, 4, 8 or 16 blocks per wave by size: 1161 blocks
+# (129 x 2304), 20800 (1300 x 4096), 49600 (3100 x 4096), 65600 (4100 x 4096:
+# the large-call path with a partial last wave; its gather takes 8,203 rows)
 @pytest.mark.parametrize("N,K", [(1, 256), (3, 768), (70, 4096), (129, 2304), (16, 16384),
-                                 (4100, 4096)])
+                                 (4100, 4096), (1300, 4096), (3100, 4096)])
 @pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
 def test_tq1_dequantize_bit_exact(bqm, N, K, dtype):
     import torch
