@@ -94,13 +94,14 @@ __device__ __forceinline__ uint32_t digit_level(uint32_t w, int c, bool qh)
     return f_c - mul3_bytes(f_n);
 }
 
-// Blocks per wave, the loads of all of them issued before any decode: fp32
-// 8; fp16 and bf16 16 on large calls (more bytes per wave to cover its HBM
-// round trip), and fewer, for more waves, on smaller ones: 8 below
-// kDqLargeBlocks blocks, 4 below kDqMidBlocks, 2 below kDqSmallBlocks
-// (row gathers from a 14336 x 4096 matrix: 64 rows 3.54 -> 2.23 us, 256 rows
-// 3.96 -> 2.63 us, 1024 rows 5.80 -> 4.91 us, 2048 rows 7.85 -> 7.08 us; at
-// 3072 rows eight blocks per wave stay faster, 8.9 against 9.8 us).
+// Blocks per wave, the loads of all of them issued before any decode: fp16
+// and bf16 16 on large calls (more bytes per wave to cover its HBM round
+// trip); fewer, for more waves, on smaller calls of every type: 8 below
+// kDqLargeBlocks blocks (fp32: from kDqMidBlocks up), 4 below kDqMidBlocks,
+// 2 below kDqSmallBlocks (fp16 row gathers from a 14336 x 4096 matrix: 64
+// rows 3.54 -> 2.23 us, 256 rows 3.96 -> 2.63 us, 1024 rows 5.80 -> 4.91 us,
+// 2048 rows 7.85 -> 7.08 us; at 3072 rows eight blocks per wave stay faster,
+// 8.9 against 9.8 us).
 constexpr int kDqBlocksPerWave = 8;
 constexpr int64_t kDqLargeBlocks = 65536;
 constexpr int64_t kDqMidBlocks = 40960;
@@ -190,6 +191,7 @@ __global__ __launch_bounds__(256) void tq1_dequantize_kernel(const uint8_t *__re
 
 // fp32 output: one wave per block, lane L writing elements 4L..4L+3 (one
 // 16-byte store per lane, a wave's store 1 KiB of consecutive outputs).
+template <int BPW>
 __global__ __launch_bounds__(256) void tq1_dequantize_f32_kernel(const uint8_t *__restrict__ w,
                                                                  const int32_t *__restrict__ rows,
                                                                  void *__restrict__ out, int64_t N,
@@ -200,7 +202,7 @@ __global__ __launch_bounds__(256) void tq1_dequantize_f32_kernel(const uint8_t *
     const int64_t wave = (int64_t)blockIdx.x * (blockDim.x >> 6) +
                          __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int64_t nblocks = n_rows * nb;
-    const int64_t first = wave * kDqBlocksPerWave;
+    const int64_t first = wave * BPW;
     if (first >= nblocks)
         return;  // whole waves
     // this lane's elements 4L..4L+3 of every block: their dword and digit level
@@ -219,10 +221,10 @@ __global__ __launch_bounds__(256) void tq1_dequantize_f32_kernel(const uint8_t *
     const __amdgpu_buffer_rsrc_t rw = make_rsrc(w, (uint64_t)N * nb * kTq1BlockBytes);
     int64_t i = first / nb;
     int B = (int)(first - i * nb);
-    u32x2 v[kDqBlocksPerWave];
-    uint32_t dd[kDqBlocksPerWave], sh[kDqBlocksPerWave];
+    u32x2 v[BPW];
+    uint32_t dd[BPW], sh[BPW];
 #pragma unroll
-    for (int k = 0; k < kDqBlocksPerWave; k++) {
+    for (int k = 0; k < BPW; k++) {
         // blocks past the end reload the last one (their stores are skipped)
         const int64_t ic = first + k < nblocks ? i : n_rows - 1;
         const int Bc = first + k < nblocks ? B : nb - 1;
@@ -239,7 +241,7 @@ __global__ __launch_bounds__(256) void tq1_dequantize_f32_kernel(const uint8_t *
         }
     }
 #pragma unroll
-    for (int k = 0; k < kDqBlocksPerWave; k++) {
+    for (int k = 0; k < BPW; k++) {
         if (first + k < nblocks) {
             const uint32_t d16 = sh[k] ? (dd[k] >> 16) : (dd[k] & 0xffffu);
             const float d = f16_bits_to_f32(d16);
@@ -259,6 +261,16 @@ static void launch_half(const uint8_t *w, const int32_t *rows, void *out, int64_
                        N, nb, n_rows);
 }
 
+template <int BPW>
+static void launch_f32(const uint8_t *w, const int32_t *rows, void *out, int64_t N, int nb,
+                       int64_t n_rows, hipStream_t stream)
+{
+    const int64_t waves = (n_rows * nb + BPW - 1) / BPW;
+    const dim3 grid((unsigned)((waves * 64 + 255) / 256));
+    hipLaunchKernelGGL((tq1_dequantize_f32_kernel<BPW>), grid, dim3(256), 0, stream, w, rows, out,
+                       N, nb, n_rows);
+}
+
 int launch_tq1_dequantize(const void *w, const int32_t *rows, void *out, int64_t N, int64_t K,
                           int64_t n_rows, int dtype, hipStream_t stream)
 {
@@ -266,10 +278,12 @@ int launch_tq1_dequantize(const void *w, const int32_t *rows, void *out, int64_t
     const uint8_t *wp = static_cast<const uint8_t *>(w);
     const int64_t blocks = n_rows * nb;
     if (dtype == BQM_DTYPE_F32) {
-        const int64_t waves = (n_rows * nb + kDqBlocksPerWave - 1) / kDqBlocksPerWave;
-        const dim3 grid((unsigned)((waves * 64 + 255) / 256));
-        hipLaunchKernelGGL(tq1_dequantize_f32_kernel, grid, dim3(256), 0, stream, wp, rows, out, N,
-                           nb, n_rows);
+        if (blocks >= kDqMidBlocks)
+            launch_f32<kDqBlocksPerWave>(wp, rows, out, N, nb, n_rows, stream);
+        else if (blocks >= kDqSmallBlocks)
+            launch_f32<4>(wp, rows, out, N, nb, n_rows, stream);
+        else
+            launch_f32<2>(wp, rows, out, N, nb, n_rows, stream);
     } else if (dtype == BQM_DTYPE_F16) {
         if (blocks >= kDqLargeBlocks)
             launch_half<BQM_DTYPE_F16, 16>(wp, rows, out, N, nb, n_rows, stream);
