@@ -140,25 +140,123 @@ def rotation(torch, w0, dev, extra=1):
     return wrot, R
 
 
-def cpu_baseline(inp, N, K, T, step_bytes, seconds):
+def host_cpu_info():
+    """What the oracle runs on: the CPU model, the logical CPUs the host
+    reports, the CPUs this process may run on, and the OpenMP thread cap the
+    job was given (the share of the host that goes with one GPU)."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for ln in f:
+                if ln.startswith("model name"):
+                    model = ln.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        affinity = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        affinity = None
+    return {"cpu_model": model, "nproc": os.cpu_count(), "affinity_cpus": affinity,
+            "omp_num_threads_env": os.environ.get("OMP_NUM_THREADS")}
+
+
+def oracle_threads_all():
+    """Threads for the all-cores oracle run: every CPU this process may use,
+    capped by OMP_NUM_THREADS when the job sets it (a GPU machine grants each GPU
+    a fixed share of its host CPUs and sets OMP_NUM_THREADS to that share)."""
+    info = host_cpu_info()
+    n = info["affinity_cpus"] or info["nproc"] or 1
+    env = info["omp_num_threads_env"]
+    if env and env.isdigit() and int(env) > 0:
+        n = min(n, int(env))
+    return max(1, n)
+
+
+def oracle_median_us(fn, runs=5):
+    """Median wall time (us) of fn over `runs` calls after one warm-up call."""
+    import statistics
+    fn()
+    ts = []
+    for _ in range(runs):
+        t0 = time.perf_counter()
+        fn()
+        ts.append((time.perf_counter() - t0) * 1e6)
+    return statistics.median(ts)
+
+
+def cpu_baseline(inp, N, K, T, seconds):
+    """The oracle's mat-vec on the decode workload, timed apart from its
+    quantization (median of 5 after 1 warm-up, more runs to fill about
+    `seconds` of CPU work): on all the job's host CPUs and on one thread."""
     import oracle
-    threads = max(1, min(16, os.cpu_count() or 1))
-    oracle.set_threads(threads)
+    info = host_cpu_info()
+    threads = oracle_threads_all()
     w_ref = oracle.tq1_pack(inp.trits, inp.d16)
     x = inp.x[:T]
-    n = 0
-    t0 = time.perf_counter()
-    while True:
-        a = oracle.q8_1_quantize(x)
-        oracle.mmvq(w_ref, a, N, K, T)
-        n += 1
-        el = time.perf_counter() - t0
-        if el >= seconds:
-            break
-    return {"value": round(step_bytes * n / el / 1e9, 4), "unit": "GB/s", "cores": threads,
-            "kind": "oracle",
-            "sample": "%d full decode steps (Q8_1 quantize + %dx%d mat-vec, T=%d) in %.1f s; "
-                      "%.1f ms per step" % (n, N, K, T, el, 1e3 * el / n)}
+    a = oracle.q8_1_quantize(x)
+    out = {}
+    for label, nt in (("all", threads), ("one", 1)):
+        oracle.set_threads(nt)
+        t0 = time.perf_counter()
+        one = oracle_median_us(lambda: oracle.mmvq(w_ref, a, N, K, T), runs=1)
+        runs = int(max(5, min(200, 0.5 * seconds * 1e6 / max(one, 1.0))))
+        mm_us = oracle_median_us(lambda: oracle.mmvq(w_ref, a, N, K, T), runs=runs)
+        q_us = oracle_median_us(lambda: oracle.q8_1_quantize(x), runs=runs)
+        out[label] = {"threads": nt, "mmvq_us": round(mm_us, 1), "quantize_us": round(q_us, 1),
+                      "runs": runs, "seconds": round(time.perf_counter() - t0, 1)}
+    oracle.set_threads(threads)
+    mm_bytes = algorithmic_bytes(N, K, T)
+    base = {"value": round(mm_bytes / out["all"]["mmvq_us"] / 1e3, 4), "unit": "GB/s",
+            "cores": threads, "kind": "oracle",
+            "sample": "the oracle's %dx%d T=%d mat-vec alone (its Q8_1 quantization timed "
+                      "apart), median of %d runs after one warm-up on %d threads: %.1f us; on "
+                      "one thread %.1f us; quantize %.1f us (%d threads), %.1f us (one)"
+                      % (N, K, T, out["all"]["runs"], threads, out["all"]["mmvq_us"],
+                         out["one"]["mmvq_us"], out["all"]["quantize_us"], threads,
+                         out["one"]["quantize_us"]),
+            "single_thread_gbs": round(mm_bytes / out["one"]["mmvq_us"] / 1e3, 4),
+            "runs": out}
+    base.update(info)
+    return base
+
+
+def cpu_table(path):
+    """The oracle on every workload shape and column count (no GPU): median
+    of 3 runs after one warm-up, on one thread and on all the job's CPUs;
+    mat-vec and expert-routed product timed apart from quantization."""
+    import numpy as np
+    import oracle
+    from bit_quantized_mat_amd import synth
+    info = host_cpu_info()
+    threads = oracle_threads_all()
+    rows = []
+    for name in ("tiny", "decode", "multicol", "ffn", "moe"):
+        wl = synth.WORKLOADS[name]
+        inp = synth.make_inputs(wl)
+        w_ref = oracle.tq1_pack(inp.trits, inp.d16)
+        a_all = oracle.q8_1_quantize(inp.x)
+        for T in wl.Ts:
+            a = np.ascontiguousarray(a_all[:T])
+            row = {"workload": name, "T": T, "N": wl.N, "K": wl.K}
+            for label, nt in (("one", 1), ("all", threads)):
+                oracle.set_threads(nt)
+                if wl.experts:
+                    ids = np.ascontiguousarray(inp.ids[:T])
+                    fn = lambda: oracle.mmvq_id(w_ref, a, ids, wl.experts, wl.N, wl.K, T,
+                                                wl.n_used)
+                else:
+                    fn = lambda: oracle.mmvq(w_ref, a, wl.N, wl.K, T)
+                row["oracle_us_" + label] = round(oracle_median_us(fn, runs=3), 1)
+                row["quantize_us_" + label] = round(oracle_median_us(
+                    lambda: oracle.q8_1_quantize(inp.x[:T]), runs=3), 1)
+            row["threads_all"] = threads
+            rows.append(row)
+            log("cpu", row)
+    oracle.set_threads(threads)
+    with open(path, "w") as f:
+        json.dump({"host": info, "rows": rows}, f, indent=1)
+    return rows
 
 
 def calibrate(torch, np, wrot, R, nbytes, grid_wg):
@@ -179,7 +277,35 @@ def calibrate(torch, np, wrot, R, nbytes, grid_wg):
         cal["read_%d_wg_gbs" % g] = round(rd / us / 1e3, 1)
     cal["read_bytes"] = int(rd)
     cal["mmvq_grid_wg"] = int(grid_wg)
+    cal.update(valu_rates(torch, probes))
     return {k: (round(v, 4) if isinstance(v, float) else v) for k, v in cal.items()}
+
+
+# 256 compute units x 4 SIMDs x 16 lanes x 2.4 GHz: one 32-bit vector
+# instruction per lane per cycle at full rate (a wave of 64 lanes issues over
+# four cycles on its 16-lane SIMD)
+VALU_PEAK_LANE_OPS = 256 * 64 * 2.4e9
+
+
+def valu_rates(torch, probes):
+    """Vector-ALU issue rate of the instruction kinds the decode is made of:
+    lane operations per second of long independent chains of one kind
+    (8192 waves, 8 per SIMD), and the fraction of the 256 CU x 64 lanes x
+    2.4 GHz figure."""
+    probes.bqm_probe_valu.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_int,
+                                      ctypes.c_void_p]
+    grid, iters = 2048, 2048
+    out = torch.empty(grid * 256, dtype=torch.int32, device="cuda")
+    cur = lambda: ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    res = {}
+    for kind, name in enumerate(("dot4_i32_i8", "mad_u32_u24", "pk_mul_lo_u16", "perm_b32")):
+        us = graph_us(torch, lambda i: probes.bqm_probe_valu(kind, iters, ctypes.c_void_p(
+            out.data_ptr()), grid, cur()), 5)
+        lane_ops = grid * 4 * 32 * iters * 64.0
+        rate = lane_ops / (us * 1e-6)
+        res["valu_%s_lane_ops_per_s" % name] = float("%.4g" % rate)
+        res["valu_%s_frac" % name] = round(rate / VALU_PEAK_LANE_OPS, 4)
+    return res
 
 
 def read_probe_row(torch, wrot, R, nbytes, name, launches):
@@ -486,7 +612,14 @@ def main():
     ap.add_argument("--write-counters", nargs=3, metavar=("FETCH_DIR", "WRITE_DIR", "PROBE_BYTES"),
                     help="no GPU: turn two rocprofv3 --pmc runs of --profile decode:1 "
                          "(FETCH_SIZE, then WRITE_SIZE) into the committed traffic figures")
+    ap.add_argument("--cpu-table", metavar="PATH",
+                    help="no GPU: time the oracle on every workload (one thread and all the "
+                         "job's CPUs) and write a JSON table")
     args = ap.parse_args()
+
+    if args.cpu_table:
+        cpu_table(args.cpu_table)
+        return
 
     if args.write_counters:
         write_counters(args.write_counters[0], args.write_counters[1],
@@ -572,7 +705,7 @@ def main():
 
     base = None
     if not args.no_cpu_baseline:
-        base = cpu_baseline(inp, N, K, T, step_bytes, args.cpu_seconds)
+        base = cpu_baseline(inp, N, K, T, args.cpu_seconds)
         log("cpu baseline:", base)
 
     line = {

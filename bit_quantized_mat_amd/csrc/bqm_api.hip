@@ -2,6 +2,8 @@
 // the host, one dispatch point per entry, launches on the caller's stream.
 #include <string.h>
 
+#include <atomic>
+
 #include "launch.hpp"
 
 namespace {
@@ -14,17 +16,22 @@ bool aligned4(const void *p) { return ((uintptr_t)p & 3u) == 0; }
 // Device check, cached per device ordinal: gfx950 only.
 int check_device()
 {
-    static int cached[64];  // 0 unknown, 1 ok, -1 not gfx950 (benign race: idempotent)
+    // 0 unknown, 1 ok, -1 not gfx950; atomics, so concurrent first calls
+    // from several host threads each store the same value without a race
+    static std::atomic<int> cached[64];
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0)
         return BQM_ERR_DEVICE;
-    if (dev < 64 && cached[dev])
-        return cached[dev] > 0 ? BQM_OK : BQM_ERR_DEVICE;
+    if (dev < 64) {
+        const int c = cached[dev].load(std::memory_order_relaxed);
+        if (c)
+            return c > 0 ? BQM_OK : BQM_ERR_DEVICE;
+    }
     hipDeviceProp_t prop;
     int ok = hipGetDeviceProperties(&prop, dev) == hipSuccess &&
              strncmp(prop.gcnArchName, "gfx950", 6) == 0;
     if (dev < 64)
-        cached[dev] = ok ? 1 : -1;
+        cached[dev].store(ok ? 1 : -1, std::memory_order_relaxed);
     return ok ? BQM_OK : BQM_ERR_DEVICE;
 }
 

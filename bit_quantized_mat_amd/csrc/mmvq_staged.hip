@@ -16,6 +16,9 @@
 // up to 128 blocks, transposed so that dword j of all eight sub-blocks of a
 // 256-element block sits together, and precomputes each sub-block's fp32
 // scale and -sum(q). Every row of the workgroup reuses the staged copy.
+#include <atomic>
+#include <mutex>
+
 #include "mmvq_staged.hpp"
 
 namespace bqm {
@@ -57,64 +60,81 @@ int lanes_per_row_log2(int64_t nb)
     return l;
 }
 
+// Host-side caches of this file. Each is safe to use from several host
+// threads at once: the per-device attribute caches are arrays of atomics
+// (a value is computed by whichever thread first asks and every thread
+// computes the same value), and the occupancy cache sits behind a mutex.
 size_t lds_budget()
 {
     // dynamic LDS per workgroup this device allows, cached per device
-    static size_t cached[64];
+    static std::atomic<size_t> cached[64];
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64)
         return kLdsDefault;
-    if (!cached[dev]) {
-        int v = 0;
-        if (hipDeviceGetAttribute(&v, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess ||
-            v <= 0)
-            v = (int)kLdsDefault;
-        cached[dev] = (size_t)v < kLdsMax ? (size_t)v : kLdsMax;
+    size_t v = cached[dev].load(std::memory_order_relaxed);
+    if (!v) {
+        int a = 0;
+        if (hipDeviceGetAttribute(&a, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess ||
+            a <= 0)
+            a = (int)kLdsDefault;
+        v = (size_t)a < kLdsMax ? (size_t)a : kLdsMax;
+        cached[dev].store(v, std::memory_order_relaxed);
     }
-    return cached[dev];
+    return v;
 }
 
 int compute_units()
 {
     // compute units of the current device, cached per device
-    static int cached[64];
+    static std::atomic<int> cached[64];
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64)
         return 256;
-    if (!cached[dev]) {
-        int v = 0;
+    int v = cached[dev].load(std::memory_order_relaxed);
+    if (!v) {
         if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
             v <= 0)
             v = 256;
-        cached[dev] = v;
+        cached[dev].store(v, std::memory_order_relaxed);
     }
-    return cached[dev];
+    return v;
 }
 
 int resident_workgroups(const void *kernel, int threads, size_t lds)
 {
-    // workgroups of this kernel the whole device holds at once; remembered for
-    // the last few (kernel, shape, device) triples asked about
+    // workgroups of this kernel the whole device holds at once; remembered
+    // for every (kernel, block size, dynamic LDS, device) asked about. The
+    // library launches a fixed set of kernels at a handful of block sizes and
+    // LDS sizes per kernel, so the table stays small; past kMaxEntries (never
+    // reached by the launchers here) further queries are answered uncached.
     struct Entry {
         const void *kernel;
         int threads, dev;
         size_t lds;
         int count;
     };
-    static Entry cache[32];
-    static int next;
+    constexpr int kMaxEntries = 256;
+    static std::mutex mu;
+    static Entry cache[kMaxEntries];
+    static int used;
     int dev = 0;
     (void)hipGetDevice(&dev);
-    for (const Entry &e : cache)
-        if (e.kernel == kernel && e.threads == threads && e.lds == lds && e.dev == dev && e.count > 0)
-            return e.count;
+    {
+        std::lock_guard<std::mutex> lock(mu);
+        for (int i = 0; i < used; i++) {
+            const Entry &e = cache[i];
+            if (e.kernel == kernel && e.threads == threads && e.lds == lds && e.dev == dev)
+                return e.count;
+        }
+    }
     int per_cu = 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, threads, lds) != hipSuccess ||
         per_cu < 1)
         per_cu = 1;
     const int count = per_cu * compute_units();
-    cache[next] = Entry{kernel, threads, dev, lds, count};
-    next = (next + 1) % 32;
+    std::lock_guard<std::mutex> lock(mu);
+    if (used < kMaxEntries)
+        cache[used++] = Entry{kernel, threads, dev, lds, count};
     return count;
 }
 

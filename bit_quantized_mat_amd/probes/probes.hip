@@ -6,6 +6,9 @@
 // same grid can reach on the same number of bytes. bqm_probe_copy: copies a
 // buffer with 16-byte loads and stores, a transfer of known size against which
 // the memory counters (bytes fetched from and written to HBM) are scaled.
+// bqm_probe_valu: long chains of one vector ALU instruction kind per lane, for
+// the device's vector-ALU issue rate (lane operations per second) on the
+// instruction kinds the TQ1_0 decode is made of.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -40,6 +43,55 @@ __global__ __launch_bounds__(256) void copy_kernel(const uint4 *__restrict__ src
         dst[i] = src[i];
 }
 
+// Eight independent dependency chains per lane, four steps of each per loop
+// iteration: 32 instructions of the chosen kind per iteration and wave (the
+// loop counter lives in scalar registers). Kinds: 0 v_dot4_i32_i8, 1
+// v_mad_u32_u24, 2 v_pk_mul_lo_u16, 3 v_perm_b32.
+typedef unsigned short probe_u16x2 __attribute__((ext_vector_type(2)));
+
+template <int KIND>
+__device__ __forceinline__ uint32_t valu_step(uint32_t a, uint32_t b)
+{
+    if (KIND == 0)
+        return (uint32_t)__builtin_amdgcn_sdot4((int)a, (int)b, (int)a, false);
+    if (KIND == 1)
+        return __umul24(a, 0x9e37u) + b;
+    if (KIND == 2) {
+        probe_u16x2 x = __builtin_bit_cast(probe_u16x2, a), y = __builtin_bit_cast(probe_u16x2, b);
+        return __builtin_bit_cast(uint32_t, (probe_u16x2)(x * y));
+    }
+    return __builtin_amdgcn_perm(a, b, 0x07050301u);
+}
+
+template <int KIND>
+__global__ __launch_bounds__(256) void valu_kernel(int iters, uint32_t seed,
+                                                   uint32_t *__restrict__ out)
+{
+    const uint32_t t = blockIdx.x * blockDim.x + threadIdx.x;
+    uint32_t a[8], b[8];
+#pragma unroll
+    for (int k = 0; k < 8; k++) {
+        a[k] = seed ^ (t * 2654435761u + 97u * k);
+        b[k] = seed + 0x01010101u * (k + 1) + t;
+    }
+    for (int i = 0; i < iters; i++) {
+#pragma unroll
+        for (int u = 0; u < 4; u++)
+#pragma unroll
+            for (int k = 0; k < 8; k++) {
+                a[k] = valu_step<KIND>(a[k], b[k]);
+                // an empty statement that keeps each step one instruction: the
+                // compiler would otherwise merge consecutive steps algebraically
+                asm volatile("" : "+v"(a[k]));
+            }
+    }
+    uint32_t x = 0;
+#pragma unroll
+    for (int k = 0; k < 8; k++)
+        x ^= a[k];
+    out[t] = x;
+}
+
 }  // namespace
 
 extern "C" {
@@ -71,6 +123,23 @@ __attribute__((visibility("default"))) int bqm_probe_copy(const void *src, void 
         return -2;
     hipLaunchKernelGGL(copy_kernel, dim3(grid), dim3(256), 0, (hipStream_t)stream,
                        (const uint4 *)src, (uint4 *)dst, bytes / 16);
+    return hipGetLastError() == hipSuccess ? 0 : -5;
+}
+
+// out: device buffer of grid * 256 dwords. Each wave issues 32 * iters
+// instructions of the kind chosen (0 dot4, 1 mad_u24, 2 pk_mul_lo_u16, 3 perm).
+__attribute__((visibility("default"))) int bqm_probe_valu(int kind, int iters, uint32_t *out,
+                                                          int grid, void *stream)
+{
+    if (!out || grid < 1 || iters < 1 || kind < 0 || kind > 3)
+        return -2;
+    const dim3 g(grid), b(256);
+    switch (kind) {
+    case 0: hipLaunchKernelGGL(valu_kernel<0>, g, b, 0, (hipStream_t)stream, iters, 12345u, out); break;
+    case 1: hipLaunchKernelGGL(valu_kernel<1>, g, b, 0, (hipStream_t)stream, iters, 12345u, out); break;
+    case 2: hipLaunchKernelGGL(valu_kernel<2>, g, b, 0, (hipStream_t)stream, iters, 12345u, out); break;
+    default: hipLaunchKernelGGL(valu_kernel<3>, g, b, 0, (hipStream_t)stream, iters, 12345u, out); break;
+    }
     return hipGetLastError() == hipSuccess ? 0 : -5;
 }
 

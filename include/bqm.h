@@ -34,9 +34,18 @@
  *
  * Common contract:
  *   - All buffer pointers are DEVICE pointers owned by the caller; the library
- *     never allocates, frees or synchronizes, holds no mutable global state,
- *     and enqueues work only on `stream` (a hipStream_t; NULL = the null
- *     stream). Calls are asynchronous; outputs are fully overwritten.
+ *     never allocates, frees or synchronizes, and enqueues work only on
+ *     `stream` (a hipStream_t; NULL = the null stream). Calls are
+ *     asynchronous; outputs are fully overwritten.
+ *   - Host state: the library keeps only caches of facts about devices and
+ *     kernels, filled on first use and never invalidated: per device ordinal
+ *     (up to 64), whether it is a gfx950 GPU, its compute-unit count and its
+ *     per-workgroup LDS limit (arrays of atomics); and, per (kernel, block
+ *     size, LDS size, device), how many workgroups the device holds at once
+ *     (a table behind a mutex). Every thread that fills an entry computes the
+ *     same value, so calls from several host threads at once are safe. The
+ *     launchers also raise a kernel's dynamic-LDS limit through the runtime
+ *     (hipFuncSetAttribute, idempotent). There is no other global state.
  *   - Inputs must not alias outputs.
  *   - Arguments are validated on the host before anything is enqueued; on an
  *     error nothing is enqueued and nothing is written.
@@ -82,7 +91,11 @@ enum {
 /* Largest number of activation columns mmvq_tq1_0 accepts. */
 #define BQM_MMVQ_MAX_COLS 32
 
-/* Pack ternary weights into TQ1_0 blocks.
+/* Pack ternary weights into TQ1_0 blocks: the inverse of the element map
+ * above. "CUDA: TQ1_0 mat-vec is load-bound by the per-32-element chunk
+ * contract", "Current behavior": five base-3 trits per qs byte, the qs bytes
+ * read digit by digit in 32-element chunks, four trits per qh byte, one fp16
+ * scale per 256-element block.
  *   trits [N][K] int8, values -1, 0, +1, row-major.
  *   d     [N][K/256] fp16 bit patterns (uint16), the block scales.
  *   w     [N][K/256] x 54 bytes, output.
@@ -90,13 +103,21 @@ enum {
 BQM_API int tq1_pack(const int8_t *trits, const uint16_t *d, void *w,
              int64_t N, int64_t K, void *stream);
 
-/* Quantize activations to Q8_1.
+/* Quantize activations to Q8_1: the activation blocks the mat-vec consumes
+ * ("CUDA: TQ1_0 mat-vec is load-bound by the per-32-element chunk contract",
+ * "Current behavior": the vec_dot reads Q8_1 blocks of 32 activations, each
+ * with its own scale), with the scale rule and rounding stated above.
  *   x [T][K] fp32, row-major (column t of the product is row t of x).
  *   a [T][K/32] x 36 bytes, output.
  * Shapes: T >= 1, K >= 32, K % 32 == 0. Alignment: x 4 bytes, a 4 bytes. */
 BQM_API int q8_1_quantize(const float *x, void *a, int64_t T, int64_t K, void *stream);
 
-/* Quantized mat-vec / small-batch product:
+/* Quantized mat-vec / small-batch product ("CUDA: TQ1_0 mat-vec is
+ * load-bound by the per-32-element chunk contract", "Current behavior" and
+ * "Proposed approach": the blockwise product of TQ1_0 rows and Q8_1 columns,
+ * computed by a kernel that reads each packed byte once; several columns per
+ * call as in "cuda: opt-in MMVQ activation reuse across output rows", each
+ * column's result bitwise that of a one-column call):
  *   y[t][n] = sum_{j < K/32} fp32(d_w[n][j/8]) * fp32(d_a[t][j]) * isum[t][n][j]
  *   isum[t][n][j] = sum_{i < 32} trit[n][32j+i] * q[t][32j+i]   (exact int32)
  *   w [N][K/256] TQ1_0 blocks; a [T][K/32] Q8_1 blocks; y [T][N] fp32 output.
@@ -110,7 +131,7 @@ BQM_API int mmvq_tq1_0(const void *w, const void *a, float *y,
 /* Largest number of activation columns mm_tq1_0 accepts. */
 #define BQM_MM_MAX_COLS 65536
 
-/* Many-column product (prefill-sized batches; row f2 beside the decode
+/* Many-column product (prefill-sized batches; the step beside the decode
  * product: the pages' pp512 workload, "CUDA: TQ1_0 mat-vec is load-bound by
  * the per-32-element chunk contract", "Measured impact"): the same
  *   y[t][n] = sum_j fp32(d_w[n][j/8]) * fp32(d_a[t][j]) * isum[t][n][j]
@@ -157,7 +178,12 @@ BQM_API int mmvq_tq1_0_f32(const void *w, const float *x, float *y,
 BQM_API int tq1_dequantize(const void *w, const int32_t *rows, void *out,
                    int64_t N, int64_t K, int64_t n_rows, int32_t out_dtype, void *stream);
 
-/* Expert-routed product (mixture of experts):
+/* Expert-routed product (mixture of experts; MUL_MAT_ID of "CUDA: TQ1_0
+ * mat-vec is load-bound by the per-32-element chunk contract", "Acceptance
+ * criteria": one activation per token (ne11 = 1), more than one block per
+ * row, fewer experts used than available; the per-expert grouping of tokens
+ * is the ids compaction of "tools: add mmq-tune, an MMQ tile-width autotuning
+ * harness", "Summary"):
  *   y[t][s][n] = mmvq(W[ids[t][s]], a[t])[n]   for t < T, s < n_used
  *   w   [E][N][K/256] TQ1_0 blocks (expert-major, each expert an N x K matrix).
  *   a   [T][K/32] Q8_1 blocks, one activation per token shared by its slots.

@@ -24,13 +24,78 @@ def _say(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+class _SentinelOutputs:
+    """The binding with every output buffer pre-filled with a sentinel that
+    no correct result holds: NaN for fp32 outputs, INT32_MIN for integer sums
+    (|isum| <= 4064), 0xFF bytes for packed weights (255 is not a valid qs or
+    qh byte) and for Q8_1 blocks and dequantized rows (0xFFFF is a NaN in
+    fp16 and bf16). An output a kernel leaves unwritten then fails the
+    comparison instead of passing on whatever the allocator left there."""
+
+    def __init__(self, m):
+        self._m = m
+
+    def __getattr__(self, name):
+        return getattr(self._m, name)
+
+    @staticmethod
+    def _full(shape, dtype, value, device):
+        return torch.full(shape, value, dtype=dtype, device=device)
+
+    def tq1_pack(self, trits, d16, **kw):
+        N, K = trits.shape
+        kw.setdefault("out", self._full((N, K // 256 * 54), torch.uint8, 255, trits.device))
+        return self._m.tq1_pack(trits, d16, **kw)
+
+    def q8_1_quantize(self, x, **kw):
+        T, K = x.shape
+        kw.setdefault("out", self._full((T, K // 32 * 36), torch.uint8, 255, x.device))
+        return self._m.q8_1_quantize(x, **kw)
+
+    def _y(self, shape, dev):
+        return self._full(shape, torch.float32, float("nan"), dev)
+
+    def mmvq_tq1_0(self, w, a, N, K, T, **kw):
+        kw.setdefault("out", self._y((T, N), w.device))
+        return self._m.mmvq_tq1_0(w, a, N, K, T, **kw)
+
+    def mm_tq1_0(self, w, a, N, K, T, **kw):
+        kw.setdefault("out", self._y((T, N), w.device))
+        return self._m.mm_tq1_0(w, a, N, K, T, **kw)
+
+    def mmvq_tq1_0_f32(self, w, x, N, K, T, **kw):
+        kw.setdefault("out", self._y((T, N), w.device))
+        return self._m.mmvq_tq1_0_f32(w, x, N, K, T, **kw)
+
+    def mmvq_tq1_0_block_isums(self, w, a, N, K, T, **kw):
+        kw.setdefault("out", self._full((T, N, K // 32), torch.int32, -2 ** 31, w.device))
+        return self._m.mmvq_tq1_0_block_isums(w, a, N, K, T, **kw)
+
+    def mmvq_id_tq1_0(self, w, a, ids, E, N, K, T, n_used, **kw):
+        kw.setdefault("out", self._y((T, n_used, N), w.device))
+        return self._m.mmvq_id_tq1_0(w, a, ids, E, N, K, T, n_used, **kw)
+
+    def mmvq_id_tq1_0_slots(self, w, a, ids, E, N, K, T, n_used, **kw):
+        kw.setdefault("out", self._y((T, n_used, N), w.device))
+        return self._m.mmvq_id_tq1_0_slots(w, a, ids, E, N, K, T, n_used, **kw)
+
+    def tq1_dequantize(self, w, N, K, rows=None, dtype=None, **kw):
+        dt = torch.float16 if dtype is None else dtype
+        n_rows = N if rows is None else rows.numel()
+        if "out" not in kw:
+            out = torch.empty((n_rows, K), dtype=dt, device=w.device)
+            out.view(torch.uint8).fill_(255)
+            kw["out"] = out
+        return self._m.tq1_dequantize(w, N, K, rows=rows, dtype=dtype, **kw)
+
+
 @pytest.fixture(scope="module")
 def bqm():
     if not torch.cuda.is_available():
         pytest.skip("no GPU")
     import bit_quantized_mat_amd as m
     m.library()
-    return m
+    return _SentinelOutputs(m)
 
 
 def _dev(a):
@@ -43,9 +108,16 @@ def _host(t):
 
 
 def _assert_close(y, y64, ab, what):
+    """|y - y64| <= 1e-5 * sum|terms| everywhere; NaN or an unwritten
+    (sentinel) output fails, since the comparison is written so that a NaN
+    error never counts as within the bound."""
+    assert y.shape == y64.shape == ab.shape, what
+    assert np.all(np.isfinite(y64)) and np.all(np.isfinite(ab)), what
+    n_bad_finite = int((~np.isfinite(y)).sum())
+    assert n_bad_finite == 0, "%s: %d outputs are NaN or infinite" % (what, n_bad_finite)
     err = np.abs(y.astype(np.float64) - y64)
     bound = REL_TOL * ab
-    bad = err > bound
+    bad = ~(err <= bound)
     zero = ab == 0
     assert np.all(y[zero] == 0), what
     if bad.any():
@@ -71,10 +143,14 @@ def _case(N, K, T, seed, p_zero=1 / 3, outliers=0.01, d_lo=0.01, d_hi=0.1):
 # (67 x 768); otherwise the matrix-core kernel, with the activations resident
 # in LDS when they fit and a row has at least as many lane groups as the
 # workgroup has waves, else streamed per block)
+# The last four put the one- and two-column staged kernel on rows longer than
+# one staging pass (more than 64 blocks: passes of 64 below 128 blocks, of
+# 128 from there): 65 blocks (a one-block last pass), 96 (a partial second
+# pass), 129 (two full passes of 128 and a one-block tail) and 256.
 SHAPES = [(256, 1024, 1), (1, 256, 1), (33, 256, 2), (67, 768, 3), (130, 2304, 5),
           (515, 4096, 8), (96, 6144, 4), (40, 16384, 1), (17, 1280, 32), (300, 512, 16),
           (40, 16384, 6), (50, 9216, 5), (21, 4096, 17), (1, 2304, 9), (4500, 4096, 3),
-          (4200, 2560, 4)]
+          (4200, 2560, 4), (50, 16640, 1), (33, 24576, 2), (300, 33024, 1), (70, 65536, 2)]
 
 
 # ---------------------------------------------------------------------------
@@ -434,37 +510,67 @@ def test_mmvq_id_slots_parity(bqm, E, N, K, T, n_used, seed):
             assert np.array_equal(y1[0], y[t, s])
 
 
-def test_workload_moe_parity(bqm):
+@pytest.fixture(scope="module")
+def moe_workload(bqm):
+    """The 128-expert MoE workload, packed and quantized once (on the GPU and
+    by the oracle, compared byte for byte), with both activation sets."""
     wl, inp = _workload_inputs("moe")
-    E, N, K, n_used = wl.experts, wl.N, wl.K, wl.n_used
-    w, a_all, w_ref, a_ref_all = _prep(bqm, inp.trits, inp.d16, inp.x)
-    for T in wl.Ts:
-        _say("workload moe", T)
-        ids = inp.ids[:T]
-        y = _host(bqm.mmvq_id_tq1_0(w, a_all[:T].contiguous(), _dev(ids), E, N, K, T, n_used))
-        # oracle on a sample of tokens (rows of y are independent per token)
-        ts = sorted(set([0, T - 1, T // 2]))
-        for t in ts:
-            _, y64, ab = oracle.mmvq_id(w_ref, a_ref_all[t:t + 1], ids[t:t + 1], E, N, K, 1, n_used)
-            _assert_close(y[t:t + 1], y64, ab, "moe T=%d token %d" % (T, t))
-
-
-def test_workload_moe_slots_parity(bqm):
-    """The MoE workload with one activation per (token, slot) pair."""
-    wl, inp = _workload_inputs("moe")
-    E, N, K, n_used = wl.experts, wl.N, wl.K, wl.n_used
     xs = synth.slot_activations(wl)
-    w, a_all, w_ref, a_ref_all = _prep(bqm, inp.trits, inp.d16, xs)
-    for T in wl.Ts:
-        _say("workload moe slots", T)
-        ids = inp.ids[:T]
-        y = _host(bqm.mmvq_id_tq1_0_slots(w, a_all[:T * n_used].contiguous(), _dev(ids),
-                                          E, N, K, T, n_used))
-        for t in sorted(set([0, T - 1, T // 2])):
-            cols = a_ref_all[t * n_used:(t + 1) * n_used]
-            _, y64, ab = oracle.mmvq_id(w_ref, cols, ids[t:t + 1], E, N, K, 1, n_used,
-                                        per_slot=True)
-            _assert_close(y[t:t + 1], y64, ab, "moe slots T=%d token %d" % (T, t))
+    w, a_tok, w_ref, a_tok_ref = _prep(bqm, inp.trits, inp.d16, inp.x)
+    a_slot = bqm.q8_1_quantize(_dev(xs))
+    a_slot_ref = oracle.q8_1_quantize(xs)
+    assert np.array_equal(_host(a_slot), a_slot_ref)
+    return wl, inp, w, w_ref, a_tok, a_tok_ref, a_slot, a_slot_ref
+
+
+@pytest.mark.parametrize("T", [1, 8, 64])
+def test_workload_moe_parity(bqm, moe_workload, T):
+    """Every output of the MoE workload (T tokens x 8 slots x 1536 rows)
+    against the oracle: the routing inside the wave at T = 1 and 8, the
+    pre-pass with narrow and matrix-core items at T = 64."""
+    wl, inp, w, w_ref, a_all, a_ref_all, _, _ = moe_workload
+    E, N, K, n_used = wl.experts, wl.N, wl.K, wl.n_used
+    _say("workload moe", T)
+    ids = inp.ids[:T]
+    y = _host(bqm.mmvq_id_tq1_0(w, a_all[:T].contiguous(), _dev(ids), E, N, K, T, n_used))
+    _, y64, ab = oracle.mmvq_id(w_ref, a_ref_all[:T], ids, E, N, K, T, n_used)
+    _assert_close(y, y64, ab, "moe T=%d" % T)
+
+
+@pytest.mark.parametrize("T", [1, 8, 64])
+def test_workload_moe_slots_parity(bqm, moe_workload, T):
+    """The MoE workload with one activation per (token, slot) pair: every
+    output against the oracle."""
+    wl, inp, w, w_ref, _, _, a_all, a_ref_all = moe_workload
+    E, N, K, n_used = wl.experts, wl.N, wl.K, wl.n_used
+    _say("workload moe slots", T)
+    ids = inp.ids[:T]
+    y = _host(bqm.mmvq_id_tq1_0_slots(w, a_all[:T * n_used].contiguous(), _dev(ids),
+                                      E, N, K, T, n_used))
+    _, y64, ab = oracle.mmvq_id(w_ref, a_ref_all[:T * n_used], ids, E, N, K, T, n_used,
+                                per_slot=True)
+    _assert_close(y, y64, ab, "moe slots T=%d" % T)
+
+
+def test_workload_moe_slots_equal_plain_calls(bqm, moe_workload):
+    """At 8 tokens (64 pairs, routed inside the wave), every (token, slot)
+    output of both expert-routed calls is bitwise the plain one-column
+    product of its expert's matrix on its own column."""
+    wl, inp, w, _, a_tok, _, a_slot, _ = moe_workload
+    E, N, K, n_used, T = wl.experts, wl.N, wl.K, wl.n_used, 8
+    ids = inp.ids[:T]
+    y_tok = _host(bqm.mmvq_id_tq1_0(w, a_tok[:T].contiguous(), _dev(ids), E, N, K, T, n_used))
+    y_slot = _host(bqm.mmvq_id_tq1_0_slots(w, a_slot[:T * n_used].contiguous(), _dev(ids),
+                                           E, N, K, T, n_used))
+    wr = w.view(E, N, -1)
+    for t in range(T):
+        for s in range(n_used):
+            we = wr[ids[t, s]].clone()
+            y1 = _host(bqm.mmvq_tq1_0(we, a_tok[t:t + 1].clone(), N, K, 1))
+            assert np.array_equal(y1[0].view(np.uint32), y_tok[t, s].view(np.uint32)), (t, s)
+            p = t * n_used + s
+            y1 = _host(bqm.mmvq_tq1_0(we, a_slot[p:p + 1].clone(), N, K, 1))
+            assert np.array_equal(y1[0].view(np.uint32), y_slot[t, s].view(np.uint32)), (t, s)
 
 
 # ---------------------------------------------------------------------------
@@ -511,7 +617,7 @@ def test_mm_stream_kernel(bqm):
 
 
 def test_mm_prefill_workload(bqm):
-    """The ffn matrix against 512 columns (a prefill batch), sampled columns
+    """The ffn matrix against 512 columns (a prefill batch): every output
     against the oracle."""
     wl = synth.WORKLOADS["ffn"]
     inp = synth.make_inputs(wl, T=512)
@@ -519,9 +625,8 @@ def test_mm_prefill_workload(bqm):
     w, a, w_ref, a_ref = _prep(bqm, inp.trits, inp.d16, inp.x)
     _say("mm prefill", N, K, T)
     y = _host(bqm.mm_tq1_0(w, a, N, K, T))
-    for t in (0, 255, 511):
-        _, y64, ab = oracle.mmvq(w_ref, a_ref[t:t + 1], N, K, 1)
-        _assert_close(y[t:t + 1], y64, ab, "prefill column %d" % t)
+    _, y64, ab = oracle.mmvq(w_ref, a_ref, N, K, T)
+    _assert_close(y, y64, ab, "prefill")
 
 
 # ---------------------------------------------------------------------------
@@ -535,7 +640,8 @@ def test_mm_prefill_workload(bqm):
                                    (77, 32768, 7), (64, 65536, 5), (4100, 4096, 8),
                                    (14330, 4096, 8), (14330, 2304, 5), (14330, 4096, 1),
                                    (12345, 6144, 2), (1, 4096, 6), (3, 2560, 8),
-                                   (70, 2048, 6), (33, 1024, 8)])
+                                   (70, 2048, 6), (33, 1024, 8), (50, 16640, 1),
+                                   (33, 24576, 2), (300, 33024, 1), (70, 65536, 2)])
 def test_mmvq_f32_equals_quantize_then_mmvq(bqm, N, K, T):
     trits, d16, x = _case(N, K, T, seed=N * 7 + K + T)
     w, a, w_ref, a_ref = _prep(bqm, trits, d16, x)
@@ -558,9 +664,51 @@ def test_mmvq_f32_quantization_edge_blocks(bqm):
     trits = synth.ternary(rng, (N, K))
     d16 = synth.block_scales_f16(rng, (N, K // 256), 0.01, 0.1)
     w, a, w_ref, a_ref = _prep(bqm, trits, d16, x)
-    y2 = _host(bqm.mmvq_tq1_0(w, a, N, K, T))
-    y1 = _host(bqm.mmvq_tq1_0_f32(w, _dev(x), N, K, T))
-    assert np.array_equal(y1.view(np.uint32), y2.view(np.uint32))
+    _, y64, ab = oracle.mmvq(w_ref, a_ref, N, K, T)
+    for t0 in range(0, T, 8):
+        # the fused entry point takes up to 8 columns; the plain product all
+        t1 = min(T, t0 + 8)
+        y2 = _host(bqm.mmvq_tq1_0(w, a[t0:t1].contiguous(), N, K, t1 - t0))
+        y1 = _host(bqm.mmvq_tq1_0_f32(w, _dev(x[t0:t1]), N, K, t1 - t0))
+        assert np.array_equal(y1.view(np.uint32), y2.view(np.uint32))
+        _assert_close(y2, y64[t0:t1], ab[t0:t1], "edge activations, columns %d..%d" % (t0, t1))
+    # and all columns in one plain call (the matrix-core kernel)
+    yall = _host(bqm.mmvq_tq1_0(w, a, N, K, T))
+    _assert_close(yall, y64, ab, "edge activations, %d columns" % T)
+
+
+def _odd_weight_scales(rng, shape):
+    """fp16 block scales mixing positive and negative normal values, positive
+    and negative subnormals (0x0001 .. 0x03ff), and signed zeros."""
+    n = int(np.prod(shape))
+    kind = rng.integers(0, 5, n)
+    mag = np.where(kind < 2, rng.integers(0x1400, 0x2e66, n),        # normal, ~0.001 .. 0.1
+                   np.where(kind < 4, rng.integers(1, 0x400, n), 0))  # subnormal / zero
+    sign = rng.integers(0, 2, n) << 15
+    return (mag | sign).astype(np.uint16).reshape(shape)
+
+
+# one shape per kernel: staged (one, two and three columns), quad (four),
+# resident matrix-core (8 and 32), streamed matrix-core (K too long to keep
+# five columns resident), staged multi-pass
+@pytest.mark.parametrize("N,K,T", [(256, 1024, 1), (70, 2304, 2), (4500, 4096, 3),
+                                   (333, 2304, 4), (515, 4096, 8), (17, 1280, 32),
+                                   (50, 9216, 5), (50, 16640, 1)])
+def test_mmvq_negative_and_subnormal_weight_scales(bqm, N, K, T):
+    """Negative, fp16-subnormal and zero weight scales: against the oracle,
+    and the fused call (up to 8 columns) bitwise the two-call path."""
+    rng = np.random.default_rng(8800 + N + T)
+    trits = synth.ternary(rng, (N, K))
+    d16 = _odd_weight_scales(rng, (N, K // 256))
+    x = synth.activations(rng, T, K, outlier_frac=0.01)
+    w, a, w_ref, a_ref = _prep(bqm, trits, d16, x)
+    _say("odd weight scales", N, K, T)
+    y = _host(bqm.mmvq_tq1_0(w, a, N, K, T))
+    _, y64, ab = oracle.mmvq(w_ref, a_ref, N, K, T)
+    _assert_close(y, y64, ab, "odd scales %dx%d T=%d" % (N, K, T))
+    if T <= 8:
+        yf = _host(bqm.mmvq_tq1_0_f32(w, _dev(x), N, K, T))
+        assert np.array_equal(yf.view(np.uint32), y.view(np.uint32))
 
 
 def test_mmvq_f32_decode_workload(bqm):
