@@ -14,6 +14,7 @@ __all__ = [
     "MM_MAX_COLS",
     "mmvq_tq1_0_f32", "MMVQ_F32_MAX_COLS", "tq1_dequantize",
     "mmvq_id_tq1_0", "mmvq_id_tq1_0_slots", "mmvq_id_tq1_0_workspace_bytes",
+    "mmvq_id_tq1_0_noalloc", "NOALLOC_SCRATCH_BYTES",
     "mmvq_tq1_0_block_isums",
     "TQ1_BLOCK_BYTES", "Q81_BLOCK_BYTES", "MMVQ_MAX_COLS",
 ]
@@ -23,6 +24,7 @@ Q81_BLOCK_BYTES = 36
 MMVQ_MAX_COLS = 32
 MMVQ_F32_MAX_COLS = 8
 MM_MAX_COLS = 65536
+NOALLOC_SCRATCH_BYTES = 768 * 1024
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _lib = None
@@ -61,6 +63,7 @@ def library():
         L.mmvq_tq1_0_block_isums.argtypes = [_p, _p, _p, _i64, _i64, _i32, _p]
         L.mmvq_id_tq1_0.argtypes = [_p, _p, _p, _p, _i64, _i64, _i64, _i64, _i32, _p, _sz, _p]
         L.mmvq_id_tq1_0_slots.argtypes = L.mmvq_id_tq1_0.argtypes
+        L.mmvq_id_tq1_0_noalloc.argtypes = [_p, _p, _p, _p, _i64, _i64, _i64, _i64, _i32, _p]
         L.mmvq_id_tq1_0_workspace_bytes.argtypes = [_i64, _i64, _i32]
         L.mmvq_id_tq1_0_workspace_bytes.restype = _sz
         L.bqm_status_string.argtypes = [ctypes.c_int]
@@ -68,7 +71,7 @@ def library():
         L.bqm_version.restype = ctypes.c_int
         for name in ("tq1_pack", "q8_1_quantize", "mmvq_tq1_0", "mm_tq1_0", "mmvq_tq1_0_f32",
                      "mmvq_tq1_0_block_isums", "mmvq_id_tq1_0", "mmvq_id_tq1_0_slots",
-                     "tq1_dequantize"):
+                     "mmvq_id_tq1_0_noalloc", "tq1_dequantize"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -248,3 +251,19 @@ def mmvq_id_tq1_0_slots(w, a, ids, E, N, K, T, n_used, out=None, workspace=None,
     activation (a: [T * n_used, K/32] Q8_1 blocks)."""
     return _mmvq_id("mmvq_id_tq1_0_slots", T * n_used, w, a, ids, E, N, K, T, n_used, out,
                     workspace, stream)
+
+
+def mmvq_id_tq1_0_noalloc(w, a, ids, E, N, K, T, n_used, out=None, stream=None):
+    """mmvq_id_tq1_0 with the library's own device scratch instead of a
+    workspace: the call allocates nothing (``out`` is allocated here only if
+    it is not given)."""
+    torch = _torch()
+    if out is None:
+        out = torch.empty((T, n_used, N), dtype=torch.float32, device=w.device)
+    _call("mmvq_id_tq1_0_noalloc",
+          _dev_tensor(w, "w", (torch.uint8,), E * N * (K // 256) * TQ1_BLOCK_BYTES),
+          _dev_tensor(a, "a", (torch.uint8,), T * (K // 32) * Q81_BLOCK_BYTES, w.device),
+          _dev_tensor(ids, "ids", (torch.int32,), T * n_used * 4, w.device),
+          _dev_tensor(out, "out", (torch.float32,), T * n_used * N * 4, w.device),
+          E, N, K, T, n_used, _stream(stream, w.device))
+    return out

@@ -207,6 +207,32 @@ int mmvq_id_tq1_0(const void *w, const void *a, const int32_t *ids, float *y, in
                         stream);
 }
 
+int mmvq_id_tq1_0_noalloc(const void *w, const void *a, const int32_t *ids, float *y, int64_t E,
+                          int64_t N, int64_t K, int64_t T, int32_t n_used, void *stream)
+{
+    // the same checks as mmvq_id_tq1_0, except that the workspace is the
+    // library's device scratch
+    if (!w || !a || !ids || !y)
+        return BQM_ERR_NULL;
+    if (E < 1 || T < 1 || n_used < 1 || n_used > E || T * (int64_t)n_used > 65535)
+        return BQM_ERR_SHAPE;
+    if (int rc = check_matrix(N, K))
+        return rc;
+    if ((uint64_t)T * (uint64_t)(K / 32) * 36ull > kMaxBufferBytes)
+        return BQM_ERR_SHAPE;
+    if (!aligned4(w) || !aligned4(a) || !aligned4(ids) || !aligned4(y))
+        return BQM_ERR_ALIGN;
+    if (bqm::mmvq_id_workspace_bytes(E, T, n_used) > bqm::kNoAllocScratchBytes)
+        return BQM_ERR_WORKSPACE;
+    if (int rc = check_device())
+        return rc;
+    void *scratch = nullptr;
+    if (int rc = bqm::noalloc_scratch(&scratch))
+        return rc;
+    return bqm::launch_mmvq_id(w, a, ids, y, E, N, K, T, n_used, false, scratch,
+                               as_stream(stream));
+}
+
 int mmvq_id_tq1_0_slots(const void *w, const void *a, const int32_t *ids, float *y, int64_t E,
                         int64_t N, int64_t K, int64_t T, int32_t n_used, void *workspace,
                         size_t workspace_bytes, void *stream)

@@ -101,6 +101,13 @@ int launch_mmvq_id(const void *w, const void *a, const int32_t *ids, float *y, i
                    int64_t N, int64_t K, int64_t T, int32_t n_used, bool per_slot,
                    void *workspace, hipStream_t stream);
 size_t mmvq_id_workspace_bytes(int64_t E, int64_t T, int32_t n_used);
+// Size of the device-resident scratch of mmvq_id_tq1_0_noalloc: at least the
+// workspace of the largest call mmvq_id_tq1_0 accepts that uses one (4096
+// experts, 65535 pairs: 729,344 bytes).
+constexpr size_t kNoAllocScratchBytes = 768 * 1024;
+// Device address of that scratch on the current device (looked up on the
+// first call per device, then cached).
+int noalloc_scratch(void **ptr);
 int launch_mmvq_id_pairs(const void *w, const void *a, const int32_t *ids, float *y, int64_t E,
                          int64_t N, int64_t K, int64_t T, int32_t n_used, int pairs_per_col,
                          hipStream_t stream);

@@ -26,6 +26,8 @@
 // items grows. Each column's arithmetic does not depend on which other columns
 // share the item, nor on the rows a workgroup walks, so results are bitwise
 // those of a plain one-column call on the expert.
+#include <atomic>
+
 #include "launch.hpp"
 #include "mmvq_staged.hpp"
 
@@ -518,6 +520,32 @@ int launch_mmvq_id(const void *w, const void *a, const int32_t *ids, float *y, i
     const int64_t max_wide = wide_experts + P / kWideCols;
     return launch_mmvq_mfma_resident_id(w, a, y, N, K, P / pairs_per_col, routed, (int)max_items,
                                         (int)max_wide, pairs_per_col, stream);
+}
+
+// ---------------------------------------------------------------------------
+// Device scratch of the allocation-free expert-routed entry point: the
+// routing pre-pass's workspace, held in a file-scope device array that each
+// GPU the library runs on keeps until the process ends. Host code never
+// passes the array's name to a kernel (on the host it names a stand-in, not
+// device memory): the entry point looks up the array's device address once
+// per device, with that device current, and passes that address.
+// ---------------------------------------------------------------------------
+static __device__ __align__(256) uint8_t scratch[kNoAllocScratchBytes];
+
+int noalloc_scratch(void **ptr)
+{
+    static std::atomic<void *> addr[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64)
+        return BQM_ERR_DEVICE;
+    void *p = addr[dev].load(std::memory_order_acquire);
+    if (!p) {
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p)
+            return BQM_ERR_LAUNCH;
+        addr[dev].store(p, std::memory_order_release);
+    }
+    *ptr = p;
+    return BQM_OK;
 }
 
 }  // namespace bqm

@@ -222,6 +222,27 @@ BQM_API int mmvq_id_tq1_0_slots(const void *w, const void *a, const int32_t *ids
                         int64_t E, int64_t N, int64_t K, int64_t T, int32_t n_used,
                         void *workspace, size_t workspace_bytes, void *stream);
 
+/* mmvq_id_tq1_0 without a workspace argument, for callers that cannot
+ * allocate device memory (code under graph capture, tight serving loops,
+ * harnesses that forbid allocation). The call itself allocates nothing: the
+ * routing pre-pass writes its work items to a device array the library holds
+ * (BQM_NOALLOC_SCRATCH_BYTES per GPU it runs on, kept until the process
+ * ends; its device address is looked up on the first call per device).
+ * Every shape mmvq_id_tq1_0 accepts fits that array (the largest workspace,
+ * 4096 experts and 65535 pairs, is 729,344 bytes); a shape whose workspace
+ * would not fit returns BQM_ERR_WORKSPACE before anything is enqueued.
+ * Arguments, shapes, alignment, other errors and results (bitwise) as
+ * mmvq_id_tq1_0. The array is shared by every call on one GPU and keeps the
+ * last call's contents; the pre-pass writes every entry the product kernels
+ * read, so nothing has to start at zero. Calls on one GPU that overlap in
+ * time (on different streams, or from host threads whose streams are not
+ * ordered) race on the array and must not be issued: order them on one
+ * stream. */
+#define BQM_NOALLOC_SCRATCH_BYTES (768 * 1024)
+BQM_API int mmvq_id_tq1_0_noalloc(const void *w, const void *a, const int32_t *ids, float *y,
+                          int64_t E, int64_t N, int64_t K, int64_t T, int32_t n_used,
+                          void *stream);
+
 /* Workspace size mmvq_id_tq1_0 and mmvq_id_tq1_0_slots need for these sizes
  * (may be 0). */
 BQM_API size_t mmvq_id_tq1_0_workspace_bytes(int64_t E, int64_t T, int32_t n_used);

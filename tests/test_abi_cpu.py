@@ -217,3 +217,30 @@ def test_binding_raises_without_gpu_tensors():
     import torch
     with pytest.raises(TypeError):
         bqm.mmvq_tq1_0(torch.zeros(54, dtype=torch.uint8), torch.zeros(36, dtype=torch.uint8), 1, 256, 1)
+
+
+def test_mmvq_id_noalloc_rejects():
+    # the allocation-free expert-routed call validates like mmvq_id_tq1_0
+    # (every call below fails before touching the device), and every shape it
+    # accepts has a workspace no larger than its device scratch
+    lib = bqm.library()
+    base = [GOOD, GOOD, GOOD, GOOD, 8, 16, 256, 4, 2, None]
+
+    def call(**kw):
+        args = list(base)
+        names = ["w", "a", "ids", "y", "E", "N", "K", "T", "n_used", "s"]
+        for k, v in kw.items():
+            args[names.index(k)] = v
+        return lib.mmvq_id_tq1_0_noalloc(*args)
+
+    assert call(w=None) == -1 and call(a=None) == -1 and call(ids=None) == -1
+    assert call(y=None) == -1
+    assert call(E=0) == -2 and call(n_used=0) == -2 and call(n_used=9) == -2
+    assert call(T=0) == -2 and call(K=100) == -2 and call(N=0) == -2
+    assert call(T=40000, n_used=2) == -2
+    assert call(K=1 << 24, T=300, n_used=1) == -2          # activations past 4 GiB
+    assert call(w=ODD) == -3 and call(ids=ODD) == -3 and call(y=ODD) == -3
+    worst = max(lib.mmvq_id_tq1_0_workspace_bytes(E, 65535 // n, n)
+                for E in (1, 64, 4095, 4096) for n in (1, 2, 8, 64) if n <= E)
+    assert worst == 729344
+    assert worst <= bqm.NOALLOC_SCRATCH_BYTES == 768 * 1024
