@@ -654,6 +654,7 @@ def main():
     x = torch.from_numpy(inp.x[:T]).to(dev)
     a = torch.empty((T, (K // 32) * 36), dtype=torch.uint8, device=dev)
     y = torch.empty((T, N), dtype=torch.float32, device=dev)
+    a_y = torch.empty((T, N), dtype=torch.float32, device=dev)
     torch.cuda.synchronize()
     log("rotation: %d copies of %d bytes (%.2f GiB)" % (R, wbytes, R * wbytes / 2**30))
 
@@ -683,6 +684,15 @@ def main():
     mmvq_us = graph_us(torch, lambda i: bqm.mmvq_tq1_0(wrot[(7 * i) % R], a, N, K, T, out=y),
                        args.kernel_launches)
     quant_us = graph_us(torch, lambda i: bqm.q8_1_quantize(x, out=a), 200)
+    # the residual-block form of the step: quantize, multiply and add the
+    # residual in one launch, against the same with the add as a second launch
+    resid = torch.randn((T, N), dtype=torch.float32, device=dev)
+    add_fused_us = graph_us(torch, lambda i: bqm.mmvq_tq1_0_f32_add(
+        wrot[(7 * i) % R], x, resid, N, K, T, out=y), args.kernel_launches)
+    add_two_us = graph_us(torch, lambda i: (bqm.mmvq_tq1_0_f32(wrot[(7 * i) % R], x, N, K, T,
+                                                               out=a_y),
+                                            torch.add(a_y, resid, out=y)),
+                          args.kernel_launches)
     grid_wg = -(-N // (4 * (64 >> lanes_per_row_log2(K // 256))))
     cal = calibrate(torch, np, wrot, R, wbytes, grid_wg)
     log("calibration:", cal)
@@ -695,6 +705,8 @@ def main():
     log("two calls: %.3f us (quantize %.3f us, mat-vec %.3f us = %.1f GB/s)"
         % (two_call_us, quant_us, mmvq_us, algorithmic_bytes(N, K, T) / mmvq_us / 1e3))
     log("step: %.3f us graph-replayed, %.3f us eager" % (step_us, eager_us))
+    log("with a residual: %.3f us fused (quantize + mat-vec + add, one launch), %.3f us as "
+        "mat-vec then a separate add" % (add_fused_us, add_two_us))
 
     table = None
     if args.sweep:
@@ -731,6 +743,8 @@ def main():
         "mmvq_gbs": round(algorithmic_bytes(N, K, T) / mmvq_us / 1e3, 2),
         "quantize_us": round(quant_us, 4),
         "us_per_step_eager": round(eager_us, 4),
+        "residual_add_fused_us": round(add_fused_us, 4),
+        "residual_add_two_launch_us": round(add_two_us, 4),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic_from_counters(N, K, T),

@@ -12,7 +12,8 @@ import os
 __all__ = [
     "BqmError", "library", "library_path", "tq1_pack", "q8_1_quantize", "mmvq_tq1_0", "mm_tq1_0",
     "MM_MAX_COLS",
-    "mmvq_tq1_0_f32", "MMVQ_F32_MAX_COLS", "tq1_dequantize",
+    "mmvq_tq1_0_f32", "MMVQ_F32_MAX_COLS", "tq1_dequantize", "mmvq_tq1_0_add",
+    "mmvq_tq1_0_f32_add",
     "mmvq_id_tq1_0", "mmvq_id_tq1_0_slots", "mmvq_id_tq1_0_workspace_bytes",
     "mmvq_id_tq1_0_noalloc", "NOALLOC_SCRATCH_BYTES",
     "mmvq_tq1_0_block_isums",
@@ -58,6 +59,8 @@ def library():
         L.q8_1_quantize.argtypes = [_p, _p, _i64, _i64, _p]
         L.mmvq_tq1_0.argtypes = [_p, _p, _p, _i64, _i64, _i32, _p]
         L.mmvq_tq1_0_f32.argtypes = [_p, _p, _p, _i64, _i64, _i32, _p]
+        L.mmvq_tq1_0_add.argtypes = [_p, _p, _p, _p, _i64, _i64, _i32, _p]
+        L.mmvq_tq1_0_f32_add.argtypes = [_p, _p, _p, _p, _i64, _i64, _i32, _p]
         L.mm_tq1_0.argtypes = [_p, _p, _p, _i64, _i64, _i64, _p]
         L.tq1_dequantize.argtypes = [_p, _p, _p, _i64, _i64, _i64, _i32, _p]
         L.mmvq_tq1_0_block_isums.argtypes = [_p, _p, _p, _i64, _i64, _i32, _p]
@@ -70,6 +73,7 @@ def library():
         L.bqm_status_string.restype = ctypes.c_char_p
         L.bqm_version.restype = ctypes.c_int
         for name in ("tq1_pack", "q8_1_quantize", "mmvq_tq1_0", "mm_tq1_0", "mmvq_tq1_0_f32",
+                     "mmvq_tq1_0_add", "mmvq_tq1_0_f32_add",
                      "mmvq_tq1_0_block_isums", "mmvq_id_tq1_0", "mmvq_id_tq1_0_slots",
                      "mmvq_id_tq1_0_noalloc", "tq1_dequantize"):
             getattr(L, name).restype = ctypes.c_int
@@ -179,6 +183,34 @@ def mmvq_tq1_0_f32(w, x, N, K, T, out=None, stream=None):
     _call("mmvq_tq1_0_f32",
           _dev_tensor(w, "w", (torch.uint8,), N * (K // 256) * TQ1_BLOCK_BYTES),
           _dev_tensor(x, "x", (torch.float32,), T * K * 4, w.device),
+          _dev_tensor(out, "out", (torch.float32,), T * N * 4, w.device),
+          N, K, T, _stream(stream, w.device))
+    return out
+
+
+def mmvq_tq1_0_add(w, a, r, N, K, T, out=None, stream=None):
+    """y fp32 [T, N] = mmvq_tq1_0(w, a) + r (r fp32 [T, N]; out may be r
+    itself for an in-place accumulate)."""
+    torch = _torch()
+    if out is None:
+        out = torch.empty((T, N), dtype=torch.float32, device=w.device)
+    pw, pa = _mmvq_args(w, a, N, K, T)
+    _call("mmvq_tq1_0_add", pw, pa, _dev_tensor(r, "r", (torch.float32,), T * N * 4, w.device),
+          _dev_tensor(out, "out", (torch.float32,), T * N * 4, w.device),
+          N, K, T, _stream(stream, w.device))
+    return out
+
+
+def mmvq_tq1_0_f32_add(w, x, r, N, K, T, out=None, stream=None):
+    """y fp32 [T, N] = mmvq_tq1_0_f32(w, x) + r (quantize, multiply and add
+    in one launch; out may be r itself)."""
+    torch = _torch()
+    if out is None:
+        out = torch.empty((T, N), dtype=torch.float32, device=w.device)
+    _call("mmvq_tq1_0_f32_add",
+          _dev_tensor(w, "w", (torch.uint8,), N * (K // 256) * TQ1_BLOCK_BYTES),
+          _dev_tensor(x, "x", (torch.float32,), T * K * 4, w.device),
+          _dev_tensor(r, "r", (torch.float32,), T * N * 4, w.device),
           _dev_tensor(out, "out", (torch.float32,), T * N * 4, w.device),
           N, K, T, _stream(stream, w.device))
     return out

@@ -75,8 +75,20 @@ int q8_1_quantize(const float *x, void *a, int64_t T, int64_t K, void *stream)
     return bqm::launch_q8_1_quantize(x, a, T, K, as_stream(stream));
 }
 
+// The residual must be the output itself or lie wholly outside it: each
+// output element is read from r and written to y by the same lane, so only
+// a partial overlap could mix elements.
+static bool residual_ok(const float *r, const void *y, int64_t N, int32_t T)
+{
+    if ((const void *)r == y)
+        return true;
+    const uintptr_t rb = (uintptr_t)r, yb = (uintptr_t)y, n = (uintptr_t)N * (uintptr_t)T * 4u;
+    return rb + n <= yb || yb + n <= rb;
+}
+
+// r: the residual of the add entry point (nullptr for the others).
 static int mmvq_common(const void *w, const void *a, const void *out, int64_t N, int64_t K,
-                       int32_t T)
+                       int32_t T, const float *r = nullptr)
 {
     if (!w || !a || !out)
         return BQM_ERR_NULL;
@@ -86,7 +98,9 @@ static int mmvq_common(const void *w, const void *a, const void *out, int64_t N,
         return BQM_ERR_SHAPE;
     if ((uint64_t)T * (uint64_t)(K / 32) * 36ull > kMaxBufferBytes)
         return BQM_ERR_SHAPE;
-    if (!aligned4(w) || !aligned4(a) || !aligned4(out))
+    if (r && !residual_ok(r, out, N, T))
+        return BQM_ERR_SHAPE;
+    if (!aligned4(w) || !aligned4(a) || !aligned4(out) || (r && !aligned4(r)))
         return BQM_ERR_ALIGN;
     return check_device();
 }
@@ -97,6 +111,16 @@ int mmvq_tq1_0(const void *w, const void *a, float *y, int64_t N, int64_t K, int
     if (int rc = mmvq_common(w, a, y, N, K, T))
         return rc;
     return bqm::launch_mmvq(w, a, y, nullptr, N, K, T, as_stream(stream));
+}
+
+int mmvq_tq1_0_add(const void *w, const void *a, const float *r, float *y, int64_t N, int64_t K,
+                   int32_t T, void *stream)
+{
+    if (!r)
+        return BQM_ERR_NULL;
+    if (int rc = mmvq_common(w, a, y, N, K, T, r))
+        return rc;
+    return bqm::launch_mmvq(w, a, y, nullptr, N, K, T, as_stream(stream), r);
 }
 
 int mm_tq1_0(const void *w, const void *a, float *y, int64_t N, int64_t K, int64_t T,
@@ -115,16 +139,19 @@ int mm_tq1_0(const void *w, const void *a, float *y, int64_t N, int64_t K, int64
     return bqm::launch_mm(w, a, y, N, K, T, as_stream(stream));
 }
 
-int mmvq_tq1_0_f32(const void *w, const float *x, float *y, int64_t N, int64_t K, int32_t T,
-                   void *stream)
+// with_r: the residual-add entry point (r required).
+static int mmvq_f32_call(const void *w, const float *x, const float *r, bool with_r, float *y,
+                         int64_t N, int64_t K, int32_t T, void *stream)
 {
-    if (!w || !x || !y)
+    if (!w || !x || !y || (with_r && !r))
         return BQM_ERR_NULL;
     if (int rc = check_matrix(N, K))
         return rc;
     if (T < 1 || T > BQM_MMVQ_F32_MAX_COLS || (uint64_t)T * (uint64_t)K * 4ull > kMaxBufferBytes)
         return BQM_ERR_SHAPE;
-    if (!aligned4(w) || !aligned4(x) || !aligned4(y))
+    if (with_r && !residual_ok(r, y, N, T))
+        return BQM_ERR_SHAPE;
+    if (!aligned4(w) || !aligned4(x) || !aligned4(y) || (with_r && !aligned4(r)))
         return BQM_ERR_ALIGN;
     if (int rc = check_device())
         return rc;
@@ -132,10 +159,22 @@ int mmvq_tq1_0_f32(const void *w, const float *x, float *y, int64_t N, int64_t K
     // stages, and so quantizes, each column once per 16 rows like the staged
     // kernel, with a quarter of the staged kernel's LDS reads)
     if (bqm::quad_supported(K, T))
-        return bqm::launch_mmvq_quad_f32(w, x, y, N, K, T, as_stream(stream));
+        return bqm::launch_mmvq_quad_f32(w, x, y, N, K, T, as_stream(stream), r);
     if (!bqm::staged_supported(K, T))
         return BQM_ERR_SHAPE;
-    return bqm::launch_mmvq_staged_f32(w, x, y, N, K, T, as_stream(stream));
+    return bqm::launch_mmvq_staged_f32(w, x, y, N, K, T, as_stream(stream), r);
+}
+
+int mmvq_tq1_0_f32(const void *w, const float *x, float *y, int64_t N, int64_t K, int32_t T,
+                   void *stream)
+{
+    return mmvq_f32_call(w, x, nullptr, false, y, N, K, T, stream);
+}
+
+int mmvq_tq1_0_f32_add(const void *w, const float *x, const float *r, float *y, int64_t N,
+                       int64_t K, int32_t T, void *stream)
+{
+    return mmvq_f32_call(w, x, r, true, y, N, K, T, stream);
 }
 
 int mmvq_tq1_0_block_isums(const void *w, const void *a, int32_t *isums, int64_t N, int64_t K,

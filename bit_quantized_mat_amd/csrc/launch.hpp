@@ -46,20 +46,22 @@ int resident_workgroups(const void *kernel, int threads, size_t lds);
 // Staged kernel (one to eight columns, activations staged in LDS): whether it
 // takes this shape, and its launcher.
 bool staged_supported(int64_t K, int32_t T);
+// r (every product launcher): when given, y = product + r, one fp32 addition
+// after the product's own result (r [T][N], may be y itself).
 int launch_mmvq_staged(const void *w, const void *a, float *y, int32_t *isums, int64_t N,
-                       int64_t K, int32_t T, hipStream_t stream);
+                       int64_t K, int32_t T, hipStream_t stream, const float *r = nullptr);
 // The staged kernel on fp32 activations, quantized to Q8_1 while staging.
 int launch_mmvq_staged_f32(const void *w, const float *x, float *y, int64_t N, int64_t K,
-                           int32_t T, hipStream_t stream);
+                           int32_t T, hipStream_t stream, const float *r = nullptr);
 // Quad kernel (three to eight columns, whole-block decode per lane, sub-block
 // sums on the matrix cores; rows of more than 8 blocks): whether it takes this
 // shape, and its launchers (Q8_1 activations, and fp32 activations quantized
 // while staging).
 bool quad_supported(int64_t K, int32_t T);
 int launch_mmvq_quad(const void *w, const void *a, float *y, int32_t *isums, int64_t N,
-                     int64_t K, int32_t T, hipStream_t stream);
+                     int64_t K, int32_t T, hipStream_t stream, const float *r = nullptr);
 int launch_mmvq_quad_f32(const void *w, const float *x, float *y, int64_t N, int64_t K,
-                         int32_t T, hipStream_t stream);
+                         int32_t T, hipStream_t stream, const float *r = nullptr);
 // Matrix-core kernel: any shape, 1 to 32 columns; the dispatcher gives it
 // every call of at least kMfmaMinCols columns, and the calls of fewer that
 // neither the quad kernel nor the staged kernel takes or that are too small
@@ -67,13 +69,13 @@ int launch_mmvq_quad_f32(const void *w, const float *x, float *y, int64_t N, int
 constexpr int kMfmaMinCols = 5;
 
 int launch_mmvq_mfma(const void *w, const void *a, float *y, int32_t *isums, int64_t N,
-                     int64_t K, int32_t T, hipStream_t stream);
+                     int64_t K, int32_t T, hipStream_t stream, const float *r = nullptr);
 // Matrix-core kernel with all activation columns resident in LDS: whether it
 // takes this shape (the columns fit and a row has at least as many lane
 // groups as the workgroup has waves), and its launcher.
 bool mfma_resident_supported(int64_t K, int32_t T);
 int launch_mmvq_mfma_resident(const void *w, const void *a, float *y, int32_t *isums, int64_t N,
-                              int64_t K, int32_t T, hipStream_t stream);
+                              int64_t K, int32_t T, hipStream_t stream, const float *r = nullptr);
 // Its expert-routed mode (wide work items of up to 16 pairs, written by the
 // routing pre-pass): whether it takes rows of K elements, and its launcher.
 bool mfma_resident_id_supported(int64_t K);
@@ -87,7 +89,7 @@ bool mm_chunked_supported(int64_t K);
 int launch_mm_chunked(const void *w, const void *a, float *y, int64_t N, int64_t K, int64_t T,
                       hipStream_t stream);
 int launch_mmvq(const void *w, const void *a, float *y, int32_t *isums, int64_t N, int64_t K,
-                int32_t T, hipStream_t stream);
+                int32_t T, hipStream_t stream, const float *r = nullptr);
 int launch_mm(const void *w, const void *a, float *y, int64_t N, int64_t K, int64_t T,
               hipStream_t stream);
 // K-streaming matrix-core kernel for many columns (any K and T): its grid

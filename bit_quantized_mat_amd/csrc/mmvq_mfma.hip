@@ -97,7 +97,7 @@ struct StagePieces {
 template <int GPW, int NT, int R, bool ISUMS>
 __global__ __launch_bounds__(512) void mmvq_mfma_kernel(const uint8_t *__restrict__ w,
                                                         const uint8_t *__restrict__ a,
-                                                        float *__restrict__ y,
+                                                        float *y, const float *resid,
                                                         int32_t *__restrict__ isums, int64_t N,
                                                         int nb, int T, int lr_log2, int ntiles)
 {
@@ -308,8 +308,11 @@ __global__ __launch_bounds__(512) void mmvq_mfma_kernel(const uint8_t *__restric
 #pragma unroll
                             for (int i = 0; i < 4; i++) {
                                 const int64_t row = r0 + 16 * rt + 4 * rg + i;
-                                if (row < N)
-                                    y[(int64_t)c * N + row] = acc[0][rt][ct][i];
+                                if (row < N) {
+                                    const int64_t o = (int64_t)c * N + row;
+                                    y[o] = resid ? acc[0][rt][ct][i] + resid[o]
+                                                 : acc[0][rt][ct][i];
+                                }
                             }
                         }
                     }
@@ -322,7 +325,8 @@ __global__ __launch_bounds__(512) void mmvq_mfma_kernel(const uint8_t *__restric
 }
 
 template <int GPW, int NT, int R>
-static void launch_mfma_r(const uint8_t *w, const uint8_t *a, float *y, int32_t *isums,
+static void launch_mfma_r(const uint8_t *w, const uint8_t *a, float *y, const float *r,
+                          int32_t *isums,
                           int64_t N, int nb, int T, int lr, int nw, hipStream_t stream)
 {
     const int64_t ntiles = (N + 16 * R - 1) / (16 * R);
@@ -340,14 +344,15 @@ static void launch_mfma_r(const uint8_t *w, const uint8_t *a, float *y, int32_t 
     const dim3 grid((unsigned)((ntiles + per - 1) / per));
     if (isums)
         hipLaunchKernelGGL((mmvq_mfma_kernel<GPW, NT, R, true>), grid, dim3(64 * nw), lds,
-                           stream, w, a, nullptr, isums, N, nb, T, lr, (int)ntiles);
+                           stream, w, a, nullptr, nullptr, isums, N, nb, T, lr, (int)ntiles);
     else
         hipLaunchKernelGGL((mmvq_mfma_kernel<GPW, NT, R, false>), grid, dim3(64 * nw), lds,
-                           stream, w, a, y, nullptr, N, nb, T, lr, (int)ntiles);
+                           stream, w, a, y, r, nullptr, N, nb, T, lr, (int)ntiles);
 }
 
 template <int GPW, int NT>
-static void launch_mfma_gn(const uint8_t *w, const uint8_t *a, float *y, int32_t *isums,
+static void launch_mfma_gn(const uint8_t *w, const uint8_t *a, float *y, const float *r,
+                           int32_t *isums,
                            int64_t N, int nb, int T, int lr, int nw, hipStream_t stream)
 {
     // R, the row tiles sharing each staged activation block: at most what
@@ -359,36 +364,37 @@ static void launch_mfma_gn(const uint8_t *w, const uint8_t *a, float *y, int32_t
     constexpr int Rmax = Racc < Rcap ? Racc : Rcap;
     const int64_t want = 2 * (int64_t)compute_units();
     if (Rmax >= 2 && (N + 31) / 32 >= want)
-        launch_mfma_r<GPW, NT, (Rmax >= 2 ? 2 : 1)>(w, a, y, isums, N, nb, T, lr, nw, stream);
+        launch_mfma_r<GPW, NT, (Rmax >= 2 ? 2 : 1)>(w, a, y, r, isums, N, nb, T, lr, nw, stream);
     else
-        launch_mfma_r<GPW, NT, 1>(w, a, y, isums, N, nb, T, lr, nw, stream);
+        launch_mfma_r<GPW, NT, 1>(w, a, y, r, isums, N, nb, T, lr, nw, stream);
 }
 
 template <int NT>
-static void launch_mfma_n(const uint8_t *w, const uint8_t *a, float *y, int32_t *isums,
+static void launch_mfma_n(const uint8_t *w, const uint8_t *a, float *y, const float *r,
+                          int32_t *isums,
                           int64_t N, int nb, int T, int lr, hipStream_t stream)
 {
     const int Lr = 1 << lr;
     const int nw = Lr < kMfmaMaxWaves ? Lr : kMfmaMaxWaves;
     switch (Lr / nw) {
-    case 1: launch_mfma_gn<1, NT>(w, a, y, isums, N, nb, T, lr, nw, stream); break;
-    case 2: launch_mfma_gn<2, NT>(w, a, y, isums, N, nb, T, lr, nw, stream); break;
-    case 4: launch_mfma_gn<4, NT>(w, a, y, isums, N, nb, T, lr, nw, stream); break;
-    default: launch_mfma_gn<8, NT>(w, a, y, isums, N, nb, T, lr, nw, stream); break;
+    case 1: launch_mfma_gn<1, NT>(w, a, y, r, isums, N, nb, T, lr, nw, stream); break;
+    case 2: launch_mfma_gn<2, NT>(w, a, y, r, isums, N, nb, T, lr, nw, stream); break;
+    case 4: launch_mfma_gn<4, NT>(w, a, y, r, isums, N, nb, T, lr, nw, stream); break;
+    default: launch_mfma_gn<8, NT>(w, a, y, r, isums, N, nb, T, lr, nw, stream); break;
     }
 }
 
 int launch_mmvq_mfma(const void *w, const void *a, float *y, int32_t *isums, int64_t N,
-                     int64_t K, int32_t T, hipStream_t stream)
+                     int64_t K, int32_t T, hipStream_t stream, const float *r)
 {
     const int nb = (int)(K / kTq1BlockElems);
     const int lr = lanes_per_row_log2(nb);
     const uint8_t *wp = static_cast<const uint8_t *>(w);
     const uint8_t *ap = static_cast<const uint8_t *>(a);
     if (T <= 16)
-        launch_mfma_n<1>(wp, ap, y, isums, N, nb, T, lr, stream);
+        launch_mfma_n<1>(wp, ap, y, r, isums, N, nb, T, lr, stream);
     else
-        launch_mfma_n<2>(wp, ap, y, isums, N, nb, T, lr, stream);
+        launch_mfma_n<2>(wp, ap, y, r, isums, N, nb, T, lr, stream);
     return check_launch();
 }
 

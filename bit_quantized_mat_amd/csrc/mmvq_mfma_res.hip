@@ -143,7 +143,7 @@ struct WideItems {
 template <int NW, int GPW, int NT, int R, bool DB, bool ISUMS, bool ID, bool RUNS>
 __global__ __launch_bounds__(64 * NW) void mmvq_mfma_res_kernel(const uint8_t *__restrict__ w,
                                                                 const uint8_t *__restrict__ a,
-                                                                float *__restrict__ y,
+                                                                float *y, const float *resid,
                                                                 int32_t *__restrict__ isums,
                                                                 int64_t N, int nb, int T,
                                                                 int ntiles, int a_cols,
@@ -419,7 +419,8 @@ __global__ __launch_bounds__(64 * NW) void mmvq_mfma_res_kernel(const uint8_t *_
                     const int64_t row = r0 + 16 * rt + 4 * org + i;
                     if (j == 0 && c < T && row < N) {
                         const int64_t yc = ID ? colpair[c] : c;
-                        y[yc * N + row] = v;
+                        const int64_t o = yc * N + row;
+                        y[o] = resid ? v + resid[o] : v;
                     }
                 }
             } else {
@@ -452,8 +453,11 @@ __global__ __launch_bounds__(64 * NW) void mmvq_mfma_res_kernel(const uint8_t *_
 #pragma unroll
                                 for (int i = 0; i < 4; i++) {
                                     const int64_t row = r0 + 16 * rt + 4 * rg + i;
-                                    if (row < N)
-                                        y[yc * N + row] = acc[0][rt][ct][i];
+                                    if (row < N) {
+                                        const int64_t o = yc * N + row;
+                                        y[o] = resid ? acc[0][rt][ct][i] + resid[o]
+                                                     : acc[0][rt][ct][i];
+                                    }
                                 }
                             }
                         }
@@ -480,8 +484,8 @@ __global__ __launch_bounds__(64 * NW) void mmvq_mfma_res_kernel(const uint8_t *_
 }
 
 template <int NW, int GPW, int NT, bool DB>
-static int launch_res(const uint8_t *w, const uint8_t *a, float *y, int32_t *isums, int64_t N,
-                      int nb, int T, hipStream_t stream)
+static int launch_res(const uint8_t *w, const uint8_t *a, float *y, const float *r,
+                      int32_t *isums, int64_t N, int nb, int T, hipStream_t stream)
 {
     constexpr int R = 1;
     const int64_t ntiles = (N + 16 * R - 1) / (16 * R);
@@ -497,12 +501,12 @@ static int launch_res(const uint8_t *w, const uint8_t *a, float *y, int32_t *isu
     const WideItems none = {nullptr, 0, 1};
     if (isums)
         hipLaunchKernelGGL((mmvq_mfma_res_kernel<NW, GPW, NT, R, DB, true, false, true>), grid,
-                           dim3(64 * NW), lds, stream, w, a, nullptr, isums, N, nb, T,
+                           dim3(64 * NW), lds, stream, w, a, nullptr, nullptr, isums, N, nb, T,
                            (int)ntiles, T, none);
     else
         hipLaunchKernelGGL((mmvq_mfma_res_kernel<NW, GPW, NT, R, DB, false, false, true>), grid,
-                           dim3(64 * NW), lds, stream, w, a, y, nullptr, N, nb, T, (int)ntiles,
-                           T, none);
+                           dim3(64 * NW), lds, stream, w, a, y, r, nullptr, N, nb, T,
+                           (int)ntiles, T, none);
     return check_launch();
 }
 
@@ -525,8 +529,8 @@ static int launch_res_id(const uint8_t *w, const uint8_t *a, float *y, int64_t N
     const dim3 grid((unsigned)(most < cap ? most : cap));
     const WideItems items = {routed, max_items, pairs_per_col};
     hipLaunchKernelGGL((mmvq_mfma_res_kernel<NW, GPW, NT, R, DB, false, true, false>), grid,
-                       dim3(64 * NW), lds, stream, w, a, y, nullptr, N, nb, 16, (int)ntiles,
-                       a_cols, items);
+                       dim3(64 * NW), lds, stream, w, a, y, nullptr, nullptr, N, nb, 16,
+                       (int)ntiles, a_cols, items);
     return check_launch();
 }
 
@@ -563,8 +567,8 @@ static int launch_mm(const uint8_t *w, const uint8_t *a, float *y, int64_t N, in
     const dim3 grid((unsigned)(units < cap ? units : cap));
     const WideItems chunks = {nullptr, 0, 1};
     hipLaunchKernelGGL((mmvq_mfma_res_kernel<NW, GPW, NT, R, DB, false, true, true>), grid,
-                       dim3(64 * NW), lds, stream, w, a, y, nullptr, N, nb, 16 * NT, (int)ntiles,
-                       T, chunks);
+                       dim3(64 * NW), lds, stream, w, a, y, nullptr, nullptr, N, nb, 16 * NT,
+                       (int)ntiles, T, chunks);
     return check_launch();
 }
 
@@ -628,7 +632,7 @@ bool mfma_resident_supported(int64_t K, int32_t T)
 }
 
 int launch_mmvq_mfma_resident(const void *w, const void *a, float *y, int32_t *isums, int64_t N,
-                              int64_t K, int32_t T, hipStream_t stream)
+                              int64_t K, int32_t T, hipStream_t stream, const float *r)
 {
     const int nb = (int)(K / kTq1BlockElems);
     const int Lr = 1 << lanes_per_row_log2(nb);
@@ -636,16 +640,16 @@ int launch_mmvq_mfma_resident(const void *w, const void *a, float *y, int32_t *i
     const uint8_t *ap = static_cast<const uint8_t *>(a);
     if (T <= 16) {
         switch (Lr) {
-        case 16: return launch_res<16, 1, 1, true>(wp, ap, y, isums, N, nb, T, stream);
-        case 32: return launch_res<16, 2, 1, true>(wp, ap, y, isums, N, nb, T, stream);
-        default: return launch_res<16, 4, 1, true>(wp, ap, y, isums, N, nb, T, stream);
+        case 16: return launch_res<16, 1, 1, true>(wp, ap, y, r, isums, N, nb, T, stream);
+        case 32: return launch_res<16, 2, 1, true>(wp, ap, y, r, isums, N, nb, T, stream);
+        default: return launch_res<16, 4, 1, true>(wp, ap, y, r, isums, N, nb, T, stream);
         }
     }
     switch (Lr) {
-    case 8: return launch_res<8, 1, 2, false>(wp, ap, y, isums, N, nb, T, stream);
-    case 16: return launch_res<8, 2, 2, false>(wp, ap, y, isums, N, nb, T, stream);
-    case 32: return launch_res<8, 4, 2, false>(wp, ap, y, isums, N, nb, T, stream);
-    default: return launch_res<8, 8, 2, false>(wp, ap, y, isums, N, nb, T, stream);
+    case 8: return launch_res<8, 1, 2, false>(wp, ap, y, r, isums, N, nb, T, stream);
+    case 16: return launch_res<8, 2, 2, false>(wp, ap, y, r, isums, N, nb, T, stream);
+    case 32: return launch_res<8, 4, 2, false>(wp, ap, y, r, isums, N, nb, T, stream);
+    default: return launch_res<8, 8, 2, false>(wp, ap, y, r, isums, N, nb, T, stream);
     }
 }
 

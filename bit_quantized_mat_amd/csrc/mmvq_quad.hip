@@ -57,7 +57,7 @@ static int quad_chunk(int nb, int lr, int T, size_t budget)
 template <int CG, int GPW, bool ISUMS, bool F32, int WPG>
 __global__ __launch_bounds__(64 * WPG) void mmvq_quad_kernel(const uint8_t *__restrict__ w,
                                                         const uint8_t *__restrict__ a,
-                                                        float *__restrict__ y,
+                                                        float *y, const float *resid,
                                                         int32_t *__restrict__ isums, int64_t N,
                                                         int nb, int T, int chunk)
 {
@@ -263,8 +263,10 @@ __global__ __launch_bounds__(64 * WPG) void mmvq_quad_kernel(const uint8_t *__re
             const int col = 4 * cg + qi;
 #pragma unroll
             for (int v = 0; v < 4; v++)
-                if (col < T && row0 + v < N)
-                    y[(int64_t)col * N + row0 + v] = out[cg][v];
+                if (col < T && row0 + v < N) {
+                    const int64_t o = (int64_t)col * N + row0 + v;
+                    y[o] = resid ? out[cg][v] + resid[o] : out[cg][v];
+                }
         }
     }
 }
@@ -293,7 +295,8 @@ static int quad_waves(int64_t N)
 }
 
 template <int CG, int GPW, bool F32, int WPG>
-static void launch_quad_cg(const uint8_t *w, const uint8_t *a, float *y, int32_t *isums,
+static void launch_quad_cg(const uint8_t *w, const uint8_t *a, float *y, const float *r,
+                           int32_t *isums,
                            int64_t N, int nb, int T, int chunk, size_t lds, hipStream_t stream)
 {
     const dim3 grid((unsigned)((N + 4 * WPG - 1) / (4 * WPG))), block(64 * WPG);
@@ -301,31 +304,32 @@ static void launch_quad_cg(const uint8_t *w, const uint8_t *a, float *y, int32_t
         const void *k = reinterpret_cast<const void *>(&mmvq_quad_kernel<CG, GPW, true, false, WPG>);
         allow_dynamic_lds(k, lds);
         hipLaunchKernelGGL((mmvq_quad_kernel<CG, GPW, true, false, WPG>), grid, block, lds, stream,
-                           w, a, nullptr, isums, N, nb, T, chunk);
+                           w, a, nullptr, nullptr, isums, N, nb, T, chunk);
     } else {
         const void *k = reinterpret_cast<const void *>(&mmvq_quad_kernel<CG, GPW, false, F32, WPG>);
         allow_dynamic_lds(k, lds);
         hipLaunchKernelGGL((mmvq_quad_kernel<CG, GPW, false, F32, WPG>), grid, block, lds, stream,
-                           w, a, y, nullptr, N, nb, T, chunk);
+                           w, a, y, r, nullptr, N, nb, T, chunk);
     }
 }
 
 template <int GPW, bool F32>
-static void launch_quad_gpw(const uint8_t *w, const uint8_t *a, float *y, int32_t *isums,
+static void launch_quad_gpw(const uint8_t *w, const uint8_t *a, float *y, const float *r,
+                            int32_t *isums,
                             int64_t N, int nb, int T, int chunk, size_t lds, hipStream_t stream)
 {
     const bool two = T > 4, wide = quad_waves(N) == 8;
     if (two)
-        wide ? launch_quad_cg<2, GPW, F32, 8>(w, a, y, isums, N, nb, T, chunk, lds, stream)
-             : launch_quad_cg<2, GPW, F32, 4>(w, a, y, isums, N, nb, T, chunk, lds, stream);
+        wide ? launch_quad_cg<2, GPW, F32, 8>(w, a, y, r, isums, N, nb, T, chunk, lds, stream)
+             : launch_quad_cg<2, GPW, F32, 4>(w, a, y, r, isums, N, nb, T, chunk, lds, stream);
     else
-        wide ? launch_quad_cg<1, GPW, F32, 8>(w, a, y, isums, N, nb, T, chunk, lds, stream)
-             : launch_quad_cg<1, GPW, F32, 4>(w, a, y, isums, N, nb, T, chunk, lds, stream);
+        wide ? launch_quad_cg<1, GPW, F32, 8>(w, a, y, r, isums, N, nb, T, chunk, lds, stream)
+             : launch_quad_cg<1, GPW, F32, 4>(w, a, y, r, isums, N, nb, T, chunk, lds, stream);
 }
 
 template <bool F32>
-static int launch_quad(const void *w, const void *a, float *y, int32_t *isums, int64_t N,
-                       int64_t K, int32_t T, hipStream_t stream)
+static int launch_quad(const void *w, const void *a, float *y, const float *r, int32_t *isums,
+                       int64_t N, int64_t K, int32_t T, hipStream_t stream)
 {
     const int nb = (int)(K / kTq1BlockElems);
     const int lr = lanes_per_row_log2(nb);
@@ -336,23 +340,23 @@ static int launch_quad(const void *w, const void *a, float *y, int32_t *isums, i
     const uint8_t *wp = static_cast<const uint8_t *>(w);
     const uint8_t *ap = static_cast<const uint8_t *>(a);
     switch (lr) {
-    case 4: launch_quad_gpw<1, F32>(wp, ap, y, isums, N, nb, T, chunk, lds, stream); break;
-    case 5: launch_quad_gpw<2, F32>(wp, ap, y, isums, N, nb, T, chunk, lds, stream); break;
-    default: launch_quad_gpw<4, F32>(wp, ap, y, isums, N, nb, T, chunk, lds, stream); break;
+    case 4: launch_quad_gpw<1, F32>(wp, ap, y, r, isums, N, nb, T, chunk, lds, stream); break;
+    case 5: launch_quad_gpw<2, F32>(wp, ap, y, r, isums, N, nb, T, chunk, lds, stream); break;
+    default: launch_quad_gpw<4, F32>(wp, ap, y, r, isums, N, nb, T, chunk, lds, stream); break;
     }
     return check_launch();
 }
 
 int launch_mmvq_quad(const void *w, const void *a, float *y, int32_t *isums, int64_t N,
-                     int64_t K, int32_t T, hipStream_t stream)
+                     int64_t K, int32_t T, hipStream_t stream, const float *r)
 {
-    return launch_quad<false>(w, a, y, isums, N, K, T, stream);
+    return launch_quad<false>(w, a, y, r, isums, N, K, T, stream);
 }
 
 int launch_mmvq_quad_f32(const void *w, const float *x, float *y, int64_t N, int64_t K,
-                         int32_t T, hipStream_t stream)
+                         int32_t T, hipStream_t stream, const float *r)
 {
-    return launch_quad<true>(w, x, y, nullptr, N, K, T, stream);
+    return launch_quad<true>(w, x, y, r, nullptr, N, K, T, stream);
 }
 
 }  // namespace bqm

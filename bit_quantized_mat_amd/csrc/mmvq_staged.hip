@@ -28,7 +28,7 @@ namespace bqm {
 template <int TC, bool ISUMS, bool F32, int WPG>
 __global__ __launch_bounds__(64 * WPG) void mmvq_staged_kernel(const uint8_t *__restrict__ w,
                                                           const uint8_t *__restrict__ a,
-                                                          float *__restrict__ y,
+                                                          float *y, const float *resid,
                                                           int32_t *__restrict__ isums, int64_t N,
                                                           int nb, int T, int lr_log2, int chunk)
 {
@@ -46,7 +46,8 @@ __global__ __launch_bounds__(64 * WPG) void mmvq_staged_kernel(const uint8_t *__
         col_off[t] = (uint32_t)t * col_bytes;
         out[t] = ISUMS ? nullptr : y + (int64_t)t * N;
     }
-    staged_rows<TC, ISUMS, F32>(rw, ra, col_off, out, isums, reinterpret_cast<uint32_t *>(act_lds),
+    staged_rows<TC, ISUMS, F32>(rw, ra, col_off, out, resid, isums,
+                                reinterpret_cast<uint32_t *>(act_lds),
                                 row, row < N, N, nb, T, lr_log2, chunk, 64 * WPG);
 }
 
@@ -147,7 +148,8 @@ bool staged_supported(int64_t K, int32_t T)
 }
 
 template <int TC, bool F32, int WPG>
-static void launch_staged_tc(const uint8_t *w, const uint8_t *a, float *y, int32_t *isums,
+static void launch_staged_tc(const uint8_t *w, const uint8_t *a, float *y, const float *r,
+                             int32_t *isums,
                              int64_t N, int nb, int T, int lr, int chunk, size_t lds,
                              hipStream_t stream)
 {
@@ -156,11 +158,11 @@ static void launch_staged_tc(const uint8_t *w, const uint8_t *a, float *y, int32
     if (isums && !F32) {
         allow_dynamic_lds(reinterpret_cast<const void *>(&mmvq_staged_kernel<TC, true, false, WPG>), lds);
         hipLaunchKernelGGL((mmvq_staged_kernel<TC, true, false, WPG>), grid, block, lds, stream, w,
-                           a, nullptr, isums, N, nb, T, lr, chunk);
+                           a, nullptr, nullptr, isums, N, nb, T, lr, chunk);
     } else {
         allow_dynamic_lds(reinterpret_cast<const void *>(&mmvq_staged_kernel<TC, false, F32, WPG>), lds);
         hipLaunchKernelGGL((mmvq_staged_kernel<TC, false, F32, WPG>), grid, block, lds, stream, w,
-                           a, y, nullptr, N, nb, T, lr, chunk);
+                           a, y, r, nullptr, N, nb, T, lr, chunk);
     }
 }
 
@@ -176,7 +178,8 @@ static int staged_waves(int64_t N, int lr)
 }
 
 template <int TC, bool F32>
-static void launch_staged_w(const uint8_t *w, const uint8_t *a, float *y, int32_t *isums,
+static void launch_staged_w(const uint8_t *w, const uint8_t *a, float *y, const float *r,
+                            int32_t *isums,
                             int64_t N, int nb, int T, int lr, int chunk, size_t lds,
                             hipStream_t stream)
 {
@@ -185,16 +188,16 @@ static void launch_staged_w(const uint8_t *w, const uint8_t *a, float *y, int32_
     // 2.47 us, fused 2.99 -> 2.88 us)
     const int64_t rows4 = 4 * (64 >> lr);
     if ((N + rows4 - 1) / rows4 * 4 <= compute_units())
-        launch_staged_tc<TC, F32, 1>(w, a, y, isums, N, nb, T, lr, chunk, lds, stream);
+        launch_staged_tc<TC, F32, 1>(w, a, y, r, isums, N, nb, T, lr, chunk, lds, stream);
     else if (staged_waves(N, lr) == 8)
-        launch_staged_tc<TC, F32, 8>(w, a, y, isums, N, nb, T, lr, chunk, lds, stream);
+        launch_staged_tc<TC, F32, 8>(w, a, y, r, isums, N, nb, T, lr, chunk, lds, stream);
     else
-        launch_staged_tc<TC, F32, 4>(w, a, y, isums, N, nb, T, lr, chunk, lds, stream);
+        launch_staged_tc<TC, F32, 4>(w, a, y, r, isums, N, nb, T, lr, chunk, lds, stream);
 }
 
 template <bool F32>
-static int launch_staged(const void *w, const void *a, float *y, int32_t *isums, int64_t N,
-                         int64_t K, int32_t T, hipStream_t stream)
+static int launch_staged(const void *w, const void *a, float *y, const float *r,
+                         int32_t *isums, int64_t N, int64_t K, int32_t T, hipStream_t stream)
 {
     const int nb = (int)(K / kTq1BlockElems);
     const int lr = lanes_per_row_log2(nb);
@@ -204,26 +207,26 @@ static int launch_staged(const void *w, const void *a, float *y, int32_t *isums,
     const uint8_t *ap = static_cast<const uint8_t *>(a);
     // column-capacity ladder: a call pays for the next rung up, never for 8
     if (T == 1)
-        launch_staged_w<1, F32>(wp, ap, y, isums, N, nb, T, lr, chunk, lds, stream);
+        launch_staged_w<1, F32>(wp, ap, y, r, isums, N, nb, T, lr, chunk, lds, stream);
     else if (T == 2)
-        launch_staged_w<2, F32>(wp, ap, y, isums, N, nb, T, lr, chunk, lds, stream);
+        launch_staged_w<2, F32>(wp, ap, y, r, isums, N, nb, T, lr, chunk, lds, stream);
     else if (T <= 4)
-        launch_staged_w<4, F32>(wp, ap, y, isums, N, nb, T, lr, chunk, lds, stream);
+        launch_staged_w<4, F32>(wp, ap, y, r, isums, N, nb, T, lr, chunk, lds, stream);
     else
-        launch_staged_w<8, F32>(wp, ap, y, isums, N, nb, T, lr, chunk, lds, stream);
+        launch_staged_w<8, F32>(wp, ap, y, r, isums, N, nb, T, lr, chunk, lds, stream);
     return check_launch();
 }
 
 int launch_mmvq_staged(const void *w, const void *a, float *y, int32_t *isums, int64_t N,
-                       int64_t K, int32_t T, hipStream_t stream)
+                       int64_t K, int32_t T, hipStream_t stream, const float *r)
 {
-    return launch_staged<false>(w, a, y, isums, N, K, T, stream);
+    return launch_staged<false>(w, a, y, r, isums, N, K, T, stream);
 }
 
 int launch_mmvq_staged_f32(const void *w, const float *x, float *y, int64_t N, int64_t K,
-                           int32_t T, hipStream_t stream)
+                           int32_t T, hipStream_t stream, const float *r)
 {
-    return launch_staged<true>(w, x, y, nullptr, N, K, T, stream);
+    return launch_staged<true>(w, x, y, r, nullptr, N, K, T, stream);
 }
 
 }  // namespace bqm

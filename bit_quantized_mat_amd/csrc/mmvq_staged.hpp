@@ -299,13 +299,16 @@ __device__ __forceinline__ void dword_sums_staged(const RawBlock &raw,
 
 // The rows of one workgroup against T <= TC activation columns. Column t's
 // Q8_1 row (fp32 row when F32: quantized while staging) starts at byte
-// col_off[t] of the activation buffer ra and its outputs go to out[t][row].
+// col_off[t] of the activation buffer ra and its outputs go to out[t][row],
+// plus resid[t * N + row] when resid is given (one fp32 addition after the
+// product's own result; resid may be the output buffer itself).
 // All nthreads threads of the workgroup (its whole size) must call this (it
 // synchronizes); lanes whose row is out of range only help with staging.
 template <int TC, bool ISUMS, bool F32 = false>
 __device__ __forceinline__ void staged_rows(__amdgpu_buffer_rsrc_t rw, __amdgpu_buffer_rsrc_t ra,
                                             const uint32_t (&col_off)[TC],
-                                            float *const (&out)[TC], int32_t *__restrict__ isums,
+                                            float *const (&out)[TC], const float *resid,
+                                            int32_t *__restrict__ isums,
                                             uint32_t *__restrict__ act, int64_t row, bool row_ok,
                                             int64_t N, int nb, int T, int lr_log2, int chunk,
                                             int nthreads = 256)
@@ -423,7 +426,7 @@ __device__ __forceinline__ void staged_rows(__amdgpu_buffer_rsrc_t rw, __amdgpu_
 #pragma unroll
             for (int t = 0; t < TC; t++)
                 if (t < T)
-                    out[t][row] = acc[t];
+                    out[t][row] = resid ? acc[t] + resid[(int64_t)t * N + row] : acc[t];
         }
     }
 }

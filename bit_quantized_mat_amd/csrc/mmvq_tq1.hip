@@ -211,15 +211,15 @@ static bool use_staged(int64_t N, int64_t K, int32_t T)
 // columns they win (8.9 against 11.6 us at four, 4096 x 4096: 5.1 against
 // 5.6 us).
 int launch_mmvq(const void *w, const void *a, float *y, int32_t *isums, int64_t N, int64_t K,
-                int32_t T, hipStream_t stream)
+                int32_t T, hipStream_t stream, const float *r)
 {
     if (T >= 3 && T <= 4 && quad_supported(K, T))
-        return launch_mmvq_quad(w, a, y, isums, N, K, T, stream);
+        return launch_mmvq_quad(w, a, y, isums, N, K, T, stream, r);
     if (use_staged(N, K, T))
-        return launch_mmvq_staged(w, a, y, isums, N, K, T, stream);
+        return launch_mmvq_staged(w, a, y, isums, N, K, T, stream, r);
     if (mfma_resident_supported(K, T))
-        return launch_mmvq_mfma_resident(w, a, y, isums, N, K, T, stream);
-    return launch_mmvq_mfma(w, a, y, isums, N, K, T, stream);
+        return launch_mmvq_mfma_resident(w, a, y, isums, N, K, T, stream, r);
+    return launch_mmvq_mfma(w, a, y, isums, N, K, T, stream, r);
 }
 
 // Many-column product: up to BQM_MMVQ_MAX_COLS columns the plain product.

@@ -128,6 +128,20 @@ BQM_API int q8_1_quantize(const float *x, void *a, int64_t T, int64_t K, void *s
 BQM_API int mmvq_tq1_0(const void *w, const void *a, float *y,
                int64_t N, int64_t K, int32_t T, void *stream);
 
+/* The product with a residual added in its epilogue (the linear-plus-add of a
+ * residual block, one launch instead of two: "ops::linear q5: one
+ * Capacity=32 K-split rung serves all T<=96", the linear_add route beside
+ * the plain linear one):
+ *   y[t][n] = mmvq_tq1_0(w, a)[t][n] + r[t][n]
+ * computed as one fp32 addition after the product's own result, so y is
+ * bitwise fp32(mmvq_tq1_0's output + r) and within 1e-5 of sum |terms| +
+ * |r| of the exact value (the addition's rounding is one ulp of |y|).
+ *   r [T][N] fp32, read once; it may be y itself (in-place accumulate) but
+ *   must not otherwise overlap y (BQM_ERR_SHAPE).
+ * Shapes, other arguments, alignment (r 4 bytes) and errors as mmvq_tq1_0. */
+BQM_API int mmvq_tq1_0_add(const void *w, const void *a, const float *r, float *y,
+                   int64_t N, int64_t K, int32_t T, void *stream);
+
 /* Largest number of activation columns mm_tq1_0 accepts. */
 #define BQM_MM_MAX_COLS 65536
 
@@ -162,6 +176,14 @@ BQM_API int mm_tq1_0(const void *w, const void *a, float *y,
  * Alignment: w, x, y 4 bytes. */
 BQM_API int mmvq_tq1_0_f32(const void *w, const float *x, float *y,
                    int64_t N, int64_t K, int32_t T, void *stream);
+
+/* mmvq_tq1_0_f32 with a residual added in its epilogue: the decode step of
+ * a residual block in one launch (quantize, multiply, add):
+ *   y[t][n] = mmvq_tq1_0_f32(w, x)[t][n] + r[t][n]
+ * bitwise fp32(mmvq_tq1_0_f32's output + r); r as for mmvq_tq1_0_add.
+ * Shapes, other arguments, alignment and errors as mmvq_tq1_0_f32. */
+BQM_API int mmvq_tq1_0_f32_add(const void *w, const float *x, const float *r, float *y,
+                       int64_t N, int64_t K, int32_t T, void *stream);
 
 /* Dequantize TQ1_0 rows (the dequantize and get_rows operations that sit
  * beside the mat-vec, "CUDA: TQ1_0 mat-vec is load-bound by the per-32-element

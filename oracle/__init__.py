@@ -53,6 +53,8 @@ def lib():
             getattr(L, name).restype = ctypes.c_int
         L.oracle_mmvq.argtypes = [_p, _p, _p, _p, _p, _i64, _i64, _i64]
         L.oracle_mmvq.restype = ctypes.c_int
+        L.oracle_mmvq_add.argtypes = [_p, _p, _p, _p, _p, _p, _i64, _i64, _i64]
+        L.oracle_mmvq_add.restype = ctypes.c_int
         L.oracle_mmvq_id.argtypes = [_p, _p, _p, _p, _p, _p, _i64, _i64, _i64, _i64, _i64]
         L.oracle_mmvq_id.restype = ctypes.c_int
         L.oracle_mmvq_id_slots.argtypes = [_p, _p, _p, _p, _p, _p, _i64, _i64, _i64, _i64, _i64]
@@ -176,6 +178,21 @@ def mmvq(w, a, N, K, T):
     y64 = np.empty((T, N), dtype=np.float64)
     ab = np.empty((T, N), dtype=np.float64)
     _check(lib().oracle_mmvq(_ptr(w), _ptr(a), _ptr(y), _ptr(y64), _ptr(ab), N, K, T), "mmvq")
+    return y, y64, ab
+
+
+def mmvq_add(w, a, r, N, K, T):
+    """The mat-vec plus a residual r float32 [T, N]: returns (y, y64, abs64),
+    each [T, N], with abs64 = sum |terms| + |r|."""
+    w = _c(w, np.uint8)
+    a = _c(a, np.uint8)
+    r = _c(r, np.float32)
+    assert r.shape == (T, N)
+    y = np.empty((T, N), dtype=np.float32)
+    y64 = np.empty((T, N), dtype=np.float64)
+    ab = np.empty((T, N), dtype=np.float64)
+    _check(lib().oracle_mmvq_add(_ptr(w), _ptr(a), _ptr(r), _ptr(y), _ptr(y64), _ptr(ab), N, K,
+                                 T), "mmvq_add")
     return y, y64, ab
 
 

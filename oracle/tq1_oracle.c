@@ -441,6 +441,29 @@ int oracle_mmvq(const uint8_t *w, const uint8_t *a, float *y, double *y64,
     return bad ? -1 : 0;
 }
 
+/* Mat-vec with a residual: y[t][n] = (the mat-vec's exact value) + r[t][n].
+ * The linear-plus-add of "ops::linear q5: one Capacity=32 K-split rung
+ * serves all T<=96" (its linear_add route): the product as above, then the
+ * residual added once, in fp64, to the fp64 sum of the terms. abs64 is
+ * sum |term| + |r|, the scale of the comparison tolerance. r is [T][N]. */
+int oracle_mmvq_add(const uint8_t *w, const uint8_t *a, const float *r, float *y,
+                    double *y64, double *abs64, int64_t N, int64_t K, int64_t T)
+{
+    if (!r || !y64 || !abs64)
+        return -1;
+    if (oracle_mmvq(w, a, NULL, y64, abs64, N, K, T))
+        return -1;
+    for (int64_t t = 0; t < T; t++)
+        for (int64_t n = 0; n < N; n++) {
+            double rv = (double)r[t * N + n];
+            y64[t * N + n] = y64[t * N + n] + rv;
+            abs64[t * N + n] = abs64[t * N + n] + fabs(rv);
+            if (y)
+                y[t * N + n] = (float)y64[t * N + n];
+        }
+    return 0;
+}
+
 /* The expert-routed products: pair ts = t * n_used + s multiplies expert
  * ids[ts]'s matrix by activation column col(ts), where col(ts) = t when a
  * token's slots share its column and col(ts) = ts when every pair has its own.

@@ -244,3 +244,23 @@ def test_mmvq_id_noalloc_rejects():
                 for E in (1, 64, 4095, 4096) for n in (1, 2, 8, 64) if n <= E)
     assert worst == 729344
     assert worst <= bqm.NOALLOC_SCRATCH_BYTES == 768 * 1024
+
+
+def test_mmvq_add_rejects():
+    # the residual-add products validate like the plain ones, plus the
+    # residual: required, 4-byte aligned, the output itself or disjoint from it
+    lib = bqm.library()
+    Y = P(0x200000)
+    for fn, T in (("mmvq_tq1_0_add", 32), ("mmvq_tq1_0_f32_add", 8)):
+        f = getattr(lib, fn)
+        assert f(GOOD, GOOD, None, Y, 8, 256, 1, None) == -1
+        assert f(None, GOOD, GOOD, Y, 8, 256, 1, None) == -1
+        assert f(GOOD, GOOD, GOOD, None, 8, 256, 1, None) == -1
+        assert f(GOOD, GOOD, GOOD, Y, 8, 256, T + 1, None) == -2
+        assert f(GOOD, GOOD, GOOD, Y, 8, 300, 1, None) == -2
+        # overlapping but not identical residual and output: -2
+        assert f(GOOD, GOOD, P(0x200000 + 16), Y, 8, 256, 2, None) == -2
+        assert f(GOOD, GOOD, P(0x200000 - 16), Y, 8, 256, 2, None) == -2
+        assert f(GOOD, GOOD, P(0x200002), Y, 8, 256, 1, None) == -2   # overlaps, misaligned
+        assert f(GOOD, GOOD, P(0x300002), Y, 8, 256, 1, None) == -3   # disjoint, misaligned
+        assert f(GOOD, GOOD, GOOD, P(0x200002), 8, 256, 1, None) == -3

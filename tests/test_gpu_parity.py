@@ -67,6 +67,14 @@ class _SentinelOutputs:
         kw.setdefault("out", self._y((T, N), w.device))
         return self._m.mmvq_tq1_0_f32(w, x, N, K, T, **kw)
 
+    def mmvq_tq1_0_add(self, w, a, r, N, K, T, **kw):
+        kw.setdefault("out", self._y((T, N), w.device))
+        return self._m.mmvq_tq1_0_add(w, a, r, N, K, T, **kw)
+
+    def mmvq_tq1_0_f32_add(self, w, x, r, N, K, T, **kw):
+        kw.setdefault("out", self._y((T, N), w.device))
+        return self._m.mmvq_tq1_0_f32_add(w, x, r, N, K, T, **kw)
+
     def mmvq_tq1_0_block_isums(self, w, a, N, K, T, **kw):
         kw.setdefault("out", self._full((T, N, K // 32), torch.int32, -2 ** 31, w.device))
         return self._m.mmvq_tq1_0_block_isums(w, a, N, K, T, **kw)
@@ -709,6 +717,55 @@ def test_mmvq_negative_and_subnormal_weight_scales(bqm, N, K, T):
     if T <= 8:
         yf = _host(bqm.mmvq_tq1_0_f32(w, _dev(x), N, K, T))
         assert np.array_equal(yf.view(np.uint32), y.view(np.uint32))
+
+
+# ---------------------------------------------------------------------------
+# Residual add in the epilogue: y = product + r, one fp32 addition after the
+# product's own result
+# ---------------------------------------------------------------------------
+
+# one shape per kernel: staged (one and two columns, three on a large staged
+# grid), quad (four), resident matrix-core (8 and 32 columns), streamed
+# matrix-core (five columns over K too long to keep resident), staged
+# multi-pass rows
+ADD_SHAPES = [(256, 1024, 1), (4500, 4096, 2), (4500, 4096, 3), (333, 2304, 4), (515, 4096, 8),
+              (17, 1280, 32), (50, 9216, 5), (50, 16640, 1)]
+
+
+@pytest.mark.parametrize("N,K,T", ADD_SHAPES)
+def test_mmvq_add_parity(bqm, N, K, T):
+    """Against the oracle's product-plus-residual; bitwise fp32(mmvq + r);
+    the same bits in place (out = r); and the fused fp32-input call (up to 8
+    columns) bitwise fp32(mmvq_f32 + r)."""
+    trits, d16, x = _case(N, K, T, seed=6100 + N + T)
+    w, a, w_ref, a_ref = _prep(bqm, trits, d16, x)
+    rng = np.random.default_rng(6200 + N)
+    r = (rng.standard_normal((T, N)) * 3.0).astype(np.float32)
+    r[0, :min(N, 4)] = [0.0, -0.0, 1e-30, -7.5][:min(N, 4)]
+    _say("mmvq_add", N, K, T)
+    rd = _dev(r)
+    y = _host(bqm.mmvq_tq1_0_add(w, a, rd, N, K, T))
+    _, y64, ab = oracle.mmvq_add(w_ref, a_ref, r, N, K, T)
+    _assert_close(y, y64, ab, "mmvq_add %dx%d T=%d" % (N, K, T))
+    y0 = _host(bqm.mmvq_tq1_0(w, a, N, K, T))
+    assert np.array_equal(y.view(np.uint32), (y0 + r).view(np.uint32))
+    inplace = rd.clone()
+    bqm.mmvq_tq1_0_add(w, a, inplace, N, K, T, out=inplace)
+    assert np.array_equal(_host(inplace).view(np.uint32), y.view(np.uint32))
+    if T <= 8:
+        yf = _host(bqm.mmvq_tq1_0_f32_add(w, _dev(x), rd, N, K, T))
+        assert np.array_equal(yf.view(np.uint32), y.view(np.uint32))
+
+
+def test_mmvq_add_decode_workload(bqm):
+    """The decode workload's fused step with a residual, against the oracle."""
+    wl, inp = _workload_inputs("decode")
+    N, K = wl.N, wl.K
+    w, a, w_ref, a_ref = _prep(bqm, inp.trits, inp.d16, inp.x)
+    r = np.random.default_rng(9).standard_normal((1, N)).astype(np.float32)
+    y = _host(bqm.mmvq_tq1_0_f32_add(w, _dev(inp.x[:1]), _dev(r), N, K, 1))
+    _, y64, ab = oracle.mmvq_add(w_ref, a_ref[:1], r, N, K, 1)
+    _assert_close(y, y64, ab, "decode fused add")
 
 
 def test_mmvq_f32_decode_workload(bqm):

@@ -28,6 +28,10 @@ MUTATIONS = {
                                     "oracle_f16_to_f32(dd[(k / TQ1_BLOCK_ELEMS + 1) % nb])"),
     "bf16_truncates": ("if (lower > 0x8000u || (lower == 0x8000u && (upper & 1u)))",
                        "if (0)"),
+    "residual_subtracted": ("y64[t * N + n] = y64[t * N + n] + rv;",
+                            "y64[t * N + n] = y64[t * N + n] - rv;"),
+    "residual_transposed": ("double rv = (double)r[t * N + n];",
+                            "double rv = (double)r[(n * T + t) % (N * T)];"),
     "slots_read_token_column": ("int64_t col = column_per_pair ? ts : ts / n_used;",
                                 "int64_t col = ts / n_used;"),
 }

@@ -341,6 +341,39 @@ def test_mmvq_scale_and_sign_invariants():
     assert np.array_equal(yp, y1[:, perm])
 
 
+def test_mmvq_add_unit_scales_is_integer_matvec_plus_residual_exactly():
+    """Unit scales and an integer residual: y is the int64 product t @ q plus
+    r, exactly, with r laid out [T][N] (T != N, so a transposed residual or
+    a dropped or negated one fails)."""
+    N, K, T = 5, 768, 3
+    rng = np.random.default_rng(41)
+    trits = synth.ternary(rng, (N, K))
+    q = rng.integers(-127, 128, (T, K)).astype(np.int8)
+    a = synth.q8_1_blocks_from_fields(q, np.full((T, K // 32), 0x3C00, np.uint16),
+                                      np.zeros((T, K // 32), np.uint16))
+    w = oracle.tq1_pack(trits, np.full((N, K // 256), 0x3C00, np.uint16))
+    r = rng.integers(-5000, 5000, (T, N)).astype(np.float32)
+    y, y64, ab = oracle.mmvq_add(w, a, r, N, K, T)
+    ref = q.astype(np.int64) @ trits.astype(np.int64).T + r.astype(np.int64)
+    assert np.array_equal(y64, ref.astype(np.float64))
+    assert np.array_equal(y, ref.astype(np.float32))
+    # the tolerance scale: sum |term| over the 32-element sub-block terms
+    # (unit scales: |sub-block integer sum|) plus |r|
+    prod = trits.astype(np.int64)[None, :, :] * q.astype(np.int64)[:, None, :]
+    sub = np.abs(prod.reshape(T, N, K // 32, 32).sum(axis=3)).sum(axis=2)
+    assert np.array_equal(ab, sub + np.abs(r))
+
+
+def test_mmvq_add_zero_residual_is_mmvq():
+    N, K, T = 12, 1024, 2
+    trits, d16, x = _case(N, K, T, 42)
+    w = oracle.tq1_pack(trits, d16)
+    a = oracle.q8_1_quantize(x)
+    y0, y640, ab0 = oracle.mmvq(w, a, N, K, T)
+    y, y64, ab = oracle.mmvq_add(w, a, np.zeros((T, N), np.float32), N, K, T)
+    assert np.array_equal(y, y0) and np.array_equal(y64, y640) and np.array_equal(ab, ab0)
+
+
 def test_mmvq_id_equals_gathered_mmvq():
     E, N, K, T, n_used = 6, 10, 512, 4, 3
     rng = np.random.default_rng(41)
