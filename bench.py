@@ -376,10 +376,83 @@ def dequant_rows(torch, bqm, wrot, R, wbytes, name, N, K, launches):
     return rows_out
 
 
+class SweepTimer:
+    """Times sweep rows and tags them for the kernel trace.
+
+    Around each row's graph two marker dispatches (the empty probe kernel on
+    MARKER_BASE + 2 row-index workgroups before, one more after) are
+    launched, so that a rocprofv3 kernel trace of the sweep can be cut into
+    rows (--trace-summary). After
+    the timing the row records a position-weighted checksum of its output,
+    sum over k of (k + 1) * y[k] in float64 over the flattened output, which
+    moves when an output lands in the wrong place."""
+
+    MARKER_BASE = 1000
+
+    def __init__(self, torch, table):
+        self.torch = torch
+        self.table = table
+        self.probes = ctypes.CDLL(os.path.join(ROOT, "bit_quantized_mat_amd",
+                                               "libbqm_probes.so"))
+        self.probes.bqm_probe_empty.argtypes = [ctypes.c_int, ctypes.c_void_p]
+
+    def marker(self, tag, end):
+        torch = self.torch
+        self.probes.bqm_probe_empty(self.MARKER_BASE + 2 * tag + int(end),
+                                    ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+
+    def time(self, row, launch, count, out=None):
+        torch = self.torch
+        self.marker(len(self.table), False)
+        us = graph_us(torch, launch, count)
+        self.marker(len(self.table), True)
+        row["us"] = round(us, 3)
+        row["launches"] = count
+        row["row_index"] = len(self.table)
+        if out is not None:
+            torch.cuda.synchronize()
+            v = out.detach().reshape(-1).double()
+            k = torch.arange(1, v.numel() + 1, dtype=torch.float64, device=v.device)
+            row["checksum"] = float((k * v).sum().item())
+        self.table.append(row)
+        log("sweep", row)
+        return us
+
+
+def _rate_fields(row, b, us, read_gbs=None):
+    row["algorithmic_bytes"] = b
+    row["gbs"] = round(b / us / 1e3, 1)
+    row["frac_of_8tbs"] = round(b / us / 1e3 / HBM_PEAK_GBS, 4)
+    if read_gbs:
+        # fraction of what a plain read of the same weight bytes reaches in one
+        # dispatch (the read probe's rate on this workload's matrix)
+        row["frac_of_read_probe"] = round(b / us / 1e3 / read_gbs, 4)
+
+
 def sweep(path, torch, np, bqm, synth, dev, launches, only=None):
-    """Every workload shape and column count, cold weights, graph-timed.
+    """Every workload shape and column count, cold weights, graph-timed; an
+    untouched control row (decode T = 1) first and last to bound drift.
     only: optional set of workload names to restrict the sweep to."""
     table = []
+    timer = SweepTimer(torch, table)
+
+    def control(label):
+        wl = synth.WORKLOADS["decode"]
+        inp = synth.make_inputs(wl)
+        N, K = wl.N, wl.K
+        w0 = bqm.tq1_pack(torch.from_numpy(inp.trits).to(dev),
+                          torch.from_numpy(inp.d16.view(np.int16)).to(dev))
+        wrot, R = rotation(torch, w0, dev)
+        a = bqm.q8_1_quantize(torch.from_numpy(inp.x[:1]).to(dev))
+        y = torch.empty((1, N), dtype=torch.float32, device=dev)
+        row = {"workload": "control (decode, " + label + ")", "op": "mmvq_tq1_0", "N": N, "K": K,
+               "T": 1}
+        us = timer.time(row, lambda i: bqm.mmvq_tq1_0(wrot[i % R], a, N, K, 1, out=y), launches, y)
+        _rate_fields(row, algorithmic_bytes(N, K, 1), us)
+        del wrot, w0
+        torch.cuda.empty_cache()
+
+    control("session start")
     for name in ("tiny", "decode", "multicol", "ffn"):
         if only and name not in only:
             continue
@@ -391,20 +464,17 @@ def sweep(path, torch, np, bqm, synth, dev, launches, only=None):
         wrot, R = rotation(torch, w0, dev)
         a_all = bqm.q8_1_quantize(torch.from_numpy(inp.x).to(dev))
         table.append(read_probe_row(torch, wrot, R, w0.numel(), name, launches))
+        read_gbs = table[-1]["gbs"]
         log("sweep", table[-1])
         if name in ("decode", "ffn"):
             table.extend(dequant_rows(torch, bqm, wrot, R, w0.numel(), name, N, K, launches))
         for T in wl.Ts:
             a = a_all[:T].contiguous()
             y = torch.empty((T, N), dtype=torch.float32, device=dev)
-            us = graph_us(torch, lambda i: bqm.mmvq_tq1_0(wrot[i % R], a, N, K, T, out=y),
-                          launches)
-            b = algorithmic_bytes(N, K, T)
-            row = {"workload": name, "op": "mmvq_tq1_0", "N": N, "K": K, "T": T, "us": round(us, 3),
-                   "algorithmic_bytes": b, "gbs": round(b / us / 1e3, 1),
-                   "frac_of_8tbs": round(b / us / 1e3 / HBM_PEAK_GBS, 4)}
-            table.append(row)
-            log("sweep", row)
+            row = {"workload": name, "op": "mmvq_tq1_0", "N": N, "K": K, "T": T}
+            us = timer.time(row, lambda i: bqm.mmvq_tq1_0(wrot[i % R], a, N, K, T, out=y),
+                            launches, y)
+            _rate_fields(row, algorithmic_bytes(N, K, T), us, read_gbs)
         del wrot, a_all, w0
         torch.cuda.empty_cache()
     # many-column product: prefill batches on the decode and ffn matrices
@@ -422,70 +492,103 @@ def sweep(path, torch, np, bqm, synth, dev, launches, only=None):
         for T in PREFILL_COLS:
             a = a_all[:T].contiguous()
             y = torch.empty((T, N), dtype=torch.float32, device=dev)
-            us = graph_us(torch, lambda i: bqm.mm_tq1_0(wrot[i % R], a, N, K, T, out=y),
-                          max(10, launches // 4))
-            b = algorithmic_bytes(N, K, T)
-            row = {"workload": name + " prefill", "op": "mm_tq1_0", "N": N, "K": K, "T": T,
-                   "us": round(us, 3), "algorithmic_bytes": b, "gbs": round(b / us / 1e3, 1),
-                   "frac_of_8tbs": round(b / us / 1e3 / HBM_PEAK_GBS, 4),
-                   "int8_tops": round(2.0 * N * K * T / us / 1e6, 1)}
-            table.append(row)
-            log("sweep", row)
+            row = {"workload": name + " prefill", "op": "mm_tq1_0", "N": N, "K": K, "T": T}
+            us = timer.time(row, lambda i: bqm.mm_tq1_0(wrot[i % R], a, N, K, T, out=y),
+                            max(10, launches // 4), y)
+            _rate_fields(row, algorithmic_bytes(N, K, T), us)
+            row["int8_tops"] = round(2.0 * N * K * T / us / 1e6, 1)
         del wrot, a_all, w0
         torch.cuda.empty_cache()
-    if only and "moe" not in only:
-        with open(path, "w") as f:
-            json.dump(table, f, indent=1)
-        return table
-    wl = synth.WORKLOADS["moe"]
-    inp = synth.make_inputs(wl)
-    E, N, K, n_used = wl.experts, wl.N, wl.K, wl.n_used
-    w0 = bqm.tq1_pack(torch.from_numpy(inp.trits).to(dev),
-                      torch.from_numpy(inp.d16.view(np.int16)).to(dev))
-    wrot, R = rotation(torch, w0, dev)
-    a_all = bqm.q8_1_quantize(torch.from_numpy(inp.x).to(dev))
-    table.append(read_probe_row(torch, wrot, R, w0.numel(), "moe (all experts)", launches))
-    log("sweep", table[-1])
-    for T in wl.Ts:
-        ids_np = np.ascontiguousarray(inp.ids[:T])
-        ids = torch.from_numpy(ids_np).to(dev)
-        a = a_all[:T].contiguous()
-        y = torch.empty((T, n_used, N), dtype=torch.float32, device=dev)
-        ws = torch.empty(max(bqm.mmvq_id_tq1_0_workspace_bytes(E, T, n_used), 256),
-                         dtype=torch.uint8, device=dev)
-        us = graph_us(torch, lambda i: bqm.mmvq_id_tq1_0(wrot[i % R], a, ids, E, N, K, T, n_used,
-                                                         out=y, workspace=ws), launches)
-        b, distinct = moe_algorithmic_bytes(ids_np, N, K)
-        row = {"workload": "moe", "op": "mmvq_id_tq1_0", "E": E, "N": N, "K": K, "T": T,
-               "n_used": n_used, "distinct_experts": distinct, "us": round(us, 3),
-               "algorithmic_bytes": b, "gbs": round(b / us / 1e3, 1),
-               "frac_of_8tbs": round(b / us / 1e3 / HBM_PEAK_GBS, 4)}
-        table.append(row)
-        log("sweep", row)
-    # one activation per (token, slot) pair: the down-projection shape
-    a_slots = bqm.q8_1_quantize(torch.from_numpy(synth.slot_activations(wl)).to(dev))
-    for T in wl.Ts:
-        ids_np = np.ascontiguousarray(inp.ids[:T])
-        ids = torch.from_numpy(ids_np).to(dev)
-        a = a_slots[:T * n_used].contiguous()
-        y = torch.empty((T, n_used, N), dtype=torch.float32, device=dev)
-        ws = torch.empty(max(bqm.mmvq_id_tq1_0_workspace_bytes(E, T, n_used), 256),
-                         dtype=torch.uint8, device=dev)
-        us = graph_us(torch, lambda i: bqm.mmvq_id_tq1_0_slots(wrot[i % R], a, ids, E, N, K, T,
-                                                               n_used, out=y, workspace=ws),
-                      launches)
-        b, distinct = moe_algorithmic_bytes(ids_np, N, K, per_slot=True)
-        row = {"workload": "moe", "op": "mmvq_id_tq1_0_slots", "E": E, "N": N, "K": K, "T": T,
-               "n_used": n_used, "distinct_experts": distinct, "us": round(us, 3),
-               "algorithmic_bytes": b, "gbs": round(b / us / 1e3, 1),
-               "frac_of_8tbs": round(b / us / 1e3 / HBM_PEAK_GBS, 4)}
-        table.append(row)
-        log("sweep", row)
-    del wrot, a_all, a_slots, w0
-    torch.cuda.empty_cache()
+    if not only or "moe" in only:
+        wl = synth.WORKLOADS["moe"]
+        inp = synth.make_inputs(wl)
+        E, N, K, n_used = wl.experts, wl.N, wl.K, wl.n_used
+        w0 = bqm.tq1_pack(torch.from_numpy(inp.trits).to(dev),
+                          torch.from_numpy(inp.d16.view(np.int16)).to(dev))
+        wrot, R = rotation(torch, w0, dev)
+        a_all = bqm.q8_1_quantize(torch.from_numpy(inp.x).to(dev))
+        table.append(read_probe_row(torch, wrot, R, w0.numel(), "moe (all experts)", launches))
+        read_gbs = table[-1]["gbs"]
+        log("sweep", table[-1])
+        a_slots = bqm.q8_1_quantize(torch.from_numpy(synth.slot_activations(wl)).to(dev))
+        for op, per_slot in (("mmvq_id_tq1_0", False), ("mmvq_id_tq1_0_slots", True)):
+            fn = getattr(bqm, op)
+            for T in wl.Ts:
+                ids_np = np.ascontiguousarray(inp.ids[:T])
+                ids = torch.from_numpy(ids_np).to(dev)
+                a = (a_slots[:T * n_used] if per_slot else a_all[:T]).contiguous()
+                y = torch.empty((T, n_used, N), dtype=torch.float32, device=dev)
+                ws = torch.empty(max(bqm.mmvq_id_tq1_0_workspace_bytes(E, T, n_used), 256),
+                                 dtype=torch.uint8, device=dev)
+                b, distinct = moe_algorithmic_bytes(ids_np, N, K, per_slot=per_slot)
+                row = {"workload": "moe", "op": op, "E": E, "N": N, "K": K, "T": T,
+                       "n_used": n_used, "distinct_experts": distinct}
+                us = timer.time(row, lambda i: fn(wrot[i % R], a, ids, E, N, K, T, n_used, out=y,
+                                                  workspace=ws), launches, y)
+                _rate_fields(row, b, us, read_gbs)
+        del wrot, a_all, a_slots, w0
+        torch.cuda.empty_cache()
+    control("session end")
     with open(path, "w") as f:
         json.dump(table, f, indent=1)
     return table
+
+
+def trace_summary(trace_csv, sweep_json, out_md):
+    """Per-row kernel durations of a sweep run under rocprofv3 --kernel-trace:
+    the marker dispatches cut the trace into rows; within a row every call
+    (its kernels: 1 for the products, up to 3 for the expert-routed one) is
+    one unit, its duration the sum of its kernels' (end - start); median,
+    p10 and p90 over all replayed calls. Writes them into the sweep JSON and
+    a markdown table."""
+    import csv
+    with open(trace_csv) as f:
+        recs = list(csv.DictReader(f))
+    key = lambda r, *names: next(r[n] for n in names if n in r)
+    recs.sort(key=lambda r: int(key(r, "Start_Timestamp", "start_timestamp")))
+    with open(sweep_json) as f:
+        table = json.load(f)
+    rows = {r["row_index"]: r for r in table if "row_index" in r}
+    seg, cur = {}, None
+    for r in recs:
+        name = key(r, "Kernel_Name", "kernel_name")
+        grid = int(key(r, "Grid_Size_X", "Grid_Size", "grid_size_x"))
+        wg = int(key(r, "Workgroup_Size_X", "Workgroup_Size", "workgroup_size_x"))
+        if "empty_kernel" in name and grid // max(wg, 1) >= SweepTimer.MARKER_BASE:
+            m = grid // wg - SweepTimer.MARKER_BASE
+            cur = None if m & 1 else m // 2
+            if cur is not None:
+                seg[cur] = []
+            continue
+        if cur is not None and cur in rows:
+            d = (int(key(r, "End_Timestamp", "end_timestamp")) -
+                 int(key(r, "Start_Timestamp", "start_timestamp"))) / 1e3
+            seg[cur].append((name, d))
+    lines = ["| row | workload | op | T | calls | kernels per call | median µs | p10 | p90 | "
+             "event-timed µs |", "|---|---|---|---|---|---|---|---|---|---|"]
+    for idx, row in sorted(rows.items()):
+        ds = seg.get(idx, [])
+        # each row's graph is replayed twice (warm, then timed)
+        ncalls = 2 * row["launches"]
+        if not ds or len(ds) % ncalls:
+            row["trace"] = {"dispatches": len(ds), "note": "dispatch count not a multiple of calls"}
+            continue
+        kpc = len(ds) // ncalls
+        calls = [sum(d for _, d in ds[c * kpc:(c + 1) * kpc]) for c in range(ncalls)]
+        calls.sort()
+        q = lambda p: calls[min(len(calls) - 1, int(p * len(calls)))]
+        med = calls[len(calls) // 2]
+        row["trace"] = {"calls": ncalls, "kernels_per_call": kpc, "median_us": round(med, 3),
+                        "p10_us": round(q(0.10), 3), "p90_us": round(q(0.90), 3),
+                        "kernels": sorted(set(n.split("(")[0] for n, _ in ds))}
+        lines.append("| %d | %s | %s | %s | %d | %d | %.3f | %.3f | %.3f | %.3f |" % (
+            idx, row["workload"], row["op"], row.get("T", ""), ncalls, kpc, med, q(0.10),
+            q(0.90), row["us"]))
+    with open(sweep_json, "w") as f:
+        json.dump(table, f, indent=1)
+    with open(out_md, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
 
 
 def profile_run(spec, torch, np, bqm, synth, dev):
@@ -612,6 +715,9 @@ def main():
     ap.add_argument("--write-counters", nargs=3, metavar=("FETCH_DIR", "WRITE_DIR", "PROBE_BYTES"),
                     help="no GPU: turn two rocprofv3 --pmc runs of --profile decode:1 "
                          "(FETCH_SIZE, then WRITE_SIZE) into the committed traffic figures")
+    ap.add_argument("--trace-summary", nargs=3, metavar=("TRACE_CSV", "SWEEP_JSON", "OUT_MD"),
+                    help="no GPU: per-row median/p10/p90 kernel durations of a sweep run "
+                         "under rocprofv3 --kernel-trace")
     ap.add_argument("--cpu-table", metavar="PATH",
                     help="no GPU: time the oracle on every workload (one thread and all the "
                          "job's CPUs) and write a JSON table")
@@ -619,6 +725,9 @@ def main():
 
     if args.cpu_table:
         cpu_table(args.cpu_table)
+        return
+    if args.trace_summary:
+        trace_summary(*args.trace_summary)
         return
 
     if args.write_counters:

@@ -76,6 +76,12 @@ int launch_mmvq_mfma(const void *w, const void *a, float *y, int32_t *isums, int
 bool mfma_resident_supported(int64_t K, int32_t T);
 int launch_mmvq_mfma_resident(const void *w, const void *a, float *y, int32_t *isums, int64_t N,
                               int64_t K, int32_t T, hipStream_t stream, const float *r = nullptr);
+// Matrix-core kernel with each wave's activation operands in registers
+// (rows of 5 to 16 blocks, up to 32 columns): whether it takes this shape,
+// and its launcher.
+bool mfma_reg_supported(int64_t K, int32_t T);
+int launch_mmvq_mfma_reg(const void *w, const void *a, float *y, int32_t *isums, int64_t N,
+                         int64_t K, int32_t T, hipStream_t stream, const float *r = nullptr);
 // Its expert-routed mode (wide work items of up to 16 pairs, written by the
 // routing pre-pass): whether it takes rows of K elements, and its launcher.
 bool mfma_resident_id_supported(int64_t K);

@@ -30,62 +30,6 @@
 namespace bqm {
 
 constexpr int kMfmaMaxWaves = 8;     // waves per workgroup
-constexpr int kStageCol = 74;        // dwords per staged column: 8 x 9 of Q8_1 data, 2 of padding
-
-// Block B of activation columns 0 .. 16 NT - 1, in flight to this wave's
-// stage: column c's eight Q8_1 blocks (288 bytes, 36 pieces of 8 bytes) go to
-// dwords c * kStageCol .. c * kStageCol + 71. A 16-column tile is 576 pieces,
-// nine per lane: piece i = lane + 64 k. The loads are issued one block ahead
-// and written to LDS once the stage is free.
-//
-// Columns at or past T are not masked: their loads fall past the end of the
-// activation buffer and read zeros, or (when the 32-bit offset wraps) some
-// in-range bytes, and either way they only feed output columns that are never
-// stored.
-struct StageMap {
-    uint32_t gofs[9];  // byte offset of piece k in block 0 of column tile 0
-    uint32_t lofs[9];  // its dword offset in the stage
-
-    __device__ __forceinline__ StageMap(uint32_t col_bytes, int lane)
-    {
-#pragma unroll
-        for (int k = 0; k < 9; k++) {
-            const int i = lane + 64 * k;
-            const int c = i / 36, p = i - 36 * c;
-            gofs[k] = (uint32_t)c * col_bytes + 8 * p;
-            lofs[k] = c * kStageCol + 2 * p;
-        }
-    }
-};
-
-template <int NT>
-struct StagePieces {
-    u32x2 v[NT][9];
-
-    __device__ __forceinline__ void issue(__amdgpu_buffer_rsrc_t ra, const StageMap &m,
-                                          uint32_t col_bytes, int B)
-    {
-#pragma unroll
-        for (int ct = 0; ct < NT; ct++) {
-            // wave-uniform part of the offset
-            const uint32_t so = __builtin_amdgcn_readfirstlane(
-                (uint32_t)B * (8 * kQ81BlockBytes) + (uint32_t)ct * 16 * col_bytes);
-#pragma unroll
-            for (int k = 0; k < 9; k++)
-                v[ct][k] = __builtin_amdgcn_raw_buffer_load_b64(ra, m.gofs[k], so, 0);
-        }
-    }
-
-    __device__ __forceinline__ void land(uint32_t *__restrict__ stage, const StageMap &m) const
-    {
-#pragma unroll
-        for (int ct = 0; ct < NT; ct++)
-#pragma unroll
-            for (int k = 0; k < 9; k++)
-                *reinterpret_cast<u32x2 *>(stage + ct * 16 * kStageCol + m.lofs[k]) = v[ct][k];
-    }
-};
-
 // GPW: butterfly groups per wave (Lr / waves); NT: 16-column tiles (1 or 2);
 // R: 16-row tiles that share each staged activation block; ISUMS: write the
 // exact per-sub-block sums instead of outputs.

@@ -217,6 +217,8 @@ int launch_mmvq(const void *w, const void *a, float *y, int32_t *isums, int64_t 
         return launch_mmvq_quad(w, a, y, isums, N, K, T, stream, r);
     if (use_staged(N, K, T))
         return launch_mmvq_staged(w, a, y, isums, N, K, T, stream, r);
+    if (mfma_reg_supported(K, T))
+        return launch_mmvq_mfma_reg(w, a, y, isums, N, K, T, stream, r);
     if (mfma_resident_supported(K, T))
         return launch_mmvq_mfma_resident(w, a, y, isums, N, K, T, stream, r);
     return launch_mmvq_mfma(w, a, y, isums, N, K, T, stream, r);

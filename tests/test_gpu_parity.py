@@ -148,17 +148,23 @@ def _case(N, K, T, seed, p_zero=1 / 3, outliers=0.01, d_lo=0.01, d_hi=0.1):
 # (which kernel takes each: staged for T < 3, and for T = 3, 4 when the
 # call gives the staged grid more than one wave per SIMD (4500 x 4096,
 # 4200 x 2560) or the matrix-core kernel cannot keep the columns resident
-# (67 x 768); otherwise the matrix-core kernel, with the activations resident
-# in LDS when they fit and a row has at least as many lane groups as the
-# workgroup has waves, else streamed per block)
-# The last four put the one- and two-column staged kernel on rows longer than
-# one staging pass (more than 64 blocks: passes of 64 below 128 blocks, of
-# 128 from there): 65 blocks (a one-block last pass), 96 (a partial second
-# pass), 129 (two full passes of 128 and a one-block tail) and 256.
+# (67 x 768); otherwise the matrix-core kernels: for rows of 5 to 16 blocks
+# the one with each wave's activation operands in registers (8 or 16 waves,
+# one or two column tiles; 130 x 2304 leaves 7 of its 16 waves without a
+# block), else the one with the activations resident in LDS when they fit and
+# a row has at least as many lane groups as the workgroup has waves, else
+# the one streaming them per block)
+# Four put the one- and two-column staged kernel on rows longer than one
+# staging pass (more than 64 blocks: passes of 64 below 128 blocks, of 128
+# from there): 65 blocks (a one-block last pass), 96 (a partial second pass),
+# 129 (two full passes of 128 and a one-block tail) and 256. The last two
+# give the register-operand kernel more row tiles than workgroups (several
+# tiles per workgroup, both halves of its partial-sum buffer).
 SHAPES = [(256, 1024, 1), (1, 256, 1), (33, 256, 2), (67, 768, 3), (130, 2304, 5),
           (515, 4096, 8), (96, 6144, 4), (40, 16384, 1), (17, 1280, 32), (300, 512, 16),
           (40, 16384, 6), (50, 9216, 5), (21, 4096, 17), (1, 2304, 9), (4500, 4096, 3),
-          (4200, 2560, 4), (50, 16640, 1), (33, 24576, 2), (300, 33024, 1), (70, 65536, 2)]
+          (4200, 2560, 4), (50, 16640, 1), (33, 24576, 2), (300, 33024, 1), (70, 65536, 2),
+          (9000, 4096, 7), (20000, 2048, 24)]
 
 
 # ---------------------------------------------------------------------------
@@ -313,7 +319,8 @@ def test_mmvq_one_hot_element_map(bqm):
 # the expanded block for three)
 @pytest.mark.parametrize("N,K,T", [(320, 6144, 8), (100, 6144, 20), (70, 16384, 32),
                                    (48, 4096, 12), (33, 768, 9), (40, 2048, 10), (24, 512, 6),
-                                   (4500, 4096, 2), (4300, 6144, 3)])
+                                   (4500, 4096, 2), (4300, 6144, 3), (50, 4096, 20),
+                                   (40, 2048, 25), (9000, 4096, 7)])
 def test_mmvq_columns_equal_single_column_calls(bqm, N, K, T):
     """Column t of a T-column call equals the one-column call bit for bit:
     integer sums and fp32 outputs (staged kernel up to 8 columns, matrix-core
