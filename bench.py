@@ -670,6 +670,60 @@ def _counter_medians(csv_dir, counter):
     return {k: statistics.median(v) for k, v in vals.items()}
 
 
+def _kernel_family(name):
+    """A kernel's name without its parameter list."""
+    import re
+    name = name.replace("(anonymous namespace)::", "")
+    name = re.sub(r"^void ", "", name)
+    return name.split("(")[0]
+
+
+def counter_table(dirs, probe_bytes=None):
+    """Median per-dispatch counter values by kernel, from rocprofv3 --pmc csv
+    output directories (one per counter pass), as a markdown table; with
+    probe_bytes (the bytes the read and copy probes move, printed by
+    --profile), FETCH_SIZE and WRITE_SIZE also as bytes, scaled by bytes
+    moved / counter reading of the copy probe."""
+    import csv
+    import glob
+    import statistics
+    vals = {}
+    for d in dirs:
+        for path in glob.glob(os.path.join(d, "*counter_collection.csv")):
+            with open(path) as f:
+                for r in csv.DictReader(f):
+                    fam = _kernel_family(r["Kernel_Name"])
+                    if not (fam in ("read_kernel", "copy_kernel") or fam.startswith("bqm::")):
+                        continue
+                    vals.setdefault(fam, {}).setdefault(r["Counter_Name"], []).append(
+                        float(r["Counter_Value"]))
+    med = {k: {c: statistics.median(v) for c, v in cs.items()} for k, cs in vals.items()}
+    scale = {}
+    if probe_bytes:
+        cp = med.get("copy_kernel", {})
+        for c in ("FETCH_SIZE", "WRITE_SIZE"):
+            if cp.get(c):
+                scale[c] = probe_bytes / cp[c]
+    lines = ["| kernel | counter | median per dispatch | derived |", "|---|---|---|---|"]
+    for k in sorted(med):
+        cs = med[k]
+        waves = cs.get("SQ_WAVES")
+        for c in sorted(cs):
+            v = cs[c]
+            d = ""
+            if c in scale:
+                d = "%.0f bytes" % (v * scale[c])
+            elif c == "SQ_INSTS_VALU" and waves:
+                d = "%.0f per wave, %.0f per SIMD (%.2f us of issue at 4 cycles, 2.4 GHz)" % (
+                    v / waves, v / 1024, v / 1024 * 4 / 2400)
+            elif c.startswith("SQ_INSTS_") and waves:
+                d = "%.1f per wave" % (v / waves)
+            lines.append("| `%s` | %s | %.6g | %s |" % (k, c, v, d))
+    out = "\n".join(lines)
+    print(out)
+    return out
+
+
 def write_counters(fetch_dir, write_dir, probe_bytes):
     """HBM bytes per launch of the decode step's kernel (the fused quantize
     and mat-vec) from two counter runs of `--profile decode:1`: FETCH_SIZE and
@@ -718,6 +772,10 @@ def main():
     ap.add_argument("--trace-summary", nargs=3, metavar=("TRACE_CSV", "SWEEP_JSON", "OUT_MD"),
                     help="no GPU: per-row median/p10/p90 kernel durations of a sweep run "
                          "under rocprofv3 --kernel-trace")
+    ap.add_argument("--counter-table", nargs="+", metavar="DIR",
+                    help="no GPU: markdown table of median counter values per kernel from "
+                         "rocprofv3 --pmc output directories (a leading number is the probe "
+                         "bytes for the FETCH_SIZE / WRITE_SIZE scale)")
     ap.add_argument("--cpu-table", metavar="PATH",
                     help="no GPU: time the oracle on every workload (one thread and all the "
                          "job's CPUs) and write a JSON table")
@@ -728,6 +786,13 @@ def main():
         return
     if args.trace_summary:
         trace_summary(*args.trace_summary)
+        return
+    if args.counter_table:
+        first = args.counter_table[0]
+        if first.isdigit():
+            counter_table(args.counter_table[1:], int(first))
+        else:
+            counter_table(args.counter_table)
         return
 
     if args.write_counters:
