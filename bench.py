@@ -560,12 +560,13 @@ def trace_summary(trace_csv, sweep_json, out_md):
             if cur is not None:
                 seg[cur] = []
             continue
-        if cur is not None and cur in rows:
+        if cur is not None and cur in rows and _kernel_family(name).startswith("bqm::"):
+            # (torch's own small kernels of the graph capture are left out)
             d = (int(key(r, "End_Timestamp", "end_timestamp")) -
                  int(key(r, "Start_Timestamp", "start_timestamp"))) / 1e3
             seg[cur].append((name, d))
     lines = ["| row | workload | op | T | calls | kernels per call | median µs | p10 | p90 | "
-             "event-timed µs |", "|---|---|---|---|---|---|---|---|---|---|"]
+             "replay corr. | event-timed µs |", "|---|---|---|---|---|---|---|---|---|---|---|"]
     for idx, row in sorted(rows.items()):
         ds = seg.get(idx, [])
         # each row's graph is replayed twice (warm, then timed)
@@ -575,20 +576,83 @@ def trace_summary(trace_csv, sweep_json, out_md):
             continue
         kpc = len(ds) // ncalls
         calls = [sum(d for _, d in ds[c * kpc:(c + 1) * kpc]) for c in range(ncalls)]
+        # the two replays run the same launches on the same weight copies in
+        # the same order: a duration spread tied to the copy (where its pages
+        # sit in HBM) repeats from one replay to the other, one that comes
+        # from the moment does not
+        half = ncalls // 2
+        a, b = calls[:half], calls[half:]
+        ma, mb = sum(a) / half, sum(b) / half
+        cov = sum((x - ma) * (z - mb) for x, z in zip(a, b))
+        va = sum((x - ma) ** 2 for x in a)
+        vb = sum((z - mb) ** 2 for z in b)
+        replay_corr = cov / (va * vb) ** 0.5 if va > 0 and vb > 0 else 0.0
         calls.sort()
         q = lambda p: calls[min(len(calls) - 1, int(p * len(calls)))]
         med = calls[len(calls) // 2]
         row["trace"] = {"calls": ncalls, "kernels_per_call": kpc, "median_us": round(med, 3),
                         "p10_us": round(q(0.10), 3), "p90_us": round(q(0.90), 3),
-                        "kernels": sorted(set(n.split("(")[0] for n, _ in ds))}
-        lines.append("| %d | %s | %s | %s | %d | %d | %.3f | %.3f | %.3f | %.3f |" % (
+                        "replay_corr": round(replay_corr, 3),
+                        "kernels": sorted(set(_kernel_family(n) for n, _ in ds))}
+        if "algorithmic_bytes" in row:
+            row["trace"]["gbs_at_median"] = round(row["algorithmic_bytes"] / med / 1e3, 1)
+        lines.append("| %d | %s | %s | %s | %d | %d | %.3f | %.3f | %.3f | %.2f | %.3f |" % (
             idx, row["workload"], row["op"], row.get("T", ""), ncalls, kpc, med, q(0.10),
-            q(0.90), row["us"]))
+            q(0.90), replay_corr, row["us"]))
     with open(sweep_json, "w") as f:
         json.dump(table, f, indent=1)
     with open(out_md, "w") as f:
         f.write("\n".join(lines) + "\n")
     print("\n".join(lines))
+
+
+def sweep_report(sweep_json, traced_json=None, cpu_json=None):
+    """Markdown tables of a sweep (event-timed rows; with traced_json, the
+    per-dispatch median, p10 and p90 of the same rows from a traced run after
+    --trace-summary; with cpu_json, the oracle's times from --cpu-table)."""
+    with open(sweep_json) as f:
+        rows = json.load(f)
+    tr = {}
+    if traced_json:
+        with open(traced_json) as f:
+            tr = {(r["workload"], r["op"], r.get("T")): r.get("trace") for r in json.load(f)
+                  if r.get("trace") and "median_us" in r.get("trace", {})}
+    cpu = {}
+    if cpu_json:
+        with open(cpu_json) as f:
+            c = json.load(f)
+        cpu = {(r["workload"], r["T"]): r for r in c["rows"]}
+    out = ["| workload | op | N x K | T | event µs | GB/s | % of 8 TB/s | % of read probe | "
+           "trace median µs (p10, p90) | GB/s at median | oracle µs, 1 thread / all | "
+           "checksum |", "|---|---|---|---|---|---|---|---|---|---|---|---|"]
+    for r in rows:
+        if r["op"] in ("read_probe", "copy_probe", "tq1_dequantize", "tq1_get_rows"):
+            continue
+        t = tr.get((r["workload"], r["op"], r.get("T")))
+        cp = cpu.get((r["workload"], r.get("T"))) if r["op"].startswith("mmvq") else None
+        nk = ("%d x %d x %d" % (r["E"], r["N"], r["K"])) if "E" in r else (
+            "%d x %d" % (r["N"], r["K"]))
+        out.append("| %s | %s | %s | %s | %.3f | %.1f | %.1f | %s | %s | %s | %s | %s |" % (
+            r["workload"] + ((" (%d distinct)" % r["distinct_experts"]) if "distinct_experts" in r
+                             else ""),
+            r["op"], nk, r.get("T", ""), r["us"], r["gbs"], 100 * r["frac_of_8tbs"],
+            ("%.1f" % (100 * r["frac_of_read_probe"])) if r.get("frac_of_read_probe") else "",
+            ("%.3f (%.3f, %.3f)" % (t["median_us"], t["p10_us"], t["p90_us"])) if t else "",
+            ("%.1f" % t["gbs_at_median"]) if t and "gbs_at_median" in t else "",
+            ("%.0f / %.0f" % (cp["oracle_us_one"], cp["oracle_us_all"])) if cp else "",
+            ("%.6g" % r["checksum"]) if "checksum" in r else ""))
+    out.append("")
+    out.append("| workload | op | bytes | µs | GB/s | % of 8 TB/s |")
+    out.append("|---|---|---|---|---|---|")
+    for r in rows:
+        if r["op"] in ("read_probe", "copy_probe", "tq1_dequantize", "tq1_get_rows"):
+            b = r.get("bytes") or r.get("bytes_moved") or r.get("algorithmic_bytes")
+            out.append("| %s | %s%s | %d | %.3f | %.1f | %.1f |" % (
+                r["workload"], r["op"], (" " + r["dtype"]) if "dtype" in r else "", b, r["us"],
+                r["gbs"], 100 * r["frac_of_8tbs"]))
+    text = "\n".join(out)
+    print(text)
+    return text
 
 
 def profile_run(spec, torch, np, bqm, synth, dev):
@@ -776,6 +840,9 @@ def main():
                     help="no GPU: markdown table of median counter values per kernel from "
                          "rocprofv3 --pmc output directories (a leading number is the probe "
                          "bytes for the FETCH_SIZE / WRITE_SIZE scale)")
+    ap.add_argument("--sweep-report", nargs="+", metavar="JSON",
+                    help="no GPU: markdown tables of a sweep JSON [traced sweep JSON after "
+                         "--trace-summary [--cpu-table JSON]]")
     ap.add_argument("--cpu-table", metavar="PATH",
                     help="no GPU: time the oracle on every workload (one thread and all the "
                          "job's CPUs) and write a JSON table")
@@ -786,6 +853,9 @@ def main():
         return
     if args.trace_summary:
         trace_summary(*args.trace_summary)
+        return
+    if args.sweep_report:
+        sweep_report(*args.sweep_report)
         return
     if args.counter_table:
         first = args.counter_table[0]
