@@ -59,6 +59,15 @@ def lib():
         L.oracle_mmvq_id.restype = ctypes.c_int
         L.oracle_mmvq_id_slots.argtypes = [_p, _p, _p, _p, _p, _p, _i64, _i64, _i64, _i64, _i64]
         L.oracle_mmvq_id_slots.restype = ctypes.c_int
+        L.oracle_tq2_element_slot.argtypes = [ctypes.c_int, _p, _p]
+        for name in ("oracle_tq2_pack", "oracle_tq2_unpack"):
+            getattr(L, name).argtypes = [_p, _p, _p, _i64, _i64]
+            getattr(L, name).restype = ctypes.c_int
+        for name in ("oracle_tq2_block_isums_elem", "oracle_tq2_block_isums_bytes"):
+            getattr(L, name).argtypes = [_p, _p, _p, _i64, _i64, _i64]
+            getattr(L, name).restype = ctypes.c_int
+        L.oracle_tq2_mmvq.argtypes = [_p, _p, _p, _p, _p, _i64, _i64, _i64]
+        L.oracle_tq2_mmvq.restype = ctypes.c_int
         L.oracle_f32_to_bf16.restype = ctypes.c_uint16
         L.oracle_f32_to_bf16.argtypes = [ctypes.c_float]
         L.oracle_tq1_dequantize_rows.argtypes = [_p, _p, _p, _i64, _i64, _i64, ctypes.c_int]
@@ -210,6 +219,59 @@ def mmvq_id(w, a, ids, E, N, K, T, n_used, per_slot=False):
     f = lib().oracle_mmvq_id_slots if per_slot else lib().oracle_mmvq_id
     _check(f(_ptr(w), _ptr(a), _ptr(ids), _ptr(y), _ptr(y64), _ptr(ab), E, N, K, T, n_used),
            "mmvq_id")
+    return y, y64, ab
+
+
+# ---- TQ2_0 (2-bit digit fields; the reading is stated in tq1_oracle.c) -----------
+
+TQ2_BLOCK_BYTES = 66
+
+
+def tq2_element_slot(e):
+    b = ctypes.c_int()
+    f = ctypes.c_int()
+    lib().oracle_tq2_element_slot(int(e), ctypes.byref(b), ctypes.byref(f))
+    return b.value, f.value
+
+
+def tq2_pack(trits, d16):
+    """trits int8 [N, K] in {-1,0,1}; d16 uint16 [N, K/256] -> uint8 [N, K/256*66]."""
+    trits = _c(trits, np.int8)
+    d16 = _c(d16, np.uint16)
+    N, K = trits.shape
+    out = np.empty((N, (K // 256) * TQ2_BLOCK_BYTES), dtype=np.uint8)
+    _check(lib().oracle_tq2_pack(_ptr(trits), _ptr(d16), _ptr(out), N, K), "tq2_pack")
+    return out
+
+
+def tq2_unpack(w, N, K):
+    w = _c(w, np.uint8)
+    trits = np.empty((N, K), dtype=np.int8)
+    d16 = np.empty((N, K // 256), dtype=np.uint16)
+    _check(lib().oracle_tq2_unpack(_ptr(w), _ptr(trits), _ptr(d16), N, K), "tq2_unpack")
+    return trits, d16
+
+
+def tq2_block_isums(w, a, N, K, T, method="elem"):
+    """Per-32-element integer sums of TQ2_0 rows, int32 [T, N, K/32]."""
+    w = _c(w, np.uint8)
+    a = _c(a, np.uint8)
+    out = np.empty((T, N, K // 32), dtype=np.int32)
+    fn = {"elem": lib().oracle_tq2_block_isums_elem,
+          "bytes": lib().oracle_tq2_block_isums_bytes}[method]
+    _check(fn(_ptr(w), _ptr(a), _ptr(out), N, K, T), "tq2_block_isums")
+    return out
+
+
+def tq2_mmvq(w, a, N, K, T):
+    """TQ2_0 mat-vec: (y float32 [T,N], y64 float64 [T,N], abs64 float64 [T,N])."""
+    w = _c(w, np.uint8)
+    a = _c(a, np.uint8)
+    y = np.empty((T, N), dtype=np.float32)
+    y64 = np.empty((T, N), dtype=np.float64)
+    ab = np.empty((T, N), dtype=np.float64)
+    _check(lib().oracle_tq2_mmvq(_ptr(w), _ptr(a), _ptr(y), _ptr(y64), _ptr(ab), N, K, T),
+           "tq2_mmvq")
     return y, y64, ab
 
 

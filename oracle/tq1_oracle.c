@@ -27,6 +27,18 @@
  *    d = amax/127 (fp32), q = round-half-away(x * (1/d)) clamped to +-127,
  *    s = fp16(d * sum q); fp16 conversions round to nearest even.
  *
+ *  [P1-up] same page, section "Upstream state": names a second ternary type,
+ *       TQ2_0, and gives no layout for it. Reading used here (the plainest
+ *       one beside TQ1_0): 256-element blocks, one 2-bit field per element
+ *       holding the digit u = trit + 1 (the value 3 unused), four fields per
+ *       byte, then the fp16 scale: qs[64] at 0, d at 64 (66 bytes). Element
+ *       e lives in byte 32 * (e / 128) + e % 32, field (e % 128) / 32 (bits
+ *       2f, 2f + 1): TQ1_0's digit-major order for its first 128 elements,
+ *       repeated on the second 32 bytes, so 32-element chunk c is field c % 4
+ *       of bytes 32 * (c / 4) .. + 31. Pinned by hand-worked blocks
+ *       (tests/golden/tq2_blocks.txt) and by bitwise agreement with the TQ1_0
+ *       product of the same trits.
+ *
  * Parity pins for every function are in tests/test_oracle_pins.py.
  */
 #include <math.h>
@@ -41,6 +53,8 @@
 #define TQ1_BLOCK_BYTES 54
 #define Q81_BLOCK_ELEMS 32
 #define Q81_BLOCK_BYTES 36
+
+#define TQ2_BLOCK_BYTES 66
 
 /* ------------------------------------------------------------------------ */
 /* IEEE 754 binary16 <-> binary32, written from the format definition.      */
@@ -604,4 +618,192 @@ int oracle_max_threads(void)
 #else
     return 1;
 #endif
+}
+
+
+/* ------------------------------------------------------------------------ */
+/* TQ2_0 (reading stated in the header): 2-bit digit fields.                */
+/* ------------------------------------------------------------------------ */
+
+/* Element e of a TQ2_0 block -> (byte index, 2-bit field index). */
+void oracle_tq2_element_slot(int e, int *byte_index, int *field)
+{
+    *byte_index = 32 * (e / 128) + e % 32;
+    *field = (e % 128) / 32;
+}
+
+int oracle_tq2_pack(const int8_t *trits, const uint16_t *d, uint8_t *w,
+                    int64_t N, int64_t K)
+{
+    if (N < 0 || K <= 0 || K % TQ1_BLOCK_ELEMS)
+        return -1;
+    int64_t nb = K / TQ1_BLOCK_ELEMS;
+    for (int64_t n = 0; n < N; n++) {
+        for (int64_t B = 0; B < nb; B++) {
+            uint8_t *blk = w + (n * nb + B) * TQ2_BLOCK_BYTES;
+            int value[64];
+            for (int p = 0; p < 64; p++)
+                value[p] = 0;
+            for (int e = 0; e < TQ1_BLOCK_ELEMS; e++) {
+                int t = trits[n * K + B * TQ1_BLOCK_ELEMS + e];
+                if (t < -1 || t > 1)
+                    return -1;
+                int p, f;
+                oracle_tq2_element_slot(e, &p, &f);
+                value[p] += (t + 1) << (2 * f);
+            }
+            for (int p = 0; p < 64; p++)
+                blk[p] = (uint8_t)value[p];
+            uint16_t h = d[n * nb + B];
+            blk[64] = (uint8_t)(h & 0xff);
+            blk[65] = (uint8_t)(h >> 8);
+        }
+    }
+    return 0;
+}
+
+/* Trits and scales of one TQ2_0 row; -1 if a field holds 3. */
+static int unpack2_row(const uint8_t *row, int64_t K, int8_t *trits, uint16_t *d)
+{
+    int64_t nb = K / TQ1_BLOCK_ELEMS;
+    for (int64_t B = 0; B < nb; B++) {
+        const uint8_t *blk = row + B * TQ2_BLOCK_BYTES;
+        for (int e = 0; e < TQ1_BLOCK_ELEMS; e++) {
+            int p, f;
+            oracle_tq2_element_slot(e, &p, &f);
+            int u = (blk[p] >> (2 * f)) & 3;
+            if (u == 3)
+                return -1;
+            trits[B * TQ1_BLOCK_ELEMS + e] = (int8_t)(u - 1);
+        }
+        if (d)
+            d[B] = (uint16_t)(blk[64] | (blk[65] << 8));
+    }
+    return 0;
+}
+
+int oracle_tq2_unpack(const uint8_t *w, int8_t *trits, uint16_t *d, int64_t N, int64_t K)
+{
+    if (N < 0 || K <= 0 || K % TQ1_BLOCK_ELEMS)
+        return -1;
+    int64_t nb = K / TQ1_BLOCK_ELEMS;
+    for (int64_t n = 0; n < N; n++)
+        if (unpack2_row(w + n * nb * TQ2_BLOCK_BYTES, K, trits + n * K, d + n * nb))
+            return -1;
+    return 0;
+}
+
+/* Per-32-element integer sums of TQ2_0 rows: (i) element loop over decoded
+ * trits; (ii) byte-major walk, each byte's four fields spent in place,
+ * sum(u q) - sum(q). */
+int oracle_tq2_block_isums_elem(const uint8_t *w, const uint8_t *a, int32_t *isums,
+                                int64_t N, int64_t K, int64_t T)
+{
+    if (N < 0 || T < 0 || K <= 0 || K % TQ1_BLOCK_ELEMS)
+        return -1;
+    int64_t nb = K / TQ1_BLOCK_ELEMS, nblk = K / Q81_BLOCK_ELEMS;
+    int bad = 0;
+#pragma omp parallel for schedule(static) reduction(| : bad)
+    for (int64_t n = 0; n < N; n++) {
+        int8_t *tr = (int8_t *)malloc((size_t)K);
+        if (!tr || unpack2_row(w + n * nb * TQ2_BLOCK_BYTES, K, tr, NULL)) {
+            bad = 1;
+            free(tr);
+            continue;
+        }
+        for (int64_t t = 0; t < T; t++)
+            for (int64_t j = 0; j < nblk; j++) {
+                int32_t s = 0;
+                for (int i = 0; i < Q81_BLOCK_ELEMS; i++) {
+                    int64_t k = j * Q81_BLOCK_ELEMS + i;
+                    s += (int32_t)tr[k] * (int32_t)q81_value(a, nblk, t, k);
+                }
+                isums[(t * N + n) * nblk + j] = s;
+            }
+        free(tr);
+    }
+    return bad ? -1 : 0;
+}
+
+int oracle_tq2_block_isums_bytes(const uint8_t *w, const uint8_t *a, int32_t *isums,
+                                 int64_t N, int64_t K, int64_t T)
+{
+    if (N < 0 || T < 0 || K <= 0 || K % TQ1_BLOCK_ELEMS)
+        return -1;
+    int64_t nb = K / TQ1_BLOCK_ELEMS, nblk = K / Q81_BLOCK_ELEMS;
+    int bad = 0;
+#pragma omp parallel for schedule(static) reduction(| : bad)
+    for (int64_t n = 0; n < N; n++) {
+        for (int64_t t = 0; t < T; t++) {
+            for (int64_t B = 0; B < nb; B++) {
+                const uint8_t *blk = w + (n * nb + B) * TQ2_BLOCK_BYTES;
+                int32_t su[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+                for (int p = 0; p < 64; p++) {
+                    for (int f = 0; f < 4; f++) {
+                        int u = (blk[p] >> (2 * f)) & 3;
+                        if (u == 3)
+                            bad = 1;
+                        int e = 128 * (p / 32) + 32 * f + p % 32;
+                        su[e / 32] += u * (int32_t)q81_value(a, nblk, t,
+                                                             B * TQ1_BLOCK_ELEMS + e);
+                    }
+                }
+                for (int b = 0; b < 8; b++) {
+                    int64_t j = B * 8 + b;
+                    int32_t sumq = 0;
+                    for (int i = 0; i < Q81_BLOCK_ELEMS; i++)
+                        sumq += q81_value(a, nblk, t, j * Q81_BLOCK_ELEMS + i);
+                    isums[(t * N + n) * nblk + j] = su[b] - sumq;
+                }
+            }
+        }
+    }
+    return bad ? -1 : 0;
+}
+
+/* TQ2_0 mat-vec: the same definition as oracle_mmvq, every term
+ * fp32(d_w) * fp32(d_a) * isum formed in fp64 (exact) and summed in index
+ * order in fp64; also the sum of |term|. */
+int oracle_tq2_mmvq(const uint8_t *w, const uint8_t *a, float *y, double *y64,
+                    double *abs64, int64_t N, int64_t K, int64_t T)
+{
+    if (N < 0 || T < 0 || K <= 0 || K % TQ1_BLOCK_ELEMS)
+        return -1;
+    int64_t nb = K / TQ1_BLOCK_ELEMS, nblk = K / Q81_BLOCK_ELEMS;
+    int bad = 0;
+#pragma omp parallel for schedule(static) reduction(| : bad)
+    for (int64_t n = 0; n < N; n++) {
+        int8_t *tr = (int8_t *)malloc((size_t)K);
+        uint16_t *dd = (uint16_t *)malloc((size_t)nb * sizeof(uint16_t));
+        if (!tr || !dd || unpack2_row(w + n * nb * TQ2_BLOCK_BYTES, K, tr, dd)) {
+            bad = 1;
+            free(tr);
+            free(dd);
+            continue;
+        }
+        for (int64_t t = 0; t < T; t++) {
+            double acc = 0.0, acc_abs = 0.0;
+            for (int64_t j = 0; j < nblk; j++) {
+                double dw = (double)oracle_f16_to_f32(dd[j / 8]);
+                double da = (double)oracle_f16_to_f32(q81_scale(a, nblk, t, j));
+                int32_t s = 0;
+                for (int i = 0; i < Q81_BLOCK_ELEMS; i++) {
+                    int64_t k = j * Q81_BLOCK_ELEMS + i;
+                    s += (int32_t)tr[k] * (int32_t)q81_value(a, nblk, t, k);
+                }
+                double term = dw * da * (double)s;
+                acc += term;
+                acc_abs += fabs(term);
+            }
+            if (y)
+                y[t * N + n] = (float)acc;
+            if (y64)
+                y64[t * N + n] = acc;
+            if (abs64)
+                abs64[t * N + n] = acc_abs;
+        }
+        free(tr);
+        free(dd);
+    }
+    return bad ? -1 : 0;
 }

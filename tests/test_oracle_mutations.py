@@ -32,6 +32,13 @@ MUTATIONS = {
                             "y64[t * N + n] = y64[t * N + n] - rv;"),
     "residual_transposed": ("double rv = (double)r[t * N + n];",
                             "double rv = (double)r[(n * T + t) % (N * T)];"),
+    "tq2_field_and_byte_swapped": ("*byte_index = 32 * (e / 128) + e % 32;\n    *field = (e % 128) / 32;",
+                                   "*byte_index = 32 * (e / 128) + (e % 128) / 4;\n    *field = e % 4;"),
+    "tq2_field_weight_4_to_2": ("value[p] += (t + 1) << (2 * f);", "value[p] += (t + 1) << f;"),
+    "tq2_trit_sign_flipped": ("(int8_t)(u - 1);", "(int8_t)(1 - u);"),
+    "tq2_byte_walk_drops_sum_q": ("= su[b] - sumq;", "= su[b];"),
+    "tq2_scale_of_next_block": ("oracle_f16_to_f32(dd[j / 8]);",
+                                "oracle_f16_to_f32(dd[(j / 8 + 1) % nb]);"),
     "slots_read_token_column": ("int64_t col = column_per_pair ? ts : ts / n_used;",
                                 "int64_t col = ts / n_used;"),
 }

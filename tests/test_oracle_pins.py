@@ -506,3 +506,153 @@ def test_dequantize_dtypes_and_row_gather():
         assert np.array_equal(oracle.tq1_dequantize(w, N, K, dt, rows=rows), full[rows])
     with pytest.raises(oracle.OracleError):
         oracle.tq1_dequantize(w, N, K, "f32", rows=np.array([0, 7], np.int32))
+
+
+# ---------------------------------------------------------------------------
+# TQ2_0: the 2-bit layout read from "Upstream state" (the page names the type
+# and prints no layout; the reading is stated in tests/golden/tq2_blocks.txt).
+# ---------------------------------------------------------------------------
+
+def test_tq2_element_map_is_a_bijection_and_agrees_with_tq1_first_chunks():
+    slots = [oracle.tq2_element_slot(e) for e in range(256)]
+    assert len(set(slots)) == 256
+    assert all(0 <= b < 64 and 0 <= f < 4 for b, f in slots)
+    # the first four 32-element chunks sit where TQ1_0 puts them (byte e % 32,
+    # digit / field e / 32), and chunk c + 4 is chunk c moved 32 bytes on
+    for e in range(128):
+        assert oracle.tq2_element_slot(e) == oracle.element_slot(e)
+        b, f = oracle.tq2_element_slot(e + 128)
+        assert (b - 32, f) == oracle.element_slot(e)
+
+
+def _parse_tq2_golden():
+    cases = []
+    with open(os.path.join(GOLDEN, "tq2_blocks.txt")) as f:
+        for line in f:
+            line = line.strip()
+            if not line or line.startswith("#"):
+                continue
+            name, pat, exp = [s.strip() for s in line.split("|")]
+            trits = np.zeros(256, dtype=np.int8)
+            for tok in pat.split():
+                if tok.startswith("all="):
+                    trits[:] = int(tok[4:])
+                else:
+                    e, t = tok[1:].split("=")
+                    trits[int(e)] = int(t)
+            expect = np.zeros(64, dtype=np.int64)
+            for tok in exp.split():
+                k, val = tok.split("=")
+                if k == "qs*":
+                    expect[:] = int(val)
+                else:
+                    expect[int(k[3:-1])] = int(val)
+            cases.append((name, trits, expect))
+    return cases
+
+
+@pytest.mark.parametrize("name,trits,expect", _parse_tq2_golden(), ids=lambda v: v if isinstance(v, str) else "")
+def test_tq2_pack_hand_worked_blocks(name, trits, expect):
+    w = oracle.tq2_pack(trits.reshape(1, 256), np.array([[0xBC00]], np.uint16))
+    assert w.shape == (1, 66)
+    assert np.array_equal(w[0, :64].astype(np.int64), expect), name
+    assert w[0, 64] == 0x00 and w[0, 65] == 0xBC  # little-endian fp16 -1.0
+    back, dback = oracle.tq2_unpack(w, 1, 256)
+    assert np.array_equal(back[0], trits)
+    assert dback[0, 0] == 0xBC00
+
+
+def test_tq2_every_valid_byte_roundtrips_and_field_3_is_rejected():
+    # the 81 bytes whose four fields are digits, at every byte position
+    vals = [v for v in range(256) if all((v >> (2 * f)) & 3 != 3 for f in range(4))]
+    assert len(vals) == 81
+    rows = np.zeros((81, 64), np.uint8)
+    for i, v in enumerate(vals):
+        rows[i, :] = v
+    w = np.concatenate([rows, np.zeros((81, 2), np.uint8)], axis=1)
+    trits, d = oracle.tq2_unpack(w, 81, 256)
+    assert np.array_equal(oracle.tq2_pack(trits, d), w)
+    # all 256 trits of a block decode from digits 0..2, so each byte's four
+    # trits are base-4 digits of v - 85 shifted: sum_f (t_f + 1) 4^f = v
+    for i, v in enumerate(vals):
+        for p in (0, 17, 40, 63):
+            s = sum((int(trits[i, 128 * (p // 32) + 32 * f + p % 32]) + 1) * 4 ** f
+                    for f in range(4))
+            assert s == v
+    for v in (3, 12, 48, 192, 255):
+        bad = w[:1].copy()
+        bad[0, 9] = v
+        with pytest.raises(oracle.OracleError):
+            oracle.tq2_unpack(bad, 1, 256)
+        a = oracle.q8_1_quantize(np.ones((1, 256), np.float32))
+        with pytest.raises(oracle.OracleError):
+            oracle.tq2_mmvq(bad, a, 1, 256, 1)
+        for method in ("elem", "bytes"):
+            with pytest.raises(oracle.OracleError):
+                oracle.tq2_block_isums(bad, a, 1, 256, 1, method)
+    t = np.zeros((1, 256), np.int8)
+    t[0, 77] = -2
+    with pytest.raises(oracle.OracleError):
+        oracle.tq2_pack(t, np.zeros((1, 1), np.uint16))
+
+
+@pytest.mark.parametrize("N,K,T,seed", [(7, 256, 1, 61), (16, 1024, 3, 62), (5, 2304, 2, 63)])
+def test_tq2_isums_both_methods_equal_numpy_int_contraction(N, K, T, seed):
+    trits, d16, x = _case(N, K, T, seed)
+    w = oracle.tq2_pack(trits, d16)
+    a = oracle.q8_1_quantize(x)
+    q, _, _ = oracle.q8_1_fields(a, T, K)
+    ref = _isums_numpy(trits, q)
+    assert np.array_equal(oracle.tq2_block_isums(w, a, N, K, T, "elem"), ref)
+    assert np.array_equal(oracle.tq2_block_isums(w, a, N, K, T, "bytes"), ref)
+
+
+@pytest.mark.parametrize("N,K,T,seed", [(9, 256, 1, 64), (32, 1024, 4, 65), (3, 4096, 2, 66)])
+def test_tq2_mmvq_equals_tq1_mmvq_of_the_same_trits(N, K, T, seed):
+    """One matrix, two packings: both products sum the same exact terms in
+    the same order, so they agree bit for bit; and both match the plain
+    product of dequantized operands."""
+    trits, d16, x = _case(N, K, T, seed)
+    a = oracle.q8_1_quantize(x)
+    y1, y1_64, ab1 = oracle.mmvq(oracle.tq1_pack(trits, d16), a, N, K, T)
+    y2, y2_64, ab2 = oracle.tq2_mmvq(oracle.tq2_pack(trits, d16), a, N, K, T)
+    assert np.array_equal(y2_64, y1_64) and np.array_equal(ab2, ab1)
+    assert np.array_equal(y2, y1)
+    q, da16, _ = oracle.q8_1_fields(a, T, K)
+    W = trits.astype(np.float64) * np.repeat(d16.view(np.float16).astype(np.float64), 256, axis=1)
+    A = q.astype(np.float64) * np.repeat(da16.view(np.float16).astype(np.float64), 32, axis=1)
+    assert np.all(np.abs(y2_64 - A @ W.T) <= 1e-12 * ab2 + 1e-300)
+
+
+def test_tq2_mmvq_unit_scales_is_integer_matvec_exactly():
+    N, K, T = 24, 1536, 3
+    rng = np.random.default_rng(67)
+    trits = synth.ternary(rng, (N, K))
+    q = rng.integers(-127, 128, (T, K)).astype(np.int8)
+    a = synth.q8_1_blocks_from_fields(q, np.full((T, K // 32), 0x3C00, np.uint16),
+                                      np.zeros((T, K // 32), np.uint16))
+    w = oracle.tq2_pack(trits, np.full((N, K // 256), 0x3C00, np.uint16))
+    y, y64, _ = oracle.tq2_mmvq(w, a, N, K, T)
+    ref = q.astype(np.int64) @ trits.astype(np.int64).T
+    assert np.array_equal(y64, ref.astype(np.float64))
+    assert np.array_equal(y, ref.astype(np.float32))
+
+
+def test_tq2_mmvq_scale_index_and_row_order():
+    """A scale change in one block moves only that block's terms; permuted
+    rows permute the outputs."""
+    N, K, T = 6, 768, 2
+    trits, d16, x = _case(N, K, T, 68)
+    a = oracle.q8_1_quantize(x)
+    _, y64, _ = oracle.tq2_mmvq(oracle.tq2_pack(trits, d16), a, N, K, T)
+    d2 = d16.copy()
+    d2[2, 1] = 0
+    _, z64, _ = oracle.tq2_mmvq(oracle.tq2_pack(trits, d2), a, N, K, T)
+    t0 = trits.copy()
+    t0[2, 256:512] = 0
+    _, r64, _ = oracle.tq2_mmvq(oracle.tq2_pack(t0, d16), a, N, K, T)
+    assert np.array_equal(z64, r64)
+    assert not np.array_equal(z64[:, 2], y64[:, 2])
+    perm = np.random.default_rng(2).permutation(N)
+    _, p64, _ = oracle.tq2_mmvq(oracle.tq2_pack(trits[perm], d16[perm]), a, N, K, T)
+    assert np.array_equal(p64, y64[:, perm])
