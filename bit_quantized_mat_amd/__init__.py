@@ -1,4 +1,4 @@
-"""MI355X (gfx950) TQ1_0 x Q8_1 quantized mat-vec.
+"""MI355X (gfx950) TQ1_0 (and TQ2_0) x Q8_1 quantized mat-vec.
 
 A thin binding over the C ABI in ``include/bqm.h`` (library ``libbqm.so``,
 built in-tree by ``bit_quantized_mat_amd.build``). Every function here only
@@ -16,11 +16,12 @@ __all__ = [
     "mmvq_tq1_0_f32_add",
     "mmvq_id_tq1_0", "mmvq_id_tq1_0_slots", "mmvq_id_tq1_0_workspace_bytes",
     "mmvq_id_tq1_0_noalloc", "NOALLOC_SCRATCH_BYTES",
-    "mmvq_tq1_0_block_isums",
-    "TQ1_BLOCK_BYTES", "Q81_BLOCK_BYTES", "MMVQ_MAX_COLS",
+    "mmvq_tq1_0_block_isums", "tq2_pack", "mmvq_tq2_0", "mmvq_tq2_0_block_isums",
+    "TQ1_BLOCK_BYTES", "TQ2_BLOCK_BYTES", "Q81_BLOCK_BYTES", "MMVQ_MAX_COLS",
 ]
 
 TQ1_BLOCK_BYTES = 54
+TQ2_BLOCK_BYTES = 66
 Q81_BLOCK_BYTES = 36
 MMVQ_MAX_COLS = 32
 MMVQ_F32_MAX_COLS = 8
@@ -67,6 +68,9 @@ def library():
         L.mmvq_id_tq1_0.argtypes = [_p, _p, _p, _p, _i64, _i64, _i64, _i64, _i32, _p, _sz, _p]
         L.mmvq_id_tq1_0_slots.argtypes = L.mmvq_id_tq1_0.argtypes
         L.mmvq_id_tq1_0_noalloc.argtypes = [_p, _p, _p, _p, _i64, _i64, _i64, _i64, _i32, _p]
+        L.tq2_pack.argtypes = [_p, _p, _p, _i64, _i64, _p]
+        L.mmvq_tq2_0.argtypes = [_p, _p, _p, _i64, _i64, _i32, _p]
+        L.mmvq_tq2_0_block_isums.argtypes = [_p, _p, _p, _i64, _i64, _i32, _p]
         L.mmvq_id_tq1_0_workspace_bytes.argtypes = [_i64, _i64, _i32]
         L.mmvq_id_tq1_0_workspace_bytes.restype = _sz
         L.bqm_status_string.argtypes = [ctypes.c_int]
@@ -75,7 +79,8 @@ def library():
         for name in ("tq1_pack", "q8_1_quantize", "mmvq_tq1_0", "mm_tq1_0", "mmvq_tq1_0_f32",
                      "mmvq_tq1_0_add", "mmvq_tq1_0_f32_add",
                      "mmvq_tq1_0_block_isums", "mmvq_id_tq1_0", "mmvq_id_tq1_0_slots",
-                     "mmvq_id_tq1_0_noalloc", "tq1_dequantize"):
+                     "mmvq_id_tq1_0_noalloc", "tq1_dequantize", "tq2_pack", "mmvq_tq2_0",
+                     "mmvq_tq2_0_block_isums"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -144,9 +149,9 @@ def q8_1_quantize(x, out=None, stream=None):
     return out
 
 
-def _mmvq_args(w, a, N, K, T):
+def _mmvq_args(w, a, N, K, T, block_bytes=TQ1_BLOCK_BYTES):
     torch = _torch()
-    return (_dev_tensor(w, "w", (torch.uint8,), N * (K // 256) * TQ1_BLOCK_BYTES),
+    return (_dev_tensor(w, "w", (torch.uint8,), N * (K // 256) * block_bytes),
             _dev_tensor(a, "a", (torch.uint8,), T * (K // 32) * Q81_BLOCK_BYTES, w.device))
 
 
@@ -244,6 +249,46 @@ def mmvq_tq1_0_block_isums(w, a, N, K, T, out=None, stream=None):
         out = torch.empty((T, N, K // 32), dtype=torch.int32, device=w.device)
     pw, pa = _mmvq_args(w, a, N, K, T)
     _call("mmvq_tq1_0_block_isums", pw, pa,
+          _dev_tensor(out, "out", (torch.int32,), T * N * (K // 32) * 4, w.device),
+          N, K, T, _stream(stream, w.device))
+    return out
+
+
+def tq2_pack(trits, d16, out=None, stream=None):
+    """trits int8 [N, K] (values -1/0/1), d16 fp16 or int16/uint16 bits [N, K/256]
+    -> TQ2_0 bytes uint8 [N, K/256*66]."""
+    torch = _torch()
+    N, K = trits.shape
+    nb = K // 256
+    if out is None:
+        out = torch.empty((N, nb * TQ2_BLOCK_BYTES), dtype=torch.uint8, device=trits.device)
+    dtypes16 = (torch.float16, torch.int16, torch.uint16)
+    _call("tq2_pack",
+          _dev_tensor(trits, "trits", (torch.int8,), N * K),
+          _dev_tensor(d16, "d16", dtypes16, N * nb * 2, trits.device),
+          _dev_tensor(out, "out", (torch.uint8,), N * nb * TQ2_BLOCK_BYTES, trits.device),
+          N, K, _stream(stream, trits.device))
+    return out
+
+
+def mmvq_tq2_0(w, a, N, K, T, out=None, stream=None):
+    """y fp32 [T, N] = TQ2_0 weights [N, K] times T Q8_1 activation columns."""
+    torch = _torch()
+    if out is None:
+        out = torch.empty((T, N), dtype=torch.float32, device=w.device)
+    pw, pa = _mmvq_args(w, a, N, K, T, TQ2_BLOCK_BYTES)
+    _call("mmvq_tq2_0", pw, pa, _dev_tensor(out, "out", (torch.float32,), T * N * 4, w.device),
+          N, K, T, _stream(stream, w.device))
+    return out
+
+
+def mmvq_tq2_0_block_isums(w, a, N, K, T, out=None, stream=None):
+    """Exact per-32 integer sums int32 [T, N, K/32] of TQ2_0 rows."""
+    torch = _torch()
+    if out is None:
+        out = torch.empty((T, N, K // 32), dtype=torch.int32, device=w.device)
+    pw, pa = _mmvq_args(w, a, N, K, T, TQ2_BLOCK_BYTES)
+    _call("mmvq_tq2_0_block_isums", pw, pa,
           _dev_tensor(out, "out", (torch.int32,), T * N * (K // 32) * 4, w.device),
           N, K, T, _stream(stream, w.device))
     return out

@@ -37,11 +37,12 @@ int check_device()
 
 hipStream_t as_stream(void *s) { return static_cast<hipStream_t>(s); }
 
-int check_matrix(int64_t N, int64_t K)
+// block_bytes: 54 for TQ1_0, 66 for TQ2_0
+int check_matrix(int64_t N, int64_t K, uint64_t block_bytes = 54)
 {
     if (N < 1 || K < 256 || K % 256 != 0)
         return BQM_ERR_SHAPE;
-    if ((uint64_t)N * (uint64_t)(K / 256) * 54ull > kMaxBufferBytes)
+    if ((uint64_t)N * (uint64_t)(K / 256) * block_bytes > kMaxBufferBytes)
         return BQM_ERR_SHAPE;
     return BQM_OK;
 }
@@ -86,13 +87,14 @@ static bool residual_ok(const float *r, const void *y, int64_t N, int32_t T)
     return rb + n <= yb || yb + n <= rb;
 }
 
-// r: the residual of the add entry point (nullptr for the others).
+// r: the residual of the add entry point (nullptr for the others);
+// block_bytes: the weight format's block size.
 static int mmvq_common(const void *w, const void *a, const void *out, int64_t N, int64_t K,
-                       int32_t T, const float *r = nullptr)
+                       int32_t T, const float *r = nullptr, uint64_t block_bytes = 54)
 {
     if (!w || !a || !out)
         return BQM_ERR_NULL;
-    if (int rc = check_matrix(N, K))
+    if (int rc = check_matrix(N, K, block_bytes))
         return rc;
     if (T < 1 || T > BQM_MMVQ_MAX_COLS)
         return BQM_ERR_SHAPE;
@@ -183,6 +185,34 @@ int mmvq_tq1_0_block_isums(const void *w, const void *a, int32_t *isums, int64_t
     if (int rc = mmvq_common(w, a, isums, N, K, T))
         return rc;
     return bqm::launch_mmvq(w, a, nullptr, isums, N, K, T, as_stream(stream));
+}
+
+int tq2_pack(const int8_t *trits, const uint16_t *d, void *w, int64_t N, int64_t K,
+             void *stream)
+{
+    if (!trits || !d || !w)
+        return BQM_ERR_NULL;
+    if (int rc = check_matrix(N, K, 66))
+        return rc;
+    if (int rc = check_device())
+        return rc;
+    return bqm::launch_tq2_pack(trits, d, w, N, K, as_stream(stream));
+}
+
+int mmvq_tq2_0(const void *w, const void *a, float *y, int64_t N, int64_t K, int32_t T,
+               void *stream)
+{
+    if (int rc = mmvq_common(w, a, y, N, K, T, nullptr, 66))
+        return rc;
+    return bqm::launch_mmvq_tq2(w, a, y, nullptr, N, K, T, as_stream(stream));
+}
+
+int mmvq_tq2_0_block_isums(const void *w, const void *a, int32_t *isums, int64_t N, int64_t K,
+                           int32_t T, void *stream)
+{
+    if (int rc = mmvq_common(w, a, isums, N, K, T, nullptr, 66))
+        return rc;
+    return bqm::launch_mmvq_tq2(w, a, nullptr, isums, N, K, T, as_stream(stream));
 }
 
 int tq1_dequantize(const void *w, const int32_t *rows, void *out, int64_t N, int64_t K,

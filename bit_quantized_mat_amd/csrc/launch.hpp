@@ -43,6 +43,9 @@ int compute_units();
 // Workgroups of `kernel` (with this block size and dynamic LDS) that the
 // current device runs at once.
 int resident_workgroups(const void *kernel, int threads, size_t lds);
+// Waves per workgroup of the staged kernels for N rows at 1 << lr lanes per
+// row: 1, 4 or 8.
+int staged_workgroup_waves(int64_t N, int lr);
 // Staged kernel (one to eight columns, activations staged in LDS): whether it
 // takes this shape, and its launcher.
 bool staged_supported(int64_t K, int32_t T);
@@ -82,6 +85,14 @@ int launch_mmvq_mfma_resident(const void *w, const void *a, float *y, int32_t *i
 bool mfma_reg_supported(int64_t K, int32_t T);
 int launch_mmvq_mfma_reg(const void *w, const void *a, float *y, int32_t *isums, int64_t N,
                          int64_t K, int32_t T, hipStream_t stream, const float *r = nullptr);
+// The same kernel on TQ2_0 weights (same shapes).
+int launch_mmvq_mfma_reg_tq2(const void *w, const void *a, float *y, int32_t *isums, int64_t N,
+                             int64_t K, int32_t T, hipStream_t stream, const float *r = nullptr);
+// TQ2_0: packing, and the product's dispatch (any shape mmvq_tq2_0 accepts).
+int launch_tq2_pack(const int8_t *trits, const uint16_t *d, void *w, int64_t N, int64_t K,
+                    hipStream_t stream);
+int launch_mmvq_tq2(const void *w, const void *a, float *y, int32_t *isums, int64_t N, int64_t K,
+                    int32_t T, hipStream_t stream);
 // Its expert-routed mode (wide work items of up to 16 pairs, written by the
 // routing pre-pass): whether it takes rows of K elements, and its launcher.
 bool mfma_resident_id_supported(int64_t K);

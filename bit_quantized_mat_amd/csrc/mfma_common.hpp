@@ -147,6 +147,35 @@ __device__ __forceinline__ long staged_operand(const uint32_t *__restrict__ tile
     return (long)(((uint64_t)q1 << 32) | q0);
 }
 
+// Weight format policy of the matrix-core kernels for TQ1_0 (the policy of
+// TQ2_0 is in tq2_decode.hpp): a lane's share of a block, its decode to digit
+// operands, and the staged activation bytes of its B operand.
+struct Tq1Tile {
+    static constexpr int kBlockBytes = kTq1BlockBytes;
+    static constexpr uint32_t kIdle = kIdleLoadOffset;  // offset of a load without a block
+    typedef LaneBlock Lane;
+    struct Ctx {
+        QhLaneMuls qm;
+        __device__ __forceinline__ explicit Ctx(int kg) : qm(qh_lane_muls(kg)) {}
+    };
+
+    static __device__ __forceinline__ Lane load(__amdgpu_buffer_rsrc_t rw, uint32_t off, int kg)
+    {
+        return load_lane_block(rw, off, kg);
+    }
+
+    static __device__ __forceinline__ TileOperands decode(const Lane &lb, const Ctx &c)
+    {
+        return decode_lane_block(lb, c.qm);
+    }
+
+    static __device__ __forceinline__ long operand(const uint32_t *__restrict__ tile, int col,
+                                                   int kg, int b)
+    {
+        return staged_operand(tile, col, kg, b);
+    }
+};
+
 // Orders this wave's LDS writes before its later LDS reads (a wave's LDS
 // operations are executed in order; this only keeps the compiler from moving
 // them).

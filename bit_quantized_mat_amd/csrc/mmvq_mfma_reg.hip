@@ -1,6 +1,6 @@
-// mmvq_mfma_reg.hip -- TQ1_0 x Q8_1 product for 5 to 32 activation columns on
-// gfx950 matrix cores, with every wave's activation operands held in
-// registers for the whole call.
+// mmvq_mfma_reg.hip -- TQ1_0 (and TQ2_0) x Q8_1 product for 5 to 32
+// activation columns on gfx950 matrix cores, with every wave's activation
+// operands held in registers for the whole call.
 //
 // The arithmetic is that of the other matrix-core kernels (mfma_common.hpp):
 // a 16-row tile's digit operands decoded in registers, one
@@ -23,7 +23,11 @@
 // in flight meanwhile), multiplies, scales, and the waves' partial sums are
 // combined through LDS by the xor butterfly (one barrier per tile, the
 // partial sums double-buffered).
-#include "mfma_common.hpp"
+//
+// The weight format enters through a policy (Tq1Tile, Tq2Tile): how a lane
+// loads and decodes its share of a block and which staged activation bytes
+// make its B operand. Everything else is common to both formats.
+#include "tq2_decode.hpp"
 
 namespace bqm {
 
@@ -36,6 +40,7 @@ struct RegOperands {
 };
 
 // Read them from a staged 16-column tile (mfma_common.hpp): lane (col, kg).
+template <class Fmt>
 __device__ __forceinline__ RegOperands read_reg_operands(const uint32_t *__restrict__ tile,
                                                          int col, int kg)
 {
@@ -43,7 +48,7 @@ __device__ __forceinline__ RegOperands read_reg_operands(const uint32_t *__restr
     uint32_t d[8];
 #pragma unroll
     for (int b = 0; b < 8; b++) {
-        o.Bq[b] = staged_operand(tile, col, kg, b);
+        o.Bq[b] = Fmt::operand(tile, col, kg, b);
         d[b] = tile[col * kStageCol + 9 * b + 8];
     }
 #pragma unroll
@@ -52,10 +57,10 @@ __device__ __forceinline__ RegOperands read_reg_operands(const uint32_t *__restr
     return o;
 }
 
-// NW: waves per workgroup (8 or 16); GPW: blocks per wave (Lr = NW GPW); NT:
-// 16-column tiles; ISUMS: write the exact per-sub-block sums instead of
-// outputs. Rows hold at most Lr blocks.
-template <int NW, int GPW, int NT, bool ISUMS>
+// Fmt: the weight format policy; NW: waves per workgroup (8 or 16); GPW:
+// blocks per wave (Lr = NW GPW); NT: 16-column tiles; ISUMS: write the exact
+// per-sub-block sums instead of outputs. Rows hold at most Lr blocks.
+template <class Fmt, int NW, int GPW, int NT, bool ISUMS>
 __global__ __launch_bounds__(64 * NW) void mmvq_mfma_reg_kernel(const uint8_t *__restrict__ w,
                                                                 const uint8_t *__restrict__ a,
                                                                 float *y, const float *resid,
@@ -69,11 +74,11 @@ __global__ __launch_bounds__(64 * NW) void mmvq_mfma_reg_kernel(const uint8_t *_
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
     const int kg = lane >> 4;                   // decode lane: row lane % 16, K group kg
-    const QhLaneMuls qm = qh_lane_muls(kg);
+    const typename Fmt::Ctx ctx(kg);
     const int col = lane & 15, rg = lane >> 4;  // output lane: column col, rows 4rg..4rg+3
     const int nblk = nb * 8;
     const uint32_t col_bytes = (uint32_t)nblk * kQ81BlockBytes;
-    const uint32_t row_bytes = (uint32_t)nb * kTq1BlockBytes;
+    const uint32_t row_bytes = (uint32_t)nb * Fmt::kBlockBytes;
     const __amdgpu_buffer_rsrc_t rw = make_rsrc(w, (uint64_t)N * row_bytes);
     const __amdgpu_buffer_rsrc_t ra = make_rsrc(a, (uint64_t)T * col_bytes);
 
@@ -90,13 +95,13 @@ __global__ __launch_bounds__(64 * NW) void mmvq_mfma_reg_kernel(const uint8_t *_
     };
 
     // the first tile's weights, then this wave's activation operands
-    LaneBlock lb[GPW];
+    typename Fmt::Lane lb[GPW];
     uint32_t roff = row_offset(tile);
 #pragma unroll
     for (int gi = 0; gi < GPW; gi++) {
         const int B = wave + NW * gi;
-        lb[gi] = load_lane_block(rw, B < nb ? roff + (uint32_t)B * kTq1BlockBytes : kIdleLoadOffset,
-                                 kg);
+        lb[gi] = Fmt::load(rw, B < nb ? roff + (uint32_t)B * Fmt::kBlockBytes : Fmt::kIdle,
+                           kg);
     }
     // every (block, column tile) of this wave: its 16 columns' 288-byte runs
     // of Q8_1 blocks loaded as coalesced 8-byte pieces (all sets in flight
@@ -127,7 +132,7 @@ __global__ __launch_bounds__(64 * NW) void mmvq_mfma_reg_kernel(const uint8_t *_
         for (int k = 0; k < 9; k++)
             *reinterpret_cast<u32x2 *>(stage + smap.lofs[k]) = piece[st][k];
         wave_lds_order();
-        opnd[st / NT][st % NT] = read_reg_operands(stage, col, kg);
+        opnd[st / NT][st % NT] = read_reg_operands<Fmt>(stage, col, kg);
     }
 
     int parity = 0;
@@ -137,18 +142,18 @@ __global__ __launch_bounds__(64 * NW) void mmvq_mfma_reg_kernel(const uint8_t *_
         const bool have_next = next_tile < ntiles;
         const uint32_t next_roff = row_offset(next_tile);
         // the next tile's weights, in flight while this tile is decoded and
-        // multiplied (every lane issues them, at kIdleLoadOffset when there
+        // multiplied (every lane issues them, at Fmt::kIdle when there
         // is no next tile, so that their data is first waited for where it is
         // decoded)
-        LaneBlock ln[GPW];
+        typename Fmt::Lane ln[GPW];
 #pragma unroll
         for (int gi = 0; gi < GPW; gi++) {
             const int B = wave + NW * gi;
-            ln[gi] = load_lane_block(rw,
-                                     have_next && B < nb
-                                         ? next_roff + (uint32_t)B * kTq1BlockBytes
-                                         : kIdleLoadOffset,
-                                     kg);
+            ln[gi] = Fmt::load(rw,
+                               have_next && B < nb
+                                   ? next_roff + (uint32_t)B * Fmt::kBlockBytes
+                                   : Fmt::kIdle,
+                               kg);
         }
 
         float acc[GPW][NT][4];
@@ -161,7 +166,7 @@ __global__ __launch_bounds__(64 * NW) void mmvq_mfma_reg_kernel(const uint8_t *_
                 for (int i = 0; i < 4; i++)
                     acc[gi][ct][i] = 0.0f;
             if (B < nb) {  // uniform: else this group holds no block
-            const TileOperands op = decode_lane_block(lb[gi], qm);
+            const TileOperands op = Fmt::decode(lb[gi], ctx);
             float dw[4];  // block scales of the four rows this output lane holds
 #pragma unroll
             for (int i = 0; i < 4; i++)
@@ -303,14 +308,14 @@ bool mfma_reg_supported(int64_t K, int32_t T)
     return reg_config((int)(K / kTq1BlockElems), T, NW, GPW, NT);
 }
 
-template <int NW, int GPW, int NT>
+template <class Fmt, int NW, int GPW, int NT>
 static int launch_reg(const uint8_t *w, const uint8_t *a, float *y, const float *r,
                       int32_t *isums, int64_t N, int nb, int T, hipStream_t stream)
 {
     const int64_t ntiles = (N + 15) / 16;
     const size_t lds = ((size_t)2 * NW * 64 * NT * 4 + (size_t)NW * 16 * kStageCol) * 4;
-    const void *kt = reinterpret_cast<const void *>(&mmvq_mfma_reg_kernel<NW, GPW, NT, true>);
-    const void *kf = reinterpret_cast<const void *>(&mmvq_mfma_reg_kernel<NW, GPW, NT, false>);
+    const void *kt = reinterpret_cast<const void *>(&mmvq_mfma_reg_kernel<Fmt, NW, GPW, NT, true>);
+    const void *kf = reinterpret_cast<const void *>(&mmvq_mfma_reg_kernel<Fmt, NW, GPW, NT, false>);
     allow_dynamic_lds(kt, lds);
     allow_dynamic_lds(kf, lds);
     // persistent: as many workgroups as the device holds at once, each
@@ -318,16 +323,17 @@ static int launch_reg(const uint8_t *w, const uint8_t *a, float *y, const float 
     const int cap = resident_workgroups(isums ? kt : kf, 64 * NW, lds);
     const dim3 grid((unsigned)(ntiles < cap ? ntiles : cap));
     if (isums)
-        hipLaunchKernelGGL((mmvq_mfma_reg_kernel<NW, GPW, NT, true>), grid, dim3(64 * NW), lds,
-                           stream, w, a, nullptr, nullptr, isums, N, nb, T, (int)ntiles);
+        hipLaunchKernelGGL((mmvq_mfma_reg_kernel<Fmt, NW, GPW, NT, true>), grid, dim3(64 * NW),
+                           lds, stream, w, a, nullptr, nullptr, isums, N, nb, T, (int)ntiles);
     else
-        hipLaunchKernelGGL((mmvq_mfma_reg_kernel<NW, GPW, NT, false>), grid, dim3(64 * NW), lds,
-                           stream, w, a, y, r, nullptr, N, nb, T, (int)ntiles);
+        hipLaunchKernelGGL((mmvq_mfma_reg_kernel<Fmt, NW, GPW, NT, false>), grid, dim3(64 * NW),
+                           lds, stream, w, a, y, r, nullptr, N, nb, T, (int)ntiles);
     return check_launch();
 }
 
-int launch_mmvq_mfma_reg(const void *w, const void *a, float *y, int32_t *isums, int64_t N,
-                         int64_t K, int32_t T, hipStream_t stream, const float *r)
+template <class Fmt>
+static int launch_reg_fmt(const void *w, const void *a, float *y, int32_t *isums, int64_t N,
+                          int64_t K, int32_t T, hipStream_t stream, const float *r)
 {
     const int nb = (int)(K / kTq1BlockElems);
     int NW, GPW, NT;
@@ -336,10 +342,22 @@ int launch_mmvq_mfma_reg(const void *w, const void *a, float *y, int32_t *isums,
     const uint8_t *wp = static_cast<const uint8_t *>(w);
     const uint8_t *ap = static_cast<const uint8_t *>(a);
     if (NT == 2)
-        return NW == 8 ? launch_reg<8, 1, 2>(wp, ap, y, r, isums, N, nb, T, stream)
-                       : launch_reg<16, 1, 2>(wp, ap, y, r, isums, N, nb, T, stream);
-    return NW == 8 ? launch_reg<8, 1, 1>(wp, ap, y, r, isums, N, nb, T, stream)
-                   : launch_reg<16, 1, 1>(wp, ap, y, r, isums, N, nb, T, stream);
+        return NW == 8 ? launch_reg<Fmt, 8, 1, 2>(wp, ap, y, r, isums, N, nb, T, stream)
+                       : launch_reg<Fmt, 16, 1, 2>(wp, ap, y, r, isums, N, nb, T, stream);
+    return NW == 8 ? launch_reg<Fmt, 8, 1, 1>(wp, ap, y, r, isums, N, nb, T, stream)
+                   : launch_reg<Fmt, 16, 1, 1>(wp, ap, y, r, isums, N, nb, T, stream);
+}
+
+int launch_mmvq_mfma_reg(const void *w, const void *a, float *y, int32_t *isums, int64_t N,
+                         int64_t K, int32_t T, hipStream_t stream, const float *r)
+{
+    return launch_reg_fmt<Tq1Tile>(w, a, y, isums, N, K, T, stream, r);
+}
+
+int launch_mmvq_mfma_reg_tq2(const void *w, const void *a, float *y, int32_t *isums, int64_t N,
+                             int64_t K, int32_t T, hipStream_t stream, const float *r)
+{
+    return launch_reg_fmt<Tq2Tile>(w, a, y, isums, N, K, T, stream, r);
 }
 
 }  // namespace bqm

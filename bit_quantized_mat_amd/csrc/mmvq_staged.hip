@@ -177,19 +177,27 @@ static int staged_waves(int64_t N, int lr)
     return 2 * r8 <= r4 ? 8 : 4;
 }
 
-template <int TC, bool F32>
-static void launch_staged_w(const uint8_t *w, const uint8_t *a, float *y, const float *r,
-                            int32_t *isums,
-                            int64_t N, int nb, int T, int lr, int chunk, size_t lds,
-                            hipStream_t stream)
+int staged_workgroup_waves(int64_t N, int lr)
 {
     // a grid whose one-wave workgroups all fit one per compute unit takes
     // them, spreading its few waves over the device (256 x 1024: 2.56 ->
     // 2.47 us, fused 2.99 -> 2.88 us)
     const int64_t rows4 = 4 * (64 >> lr);
     if ((N + rows4 - 1) / rows4 * 4 <= compute_units())
+        return 1;
+    return staged_waves(N, lr);
+}
+
+template <int TC, bool F32>
+static void launch_staged_w(const uint8_t *w, const uint8_t *a, float *y, const float *r,
+                            int32_t *isums,
+                            int64_t N, int nb, int T, int lr, int chunk, size_t lds,
+                            hipStream_t stream)
+{
+    const int wpg = staged_workgroup_waves(N, lr);
+    if (wpg == 1)
         launch_staged_tc<TC, F32, 1>(w, a, y, r, isums, N, nb, T, lr, chunk, lds, stream);
-    else if (staged_waves(N, lr) == 8)
+    else if (wpg == 8)
         launch_staged_tc<TC, F32, 8>(w, a, y, r, isums, N, nb, T, lr, chunk, lds, stream);
     else
         launch_staged_tc<TC, F32, 4>(w, a, y, r, isums, N, nb, T, lr, chunk, lds, stream);

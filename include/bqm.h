@@ -275,6 +275,49 @@ BQM_API size_t mmvq_id_tq1_0_workspace_bytes(int64_t E, int64_t T, int32_t n_use
 BQM_API int mmvq_tq1_0_block_isums(const void *w, const void *a, int32_t *isums,
                            int64_t N, int64_t K, int32_t T, void *stream);
 
+/* ---- TQ2_0, the other ternary type ---------------------------------------
+ * "CUDA: TQ1_0 mat-vec is load-bound by the per-32-element chunk contract",
+ * "Upstream state", names TQ2_0 beside TQ1_0 but prints no layout. The layout
+ * read here (the plainest one beside TQ1_0):
+ *   TQ2_0 block, 66 bytes: qs[64] at 0, fp16 scale d at 64 (little endian).
+ *     Each byte holds four 2-bit fields, field f in bits 2f and 2f+1, each the
+ *     digit u = trit + 1 in {0,1,2} (3 is ruled out). Element e of the block
+ *     lives in field (e % 128) / 32 of qs[32 * (e / 128) + e % 32], so
+ *     32-element chunk c is field c % 4 of qs[32 * (c / 4) .. + 31]: TQ1_0's
+ *     digit-major order for its first 128 elements, then again on the second
+ *     32 bytes. Element value fp32(d) * trit; rows as for TQ1_0: block (n, B)
+ *     starts at byte (n * (K/256) + B) * 66.
+ * Fields holding 3 are not checked on the device (results unspecified, every
+ * access stays in bounds, as for TQ1_0). */
+
+/* Pack ternary weights into TQ2_0 blocks: the inverse of the element map
+ * above.
+ *   trits [N][K] int8, values -1, 0, +1, row-major.
+ *   d     [N][K/256] fp16 bit patterns (uint16), the block scales.
+ *   w     [N][K/256] x 66 bytes, output.
+ * Shapes: N >= 1, K >= 256, K % 256 == 0, weight matrix below 4 GiB.
+ * Alignment: none required. */
+BQM_API int tq2_pack(const int8_t *trits, const uint16_t *d, void *w,
+             int64_t N, int64_t K, void *stream);
+
+/* The quantized product of mmvq_tq1_0 with TQ2_0 weights: the same
+ * definition (y[t][n] = sum_j fp32(d_w[n][j/8]) * fp32(d_a[t][j]) *
+ * isum[t][n][j], exact int32 sums), the same Q8_1 activations, the same fp32
+ * order per block (so a TQ2_0 matrix and the TQ1_0 packing of the same trits
+ * and scales give bitwise equal outputs), and a kernel that reads each packed
+ * byte once ("Upstream state": every packed byte loaded once, all its digits
+ * expanded in place).
+ *   w [N][K/256] TQ2_0 blocks; a [T][K/32] Q8_1 blocks; y [T][N] fp32 output.
+ * Shapes: N >= 1, K >= 256, K % 256 == 0, 1 <= T <= BQM_MMVQ_MAX_COLS, weight
+ * matrix below 4 GiB. Alignment: w, a, y 4 bytes. Tolerance as mmvq_tq1_0. */
+BQM_API int mmvq_tq2_0(const void *w, const void *a, float *y,
+               int64_t N, int64_t K, int32_t T, void *stream);
+
+/* Test twin of mmvq_tq2_0: the exact per-32-element sums isum[t][n][j]
+ * (int32 [T][N][K/32]) instead of the outputs. Same shapes and alignment. */
+BQM_API int mmvq_tq2_0_block_isums(const void *w, const void *a, int32_t *isums,
+                           int64_t N, int64_t K, int32_t T, void *stream);
+
 /* Human-readable text for a status code (static storage). */
 BQM_API const char *bqm_status_string(int status);
 

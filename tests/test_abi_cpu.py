@@ -26,6 +26,7 @@ def test_header_declares_the_four_calls():
               "mmvq_id_tq1_0",
               "mmvq_id_tq1_0_slots", "tq1_dequantize",
               "mmvq_id_tq1_0_workspace_bytes", "mmvq_tq1_0_block_isums",
+              "tq2_pack", "mmvq_tq2_0", "mmvq_tq2_0_block_isums",
               "bqm_status_string", "bqm_version"):
         assert n in names
 
@@ -63,6 +64,15 @@ ODD = P(0x10002)
 ])
 def test_tq1_pack_rejects(args, expect):
     assert bqm.library().tq1_pack(*args) == expect
+    # TQ2_0 packing validates the same way
+    assert bqm.library().tq2_pack(*args) == expect
+
+
+def test_tq2_size_limit_counts_66_byte_blocks():
+    # 70M blocks: 3.78 GB as TQ1_0 (accepted; then no device here), 4.62 GB as TQ2_0
+    args = (GOOD, GOOD, GOOD, 1, 256 * 70_000_000, None)
+    assert bqm.library().tq1_pack(*args) == -6
+    assert bqm.library().tq2_pack(*args) == -2
 
 
 @pytest.mark.parametrize("args,expect", [
@@ -78,7 +88,8 @@ def test_q8_1_quantize_rejects(args, expect):
     assert bqm.library().q8_1_quantize(*args) == expect
 
 
-@pytest.mark.parametrize("fn", ["mmvq_tq1_0", "mmvq_tq1_0_block_isums"])
+@pytest.mark.parametrize("fn", ["mmvq_tq1_0", "mmvq_tq1_0_block_isums", "mmvq_tq2_0",
+                                "mmvq_tq2_0_block_isums"])
 @pytest.mark.parametrize("args,expect", [
     ((None, GOOD, GOOD, 8, 256, 1, None), -1),
     ((GOOD, None, GOOD, 8, 256, 1, None), -1),

@@ -87,6 +87,19 @@ class _SentinelOutputs:
         kw.setdefault("out", self._y((T, n_used, N), w.device))
         return self._m.mmvq_id_tq1_0_slots(w, a, ids, E, N, K, T, n_used, **kw)
 
+    def tq2_pack(self, trits, d16, **kw):
+        N, K = trits.shape
+        kw.setdefault("out", self._full((N, K // 256 * 66), torch.uint8, 255, trits.device))
+        return self._m.tq2_pack(trits, d16, **kw)
+
+    def mmvq_tq2_0(self, w, a, N, K, T, **kw):
+        kw.setdefault("out", self._y((T, N), w.device))
+        return self._m.mmvq_tq2_0(w, a, N, K, T, **kw)
+
+    def mmvq_tq2_0_block_isums(self, w, a, N, K, T, **kw):
+        kw.setdefault("out", self._full((T, N, K // 32), torch.int32, -2 ** 31, w.device))
+        return self._m.mmvq_tq2_0_block_isums(w, a, N, K, T, **kw)
+
     def tq1_dequantize(self, w, N, K, rows=None, dtype=None, **kw):
         dt = torch.float16 if dtype is None else dtype
         n_rows = N if rows is None else rows.numel()
@@ -819,3 +832,143 @@ def test_tq1_dequantize_bit_exact(bqm, N, K, dtype):
     got = _dq_bits(bqm.tq1_dequantize(w, N, K, rows=_dev(rows), dtype=tdt))
     ref = oracle.tq1_dequantize(w_ref, N, K, dtype, rows=rows)
     assert np.array_equal(got, ref.view(got.dtype))
+
+
+# ---------------------------------------------------------------------------
+# TQ2_0 (2-bit fields; the layout is a reading, pinned in the oracle's tests)
+# ---------------------------------------------------------------------------
+
+# (N, K, T): the staged kernel at one, two, four and eight columns (ragged row
+# counts, odd block counts, one-block rows, rows longer than one staging pass:
+# 129 blocks); above eight columns the register-operand matrix-core kernel for
+# rows of 5 to 16 blocks (one and two column tiles, several row tiles per
+# workgroup at 20000 rows), else the staged kernel in column groups (of 8 for
+# rows of 24 blocks, of 4 where eight columns of 64 blocks exceed the LDS
+# budget: 40 x 16384 x 12)
+TQ2_SHAPES = [(256, 1024, 1), (1, 256, 1), (33, 256, 2), (67, 768, 3), (130, 2304, 5),
+              (515, 4096, 8), (96, 6144, 4), (40, 16384, 1), (17, 1280, 32), (300, 512, 16),
+              (21, 4096, 17), (1, 2304, 9), (50, 16640, 1), (33, 24576, 2), (70, 65536, 2),
+              (9000, 4096, 7), (20000, 2048, 24), (40, 16384, 12), (45, 33024, 3),
+              (4500, 4096, 3), (100, 6144, 20), (7, 256, 32)]
+
+
+def _prep_tq2(bqm, trits, d16, x):
+    w_ref = oracle.tq2_pack(trits, d16)
+    a_ref = oracle.q8_1_quantize(x)
+    w = bqm.tq2_pack(_dev(trits), _dev(d16.view(np.int16)))
+    a = bqm.q8_1_quantize(_dev(x))
+    assert np.array_equal(_host(w), w_ref)
+    assert np.array_equal(_host(a), a_ref)
+    return w, a, w_ref, a_ref
+
+
+@pytest.mark.parametrize("N,K", [(1, 256), (3, 768), (256, 1024), (129, 4096), (64, 6144)])
+def test_tq2_pack_byte_exact(bqm, N, K):
+    trits, d16, _ = _case(N, K, 1, 1100 + N)
+    _say("tq2_pack", N, K)
+    got = _host(bqm.tq2_pack(_dev(trits), _dev(d16.view(np.int16))))
+    assert np.array_equal(got, oracle.tq2_pack(trits, d16))
+
+
+def test_tq2_pack_all_byte_values(bqm):
+    # the 81 valid bytes (four fields of 0..2) at every byte position
+    vals = np.array([v for v in range(256) if all((v >> (2 * f)) & 3 != 3 for f in range(4))],
+                    np.uint8)
+    rng = np.random.default_rng(6)
+    wb = np.zeros((81, 66), dtype=np.uint8)
+    wb[:, :64] = vals[(np.arange(81)[:, None] + np.arange(64)[None, :]) % 81]
+    wb[:, 64:66] = rng.integers(0, 256, (81, 2))
+    trits, d16 = oracle.tq2_unpack(wb, 81, 256)
+    got = _host(bqm.tq2_pack(_dev(trits), _dev(d16.view(np.int16))))
+    assert np.array_equal(got, wb)
+
+
+@pytest.mark.parametrize("N,K,T", TQ2_SHAPES)
+def test_tq2_block_isums_bit_exact(bqm, N, K, T):
+    trits, d16, x = _case(N, K, T, 4000 + N + T)
+    w, a, w_ref, a_ref = _prep_tq2(bqm, trits, d16, x)
+    _say("tq2 block_isums", N, K, T)
+    got = _host(bqm.mmvq_tq2_0_block_isums(w, a, N, K, T))
+    assert np.array_equal(got, oracle.tq2_block_isums(w_ref, a_ref, N, K, T))
+
+
+@pytest.mark.parametrize("N,K,T", TQ2_SHAPES)
+def test_tq2_mmvq_within_tolerance(bqm, N, K, T):
+    trits, d16, x = _case(N, K, T, 5000 + N + T)
+    w, a, w_ref, a_ref = _prep_tq2(bqm, trits, d16, x)
+    _say("tq2 mmvq", N, K, T)
+    y = _host(bqm.mmvq_tq2_0(w, a, N, K, T))
+    _, y64, ab = oracle.tq2_mmvq(w_ref, a_ref, N, K, T)
+    _assert_close(y, y64, ab, "tq2 mmvq %dx%d T=%d" % (N, K, T))
+
+
+def test_tq2_unit_scales_exact_integer_matvec(bqm):
+    """d_w = d_a = 1: the product is the integer mat-vec, exact in fp32
+    (staged and matrix-core paths)."""
+    N, K = 200, 2304
+    rng = np.random.default_rng(98)
+    trits = synth.ternary(rng, (N, K))
+    q = rng.integers(-127, 128, (24, K)).astype(np.int8)
+    ones_w = np.full((N, K // 256), 0x3C00, np.uint16)
+    w = bqm.tq2_pack(_dev(trits), _dev(ones_w.view(np.int16)))
+    for T in (1, 3, 24):
+        a_np = synth.q8_1_blocks_from_fields(q[:T], np.full((T, K // 32), 0x3C00, np.uint16),
+                                             np.zeros((T, K // 32), np.uint16))
+        y = _host(bqm.mmvq_tq2_0(w, _dev(a_np), N, K, T))
+        ref = (q[:T].astype(np.int64) @ trits.astype(np.int64).T).astype(np.float32)
+        assert np.array_equal(y, ref), T
+
+
+def test_tq2_one_hot_element_map(bqm):
+    """A one-hot activation at element e reads back d_w * trit[n, e] for every
+    element position of the block, on both kernel families."""
+    N, K = 48, 256 * 8
+    rng = np.random.default_rng(12)
+    trits = synth.ternary(rng, (N, K))
+    d16 = np.full((N, K // 256), 0x3C00, np.uint16)
+    w = bqm.tq2_pack(_dev(trits), _dev(d16.view(np.int16)))
+    for T in (2, 16):
+        for e0 in range(0, 256, T):
+            q = np.zeros((T, K), np.int8)
+            for t in range(T):
+                q[t, 256 * (t % 8) + e0 + t] = 1
+            a_np = synth.q8_1_blocks_from_fields(q, np.full((T, K // 32), 0x3C00, np.uint16),
+                                                 np.zeros((T, K // 32), np.uint16))
+            y = _host(bqm.mmvq_tq2_0(w, _dev(a_np), N, K, T))
+            ref = (q.astype(np.int64) @ trits.astype(np.int64).T).astype(np.float32)
+            assert np.array_equal(y, ref), (T, e0)
+
+
+@pytest.mark.parametrize("N,K,T", [(515, 4096, 1), (300, 2304, 2), (4500, 4096, 3),
+                                   (96, 6144, 4), (9000, 4096, 7), (20000, 2048, 24),
+                                   (21, 4096, 17), (40, 16384, 12), (100, 6144, 20)])
+def test_tq2_equals_tq1_of_the_same_trits(bqm, N, K, T):
+    """Both formats' kernels keep the library's one fp32 order, so the TQ2_0
+    product of a matrix is bitwise the TQ1_0 product of the same trits and
+    scales, whichever kernel each call takes."""
+    trits, d16, x = _case(N, K, T, 6000 + N + T)
+    a = bqm.q8_1_quantize(_dev(x))
+    w1 = bqm.tq1_pack(_dev(trits), _dev(d16.view(np.int16)))
+    w2 = bqm.tq2_pack(_dev(trits), _dev(d16.view(np.int16)))
+    _say("tq2 vs tq1", N, K, T)
+    y1 = _host(bqm.mmvq_tq1_0(w1, a, N, K, T))
+    y2 = _host(bqm.mmvq_tq2_0(w2, a, N, K, T))
+    assert np.array_equal(y1.view(np.uint32), y2.view(np.uint32))
+
+
+@pytest.mark.parametrize("name", ["decode", "ffn"])
+def test_tq2_workload_parity(bqm, name):
+    """The decode (4096 x 4096) and FFN (14336 x 4096, T up to 32) workloads
+    packed as TQ2_0, against the oracle, with exact sums at the widest T."""
+    wl, inp = _workload_inputs(name)
+    N, K = wl.N, wl.K
+    w, a_all, w_ref, a_ref_all = _prep_tq2(bqm, inp.trits, inp.d16, inp.x)
+    for T in wl.Ts:
+        _say("tq2 workload", name, N, K, T)
+        a = a_all[:T].contiguous()
+        y = _host(bqm.mmvq_tq2_0(w, a, N, K, T))
+        _, y64, ab = oracle.tq2_mmvq(w_ref, a_ref_all[:T], N, K, T)
+        _assert_close(y, y64, ab, "tq2 %s T=%d" % (name, T))
+        if T == max(wl.Ts):
+            s = _host(bqm.mmvq_tq2_0_block_isums(w, a, N, K, T))
+            assert np.array_equal(s, oracle.tq2_block_isums(w_ref, a_ref_all[:T], N, K, T))
