@@ -88,6 +88,12 @@ int launch_mmvq_mfma_reg(const void *w, const void *a, float *y, int32_t *isums,
 // The same kernel on TQ2_0 weights (same shapes).
 int launch_mmvq_mfma_reg_tq2(const void *w, const void *a, float *y, int32_t *isums, int64_t N,
                              int64_t K, int32_t T, hipStream_t stream, const float *r = nullptr);
+// The resident and streamed matrix-core kernels on TQ2_0 weights (same shapes
+// as their TQ1_0 launchers).
+int launch_mmvq_mfma_resident_tq2(const void *w, const void *a, float *y, int32_t *isums,
+                                  int64_t N, int64_t K, int32_t T, hipStream_t stream);
+int launch_mmvq_mfma_tq2(const void *w, const void *a, float *y, int32_t *isums, int64_t N,
+                         int64_t K, int32_t T, hipStream_t stream);
 // TQ2_0: packing, and the product's dispatch (any shape mmvq_tq2_0 accepts).
 int launch_tq2_pack(const int8_t *trits, const uint16_t *d, void *w, int64_t N, int64_t K,
                     hipStream_t stream);

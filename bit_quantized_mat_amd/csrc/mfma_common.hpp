@@ -174,6 +174,24 @@ struct Tq1Tile {
     {
         return staged_operand(tile, col, kg, b);
     }
+
+    // the same, given the staged sub-block's first dword
+    // (tile + col * kStageCol + 9 b)
+    static __device__ __forceinline__ long operand_at(const uint32_t *__restrict__ cs, int kg, int b)
+    {
+        const uint32_t q0 = b < 5 ? cs[2 * kg] : cs[kg];
+        const uint32_t q1 = b < 5 ? cs[2 * kg + 1] : cs[4 + kg];
+        return (long)(((uint64_t)q1 << 32) | q0);
+    }
+
+    // K group kg's B operand of sub-block b, from the eight q dwords of one
+    // Q8_1 block (the layout above)
+    static __device__ __forceinline__ u32x2 operand_dwords(const uint32_t (&q)[8], int kg, int b)
+    {
+        const uint32_t lo = b < 5 ? q[2 * kg] : q[kg];
+        const uint32_t hi = b < 5 ? q[2 * kg + 1] : q[4 + kg];
+        return (u32x2){lo, hi};
+    }
 };
 
 // Orders this wave's LDS writes before its later LDS reads (a wave's LDS

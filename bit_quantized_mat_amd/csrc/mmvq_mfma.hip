@@ -1,6 +1,6 @@
-// mmvq_mfma.hip -- TQ1_0 x Q8_1 product for many activation columns on
-// gfx950, with the integer sums on the matrix cores; activations streamed
-// through LDS one block at a time (any K).
+// mmvq_mfma.hip -- TQ1_0 (and TQ2_0) x Q8_1 product for many activation
+// columns on gfx950, with the integer sums on the matrix cores; activations
+// streamed through LDS one block at a time (any K).
 //
 // With many columns the product is a real contraction: per 32-element Q8_1
 // sub-block, a 16-row tile of weight digits times up to 16 activation columns
@@ -25,12 +25,16 @@
 // workgroup owns Lr / nw groups, accumulates each group's blocks in order,
 // and the groups are then combined by the same xor butterfly, first inside
 // the wave and then across waves through LDS.
-#include "mfma_common.hpp"
+//
+// The weight format enters through a policy (Tq1Tile, Tq2Tile; see
+// mmvq_mfma_reg.hip).
+#include "tq2_decode.hpp"
 
 namespace bqm {
 
 constexpr int kMfmaMaxWaves = 8;     // waves per workgroup
-// GPW: butterfly groups per wave (Lr / waves); NT: 16-column tiles (1 or 2);
+// Fmt: the weight format policy; GPW: butterfly groups per wave (Lr /
+// waves); NT: 16-column tiles (1 or 2);
 // R: 16-row tiles that share each staged activation block; ISUMS: write the
 // exact per-sub-block sums instead of outputs.
 //
@@ -38,7 +42,7 @@ constexpr int kMfmaMaxWaves = 8;     // waves per workgroup
 // row tiles (16 R rows each) tile = blockIdx.x, + gridDim.x, ...; the one-block
 // lookahead runs across tile boundaries, so the next tile's first block is in
 // flight while the current tile finishes and reduces.
-template <int GPW, int NT, int R, bool ISUMS>
+template <class Fmt, int GPW, int NT, int R, bool ISUMS>
 __global__ __launch_bounds__(512) void mmvq_mfma_kernel(const uint8_t *__restrict__ w,
                                                         const uint8_t *__restrict__ a,
                                                         float *y, const float *resid,
@@ -55,11 +59,11 @@ __global__ __launch_bounds__(512) void mmvq_mfma_kernel(const uint8_t *__restric
     const int lane = threadIdx.x & 63;
     const int Lr = 1 << lr_log2;
     const int kg = lane >> 4;                   // decode lane: row lane % 16, K group kg
-    const QhLaneMuls qm = qh_lane_muls(kg);
+    const typename Fmt::Ctx ctx(kg);
     const int col = lane & 15, rg = lane >> 4;  // output lane: column col, rows 4rg..4rg+3
     const int nblk = nb * 8;
     const uint32_t col_bytes = (uint32_t)nblk * kQ81BlockBytes;
-    const __amdgpu_buffer_rsrc_t rw = make_rsrc(w, (uint64_t)N * nb * kTq1BlockBytes);
+    const __amdgpu_buffer_rsrc_t rw = make_rsrc(w, (uint64_t)N * nb * Fmt::kBlockBytes);
     const __amdgpu_buffer_rsrc_t ra = make_rsrc(a, (uint64_t)T * col_bytes);
     uint32_t *stage = smem + wave * (NT * 16 * kStageCol);
     float *red = reinterpret_cast<float *>(smem + nw * (NT * 16 * kStageCol));
@@ -70,7 +74,7 @@ __global__ __launch_bounds__(512) void mmvq_mfma_kernel(const uint8_t *__restric
 #pragma unroll
         for (int rt = 0; rt < R; rt++) {
             const int64_t rowA = (int64_t)t * 16 * R + 16 * rt + (lane & 15);
-            ro[rt] = (uint32_t)((rowA < N ? rowA : 0) * nb * kTq1BlockBytes);
+            ro[rt] = (uint32_t)((rowA < N ? rowA : 0) * nb * Fmt::kBlockBytes);
         }
     };
 
@@ -79,12 +83,12 @@ __global__ __launch_bounds__(512) void mmvq_mfma_kernel(const uint8_t *__restric
     tile_rows(tile, row_off);
     // one block of lookahead: while block B is decoded and multiplied, the
     // weights and activations of the wave's next block are in flight
-    LaneBlock lb[R];
+    typename Fmt::Lane lb[R];
     StagePieces<NT> pieces;
     if (tile < ntiles && wave < nb) {
 #pragma unroll
         for (int rt = 0; rt < R; rt++)
-            lb[rt] = load_lane_block(rw, row_off[rt] + (uint32_t)wave * kTq1BlockBytes, kg);
+            lb[rt] = Fmt::load(rw, row_off[rt] + (uint32_t)wave * Fmt::kBlockBytes, kg);
         pieces.issue(ra, smap, col_bytes, wave);
         pieces.land(stage, smap);
         wave_lds_order();
@@ -116,17 +120,17 @@ __global__ __launch_bounds__(512) void mmvq_mfma_kernel(const uint8_t *__restric
                 const bool same_tile = B + Lr < nb || (gi + 1 < GPW && g + nw < nb);
                 const int Bn = B + Lr < nb ? B + Lr : (same_tile ? g + nw : wave);
                 const bool have_next = same_tile || next_tile < ntiles;
-                // the weights are loaded by every lane (at kIdleLoadOffset
+                // the weights are loaded by every lane (at Fmt::kIdle
                 // when there is no next block), so that their data is first
                 // waited for where it is decoded
-                LaneBlock ln[R];
+                typename Fmt::Lane ln[R];
 #pragma unroll
                 for (int rt = 0; rt < R; rt++)
-                    ln[rt] = load_lane_block(
+                    ln[rt] = Fmt::load(
                         rw,
                         have_next ? (same_tile ? row_off[rt] : next_off[rt]) +
-                                        (uint32_t)Bn * kTq1BlockBytes
-                                  : kIdleLoadOffset,
+                                        (uint32_t)Bn * Fmt::kBlockBytes
+                                  : Fmt::kIdle,
                         kg);
                 if (have_next)
                     pieces.issue(ra, smap, col_bytes, Bn);
@@ -137,7 +141,7 @@ __global__ __launch_bounds__(512) void mmvq_mfma_kernel(const uint8_t *__restric
                 // registers)
 #pragma unroll
                 for (int rt = 0; rt < R; rt++) {
-                    const TileOperands op = decode_lane_block(lb[rt], qm);
+                    const TileOperands op = Fmt::decode(lb[rt], ctx);
                     float dw[4];  // block scales of the four rows this output lane holds
 #pragma unroll
                     for (int i = 0; i < 4; i++)
@@ -148,9 +152,7 @@ __global__ __launch_bounds__(512) void mmvq_mfma_kernel(const uint8_t *__restric
 #pragma unroll
                         for (int ct = 0; ct < NT; ct++) {
                             const uint32_t *cs = stage + (ct * 16 + col) * kStageCol + 9 * b;
-                            const uint32_t q0 = b < 5 ? cs[2 * kg] : cs[kg];
-                            const uint32_t q1 = b < 5 ? cs[2 * kg + 1] : cs[4 + kg];
-                            const long Bq = (long)(((uint64_t)q1 << 32) | q0);
+                            const long Bq = Fmt::operand_at(cs, kg, b);
                             // -sum(q) of this lane's column on every row, then + sum(u q)
                             const i32x4 neg_sum = __builtin_amdgcn_mfma_i32_16x16x32_i8(
                                 kAllMinusOne, Bq, (i32x4){0, 0, 0, 0}, 0, 0, 0);
@@ -268,7 +270,7 @@ __global__ __launch_bounds__(512) void mmvq_mfma_kernel(const uint8_t *__restric
     }
 }
 
-template <int GPW, int NT, int R>
+template <class Fmt, int GPW, int NT, int R>
 static void launch_mfma_r(const uint8_t *w, const uint8_t *a, float *y, const float *r,
                           int32_t *isums,
                           int64_t N, int nb, int T, int lr, int nw, hipStream_t stream)
@@ -277,8 +279,8 @@ static void launch_mfma_r(const uint8_t *w, const uint8_t *a, float *y, const fl
     const size_t stage = (size_t)nw * NT * 16 * kStageCol * sizeof(uint32_t);
     const size_t exchange = (size_t)nw * 64 * R * NT * 4 * sizeof(float);
     const size_t lds = stage + exchange;
-    const void *kt = reinterpret_cast<const void *>(&mmvq_mfma_kernel<GPW, NT, R, true>);
-    const void *kf = reinterpret_cast<const void *>(&mmvq_mfma_kernel<GPW, NT, R, false>);
+    const void *kt = reinterpret_cast<const void *>(&mmvq_mfma_kernel<Fmt, GPW, NT, R, true>);
+    const void *kf = reinterpret_cast<const void *>(&mmvq_mfma_kernel<Fmt, GPW, NT, R, false>);
     allow_dynamic_lds(kt, lds);
     allow_dynamic_lds(kf, lds);
     // as many workgroups as are resident at once, each taking the same number
@@ -287,14 +289,14 @@ static void launch_mfma_r(const uint8_t *w, const uint8_t *a, float *y, const fl
     const int64_t per = (ntiles + cap - 1) / cap;
     const dim3 grid((unsigned)((ntiles + per - 1) / per));
     if (isums)
-        hipLaunchKernelGGL((mmvq_mfma_kernel<GPW, NT, R, true>), grid, dim3(64 * nw), lds,
+        hipLaunchKernelGGL((mmvq_mfma_kernel<Fmt, GPW, NT, R, true>), grid, dim3(64 * nw), lds,
                            stream, w, a, nullptr, nullptr, isums, N, nb, T, lr, (int)ntiles);
     else
-        hipLaunchKernelGGL((mmvq_mfma_kernel<GPW, NT, R, false>), grid, dim3(64 * nw), lds,
+        hipLaunchKernelGGL((mmvq_mfma_kernel<Fmt, GPW, NT, R, false>), grid, dim3(64 * nw), lds,
                            stream, w, a, y, r, nullptr, N, nb, T, lr, (int)ntiles);
 }
 
-template <int GPW, int NT>
+template <class Fmt, int GPW, int NT>
 static void launch_mfma_gn(const uint8_t *w, const uint8_t *a, float *y, const float *r,
                            int32_t *isums,
                            int64_t N, int nb, int T, int lr, int nw, hipStream_t stream)
@@ -308,12 +310,13 @@ static void launch_mfma_gn(const uint8_t *w, const uint8_t *a, float *y, const f
     constexpr int Rmax = Racc < Rcap ? Racc : Rcap;
     const int64_t want = 2 * (int64_t)compute_units();
     if (Rmax >= 2 && (N + 31) / 32 >= want)
-        launch_mfma_r<GPW, NT, (Rmax >= 2 ? 2 : 1)>(w, a, y, r, isums, N, nb, T, lr, nw, stream);
+        launch_mfma_r<Fmt, GPW, NT, (Rmax >= 2 ? 2 : 1)>(w, a, y, r, isums, N, nb, T, lr, nw,
+                                                         stream);
     else
-        launch_mfma_r<GPW, NT, 1>(w, a, y, r, isums, N, nb, T, lr, nw, stream);
+        launch_mfma_r<Fmt, GPW, NT, 1>(w, a, y, r, isums, N, nb, T, lr, nw, stream);
 }
 
-template <int NT>
+template <class Fmt, int NT>
 static void launch_mfma_n(const uint8_t *w, const uint8_t *a, float *y, const float *r,
                           int32_t *isums,
                           int64_t N, int nb, int T, int lr, hipStream_t stream)
@@ -321,25 +324,38 @@ static void launch_mfma_n(const uint8_t *w, const uint8_t *a, float *y, const fl
     const int Lr = 1 << lr;
     const int nw = Lr < kMfmaMaxWaves ? Lr : kMfmaMaxWaves;
     switch (Lr / nw) {
-    case 1: launch_mfma_gn<1, NT>(w, a, y, r, isums, N, nb, T, lr, nw, stream); break;
-    case 2: launch_mfma_gn<2, NT>(w, a, y, r, isums, N, nb, T, lr, nw, stream); break;
-    case 4: launch_mfma_gn<4, NT>(w, a, y, r, isums, N, nb, T, lr, nw, stream); break;
-    default: launch_mfma_gn<8, NT>(w, a, y, r, isums, N, nb, T, lr, nw, stream); break;
+    case 1: launch_mfma_gn<Fmt, 1, NT>(w, a, y, r, isums, N, nb, T, lr, nw, stream); break;
+    case 2: launch_mfma_gn<Fmt, 2, NT>(w, a, y, r, isums, N, nb, T, lr, nw, stream); break;
+    case 4: launch_mfma_gn<Fmt, 4, NT>(w, a, y, r, isums, N, nb, T, lr, nw, stream); break;
+    default: launch_mfma_gn<Fmt, 8, NT>(w, a, y, r, isums, N, nb, T, lr, nw, stream); break;
     }
 }
 
-int launch_mmvq_mfma(const void *w, const void *a, float *y, int32_t *isums, int64_t N,
-                     int64_t K, int32_t T, hipStream_t stream, const float *r)
+template <class Fmt>
+static int launch_mfma_fmt(const void *w, const void *a, float *y, int32_t *isums, int64_t N,
+                           int64_t K, int32_t T, hipStream_t stream, const float *r)
 {
     const int nb = (int)(K / kTq1BlockElems);
     const int lr = lanes_per_row_log2(nb);
     const uint8_t *wp = static_cast<const uint8_t *>(w);
     const uint8_t *ap = static_cast<const uint8_t *>(a);
     if (T <= 16)
-        launch_mfma_n<1>(wp, ap, y, r, isums, N, nb, T, lr, stream);
+        launch_mfma_n<Fmt, 1>(wp, ap, y, r, isums, N, nb, T, lr, stream);
     else
-        launch_mfma_n<2>(wp, ap, y, r, isums, N, nb, T, lr, stream);
+        launch_mfma_n<Fmt, 2>(wp, ap, y, r, isums, N, nb, T, lr, stream);
     return check_launch();
+}
+
+int launch_mmvq_mfma(const void *w, const void *a, float *y, int32_t *isums, int64_t N,
+                     int64_t K, int32_t T, hipStream_t stream, const float *r)
+{
+    return launch_mfma_fmt<Tq1Tile>(w, a, y, isums, N, K, T, stream, r);
+}
+
+int launch_mmvq_mfma_tq2(const void *w, const void *a, float *y, int32_t *isums, int64_t N,
+                         int64_t K, int32_t T, hipStream_t stream)
+{
+    return launch_mfma_fmt<Tq2Tile>(w, a, y, isums, N, K, T, stream, nullptr);
 }
 
 }  // namespace bqm

@@ -1,5 +1,6 @@
-// mmvq_mfma_res.hip -- TQ1_0 x Q8_1 product for many activation columns on
-// gfx950, matrix cores, with every activation column resident in LDS.
+// mmvq_mfma_res.hip -- TQ1_0 (and TQ2_0) x Q8_1 product for many activation
+// columns on gfx950, matrix cores, with every activation column resident in
+// LDS.
 //
 // Same arithmetic as the streamed matrix-core kernel (mmvq_mfma.hip): digit
 // operands decoded in registers, one v_mfma_i32_16x16x32_i8 per sub-block,
@@ -19,7 +20,11 @@
 // waves' partial sums then go through LDS, and every wave combines 16 of the
 // tile's outputs per pass by the remaining butterfly levels (four lanes per
 // output). The result is bitwise the staged kernel's.
-#include "mfma_common.hpp"
+//
+// The weight format enters through a policy (Tq1Tile, Tq2Tile): a lane's
+// share of a block, its decode, and which q bytes of a Q8_1 block make each
+// lane's B operand (so the staged operand layout follows the format).
+#include "tq2_decode.hpp"
 
 namespace bqm {
 
@@ -44,7 +49,7 @@ inline size_t res_lds_bytes(int NW, int NT, int R, int nb, bool db, bool id = fa
 
 // Store one staged Q8_1 block (block j of column c, its 36 bytes in v0, v1,
 // ds) as B operands in bq and its fp16 scale in dah.
-template <int NT>
+template <class Fmt, int NT>
 __device__ __forceinline__ void stage_block(uint32_t *__restrict__ bq, uint32_t *__restrict__ dah,
                                             int nb, int c, int j, const u32x4 &v0, const u32x4 &v1,
                                             uint32_t ds)
@@ -54,11 +59,8 @@ __device__ __forceinline__ void stage_block(uint32_t *__restrict__ bq, uint32_t 
     const uint32_t q[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
     uint32_t *dst = bq + ((size_t)(ct * nb + B) * 8 + b) * 128;
 #pragma unroll
-    for (int kg = 0; kg < 4; kg++) {
-        const uint32_t lo = b < 5 ? q[2 * kg] : q[kg];
-        const uint32_t hi = b < 5 ? q[2 * kg + 1] : q[4 + kg];
-        *reinterpret_cast<u32x2 *>(dst + 2 * (16 * kg + cc)) = (u32x2){lo, hi};
-    }
+    for (int kg = 0; kg < 4; kg++)
+        *reinterpret_cast<u32x2 *>(dst + 2 * (16 * kg + cc)) = Fmt::operand_dwords(q, kg, b);
     reinterpret_cast<uint16_t *>(dah + ((size_t)B * 16 * NT + c) * 4)[b] = (uint16_t)ds;
 }
 
@@ -74,7 +76,7 @@ __device__ __forceinline__ void stage_block(uint32_t *__restrict__ bq, uint32_t 
 // one block, which keeps every lane busy when T is not a multiple of 8.
 // Columns T .. 16 NT - 1 are left as they are: they only feed output columns
 // that are never stored.
-template <int NT, bool ID, bool RUNS>
+template <class Fmt, int NT, bool ID, bool RUNS>
 __device__ __forceinline__ void stage_all_columns(uint32_t *__restrict__ bq,
                                                   uint32_t *__restrict__ dah,
                                                   __amdgpu_buffer_rsrc_t ra, int T, int nb,
@@ -93,7 +95,7 @@ __device__ __forceinline__ void stage_all_columns(uint32_t *__restrict__ bq,
                 const uint32_t off = cbase + (uint32_t)j * kQ81BlockBytes;
                 const u32x4 v0 = ld_b128(ra, off);
                 const u32x4 v1 = ld_b128(ra, off + 16);
-                stage_block<NT>(bq, dah, nb, c, j, v0, v1, ld_b32(ra, off + 32));
+                stage_block<Fmt, NT>(bq, dah, nb, c, j, v0, v1, ld_b32(ra, off + 32));
             }
         }
         return;
@@ -111,11 +113,8 @@ __device__ __forceinline__ void stage_all_columns(uint32_t *__restrict__ bq,
         const int ct = c >> 4, cc = c & 15;
         uint32_t *dst = bq + ((size_t)(ct * nb + B) * 8 + b) * 128;
 #pragma unroll
-        for (int kg = 0; kg < 4; kg++) {
-            const uint32_t lo = b < 5 ? q[2 * kg] : q[kg];
-            const uint32_t hi = b < 5 ? q[2 * kg + 1] : q[4 + kg];
-            *reinterpret_cast<u32x2 *>(dst + 2 * (16 * kg + cc)) = (u32x2){lo, hi};
-        }
+        for (int kg = 0; kg < 4; kg++)
+            *reinterpret_cast<u32x2 *>(dst + 2 * (16 * kg + cc)) = Fmt::operand_dwords(q, kg, b);
         reinterpret_cast<uint16_t *>(dah + ((size_t)B * 16 * NT + c) * 4)[b] = (uint16_t)ds;
     }
 }
@@ -132,7 +131,8 @@ struct WideItems {
     int pairs_per_col;  // consecutive pairs that read one activation column
 };
 
-// NW: waves per workgroup; GPW: butterfly groups per wave (Lr / NW); NT:
+// Fmt: the weight format policy; NW: waves per workgroup; GPW: butterfly
+// groups per wave (Lr / NW); NT:
 // 16-column tiles (1 or 2); R: 16-row tiles per workgroup tile; DB: partial
 // sums double-buffered; ISUMS: write the exact per-sub-block sums instead of
 // outputs; ID: item mode, work items of up to 16 NT columns (an expert's
@@ -140,7 +140,7 @@ struct WideItems {
 // columns of a many-column product); RUNS: columns copied in runs of blocks
 // (stage_all_columns; plain products and column chunks, not expert items);
 // `a_cols` is the number of columns a holds (T in the plain mode).
-template <int NW, int GPW, int NT, int R, bool DB, bool ISUMS, bool ID, bool RUNS>
+template <class Fmt, int NW, int GPW, int NT, int R, bool DB, bool ISUMS, bool ID, bool RUNS>
 __global__ __launch_bounds__(64 * NW) void mmvq_mfma_res_kernel(const uint8_t *__restrict__ w,
                                                                 const uint8_t *__restrict__ a,
                                                                 float *y, const float *resid,
@@ -163,10 +163,10 @@ __global__ __launch_bounds__(64 * NW) void mmvq_mfma_res_kernel(const uint8_t *_
     const int lane = threadIdx.x & 63;
     constexpr int Lr = NW * GPW;
     const int kg = lane >> 4;                   // decode lane: row lane % 16, K group kg
-    const QhLaneMuls qm = qh_lane_muls(kg);
+    const typename Fmt::Ctx ctx(kg);
     const int col = lane & 15, rg = lane >> 4;  // output lane: column col, rows 4rg..4rg+3
     const int nblk = nb * 8;
-    const uint64_t w_bytes = (uint64_t)N * nb * kTq1BlockBytes;
+    const uint64_t w_bytes = (uint64_t)N * nb * Fmt::kBlockBytes;
     const __amdgpu_buffer_rsrc_t ra = make_rsrc(a, (uint64_t)a_cols * nblk * kQ81BlockBytes);
 
     // Work units: in the plain mode the row tiles, strided over the grid; in
@@ -225,23 +225,23 @@ __global__ __launch_bounds__(64 * NW) void mmvq_mfma_res_kernel(const uint8_t *_
 #pragma unroll
         for (int rt = 0; rt < R; rt++) {
             const int64_t rowA = (int64_t)t * 16 * R + 16 * rt + (lane & 15);
-            ro[rt] = (uint32_t)((rowA < N ? rowA : 0) * nb * kTq1BlockBytes);
+            ro[rt] = (uint32_t)((rowA < N ? rowA : 0) * nb * Fmt::kBlockBytes);
         }
     };
 
     uint32_t row_off[R];
-    LaneBlock lb[R];
+    typename Fmt::Lane lb[R];
     // the first block's weights are in flight while the activations are staged
     auto start_item = [&]() {
         tile_rows(tile, row_off);
         if (wave < nb) {
 #pragma unroll
             for (int rt = 0; rt < R; rt++)
-                lb[rt] = load_lane_block(rw, row_off[rt] + (uint32_t)wave * kTq1BlockBytes, kg);
+                lb[rt] = Fmt::load(rw, row_off[rt] + (uint32_t)wave * Fmt::kBlockBytes, kg);
         }
         if (ID)
             __syncthreads();  // the column tables
-        stage_all_columns<NT, ID, RUNS>(bq, dah, ra, T, nb, colbase);
+        stage_all_columns<Fmt, NT, ID, RUNS>(bq, dah, ra, T, nb, colbase);
         __syncthreads();
     };
     start_item();
@@ -277,21 +277,21 @@ __global__ __launch_bounds__(64 * NW) void mmvq_mfma_res_kernel(const uint8_t *_
                 const bool same_tile = B + Lr < nb || (gi + 1 < GPW && g + NW < nb);
                 const int Bn = B + Lr < nb ? B + Lr : (same_tile ? g + NW : wave);
                 const bool have_next = same_tile || next_here;
-                // issued by every lane (at kIdleLoadOffset when there is no
+                // issued by every lane (at Fmt::kIdle when there is no
                 // next block), so that the compiler can count the loads in
                 // flight and the data is first waited for where it is decoded
-                LaneBlock ln[R];
+                typename Fmt::Lane ln[R];
 #pragma unroll
                 for (int rt = 0; rt < R; rt++)
-                    ln[rt] = load_lane_block(
+                    ln[rt] = Fmt::load(
                         rw,
                         have_next ? (same_tile ? row_off[rt] : next_off[rt]) +
-                                        (uint32_t)Bn * kTq1BlockBytes
-                                  : kIdleLoadOffset,
+                                        (uint32_t)Bn * Fmt::kBlockBytes
+                                  : Fmt::kIdle,
                         kg);
 #pragma unroll
                 for (int rt = 0; rt < R; rt++) {
-                    const TileOperands op = decode_lane_block(lb[rt], qm);
+                    const TileOperands op = Fmt::decode(lb[rt], ctx);
                     float dw[4];  // block scales of the four rows this output lane holds
 #pragma unroll
                     for (int i = 0; i < 4; i++)
@@ -483,7 +483,7 @@ __global__ __launch_bounds__(64 * NW) void mmvq_mfma_res_kernel(const uint8_t *_
     }
 }
 
-template <int NW, int GPW, int NT, bool DB>
+template <class Fmt, int NW, int GPW, int NT, bool DB>
 static int launch_res(const uint8_t *w, const uint8_t *a, float *y, const float *r,
                       int32_t *isums, int64_t N, int nb, int T, hipStream_t stream)
 {
@@ -491,20 +491,20 @@ static int launch_res(const uint8_t *w, const uint8_t *a, float *y, const float 
     const int64_t ntiles = (N + 16 * R - 1) / (16 * R);
     const size_t lds = res_lds_bytes(NW, NT, R, nb, DB);
     const void *kt =
-        reinterpret_cast<const void *>(&mmvq_mfma_res_kernel<NW, GPW, NT, R, DB, true, false, true>);
+        reinterpret_cast<const void *>(&mmvq_mfma_res_kernel<Fmt, NW, GPW, NT, R, DB, true, false, true>);
     const void *kf =
-        reinterpret_cast<const void *>(&mmvq_mfma_res_kernel<NW, GPW, NT, R, DB, false, false, true>);
+        reinterpret_cast<const void *>(&mmvq_mfma_res_kernel<Fmt, NW, GPW, NT, R, DB, false, false, true>);
     allow_dynamic_lds(kt, lds);
     allow_dynamic_lds(kf, lds);
     const int cap = resident_workgroups(isums ? kt : kf, 64 * NW, lds);
     const dim3 grid((unsigned)(ntiles < cap ? ntiles : cap));
     const WideItems none = {nullptr, 0, 1};
     if (isums)
-        hipLaunchKernelGGL((mmvq_mfma_res_kernel<NW, GPW, NT, R, DB, true, false, true>), grid,
+        hipLaunchKernelGGL((mmvq_mfma_res_kernel<Fmt, NW, GPW, NT, R, DB, true, false, true>), grid,
                            dim3(64 * NW), lds, stream, w, a, nullptr, nullptr, isums, N, nb, T,
                            (int)ntiles, T, none);
     else
-        hipLaunchKernelGGL((mmvq_mfma_res_kernel<NW, GPW, NT, R, DB, false, false, true>), grid,
+        hipLaunchKernelGGL((mmvq_mfma_res_kernel<Fmt, NW, GPW, NT, R, DB, false, false, true>), grid,
                            dim3(64 * NW), lds, stream, w, a, y, r, nullptr, N, nb, T,
                            (int)ntiles, T, none);
     return check_launch();
@@ -522,13 +522,13 @@ static int launch_res_id(const uint8_t *w, const uint8_t *a, float *y, int64_t N
     const int64_t ntiles = (N + 16 * R - 1) / (16 * R);
     const size_t lds = res_lds_bytes(NW, NT, R, nb, DB, true);
     const void *k =
-        reinterpret_cast<const void *>(&mmvq_mfma_res_kernel<NW, GPW, NT, R, DB, false, true, false>);
+        reinterpret_cast<const void *>(&mmvq_mfma_res_kernel<Tq1Tile, NW, GPW, NT, R, DB, false, true, false>);
     allow_dynamic_lds(k, lds);
     const int64_t cap = resident_workgroups(k, 64 * NW, lds);
     const int64_t most = (int64_t)max_wide * ntiles;  // units when every item is in use
     const dim3 grid((unsigned)(most < cap ? most : cap));
     const WideItems items = {routed, max_items, pairs_per_col};
-    hipLaunchKernelGGL((mmvq_mfma_res_kernel<NW, GPW, NT, R, DB, false, true, false>), grid,
+    hipLaunchKernelGGL((mmvq_mfma_res_kernel<Tq1Tile, NW, GPW, NT, R, DB, false, true, false>), grid,
                        dim3(64 * NW), lds, stream, w, a, y, nullptr, nullptr, N, nb, 16,
                        (int)ntiles, a_cols, items);
     return check_launch();
@@ -560,13 +560,13 @@ static int launch_mm(const uint8_t *w, const uint8_t *a, float *y, int64_t N, in
     const int64_t ntiles = (N + 16 * R - 1) / (16 * R);
     const size_t lds = res_lds_bytes(NW, NT, R, nb, DB, true);
     const void *k =
-        reinterpret_cast<const void *>(&mmvq_mfma_res_kernel<NW, GPW, NT, R, DB, false, true, true>);
+        reinterpret_cast<const void *>(&mmvq_mfma_res_kernel<Tq1Tile, NW, GPW, NT, R, DB, false, true, true>);
     allow_dynamic_lds(k, lds);
     const int64_t cap = resident_workgroups(k, 64 * NW, lds);
     const int64_t units = (int64_t)((T + 16 * NT - 1) / (16 * NT)) * ntiles;
     const dim3 grid((unsigned)(units < cap ? units : cap));
     const WideItems chunks = {nullptr, 0, 1};
-    hipLaunchKernelGGL((mmvq_mfma_res_kernel<NW, GPW, NT, R, DB, false, true, true>), grid,
+    hipLaunchKernelGGL((mmvq_mfma_res_kernel<Tq1Tile, NW, GPW, NT, R, DB, false, true, true>), grid,
                        dim3(64 * NW), lds, stream, w, a, y, nullptr, nullptr, N, nb, 16 * NT,
                        (int)ntiles, T, chunks);
     return check_launch();
@@ -631,8 +631,9 @@ bool mfma_resident_supported(int64_t K, int32_t T)
     return Lr >= NW && res_lds_bytes(NW, NT, 1, nb, NT == 1) <= lds_budget();
 }
 
-int launch_mmvq_mfma_resident(const void *w, const void *a, float *y, int32_t *isums, int64_t N,
-                              int64_t K, int32_t T, hipStream_t stream, const float *r)
+template <class Fmt>
+static int launch_resident_fmt(const void *w, const void *a, float *y, int32_t *isums, int64_t N,
+                               int64_t K, int32_t T, hipStream_t stream, const float *r)
 {
     const int nb = (int)(K / kTq1BlockElems);
     const int Lr = 1 << lanes_per_row_log2(nb);
@@ -640,17 +641,29 @@ int launch_mmvq_mfma_resident(const void *w, const void *a, float *y, int32_t *i
     const uint8_t *ap = static_cast<const uint8_t *>(a);
     if (T <= 16) {
         switch (Lr) {
-        case 16: return launch_res<16, 1, 1, true>(wp, ap, y, r, isums, N, nb, T, stream);
-        case 32: return launch_res<16, 2, 1, true>(wp, ap, y, r, isums, N, nb, T, stream);
-        default: return launch_res<16, 4, 1, true>(wp, ap, y, r, isums, N, nb, T, stream);
+        case 16: return launch_res<Fmt, 16, 1, 1, true>(wp, ap, y, r, isums, N, nb, T, stream);
+        case 32: return launch_res<Fmt, 16, 2, 1, true>(wp, ap, y, r, isums, N, nb, T, stream);
+        default: return launch_res<Fmt, 16, 4, 1, true>(wp, ap, y, r, isums, N, nb, T, stream);
         }
     }
     switch (Lr) {
-    case 8: return launch_res<8, 1, 2, false>(wp, ap, y, r, isums, N, nb, T, stream);
-    case 16: return launch_res<8, 2, 2, false>(wp, ap, y, r, isums, N, nb, T, stream);
-    case 32: return launch_res<8, 4, 2, false>(wp, ap, y, r, isums, N, nb, T, stream);
-    default: return launch_res<8, 8, 2, false>(wp, ap, y, r, isums, N, nb, T, stream);
+    case 8: return launch_res<Fmt, 8, 1, 2, false>(wp, ap, y, r, isums, N, nb, T, stream);
+    case 16: return launch_res<Fmt, 8, 2, 2, false>(wp, ap, y, r, isums, N, nb, T, stream);
+    case 32: return launch_res<Fmt, 8, 4, 2, false>(wp, ap, y, r, isums, N, nb, T, stream);
+    default: return launch_res<Fmt, 8, 8, 2, false>(wp, ap, y, r, isums, N, nb, T, stream);
     }
+}
+
+int launch_mmvq_mfma_resident(const void *w, const void *a, float *y, int32_t *isums, int64_t N,
+                              int64_t K, int32_t T, hipStream_t stream, const float *r)
+{
+    return launch_resident_fmt<Tq1Tile>(w, a, y, isums, N, K, T, stream, r);
+}
+
+int launch_mmvq_mfma_resident_tq2(const void *w, const void *a, float *y, int32_t *isums,
+                                  int64_t N, int64_t K, int32_t T, hipStream_t stream)
+{
+    return launch_resident_fmt<Tq2Tile>(w, a, y, isums, N, K, T, stream, nullptr);
 }
 
 }  // namespace bqm

@@ -10,11 +10,13 @@
 // fields ("Upstream state": one load per packed byte, every digit expanded in
 // place), with the activations staged in LDS once per workgroup.
 //
-// Dispatch: the staged kernel below for up to kTq2StagedMaxCols columns (the
-// field extraction is one mask per field, so a lane's arithmetic stays under
-// its share of the HBM time up to several columns); above, the matrix-core
-// kernel with register-resident activations (mmvq_mfma_reg.hip, Tq2Tile) for
-// rows of 5 to 16 blocks, else the staged kernel in groups of columns.
+// Dispatch: the staged kernel below for one and two columns (the field
+// extraction is one mask per field, so a lane's arithmetic stays under its
+// share of the HBM time); from three columns the matrix-core kernels, which
+// take the format as a policy (Tq2Tile): the register-operand kernel for rows
+// of 5 to 16 blocks, else the LDS-resident one where the columns fit, else the
+// streamed one (14336 x 4096: staged 9.7, 10.9, 20.7, 24.3 us at 3, 4, 6, 8
+// columns, the register-operand kernel 10.0 to 10.1 us at each).
 #include "mmvq_staged.hpp"
 #include "tq2_decode.hpp"
 
@@ -64,7 +66,7 @@ int launch_tq2_pack(const int8_t *trits, const uint16_t *d, void *w, int64_t N, 
 // Staged product.
 // ---------------------------------------------------------------------------
 
-constexpr int kTq2StagedMaxCols = 8;
+constexpr int kTq2StagedMaxCols = 2;
 
 // Exact sub-block sums of one block against TC staged columns (column t at
 // ab0 + t * col_stride, in mmvq_staged.hpp's layout: dword j of sub-blocks
@@ -245,50 +247,30 @@ static void launch_tq2_staged_w(const uint8_t *w, const uint8_t *a, float *y, in
         launch_tq2_staged_tc<TC, 4>(w, a, y, isums, N, nb, T, lr, chunk, lds, stream);
 }
 
-// One staged launch over T <= kTq2StagedMaxCols columns whose chunk fits.
-static void launch_tq2_staged(const uint8_t *w, const uint8_t *a, float *y, int32_t *isums,
-                              int64_t N, int nb, int T, int lr, int chunk, hipStream_t stream)
-{
-    const size_t lds = (size_t)T * chunk * kActStride * 4;
-    // column-capacity ladder: a call pays for the next rung up
-    if (T == 1)
-        launch_tq2_staged_w<1>(w, a, y, isums, N, nb, T, lr, chunk, lds, stream);
-    else if (T == 2)
-        launch_tq2_staged_w<2>(w, a, y, isums, N, nb, T, lr, chunk, lds, stream);
-    else if (T <= 4)
-        launch_tq2_staged_w<4>(w, a, y, isums, N, nb, T, lr, chunk, lds, stream);
-    else
-        launch_tq2_staged_w<8>(w, a, y, isums, N, nb, T, lr, chunk, lds, stream);
-}
-
 int launch_mmvq_tq2(const void *w, const void *a, float *y, int32_t *isums, int64_t N, int64_t K,
                     int32_t T, hipStream_t stream)
 {
-    if (T > kTq2StagedMaxCols && mfma_reg_supported(K, T))
-        return launch_mmvq_mfma_reg_tq2(w, a, y, isums, N, K, T, stream);
+    if (T > kTq2StagedMaxCols) {
+        if (mfma_reg_supported(K, T))
+            return launch_mmvq_mfma_reg_tq2(w, a, y, isums, N, K, T, stream);
+        if (mfma_resident_supported(K, T))
+            return launch_mmvq_mfma_resident_tq2(w, a, y, isums, N, K, T, stream);
+        return launch_mmvq_mfma_tq2(w, a, y, isums, N, K, T, stream);
+    }
     const int nb = (int)(K / kTq1BlockElems);
     const int lr = lanes_per_row_log2(nb);
-    const size_t budget = lds_budget();
-    // the widest group of columns whose staged chunk fits the LDS budget
-    // (one column always fits: 64 blocks take 21,504 bytes)
-    int g = T < kTq2StagedMaxCols ? T : kTq2StagedMaxCols;
-    while (g > 1 && staged_chunk(nb, lr, g, budget) == 0)
-        g = g > 4 ? 4 : g / 2;
+    // two columns of 64 blocks take 43,008 bytes: always within the budget
+    const int chunk = staged_chunk(nb, lr, T, lds_budget());
+    if (chunk == 0)
+        return BQM_ERR_SHAPE;
+    const size_t lds = (size_t)T * chunk * kActStride * 4;
     const uint8_t *wp = static_cast<const uint8_t *>(w);
     const uint8_t *ap = static_cast<const uint8_t *>(a);
-    const int64_t col_bytes = (int64_t)nb * 8 * kQ81BlockBytes;
-    for (int c0 = 0; c0 < T; c0 += g) {
-        const int tg = T - c0 < g ? T - c0 : g;
-        const int chunk = staged_chunk(nb, lr, tg, budget);
-        if (chunk == 0)
-            return BQM_ERR_SHAPE;
-        launch_tq2_staged(wp, ap + c0 * col_bytes, isums ? nullptr : y + (int64_t)c0 * N,
-                          isums ? isums + (int64_t)c0 * N * nb * 8 : nullptr, N, nb, tg, lr, chunk,
-                          stream);
-        if (int rc = check_launch())
-            return rc;
-    }
-    return BQM_OK;
+    if (T == 1)
+        launch_tq2_staged_w<1>(wp, ap, y, isums, N, nb, T, lr, chunk, lds, stream);
+    else
+        launch_tq2_staged_w<2>(wp, ap, y, isums, N, nb, T, lr, chunk, lds, stream);
+    return check_launch();
 }
 
 }  // namespace bqm

@@ -138,6 +138,19 @@ struct Tq2Tile {
         const uint32_t *cs = tile + col * kStageCol + 9 * b + 2 * kg;
         return (long)(((uint64_t)cs[1] << 32) | cs[0]);
     }
+
+    // the same, given the staged sub-block's first dword
+    // (tile + col * kStageCol + 9 b)
+    static __device__ __forceinline__ long operand_at(const uint32_t *__restrict__ cs, int kg, int)
+    {
+        return (long)(((uint64_t)cs[2 * kg + 1] << 32) | cs[2 * kg]);
+    }
+
+    // the same from the eight q dwords of one Q8_1 block
+    static __device__ __forceinline__ u32x2 operand_dwords(const uint32_t (&q)[8], int kg, int)
+    {
+        return (u32x2){q[2 * kg], q[2 * kg + 1]};
+    }
 };
 
 }  // namespace bqm

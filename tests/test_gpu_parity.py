@@ -838,13 +838,13 @@ def test_tq1_dequantize_bit_exact(bqm, N, K, dtype):
 # TQ2_0 (2-bit fields; the layout is a reading, pinned in the oracle's tests)
 # ---------------------------------------------------------------------------
 
-# (N, K, T): the staged kernel at one, two, four and eight columns (ragged row
-# counts, odd block counts, one-block rows, rows longer than one staging pass:
-# 129 blocks); above eight columns the register-operand matrix-core kernel for
-# rows of 5 to 16 blocks (one and two column tiles, several row tiles per
-# workgroup at 20000 rows), else the staged kernel in column groups (of 8 for
-# rows of 24 blocks, of 4 where eight columns of 64 blocks exceed the LDS
-# budget: 40 x 16384 x 12)
+# (N, K, T): the staged kernel at one and two columns (ragged row counts, odd
+# block counts, one-block rows, rows longer than one staging pass: 65, 96 and
+# 129 blocks); from three columns the matrix-core kernels: register operands
+# for rows of 5 to 16 blocks (one and two column tiles, several row tiles per
+# workgroup at 20000 rows), LDS-resident columns for longer rows whose columns
+# fit (96 x 6144, 100 x 6144), the streamed kernel for the rest (rows of 3,
+# 64 and 129 blocks)
 TQ2_SHAPES = [(256, 1024, 1), (1, 256, 1), (33, 256, 2), (67, 768, 3), (130, 2304, 5),
               (515, 4096, 8), (96, 6144, 4), (40, 16384, 1), (17, 1280, 32), (300, 512, 16),
               (21, 4096, 17), (1, 2304, 9), (50, 16640, 1), (33, 24576, 2), (70, 65536, 2),
