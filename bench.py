@@ -62,10 +62,11 @@ def kernel_source_hash():
     return h.hexdigest()[:16]
 
 
-def algorithmic_bytes(N, K, T):
-    """Bytes a mat-vec call must move at minimum: packed weights once, the
-    Q8_1 activations once, the fp32 outputs once."""
-    return N * (K // 256) * 54 + T * (K // 32) * 36 + T * N * 4
+def algorithmic_bytes(N, K, T, block_bytes=54):
+    """Bytes a mat-vec call must move at minimum: packed weights once (54-byte
+    TQ1_0 or 66-byte TQ2_0 blocks), the Q8_1 activations once, the fp32
+    outputs once."""
+    return N * (K // 256) * block_bytes + T * (K // 32) * 36 + T * N * 4
 
 
 def moe_algorithmic_bytes(ids, N, K, per_slot=False):
@@ -253,6 +254,19 @@ def cpu_table(path):
             row["threads_all"] = threads
             rows.append(row)
             log("cpu", row)
+        if name in ("decode", "multicol", "ffn"):
+            # the same matrices packed as TQ2_0
+            w2 = oracle.tq2_pack(inp.trits, inp.d16)
+            for T in wl.Ts:
+                a = np.ascontiguousarray(a_all[:T])
+                row = {"workload": name, "op": "mmvq_tq2_0", "T": T, "N": wl.N, "K": wl.K}
+                for label, nt in (("one", 1), ("all", threads)):
+                    oracle.set_threads(nt)
+                    row["oracle_us_" + label] = round(oracle_median_us(
+                        lambda: oracle.tq2_mmvq(w2, a, wl.N, wl.K, T), runs=3), 1)
+                row["threads_all"] = threads
+                rows.append(row)
+                log("cpu", row)
     oracle.set_threads(threads)
     with open(path, "w") as f:
         json.dump({"host": info, "rows": rows}, f, indent=1)
@@ -475,7 +489,25 @@ def sweep(path, torch, np, bqm, synth, dev, launches, only=None):
             us = timer.time(row, lambda i: bqm.mmvq_tq1_0(wrot[i % R], a, N, K, T, out=y),
                             launches, y)
             _rate_fields(row, algorithmic_bytes(N, K, T), us, read_gbs)
-        del wrot, a_all, w0
+        del wrot, w0
+        torch.cuda.empty_cache()
+        if name != "tiny":
+            # the same trits and scales packed as TQ2_0 (66-byte blocks)
+            w2 = bqm.tq2_pack(torch.from_numpy(inp.trits).to(dev),
+                              torch.from_numpy(inp.d16.view(np.int16)).to(dev))
+            wrot, R = rotation(torch, w2, dev)
+            table.append(read_probe_row(torch, wrot, R, w2.numel(), name + " tq2", launches))
+            read_gbs = table[-1]["gbs"]
+            log("sweep", table[-1])
+            for T in wl.Ts:
+                a = a_all[:T].contiguous()
+                y = torch.empty((T, N), dtype=torch.float32, device=dev)
+                row = {"workload": name, "op": "mmvq_tq2_0", "N": N, "K": K, "T": T}
+                us = timer.time(row, lambda i: bqm.mmvq_tq2_0(wrot[i % R], a, N, K, T, out=y),
+                                launches, y)
+                _rate_fields(row, algorithmic_bytes(N, K, T, 66), us, read_gbs)
+            del wrot, w2
+        del a_all
         torch.cuda.empty_cache()
     # many-column product: prefill batches on the decode and ffn matrices
     for name in ("decode", "ffn"):
@@ -594,11 +626,28 @@ def trace_summary(trace_csv, sweep_json, out_md):
                         "p10_us": round(q(0.10), 3), "p90_us": round(q(0.90), 3),
                         "replay_corr": round(replay_corr, 3),
                         "kernels": sorted(set(_kernel_family(n) for n, _ in ds))}
+        if kpc > 1:
+            # calls of several kernels (the expert-routed product: routing
+            # pre-pass, narrow items, wide items): each kernel's own median
+            sub = {}
+            for c in range(ncalls):
+                for n, d in ds[c * kpc:(c + 1) * kpc]:
+                    sub.setdefault(_kernel_family(n), []).append(d)
+            row["trace"]["per_kernel_median_us"] = {
+                k: round(sorted(v)[len(v) // 2], 3) for k, v in sorted(sub.items())}
         if "algorithmic_bytes" in row:
             row["trace"]["gbs_at_median"] = round(row["algorithmic_bytes"] / med / 1e3, 1)
         lines.append("| %d | %s | %s | %s | %d | %d | %.3f | %.3f | %.3f | %.2f | %.3f |" % (
             idx, row["workload"], row["op"], row.get("T", ""), ncalls, kpc, med, q(0.10),
             q(0.90), replay_corr, row["us"]))
+    subs = [(idx, row) for idx, row in sorted(rows.items())
+            if "per_kernel_median_us" in row.get("trace", {})]
+    if subs:
+        lines += ["", "| row | workload | op | T | kernel | median µs |", "|---|---|---|---|---|---|"]
+        for idx, row in subs:
+            for k, v in row["trace"]["per_kernel_median_us"].items():
+                lines.append("| %d | %s | %s | %s | `%s` | %.3f |" % (
+                    idx, row["workload"], row["op"], row.get("T", ""), k, v))
     with open(sweep_json, "w") as f:
         json.dump(table, f, indent=1)
     with open(out_md, "w") as f:
@@ -621,7 +670,7 @@ def sweep_report(sweep_json, traced_json=None, cpu_json=None):
     if cpu_json:
         with open(cpu_json) as f:
             c = json.load(f)
-        cpu = {(r["workload"], r["T"]): r for r in c["rows"]}
+        cpu = {(r["workload"], r["T"], r.get("op", "")): r for r in c["rows"]}
     out = ["| workload | op | N x K | T | event µs | GB/s | % of 8 TB/s | % of read probe | "
            "trace median µs (p10, p90) | GB/s at median | oracle µs, 1 thread / all | "
            "checksum |", "|---|---|---|---|---|---|---|---|---|---|---|---|"]
@@ -629,7 +678,8 @@ def sweep_report(sweep_json, traced_json=None, cpu_json=None):
         if r["op"] in ("read_probe", "copy_probe", "tq1_dequantize", "tq1_get_rows"):
             continue
         t = tr.get((r["workload"], r["op"], r.get("T")))
-        cp = cpu.get((r["workload"], r.get("T"))) if r["op"].startswith("mmvq") else None
+        cp = (cpu.get((r["workload"], r.get("T"), "mmvq_tq2_0" if "tq2" in r["op"] else ""))
+              if r["op"].startswith("mmvq") else None)
         nk = ("%d x %d x %d" % (r["E"], r["N"], r["K"])) if "E" in r else (
             "%d x %d" % (r["N"], r["K"]))
         out.append("| %s | %s | %s | %s | %.3f | %.1f | %.1f | %s | %s | %s | %s | %s |" % (
