@@ -78,6 +78,23 @@ __device__ __forceinline__ TileOperands decode_lane_block(const LaneBlock &lb, Q
 
 constexpr long kAllMinusOne = -1;    // eight int8 -1 bytes
 
+// Pair-tile form (at most 8 activation columns): two 16-row tiles share one
+// v_mfma_i32_16x16x64_i8. Its 64-element K is four lane groups of 16 bytes
+// (an A lane group pairs with the same B lane group; D as above: lane (j, rg)
+// holds rows 4rg..4rg+3 of column j). Lane groups 0, 1 carry the first tile's
+// rows and the columns' q bytes in D columns 0..7; groups 2, 3 the second
+// tile's rows and the same columns' q bytes in D columns 8..15; a B lane of
+// the other half holds zeros. So D column j < 8 is the sub-block sums of the
+// first tile against column j, column 8 + j those of the second tile. Lane
+// group g = 2 t + h holds half h of each sub-block of a row of tile t: 16 of
+// its 32 elements (which 16 is the format's choice, matched on both sides).
+struct PairOperands {
+    i32x4 A[8];
+    float dw;    // the row's block scale (valid in lanes of half 1)
+};
+
+constexpr i32x4 kAllMinusOne4 = {-1, -1, -1, -1};   // sixteen int8 -1 bytes
+
 // Staging of one block of activations for a wave, through its own slice of
 // LDS (coalesced 8-byte pieces in, B operands out).
 constexpr int kStageCol = 74;        // dwords per staged column: 8 x 9 of Q8_1 data, 2 of padding
@@ -191,6 +208,66 @@ struct Tq1Tile {
         const uint32_t lo = b < 5 ? q[2 * kg] : q[kg];
         const uint32_t hi = b < 5 ? q[2 * kg + 1] : q[4 + kg];
         return (u32x2){lo, hi};
+    }
+
+    // Pair-tile form: half h of a row's block is elements 16h..16h+15 of
+    // sub-blocks 0..4 (digit b of qs dwords 4h..4h+3) and elements 8h..8h+7,
+    // 16+8h..16+8h+7 of sub-blocks 5..7 (digits of qs dwords 8+2h, 9+2h:
+    // 0 and 1 for sub-block 5, 2 and 3 for 6; for 7 digit 4 and then qh
+    // digits 2h, 2h+1). Loads: qs bytes 16h..16h+15 (five aligned dwords), qs
+    // bytes 32+8h..39+8h (three), the qh dword and the scale (two).
+    struct PairLane {
+        u32x4 lo;
+        uint32_t lo_x;
+        u32x3 hi;
+        u32x2 t;
+        uint32_t sh;
+    };
+
+    static __device__ __forceinline__ PairLane load_pair(__amdgpu_buffer_rsrc_t rw, uint32_t off,
+                                                         int h)
+    {
+        PairLane p;
+        p.sh = off & 3u;
+        const uint32_t base = off - p.sh;
+        p.lo = ld_b128(rw, base + 16 * h);
+        p.lo_x = ld_b32(rw, base + 16 * h + 16);
+        p.hi = __builtin_amdgcn_raw_buffer_load_b96(rw, base + 32 + 8 * h, 0, 0);
+        p.t = ld_b64(rw, base + 48);
+        return p;
+    }
+
+    static __device__ __forceinline__ PairOperands decode_pair(const PairLane &p, const Ctx &, int h)
+    {
+        const uint32_t w[4] = {align_bytes(p.lo.y, p.lo.x, p.sh), align_bytes(p.lo.z, p.lo.y, p.sh),
+                               align_bytes(p.lo.w, p.lo.z, p.sh), align_bytes(p.lo_x, p.lo.w, p.sh)};
+        QsDigits L[4];
+#pragma unroll
+        for (int d = 0; d < 4; d++)
+            L[d] = qs_digits<true>(w[d]);
+        const QsDigits H0 = qs_digits<true>(align_bytes(p.hi.y, p.hi.x, p.sh));
+        const QsDigits H1 = qs_digits<true>(align_bytes(p.hi.z, p.hi.y, p.sh));
+        const QhDigits Q = qh_digits<true>(align_bytes(p.t.y, p.t.x, p.sh));
+        PairOperands o;
+#pragma unroll
+        for (int c = 0; c < 5; c++)
+            o.A[c] = (i32x4){(int)L[0].U[c], (int)L[1].U[c], (int)L[2].U[c], (int)L[3].U[c]};
+        o.A[5] = (i32x4){(int)H0.U[0], (int)H1.U[0], (int)H0.U[1], (int)H1.U[1]};
+        o.A[6] = (i32x4){(int)H0.U[2], (int)H1.U[2], (int)H0.U[3], (int)H1.U[3]};
+        o.A[7] = (i32x4){(int)H0.U[4], (int)H1.U[4], (int)(h ? Q.U[2] : Q.U[0]),
+                         (int)(h ? Q.U[3] : Q.U[1])};
+        o.dw = f16_bits_to_f32(p.sh ? (p.t.y >> 16) : (p.t.y & 0xffffu));
+        return o;
+    }
+
+    // the matching q bytes of sub-block b from a staged tile
+    // (tile + col * kStageCol + 9 b: the sub-block's eight q dwords)
+    static __device__ __forceinline__ i32x4 pair_operand(const uint32_t *__restrict__ tile, int col,
+                                                         int h, int b)
+    {
+        const uint32_t *cs = tile + col * kStageCol + 9 * b;
+        return b < 5 ? (i32x4){(int)cs[4 * h], (int)cs[4 * h + 1], (int)cs[4 * h + 2], (int)cs[4 * h + 3]}
+                     : (i32x4){(int)cs[2 * h], (int)cs[2 * h + 1], (int)cs[4 + 2 * h], (int)cs[5 + 2 * h]};
     }
 };
 

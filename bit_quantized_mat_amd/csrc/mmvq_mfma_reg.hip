@@ -27,6 +27,15 @@
 // The weight format enters through a policy (Tq1Tile, Tq2Tile): how a lane
 // loads and decodes its share of a block and which staged activation bytes
 // make its B operand. Everything else is common to both formats.
+//
+// Pair-tile mode (PAIR, at most 8 columns): a work unit is 32 rows, two
+// 16-row tiles on one v_mfma_i32_16x16x64_i8 per sub-block (the layout in
+// mfma_common.hpp), so each fp32 conversion and fma of the epilogue serves a
+// real column; a decode lane then takes half of a row's block instead of a
+// quarter. The per-column fp32 order is unchanged, so the results are
+// bitwise those of the 16-column form.
+#include <type_traits>
+
 #include "tq2_decode.hpp"
 
 namespace bqm {
@@ -34,22 +43,31 @@ namespace bqm {
 // One lane's activation operands for one block and 16-column tile: the B
 // operand of each sub-block and the fp16 sub-block scales of its column,
 // two per dword (sub-block 2p in the low half, 2p + 1 in the high half).
+// PAIR: 16-byte B operands, zero in the lane groups of the other tile.
+template <bool PAIR>
 struct RegOperands {
-    long Bq[8];
+    typename std::conditional<PAIR, i32x4, long>::type Bq[8];
     uint32_t da2[4];
 };
 
 // Read them from a staged 16-column tile (mfma_common.hpp): lane (col, kg).
-template <class Fmt>
-__device__ __forceinline__ RegOperands read_reg_operands(const uint32_t *__restrict__ tile,
-                                                         int col, int kg)
+// PAIR: D column col is activation column col % 8 against tile col / 8, and
+// lane group kg carries half kg % 2 of tile kg / 2.
+template <class Fmt, bool PAIR>
+__device__ __forceinline__ RegOperands<PAIR> read_reg_operands(const uint32_t *__restrict__ tile,
+                                                               int col, int kg)
 {
-    RegOperands o;
+    RegOperands<PAIR> o;
     uint32_t d[8];
+    const int c = PAIR ? (col & 7) : col;
 #pragma unroll
     for (int b = 0; b < 8; b++) {
-        o.Bq[b] = Fmt::operand(tile, col, kg, b);
-        d[b] = tile[col * kStageCol + 9 * b + 8];
+        if constexpr (PAIR)
+            o.Bq[b] = (col >> 3) == (kg >> 1) ? Fmt::pair_operand(tile, c, kg & 1, b)
+                                              : (i32x4){0, 0, 0, 0};
+        else
+            o.Bq[b] = Fmt::operand(tile, col, kg, b);
+        d[b] = tile[c * kStageCol + 9 * b + 8];
     }
 #pragma unroll
     for (int p = 0; p < 4; p++)
@@ -59,8 +77,9 @@ __device__ __forceinline__ RegOperands read_reg_operands(const uint32_t *__restr
 
 // Fmt: the weight format policy; NW: waves per workgroup (8 or 16); GPW:
 // blocks per wave (Lr = NW GPW); NT: 16-column tiles; ISUMS: write the exact
-// per-sub-block sums instead of outputs. Rows hold at most Lr blocks.
-template <class Fmt, int NW, int GPW, int NT, bool ISUMS>
+// per-sub-block sums instead of outputs; PAIR: the pair-tile mode (NT = 1,
+// T <= 8, work units of 32 rows). Rows hold at most Lr blocks.
+template <class Fmt, int NW, int GPW, int NT, bool ISUMS, bool PAIR = false>
 __global__ __launch_bounds__(64 * NW) void mmvq_mfma_reg_kernel(const uint8_t *__restrict__ w,
                                                                 const uint8_t *__restrict__ a,
                                                                 float *y, const float *resid,
@@ -82,6 +101,17 @@ __global__ __launch_bounds__(64 * NW) void mmvq_mfma_reg_kernel(const uint8_t *_
     const __amdgpu_buffer_rsrc_t rw = make_rsrc(w, (uint64_t)N * row_bytes);
     const __amdgpu_buffer_rsrc_t ra = make_rsrc(a, (uint64_t)T * col_bytes);
 
+    static_assert(!PAIR || NT == 1, "pair tiles take at most 8 columns");
+    constexpr uint32_t kRows = PAIR ? 32u : 16u;  // rows per work unit
+    typedef typename std::conditional<PAIR, typename Fmt::PairLane, typename Fmt::Lane>::type
+        LaneT;
+    auto load_lane = [&](uint32_t off) -> LaneT {
+        if constexpr (PAIR)
+            return Fmt::load_pair(rw, off, kg & 1);
+        else
+            return Fmt::load(rw, off, kg);
+    };
+
     int tile = blockIdx.x;
     if (tile >= ntiles)
         return;  // uniform
@@ -90,18 +120,18 @@ __global__ __launch_bounds__(64 * NW) void mmvq_mfma_reg_kernel(const uint8_t *_
     // matrix is below 4 GiB with at least 5 blocks (270 bytes) per row, so
     // rows stay below 2^24, and a 24-bit product gives the byte offset
     auto row_offset = [&](int t) -> uint32_t {
-        const uint32_t r = (uint32_t)t * 16u + (uint32_t)(lane & 15);
+        const uint32_t r = (uint32_t)t * kRows + (PAIR ? 16u * (uint32_t)(kg >> 1) : 0u) +
+                           (uint32_t)(lane & 15);
         return r < (uint64_t)N ? __umul24(r, row_bytes) : 0u;
     };
 
     // the first tile's weights, then this wave's activation operands
-    typename Fmt::Lane lb[GPW];
+    LaneT lb[GPW];
     uint32_t roff = row_offset(tile);
 #pragma unroll
     for (int gi = 0; gi < GPW; gi++) {
         const int B = wave + NW * gi;
-        lb[gi] = Fmt::load(rw, B < nb ? roff + (uint32_t)B * Fmt::kBlockBytes : Fmt::kIdle,
-                           kg);
+        lb[gi] = load_lane(B < nb ? roff + (uint32_t)B * Fmt::kBlockBytes : Fmt::kIdle);
     }
     // every (block, column tile) of this wave: its 16 columns' 288-byte runs
     // of Q8_1 blocks loaded as coalesced 8-byte pieces (all sets in flight
@@ -123,7 +153,7 @@ __global__ __launch_bounds__(64 * NW) void mmvq_mfma_reg_kernel(const uint8_t *_
         for (int k = 0; k < 9; k++)
             piece[st][k] = __builtin_amdgcn_raw_buffer_load_b64(ra, smap.gofs[k], so, 0);
     }
-    RegOperands opnd[GPW][NT];
+    RegOperands<PAIR> opnd[GPW][NT];
 #pragma unroll
     for (int st = 0; st < kSets; st++) {
         if (st > 0)
@@ -132,12 +162,12 @@ __global__ __launch_bounds__(64 * NW) void mmvq_mfma_reg_kernel(const uint8_t *_
         for (int k = 0; k < 9; k++)
             *reinterpret_cast<u32x2 *>(stage + smap.lofs[k]) = piece[st][k];
         wave_lds_order();
-        opnd[st / NT][st % NT] = read_reg_operands<Fmt>(stage, col, kg);
+        opnd[st / NT][st % NT] = read_reg_operands<Fmt, PAIR>(stage, col, kg);
     }
 
     int parity = 0;
     for (;;) {
-        const int64_t r0 = (int64_t)tile * 16;
+        const int64_t r0 = (int64_t)tile * kRows;
         const int next_tile = tile + gridDim.x;
         const bool have_next = next_tile < ntiles;
         const uint32_t next_roff = row_offset(next_tile);
@@ -145,15 +175,12 @@ __global__ __launch_bounds__(64 * NW) void mmvq_mfma_reg_kernel(const uint8_t *_
         // multiplied (every lane issues them, at Fmt::kIdle when there
         // is no next tile, so that their data is first waited for where it is
         // decoded)
-        typename Fmt::Lane ln[GPW];
+        LaneT ln[GPW];
 #pragma unroll
         for (int gi = 0; gi < GPW; gi++) {
             const int B = wave + NW * gi;
-            ln[gi] = Fmt::load(rw,
-                               have_next && B < nb
-                                   ? next_roff + (uint32_t)B * Fmt::kBlockBytes
-                                   : Fmt::kIdle,
-                               kg);
+            ln[gi] = load_lane(have_next && B < nb ? next_roff + (uint32_t)B * Fmt::kBlockBytes
+                                                   : Fmt::kIdle);
         }
 
         float acc[GPW][NT][4];
@@ -166,27 +193,43 @@ __global__ __launch_bounds__(64 * NW) void mmvq_mfma_reg_kernel(const uint8_t *_
                 for (int i = 0; i < 4; i++)
                     acc[gi][ct][i] = 0.0f;
             if (B < nb) {  // uniform: else this group holds no block
-            const TileOperands op = Fmt::decode(lb[gi], ctx);
+            typedef typename std::conditional<PAIR, PairOperands, TileOperands>::type OpsT;
+            OpsT op;
+            if constexpr (PAIR)
+                op = Fmt::decode_pair(lb[gi], ctx, kg & 1);
+            else
+                op = Fmt::decode(lb[gi], ctx);
+            // PAIR: the output lane's rows are in tile col / 8, whose block
+            // scales sit in the decode lanes of its half 1
+            const int dw_src = PAIR ? 4 * rg + 16 * (2 * (col >> 3) + 1) : 4 * rg;
             float dw[4];  // block scales of the four rows this output lane holds
 #pragma unroll
             for (int i = 0; i < 4; i++)
-                dw[i] = __shfl(op.dw, 4 * rg + i, 64);
+                dw[i] = __shfl(op.dw, dw_src + i, 64);
 #pragma unroll
             for (int ct = 0; ct < NT; ct++) {
-                const RegOperands &o = opnd[gi][ct];
+                const RegOperands<PAIR> &o = opnd[gi][ct];
                 float s[4];
 #pragma unroll
                 for (int b = 0; b < 8; b++) {
                     // -sum(q) of this lane's column on every row, then + sum(u q)
-                    const i32x4 neg_sum = __builtin_amdgcn_mfma_i32_16x16x32_i8(
-                        kAllMinusOne, o.Bq[b], (i32x4){0, 0, 0, 0}, 0, 0, 0);
-                    const i32x4 C =
-                        __builtin_amdgcn_mfma_i32_16x16x32_i8(op.A[b], o.Bq[b], neg_sum, 0, 0, 0);
+                    i32x4 C;
+                    if constexpr (PAIR) {
+                        const i32x4 neg_sum = __builtin_amdgcn_mfma_i32_16x16x64_i8(
+                            kAllMinusOne4, o.Bq[b], (i32x4){0, 0, 0, 0}, 0, 0, 0);
+                        C = __builtin_amdgcn_mfma_i32_16x16x64_i8(op.A[b], o.Bq[b], neg_sum, 0,
+                                                                  0, 0);
+                    } else {
+                        const i32x4 neg_sum = __builtin_amdgcn_mfma_i32_16x16x32_i8(
+                            kAllMinusOne, o.Bq[b], (i32x4){0, 0, 0, 0}, 0, 0, 0);
+                        C = __builtin_amdgcn_mfma_i32_16x16x32_i8(op.A[b], o.Bq[b], neg_sum, 0,
+                                                                  0, 0);
+                    }
                     if (ISUMS) {
-                        const int c = ct * 16 + col;
+                        const int c = PAIR ? (col & 7) : ct * 16 + col;
 #pragma unroll
                         for (int i = 0; i < 4; i++) {
-                            const int64_t row = r0 + 4 * rg + i;
+                            const int64_t row = r0 + (PAIR ? 16 * (col >> 3) : 0) + 4 * rg + i;
                             if (c < T && row < N)
                                 isums[((int64_t)c * N + row) * nblk + 8 * B + b] = C[i];
                         }
@@ -267,8 +310,8 @@ __global__ __launch_bounds__(64 * NW) void mmvq_mfma_reg_kernel(const uint8_t *_
                 const int ls = o / kPer, k = o - (o / kPer) * kPer;
                 const int oc = ls & 15, org = ls >> 4;
                 const int ct = k >> 2, i = k & 3;
-                const int c = ct * 16 + oc;
-                const int64_t row = r0 + 4 * org + i;
+                const int c = PAIR ? (oc & 7) : ct * 16 + oc;
+                const int64_t row = r0 + (PAIR ? 16 * (oc >> 3) : 0) + 4 * org + i;
                 if (j == 0 && c < T && row < N) {
                     const int64_t oi = (int64_t)c * N + row;
                     y[oi] = resid ? v + resid[oi] : v;
@@ -308,14 +351,17 @@ bool mfma_reg_supported(int64_t K, int32_t T)
     return reg_config((int)(K / kTq1BlockElems), T, NW, GPW, NT);
 }
 
-template <class Fmt, int NW, int GPW, int NT>
+template <class Fmt, int NW, int GPW, int NT, bool PAIR = false>
 static int launch_reg(const uint8_t *w, const uint8_t *a, float *y, const float *r,
                       int32_t *isums, int64_t N, int nb, int T, hipStream_t stream)
 {
-    const int64_t ntiles = (N + 15) / 16;
+    const int64_t rows = PAIR ? 32 : 16;
+    const int64_t ntiles = (N + rows - 1) / rows;
     const size_t lds = ((size_t)2 * NW * 64 * NT * 4 + (size_t)NW * 16 * kStageCol) * 4;
-    const void *kt = reinterpret_cast<const void *>(&mmvq_mfma_reg_kernel<Fmt, NW, GPW, NT, true>);
-    const void *kf = reinterpret_cast<const void *>(&mmvq_mfma_reg_kernel<Fmt, NW, GPW, NT, false>);
+    const void *kt =
+        reinterpret_cast<const void *>(&mmvq_mfma_reg_kernel<Fmt, NW, GPW, NT, true, PAIR>);
+    const void *kf =
+        reinterpret_cast<const void *>(&mmvq_mfma_reg_kernel<Fmt, NW, GPW, NT, false, PAIR>);
     allow_dynamic_lds(kt, lds);
     allow_dynamic_lds(kf, lds);
     // persistent: as many workgroups as the device holds at once, each
@@ -323,12 +369,21 @@ static int launch_reg(const uint8_t *w, const uint8_t *a, float *y, const float 
     const int cap = resident_workgroups(isums ? kt : kf, 64 * NW, lds);
     const dim3 grid((unsigned)(ntiles < cap ? ntiles : cap));
     if (isums)
-        hipLaunchKernelGGL((mmvq_mfma_reg_kernel<Fmt, NW, GPW, NT, true>), grid, dim3(64 * NW),
-                           lds, stream, w, a, nullptr, nullptr, isums, N, nb, T, (int)ntiles);
+        hipLaunchKernelGGL((mmvq_mfma_reg_kernel<Fmt, NW, GPW, NT, true, PAIR>), grid,
+                           dim3(64 * NW), lds, stream, w, a, nullptr, nullptr, isums, N, nb, T,
+                           (int)ntiles);
     else
-        hipLaunchKernelGGL((mmvq_mfma_reg_kernel<Fmt, NW, GPW, NT, false>), grid, dim3(64 * NW),
-                           lds, stream, w, a, y, r, nullptr, N, nb, T, (int)ntiles);
+        hipLaunchKernelGGL((mmvq_mfma_reg_kernel<Fmt, NW, GPW, NT, false, PAIR>), grid,
+                           dim3(64 * NW), lds, stream, w, a, y, r, nullptr, N, nb, T, (int)ntiles);
     return check_launch();
+}
+
+// Pair tiles for calls of at most 8 columns when the 32-row units still give
+// every compute unit one (14336 x 4096: 11.3 -> 9.5 us at 5 columns, 11.2 ->
+// 9.7 at 8; TQ2_0 10.0 -> 8.3 at 3; at 4096 rows, 128 units, 5.6 -> 6.4 us).
+static bool use_pair(int64_t N, int T)
+{
+    return T <= 8 && (N + 31) / 32 >= compute_units();
 }
 
 template <class Fmt>
@@ -344,6 +399,9 @@ static int launch_reg_fmt(const void *w, const void *a, float *y, int32_t *isums
     if (NT == 2)
         return NW == 8 ? launch_reg<Fmt, 8, 1, 2>(wp, ap, y, r, isums, N, nb, T, stream)
                        : launch_reg<Fmt, 16, 1, 2>(wp, ap, y, r, isums, N, nb, T, stream);
+    if (use_pair(N, T))
+        return NW == 8 ? launch_reg<Fmt, 8, 1, 1, true>(wp, ap, y, r, isums, N, nb, T, stream)
+                       : launch_reg<Fmt, 16, 1, 1, true>(wp, ap, y, r, isums, N, nb, T, stream);
     return NW == 8 ? launch_reg<Fmt, 8, 1, 1>(wp, ap, y, r, isums, N, nb, T, stream)
                    : launch_reg<Fmt, 16, 1, 1>(wp, ap, y, r, isums, N, nb, T, stream);
 }

@@ -151,6 +151,60 @@ struct Tq2Tile {
     {
         return (u32x2){q[2 * kg], q[2 * kg + 1]};
     }
+
+    // Pair-tile form (mfma_common.hpp): half h of a row's block is elements
+    // 16h..16h+15 of every sub-block, i.e. fields 0..3 of qs bytes
+    // 16h..16h+15 (sub-blocks 0..3) and of qs bytes 32+16h..47+16h
+    // (sub-blocks 4..7). Loads: five aligned dwords from each; for h = 1 the
+    // fifth of the second holds the scale.
+    struct PairLane {
+        u32x4 lo;
+        uint32_t lo_x;
+        u32x4 hi;
+        uint32_t hi_x;
+        uint32_t sh;
+    };
+
+    static __device__ __forceinline__ PairLane load_pair(__amdgpu_buffer_rsrc_t rw, uint32_t off,
+                                                         int h)
+    {
+        PairLane p;
+        p.sh = off & 3u;
+        const uint32_t base = off - p.sh;
+        p.lo = ld_b128(rw, base + 16 * h);
+        p.lo_x = ld_b32(rw, base + 16 * h + 16);
+        p.hi = ld_b128(rw, base + 32 + 16 * h);
+        p.hi_x = ld_b32(rw, base + 48 + 16 * h);
+        return p;
+    }
+
+    static __device__ __forceinline__ PairOperands decode_pair(const PairLane &p, const Ctx &, int)
+    {
+        const uint32_t x[2][4] = {
+            {align_bytes(p.lo.y, p.lo.x, p.sh), align_bytes(p.lo.z, p.lo.y, p.sh),
+             align_bytes(p.lo.w, p.lo.z, p.sh), align_bytes(p.lo_x, p.lo.w, p.sh)},
+            {align_bytes(p.hi.y, p.hi.x, p.sh), align_bytes(p.hi.z, p.hi.y, p.sh),
+             align_bytes(p.hi.w, p.hi.z, p.sh), align_bytes(p.hi_x, p.hi.w, p.sh)}};
+        PairOperands o;
+#pragma unroll
+        for (int q = 0; q < 2; q++)
+#pragma unroll
+            for (int f = 0; f < 4; f++)
+                o.A[4 * q + f] = (i32x4){(int)tq2_field_digits(x[q][0], f),
+                                         (int)tq2_field_digits(x[q][1], f),
+                                         (int)tq2_field_digits(x[q][2], f),
+                                         (int)tq2_field_digits(x[q][3], f)};
+        // bytes 64, 65 of the block sit in hi_x of half 1
+        o.dw = f16_bits_to_f32(p.sh ? (p.hi_x >> 16) : (p.hi_x & 0xffffu));
+        return o;
+    }
+
+    static __device__ __forceinline__ i32x4 pair_operand(const uint32_t *__restrict__ tile, int col,
+                                                         int h, int b)
+    {
+        const uint32_t *cs = tile + col * kStageCol + 9 * b + 4 * h;
+        return (i32x4){(int)cs[0], (int)cs[1], (int)cs[2], (int)cs[3]};
+    }
 };
 
 }  // namespace bqm

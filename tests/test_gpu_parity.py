@@ -172,12 +172,15 @@ def _case(N, K, T, seed, p_zero=1 / 3, outliers=0.01, d_lo=0.01, d_hi=0.1):
 # from there): 65 blocks (a one-block last pass), 96 (a partial second pass),
 # 129 (two full passes of 128 and a one-block tail) and 256. The last two
 # give the register-operand kernel more row tiles than workgroups (several
-# tiles per workgroup, both halves of its partial-sum buffer).
+# tiles per workgroup, both halves of its partial-sum buffer). From 8192 rows
+# at 5 to 8 columns it pairs two 16-row tiles per matrix-core product: 9000 x
+# 4096, 8200 x 1280 (5 blocks per row, one 8-row tile in the last unit) and
+# 8230 x 4096.
 SHAPES = [(256, 1024, 1), (1, 256, 1), (33, 256, 2), (67, 768, 3), (130, 2304, 5),
           (515, 4096, 8), (96, 6144, 4), (40, 16384, 1), (17, 1280, 32), (300, 512, 16),
           (40, 16384, 6), (50, 9216, 5), (21, 4096, 17), (1, 2304, 9), (4500, 4096, 3),
           (4200, 2560, 4), (50, 16640, 1), (33, 24576, 2), (300, 33024, 1), (70, 65536, 2),
-          (9000, 4096, 7), (20000, 2048, 24)]
+          (9000, 4096, 7), (20000, 2048, 24), (8200, 1280, 5), (8230, 4096, 8)]
 
 
 # ---------------------------------------------------------------------------
@@ -749,7 +752,7 @@ def test_mmvq_negative_and_subnormal_weight_scales(bqm, N, K, T):
 # matrix-core (five columns over K too long to keep resident), staged
 # multi-pass rows
 ADD_SHAPES = [(256, 1024, 1), (4500, 4096, 2), (4500, 4096, 3), (333, 2304, 4), (515, 4096, 8),
-              (17, 1280, 32), (50, 9216, 5), (50, 16640, 1)]
+              (17, 1280, 32), (50, 9216, 5), (50, 16640, 1), (8250, 4096, 6)]
 
 
 @pytest.mark.parametrize("N,K,T", ADD_SHAPES)
@@ -844,12 +847,14 @@ def test_tq1_dequantize_bit_exact(bqm, N, K, dtype):
 # for rows of 5 to 16 blocks (one and two column tiles, several row tiles per
 # workgroup at 20000 rows), LDS-resident columns for longer rows whose columns
 # fit (96 x 6144, 100 x 6144), the streamed kernel for the rest (rows of 3,
-# 64 and 129 blocks)
+# 64 and 129 blocks); from 8192 rows at 3 to 8 columns the register-operand
+# kernel's pair tiles (9000 x 4096, 8200 x 2048, 8230 x 1536)
 TQ2_SHAPES = [(256, 1024, 1), (1, 256, 1), (33, 256, 2), (67, 768, 3), (130, 2304, 5),
               (515, 4096, 8), (96, 6144, 4), (40, 16384, 1), (17, 1280, 32), (300, 512, 16),
               (21, 4096, 17), (1, 2304, 9), (50, 16640, 1), (33, 24576, 2), (70, 65536, 2),
               (9000, 4096, 7), (20000, 2048, 24), (40, 16384, 12), (45, 33024, 3),
-              (4500, 4096, 3), (100, 6144, 20), (7, 256, 32)]
+              (4500, 4096, 3), (100, 6144, 20), (7, 256, 32), (9000, 4096, 3),
+              (8200, 2048, 6), (8230, 1536, 8)]
 
 
 def _prep_tq2(bqm, trits, d16, x):
@@ -941,7 +946,8 @@ def test_tq2_one_hot_element_map(bqm):
 
 @pytest.mark.parametrize("N,K,T", [(515, 4096, 1), (300, 2304, 2), (4500, 4096, 3),
                                    (96, 6144, 4), (9000, 4096, 7), (20000, 2048, 24),
-                                   (21, 4096, 17), (40, 16384, 12), (100, 6144, 20)])
+                                   (21, 4096, 17), (40, 16384, 12), (100, 6144, 20),
+                                   (8300, 4096, 5), (8300, 4096, 3)])
 def test_tq2_equals_tq1_of_the_same_trits(bqm, N, K, T):
     """Both formats' kernels keep the library's one fp32 order, so the TQ2_0
     product of a matrix is bitwise the TQ1_0 product of the same trits and
