@@ -85,6 +85,11 @@ int launch_mmvq_mfma_resident(const void *w, const void *a, float *y, int32_t *i
 bool mfma_reg_supported(int64_t K, int32_t T);
 int launch_mmvq_mfma_reg(const void *w, const void *a, float *y, int32_t *isums, int64_t N,
                          int64_t K, int32_t T, hipStream_t stream, const float *r = nullptr);
+// Whether pair tiles (two 16-row tiles per 16 x 16 x 64 matrix product, at
+// most 8 columns) pay for N rows: a 32-row unit costs about 1.5 of a 16-row
+// one, so they do when the busiest compute unit has fewer than two thirds as
+// many units.
+bool pair_tiles_pay(int64_t N);
 // The same kernel on TQ2_0 weights (same shapes).
 int launch_mmvq_mfma_reg_tq2(const void *w, const void *a, float *y, int32_t *isums, int64_t N,
                              int64_t K, int32_t T, hipStream_t stream, const float *r = nullptr);

@@ -269,6 +269,13 @@ struct Tq1Tile {
         return b < 5 ? (i32x4){(int)cs[4 * h], (int)cs[4 * h + 1], (int)cs[4 * h + 2], (int)cs[4 * h + 3]}
                      : (i32x4){(int)cs[2 * h], (int)cs[2 * h + 1], (int)cs[4 + 2 * h], (int)cs[5 + 2 * h]};
     }
+
+    // the same from the eight q dwords of one Q8_1 block
+    static __device__ __forceinline__ u32x4 pair_dwords(const uint32_t (&q)[8], int h, int b)
+    {
+        return b < 5 ? (u32x4){q[4 * h], q[4 * h + 1], q[4 * h + 2], q[4 * h + 3]}
+                     : (u32x4){q[2 * h], q[2 * h + 1], q[4 + 2 * h], q[5 + 2 * h]};
+    }
 };
 
 // Orders this wave's LDS writes before its later LDS reads (a wave's LDS

@@ -378,12 +378,19 @@ static int launch_reg(const uint8_t *w, const uint8_t *a, float *y, const float 
     return check_launch();
 }
 
-// Pair tiles for calls of at most 8 columns when the 32-row units still give
-// every compute unit one (14336 x 4096: 11.3 -> 9.5 us at 5 columns, 11.2 ->
-// 9.7 at 8; TQ2_0 10.0 -> 8.3 at 3; at 4096 rows, 128 units, 5.6 -> 6.4 us).
+bool pair_tiles_pay(int64_t N)
+{
+    const int64_t cu = compute_units();
+    const int64_t u32 = ((N + 31) / 32 + cu - 1) / cu, u16 = ((N + 15) / 16 + cu - 1) / cu;
+    return 3 * u32 < 2 * u16;
+}
+
+// Pair tiles for calls of at most 8 columns when they pay (14336 x 4096:
+// 11.3 -> 9.5 us at 5 columns, 11.2 -> 9.7 at 8; TQ2_0 10.0 -> 8.3 at 3; at
+// 4096 rows, one unit per compute unit either way, 5.6 -> 6.4 us).
 static bool use_pair(int64_t N, int T)
 {
-    return T <= 8 && (N + 31) / 32 >= compute_units();
+    return T <= 8 && pair_tiles_pay(N);
 }
 
 template <class Fmt>

@@ -24,27 +24,37 @@
 // The weight format enters through a policy (Tq1Tile, Tq2Tile): a lane's
 // share of a block, its decode, and which q bytes of a Q8_1 block make each
 // lane's B operand (so the staged operand layout follows the format).
+#include <type_traits>
+
 #include "tq2_decode.hpp"
 
 namespace bqm {
 
 // LDS layout, in dwords (nb blocks per row, NT column tiles of 16):
 //   bq   [ct][B][b][lane] x 2   B operand of `lane` for sub-block b of block B
+//        pair tiles (at most 8 columns, mfma_common.hpp): [B][b] x kPairSlot,
+//        each slot [h][c] x 4 (half h of column c's sub-block) then 4 zero
+//        dwords, read by the lanes of the other tile's half
 //   dah  [B][c] x 4             fp16 scales of column c's sub-blocks 8B..8B+7
 //   red  [DB ? 2 : 1][NW][lane][R NT 4]  partial sums of the waves
 // The partial sums are double-buffered (one barrier per tile) when LDS has
 // room for both halves, else single (a second barrier per tile).
-__host__ __device__ inline size_t res_bq_dwords(int NT, int nb) { return (size_t)NT * nb * 8 * 128; }
+constexpr int kPairSlot = 68;
+__host__ __device__ inline size_t res_bq_dwords(int NT, int nb, bool pair = false)
+{
+    return pair ? (size_t)nb * 8 * kPairSlot : (size_t)NT * nb * 8 * 128;
+}
 __host__ __device__ inline size_t res_dah_dwords(int NT, int nb) { return (size_t)nb * 16 * NT * 4; }
 __host__ __device__ inline size_t res_red_dwords(int NW, int NT, int R, bool db)
 {
     return (size_t)(db ? 2 : 1) * NW * 64 * R * NT * 4;
 }
 // id: room for the expert-routed mode's two 16 NT-entry column tables
-inline size_t res_lds_bytes(int NW, int NT, int R, int nb, bool db, bool id = false)
+inline size_t res_lds_bytes(int NW, int NT, int R, int nb, bool db, bool id = false,
+                            bool pair = false)
 {
-    return (res_bq_dwords(NT, nb) + res_dah_dwords(NT, nb) + res_red_dwords(NW, NT, R, db) +
-            (id ? 32 * NT : 0)) * 4;
+    return (res_bq_dwords(NT, nb, pair) + res_dah_dwords(NT, nb) +
+            res_red_dwords(NW, NT, R, db) + (id ? 32 * NT : 0)) * 4;
 }
 
 // Store one staged Q8_1 block (block j of column c, its 36 bytes in v0, v1,
@@ -119,6 +129,36 @@ __device__ __forceinline__ void stage_all_columns(uint32_t *__restrict__ bq,
     }
 }
 
+// Pair tiles: the T <= 8 columns into the pair slots (and dah), one Q8_1
+// block per thread and step, consecutive threads on consecutive columns of
+// one block; then the slots' zero dwords.
+template <class Fmt, bool ID>
+__device__ __forceinline__ void stage_pair_columns(uint32_t *__restrict__ bq,
+                                                   uint32_t *__restrict__ dah,
+                                                   __amdgpu_buffer_rsrc_t ra, int T, int nb,
+                                                   const uint32_t *colbase)
+{
+    const int nblk = nb * 8;
+    const int items = T * nblk;
+    for (int it = threadIdx.x; it < items; it += blockDim.x) {
+        const int j = it / T, c = it - j * T;
+        const int B = j >> 3, b = j & 7;
+        const uint32_t off = (ID ? colbase[c] : (uint32_t)c * nblk * kQ81BlockBytes) +
+                             (uint32_t)j * kQ81BlockBytes;
+        const u32x4 v0 = ld_b128(ra, off);
+        const u32x4 v1 = ld_b128(ra, off + 16);
+        const uint32_t ds = ld_b32(ra, off + 32);
+        const uint32_t q[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+        uint32_t *slot = bq + (size_t)j * kPairSlot;
+#pragma unroll
+        for (int h = 0; h < 2; h++)
+            *reinterpret_cast<u32x4 *>(slot + (h * 8 + c) * 4) = Fmt::pair_dwords(q, h, b);
+        reinterpret_cast<uint16_t *>(dah + ((size_t)B * 16 + c) * 4)[b] = (uint16_t)ds;
+    }
+    for (int j = threadIdx.x; j < nblk; j += blockDim.x)
+        *reinterpret_cast<u32x4 *>(bq + (size_t)j * kPairSlot + 64) = (u32x4){0, 0, 0, 0};
+}
+
 // Work items of the item mode. Expert-routed products: the routing table the
 // routing pre-pass writes (mmvq_id.hip): item k of the wide list is
 // routed[2 + 3 (max_items + k) ..] = (expert, first run slot, pairs), and run
@@ -139,8 +179,10 @@ struct WideItems {
 // matrix against its pairs' columns, outputs y[pair][row]; or a chunk of the
 // columns of a many-column product); RUNS: columns copied in runs of blocks
 // (stage_all_columns; plain products and column chunks, not expert items);
-// `a_cols` is the number of columns a holds (T in the plain mode).
-template <class Fmt, int NW, int GPW, int NT, int R, bool DB, bool ISUMS, bool ID, bool RUNS>
+// `a_cols` is the number of columns a holds (T in the plain mode); PAIR:
+// pair tiles (NT = R = 1, at most 8 columns, units of 32 rows).
+template <class Fmt, int NW, int GPW, int NT, int R, bool DB, bool ISUMS, bool ID, bool RUNS,
+          bool PAIR = false>
 __global__ __launch_bounds__(64 * NW) void mmvq_mfma_res_kernel(const uint8_t *__restrict__ w,
                                                                 const uint8_t *__restrict__ a,
                                                                 float *y, const float *resid,
@@ -149,9 +191,10 @@ __global__ __launch_bounds__(64 * NW) void mmvq_mfma_res_kernel(const uint8_t *_
                                                                 int ntiles, int a_cols,
                                                                 WideItems items)
 {
+    static_assert(!PAIR || (NT == 1 && R == 1 && !RUNS), "pair tiles: one 8-column tile");
     extern __shared__ uint32_t smem[];
     uint32_t *bq = smem;
-    uint32_t *dah = smem + res_bq_dwords(NT, nb);
+    uint32_t *dah = smem + res_bq_dwords(NT, nb, PAIR);
     float *red = reinterpret_cast<float *>(dah + res_dah_dwords(NT, nb));
     // ID: per-column tables after the partial sums (byte offset of the token's
     // Q8_1 row, pair index)
@@ -168,6 +211,12 @@ __global__ __launch_bounds__(64 * NW) void mmvq_mfma_res_kernel(const uint8_t *_
     const int nblk = nb * 8;
     const uint64_t w_bytes = (uint64_t)N * nb * Fmt::kBlockBytes;
     const __amdgpu_buffer_rsrc_t ra = make_rsrc(a, (uint64_t)a_cols * nblk * kQ81BlockBytes);
+    constexpr int kRows = PAIR ? 32 : 16 * R;  // rows per unit
+    typedef typename std::conditional<PAIR, typename Fmt::PairLane, typename Fmt::Lane>::type
+        LaneT;
+    // PAIR: this lane's dword offset in a pair slot (the zero dwords for a
+    // lane group of the other tile)
+    const int pair_off = (col >> 3) == (kg >> 1) ? ((kg & 1) * 8 + (col & 7)) * 4 : 64;
 
     // Work units: in the plain mode the row tiles, strided over the grid; in
     // the expert mode (wide item, row tile) pairs, item-major, workgroup i
@@ -219,36 +268,46 @@ __global__ __launch_bounds__(64 * NW) void mmvq_mfma_res_kernel(const uint8_t *_
         return make_rsrc(w + (uint64_t)expert * w_bytes, w_bytes);
     };
     __amdgpu_buffer_rsrc_t rw = ID ? take_item(item) : make_rsrc(w, w_bytes);
+    auto load_lane = [&](uint32_t off) -> LaneT {
+        if constexpr (PAIR)
+            return Fmt::load_pair(rw, off, kg & 1);
+        else
+            return Fmt::load(rw, off, kg);
+    };
 
     // byte offsets of this decode lane's rows in tile t (rows past N read row 0)
     auto tile_rows = [&](int t, uint32_t (&ro)[R]) {
 #pragma unroll
         for (int rt = 0; rt < R; rt++) {
-            const int64_t rowA = (int64_t)t * 16 * R + 16 * rt + (lane & 15);
+            const int64_t rowA = (int64_t)t * kRows + (PAIR ? 16 * (kg >> 1) : 16 * rt) +
+                                 (lane & 15);
             ro[rt] = (uint32_t)((rowA < N ? rowA : 0) * nb * Fmt::kBlockBytes);
         }
     };
 
     uint32_t row_off[R];
-    typename Fmt::Lane lb[R];
+    LaneT lb[R];
     // the first block's weights are in flight while the activations are staged
     auto start_item = [&]() {
         tile_rows(tile, row_off);
         if (wave < nb) {
 #pragma unroll
             for (int rt = 0; rt < R; rt++)
-                lb[rt] = Fmt::load(rw, row_off[rt] + (uint32_t)wave * Fmt::kBlockBytes, kg);
+                lb[rt] = load_lane(row_off[rt] + (uint32_t)wave * Fmt::kBlockBytes);
         }
         if (ID)
             __syncthreads();  // the column tables
-        stage_all_columns<Fmt, NT, ID, RUNS>(bq, dah, ra, T, nb, colbase);
+        if constexpr (PAIR)
+            stage_pair_columns<Fmt, ID>(bq, dah, ra, T, nb, colbase);
+        else
+            stage_all_columns<Fmt, NT, ID, RUNS>(bq, dah, ra, T, nb, colbase);
         __syncthreads();
     };
     start_item();
 
     int parity = 0;
     for (;;) {
-        const int64_t r0 = (int64_t)tile * 16 * R;
+        const int64_t r0 = (int64_t)tile * kRows;
         const int64_t un = u + ustride;
         const int item_n = ID ? (int)(un / ntiles) : 0;
         const int next_tile = (int)(un - (int64_t)item_n * ntiles);
@@ -280,43 +339,61 @@ __global__ __launch_bounds__(64 * NW) void mmvq_mfma_res_kernel(const uint8_t *_
                 // issued by every lane (at Fmt::kIdle when there is no
                 // next block), so that the compiler can count the loads in
                 // flight and the data is first waited for where it is decoded
-                typename Fmt::Lane ln[R];
+                LaneT ln[R];
 #pragma unroll
                 for (int rt = 0; rt < R; rt++)
-                    ln[rt] = Fmt::load(
-                        rw,
-                        have_next ? (same_tile ? row_off[rt] : next_off[rt]) +
-                                        (uint32_t)Bn * Fmt::kBlockBytes
-                                  : Fmt::kIdle,
-                        kg);
+                    ln[rt] = load_lane(have_next ? (same_tile ? row_off[rt] : next_off[rt]) +
+                                                       (uint32_t)Bn * Fmt::kBlockBytes
+                                                 : Fmt::kIdle);
 #pragma unroll
                 for (int rt = 0; rt < R; rt++) {
-                    const TileOperands op = Fmt::decode(lb[rt], ctx);
+                    typedef typename std::conditional<PAIR, PairOperands, TileOperands>::type OpsT;
+                    OpsT op;
+                    if constexpr (PAIR)
+                        op = Fmt::decode_pair(lb[rt], ctx, kg & 1);
+                    else
+                        op = Fmt::decode(lb[rt], ctx);
+                    // PAIR: the output lane's rows are in tile col / 8, whose
+                    // block scales sit in the decode lanes of its half 1
+                    const int dw_src = PAIR ? 4 * rg + 16 * (2 * (col >> 3) + 1) : 4 * rg;
                     float dw[4];  // block scales of the four rows this output lane holds
 #pragma unroll
                     for (int i = 0; i < 4; i++)
-                        dw[i] = __shfl(op.dw, 4 * rg + i, 64);
+                        dw[i] = __shfl(op.dw, dw_src + i, 64);
 #pragma unroll
                     for (int ct = 0; ct < NT; ct++) {
                         // this output lane's column scales, sub-blocks 8B .. 8B+7
                         const u32x4 dv = *reinterpret_cast<const u32x4 *>(
-                            dah + ((size_t)B * 16 * NT + ct * 16 + col) * 4);
+                            dah + ((size_t)B * 16 * NT + ct * 16 + (PAIR ? col & 7 : col)) * 4);
                         const uint32_t *bqb = bq + (size_t)(ct * nb + B) * 8 * 128 + 2 * lane;
                         float s[4];
 #pragma unroll
                         for (int b = 0; b < 8; b++) {
-                            const u32x2 bv = *reinterpret_cast<const u32x2 *>(bqb + b * 128);
-                            const long Bq = (long)(((uint64_t)bv.y << 32) | bv.x);
                             // -sum(q) of this lane's column on every row, then + sum(u q)
-                            const i32x4 neg_sum = __builtin_amdgcn_mfma_i32_16x16x32_i8(
-                                kAllMinusOne, Bq, (i32x4){0, 0, 0, 0}, 0, 0, 0);
-                            const i32x4 C = __builtin_amdgcn_mfma_i32_16x16x32_i8(op.A[b], Bq,
-                                                                                  neg_sum, 0, 0, 0);
+                            i32x4 C;
+                            if constexpr (PAIR) {
+                                const u32x4 bv = *reinterpret_cast<const u32x4 *>(
+                                    bq + (size_t)(B * 8 + b) * kPairSlot + pair_off);
+                                const i32x4 Bq = (i32x4){(int)bv.x, (int)bv.y, (int)bv.z,
+                                                         (int)bv.w};
+                                const i32x4 neg_sum = __builtin_amdgcn_mfma_i32_16x16x64_i8(
+                                    kAllMinusOne4, Bq, (i32x4){0, 0, 0, 0}, 0, 0, 0);
+                                C = __builtin_amdgcn_mfma_i32_16x16x64_i8(op.A[b], Bq, neg_sum, 0,
+                                                                          0, 0);
+                            } else {
+                                const u32x2 bv = *reinterpret_cast<const u32x2 *>(bqb + b * 128);
+                                const long Bq = (long)(((uint64_t)bv.y << 32) | bv.x);
+                                const i32x4 neg_sum = __builtin_amdgcn_mfma_i32_16x16x32_i8(
+                                    kAllMinusOne, Bq, (i32x4){0, 0, 0, 0}, 0, 0, 0);
+                                C = __builtin_amdgcn_mfma_i32_16x16x32_i8(op.A[b], Bq, neg_sum, 0,
+                                                                          0, 0);
+                            }
                             if (ISUMS) {
-                                const int c = ct * 16 + col;
+                                const int c = PAIR ? (col & 7) : ct * 16 + col;
 #pragma unroll
                                 for (int i = 0; i < 4; i++) {
-                                    const int64_t row = r0 + 16 * rt + 4 * rg + i;
+                                    const int64_t row = r0 + (PAIR ? 16 * (col >> 3) : 16 * rt) +
+                                                        4 * rg + i;
                                     if (c < T && row < N)
                                         isums[((int64_t)c * N + row) * nblk + 8 * B + b] = C[i];
                                 }
@@ -415,8 +492,8 @@ __global__ __launch_bounds__(64 * NW) void mmvq_mfma_res_kernel(const uint8_t *_
                     const int ls = o / kPer, k = o - (o / kPer) * kPer;
                     const int oc = ls & 15, org = ls >> 4;
                     const int rt = k / (NT * 4), ct = (k >> 2) % NT, i = k & 3;
-                    const int c = ct * 16 + oc;
-                    const int64_t row = r0 + 16 * rt + 4 * org + i;
+                    const int c = PAIR ? (oc & 7) : ct * 16 + oc;
+                    const int64_t row = r0 + (PAIR ? 16 * (oc >> 3) : 16 * rt) + 4 * org + i;
                     if (j == 0 && c < T && row < N) {
                         const int64_t yc = ID ? colpair[c] : c;
                         const int64_t o = yc * N + row;
@@ -447,12 +524,13 @@ __global__ __launch_bounds__(64 * NW) void mmvq_mfma_res_kernel(const uint8_t *_
                     for (int rt = 0; rt < R; rt++)
 #pragma unroll
                         for (int ct = 0; ct < NT; ct++) {
-                            const int c = ct * 16 + col;
+                            const int c = PAIR ? (col & 7) : ct * 16 + col;
                             if (c < T) {
                                 const int64_t yc = ID ? colpair[c] : c;
 #pragma unroll
                                 for (int i = 0; i < 4; i++) {
-                                    const int64_t row = r0 + 16 * rt + 4 * rg + i;
+                                    const int64_t row = r0 + (PAIR ? 16 * (col >> 3) : 16 * rt) +
+                                                        4 * rg + i;
                                     if (row < N) {
                                         const int64_t o = yc * N + row;
                                         y[o] = resid ? acc[0][rt][ct][i] + resid[o]
@@ -483,29 +561,31 @@ __global__ __launch_bounds__(64 * NW) void mmvq_mfma_res_kernel(const uint8_t *_
     }
 }
 
-template <class Fmt, int NW, int GPW, int NT, bool DB>
+template <class Fmt, int NW, int GPW, int NT, bool DB, bool PAIR = false>
 static int launch_res(const uint8_t *w, const uint8_t *a, float *y, const float *r,
                       int32_t *isums, int64_t N, int nb, int T, hipStream_t stream)
 {
     constexpr int R = 1;
-    const int64_t ntiles = (N + 16 * R - 1) / (16 * R);
-    const size_t lds = res_lds_bytes(NW, NT, R, nb, DB);
-    const void *kt =
-        reinterpret_cast<const void *>(&mmvq_mfma_res_kernel<Fmt, NW, GPW, NT, R, DB, true, false, true>);
-    const void *kf =
-        reinterpret_cast<const void *>(&mmvq_mfma_res_kernel<Fmt, NW, GPW, NT, R, DB, false, false, true>);
+    constexpr bool RUNS = !PAIR;
+    const int64_t rows = PAIR ? 32 : 16 * R;
+    const int64_t ntiles = (N + rows - 1) / rows;
+    const size_t lds = res_lds_bytes(NW, NT, R, nb, DB, false, PAIR);
+    const void *kt = reinterpret_cast<const void *>(
+        &mmvq_mfma_res_kernel<Fmt, NW, GPW, NT, R, DB, true, false, RUNS, PAIR>);
+    const void *kf = reinterpret_cast<const void *>(
+        &mmvq_mfma_res_kernel<Fmt, NW, GPW, NT, R, DB, false, false, RUNS, PAIR>);
     allow_dynamic_lds(kt, lds);
     allow_dynamic_lds(kf, lds);
     const int cap = resident_workgroups(isums ? kt : kf, 64 * NW, lds);
     const dim3 grid((unsigned)(ntiles < cap ? ntiles : cap));
     const WideItems none = {nullptr, 0, 1};
     if (isums)
-        hipLaunchKernelGGL((mmvq_mfma_res_kernel<Fmt, NW, GPW, NT, R, DB, true, false, true>), grid,
-                           dim3(64 * NW), lds, stream, w, a, nullptr, nullptr, isums, N, nb, T,
-                           (int)ntiles, T, none);
+        hipLaunchKernelGGL((mmvq_mfma_res_kernel<Fmt, NW, GPW, NT, R, DB, true, false, RUNS, PAIR>),
+                           grid, dim3(64 * NW), lds, stream, w, a, nullptr, nullptr, isums, N, nb,
+                           T, (int)ntiles, T, none);
     else
-        hipLaunchKernelGGL((mmvq_mfma_res_kernel<Fmt, NW, GPW, NT, R, DB, false, false, true>), grid,
-                           dim3(64 * NW), lds, stream, w, a, y, r, nullptr, N, nb, T,
+        hipLaunchKernelGGL((mmvq_mfma_res_kernel<Fmt, NW, GPW, NT, R, DB, false, false, RUNS, PAIR>),
+                           grid, dim3(64 * NW), lds, stream, w, a, y, r, nullptr, N, nb, T,
                            (int)ntiles, T, none);
     return check_launch();
 }
@@ -639,6 +719,13 @@ static int launch_resident_fmt(const void *w, const void *a, float *y, int32_t *
     const int Lr = 1 << lanes_per_row_log2(nb);
     const uint8_t *wp = static_cast<const uint8_t *>(w);
     const uint8_t *ap = static_cast<const uint8_t *>(a);
+    if (T <= 8 && pair_tiles_pay(N)) {
+        switch (Lr) {
+        case 16: return launch_res<Fmt, 16, 1, 1, true, true>(wp, ap, y, r, isums, N, nb, T, stream);
+        case 32: return launch_res<Fmt, 16, 2, 1, true, true>(wp, ap, y, r, isums, N, nb, T, stream);
+        default: return launch_res<Fmt, 16, 4, 1, true, true>(wp, ap, y, r, isums, N, nb, T, stream);
+        }
+    }
     if (T <= 16) {
         switch (Lr) {
         case 16: return launch_res<Fmt, 16, 1, 1, true>(wp, ap, y, r, isums, N, nb, T, stream);

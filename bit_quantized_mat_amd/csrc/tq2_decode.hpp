@@ -205,6 +205,11 @@ struct Tq2Tile {
         const uint32_t *cs = tile + col * kStageCol + 9 * b + 4 * h;
         return (i32x4){(int)cs[0], (int)cs[1], (int)cs[2], (int)cs[3]};
     }
+
+    static __device__ __forceinline__ u32x4 pair_dwords(const uint32_t (&q)[8], int h, int)
+    {
+        return (u32x4){q[4 * h], q[4 * h + 1], q[4 * h + 2], q[4 * h + 3]};
+    }
 };
 
 }  // namespace bqm

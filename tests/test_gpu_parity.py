@@ -175,12 +175,14 @@ def _case(N, K, T, seed, p_zero=1 / 3, outliers=0.01, d_lo=0.01, d_hi=0.1):
 # tiles per workgroup, both halves of its partial-sum buffer). From 8192 rows
 # at 5 to 8 columns it pairs two 16-row tiles per matrix-core product: 9000 x
 # 4096, 8200 x 1280 (5 blocks per row, one 8-row tile in the last unit) and
-# 8230 x 4096.
+# 8230 x 4096; so does the resident kernel on longer rows (8200 x 6144,
+# 5000 x 8192).
 SHAPES = [(256, 1024, 1), (1, 256, 1), (33, 256, 2), (67, 768, 3), (130, 2304, 5),
           (515, 4096, 8), (96, 6144, 4), (40, 16384, 1), (17, 1280, 32), (300, 512, 16),
           (40, 16384, 6), (50, 9216, 5), (21, 4096, 17), (1, 2304, 9), (4500, 4096, 3),
           (4200, 2560, 4), (50, 16640, 1), (33, 24576, 2), (300, 33024, 1), (70, 65536, 2),
-          (9000, 4096, 7), (20000, 2048, 24), (8200, 1280, 5), (8230, 4096, 8)]
+          (9000, 4096, 7), (20000, 2048, 24), (8200, 1280, 5), (8230, 4096, 8),
+          (8200, 6144, 6), (5000, 8192, 5)]
 
 
 # ---------------------------------------------------------------------------
@@ -848,13 +850,14 @@ def test_tq1_dequantize_bit_exact(bqm, N, K, dtype):
 # workgroup at 20000 rows), LDS-resident columns for longer rows whose columns
 # fit (96 x 6144, 100 x 6144), the streamed kernel for the rest (rows of 3,
 # 64 and 129 blocks); from 8192 rows at 3 to 8 columns the register-operand
-# kernel's pair tiles (9000 x 4096, 8200 x 2048, 8230 x 1536)
+# kernel's pair tiles (9000 x 4096, 8200 x 2048, 8230 x 1536), and the
+# resident kernel's (8240 x 6144)
 TQ2_SHAPES = [(256, 1024, 1), (1, 256, 1), (33, 256, 2), (67, 768, 3), (130, 2304, 5),
               (515, 4096, 8), (96, 6144, 4), (40, 16384, 1), (17, 1280, 32), (300, 512, 16),
               (21, 4096, 17), (1, 2304, 9), (50, 16640, 1), (33, 24576, 2), (70, 65536, 2),
               (9000, 4096, 7), (20000, 2048, 24), (40, 16384, 12), (45, 33024, 3),
               (4500, 4096, 3), (100, 6144, 20), (7, 256, 32), (9000, 4096, 3),
-              (8200, 2048, 6), (8230, 1536, 8)]
+              (8200, 2048, 6), (8230, 1536, 8), (8240, 6144, 4)]
 
 
 def _prep_tq2(bqm, trits, d16, x):
