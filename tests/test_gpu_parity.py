@@ -477,17 +477,31 @@ def test_mmvq_id_small_cases(bqm):
 
 
 @pytest.mark.parametrize("case", ["one_expert", "one_expert_many", "repeats", "repeats_many",
-                                  "all_experts"])
+                                  "all_experts", "wave_one_expert", "wave_repeats",
+                                  "wave_threshold"])
 def test_mmvq_id_routing_edge_cases(bqm, case):
     """Routing edge cases: every pair on one expert (several groups of eight),
     the same expert twice in a token (computed twice), and n_used == E; the
-    "_many" cases carry more than 64 pairs and take the routing pre-pass."""
+    "_many" cases carry more than 64 pairs and take the routing pre-pass. The
+    "wave_" cases stay within 64 pairs (routed inside the wave) on rows of 9
+    or more blocks: one expert's 20 pairs in items of four; repeated experts
+    in a token; and an expert of exactly three pairs beside experts of one."""
     seeds = {"one_expert": 7, "one_expert_many": 10, "repeats": 8, "repeats_many": 11,
-             "all_experts": 9}
+             "all_experts": 9, "wave_one_expert": 12, "wave_repeats": 13, "wave_threshold": 14}
     rng = np.random.default_rng(seeds[case])
     if case == "one_expert":
         E, N, K, T, n_used = 4, 72, 512, 21, 1
         ids = np.full((T, n_used), 2, np.int32)
+    elif case == "wave_one_expert":
+        E, N, K, T, n_used = 4, 72, 2304, 20, 1
+        ids = np.full((T, n_used), 2, np.int32)
+    elif case == "wave_repeats":
+        E, N, K, T, n_used = 5, 40, 4096, 8, 3
+        ids = rng.integers(0, E, (T, n_used)).astype(np.int32)
+        ids[:, 1] = ids[:, 0]
+    elif case == "wave_threshold":
+        E, N, K, T, n_used = 6, 50, 2304, 3, 2
+        ids = np.array([[1, 0], [1, 2], [1, 3]], np.int32)
     elif case == "one_expert_many":
         # 101 pairs on one expert: seven matrix-core items, the last of 5 pairs
         E, N, K, T, n_used = 4, 72, 2304, 101, 1
