@@ -182,7 +182,10 @@ SHAPES = [(256, 1024, 1), (1, 256, 1), (33, 256, 2), (67, 768, 3), (130, 2304, 5
           (40, 16384, 6), (50, 9216, 5), (21, 4096, 17), (1, 2304, 9), (4500, 4096, 3),
           (4200, 2560, 4), (50, 16640, 1), (33, 24576, 2), (300, 33024, 1), (70, 65536, 2),
           (9000, 4096, 7), (20000, 2048, 24), (8200, 1280, 5), (8230, 4096, 8),
-          (8200, 6144, 6), (5000, 8192, 5)]
+          (8200, 6144, 6), (5000, 8192, 5),
+          # one column on more waves than SIMDs, not a whole number per
+          # SIMD: 16, 24 and 9 blocks per row, ragged N
+          (4500, 4096, 1), (5001, 6144, 1), (14330, 2304, 1)]
 
 
 # ---------------------------------------------------------------------------
@@ -688,7 +691,8 @@ def test_mm_prefill_workload(bqm):
                                    (14330, 4096, 8), (14330, 2304, 5), (14330, 4096, 1),
                                    (12345, 6144, 2), (1, 4096, 6), (3, 2560, 8),
                                    (70, 2048, 6), (33, 1024, 8), (50, 16640, 1),
-                                   (33, 24576, 2), (300, 33024, 1), (70, 65536, 2)])
+                                   (33, 24576, 2), (300, 33024, 1), (70, 65536, 2),
+                                   (5001, 6144, 1)])
 def test_mmvq_f32_equals_quantize_then_mmvq(bqm, N, K, T):
     trits, d16, x = _case(N, K, T, seed=N * 7 + K + T)
     w, a, w_ref, a_ref = _prep(bqm, trits, d16, x)
@@ -768,7 +772,7 @@ def test_mmvq_negative_and_subnormal_weight_scales(bqm, N, K, T):
 # matrix-core (five columns over K too long to keep resident), staged
 # multi-pass rows
 ADD_SHAPES = [(256, 1024, 1), (4500, 4096, 2), (4500, 4096, 3), (333, 2304, 4), (515, 4096, 8),
-              (17, 1280, 32), (50, 9216, 5), (50, 16640, 1), (8250, 4096, 6)]
+              (17, 1280, 32), (50, 9216, 5), (50, 16640, 1), (8250, 4096, 6), (4500, 4096, 1)]
 
 
 @pytest.mark.parametrize("N,K,T", ADD_SHAPES)
