@@ -999,3 +999,96 @@ def test_tq2_workload_parity(bqm, name):
         if T == max(wl.Ts):
             s = _host(bqm.mmvq_tq2_0_block_isums(w, a, N, K, T))
             assert np.array_equal(s, oracle.tq2_block_isums(w_ref, a_ref_all[:T], N, K, T))
+
+
+# ---------------------------------------------------------------------------
+# Seeded random shapes: every product entry point over shapes drawn from one
+# generator (row counts, block counts and column counts spread over the
+# dispatch ranges of every kernel), each against the oracle
+# ---------------------------------------------------------------------------
+
+def _random_shapes(seed, count, t_lo, t_hi, budget):
+    """(N, K, T) with N log-uniform in [1, 6000], blocks per row in [1, 96],
+    T in [t_lo, t_hi], and N K T below budget (the oracle's time)."""
+    rng = np.random.default_rng(seed)
+    shapes = []
+    while len(shapes) < count:
+        N = int(np.exp(rng.uniform(0, np.log(6000))))
+        K = 256 * int(rng.integers(1, 97))
+        T = int(rng.integers(t_lo, t_hi + 1))
+        if N * K * T <= budget:
+            shapes.append((N, K, T))
+    return shapes
+
+
+RANDOM_SHAPES = _random_shapes(71, 24, 1, 32, 3e8)
+
+
+@pytest.mark.parametrize("N,K,T", RANDOM_SHAPES)
+def test_random_shapes_mmvq(bqm, N, K, T):
+    """mmvq_tq1_0: exact sub-block sums and outputs within the bound; the
+    fused fp32-input call (up to 8 columns) bitwise the two calls; TQ2_0
+    packing of the same trits bitwise the same product."""
+    trits, d16, x = _case(N, K, T, 9000 + N + K + T)
+    w, a, w_ref, a_ref = _prep(bqm, trits, d16, x)
+    _say("random mmvq", N, K, T)
+    y = _host(bqm.mmvq_tq1_0(w, a, N, K, T))
+    _, y64, ab = oracle.mmvq(w_ref, a_ref, N, K, T)
+    _assert_close(y, y64, ab, "random mmvq %d %d %d" % (N, K, T))
+    s = _host(bqm.mmvq_tq1_0_block_isums(w, a, N, K, T))
+    assert np.array_equal(s, oracle.block_isums(w_ref, a_ref, N, K, T))
+    if T < bqm.MMVQ_F32_MAX_COLS or (T == bqm.MMVQ_F32_MAX_COLS and K <= 8192):
+        # (eight columns of more than 8192 elements do not fit one staging
+        # pass in LDS: the fused call rejects them, as its contract states)
+        yf = _host(bqm.mmvq_tq1_0_f32(w, _dev(x), N, K, T))
+        assert np.array_equal(yf.view(np.uint32), y.view(np.uint32))
+    w2 = bqm.tq2_pack(_dev(trits), _dev(d16.view(np.int16)))
+    y2 = _host(bqm.mmvq_tq2_0(w2, a, N, K, T))
+    assert np.array_equal(y2.view(np.uint32), y.view(np.uint32))
+
+
+@pytest.mark.parametrize("N,K,T", _random_shapes(72, 8, 33, 300, 4e8))
+def test_random_shapes_mm(bqm, N, K, T):
+    """mm_tq1_0 beyond 32 columns (chunked or K-streamed) against the oracle."""
+    trits, d16, x = _case(N, K, T, 9100 + N + K + T)
+    w, a, w_ref, a_ref = _prep(bqm, trits, d16, x)
+    _say("random mm", N, K, T)
+    y = _host(bqm.mm_tq1_0(w, a, N, K, T))
+    _, y64, ab = oracle.mmvq(w_ref, a_ref, N, K, T)
+    _assert_close(y, y64, ab, "random mm %d %d %d" % (N, K, T))
+
+
+def _random_moe(seed, count):
+    rng = np.random.default_rng(seed)
+    cases = []
+    while len(cases) < count:
+        E = int(rng.integers(2, 65))
+        N = int(rng.integers(1, 400))
+        K = 256 * int(rng.integers(1, 33))
+        n_used = int(rng.integers(1, min(E, 8) + 1))
+        T = int(rng.integers(1, 41))
+        if E * N * K <= 4e7 and T * n_used * N * K <= 2e8:
+            cases.append((E, N, K, T, n_used))
+    return cases
+
+
+@pytest.mark.parametrize("E,N,K,T,n_used", _random_moe(73, 10))
+def test_random_shapes_mmvq_id(bqm, E, N, K, T, n_used):
+    """mmvq_id_tq1_0 and its per-slot form on random expert counts, shapes
+    and Zipf routings (in-wave routing, pre-pass, narrow and wide items),
+    against the oracle."""
+    rng = np.random.default_rng(9200 + E + N + K + T)
+    trits = synth.ternary(rng, (E * N, K))
+    d16 = synth.block_scales_f16(rng, (E * N, K // 256), 0.01, 0.1)
+    x = synth.activations(rng, T * n_used, K)
+    ids = synth.zipf_routing(rng, T, E, n_used)
+    w, a_s, w_ref, a_s_ref = _prep(bqm, trits, d16, x)
+    _say("random mmvq_id", E, N, K, T, n_used)
+    a_t = a_s[::n_used].contiguous()                  # one column per token
+    a_t_ref = np.ascontiguousarray(a_s_ref[::n_used])
+    y = _host(bqm.mmvq_id_tq1_0(w, a_t, _dev(ids), E, N, K, T, n_used))
+    _, y64, ab = oracle.mmvq_id(w_ref, a_t_ref, ids, E, N, K, T, n_used)
+    _assert_close(y, y64, ab, "random mmvq_id %d %d %d %d %d" % (E, N, K, T, n_used))
+    ys = _host(bqm.mmvq_id_tq1_0_slots(w, a_s, _dev(ids), E, N, K, T, n_used))
+    _, y64s, abs_ = oracle.mmvq_id(w_ref, a_s_ref, ids, E, N, K, T, n_used, per_slot=True)
+    _assert_close(ys, y64s, abs_, "random mmvq_id_slots %d %d %d %d %d" % (E, N, K, T, n_used))
