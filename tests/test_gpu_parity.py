@@ -1045,6 +1045,18 @@ def test_random_shapes_mmvq(bqm, N, K, T):
     w2 = bqm.tq2_pack(_dev(trits), _dev(d16.view(np.int16)))
     y2 = _host(bqm.mmvq_tq2_0(w2, a, N, K, T))
     assert np.array_equal(y2.view(np.uint32), y.view(np.uint32))
+    # the residual add in the epilogue: bitwise fp32(product + r)
+    r = np.random.default_rng(N + T).standard_normal((T, N)).astype(np.float32)
+    ya = _host(bqm.mmvq_tq1_0_add(w, a, _dev(r), N, K, T))
+    assert np.array_equal(ya.view(np.uint32), (y + r).view(np.uint32))
+    # dequantized rows, every bit (fp16 and, on small matrices, fp32 and bf16)
+    if N * K <= 2 ** 25:
+        for dt, tdt in (("f16", torch.float16), ("f32", torch.float32), ("bf16", torch.bfloat16)):
+            if dt != "f16" and N * K > 2 ** 22:
+                continue
+            got = _dq_bits(bqm.tq1_dequantize(w, N, K, dtype=tdt))
+            ref = oracle.tq1_dequantize(w_ref, N, K, dt)
+            assert np.array_equal(got, ref.view(got.dtype)), dt
 
 
 @pytest.mark.parametrize("N,K,T", _random_shapes(72, 8, 33, 300, 4e8))
