@@ -831,11 +831,15 @@ def _dq_bits(t):
     return t.view(torch.int16).cpu().numpy().view(np.uint16)
 
 
-# 16-bit outputs take 2, 4, 8 or 16 blocks per wave by size: 1161 blocks
-# (129 x 2304), 20800 (1300 x 4096), 49600 (3100 x 4096), 65600 (4100 x 4096:
-# the large-call path with a partial last wave; its gather takes 8,203 rows)
+# Every output type takes 2, 4, 8, 16 or 32 blocks per wave by size: 1161
+# blocks (129 x 2304), 9600 (600 x 4096), 20800 (1300 x 4096), 49600 (3100 x
+# 4096), 65600 (4100 x 4096, with a partial last wave; its gather takes 8,203
+# rows, 131,248 blocks), 135,030 (4501 x 7680: waves of 32 blocks across rows
+# of 30, a partial last wave); outputs below 64 MiB are stored non-temporally
+# (4100 x 4096 fp16 is, fp32 is not)
 @pytest.mark.parametrize("N,K", [(1, 256), (3, 768), (70, 4096), (129, 2304), (16, 16384),
-                                 (4100, 4096), (1300, 4096), (3100, 4096)])
+                                 (4100, 4096), (1300, 4096), (3100, 4096), (600, 4096),
+                                 (4501, 7680)])
 @pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
 def test_tq1_dequantize_bit_exact(bqm, N, K, dtype):
     import torch
