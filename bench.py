@@ -707,11 +707,14 @@ def sweep_report(sweep_json, traced_json=None, cpu_json=None):
 
 def profile_run(spec, torch, np, bqm, synth, dev):
     """A few launches of one workload shape for counter collection: `launches`
-    mat-vec calls on cold weight copies, then as many streaming reads of the
-    same weight bytes by the probe kernel (a reference of known size)."""
+    mat-vec calls on cold weight copies (or, with a fourth field dq_f16,
+    dq_bf16 or dq_f32, dequantizations of the whole matrix to that type),
+    then as many streaming reads of the same weight bytes by the probe kernel
+    and copies of them (references of known size)."""
     parts = spec.split(":")
     name, T = parts[0], int(parts[1])
     launches = int(parts[2]) if len(parts) > 2 else 20
+    op = parts[3] if len(parts) > 3 else "mmvq"
     wl = synth.WORKLOADS[name]
     inp = synth.make_inputs(wl, T=T)
     N, K = wl.N, wl.K
@@ -719,7 +722,11 @@ def profile_run(spec, torch, np, bqm, synth, dev):
                       torch.from_numpy(inp.d16.view(np.int16)).to(dev))
     wrot, R = rotation(torch, w0, dev)
     a = bqm.q8_1_quantize(torch.from_numpy(inp.x[:T]).to(dev))
-    if wl.experts:
+    if op != "mmvq":
+        dt = {"dq_f16": torch.float16, "dq_bf16": torch.bfloat16, "dq_f32": torch.float32}[op]
+        dq = torch.empty((N, K), dtype=dt, device=dev)
+        run = lambda i: bqm.tq1_dequantize(wrot[i % R], N, K, dtype=dt, out=dq)
+    elif wl.experts:
         ids = torch.from_numpy(np.ascontiguousarray(inp.ids[:T])).to(dev)
         y = torch.empty((T, wl.n_used, N), dtype=torch.float32, device=dev)
         ws = torch.empty(max(bqm.mmvq_id_tq1_0_workspace_bytes(wl.experts, T, wl.n_used), 256),
@@ -733,7 +740,7 @@ def profile_run(spec, torch, np, bqm, synth, dev):
     for i in range(launches):
         run(i)
     torch.cuda.synchronize()
-    if not wl.experts and T <= bqm.MMVQ_F32_MAX_COLS:
+    if op == "mmvq" and not wl.experts and T <= bqm.MMVQ_F32_MAX_COLS:
         # the fused quantize-and-multiply kernel on the same shapes
         x = torch.from_numpy(inp.x[:T]).to(dev)
         for i in range(launches):
@@ -757,7 +764,7 @@ def profile_run(spec, torch, np, bqm, synth, dev):
                               ctypes.c_void_p(wrot[(i + 3) % R].data_ptr()), nbytes, 1024,
                               stream)
     torch.cuda.synchronize()
-    print(json.dumps({"profile": name, "N": N, "K": K, "T": T, "launches": launches,
+    print(json.dumps({"profile": name, "op": op, "N": N, "K": K, "T": T, "launches": launches,
                       "weight_bytes": int(w0.numel()), "probe_bytes": int(nbytes),
                       "kernel_source_hash": kernel_source_hash()}), flush=True)
 
@@ -878,7 +885,7 @@ def main():
     ap.add_argument("--sweep", metavar="PATH", help="also measure every workload; JSON table")
     ap.add_argument("--sweep-launches", type=int, default=100)
     ap.add_argument("--sweep-only", default="", help="comma-separated workload names")
-    ap.add_argument("--profile", metavar="WORKLOAD:T[:LAUNCHES]",
+    ap.add_argument("--profile", metavar="WORKLOAD:T[:LAUNCHES[:OP]]",
                     help="only run a few launches of one shape (for counter collection)")
     ap.add_argument("--write-counters", nargs=3, metavar=("FETCH_DIR", "WRITE_DIR", "PROBE_BYTES"),
                     help="no GPU: turn two rocprofv3 --pmc runs of --profile decode:1 "

@@ -46,74 +46,37 @@ __device__ __forceinline__ HalfTable half_table(float d, uint32_t d16)
     return HalfTable{nd | (zd << 16), pd};
 }
 
-// A lane's 16-byte store; NT marks it non-temporal (streamed past the
-// caches), which pays on outputs well inside the last-level cache.
-template <bool NT>
-__device__ __forceinline__ void store16(void *__restrict__ p, u32x4 v)
-{
-    if constexpr (NT)
-        __builtin_nontemporal_store(v, static_cast<u32x4 *>(p));
-    else
-        *static_cast<u32x4 *>(p) = v;
-}
-
-// Store the four values d * (u - 1) of the digit bytes of `u` at out + e
-// (fp32).
-template <bool NT>
-__device__ __forceinline__ void store_run_f32(void *__restrict__ out, int64_t e, uint32_t u, float d)
-{
-    float v[4];
-#pragma unroll
-    for (int k = 0; k < 4; k++)
-        v[k] = d * (float)((int)((u >> (8 * k)) & 0xffu) - 1);
-    store16<NT>(static_cast<float *>(out) + e, (u32x4){__float_as_uint(v[0]), __float_as_uint(v[1]),
-                                                       __float_as_uint(v[2]), __float_as_uint(v[3])});
-}
-
-// The two dwords of 16-bit patterns for the four digit bytes of u.
-__device__ __forceinline__ u32x2 half_patterns(uint32_t u, const HalfTable &tab)
-{
-    // selector bytes (2u, 2u + 1) pick the element's pattern from the table
-    const uint32_t u2 = u + u;
-    const uint32_t s01 = __builtin_amdgcn_perm(0u, u2, 0x0c010c00u) * 0x0101u + 0x01000100u;
-    const uint32_t s23 = __builtin_amdgcn_perm(0u, u2, 0x0c030c02u) * 0x0101u + 0x01000100u;
-    return (u32x2){__builtin_amdgcn_perm(tab.hi, tab.lo, s01), __builtin_amdgcn_perm(tab.hi, tab.lo, s23)};
-}
-
-// Store the eight 16-bit values d * (u - 1) of the digit bytes of ua
-// (elements e..e+3) and ub (e+4..e+7) at out + e: 16 bytes per lane.
-template <bool NT>
-__device__ __forceinline__ void store_run8(void *__restrict__ out, int64_t e, uint32_t ua,
-                                           uint32_t ub, const HalfTable &tab)
-{
-    const u32x2 a = half_patterns(ua, tab), b2 = half_patterns(ub, tab);
-    store16<NT>(static_cast<uint16_t *>(out) + e, (u32x4){a.x, a.y, b2.x, b2.y});
-}
-
-// Per-16-bit-lane multipliers of digit level c (0..4) of a qs dword, or (qh)
-// of a qh dword: X1 holds v / 3^k with k = 4 (qs) or 3 (qh), so
-// floor(v / 3^c) is byte 1 of X1 * 3^(k-c), and floor(v / 3^(c+1)) of
-// X1 * 3^(k-c-1) (a zero multiplier past the top digit). Computed once per
-// lane: the level of a lane's elements is the same in every block.
-struct LevelMuls {
-    uint32_t cur, next;  // both 16-bit lanes carry the multiplier
+// Per-16-bit-lane constants of digit level c (0..4) of a qs dword, or (qh)
+// of a qh dword. The lanes hold X1, v / 3^k in 8.8 fixed point (k = 4 for
+// qs bytes, 3 for qh; tq1_decode.hpp), whose multiples X1 * 3^m have
+// floor(v / 3^(k-m)) in byte 1. Below the top level, X = X1 * 3^(k-c-1) is
+// 256 floor(v / 3^(c+1)) + f, and floor(v / 3^c) = 3 floor(v / 3^(c+1)) +
+// floor(3 f / 256): the digit is floor(3 f / 256), byte 1 of 3 (X & 0xff).
+// At the top level c = k the digit is byte 1 of X1 itself. So
+// Y = ((X1 * m1) & mask) * m2 carries the digit in byte 1 of each 16-bit
+// lane, with (m1, mask, m2) = (3^(k-c-1), 0xff, 3) below the top and
+// (1, 0xffff, 1) at it. Computed once per lane: a lane's level is the same
+// in every block.
+struct LevelConsts {
+    uint32_t m1, mask, m2;  // both 16-bit lanes carry each constant
 };
 
-__device__ __forceinline__ uint32_t pow3_lanes(int p)
+__device__ __forceinline__ LevelConsts level_consts(int c, bool qh)
 {
-    const uint32_t m = p < 0 ? 0u : p == 0 ? 1u : p == 1 ? 3u : p == 2 ? 9u : p == 3 ? 27u : 81u;
-    return m * 0x00010001u;
+    const int p = (qh ? 3 : 4) - c - 1;
+    if (p < 0)
+        return LevelConsts{0x00010001u, 0xffffffffu, 0x00010001u};
+    const uint32_t m = p == 0 ? 1u : p == 1 ? 3u : p == 2 ? 9u : 27u;
+    return LevelConsts{m * 0x00010001u, kLaneMask, 3u * 0x00010001u};
 }
 
-__device__ __forceinline__ LevelMuls level_muls(int c, bool qh)
-{
-    const int k = qh ? 3 : 4;
-    return LevelMuls{pow3_lanes(k - c), pow3_lanes(k - c - 1)};
-}
+// The digits of one level of the four bytes of w, in byte 1 of the 16-bit
+// lanes of ye (source bytes 0 and 2) and yo (source bytes 1 and 3).
+struct DigitLanes {
+    uint32_t ye, yo;
+};
 
-// The digits of one level of the four bytes of w (a qs dword, or a qh dword
-// when qh): floor(v / 3^c) - 3 floor(v / 3^(c+1)) per byte.
-__device__ __forceinline__ uint32_t digit_level(uint32_t w, LevelMuls lm, bool qh)
+__device__ __forceinline__ DigitLanes digit_lanes(uint32_t w, LevelConsts lc, bool qh)
 {
     const uint32_t e = w & kLaneMask;
     const uint32_t o = __builtin_amdgcn_perm(0u, w, 0x0c030c01u);  // bytes 1, 3 -> lanes
@@ -121,9 +84,32 @@ __device__ __forceinline__ uint32_t digit_level(uint32_t w, LevelMuls lm, bool q
     const uint32_t shift = qh ? kQhShift : kQsShift;
     const uint32_t e1 = pk_shr(__umul24(e, mul) + add, shift);
     const uint32_t o1 = pk_shr(__umul24(o, mul) + add, shift);
-    const uint32_t f_c = hi_bytes(pk_mul_lanes(o1, lm.cur), pk_mul_lanes(e1, lm.cur));
-    const uint32_t f_n = hi_bytes(pk_mul_lanes(o1, lm.next), pk_mul_lanes(e1, lm.next));
-    return f_c - mul3_bytes(f_n);
+    return DigitLanes{pk_mul_lanes(pk_mul_lanes(e1, lc.m1) & lc.mask, lc.m2),
+                      pk_mul_lanes(pk_mul_lanes(o1, lc.m1) & lc.mask, lc.m2)};
+}
+
+// The 16-bit values of the four elements of `dl` from the table: a
+// byte-permute selector per pair of elements, bytes (2u, 2u + 1) of the
+// table for each element's digit u.
+__device__ __forceinline__ u32x2 half_values(DigitLanes dl, HalfTable tab)
+{
+    const uint32_t p01 = __builtin_amdgcn_perm(dl.yo, dl.ye, 0x05050101u);  // u0 u0 u1 u1
+    const uint32_t p23 = __builtin_amdgcn_perm(dl.yo, dl.ye, 0x07070303u);  // u2 u2 u3 u3
+    const uint32_t s01 = (p01 << 1) + 0x01000100u, s23 = (p23 << 1) + 0x01000100u;
+    return (u32x2){__builtin_amdgcn_perm(tab.hi, tab.lo, s01),
+                   __builtin_amdgcn_perm(tab.hi, tab.lo, s23)};
+}
+
+// The four fp32 values d * (u - 1) of the elements of `dl`.
+__device__ __forceinline__ u32x4 f32_values(DigitLanes dl, float d)
+{
+    const uint32_t u = __builtin_amdgcn_perm(dl.yo, dl.ye, 0x07030501u);  // u0 u1 u2 u3
+    float v[4];
+#pragma unroll
+    for (int k = 0; k < 4; k++)
+        v[k] = d * (float)((int)((u >> (8 * k)) & 0xffu) - 1);
+    return (u32x4){__float_as_uint(v[0]), __float_as_uint(v[1]), __float_as_uint(v[2]),
+                   __float_as_uint(v[3])};
 }
 
 // Blocks per wave: 32 from kDqHugeBlocks blocks and 16 from kDqLargeBlocks
@@ -141,15 +127,21 @@ constexpr int64_t kDqSmallBlocks = 4096;
 // order, or of w when rows is null). The loads: lane L < 4 BPW reads bytes
 // [16 (L mod 4), +16) of block L / 4 counted from the dword holding its first
 // byte (s = its offset mod 4, 0 or 2), one 16-byte load per lane for the
-// whole wave, into that block's 64-byte LDS slot (its bytes at s .. s + 53;
-// slot bytes 60..63 are past them in either case and carry s). The stores:
+// whole wave; each lane realigns its 16 bytes to the block's first byte with
+// the next lane's first dword, and the block's 64-byte LDS slot receives its
+// 13 dwords of digits (qs, then qh), the scale's dword, and in the last two
+// dwords (past the block) the values the output takes: the two dwords of a
+// HalfTable, or fp32 d. The stores:
 //   fp16 / bf16: step k (BPW / 2 steps) covers blocks 2k and 2k + 1, lane L
 //     writing elements 8 (L mod 32) .. +7 of block 2k + L / 32: one digit
 //     level of two consecutive qs dwords, or two levels of the qh dword;
 //   fp32: step k covers block k, lane L writing elements 4L .. 4L + 3, one
 //     digit level of one dword.
 // Each lane stores 16 bytes per step and a wave's step is one contiguous
-// 1 KiB run of the output.
+// 1 KiB run of the output, through a buffer resource over the wave's part of
+// the output (stores past the last block fall outside it and are dropped:
+// the whole offset is the lane's vector offset, which the range check
+// covers).
 template <int DT, int BPW, bool NT>
 __global__ __launch_bounds__(256) void tq1_dequantize_kernel(const uint8_t *__restrict__ w,
                                                              const int32_t *__restrict__ rows,
@@ -157,6 +149,7 @@ __global__ __launch_bounds__(256) void tq1_dequantize_kernel(const uint8_t *__re
                                                              int nb, int64_t n_rows)
 {
     constexpr bool kF32 = DT == BQM_DTYPE_F32;
+    constexpr int kEsz = kF32 ? 4 : 2;
     __shared__ u32x4 slots[4][4 * BPW];
     const int lane = threadIdx.x & 63;
     const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -169,7 +162,7 @@ __global__ __launch_bounds__(256) void tq1_dequantize_kernel(const uint8_t *__re
 #pragma unroll
     for (int q = 0; q < (4 * BPW + 63) / 64; q++) {
         // chunk t of the wave's slots; blocks past the end, and chunks past
-        // 4 BPW, load nothing (their slots are never read)
+        // 4 BPW, load nothing (their slots are never stored)
         const int t = lane + 64 * q;
         const int64_t blk = first + (t >> 2);
         const bool in = t < 4 * BPW && blk < nblocks;
@@ -180,14 +173,35 @@ __global__ __launch_bounds__(256) void tq1_dequantize_kernel(const uint8_t *__re
         r = r < 0 ? 0 : (r >= N ? N - 1 : r);  // ids outside [0, N) stay inside w
         const uint32_t off = (uint32_t)((r * nb + B) * kTq1BlockBytes);
         const uint32_t sh = off & 3u;
-        u32x4 x = ld_b128(rw, in ? off - sh + 16u * (t & 3) : kIdleLoadOffset);
-        if ((t & 3) == 3)
-            x.w = sh;
+        const u32x4 x = ld_b128(rw, in ? off - sh + 16u * (t & 3) : kIdleLoadOffset);
+        // the next lane's first dword (row shift left by one lane; the last
+        // lane of a row gets 0, and only feeds bytes past its block)
+        const uint32_t nx = (uint32_t)__builtin_amdgcn_mov_dpp((int)x.x, 0x101, 0xf, 0xf, true);
+        u32x4 a = {align_bytes(x.y, x.x, sh), align_bytes(x.z, x.y, sh),
+                   align_bytes(x.w, x.z, sh), align_bytes(nx, x.w, sh)};
+        if ((t & 3) == 3) {
+            // block bytes 48..63: the qh dword, the scale, then the values
+            const uint32_t d16 = a.y & 0xffffu;
+            const float d = f16_bits_to_f32(d16);
+            if constexpr (kF32) {
+                a.w = __float_as_uint(d);
+            } else {
+                const HalfTable tab = half_table<DT>(d, d16);
+                a.z = tab.lo;
+                a.w = tab.hi;
+            }
+        }
         if (t < 4 * BPW)
-            slots[wid][t] = x;
+            slots[wid][t] = a;
     }
     __builtin_amdgcn_wave_barrier();
     const uint32_t *slot0 = reinterpret_cast<const uint32_t *>(&slots[wid][0]);
+    // the wave's part of the output
+    const int64_t left = (nblocks - first) * kTq1BlockElems * kEsz;
+    const __amdgpu_buffer_rsrc_t ro =
+        make_rsrc(static_cast<uint8_t *>(out) + first * kTq1BlockElems * kEsz,
+                  (uint64_t)(left < BPW * kTq1BlockElems * kEsz ? left : BPW * kTq1BlockElems * kEsz));
+    constexpr int kAux = NT ? 2 : 0;  // nt: streamed past the caches
     if constexpr (kF32) {
         // elements 4L..4L+3: their dword and digit level
         const int e0 = 4 * lane;
@@ -203,18 +217,12 @@ __global__ __launch_bounds__(256) void tq1_dequantize_kernel(const uint8_t *__re
             c = lane - 60;
         }
         const bool qh = j == 12;
-        const LevelMuls lm = level_muls(c, qh);
+        const LevelConsts lc = level_consts(c, qh);
 #pragma unroll
         for (int k = 0; k < BPW; k++) {
-            const int64_t blk = first + k;
-            if (blk < nblocks) {
-                const uint32_t *sl = slot0 + 16 * k;
-                const uint32_t sh = sl[15];
-                const uint32_t dd = sl[13];
-                const uint32_t d16 = sh ? (dd >> 16) : (dd & 0xffffu);
-                const uint32_t u = digit_level(align_bytes(sl[j + 1], sl[j], sh), lm, qh);
-                store_run_f32<NT>(out, blk * kTq1BlockElems + e0, u, f16_bits_to_f32(d16));
-            }
+            const uint32_t *sl = slot0 + 16 * k;
+            const u32x4 v = f32_values(digit_lanes(sl[j], lc, qh), __uint_as_float(sl[15]));
+            __builtin_amdgcn_raw_buffer_store_b128(v, ro, 16 * lane + 1024 * k, 0, kAux);
         }
     } else {
         const int lp = lane & 31, half = lane >> 5;
@@ -231,28 +239,19 @@ __global__ __launch_bounds__(256) void tq1_dequantize_kernel(const uint8_t *__re
             c = 2 * (lp - 30);
         }
         const bool qh = j == 12;
-        // dwords jj .. jj + 2 cover the lane's bytes (qh lanes: 11 .. 13, the
-        // block's last dword at most)
-        const int jj = qh ? 11 : j;
-        const LevelMuls lma = level_muls(c, qh), lmb = level_muls(qh ? c + 1 : c, qh);
+        // qs lanes: level c of dwords j and j + 1; qh lanes: levels c and
+        // c + 1 of the qh dword
+        const int ja = j, jb = qh ? j : j + 1;
+        const LevelConsts la = level_consts(c, qh), lb = level_consts(qh ? c + 1 : c, qh);
+        const uint32_t *sw = slot0 + 16 * half;
 #pragma unroll
         for (int k = 0; k < BPW / 2; k++) {
-            const int64_t blk = first + 2 * k + half;
-            if (blk < nblocks) {
-                const uint32_t *sl = slot0 + 16 * (2 * k + half);
-                const uint32_t sh = sl[15];
-                const uint32_t dd = sl[13];
-                const uint32_t x0 = sl[jj], x1 = sl[jj + 1], x2 = sl[jj + 2];
-                const uint32_t d16 = sh ? (dd >> 16) : (dd & 0xffffu);
-                const float d = f16_bits_to_f32(d16);
-                const uint32_t w0 = align_bytes(x1, x0, sh);
-                const uint32_t w1 = align_bytes(x2, x1, sh);
-                // qh (w1 is the qh dword): levels c and c + 1 of it; else
-                // level c of the two dwords
-                const uint32_t ua = digit_level(qh ? w1 : w0, lma, qh);
-                const uint32_t ub = digit_level(w1, lmb, qh);
-                store_run8<NT>(out, blk * kTq1BlockElems + e0, ua, ub, half_table<DT>(d, d16));
-            }
+            const uint32_t *sl = sw + 32 * k;
+            const HalfTable tab = {sl[14], sl[15]};
+            const u32x2 va = half_values(digit_lanes(sl[ja], la, qh), tab);
+            const u32x2 vb = half_values(digit_lanes(sl[jb], lb, qh), tab);
+            __builtin_amdgcn_raw_buffer_store_b128((u32x4){va.x, va.y, vb.x, vb.y}, ro,
+                                                   512 * half + 2 * e0 + 1024 * k, 0, kAux);
         }
     }
 }

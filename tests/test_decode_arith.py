@@ -134,3 +134,35 @@ def test_single_level_digit_extraction_exhaustive():
                 f_n = ((x1 * m_n) & M16) >> 8
                 assert f_c == v // 3 ** c, (qh, v, c)
                 assert f_c - 3 * f_n == (v // 3 ** c) % 3, (qh, v, c)
+
+
+DEQ = os.path.join(os.path.dirname(HDR), "dequant.hip")
+
+
+def _dequant_level_multipliers():
+    """The multipliers 3^p of level_consts in dequant.hip, read from the source."""
+    text = open(DEQ).read()
+    m = re.search(r"p == 0 \? (\d+)u : p == 1 \? (\d+)u : p == 2 \? (\d+)u : (\d+)u", text)
+    assert m, "level_consts"
+    return [int(g) for g in m.groups()]
+
+
+def test_dequant_digit_from_low_byte_exhaustive():
+    # digit_lanes in dequant.hip: below the top level c < k, the digit is byte 1
+    # of 3 * ((X1 * 3^(k-c-1)) & 0xff) (mod 2^16 per lane); at c = k, byte 1 of
+    # X1. Checked for every qs byte (k = 4) and qh byte (k = 3) at every level
+    # against Python's base-3 digits.
+    pw = _dequant_level_multipliers()
+    assert pw == [1, 3, 9, 27]
+    for k, n, mul, add, shift in ((4, 243, C["kQsMul"], C["kQsAdd"], C["kQsShift"]),
+                                   (3, 81, C["kQhMul"], C["kQhAdd"], C["kQhShift"])):
+        for v in range(n):
+            (x1,) = _lane_chain(v, mul, add, shift, ())
+            for c in range(k + 1):
+                p = k - c - 1
+                if p < 0:
+                    y = x1
+                else:
+                    x = (x1 * pw[p]) & M16
+                    y = ((x & 0xFF) * 3) & M16
+                assert (y >> 8) & 0xFF == (v // 3 ** c) % 3, (k, v, c)
