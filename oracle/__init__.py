@@ -55,6 +55,8 @@ def lib():
         L.oracle_mmvq.restype = ctypes.c_int
         L.oracle_mmvq_add.argtypes = [_p, _p, _p, _p, _p, _p, _i64, _i64, _i64]
         L.oracle_mmvq_add.restype = ctypes.c_int
+        L.oracle_mmvq_glu.argtypes = [_p] * 9 + [_i64, _i64, _i64]
+        L.oracle_mmvq_glu.restype = ctypes.c_int
         L.oracle_mmvq_id.argtypes = [_p, _p, _p, _p, _p, _p, _i64, _i64, _i64, _i64, _i64]
         L.oracle_mmvq_id.restype = ctypes.c_int
         L.oracle_mmvq_id_slots.argtypes = [_p, _p, _p, _p, _p, _p, _i64, _i64, _i64, _i64, _i64]
@@ -203,6 +205,20 @@ def mmvq_add(w, a, r, N, K, T):
     _check(lib().oracle_mmvq_add(_ptr(w), _ptr(a), _ptr(r), _ptr(y), _ptr(y64), _ptr(ab), N, K,
                                  T), "mmvq_add")
     return y, y64, ab
+
+
+def mmvq_glu(w_gate, w_up, a, N, K, T):
+    """The gate-up pair with its gated-linear-unit epilogue, y = silu(g) * u:
+    returns (y float32, y64, g64, u64, absg, absu), each [T, N], where g and
+    u are the two exact mat-vecs and absg, absu their sum |terms|."""
+    wg = _c(w_gate, np.uint8)
+    wu = _c(w_up, np.uint8)
+    a = _c(a, np.uint8)
+    out = [np.empty((T, N), dtype=np.float32)] + [np.empty((T, N), dtype=np.float64)
+                                                   for _ in range(5)]
+    _check(lib().oracle_mmvq_glu(_ptr(wg), _ptr(wu), _ptr(a), *[_ptr(o) for o in out], N, K, T),
+           "mmvq_glu")
+    return tuple(out)
 
 
 def mmvq_id(w, a, ids, E, N, K, T, n_used, per_slot=False):

@@ -478,6 +478,34 @@ int oracle_mmvq_add(const uint8_t *w, const uint8_t *a, const float *r, float *y
     return 0;
 }
 
+/* The gate-up pair with a gated-linear-unit epilogue: two mat-vecs of the
+ * same activation columns, g by the gate matrix and u by the up matrix (each
+ * exactly as oracle_mmvq), then y[t][n] = silu(g) * u with silu(x) =
+ * x / (1 + exp(-x)), all in fp64. The fused mat-vec paths of "CUDA: TQ1_0
+ * mat-vec is load-bound by the per-32-element chunk contract" ("Proposed
+ * approach": the fusion predicate is a third gate beside the plain and
+ * expert paths) are named there but not spelled out; the reading used here
+ * is the SiLU-gated unit of a transformer feed-forward block (gate and up
+ * projections of the same input). g64, u64 and their sum |term| scales
+ * absg, absu are returned for the comparison tolerance. Arrays are [T][N]. */
+int oracle_mmvq_glu(const uint8_t *wg, const uint8_t *wu, const uint8_t *a, float *y,
+                    double *y64, double *g64, double *u64, double *absg, double *absu,
+                    int64_t N, int64_t K, int64_t T)
+{
+    if (!y64 || !g64 || !u64 || !absg || !absu)
+        return -1;
+    if (oracle_mmvq(wg, a, NULL, g64, absg, N, K, T) || oracle_mmvq(wu, a, NULL, u64, absu, N, K, T))
+        return -1;
+    for (int64_t i = 0; i < T * N; i++) {
+        double g = g64[i];
+        double silu = g / (1.0 + exp(-g));
+        y64[i] = silu * u64[i];
+        if (y)
+            y[i] = (float)y64[i];
+    }
+    return 0;
+}
+
 /* The expert-routed products: pair ts = t * n_used + s multiplies expert
  * ids[ts]'s matrix by activation column col(ts), where col(ts) = t when a
  * token's slots share its column and col(ts) = ts when every pair has its own.

@@ -41,6 +41,10 @@ MUTATIONS = {
                                 "oracle_f16_to_f32(dd[(j / 8 + 1) % nb]);"),
     "slots_read_token_column": ("int64_t col = column_per_pair ? ts : ts / n_used;",
                                 "int64_t col = ts / n_used;"),
+    "glu_sigmoid_without_its_argument": ("double silu = g / (1.0 + exp(-g));",
+                                         "double silu = 1.0 / (1.0 + exp(-g));"),
+    "glu_gate_and_up_swapped": ("oracle_mmvq(wg, a, NULL, g64, absg, N, K, T) || oracle_mmvq(wu, a, NULL, u64, absu, N, K, T)",
+                                "oracle_mmvq(wu, a, NULL, g64, absg, N, K, T) || oracle_mmvq(wg, a, NULL, u64, absu, N, K, T)"),
 }
 
 

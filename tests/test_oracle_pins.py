@@ -656,3 +656,53 @@ def test_tq2_mmvq_scale_index_and_row_order():
     perm = np.random.default_rng(2).permutation(N)
     _, p64, _ = oracle.tq2_mmvq(oracle.tq2_pack(trits[perm], d16[perm]), a, N, K, T)
     assert np.array_equal(p64, y64[:, perm])
+
+
+# The logistic function sigma(x) = e^x / (1 + e^x) at x = 1 and 2, with
+# e = 2.718281828459045: e / (1 + e) and e^2 / (1 + e^2). silu(x) = x sigma(x),
+# and sigma(-x) = 1 - sigma(x).
+SIGMA_1 = 0.7310585786300049
+SIGMA_2 = 0.8807970779778823
+
+
+def test_mmvq_glu_unit_scales_against_logistic_values():
+    """Unit scales and an all-ones activation column make the gate and up
+    products small integers g, u (g ones or minus ones in the gate row, u in
+    the up row); y = silu(g) * u is checked against the logistic function's
+    values, silu(0) = 0, silu(40) = 40 in fp64 and silu(-40) ~ -40 e^-40. The
+    gate and up rows differ, so swapped operands or a dropped factor fail."""
+    K, T = 256, 1
+    cases = [(1, 2), (2, 1), (-1, 3), (2, -1), (0, 5), (-2, -2), (40, 1), (-40, 1), (3, 0)]
+    N = len(cases)
+    gate = np.zeros((N, K), np.int8)
+    up = np.zeros((N, K), np.int8)
+    for n, (g, u) in enumerate(cases):
+        gate[n, :abs(g)] = np.sign(g)
+        up[n, :abs(u)] = np.sign(u)
+    unit = np.full((N, K // 256), 0x3C00, np.uint16)
+    wg, wu = oracle.tq1_pack(gate, unit), oracle.tq1_pack(up, unit)
+    a = synth.q8_1_blocks_from_fields(np.ones((T, K), np.int8),
+                                      np.full((T, K // 32), 0x3C00, np.uint16),
+                                      np.zeros((T, K // 32), np.uint16))
+    y, y64, g64, u64, absg, absu = oracle.mmvq_glu(wg, wu, a, N, K, T)
+    assert g64[0].tolist() == [float(c[0]) for c in cases]
+    assert u64[0].tolist() == [float(c[1]) for c in cases]
+    assert absg[0].tolist() == [float(abs(c[0])) for c in cases]
+    expect = [SIGMA_1 * 2, 2 * SIGMA_2, -(1 - SIGMA_1) * 3, -2 * SIGMA_2, 0.0,
+              -2 * (1 - SIGMA_2) * -2, 40.0, -40 * np.exp(-40.0), 0.0]
+    assert np.allclose(y64[0], expect, rtol=1e-13, atol=0)
+    assert y64[0, 4] == 0.0 and y64[0, 6] == 40.0
+    assert np.array_equal(y, y64.astype(np.float32))
+
+
+def test_mmvq_glu_products_are_the_two_matvecs():
+    N, K, T = 9, 1024, 2
+    tg, d16g, x = _case(N, K, T, 51)
+    tu, d16u, _ = _case(N, K, T, 52)
+    wg, wu = oracle.tq1_pack(tg, d16g), oracle.tq1_pack(tu, d16u)
+    a = oracle.q8_1_quantize(x)
+    y, y64, g64, u64, absg, absu = oracle.mmvq_glu(wg, wu, a, N, K, T)
+    _, gy64, gab = oracle.mmvq(wg, a, N, K, T)
+    _, uy64, uab = oracle.mmvq(wu, a, N, K, T)
+    assert np.array_equal(g64, gy64) and np.array_equal(absg, gab)
+    assert np.array_equal(u64, uy64) and np.array_equal(absu, uab)
