@@ -13,7 +13,7 @@ __all__ = [
     "BqmError", "library", "library_path", "tq1_pack", "q8_1_quantize", "mmvq_tq1_0", "mm_tq1_0",
     "MM_MAX_COLS",
     "mmvq_tq1_0_f32", "MMVQ_F32_MAX_COLS", "tq1_dequantize", "mmvq_tq1_0_add",
-    "mmvq_tq1_0_f32_add",
+    "mmvq_tq1_0_f32_add", "mmvq_tq1_0_glu", "mmvq_tq1_0_f32_glu", "GLU_MAX_COLS",
     "mmvq_id_tq1_0", "mmvq_id_tq1_0_slots", "mmvq_id_tq1_0_workspace_bytes",
     "mmvq_id_tq1_0_noalloc", "NOALLOC_SCRATCH_BYTES",
     "mmvq_tq1_0_block_isums", "tq2_pack", "mmvq_tq2_0", "mmvq_tq2_0_block_isums",
@@ -26,6 +26,7 @@ Q81_BLOCK_BYTES = 36
 MMVQ_MAX_COLS = 32
 MMVQ_F32_MAX_COLS = 8
 MM_MAX_COLS = 65536
+GLU_MAX_COLS = 2
 NOALLOC_SCRATCH_BYTES = 768 * 1024
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -62,6 +63,8 @@ def library():
         L.mmvq_tq1_0_f32.argtypes = [_p, _p, _p, _i64, _i64, _i32, _p]
         L.mmvq_tq1_0_add.argtypes = [_p, _p, _p, _p, _i64, _i64, _i32, _p]
         L.mmvq_tq1_0_f32_add.argtypes = [_p, _p, _p, _p, _i64, _i64, _i32, _p]
+        L.mmvq_tq1_0_glu.argtypes = [_p, _p, _p, _p, _i64, _i64, _i32, _p]
+        L.mmvq_tq1_0_f32_glu.argtypes = [_p, _p, _p, _p, _i64, _i64, _i32, _p]
         L.mm_tq1_0.argtypes = [_p, _p, _p, _i64, _i64, _i64, _p]
         L.tq1_dequantize.argtypes = [_p, _p, _p, _i64, _i64, _i64, _i32, _p]
         L.mmvq_tq1_0_block_isums.argtypes = [_p, _p, _p, _i64, _i64, _i32, _p]
@@ -77,8 +80,8 @@ def library():
         L.bqm_status_string.restype = ctypes.c_char_p
         L.bqm_version.restype = ctypes.c_int
         for name in ("tq1_pack", "q8_1_quantize", "mmvq_tq1_0", "mm_tq1_0", "mmvq_tq1_0_f32",
-                     "mmvq_tq1_0_add", "mmvq_tq1_0_f32_add",
-                     "mmvq_tq1_0_block_isums", "mmvq_id_tq1_0", "mmvq_id_tq1_0_slots",
+                     "mmvq_tq1_0_add", "mmvq_tq1_0_f32_add", "mmvq_tq1_0_glu",
+                     "mmvq_tq1_0_f32_glu", "mmvq_tq1_0_block_isums", "mmvq_id_tq1_0", "mmvq_id_tq1_0_slots",
                      "mmvq_id_tq1_0_noalloc", "tq1_dequantize", "tq2_pack", "mmvq_tq2_0",
                      "mmvq_tq2_0_block_isums"):
             getattr(L, name).restype = ctypes.c_int
@@ -218,6 +221,36 @@ def mmvq_tq1_0_f32_add(w, x, r, N, K, T, out=None, stream=None):
           _dev_tensor(r, "r", (torch.float32,), T * N * 4, w.device),
           _dev_tensor(out, "out", (torch.float32,), T * N * 4, w.device),
           N, K, T, _stream(stream, w.device))
+    return out
+
+
+def mmvq_tq1_0_glu(w_gate, w_up, a, N, K, T, out=None, stream=None):
+    """y fp32 [T, N] = silu(mmvq_tq1_0(w_gate, a)) * mmvq_tq1_0(w_up, a) in one
+    launch, 1 <= T <= GLU_MAX_COLS."""
+    torch = _torch()
+    if out is None:
+        out = torch.empty((T, N), dtype=torch.float32, device=w_gate.device)
+    pw, pa = _mmvq_args(w_gate, a, N, K, T)
+    _call("mmvq_tq1_0_glu", pw,
+          _dev_tensor(w_up, "w_up", (torch.uint8,), N * (K // 256) * TQ1_BLOCK_BYTES,
+                      w_gate.device), pa,
+          _dev_tensor(out, "out", (torch.float32,), T * N * 4, w_gate.device),
+          N, K, T, _stream(stream, w_gate.device))
+    return out
+
+
+def mmvq_tq1_0_f32_glu(w_gate, w_up, x, N, K, T, out=None, stream=None):
+    """The same on fp32 activations x [T, K], quantized inside the call."""
+    torch = _torch()
+    if out is None:
+        out = torch.empty((T, N), dtype=torch.float32, device=w_gate.device)
+    _call("mmvq_tq1_0_f32_glu",
+          _dev_tensor(w_gate, "w_gate", (torch.uint8,), N * (K // 256) * TQ1_BLOCK_BYTES),
+          _dev_tensor(w_up, "w_up", (torch.uint8,), N * (K // 256) * TQ1_BLOCK_BYTES,
+                      w_gate.device),
+          _dev_tensor(x, "x", (torch.float32,), T * K * 4, w_gate.device),
+          _dev_tensor(out, "out", (torch.float32,), T * N * 4, w_gate.device),
+          N, K, T, _stream(stream, w_gate.device))
     return out
 
 

@@ -179,6 +179,36 @@ int mmvq_tq1_0_f32_add(const void *w, const float *x, const float *r, float *y, 
     return mmvq_f32_call(w, x, r, true, y, N, K, T, stream);
 }
 
+// f32: the columns are fp32 (quantized inside the call), else Q8_1 blocks.
+static int glu_call(const void *wg, const void *wu, const void *a, float *y, int64_t N,
+                    int64_t K, int32_t T, bool f32, void *stream)
+{
+    if (!wg || !wu || !a || !y)
+        return BQM_ERR_NULL;
+    if (int rc = check_matrix(N, K))
+        return rc;
+    const uint64_t col_bytes = f32 ? (uint64_t)K * 4ull : (uint64_t)(K / 32) * 36ull;
+    if (T < 1 || T > BQM_GLU_MAX_COLS || (uint64_t)T * col_bytes > kMaxBufferBytes)
+        return BQM_ERR_SHAPE;
+    if (!aligned4(wg) || !aligned4(wu) || !aligned4(a) || !aligned4(y))
+        return BQM_ERR_ALIGN;
+    if (int rc = check_device())
+        return rc;
+    return bqm::launch_mmvq_glu(wg, wu, a, y, N, K, T, f32, as_stream(stream));
+}
+
+int mmvq_tq1_0_glu(const void *w_gate, const void *w_up, const void *a, float *y, int64_t N,
+                   int64_t K, int32_t T, void *stream)
+{
+    return glu_call(w_gate, w_up, a, y, N, K, T, false, stream);
+}
+
+int mmvq_tq1_0_f32_glu(const void *w_gate, const void *w_up, const float *x, float *y,
+                       int64_t N, int64_t K, int32_t T, void *stream)
+{
+    return glu_call(w_gate, w_up, x, y, N, K, T, true, stream);
+}
+
 int mmvq_tq1_0_block_isums(const void *w, const void *a, int32_t *isums, int64_t N, int64_t K,
                            int32_t T, void *stream)
 {

@@ -56,6 +56,12 @@ int launch_mmvq_staged(const void *w, const void *a, float *y, int32_t *isums, i
 // The staged kernel on fp32 activations, quantized to Q8_1 while staging.
 int launch_mmvq_staged_f32(const void *w, const float *x, float *y, int64_t N, int64_t K,
                            int32_t T, hipStream_t stream, const float *r = nullptr);
+// Gate-up pair with the SiLU-gated epilogue, y = silu(wg . a) * (wu . a), on
+// the staged kernel: one or two columns (f32: fp32 columns, quantized while
+// staging); BQM_ERR_SHAPE for other column counts or rows it cannot stage.
+constexpr int kGluMaxCols = 2;
+int launch_mmvq_glu(const void *wg, const void *wu, const void *a, float *y, int64_t N, int64_t K,
+                    int32_t T, bool f32, hipStream_t stream);
 // Quad kernel (three to eight columns, whole-block decode per lane, sub-block
 // sums on the matrix cores; rows of more than 8 blocks): whether it takes this
 // shape, and its launchers (Q8_1 activations, and fp32 activations quantized

@@ -46,9 +46,39 @@ __global__ __launch_bounds__(64 * WPG) void mmvq_staged_kernel(const uint8_t *__
         col_off[t] = (uint32_t)t * col_bytes;
         out[t] = ISUMS ? nullptr : y + (int64_t)t * N;
     }
-    staged_rows<TC, ISUMS, F32>(rw, ra, col_off, out, resid, isums,
+    staged_rows<TC, ISUMS, F32>(rw, rw, ra, col_off, out, resid, isums,
                                 reinterpret_cast<uint32_t *>(act_lds),
                                 row, row < N, N, nb, T, lr_log2, chunk, 64 * WPG);
+}
+
+// Gate-up pair with the SiLU-gated epilogue: y[t][n] = silu(g) * u, where g
+// and u are row n of the gate matrix wg and of the up matrix wu against
+// column t, one or two columns (F32: fp32 columns, quantized while staging).
+template <int TC, bool F32, int WPG>
+__global__ __launch_bounds__(64 * WPG) void mmvq_glu_kernel(const uint8_t *__restrict__ wg,
+                                                       const uint8_t *__restrict__ wu,
+                                                       const uint8_t *__restrict__ a, float *y,
+                                                       int64_t N, int nb, int T, int lr_log2,
+                                                       int chunk)
+{
+    extern __shared__ uint4 act_lds[];
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int64_t row = ((int64_t)blockIdx.x * WPG + wave) * (64 >> lr_log2) + (lane >> lr_log2);
+    const int nblk = nb * 8;
+    const uint32_t col_bytes = F32 ? (uint32_t)nb * kTq1BlockElems * 4 : (uint32_t)nblk * kQ81BlockBytes;
+    const __amdgpu_buffer_rsrc_t rwg = make_rsrc(wg, (uint64_t)N * nb * kTq1BlockBytes);
+    const __amdgpu_buffer_rsrc_t rwu = make_rsrc(wu, (uint64_t)N * nb * kTq1BlockBytes);
+    const __amdgpu_buffer_rsrc_t ra = make_rsrc(a, (uint64_t)T * col_bytes);
+    uint32_t col_off[TC];
+    float *out[TC];
+#pragma unroll
+    for (int t = 0; t < TC; t++) {
+        col_off[t] = (uint32_t)t * col_bytes;
+        out[t] = y + (int64_t)t * N;
+    }
+    staged_rows<TC, false, F32, true>(rwg, rwu, ra, col_off, out, nullptr, nullptr,
+                                      reinterpret_cast<uint32_t *>(act_lds),
+                                      row, row < N, N, nb, T, lr_log2, chunk, 64 * WPG);
 }
 
 int lanes_per_row_log2(int64_t nb)
@@ -235,6 +265,54 @@ int launch_mmvq_staged_f32(const void *w, const float *x, float *y, int64_t N, i
                            int32_t T, hipStream_t stream, const float *r)
 {
     return launch_staged<true>(w, x, y, r, nullptr, N, K, T, stream);
+}
+
+template <int TC, bool F32, int WPG>
+static void launch_glu_tc(const uint8_t *wg, const uint8_t *wu, const uint8_t *a, float *y,
+                          int64_t N, int nb, int T, int lr, int chunk, size_t lds,
+                          hipStream_t stream)
+{
+    const int64_t rows_per_wg = WPG * (64 >> lr);
+    const dim3 grid((unsigned)((N + rows_per_wg - 1) / rows_per_wg)), block(64 * WPG);
+    allow_dynamic_lds(reinterpret_cast<const void *>(&mmvq_glu_kernel<TC, F32, WPG>), lds);
+    hipLaunchKernelGGL((mmvq_glu_kernel<TC, F32, WPG>), grid, block, lds, stream, wg, wu, a, y, N,
+                       nb, T, lr, chunk);
+}
+
+template <int TC, bool F32>
+static void launch_glu_w(const uint8_t *wg, const uint8_t *wu, const uint8_t *a, float *y,
+                         int64_t N, int nb, int T, int lr, int chunk, size_t lds,
+                         hipStream_t stream)
+{
+    const int wpg = staged_workgroup_waves(N, lr);
+    if (wpg == 1)
+        launch_glu_tc<TC, F32, 1>(wg, wu, a, y, N, nb, T, lr, chunk, lds, stream);
+    else if (wpg == 8)
+        launch_glu_tc<TC, F32, 8>(wg, wu, a, y, N, nb, T, lr, chunk, lds, stream);
+    else
+        launch_glu_tc<TC, F32, 4>(wg, wu, a, y, N, nb, T, lr, chunk, lds, stream);
+}
+
+int launch_mmvq_glu(const void *wg, const void *wu, const void *a, float *y, int64_t N, int64_t K,
+                    int32_t T, bool f32, hipStream_t stream)
+{
+    const int nb = (int)(K / kTq1BlockElems);
+    const int lr = lanes_per_row_log2(nb);
+    const int chunk = staged_chunk(nb, lr, T, lds_budget());
+    if (T < 1 || T > kGluMaxCols || chunk == 0)
+        return BQM_ERR_SHAPE;
+    const size_t lds = (size_t)T * chunk * kActStride * 4;
+    const uint8_t *g = static_cast<const uint8_t *>(wg), *u = static_cast<const uint8_t *>(wu);
+    const uint8_t *ap = static_cast<const uint8_t *>(a);
+    if (T == 1 && f32)
+        launch_glu_w<1, true>(g, u, ap, y, N, nb, T, lr, chunk, lds, stream);
+    else if (T == 1)
+        launch_glu_w<1, false>(g, u, ap, y, N, nb, T, lr, chunk, lds, stream);
+    else if (f32)
+        launch_glu_w<2, true>(g, u, ap, y, N, nb, T, lr, chunk, lds, stream);
+    else
+        launch_glu_w<2, false>(g, u, ap, y, N, nb, T, lr, chunk, lds, stream);
+    return check_launch();
 }
 
 }  // namespace bqm

@@ -302,10 +302,15 @@ __device__ __forceinline__ void dword_sums_staged(const RawBlock &raw,
 // col_off[t] of the activation buffer ra and its outputs go to out[t][row],
 // plus resid[t * N + row] when resid is given (one fp32 addition after the
 // product's own result; resid may be the output buffer itself).
+// GLU: rw is the gate matrix and rw2 the up matrix of the same shape; each
+// lane takes the same block of both rows against the staged columns (both
+// products in the plain product's fp32 order) and the output is
+// silu(gate) * up. Otherwise rw2 is unused.
 // All nthreads threads of the workgroup (its whole size) must call this (it
 // synchronizes); lanes whose row is out of range only help with staging.
-template <int TC, bool ISUMS, bool F32 = false>
-__device__ __forceinline__ void staged_rows(__amdgpu_buffer_rsrc_t rw, __amdgpu_buffer_rsrc_t ra,
+template <int TC, bool ISUMS, bool F32 = false, bool GLU = false>
+__device__ __forceinline__ void staged_rows(__amdgpu_buffer_rsrc_t rw, __amdgpu_buffer_rsrc_t rw2,
+                                            __amdgpu_buffer_rsrc_t ra,
                                             const uint32_t (&col_off)[TC],
                                             float *const (&out)[TC], const float *resid,
                                             int32_t *__restrict__ isums,
@@ -318,10 +323,11 @@ __device__ __forceinline__ void staged_rows(__amdgpu_buffer_rsrc_t rw, __amdgpu_
     const int sub = lane & (Lr - 1);
     const int nblk = nb * 8;
     const uint32_t row_off = (uint32_t)((row_ok ? row : 0) * nb * kTq1BlockBytes);
-    float acc[TC];
+    static_assert(!(GLU && ISUMS), "the gated product has no block-sum twin");
+    float acc[TC], acc2[TC];
 #pragma unroll
     for (int t = 0; t < TC; t++)
-        acc[t] = 0.0f;
+        acc[t] = acc2[t] = 0.0f;
 
     // one pass over the blocks [B0, B0 + chunk) of the row
     auto pass = [&](int B0) {
@@ -343,9 +349,13 @@ __device__ __forceinline__ void staged_rows(__amdgpu_buffer_rsrc_t rw, __amdgpu_
         StageBatch<F32> head;
         stage_load<F32>(head, ra, col_off[0], B0, cb, 0, tid, nthreads);
         __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-        RawBlock cur = load_raw_block(rw, row_ok && first < end
-                                              ? row_off + (uint32_t)first * kTq1BlockBytes
-                                              : kIdleLoadOffset);
+        const uint32_t first_off = row_ok && first < end
+                                       ? row_off + (uint32_t)first * kTq1BlockBytes
+                                       : kIdleLoadOffset;
+        RawBlock cur = load_raw_block(rw, first_off);
+        RawBlock cur2;
+        if constexpr (GLU)
+            cur2 = load_raw_block(rw2, first_off);
         __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
         // and no arithmetic on the batch (with its wait) moves up between
         // the weight loads
@@ -357,55 +367,65 @@ __device__ __forceinline__ void staged_rows(__amdgpu_buffer_rsrc_t rw, __amdgpu_
                 stage_column<F32>(act + t * cb * kActStride, ra, col_off[t], B0, cb, tid, nthreads,
                                   nullptr);
         __syncthreads();
-        if (row_ok) {
-            for (int B = first; B < end; B += Lr) {
-                if (B != first)
-                    cur = load_raw_block(rw, row_off + (uint32_t)B * kTq1BlockBytes);
-                const float dw = f16_bits_to_f32(raw_scale_bits(cur));
-                DigitBlock d;
-                if (TC > 2)
-                    expand_block(cur, d);
-                // two columns (T == 2 exactly): one dword's digits at a time
-                int isum2[2][8];
-                if (TC == 2) {
-                    dword_sums_staged<2>(cur, act + (B - B0) * kActStride, cb * kActStride, isum2);
-                    // the exact sums pass through an empty asm statement
-                    // before their fp32 terms: without it the compiler
-                    // reshapes the products around the conversions and needs
-                    // over 250 registers
+        // one block of a row (cur, or the up matrix's cur2) against the
+        // staged columns, into ac[]
+        auto block_terms = [&](const RawBlock &blk, float (&ac)[TC], int B) {
+            const float dw = f16_bits_to_f32(raw_scale_bits(blk));
+            DigitBlock d;
+            if (TC > 2)
+                expand_block(blk, d);
+            // two columns (T == 2 exactly): one dword's digits at a time
+            int isum2[2][8];
+            if (TC == 2) {
+                dword_sums_staged<2>(blk, act + (B - B0) * kActStride, cb * kActStride, isum2);
+                // the exact sums pass through an empty asm statement
+                // before their fp32 terms: without it the compiler
+                // reshapes the products around the conversions and needs
+                // over 250 registers
 #pragma unroll
-                    for (int t = 0; t < 2; t++)
+                for (int t = 0; t < 2; t++)
+#pragma unroll
+                    for (int b = 0; b < 8; b++)
+                        asm volatile("" : "+v"(isum2[t][b]));
+            }
+#pragma unroll
+            for (int t = 0; t < TC; t++) {
+                if (t < T) {
+                    const uint32_t *ab = act + (t * cb + (B - B0)) * kActStride;
+                    int isum[8];
+                    if (TC == 1)
+                        block_sums_staged(blk, ab, isum);
+                    else if (TC == 2)
 #pragma unroll
                         for (int b = 0; b < 8; b++)
-                            asm volatile("" : "+v"(isum2[t][b]));
-                }
+                            isum[b] = isum2[t][b];
+                    else
+                        digit_sums_staged(d, ab, isum);
+                    if (ISUMS) {
+                        int32_t *dst = isums + ((int64_t)t * N + row) * nblk + 8 * B;
 #pragma unroll
-                for (int t = 0; t < TC; t++) {
-                    if (t < T) {
-                        const uint32_t *ab = act + (t * cb + (B - B0)) * kActStride;
-                        int isum[8];
-                        if (TC == 1)
-                            block_sums_staged(cur, ab, isum);
-                        else if (TC == 2)
+                        for (int b = 0; b < 8; b++)
+                            dst[b] = isum[b];
+                    } else {
+                        float da[8];
 #pragma unroll
-                            for (int b = 0; b < 8; b++)
-                                isum[b] = isum2[t][b];
-                        else
-                            digit_sums_staged(d, ab, isum);
-                        if (ISUMS) {
-                            int32_t *dst = isums + ((int64_t)t * N + row) * nblk + 8 * B;
-#pragma unroll
-                            for (int b = 0; b < 8; b++)
-                                dst[b] = isum[b];
-                        } else {
-                            float da[8];
-#pragma unroll
-                            for (int b = 0; b < 8; b++)
-                                da[b] = __uint_as_float(ab[64 + b]);
-                            acc[t] = fmaf(dw, block_dot_f32(isum, da), acc[t]);
-                        }
+                        for (int b = 0; b < 8; b++)
+                            da[b] = __uint_as_float(ab[64 + b]);
+                        ac[t] = fmaf(dw, block_dot_f32(isum, da), ac[t]);
                     }
                 }
+            }
+        };
+        if (row_ok) {
+            for (int B = first; B < end; B += Lr) {
+                if (B != first) {
+                    cur = load_raw_block(rw, row_off + (uint32_t)B * kTq1BlockBytes);
+                    if constexpr (GLU)
+                        cur2 = load_raw_block(rw2, row_off + (uint32_t)B * kTq1BlockBytes);
+                }
+                block_terms(cur, acc, B);
+                if constexpr (GLU)
+                    block_terms(cur2, acc2, B);
             }
         }
     };
@@ -420,13 +440,20 @@ __device__ __forceinline__ void staged_rows(__amdgpu_buffer_rsrc_t rw, __amdgpu_
     if (!ISUMS) {
         // butterfly over the Lr lanes of the row (every lane of the wave takes part)
 #pragma unroll
-        for (int t = 0; t < TC; t++)
+        for (int t = 0; t < TC; t++) {
             acc[t] = row_sum(acc[t], lr_log2);
+            if constexpr (GLU)
+                acc2[t] = row_sum(acc2[t], lr_log2);
+        }
         if (row_ok && sub == 0) {
 #pragma unroll
             for (int t = 0; t < TC; t++)
-                if (t < T)
-                    out[t][row] = resid ? acc[t] + resid[(int64_t)t * N + row] : acc[t];
+                if (t < T) {
+                    if constexpr (GLU)
+                        out[t][row] = acc[t] / (1.0f + expf(-acc[t])) * acc2[t];
+                    else
+                        out[t][row] = resid ? acc[t] + resid[(int64_t)t * N + row] : acc[t];
+                }
         }
     }
 }

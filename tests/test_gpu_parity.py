@@ -75,6 +75,14 @@ class _SentinelOutputs:
         kw.setdefault("out", self._y((T, N), w.device))
         return self._m.mmvq_tq1_0_f32_add(w, x, r, N, K, T, **kw)
 
+    def mmvq_tq1_0_glu(self, wg, wu, a, N, K, T, **kw):
+        kw.setdefault("out", self._y((T, N), wg.device))
+        return self._m.mmvq_tq1_0_glu(wg, wu, a, N, K, T, **kw)
+
+    def mmvq_tq1_0_f32_glu(self, wg, wu, x, N, K, T, **kw):
+        kw.setdefault("out", self._y((T, N), wg.device))
+        return self._m.mmvq_tq1_0_f32_glu(wg, wu, x, N, K, T, **kw)
+
     def mmvq_tq1_0_block_isums(self, w, a, N, K, T, **kw):
         kw.setdefault("out", self._full((T, N, K // 32), torch.int32, -2 ** 31, w.device))
         return self._m.mmvq_tq1_0_block_isums(w, a, N, K, T, **kw)
@@ -818,6 +826,100 @@ def test_mmvq_f32_decode_workload(bqm):
     y = _host(bqm.mmvq_tq1_0_f32(w, _dev(inp.x[:1]), N, K, 1))
     _, y64, ab = oracle.mmvq(w_ref, a_ref[:1], N, K, 1)
     _assert_close(y, y64, ab, "decode fused")
+
+
+# ---------------------------------------------------------------------------
+# Gate-up pair with the SiLU-gated epilogue
+# ---------------------------------------------------------------------------
+
+EPS32 = 2.0 ** -24
+
+
+def _assert_glu_close(y, y64, g64, u64, absg, absu, what):
+    """The products' tolerance carried through the epilogue: g and u are each
+    within B = 1e-5 sum|terms| of exact, silu is 1.1-Lipschitz (its slope lies
+    in (-0.1, 1.1)), and the fp32 epilogue (exp, add, divide, multiply) adds a
+    few ulp, so |y - y64| <= (|silu(g)| + 1.1 Bg) Bu + |u| (1.1 Bg +
+    8 eps |silu(g)|) + 4 eps |y| with eps = 2^-24. NaN or an unwritten output
+    fails."""
+    assert np.all(np.isfinite(y)), "%s: non-finite outputs" % what
+    bg, bu = REL_TOL * absg, REL_TOL * absu
+    s64 = g64 / (1.0 + np.exp(-g64))
+    bound = ((np.abs(s64) + 1.1 * bg) * bu + np.abs(u64) * (1.1 * bg + 8 * EPS32 * np.abs(s64))
+             + 4 * EPS32 * np.abs(y64))
+    err = np.abs(y.astype(np.float64) - y64)
+    bad = ~(err <= bound)
+    if bad.any():
+        i = tuple(np.argwhere(bad)[0])
+        raise AssertionError("%s: %d outputs outside the bound, first at %s: gpu %r exact %r bound %r"
+                             % (what, bad.sum(), i, y[i], y64[i], bound[i]))
+
+
+def _glu_case(bqm, N, K, T, seed, gate_scale=(0.01, 0.1)):
+    tg, dg, x = _case(N, K, T, seed, d_lo=gate_scale[0], d_hi=gate_scale[1])
+    tu, du, _ = _case(N, K, T, seed + 1)
+    wg, a, wg_ref, a_ref = _prep(bqm, tg, dg, x)
+    wu = bqm.tq1_pack(_dev(tu), _dev(du.view(np.int16)))
+    wu_ref = oracle.tq1_pack(tu, du)
+    return wg, wu, a, x, wg_ref, wu_ref, a_ref
+
+
+# (N, K, T): one and two columns; ragged row counts, odd block counts, one-block
+# rows, the decode and FFN matrices, rows longer than one staging pass (129
+# blocks)
+GLU_SHAPES = [(1, 256, 1), (5, 256, 2), (70, 768, 1), (70, 768, 2), (129, 2304, 1),
+              (300, 4096, 2), (4096, 4096, 1), (4096, 4096, 2), (14336, 4096, 1),
+              (64, 33024, 1), (40, 33024, 2)]
+
+
+@pytest.mark.parametrize("N,K,T", GLU_SHAPES)
+def test_mmvq_glu_parity(bqm, N, K, T):
+    """Against the oracle's silu(g) * u with the carried tolerance; within a
+    few ulp of the same epilogue applied (in fp64) to the two plain products;
+    the fp32-input call bitwise the Q8_1 one."""
+    wg, wu, a, x, wg_ref, wu_ref, a_ref = _glu_case(bqm, N, K, T, 7100 + N + T)
+    _say("mmvq_glu", N, K, T)
+    y = _host(bqm.mmvq_tq1_0_glu(wg, wu, a, N, K, T))
+    _, y64, g64, u64, absg, absu = oracle.mmvq_glu(wg_ref, wu_ref, a_ref, N, K, T)
+    _assert_glu_close(y, y64, g64, u64, absg, absu, "mmvq_glu %dx%d T=%d" % (N, K, T))
+    g = _host(bqm.mmvq_tq1_0(wg, a, N, K, T)).astype(np.float64)
+    u = _host(bqm.mmvq_tq1_0(wu, a, N, K, T)).astype(np.float64)
+    yr = g / (1.0 + np.exp(-g)) * u
+    assert np.all(np.abs(y - yr) <= 8 * EPS32 * np.abs(yr) + 1e-37)
+    yf = _host(bqm.mmvq_tq1_0_f32_glu(wg, wu, _dev(x), N, K, T))
+    assert np.array_equal(yf.view(np.uint32), y.view(np.uint32))
+
+
+def test_mmvq_glu_saturation_and_zero_gate(bqm):
+    """Gate scales near 1 put |g| in the tens (silu(g) -> g above, -> -0
+    below); a zero gate row gives exactly zero."""
+    N, K, T = 256, 4096, 2
+    wg, wu, a, x, wg_ref, wu_ref, a_ref = _glu_case(bqm, N, K, T, 7300, gate_scale=(0.5, 1.0))
+    y = _host(bqm.mmvq_tq1_0_glu(wg, wu, a, N, K, T))
+    _, y64, g64, u64, absg, absu = oracle.mmvq_glu(wg_ref, wu_ref, a_ref, N, K, T)
+    assert np.abs(g64).max() > 20
+    _assert_glu_close(y, y64, g64, u64, absg, absu, "saturated gate")
+    tz = np.zeros((N, K), np.int8)
+    dz = np.full((N, K // 256), 0x2E66, np.uint16)
+    wz = bqm.tq1_pack(_dev(tz), _dev(dz.view(np.int16)))
+    yz = _host(bqm.mmvq_tq1_0_glu(wz, wu, a, N, K, T))
+    assert np.all(yz == 0)
+
+
+def test_mmvq_glu_ffn_workload(bqm):
+    """The FFN matrix as both gate and up (different trits) at one column,
+    every output against the oracle."""
+    wl, inp = _workload_inputs("ffn")
+    N, K = wl.N, wl.K
+    wg, a, wg_ref, a_ref = _prep(bqm, inp.trits, inp.d16, inp.x[:1])
+    rng = np.random.default_rng(7400)
+    tu = synth.ternary(rng, (N, K), 0.4)
+    du = synth.block_scales_f16(rng, (N, K // 256), 0.005, 0.05)
+    wu = bqm.tq1_pack(_dev(tu), _dev(du.view(np.int16)))
+    wu_ref = oracle.tq1_pack(tu, du)
+    y = _host(bqm.mmvq_tq1_0_f32_glu(wg, wu, _dev(inp.x[:1]), N, K, 1))
+    _, y64, g64, u64, absg, absu = oracle.mmvq_glu(wg_ref, wu_ref, a_ref, N, K, 1)
+    _assert_glu_close(y, y64, g64, u64, absg, absu, "ffn glu")
 
 
 # ---------------------------------------------------------------------------
