@@ -489,6 +489,20 @@ def sweep(path, torch, np, bqm, synth, dev, launches, only=None):
             us = timer.time(row, lambda i: bqm.mmvq_tq1_0(wrot[i % R], a, N, K, T, out=y),
                             launches, y)
             _rate_fields(row, algorithmic_bytes(N, K, T), us, read_gbs)
+        if name in ("decode", "ffn"):
+            # the gate-up pair with its SiLU-gated epilogue: two matrices of
+            # this shape (two rotation copies) against the same columns
+            x_all = torch.from_numpy(inp.x).to(dev)
+            for op, T in (("mmvq_tq1_0_glu", 1), ("mmvq_tq1_0_glu", 2), ("mmvq_tq1_0_f32_glu", 1)):
+                src = (x_all if op == "mmvq_tq1_0_f32_glu" else a_all)[:T].contiguous()
+                fn = getattr(bqm, op)
+                y = torch.empty((T, N), dtype=torch.float32, device=dev)
+                row = {"workload": name, "op": op, "N": N, "K": K, "T": T}
+                us = timer.time(row, lambda i: fn(wrot[i % R], wrot[(i + 1) % R], src, N, K, T,
+                                                  out=y), launches, y)
+                xb = T * K * 4 - T * (K // 32) * 36 if op == "mmvq_tq1_0_f32_glu" else 0
+                _rate_fields(row, algorithmic_bytes(N, K, T) + w0.numel() + xb, us, read_gbs)
+            del x_all
         del wrot, w0
         torch.cuda.empty_cache()
         if name != "tiny":

@@ -46,7 +46,7 @@ __global__ __launch_bounds__(64 * WPG) void mmvq_staged_kernel(const uint8_t *__
         col_off[t] = (uint32_t)t * col_bytes;
         out[t] = ISUMS ? nullptr : y + (int64_t)t * N;
     }
-    staged_rows<TC, ISUMS, F32>(rw, rw, ra, col_off, out, resid, isums,
+    staged_rows<TC, ISUMS, F32>(rw, ra, col_off, out, resid, isums,
                                 reinterpret_cast<uint32_t *>(act_lds),
                                 row, row < N, N, nb, T, lr_log2, chunk, 64 * WPG);
 }
@@ -54,6 +54,12 @@ __global__ __launch_bounds__(64 * WPG) void mmvq_staged_kernel(const uint8_t *__
 // Gate-up pair with the SiLU-gated epilogue: y[t][n] = silu(g) * u, where g
 // and u are row n of the gate matrix wg and of the up matrix wu against
 // column t, one or two columns (F32: fp32 columns, quantized while staging).
+// Waves come in pairs over the same rows: the even wave of a pair runs the
+// plain staged product on the gate rows and the odd one on the up rows (each
+// in the plain product's fp32 order, so g and u are bitwise mmvq_tq1_0's);
+// the odd wave hands its sums over through LDS, and after one barrier the
+// even wave's row lanes store silu(g) * u. Both waves share the workgroup's
+// staged columns.
 template <int TC, bool F32, int WPG>
 __global__ __launch_bounds__(64 * WPG) void mmvq_glu_kernel(const uint8_t *__restrict__ wg,
                                                        const uint8_t *__restrict__ wu,
@@ -61,24 +67,43 @@ __global__ __launch_bounds__(64 * WPG) void mmvq_glu_kernel(const uint8_t *__res
                                                        int64_t N, int nb, int T, int lr_log2,
                                                        int chunk)
 {
+    static_assert(WPG % 2 == 0, "waves come in gate-up pairs");
     extern __shared__ uint4 act_lds[];
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int64_t row = ((int64_t)blockIdx.x * WPG + wave) * (64 >> lr_log2) + (lane >> lr_log2);
+    __shared__ float up_sums[WPG / 2][TC][64];
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+    const int pair = wave >> 1;
+    const bool up = wave & 1;
+    const int64_t row =
+        ((int64_t)blockIdx.x * (WPG / 2) + pair) * (64 >> lr_log2) + (lane >> lr_log2);
     const int nblk = nb * 8;
     const uint32_t col_bytes = F32 ? (uint32_t)nb * kTq1BlockElems * 4 : (uint32_t)nblk * kQ81BlockBytes;
-    const __amdgpu_buffer_rsrc_t rwg = make_rsrc(wg, (uint64_t)N * nb * kTq1BlockBytes);
-    const __amdgpu_buffer_rsrc_t rwu = make_rsrc(wu, (uint64_t)N * nb * kTq1BlockBytes);
+    const __amdgpu_buffer_rsrc_t rw = make_rsrc(up ? wu : wg, (uint64_t)N * nb * kTq1BlockBytes);
     const __amdgpu_buffer_rsrc_t ra = make_rsrc(a, (uint64_t)T * col_bytes);
     uint32_t col_off[TC];
     float *out[TC];
 #pragma unroll
     for (int t = 0; t < TC; t++) {
         col_off[t] = (uint32_t)t * col_bytes;
-        out[t] = y + (int64_t)t * N;
+        out[t] = nullptr;
     }
-    staged_rows<TC, false, F32, true>(rwg, rwu, ra, col_off, out, nullptr, nullptr,
-                                      reinterpret_cast<uint32_t *>(act_lds),
-                                      row, row < N, N, nb, T, lr_log2, chunk, 64 * WPG);
+    float g[TC];
+    auto store = [&](int t, float v) {
+        if (up)
+            up_sums[pair][t][lane >> lr_log2] = v;
+        else
+            g[t] = v;
+    };
+    staged_rows<TC, false, F32>(rw, ra, col_off, out, nullptr, nullptr,
+                                reinterpret_cast<uint32_t *>(act_lds), row, row < N, N, nb, T,
+                                lr_log2, chunk, 64 * WPG, store);
+    __syncthreads();
+    if (!up && row < N && (lane & ((1 << lr_log2) - 1)) == 0) {
+#pragma unroll
+        for (int t = 0; t < TC; t++)
+            if (t < T)
+                y[(int64_t)t * N + row] =
+                    g[t] / (1.0f + expf(-g[t])) * up_sums[pair][t][lane >> lr_log2];
+    }
 }
 
 int lanes_per_row_log2(int64_t nb)
@@ -272,7 +297,7 @@ static void launch_glu_tc(const uint8_t *wg, const uint8_t *wu, const uint8_t *a
                           int64_t N, int nb, int T, int lr, int chunk, size_t lds,
                           hipStream_t stream)
 {
-    const int64_t rows_per_wg = WPG * (64 >> lr);
+    const int64_t rows_per_wg = WPG / 2 * (64 >> lr);
     const dim3 grid((unsigned)((N + rows_per_wg - 1) / rows_per_wg)), block(64 * WPG);
     allow_dynamic_lds(reinterpret_cast<const void *>(&mmvq_glu_kernel<TC, F32, WPG>), lds);
     hipLaunchKernelGGL((mmvq_glu_kernel<TC, F32, WPG>), grid, block, lds, stream, wg, wu, a, y, N,
@@ -284,9 +309,11 @@ static void launch_glu_w(const uint8_t *wg, const uint8_t *wu, const uint8_t *a,
                          int64_t N, int nb, int T, int lr, int chunk, size_t lds,
                          hipStream_t stream)
 {
-    const int wpg = staged_workgroup_waves(N, lr);
+    // the workgroup shapes of the plain kernel on the 2N rows of both
+    // matrices, with pairs of waves in place of single ones
+    const int wpg = staged_workgroup_waves(2 * N, lr);
     if (wpg == 1)
-        launch_glu_tc<TC, F32, 1>(wg, wu, a, y, N, nb, T, lr, chunk, lds, stream);
+        launch_glu_tc<TC, F32, 2>(wg, wu, a, y, N, nb, T, lr, chunk, lds, stream);
     else if (wpg == 8)
         launch_glu_tc<TC, F32, 8>(wg, wu, a, y, N, nb, T, lr, chunk, lds, stream);
     else

@@ -3,6 +3,9 @@
 // and the expert-routed products.
 #pragma once
 
+#include <cstddef>
+#include <type_traits>
+
 #include "launch.hpp"
 #include "q8_1.hpp"
 #include "tq1_decode.hpp"
@@ -302,32 +305,28 @@ __device__ __forceinline__ void dword_sums_staged(const RawBlock &raw,
 // col_off[t] of the activation buffer ra and its outputs go to out[t][row],
 // plus resid[t * N + row] when resid is given (one fp32 addition after the
 // product's own result; resid may be the output buffer itself).
-// GLU: rw is the gate matrix and rw2 the up matrix of the same shape; each
-// lane takes the same block of both rows against the staged columns (both
-// products in the plain product's fp32 order) and the output is
-// silu(gate) * up. Otherwise rw2 is unused.
+// With a `store` functor, the row's lane 0 hands store(t, value) each
+// column's result instead of writing out[t][row] (out and resid unused).
 // All nthreads threads of the workgroup (its whole size) must call this (it
 // synchronizes); lanes whose row is out of range only help with staging.
-template <int TC, bool ISUMS, bool F32 = false, bool GLU = false>
-__device__ __forceinline__ void staged_rows(__amdgpu_buffer_rsrc_t rw, __amdgpu_buffer_rsrc_t rw2,
-                                            __amdgpu_buffer_rsrc_t ra,
+template <int TC, bool ISUMS, bool F32 = false, class Store = std::nullptr_t>
+__device__ __forceinline__ void staged_rows(__amdgpu_buffer_rsrc_t rw, __amdgpu_buffer_rsrc_t ra,
                                             const uint32_t (&col_off)[TC],
                                             float *const (&out)[TC], const float *resid,
                                             int32_t *__restrict__ isums,
                                             uint32_t *__restrict__ act, int64_t row, bool row_ok,
                                             int64_t N, int nb, int T, int lr_log2, int chunk,
-                                            int nthreads = 256)
+                                            int nthreads = 256, Store store = nullptr)
 {
     const int tid = threadIdx.x, lane = tid & 63;
     const int Lr = 1 << lr_log2;
     const int sub = lane & (Lr - 1);
     const int nblk = nb * 8;
     const uint32_t row_off = (uint32_t)((row_ok ? row : 0) * nb * kTq1BlockBytes);
-    static_assert(!(GLU && ISUMS), "the gated product has no block-sum twin");
-    float acc[TC], acc2[TC];
+    float acc[TC];
 #pragma unroll
     for (int t = 0; t < TC; t++)
-        acc[t] = acc2[t] = 0.0f;
+        acc[t] = 0.0f;
 
     // one pass over the blocks [B0, B0 + chunk) of the row
     auto pass = [&](int B0) {
@@ -349,13 +348,9 @@ __device__ __forceinline__ void staged_rows(__amdgpu_buffer_rsrc_t rw, __amdgpu_
         StageBatch<F32> head;
         stage_load<F32>(head, ra, col_off[0], B0, cb, 0, tid, nthreads);
         __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-        const uint32_t first_off = row_ok && first < end
-                                       ? row_off + (uint32_t)first * kTq1BlockBytes
-                                       : kIdleLoadOffset;
-        RawBlock cur = load_raw_block(rw, first_off);
-        RawBlock cur2;
-        if constexpr (GLU)
-            cur2 = load_raw_block(rw2, first_off);
+        RawBlock cur = load_raw_block(rw, row_ok && first < end
+                                              ? row_off + (uint32_t)first * kTq1BlockBytes
+                                              : kIdleLoadOffset);
         __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
         // and no arithmetic on the batch (with its wait) moves up between
         // the weight loads
@@ -367,8 +362,7 @@ __device__ __forceinline__ void staged_rows(__amdgpu_buffer_rsrc_t rw, __amdgpu_
                 stage_column<F32>(act + t * cb * kActStride, ra, col_off[t], B0, cb, tid, nthreads,
                                   nullptr);
         __syncthreads();
-        // one block of a row (cur, or the up matrix's cur2) against the
-        // staged columns, into ac[]
+        // one block of the row against the staged columns, into ac[]
         auto block_terms = [&](const RawBlock &blk, float (&ac)[TC], int B) {
             const float dw = f16_bits_to_f32(raw_scale_bits(blk));
             DigitBlock d;
@@ -418,14 +412,9 @@ __device__ __forceinline__ void staged_rows(__amdgpu_buffer_rsrc_t rw, __amdgpu_
         };
         if (row_ok) {
             for (int B = first; B < end; B += Lr) {
-                if (B != first) {
+                if (B != first)
                     cur = load_raw_block(rw, row_off + (uint32_t)B * kTq1BlockBytes);
-                    if constexpr (GLU)
-                        cur2 = load_raw_block(rw2, row_off + (uint32_t)B * kTq1BlockBytes);
-                }
                 block_terms(cur, acc, B);
-                if constexpr (GLU)
-                    block_terms(cur2, acc2, B);
             }
         }
     };
@@ -440,19 +429,16 @@ __device__ __forceinline__ void staged_rows(__amdgpu_buffer_rsrc_t rw, __amdgpu_
     if (!ISUMS) {
         // butterfly over the Lr lanes of the row (every lane of the wave takes part)
 #pragma unroll
-        for (int t = 0; t < TC; t++) {
+        for (int t = 0; t < TC; t++)
             acc[t] = row_sum(acc[t], lr_log2);
-            if constexpr (GLU)
-                acc2[t] = row_sum(acc2[t], lr_log2);
-        }
         if (row_ok && sub == 0) {
 #pragma unroll
             for (int t = 0; t < TC; t++)
                 if (t < T) {
-                    if constexpr (GLU)
-                        out[t][row] = acc[t] / (1.0f + expf(-acc[t])) * acc2[t];
-                    else
+                    if constexpr (std::is_same_v<Store, std::nullptr_t>)
                         out[t][row] = resid ? acc[t] + resid[(int64_t)t * N + row] : acc[t];
+                    else
+                        store(t, acc[t]);
                 }
         }
     }
