@@ -343,6 +343,32 @@ def read_probe_row(torch, wrot, R, nbytes, name, launches):
             "frac_of_8tbs": round(rd / best[0] / 1e3 / HBM_PEAK_GBS, 4)}
 
 
+def c_abi_eager(torch, bqm, wrot, R, x, y, N, K, T, iters):
+    """Eager steps of mmvq_tq1_0_f32 called from C (the probe library's loop
+    over the library's own entry point, rotating weight copies): host time
+    per call to enqueue, and wall time per call until the stream drains."""
+    probes = ctypes.CDLL(os.path.join(ROOT, "bit_quantized_mat_amd", "libbqm_probes.so"))
+    probes.bqm_probe_eager.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_uint64,
+                                       ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
+                                       ctypes.c_int64, ctypes.c_int64, ctypes.c_int32,
+                                       ctypes.c_int, ctypes.c_void_p,
+                                       ctypes.POINTER(ctypes.c_double),
+                                       ctypes.POINTER(ctypes.c_double)]
+    fn = ctypes.cast(bqm.library().mmvq_tq1_0_f32, ctypes.c_void_p)
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    enq, wall = ctypes.c_double(), ctypes.c_double()
+    res = {}
+    for rep in range(2):  # the first pass warms the host path
+        rc = probes.bqm_probe_eager(fn, ctypes.c_void_p(wrot.data_ptr()), wrot.shape[1], R,
+                                    ctypes.c_void_p(x.data_ptr()), ctypes.c_void_p(y.data_ptr()),
+                                    N, K, T, iters, stream, ctypes.byref(enq), ctypes.byref(wall))
+        if rc != 0:
+            raise RuntimeError("bqm_probe_eager: status %d" % rc)
+        res = {"enqueue_us": round(enq.value, 4), "wall_us": round(wall.value, 4),
+               "calls": iters}
+    return res
+
+
 def dequant_rows(torch, bqm, wrot, R, wbytes, name, N, K, launches):
     """Dequantize the whole matrix (fp16, bf16, fp32) and gather 1024 rows
     (fp16); beside them a copy probe moving as many bytes, for scale."""
@@ -986,6 +1012,8 @@ def main():
         step(i)
     torch.cuda.synchronize()
     eager_us = (time.perf_counter() - t0) * 1e6 / args.steps
+    # the same eager steps through the C ABI with no Python in the loop
+    c_eager = c_abi_eager(torch, bqm, wrot, R, x, y, N, K, T, max(args.steps, 200))
 
     # timed region: the K steps as one graph
     step_us = graph_us(torch, lambda i: step(args.warmup + i), args.steps)
@@ -1019,7 +1047,9 @@ def main():
         % (us_call, args.kernel_launches, achieved, 100 * achieved / HBM_PEAK_GBS, HBM_PEAK_GBS))
     log("two calls: %.3f us (quantize %.3f us, mat-vec %.3f us = %.1f GB/s)"
         % (two_call_us, quant_us, mmvq_us, algorithmic_bytes(N, K, T) / mmvq_us / 1e3))
-    log("step: %.3f us graph-replayed, %.3f us eager" % (step_us, eager_us))
+    log("step: %.3f us graph-replayed, %.3f us eager from Python, %.3f us eager from C "
+        "(%.3f us of host time to enqueue each call)"
+        % (step_us, eager_us, c_eager["wall_us"], c_eager["enqueue_us"]))
     log("with a residual: %.3f us fused (quantize + mat-vec + add, one launch), %.3f us as "
         "mat-vec then a separate add" % (add_fused_us, add_two_us))
 
@@ -1058,6 +1088,7 @@ def main():
         "mmvq_gbs": round(algorithmic_bytes(N, K, T) / mmvq_us / 1e3, 2),
         "quantize_us": round(quant_us, 4),
         "us_per_step_eager": round(eager_us, 4),
+        "us_per_step_eager_c_abi": c_eager,
         "residual_add_fused_us": round(add_fused_us, 4),
         "residual_add_two_launch_us": round(add_two_us, 4),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,

@@ -10,6 +10,8 @@
 // the device's vector-ALU issue rate (lane operations per second) on the
 // instruction kinds the TQ1_0 decode is made of.
 #include <hip/hip_runtime.h>
+
+#include <chrono>
 #include <stdint.h>
 
 namespace {
@@ -141,6 +143,40 @@ __attribute__((visibility("default"))) int bqm_probe_valu(int kind, int iters, u
     default: hipLaunchKernelGGL(valu_kernel<3>, g, b, 0, (hipStream_t)stream, iters, 12345u, out); break;
     }
     return hipGetLastError() == hipSuccess ? 0 : -5;
+}
+
+// Eager stepping through the C ABI with no Python in the loop: `iters`
+// calls of fn (the signature of mmvq_tq1_0_f32) on the weight copies
+// w_base + (i mod R) * w_stride, enqueued back to back on the stream. Writes
+// the host time per call spent enqueueing (enqueue_us) and the wall time per
+// call until the stream drains (wall_us). Returns fn's first nonzero status.
+typedef int (*bqm_f32_fn)(const void *, const float *, float *, int64_t, int64_t, int32_t,
+                          void *);
+__attribute__((visibility("default"))) int bqm_probe_eager(void *fn, const uint8_t *w_base,
+                                                           uint64_t w_stride, int R,
+                                                           const float *x, float *y, int64_t N,
+                                                           int64_t K, int32_t T, int iters,
+                                                           void *stream, double *enqueue_us,
+                                                           double *wall_us)
+{
+    if (!fn || !w_base || R < 1 || iters < 1 || !enqueue_us || !wall_us)
+        return -2;
+    const bqm_f32_fn f = reinterpret_cast<bqm_f32_fn>(fn);
+    if (hipStreamSynchronize((hipStream_t)stream) != hipSuccess)
+        return -5;
+    const auto t0 = std::chrono::steady_clock::now();
+    for (int i = 0; i < iters; i++) {
+        const int rc = f(w_base + (uint64_t)(i % R) * w_stride, x, y, N, K, T, stream);
+        if (rc)
+            return rc;
+    }
+    const auto t1 = std::chrono::steady_clock::now();
+    if (hipStreamSynchronize((hipStream_t)stream) != hipSuccess)
+        return -5;
+    const auto t2 = std::chrono::steady_clock::now();
+    *enqueue_us = std::chrono::duration<double, std::micro>(t1 - t0).count() / iters;
+    *wall_us = std::chrono::duration<double, std::micro>(t2 - t0).count() / iters;
+    return 0;
 }
 
 }  // extern "C"
