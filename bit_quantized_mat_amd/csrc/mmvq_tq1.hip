@@ -237,6 +237,21 @@ int launch_mm(const void *w, const void *a, float *y, int64_t N, int64_t K, int6
 {
     if (T <= BQM_MMVQ_MAX_COLS)
         return launch_mmvq(w, a, y, nullptr, N, K, (int32_t)T, stream);
+    // up to three chunks of 32 columns on rows of 5 to 16 blocks: one plain
+    // product per chunk (on the register-operand kernel) beats one launch of
+    // the column-chunked or K-streaming kernels there (14336 x 4096: 33 / 64 /
+    // 80 / 96 columns 36.3 / 36.0 / 58.2 / 57.5 -> 21.7 / 31.4 / 42.1 / 46.9 us;
+    // at 128 columns 57.7 -> 61.8, so not beyond 96)
+    if (T <= 3 * BQM_MMVQ_MAX_COLS && mfma_reg_supported(K, BQM_MMVQ_MAX_COLS)) {
+        const int64_t col_bytes = K / 32 * kQ81BlockBytes;
+        for (int64_t t0 = 0; t0 < T; t0 += BQM_MMVQ_MAX_COLS) {
+            const int64_t tc = T - t0 < BQM_MMVQ_MAX_COLS ? T - t0 : BQM_MMVQ_MAX_COLS;
+            if (int rc = launch_mmvq(w, static_cast<const uint8_t *>(a) + t0 * col_bytes,
+                                     y + t0 * N, nullptr, N, K, (int32_t)tc, stream))
+                return rc;
+        }
+        return BQM_OK;
+    }
     if (2 * mm_stream_workgroups(N, T) < 3ll * compute_units() && mm_chunked_supported(K))
         return launch_mm_chunked(w, a, y, N, K, T, stream);
     return launch_mm_stream(w, a, y, N, K, T, stream);

@@ -637,7 +637,10 @@ def test_workload_moe_slots_equal_plain_calls(bqm, moe_workload):
 
 @pytest.mark.parametrize("N,K,T", [
     (300, 4096, 100),   # column chunks of 32 on the resident kernel, a ragged last one
-    (67, 2304, 40),     # rows of 9 blocks
+    (67, 2304, 40),     # rows of 9 blocks: two plain products (32 + 8 columns)
+    (515, 4096, 33),    # two plain products, the second of one column
+    (300, 4096, 64),    # two plain products of 32
+    (130, 4096, 96),    # three plain products of 32
     (130, 6144, 170),   # chunks of 16 (32 do not fit LDS)
     (40, 16384, 50),    # no chunk fits: the K-streaming kernel, one fold (64 blocks)
     (21, 33024, 33),    # K-streaming, 129 blocks: two folds and a tail
@@ -651,9 +654,10 @@ def test_mm_parity(bqm, N, K, T):
     y = _host(bqm.mm_tq1_0(w, a, N, K, T))
     _, y64, ab = oracle.mmvq(w_ref, a_ref, N, K, T)
     _assert_close(y, y64, ab, "mm N=%d K=%d T=%d" % (N, K, T))
-    if T <= 32:
-        # the plain product: columns bitwise the single-column calls'
-        for t in sorted(set([0, T // 2, T - 1])):
+    if T <= 32 or (T <= 96 and 5 <= K // 256 <= 16):
+        # the plain product (over chunks of 32 columns from 33 to 96 columns
+        # on rows of 5 to 16 blocks): columns bitwise the single-column calls'
+        for t in sorted(set([0, T // 2, T - 1, min(T - 1, 32)])):
             y1 = _host(bqm.mmvq_tq1_0(w, a[t:t + 1].clone(), N, K, 1))
             assert np.array_equal(y1[0].view(np.uint32), y[t].view(np.uint32)), t
 
