@@ -497,7 +497,8 @@ def sweep(path, torch, np, bqm, synth, dev, launches, only=None):
         if only and name not in only:
             continue
         wl = synth.WORKLOADS[name]
-        inp = synth.make_inputs(wl)
+        # at least two columns: the gate-up rows take one and two
+        inp = synth.make_inputs(wl, T=max(max(wl.Ts), 2))
         N, K = wl.N, wl.K
         w0 = bqm.tq1_pack(torch.from_numpy(inp.trits).to(dev),
                           torch.from_numpy(inp.d16.view(np.int16)).to(dev))
@@ -527,7 +528,8 @@ def sweep(path, torch, np, bqm, synth, dev, launches, only=None):
                 us = timer.time(row, lambda i: fn(wrot[i % R], wrot[(i + 1) % R], src, N, K, T,
                                                   out=y), launches, y)
                 xb = T * K * 4 - T * (K // 32) * 36 if op == "mmvq_tq1_0_f32_glu" else 0
-                _rate_fields(row, algorithmic_bytes(N, K, T) + w0.numel() + xb, us, read_gbs)
+                # no read-probe fraction: the probe reads one matrix, the call two
+                _rate_fields(row, algorithmic_bytes(N, K, T) + w0.numel() + xb, us)
             del x_all
         del wrot, w0
         torch.cuda.empty_cache()
@@ -719,7 +721,7 @@ def sweep_report(sweep_json, traced_json=None, cpu_json=None):
             continue
         t = tr.get((r["workload"], r["op"], r.get("T")))
         cp = (cpu.get((r["workload"], r.get("T"), "mmvq_tq2_0" if "tq2" in r["op"] else ""))
-              if r["op"].startswith("mmvq") else None)
+              if r["op"].startswith("mmvq") and "glu" not in r["op"] else None)
         nk = ("%d x %d x %d" % (r["E"], r["N"], r["K"])) if "E" in r else (
             "%d x %d" % (r["N"], r["K"]))
         out.append("| %s | %s | %s | %s | %.3f | %.1f | %.1f | %s | %s | %s | %s | %s |" % (
