@@ -169,7 +169,8 @@ __global__ __launch_bounds__(256) void tq1_dequantize_kernel(const uint8_t *__re
         // output block -> (result row i, block B); fewer than 2^27 blocks
         const uint32_t ub = in ? (uint32_t)blk : 0u;
         const uint32_t i = ub / (uint32_t)nb, B = ub - i * (uint32_t)nb;
-        int64_t r = rows ? rows[i] : i;
+        // (signed: a negative id must not turn into a large unsigned one)
+        int64_t r = rows ? (int64_t)rows[i] : (int64_t)i;
         r = r < 0 ? 0 : (r >= N ? N - 1 : r);  // ids outside [0, N) stay inside w
         const uint32_t off = (uint32_t)((r * nb + B) * kTq1BlockBytes);
         const uint32_t sh = off & 3u;

@@ -641,6 +641,7 @@ def test_workload_moe_slots_equal_plain_calls(bqm, moe_workload):
     (515, 4096, 33),    # two plain products, the second of one column
     (300, 4096, 64),    # two plain products of 32
     (130, 4096, 96),    # three plain products of 32
+    (100, 1280, 70),    # rows of 5 blocks: three plain products (32 + 32 + 6)
     (130, 6144, 170),   # chunks of 16 (32 do not fit LDS)
     (40, 16384, 50),    # no chunk fits: the K-streaming kernel, one fold (64 blocks)
     (21, 33024, 33),    # K-streaming, 129 blocks: two folds and a tail
@@ -965,6 +966,23 @@ def test_tq1_dequantize_bit_exact(bqm, N, K, dtype):
     got = _dq_bits(bqm.tq1_dequantize(w, N, K, rows=_dev(rows), dtype=tdt))
     ref = oracle.tq1_dequantize(w_ref, N, K, dtype, rows=rows)
     assert np.array_equal(got, ref.view(got.dtype))
+
+
+def test_tq1_dequantize_gather_clamps_row_ids(bqm):
+    """Row ids outside [0, N) read the nearest valid row (below 0: row 0;
+    N and above: row N - 1), in every output type and on both sides of the
+    non-temporal threshold's block counts."""
+    import torch
+    N, K = 37, 1280
+    trits, d16, _ = _case(N, K, 1, seed=8100)
+    w = bqm.tq1_pack(_dev(trits), _dev(d16.view(np.int16)))
+    w_ref = oracle.tq1_pack(trits, d16)
+    rows = np.array([-1, 0, N - 1, N, N + 5, -(2 ** 31), 2 ** 31 - 1, 17], dtype=np.int32)
+    clamped = np.clip(rows.astype(np.int64), 0, N - 1).astype(np.int32)
+    for dtype, tdt in (("f32", torch.float32), ("f16", torch.float16), ("bf16", torch.bfloat16)):
+        got = _dq_bits(bqm.tq1_dequantize(w, N, K, rows=_dev(rows), dtype=tdt))
+        ref = oracle.tq1_dequantize(w_ref, N, K, dtype, rows=clamped)
+        assert np.array_equal(got, ref.view(got.dtype)), dtype
 
 
 # ---------------------------------------------------------------------------
