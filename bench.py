@@ -811,6 +811,64 @@ def profile_run(spec, torch, np, bqm, synth, dev):
                       "kernel_source_hash": kernel_source_hash()}), flush=True)
 
 
+SPREAD_PATTERNS = (("graph of 300 calls, replayed twice", 600),
+                   ("eager, back to back", 300),
+                   ("eager, a device sync after each call", 300),
+                   ("one warm weight copy, a device sync after each call", 300))
+
+
+def spread_run(torch, np, bqm, synth, dev):
+    """The decode step's fused call launched in four patterns, for a kernel
+    trace of how per-dispatch durations spread: back to back in a graph,
+    eagerly back to back, eagerly with a device sync after each call (cold
+    weight copies), and with a sync after each call on one warm copy."""
+    wl = synth.WORKLOADS["decode"]
+    inp = synth.make_inputs(wl)
+    N, K = wl.N, wl.K
+    w0 = bqm.tq1_pack(torch.from_numpy(inp.trits).to(dev),
+                      torch.from_numpy(inp.d16.view(np.int16)).to(dev))
+    wrot, R = rotation(torch, w0, dev)
+    x = torch.from_numpy(inp.x[:1]).to(dev)
+    y = torch.empty((1, N), dtype=torch.float32, device=dev)
+    torch.cuda.synchronize()
+    graph_us(torch, lambda i: bqm.mmvq_tq1_0_f32(wrot[i % R], x, N, K, 1, out=y), 300)
+    log("spread: graph done")
+    for i in range(300):
+        bqm.mmvq_tq1_0_f32(wrot[i % R], x, N, K, 1, out=y)
+    torch.cuda.synchronize()
+    for i in range(300):
+        bqm.mmvq_tq1_0_f32(wrot[i % R], x, N, K, 1, out=y)
+        torch.cuda.synchronize()
+    for i in range(300):
+        bqm.mmvq_tq1_0_f32(wrot[0], x, N, K, 1, out=y)
+        torch.cuda.synchronize()
+    log("spread: done")
+
+
+def spread_summary(trace_csv):
+    """Median, p10, p90 of the fused call's dispatch durations per pattern of
+    --spread, and the median gap from the previous dispatch's end (µs)."""
+    import csv
+    import statistics
+    with open(trace_csv) as f:
+        rows = [r for r in csv.DictReader(f)
+                if "mmvq_staged_kernel<1, false, true, 4>" in r["Kernel_Name"]]
+    rows.sort(key=lambda r: int(r["Start_Timestamp"]))
+    st = [int(r["Start_Timestamp"]) for r in rows]
+    en = [int(r["End_Timestamp"]) for r in rows]
+    lines = ["| pattern | dispatches | median | p10 | p90 | min | max | gap to the previous dispatch (median) |",
+             "|---|---|---|---|---|---|---|---|"]
+    i = 0
+    for name, n in SPREAD_PATTERNS:
+        d = sorted((en[k] - st[k]) / 1e3 for k in range(i, i + n))
+        gaps = [(st[k] - en[k - 1]) / 1e3 for k in range(i + 1, i + n)]
+        lines.append("| %s | %d | %.3f | %.3f | %.3f | %.3f | %.3f | %.2f |" % (
+            name, n, statistics.median(d), d[int(0.1 * (n - 1))], d[int(0.9 * (n - 1))], d[0],
+            d[-1], statistics.median(gaps)))
+        i += n
+    return "\n".join(lines)
+
+
 def _counter_medians(csv_dir, counter):
     """Median per-dispatch value of one counter, by kernel family, from a
     rocprofv3 --pmc csv output directory."""
@@ -927,6 +985,11 @@ def main():
     ap.add_argument("--sweep", metavar="PATH", help="also measure every workload; JSON table")
     ap.add_argument("--sweep-launches", type=int, default=100)
     ap.add_argument("--sweep-only", default="", help="comma-separated workload names")
+    ap.add_argument("--spread", action="store_true",
+                    help="only launch the decode step's fused call in four patterns (for a kernel "
+                         "trace of per-dispatch spread; --spread-summary reads the trace)")
+    ap.add_argument("--spread-summary", metavar="TRACE_CSV",
+                    help="no GPU: per-pattern duration spread from a kernel trace of --spread")
     ap.add_argument("--profile", metavar="WORKLOAD:T[:LAUNCHES[:OP]]",
                     help="only run a few launches of one shape (for counter collection)")
     ap.add_argument("--write-counters", nargs=3, metavar=("FETCH_DIR", "WRITE_DIR", "PROBE_BYTES"),
@@ -949,6 +1012,9 @@ def main():
 
     if args.cpu_table:
         cpu_table(args.cpu_table)
+        return
+    if args.spread_summary:
+        print(spread_summary(args.spread_summary))
         return
     if args.trace_summary:
         trace_summary(*args.trace_summary)
@@ -984,6 +1050,9 @@ def main():
     torch.cuda.set_device(dev)
     if args.profile:
         profile_run(args.profile, torch, np, bqm, synth, dev)
+        return
+    if args.spread:
+        spread_run(torch, np, bqm, synth, dev)
         return
     wl = synth.WORKLOADS["decode"]
     N, K, T = wl.N, wl.K, 1
