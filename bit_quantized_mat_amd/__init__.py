@@ -14,6 +14,7 @@ __all__ = [
     "MM_MAX_COLS",
     "mmvq_tq1_0_f32", "MMVQ_F32_MAX_COLS", "tq1_dequantize", "mmvq_tq1_0_add",
     "mmvq_tq1_0_f32_add", "mmvq_tq1_0_glu", "mmvq_tq1_0_f32_glu", "GLU_MAX_COLS",
+    "GLU_F32_MAX_COLS",
     "mmvq_id_tq1_0", "mmvq_id_tq1_0_slots", "mmvq_id_tq1_0_workspace_bytes",
     "mmvq_id_tq1_0_noalloc", "NOALLOC_SCRATCH_BYTES",
     "mmvq_tq1_0_block_isums", "tq2_pack", "mmvq_tq2_0", "mmvq_tq2_0_block_isums",
@@ -26,7 +27,8 @@ Q81_BLOCK_BYTES = 36
 MMVQ_MAX_COLS = 32
 MMVQ_F32_MAX_COLS = 8
 MM_MAX_COLS = 65536
-GLU_MAX_COLS = 2
+GLU_MAX_COLS = 32
+GLU_F32_MAX_COLS = 2
 NOALLOC_SCRATCH_BYTES = 768 * 1024
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -225,8 +227,8 @@ def mmvq_tq1_0_f32_add(w, x, r, N, K, T, out=None, stream=None):
 
 
 def mmvq_tq1_0_glu(w_gate, w_up, a, N, K, T, out=None, stream=None):
-    """y fp32 [T, N] = silu(mmvq_tq1_0(w_gate, a)) * mmvq_tq1_0(w_up, a) in one
-    launch, 1 <= T <= GLU_MAX_COLS."""
+    """y fp32 [T, N] = silu(mmvq_tq1_0(w_gate, a)) * mmvq_tq1_0(w_up, a),
+    1 <= T <= GLU_MAX_COLS (one launch up to two columns, two beyond)."""
     torch = _torch()
     if out is None:
         out = torch.empty((T, N), dtype=torch.float32, device=w_gate.device)
@@ -240,7 +242,8 @@ def mmvq_tq1_0_glu(w_gate, w_up, a, N, K, T, out=None, stream=None):
 
 
 def mmvq_tq1_0_f32_glu(w_gate, w_up, x, N, K, T, out=None, stream=None):
-    """The same on fp32 activations x [T, K], quantized inside the call."""
+    """The same on fp32 activations x [T, K], quantized inside the call
+    (1 <= T <= GLU_F32_MAX_COLS)."""
     torch = _torch()
     if out is None:
         out = torch.empty((T, N), dtype=torch.float32, device=w_gate.device)

@@ -4,6 +4,7 @@
 
 #include <atomic>
 
+#include "common.hpp"
 #include "launch.hpp"
 
 namespace {
@@ -179,7 +180,10 @@ int mmvq_tq1_0_f32_add(const void *w, const float *x, const float *r, float *y, 
     return mmvq_f32_call(w, x, r, true, y, N, K, T, stream);
 }
 
-// f32: the columns are fp32 (quantized inside the call), else Q8_1 blocks.
+// f32: the columns are fp32 (quantized inside the call, at most two), else
+// Q8_1 blocks. Up to two columns one launch of the staged wave pairs; beyond,
+// the gate product into y, then the up product with the gated epilogue
+// reading y.
 static int glu_call(const void *wg, const void *wu, const void *a, float *y, int64_t N,
                     int64_t K, int32_t T, bool f32, void *stream)
 {
@@ -188,13 +192,19 @@ static int glu_call(const void *wg, const void *wu, const void *a, float *y, int
     if (int rc = check_matrix(N, K))
         return rc;
     const uint64_t col_bytes = f32 ? (uint64_t)K * 4ull : (uint64_t)(K / 32) * 36ull;
-    if (T < 1 || T > BQM_GLU_MAX_COLS || (uint64_t)T * col_bytes > kMaxBufferBytes)
+    const int max_cols = f32 ? BQM_GLU_F32_MAX_COLS : BQM_GLU_MAX_COLS;
+    if (T < 1 || T > max_cols || (uint64_t)T * col_bytes > kMaxBufferBytes)
         return BQM_ERR_SHAPE;
     if (!aligned4(wg) || !aligned4(wu) || !aligned4(a) || !aligned4(y))
         return BQM_ERR_ALIGN;
     if (int rc = check_device())
         return rc;
-    return bqm::launch_mmvq_glu(wg, wu, a, y, N, K, T, f32, as_stream(stream));
+    const hipStream_t st = as_stream(stream);
+    if (T <= bqm::kGluMaxCols)
+        return bqm::launch_mmvq_glu(wg, wu, a, y, N, K, T, f32, st);
+    if (int rc = bqm::launch_mmvq(wg, a, y, nullptr, N, K, T, st))
+        return rc;
+    return bqm::launch_mmvq(wu, a, y, nullptr, N, K, T, st, bqm::gated_epilogue(y));
 }
 
 int mmvq_tq1_0_glu(const void *w_gate, const void *w_up, const void *a, float *y, int64_t N,

@@ -77,6 +77,28 @@ __device__ __forceinline__ uint32_t f32_to_f16_bits(float f)
     return b;
 }
 
+// The residual argument of the product kernels, as their launchers pass it:
+// nullptr; a residual r [T][N] (y = product + r); or, with bit 0 set, the
+// gate products g [T][N] of a gate-up pair (y = silu(g) * product with
+// silu(g) = g / (1 + exp(-g)), the gated unit's epilogue). r or g may be the
+// output itself: each element is read and written by the same lane. The tag
+// never crosses the C ABI, whose pointers are 4-byte aligned.
+inline const float *gated_epilogue(const float *g)
+{
+    return reinterpret_cast<const float *>(reinterpret_cast<uintptr_t>(g) | 1u);
+}
+
+// The stored value of output element o for product value v.
+__device__ __forceinline__ float epilogue(float v, const float *tagged, int64_t o)
+{
+    const uintptr_t p = reinterpret_cast<uintptr_t>(tagged);
+    const float *r = reinterpret_cast<const float *>(p & ~(uintptr_t)1);
+    if (!r)
+        return v;
+    const float e = r[o];
+    return (p & 1u) ? e / (1.0f + expf(-e)) * v : v + e;
+}
+
 // Bytes [s, s+4) of the 8-byte little-endian value hi:lo, s in {0, 2}.
 __device__ __forceinline__ uint32_t align_bytes(uint32_t hi, uint32_t lo, uint32_t s)
 {

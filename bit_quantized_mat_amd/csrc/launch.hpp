@@ -50,15 +50,19 @@ int staged_workgroup_waves(int64_t N, int lr);
 // takes this shape, and its launcher.
 bool staged_supported(int64_t K, int32_t T);
 // r (every product launcher): when given, y = product + r, one fp32 addition
-// after the product's own result (r [T][N], may be y itself).
+// after the product's own result (r [T][N], may be y itself); tagged by
+// gated_epilogue (common.hpp), y = silu(r) * product instead (the up product
+// of a gate-up pair, r the gate products).
 int launch_mmvq_staged(const void *w, const void *a, float *y, int32_t *isums, int64_t N,
                        int64_t K, int32_t T, hipStream_t stream, const float *r = nullptr);
 // The staged kernel on fp32 activations, quantized to Q8_1 while staging.
 int launch_mmvq_staged_f32(const void *w, const float *x, float *y, int64_t N, int64_t K,
                            int32_t T, hipStream_t stream, const float *r = nullptr);
-// Gate-up pair with the SiLU-gated epilogue, y = silu(wg . a) * (wu . a), on
-// the staged kernel: one or two columns (f32: fp32 columns, quantized while
-// staging); BQM_ERR_SHAPE for other column counts or rows it cannot stage.
+// Gate-up pair with the SiLU-gated epilogue, y = silu(wg . a) * (wu . a), in
+// one launch of the staged kernel's wave pairs: one or two columns (f32:
+// fp32 columns, quantized while staging); BQM_ERR_SHAPE for other column
+// counts or rows it cannot stage. (Wider calls run the gate product into y,
+// then the up product with the gated epilogue reading y.)
 constexpr int kGluMaxCols = 2;
 int launch_mmvq_glu(const void *wg, const void *wu, const void *a, float *y, int64_t N, int64_t K,
                     int32_t T, bool f32, hipStream_t stream);

@@ -256,8 +256,7 @@ __global__ __launch_bounds__(512) void mmvq_mfma_kernel(const uint8_t *__restric
                                 const int64_t row = r0 + 16 * rt + 4 * rg + i;
                                 if (row < N) {
                                     const int64_t o = (int64_t)c * N + row;
-                                    y[o] = resid ? acc[0][rt][ct][i] + resid[o]
-                                                 : acc[0][rt][ct][i];
+                                    y[o] = epilogue(acc[0][rt][ct][i], resid, o);
                                 }
                             }
                         }

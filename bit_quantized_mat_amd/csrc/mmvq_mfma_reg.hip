@@ -314,7 +314,7 @@ __global__ __launch_bounds__(64 * NW) void mmvq_mfma_reg_kernel(const uint8_t *_
                 const int64_t row = r0 + (PAIR ? 16 * (oc >> 3) : 0) + 4 * org + i;
                 if (j == 0 && c < T && row < N) {
                     const int64_t oi = (int64_t)c * N + row;
-                    y[oi] = resid ? v + resid[oi] : v;
+                    y[oi] = epilogue(v, resid, oi);
                 }
             }
         }

@@ -497,7 +497,7 @@ __global__ __launch_bounds__(64 * NW) void mmvq_mfma_res_kernel(const uint8_t *_
                     if (j == 0 && c < T && row < N) {
                         const int64_t yc = ID ? colpair[c] : c;
                         const int64_t o = yc * N + row;
-                        y[o] = resid ? v + resid[o] : v;
+                        y[o] = epilogue(v, resid, o);
                     }
                 }
             } else {
@@ -533,8 +533,7 @@ __global__ __launch_bounds__(64 * NW) void mmvq_mfma_res_kernel(const uint8_t *_
                                                         4 * rg + i;
                                     if (row < N) {
                                         const int64_t o = yc * N + row;
-                                        y[o] = resid ? acc[0][rt][ct][i] + resid[o]
-                                                     : acc[0][rt][ct][i];
+                                        y[o] = epilogue(acc[0][rt][ct][i], resid, o);
                                     }
                                 }
                             }

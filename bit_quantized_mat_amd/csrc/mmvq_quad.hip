@@ -265,7 +265,7 @@ __global__ __launch_bounds__(64 * WPG) void mmvq_quad_kernel(const uint8_t *__re
             for (int v = 0; v < 4; v++)
                 if (col < T && row0 + v < N) {
                     const int64_t o = (int64_t)col * N + row0 + v;
-                    y[o] = resid ? out[cg][v] + resid[o] : out[cg][v];
+                    y[o] = epilogue(out[cg][v], resid, o);
                 }
         }
     }

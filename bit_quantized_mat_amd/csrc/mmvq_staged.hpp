@@ -302,9 +302,11 @@ __device__ __forceinline__ void dword_sums_staged(const RawBlock &raw,
 
 // The rows of one workgroup against T <= TC activation columns. Column t's
 // Q8_1 row (fp32 row when F32: quantized while staging) starts at byte
-// col_off[t] of the activation buffer ra and its outputs go to out[t][row],
-// plus resid[t * N + row] when resid is given (one fp32 addition after the
-// product's own result; resid may be the output buffer itself).
+// col_off[t] of the activation buffer ra and its outputs go to out[t][row]
+// through the residual epilogue (common.hpp): plus resid[t * N + row] when
+// resid is given (one fp32 addition after the product's own result), or, when
+// resid is tagged as gate products, silu(gate) times the product; resid may
+// be the output buffer itself.
 // With a `store` functor, the row's lane 0 hands store(t, value) each
 // column's result instead of writing out[t][row] (out and resid unused).
 // All nthreads threads of the workgroup (its whole size) must call this (it
@@ -436,7 +438,7 @@ __device__ __forceinline__ void staged_rows(__amdgpu_buffer_rsrc_t rw, __amdgpu_
             for (int t = 0; t < TC; t++)
                 if (t < T) {
                     if constexpr (std::is_same_v<Store, std::nullptr_t>)
-                        out[t][row] = resid ? acc[t] + resid[(int64_t)t * N + row] : acc[t];
+                        out[t][row] = epilogue(acc[t], resid, (int64_t)t * N + row);
                     else
                         store(t, acc[t]);
                 }

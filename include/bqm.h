@@ -185,8 +185,10 @@ BQM_API int mmvq_tq1_0_f32(const void *w, const float *x, float *y,
 BQM_API int mmvq_tq1_0_f32_add(const void *w, const float *x, const float *r, float *y,
                        int64_t N, int64_t K, int32_t T, void *stream);
 
-/* Largest number of activation columns the gated entry points accept. */
-#define BQM_GLU_MAX_COLS 2
+/* Largest numbers of activation columns mmvq_tq1_0_glu and
+ * mmvq_tq1_0_f32_glu accept. */
+#define BQM_GLU_MAX_COLS 32
+#define BQM_GLU_F32_MAX_COLS 2
 
 /* Gate-up pair with a SiLU-gated epilogue in one launch (the fused mat-vec
  * path of "CUDA: TQ1_0 mat-vec is load-bound by the per-32-element chunk
@@ -196,19 +198,21 @@ BQM_API int mmvq_tq1_0_f32_add(const void *w, const float *x, const float *r, fl
  *   y[t][n] = silu(g[t][n]) * u[t][n],  silu(x) = x / (1 + exp(-x)),
  *   g = mmvq_tq1_0(w_gate, a), u = mmvq_tq1_0(w_up, a)
  * g and u are bitwise those two products' outputs; the epilogue is fp32
- * (exp accurate to a few ulp). Both matrices are read once, the columns
- * staged once for both.
+ * (exp accurate to a few ulp). Each matrix is read once: up to two columns in
+ * one launch (the columns staged once for both matrices); from three, two
+ * launches, the gate product into y and then the up product, whose epilogue
+ * reads g back from y (no scratch memory).
  *   w_gate, w_up [N][K/256] TQ1_0 blocks each (same shape); a [T][K/32] Q8_1
  *   blocks; y [T][N] fp32 (must not overlap the inputs).
- * 1 <= T <= BQM_GLU_MAX_COLS (decode-time calls; wider calls take the two
- * products and the epilogue apart) and rows the one-column kernel stages
- * (BQM_ERR_SHAPE otherwise). Other shapes, alignment and errors as
+ * 1 <= T <= BQM_GLU_MAX_COLS. Other shapes, alignment and errors as
  * mmvq_tq1_0. */
 BQM_API int mmvq_tq1_0_glu(const void *w_gate, const void *w_up, const void *a, float *y,
                            int64_t N, int64_t K, int32_t T, void *stream);
 
 /* The same on fp32 activations quantized to Q8_1 inside the call (bitwise
- * q8_1_quantize followed by mmvq_tq1_0_glu): x [T][K] fp32, 4-byte aligned. */
+ * q8_1_quantize followed by mmvq_tq1_0_glu): x [T][K] fp32, 4-byte aligned,
+ * 1 <= T <= BQM_GLU_F32_MAX_COLS (the decode step; wider calls quantize once
+ * and call mmvq_tq1_0_glu, which beats quantizing inside both products). */
 BQM_API int mmvq_tq1_0_f32_glu(const void *w_gate, const void *w_up, const float *x, float *y,
                                int64_t N, int64_t K, int32_t T, void *stream);
 

@@ -279,19 +279,20 @@ def test_mmvq_add_rejects():
 
 def test_mmvq_glu_rejects():
     # the gated pair: both matrices, the columns and the output required;
-    # one or two columns; every pointer 4-byte aligned
+    # up to 32 columns (fp32 columns: 2); every pointer 4-byte aligned
     lib = bqm.library()
     Y = P(0x200000)
-    assert bqm.GLU_MAX_COLS == 2
-    for fn in ("mmvq_tq1_0_glu", "mmvq_tq1_0_f32_glu"):
+    assert bqm.GLU_MAX_COLS == 32
+    assert bqm.GLU_F32_MAX_COLS == 2
+    for fn, tmax in (("mmvq_tq1_0_glu", 32), ("mmvq_tq1_0_f32_glu", 2)):
         f = getattr(lib, fn)
         f.restype = ctypes.c_int
+        assert f(GOOD, GOOD, GOOD, Y, 8, 256, tmax + 1, None) == -2
         assert f(None, GOOD, GOOD, Y, 8, 256, 1, None) == -1
         assert f(GOOD, None, GOOD, Y, 8, 256, 1, None) == -1
         assert f(GOOD, GOOD, None, Y, 8, 256, 1, None) == -1
         assert f(GOOD, GOOD, GOOD, None, 8, 256, 1, None) == -1
         assert f(GOOD, GOOD, GOOD, Y, 8, 256, 0, None) == -2
-        assert f(GOOD, GOOD, GOOD, Y, 8, 256, 3, None) == -2
         assert f(GOOD, GOOD, GOOD, Y, 0, 256, 1, None) == -2
         assert f(GOOD, GOOD, GOOD, Y, 8, 300, 1, None) == -2
         assert f(ODD, GOOD, GOOD, Y, 8, 256, 1, None) == -3

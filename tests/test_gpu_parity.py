@@ -869,19 +869,26 @@ def _glu_case(bqm, N, K, T, seed, gate_scale=(0.01, 0.1)):
     return wg, wu, a, x, wg_ref, wu_ref, a_ref
 
 
-# (N, K, T): one and two columns; ragged row counts, odd block counts, one-block
-# rows, the decode and FFN matrices, rows longer than one staging pass (129
-# blocks)
+# (N, K, T): one and two columns (one launch of wave pairs); ragged row counts,
+# odd block counts, one-block rows, the decode and FFN matrices, rows longer
+# than one staging pass (129 blocks). From three columns two launches, the up
+# product's epilogue reading the gate products: three and four columns on the
+# quad kernel (rows of more than 8 blocks) and on the staged kernel (shorter
+# rows), 5 to 32 on the register-operand kernel (rows of 5 to 16 blocks), the
+# resident kernel (5120 x 6144) and the streamed one (rows of 129 blocks).
 GLU_SHAPES = [(1, 256, 1), (5, 256, 2), (70, 768, 1), (70, 768, 2), (129, 2304, 1),
               (300, 4096, 2), (4096, 4096, 1), (4096, 4096, 2), (14336, 4096, 1),
-              (64, 33024, 1), (40, 33024, 2)]
+              (64, 33024, 1), (40, 33024, 2),
+              (300, 4096, 3), (130, 2304, 4), (70, 768, 3), (50, 1280, 8),
+              (300, 4096, 5), (4096, 4096, 16), (200, 4096, 32), (5120, 6144, 8),
+              (96, 6144, 20), (40, 33024, 6)]
 
 
 @pytest.mark.parametrize("N,K,T", GLU_SHAPES)
 def test_mmvq_glu_parity(bqm, N, K, T):
     """Against the oracle's silu(g) * u with the carried tolerance; within a
     few ulp of the same epilogue applied (in fp64) to the two plain products;
-    the fp32-input call bitwise the Q8_1 one."""
+    the fp32-input call (up to two columns) bitwise the Q8_1 one."""
     wg, wu, a, x, wg_ref, wu_ref, a_ref = _glu_case(bqm, N, K, T, 7100 + N + T)
     _say("mmvq_glu", N, K, T)
     y = _host(bqm.mmvq_tq1_0_glu(wg, wu, a, N, K, T))
@@ -891,8 +898,9 @@ def test_mmvq_glu_parity(bqm, N, K, T):
     u = _host(bqm.mmvq_tq1_0(wu, a, N, K, T)).astype(np.float64)
     yr = g / (1.0 + np.exp(-g)) * u
     assert np.all(np.abs(y - yr) <= 8 * EPS32 * np.abs(yr) + 1e-37)
-    yf = _host(bqm.mmvq_tq1_0_f32_glu(wg, wu, _dev(x), N, K, T))
-    assert np.array_equal(yf.view(np.uint32), y.view(np.uint32))
+    if T <= 2:
+        yf = _host(bqm.mmvq_tq1_0_f32_glu(wg, wu, _dev(x), N, K, T))
+        assert np.array_equal(yf.view(np.uint32), y.view(np.uint32))
 
 
 def test_mmvq_glu_saturation_and_zero_gate(bqm):
