@@ -1240,3 +1240,76 @@ def test_random_shapes_mmvq_id(bqm, E, N, K, T, n_used):
     ys = _host(bqm.mmvq_id_tq1_0_slots(w, a_s, _dev(ids), E, N, K, T, n_used))
     _, y64s, abs_ = oracle.mmvq_id(w_ref, a_s_ref, ids, E, N, K, T, n_used, per_slot=True)
     _assert_close(ys, y64s, abs_, "random mmvq_id_slots %d %d %d %d %d" % (E, N, K, T, n_used))
+
+
+# ---------------------------------------------------------------------------
+# Graph capture: every entry point recorded in one HIP graph, replayed several
+# times with eager work and synchronizations in between, each replay bitwise
+# the eager results
+# ---------------------------------------------------------------------------
+
+def test_graph_replays_match_eager(bqm):
+    import torch
+    m = bqm._m  # the binding itself: outputs allocated here, before capture
+    N, K, T = 512, 2048, 8
+    trits, d16, x = _case(N, K, T, seed=9100)
+    tu, du, _ = _case(N, K, T, seed=9101)
+    w = m.tq1_pack(_dev(trits), _dev(d16.view(np.int16)))
+    wu = m.tq1_pack(_dev(tu), _dev(du.view(np.int16)))
+    xd = _dev(x)
+    r = _dev(np.random.default_rng(9102).standard_normal((T, N)).astype(np.float32))
+    E, NE, KE, TE, n_used = 16, 256, 1024, 20, 4  # 80 pairs: the routing pre-pass
+    rng = np.random.default_rng(9103)
+    te = synth.ternary(rng, (E * NE, KE))
+    de = synth.block_scales_f16(rng, (E * NE, KE // 256), 0.01, 0.1)
+    we = m.tq1_pack(_dev(te), _dev(de.view(np.int16)))
+    ids = _dev(synth.zipf_routing(rng, TE, E, n_used))
+    xe = _dev(synth.activations(rng, TE, KE))
+    ws = torch.empty(max(m.mmvq_id_tq1_0_workspace_bytes(E, TE, n_used), 256), dtype=torch.uint8,
+                     device="cuda")
+    rows = _dev(np.array([3, 0, N - 1, 77], np.int32))
+    xm = _dev(synth.activations(np.random.default_rng(9104), 64, K))
+    outs = {
+        "a": torch.empty((T, K // 32 * 36), dtype=torch.uint8, device="cuda"),
+        "ae": torch.empty((TE, KE // 32 * 36), dtype=torch.uint8, device="cuda"),
+        "am": torch.empty((64, K // 32 * 36), dtype=torch.uint8, device="cuda"),
+        "y1": torch.empty((1, N), device="cuda"), "y8": torch.empty((T, N), device="cuda"),
+        "yf": torch.empty((1, N), device="cuda"), "yadd": torch.empty((T, N), device="cuda"),
+        "yg2": torch.empty((2, N), device="cuda"), "yg8": torch.empty((T, N), device="cuda"),
+        "ym": torch.empty((64, N), device="cuda"),
+        "ye": torch.empty((TE, n_used, NE), device="cuda"),
+        "dq": torch.empty((N, K), dtype=torch.float16, device="cuda"),
+        "dg": torch.empty((4, K), dtype=torch.bfloat16, device="cuda"),
+    }
+
+    def step():
+        o = outs
+        m.q8_1_quantize(xd, out=o["a"])
+        m.q8_1_quantize(xe, out=o["ae"])
+        m.q8_1_quantize(xm, out=o["am"])
+        m.mmvq_tq1_0(w, o["a"][:1], N, K, 1, out=o["y1"])
+        m.mmvq_tq1_0(w, o["a"], N, K, T, out=o["y8"])
+        m.mmvq_tq1_0_f32(w, xd[:1], N, K, 1, out=o["yf"])
+        m.mmvq_tq1_0_add(w, o["a"], r, N, K, T, out=o["yadd"])
+        m.mmvq_tq1_0_glu(w, wu, o["a"][:2], N, K, 2, out=o["yg2"])
+        m.mmvq_tq1_0_glu(w, wu, o["a"], N, K, T, out=o["yg8"])
+        m.mm_tq1_0(w, o["am"], N, K, 64, out=o["ym"])
+        m.mmvq_id_tq1_0(we, o["ae"], ids, E, NE, KE, TE, n_used, out=o["ye"], workspace=ws)
+        m.tq1_dequantize(w, N, K, dtype=torch.float16, out=o["dq"])
+        m.tq1_dequantize(w, N, K, rows=rows, dtype=torch.bfloat16, out=o["dg"])
+
+    _say("graph replays", N, K, T)
+    step()
+    torch.cuda.synchronize()
+    eager = {k: v.clone() for k, v in outs.items()}
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    for rep in range(3):
+        for v in outs.values():
+            v.view(torch.uint8).fill_(0xA5)  # eager work between replays
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for k, v in outs.items():
+            assert torch.equal(v.view(torch.uint8), eager[k].view(torch.uint8)), (rep, k)
