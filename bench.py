@@ -749,8 +749,9 @@ def sweep_report(sweep_json, traced_json=None, cpu_json=None):
 
 def profile_run(spec, torch, np, bqm, synth, dev):
     """A few launches of one workload shape for counter collection: `launches`
-    mat-vec calls on cold weight copies (or, with a fourth field dq_f16,
-    dq_bf16 or dq_f32, dequantizations of the whole matrix to that type),
+    mat-vec calls on cold weight copies (or, with a fourth field mm, calls of
+    the many-column product; with dq_f16, dq_bf16 or dq_f32, dequantizations
+    of the whole matrix to that type),
     then as many streaming reads of the same weight bytes by the probe kernel
     and copies of them (references of known size)."""
     parts = spec.split(":")
@@ -764,7 +765,10 @@ def profile_run(spec, torch, np, bqm, synth, dev):
                       torch.from_numpy(inp.d16.view(np.int16)).to(dev))
     wrot, R = rotation(torch, w0, dev)
     a = bqm.q8_1_quantize(torch.from_numpy(inp.x[:T]).to(dev))
-    if op != "mmvq":
+    if op == "mm":
+        y = torch.empty((T, N), dtype=torch.float32, device=dev)
+        run = lambda i: bqm.mm_tq1_0(wrot[i % R], a, N, K, T, out=y)
+    elif op != "mmvq":
         dt = {"dq_f16": torch.float16, "dq_bf16": torch.bfloat16, "dq_f32": torch.float32}[op]
         dq = torch.empty((N, K), dtype=dt, device=dev)
         run = lambda i: bqm.tq1_dequantize(wrot[i % R], N, K, dtype=dt, out=dq)

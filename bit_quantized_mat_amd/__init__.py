@@ -173,7 +173,9 @@ def mmvq_tq1_0(w, a, N, K, T, out=None, stream=None):
 
 def mm_tq1_0(w, a, N, K, T, out=None, stream=None):
     """y fp32 [T, N] = TQ1_0 weights [N, K] times T Q8_1 activation columns,
-    any T up to MM_MAX_COLS (each column bitwise mmvq_tq1_0's)."""
+    any T up to MM_MAX_COLS: within the header's stated bound of the exact
+    sums; up to 32 columns the call is mmvq_tq1_0, beyond it not necessarily
+    bitwise mmvq_tq1_0's."""
     torch = _torch()
     if out is None:
         out = torch.empty((T, N), dtype=torch.float32, device=w.device)
