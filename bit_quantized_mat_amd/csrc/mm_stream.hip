@@ -115,26 +115,45 @@ __device__ __forceinline__ void row_group(__amdgpu_buffer_rsrc_t rw, __amdgpu_bu
 #pragma unroll
         for (int i = 0; i < 4; i++)
             dw[i] = __shfl(op.dw, 4 * rg + i, 64);
+        // the products of (column tile, sub-block) j + 1 are issued before
+        // the fp32 work on those of j, and the B operand of j + 2 is read
+        // from LDS meanwhile, so neither waits on the one just issued
+        auto bq_at = [&](int j) -> long {
+            const u32x2 bv = *reinterpret_cast<const u32x2 *>(bqB + (j >> 3) * 8 * 128 + 2 * lane +
+                                                             (j & 7) * 128);
+            return (long)(((uint64_t)bv.y << 32) | bv.x);
+        };
+        auto product = [&](int j, long Bq) -> i32x4 {
+            const i32x4 neg_sum = __builtin_amdgcn_mfma_i32_16x16x32_i8(kAllMinusOne, Bq,
+                                                                        (i32x4){0, 0, 0, 0}, 0, 0, 0);
+            return __builtin_amdgcn_mfma_i32_16x16x32_i8(op.A[j & 7], Bq, neg_sum, 0, 0, 0);
+        };
+        constexpr int kJ = 8 * kMmCols;
+        long Bn = bq_at(1);
+        i32x4 Cn = product(0, bq_at(0));
+        u32x4 dv;
+        float s[4];
 #pragma unroll
-        for (int ct = 0; ct < kMmCols; ct++) {
-            const u32x4 dv = *reinterpret_cast<const u32x4 *>(dahB + (ct * 16 + col) * 4);
-            const uint32_t *bqc = bqB + ct * 8 * 128 + 2 * lane;
-            float s[4];
-#pragma unroll
-            for (int b = 0; b < 8; b++) {
-                const u32x2 bv = *reinterpret_cast<const u32x2 *>(bqc + b * 128);
-                const long Bq = (long)(((uint64_t)bv.y << 32) | bv.x);
-                const i32x4 neg_sum = __builtin_amdgcn_mfma_i32_16x16x32_i8(
-                    kAllMinusOne, Bq, (i32x4){0, 0, 0, 0}, 0, 0, 0);
-                const i32x4 C = __builtin_amdgcn_mfma_i32_16x16x32_i8(op.A[b], Bq, neg_sum, 0, 0, 0);
-                const float da = f16_bits_to_f32(dv[b >> 1] >> (16 * (b & 1)));
-#pragma unroll
-                for (int i = 0; i < 4; i++)
-                    s[i] = b == 0 ? da * (float)C[i] : fmaf(da, (float)C[i], s[i]);
+        for (int j = 0; j < kJ; j++) {
+            const int ct = j >> 3, b = j & 7;
+            const i32x4 C = Cn;
+            if (j + 1 < kJ) {
+                Cn = product(j + 1, Bn);
+                if (j + 2 < kJ)
+                    Bn = bq_at(j + 2);
             }
+            if (b == 0)
+                dv = *reinterpret_cast<const u32x4 *>(dahB + (ct * 16 + col) * 4);
+            __builtin_amdgcn_sched_barrier(0);
+            const float da = f16_bits_to_f32(dv[b >> 1] >> (16 * (b & 1)));
 #pragma unroll
             for (int i = 0; i < 4; i++)
-                acc[ct][i] = fmaf(dw[i], s[i], acc[ct][i]);
+                s[i] = b == 0 ? da * (float)C[i] : fmaf(da, (float)C[i], s[i]);
+            if (b == 7) {
+#pragma unroll
+                for (int i = 0; i < 4; i++)
+                    acc[ct][i] = fmaf(dw[i], s[i], acc[ct][i]);
+            }
         }
         if ((B + 1) % kFoldBlocks == 0) {
 #pragma unroll
@@ -165,10 +184,11 @@ __device__ __forceinline__ void row_group(__amdgpu_buffer_rsrc_t rw, __amdgpu_bu
 // 65535; the few workgroups past the last row group exit at once).
 // Workgroups of one row group are adjacent in dispatch order, so the L2
 // serves the row group's weights to its column groups from one HBM read.
-// Three waves per SIMD rather than four: at the 128 registers of four, the
-// compiler funnels every matrix-core product through one or two accumulator
-// quads and serializes them; with room for about 133 each sub-block's
-// products get registers of their own.
+// The register budget is that of three waves per SIMD: under the 128
+// registers of four, the compiler would funnel every matrix-core product
+// through one or two accumulator quads and serialize them. With the products
+// issued one (column tile, sub-block) ahead of their fp32 work the kernel
+// needs 126, so four waves still fit.
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void mm_stream_kernel(
     const uint8_t *__restrict__ w, const uint8_t *__restrict__ a, float *__restrict__ y, int64_t N,
     int nb, int T, int64_t nrowgroups)

@@ -206,46 +206,55 @@ __global__ __launch_bounds__(64 * NW) void mmvq_mfma_reg_kernel(const uint8_t *_
 #pragma unroll
             for (int i = 0; i < 4; i++)
                 dw[i] = __shfl(op.dw, dw_src + i, 64);
-#pragma unroll
-            for (int ct = 0; ct < NT; ct++) {
-                const RegOperands<PAIR> &o = opnd[gi][ct];
-                float s[4];
-#pragma unroll
-                for (int b = 0; b < 8; b++) {
-                    // -sum(q) of this lane's column on every row, then + sum(u q)
-                    i32x4 C;
-                    if constexpr (PAIR) {
-                        const i32x4 neg_sum = __builtin_amdgcn_mfma_i32_16x16x64_i8(
-                            kAllMinusOne4, o.Bq[b], (i32x4){0, 0, 0, 0}, 0, 0, 0);
-                        C = __builtin_amdgcn_mfma_i32_16x16x64_i8(op.A[b], o.Bq[b], neg_sum, 0,
-                                                                  0, 0);
-                    } else {
-                        const i32x4 neg_sum = __builtin_amdgcn_mfma_i32_16x16x32_i8(
-                            kAllMinusOne, o.Bq[b], (i32x4){0, 0, 0, 0}, 0, 0, 0);
-                        C = __builtin_amdgcn_mfma_i32_16x16x32_i8(op.A[b], o.Bq[b], neg_sum, 0,
-                                                                  0, 0);
-                    }
-                    if (ISUMS) {
-                        const int c = PAIR ? (col & 7) : ct * 16 + col;
-#pragma unroll
-                        for (int i = 0; i < 4; i++) {
-                            const int64_t row = r0 + (PAIR ? 16 * (col >> 3) : 0) + 4 * rg + i;
-                            if (c < T && row < N)
-                                isums[((int64_t)c * N + row) * nblk + 8 * B + b] = C[i];
-                        }
-                    } else {
-                        // the staged kernels' fp32 order: s = sum_b da[b] * isum[b]
-                        // from b = 0 up, then acc + dw * s
-                        const float da = f16_bits_to_f32(o.da2[b >> 1] >> (16 * (b & 1)));
-#pragma unroll
-                        for (int i = 0; i < 4; i++)
-                            s[i] = b == 0 ? da * (float)C[i] : fmaf(da, (float)C[i], s[i]);
-                    }
+            // the products of (column tile, sub-block) j + 1 are issued
+            // before the work on those of j, so that work does not wait for
+            // the matrix cores
+            auto product = [&](int j) -> i32x4 {
+                const RegOperands<PAIR> &o = opnd[gi][j >> 3];
+                const int b = j & 7;
+                // -sum(q) of this lane's column on every row, then + sum(u q)
+                if constexpr (PAIR) {
+                    const i32x4 neg_sum = __builtin_amdgcn_mfma_i32_16x16x64_i8(
+                        kAllMinusOne4, o.Bq[b], (i32x4){0, 0, 0, 0}, 0, 0, 0);
+                    return __builtin_amdgcn_mfma_i32_16x16x64_i8(op.A[b], o.Bq[b], neg_sum, 0, 0,
+                                                                 0);
+                } else {
+                    const i32x4 neg_sum = __builtin_amdgcn_mfma_i32_16x16x32_i8(
+                        kAllMinusOne, o.Bq[b], (i32x4){0, 0, 0, 0}, 0, 0, 0);
+                    return __builtin_amdgcn_mfma_i32_16x16x32_i8(op.A[b], o.Bq[b], neg_sum, 0, 0,
+                                                                 0);
                 }
-                if (!ISUMS) {
+            };
+            i32x4 Cn = product(0);
+            float s[4];
+#pragma unroll
+            for (int j = 0; j < 8 * NT; j++) {
+                const int ct = j >> 3, b = j & 7;
+                const i32x4 C = Cn;
+                if (j + 1 < 8 * NT)
+                    Cn = product(j + 1);
+                __builtin_amdgcn_sched_barrier(0);
+                if (ISUMS) {
+                    const int c = PAIR ? (col & 7) : ct * 16 + col;
+#pragma unroll
+                    for (int i = 0; i < 4; i++) {
+                        const int64_t row = r0 + (PAIR ? 16 * (col >> 3) : 0) + 4 * rg + i;
+                        if (c < T && row < N)
+                            isums[((int64_t)c * N + row) * nblk + 8 * B + b] = C[i];
+                    }
+                } else {
+                    // the staged kernels' fp32 order: s = sum_b da[b] * isum[b]
+                    // from b = 0 up, then acc + dw * s
+                    const float da =
+                        f16_bits_to_f32(opnd[gi][ct].da2[b >> 1] >> (16 * (b & 1)));
 #pragma unroll
                     for (int i = 0; i < 4; i++)
-                        acc[gi][ct][i] = fmaf(dw[i], s[i], acc[gi][ct][i]);
+                        s[i] = b == 0 ? da * (float)C[i] : fmaf(da, (float)C[i], s[i]);
+                    if (b == 7) {
+#pragma unroll
+                        for (int i = 0; i < 4; i++)
+                            acc[gi][ct][i] = fmaf(dw[i], s[i], acc[gi][ct][i]);
+                    }
                 }
             }
             }
