@@ -497,7 +497,7 @@ __global__ __launch_bounds__(64 * NW) void mmvq_mfma_res_kernel(const uint8_t *_
                     if (j == 0 && c < T && row < N) {
                         const int64_t yc = ID ? colpair[c] : c;
                         const int64_t o = yc * N + row;
-                        y[o] = epilogue(v, resid, o);
+                        y[o] = ID ? v : epilogue(v, resid, o);  // expert items add nothing
                     }
                 }
             } else {
@@ -533,7 +533,8 @@ __global__ __launch_bounds__(64 * NW) void mmvq_mfma_res_kernel(const uint8_t *_
                                                         4 * rg + i;
                                     if (row < N) {
                                         const int64_t o = yc * N + row;
-                                        y[o] = epilogue(acc[0][rt][ct][i], resid, o);
+                                        y[o] = ID ? acc[0][rt][ct][i]
+                                                  : epilogue(acc[0][rt][ct][i], resid, o);
                                     }
                                 }
                             }
