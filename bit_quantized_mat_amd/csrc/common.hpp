@@ -88,7 +88,18 @@ inline const float *gated_epilogue(const float *g)
     return reinterpret_cast<const float *>(reinterpret_cast<uintptr_t>(g) | 1u);
 }
 
-// The stored value of output element o for product value v.
+// silu(g) * v, kept out of line: only gate-up calls take it, and its exp
+// inlined into every product kernel grew their code and slowed the plain
+// calls of the larger ones
+__device__ __attribute__((noinline)) float gated_value(float g, float v)
+{
+    return g / (1.0f + expf(-g)) * v;
+}
+
+// The stored value of output element o for product value v. GATED = false
+// for kernel instances that gate-up calls never reach (they take the
+// residual add only, and carry no call).
+template <bool GATED = true>
 __device__ __forceinline__ float epilogue(float v, const float *tagged, int64_t o)
 {
     const uintptr_t p = reinterpret_cast<uintptr_t>(tagged);
@@ -96,7 +107,10 @@ __device__ __forceinline__ float epilogue(float v, const float *tagged, int64_t 
     if (!r)
         return v;
     const float e = r[o];
-    return (p & 1u) ? e / (1.0f + expf(-e)) * v : v + e;
+    if constexpr (!GATED)
+        return v + e;
+    else
+        return (p & 1u) ? gated_value(e, v) : v + e;
 }
 
 // Bytes [s, s+4) of the 8-byte little-endian value hi:lo, s in {0, 2}.

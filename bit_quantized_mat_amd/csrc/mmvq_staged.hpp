@@ -438,7 +438,8 @@ __device__ __forceinline__ void staged_rows(__amdgpu_buffer_rsrc_t rw, __amdgpu_
             for (int t = 0; t < TC; t++)
                 if (t < T) {
                     if constexpr (std::is_same_v<Store, std::nullptr_t>)
-                        out[t][row] = epilogue(acc[t], resid, (int64_t)t * N + row);
+                        // gate-up calls come here from three columns (TC 4, 8)
+                        out[t][row] = epilogue<(TC > 2)>(acc[t], resid, (int64_t)t * N + row);
                     else
                         store(t, acc[t]);
                 }
